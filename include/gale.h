@@ -1,0 +1,223 @@
+/*
+ * gale.h - C ABI of libgale: the GALE 1-bit routed-expert matmul on one AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The method (DeepSeek-V4-Flash GALE 1-bit model card, "What is in the pack"):
+ * every routed-expert matrix Wq [rows, cols] stores one sign bit per weight under
+ * a blocked FWHT-1024 rotation of the input, an fp16 scale per 128-weight block,
+ * and about 1 % outliers as int4 values with a per-row fp16 scale.  A product is
+ *     y = Wq . (blockdiag(H_1024) . x),   H[i][j] = (-1)^popcount(i & j) / 32,
+ * with Wq[n][k] = s[n][k/128] * (1 - 2 b[n][k]) + r[n] * q at each outlier (n, k).
+ * The expert FFN (w1 gate, w3 up, w2 down; same card, "What is in the pack") is
+ *     h = silu(w1 . H x) * (w3 . H x),   y = w2 . (H h),
+ * and a routed layer sums the top-k experts of each token weighted by the softmax
+ * of their router logits (same card, "Measured performance": 43 x 6 experts per token).
+ * The decode kernels multiply straight out of the packed record, as the
+ * DeepSeek-V4-Pro-671B-GALE-1bit-v4 page describes for its direct GEMV (serving
+ * knobs paragraph, DSV4_DIRECT_GEMV) and its single-kernel Walsh-Hadamard
+ * transform (DSV4_FWHT=butterfly).
+ *
+ * Conventions for every entry point
+ *  - Pointers are device pointers unless a comment says "host".
+ *  - The caller owns every buffer (weights, descriptor tables, activations,
+ *    outputs, workspace).  The library never allocates or frees memory and keeps
+ *    no state except a thread-local error message.
+ *  - Compute calls enqueue on `stream` and return without synchronising.  They
+ *    make no allocation, no synchronisation and no host<->device copy.
+ *  - Arguments are validated on the host before anything is enqueued; a call that
+ *    returns an error has enqueued nothing.  Launch failures return GALE_ERR_HIP.
+ *    Device faults surface at the caller's next synchronisation.
+ *  - Descriptor contents (pointers, CSR offsets) are trusted on the device; use
+ *    gale_check_canonical() on the host to validate canonical data before packing.
+ *  - fp16 values are IEEE binary16 bit patterns (uint16_t); fp16 outputs are
+ *    rounded to nearest even; subnormal fp16 scales are honoured.
+ */
+#ifndef GALE_H
+#define GALE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------- */
+#define GALE_OK               0
+#define GALE_ERR_NULL        (-1)  /* a required pointer is NULL */
+#define GALE_ERR_SHAPE       (-2)  /* a size is out of range or inconsistent */
+#define GALE_ERR_DTYPE       (-3)  /* unknown dtype code */
+#define GALE_ERR_ALIGN       (-4)  /* a pointer is not aligned as required */
+#define GALE_ERR_WORKSPACE   (-5)  /* workspace missing or too small */
+#define GALE_ERR_UNSUPPORTED (-6)  /* valid request this build does not implement */
+#define GALE_ERR_FORMAT      (-7)  /* canonical data violates the format */
+#define GALE_ERR_HIP         (-8)  /* a HIP runtime call failed */
+
+/* ---- dtype codes and flags ---------------------------------------------- */
+#define GALE_F16 1
+#define GALE_F32 2
+
+#define GALE_X_ROTATED    0x1u   /* x is already H.x (fp32 or fp16); skip the rotation */
+#define GALE_PATH_DECODE  0x10u  /* gale_moe_layer_fwd: force the per-expert GEMV path */
+#define GALE_PATH_GROUPED 0x20u  /* gale_moe_layer_fwd: force the grouped MFMA path */
+
+/* ---- limits -------------------------------------------------------------- */
+#define GALE_FWHT_N        1024   /* rotation block ("blocked FWHT-1024") */
+#define GALE_SCALE_BLOCK    128   /* weights per fp16 block scale */
+#define GALE_MAX_COLS     16384   /* cols: multiple of 1024, at most this */
+#define GALE_MAX_ROWS   1048576   /* rows: multiple of 16, at most this */
+#define GALE_MAX_TOPK         8
+#define GALE_MAX_EXPERTS    512
+#define GALE_MAX_DECODE_TOKENS 64 /* gale_moe_layer_fwd decode path limit */
+
+/*
+ * Device layout of one packed matrix (produced by gale_pack_*), rows % 16 == 0,
+ * cols % 1024 == 0, C = cols / 1024:
+ *  signs         uint32 [rows/16][C][2][64][4]   (rows*cols/32 words, 16-byte aligned)
+ *      word (t, c, h, l, e) holds, for row n = 16 t + (l % 16) and
+ *      q = 8 (l / 16) + 4 h + e, bit (8 i + d) = b[n][1024 c + 128 d + 4 q + i],
+ *      i in 0..3, d in 0..7.  One 2 KB tile = 16 rows x 1024 columns, read by one
+ *      wavefront as two fully coalesced 1 KB dwordx4 loads.
+ *  block_scales  fp16 [rows/16][C][16][8]: s[16 t + r][8 c + d] (16-byte aligned)
+ *  row_scales    fp16 [rows]                 (canonical)
+ *  row_ptr       int32 [rows + 1]            (canonical CSR offsets)
+ *  out_cols      uint16 [nnz]                (canonical, ascending within a row)
+ *  out_vals      uint8 [ceil(nnz/2)]         (canonical int4, low nibble first)
+ */
+typedef struct gale_matrix {
+    const uint32_t* signs;
+    const uint16_t* block_scales;
+    const uint16_t* row_scales;
+    const int32_t*  row_ptr;
+    const uint16_t* out_cols;
+    const uint8_t*  out_vals;
+} gale_matrix;
+
+/* One routed expert: w1 (gate) and w3 (up) are [inter, hidden], w2 (down) is [hidden, inter]. */
+typedef struct gale_expert {
+    gale_matrix w1, w3, w2;
+} gale_expert;
+
+/* Bytes of each packed section of one matrix. */
+typedef struct gale_sizes {
+    size_t signs, block_scales, row_scales, row_ptr, out_cols, out_vals;
+    size_t format_bytes;  /* signs + block scales + row scales + out_cols + out_vals (row_ptr excluded) */
+} gale_sizes;
+
+/* ---- errors ---------------------------------------------------------------- */
+const char* gale_status_str(int status);
+/* Detail of the last error on the calling thread ("" if none). */
+const char* gale_last_error(void);
+
+/* ---- format helpers (host only, no GPU needed) ----------------------------- */
+
+/* Section sizes of a [rows, cols] matrix with nnz outliers.  out: host. */
+int gale_packed_sizes(int32_t rows, int32_t cols, int64_t nnz, gale_sizes* out);
+
+/* Validate canonical CSR outliers (host pointers): row_ptr monotone from 0 to nnz,
+ * columns < cols and strictly ascending within each row.  GALE_ERR_FORMAT on violation. */
+int gale_check_canonical(int32_t rows, int32_t cols, const int32_t* row_ptr,
+                         const uint16_t* out_cols, int64_t nnz);
+
+/* Canonical -> device layout for the sections that change (signs, block scales), on the
+ * host.  canon_signs: uint32 [rows][cols/32], b[n][k] = bit (k % 32) of word k / 32;
+ * canon_scales: fp16 [rows][cols/128].  All pointers host; outputs sized by
+ * gale_packed_sizes.  Outliers and row scales are stored canonically (copy as is). */
+int gale_pack_host(int32_t rows, int32_t cols, const uint32_t* canon_signs,
+                   const uint16_t* canon_scales, uint32_t* dev_signs, uint16_t* dev_scales);
+
+/* Inverse of gale_pack_host (host pointers). */
+int gale_unpack_host(int32_t rows, int32_t cols, const uint32_t* dev_signs,
+                     const uint16_t* dev_scales, uint32_t* canon_signs, uint16_t* canon_scales);
+
+/* ---- packing and bit-exact checks on the GPU -------------------------------- */
+
+/* gale_pack_host for n_mat matrices stored back to back, on the device. */
+int gale_pack_device(int32_t rows, int32_t cols, int32_t n_mat, const uint32_t* canon_signs,
+                     const uint16_t* canon_scales, uint32_t* dev_signs, uint16_t* dev_scales,
+                     hipStream_t stream);
+
+/* Device layout -> canonical sign words, decoding every bit with the same plane masks the
+ * GEMV kernel applies.  dev_signs: one packed matrix; canon_signs: uint32 [rows][cols/32]. */
+int gale_debug_unpack_signs(int32_t rows, int32_t cols, const uint32_t* dev_signs,
+                            uint32_t* canon_signs, hipStream_t stream);
+
+/* Decode the outliers of one matrix as the GEMV kernel does: for each CSR entry p, write its
+ * row (int32), column (int32) and int4 value (int32, -8..7).  Any pointer may be NULL. */
+int gale_debug_unpack_outliers(int32_t rows, int64_t nnz, const gale_matrix* m_host,
+                               int32_t* out_row, int32_t* out_col, int32_t* out_val,
+                               hipStream_t stream);
+
+/* ---- compute -------------------------------------------------------------- */
+
+/* Blocked Walsh-Hadamard transform (DeepSeek-V4-Pro GALE page, serving knobs: a single-kernel
+ * butterfly, exact to 1e-8 of the matrix form): for every vector v and block beta,
+ *   y[v][1024 beta + i] = sum_j H[i][j] x[v][1024 beta + j].
+ * x, y: [n_vec][len], len % 1024 == 0, dtypes GALE_F16 / GALE_F32; fp32 arithmetic.
+ * In place (x == y) is allowed when the dtypes match. */
+int gale_fwht1024(const void* x, void* y, int64_t n_vec, int32_t len, int32_t in_dtype,
+                  int32_t out_dtype, hipStream_t stream);
+
+/* Workspace bytes for gale_expert_gemv. */
+size_t gale_gemv_workspace_bytes(int32_t rows, int32_t cols, int32_t n_mat, int32_t n_tok,
+                                 int32_t x_shared);
+
+/* Batched direct GEMV (DeepSeek-V4-Pro GALE page, serving knobs: a GEMV that multiplies
+ * straight out of a packed record, with a batched mode over many matrices):
+ *   y[m][t][:] = Wq_m . (H . x[m][t][:])   for m < n_mat, t < n_tok.
+ * mats_dev: device array of n_mat gale_matrix descriptors, all [rows, cols].
+ * x: [n_mat][n_tok][cols] (or [n_tok][cols] shared by all matrices when x_shared != 0),
+ *    dtype x_dtype (GALE_F16 / GALE_F32); flags GALE_X_ROTATED means x is already H.x.
+ * y: [n_mat][n_tok][rows], dtype y_dtype.  ws: gale_gemv_workspace_bytes(...) bytes,
+ * 256-byte aligned.  fp32 accumulation. */
+int gale_expert_gemv(int32_t rows, int32_t cols, const gale_matrix* mats_dev, int32_t n_mat,
+                     const void* x, int32_t x_dtype, int32_t x_shared, int32_t n_tok,
+                     void* y, int32_t y_dtype, void* ws, size_t ws_bytes, uint32_t flags,
+                     hipStream_t stream);
+
+/* Workspace bytes for gale_expert_ffn. */
+size_t gale_ffn_workspace_bytes(int32_t hidden, int32_t inter, int32_t n_exp, int32_t n_tok,
+                                int32_t x_shared);
+
+/* Expert FFN for n_exp experts (model card naming: w1 gate, w3 up, w2 down):
+ *   y[e][t] = w2_e . H( silu(w1_e . H x) * (w3_e . H x) ),  x = x[e][t] (or x[t] if x_shared).
+ * experts_dev: device array of n_exp gale_expert.  x, y fp16 [.. ][n_tok][hidden];
+ * intermediate h and every sum in fp32. */
+int gale_expert_ffn(int32_t hidden, int32_t inter, const gale_expert* experts_dev, int32_t n_exp,
+                    const void* x, int32_t x_shared, int32_t n_tok, void* y,
+                    void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes for gale_moe_layer_fwd. */
+size_t gale_moe_workspace_bytes(int32_t n_tok, int32_t n_experts, int32_t top_k,
+                                int32_t hidden, int32_t inter, uint32_t flags);
+
+/* One routed-expert layer:
+ *   route: S_t = the top_k experts by (logit desc, expert index asc) of logits[t] (fp32
+ *          [n_tok][n_experts]); w[t] = softmax of those k logits (fp32).
+ *   y[t] = sum over slots j = 0..top_k-1, in order, of w[t][j] * FFN_{S_t[j]}(x[t]).
+ * x, y: fp16 [n_tok][hidden].  topk_idx (int32 [n_tok][top_k]) and topk_w (fp32) are
+ * written when non-NULL.  Path: decode (per-expert GEMV) when n_tok <= 64, grouped MFMA
+ * otherwise; flags GALE_PATH_DECODE / GALE_PATH_GROUPED force one. */
+int gale_moe_layer_fwd(int32_t hidden, int32_t inter, const gale_expert* experts_dev,
+                       int32_t n_experts, const float* logits, int32_t top_k, const void* x,
+                       int32_t n_tok, void* y, int32_t* topk_idx, float* topk_w,
+                       void* ws, size_t ws_bytes, uint32_t flags, hipStream_t stream);
+
+/* Workspace bytes for gale_route_topk with grouping of more than GALE_MAX_DECODE_TOKENS tokens. */
+size_t gale_route_workspace_bytes(int32_t n_tok, int32_t n_experts);
+
+/* Routing alone (same rule as gale_moe_layer_fwd), plus the stable grouping of the
+ * (token, slot) pairs p = t * top_k + j by expert: offsets int32 [n_experts + 1] and
+ * perm int32 [n_tok * top_k] (pairs of expert e in ascending order at
+ * perm[offsets[e] .. offsets[e+1])).  offsets and perm are both NULL (top-k only) or
+ * both set; grouping more than GALE_MAX_DECODE_TOKENS tokens needs ws of
+ * gale_route_workspace_bytes() bytes (otherwise ws may be NULL). */
+int gale_route_topk(const float* logits, int32_t n_tok, int32_t n_experts, int32_t top_k,
+                    int32_t* topk_idx, float* topk_w, int32_t* offsets, int32_t* perm,
+                    void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GALE_H */

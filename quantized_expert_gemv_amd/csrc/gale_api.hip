@@ -1,0 +1,460 @@
+// C-ABI entry points of libgale: host-side validation, workspace layout and the
+// launch sequence of each call.  No call allocates, synchronises or copies
+// between host and device; every launch goes on the caller's stream.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "gale_internal.h"
+
+namespace gale {
+
+static thread_local char g_err[512];
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+
+static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+static inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+static inline int dtype_ok(int d) { return d == GALE_F16 || d == GALE_F32; }
+
+static inline int dsize(int d) { return d == GALE_F16 ? 2 : 4; }
+
+static int check_matrix_shape(const char* fn, int rows, int cols) {
+  if (rows < 16 || rows % 16 || rows > GALE_MAX_ROWS) {
+    set_error("%s: rows=%d must be a positive multiple of 16 up to %d", fn, rows, GALE_MAX_ROWS);
+    return GALE_ERR_SHAPE;
+  }
+  if (cols < 1024 || cols % 1024 || cols > GALE_MAX_COLS) {
+    set_error("%s: cols=%d must be a positive multiple of 1024 up to %d", fn, cols, GALE_MAX_COLS);
+    return GALE_ERR_SHAPE;
+  }
+  return GALE_OK;
+}
+
+static int hip_status(const char* fn, hipError_t e) {
+  if (e != hipSuccess) {
+    set_error("%s: %s", fn, hipGetErrorString(e));
+    return GALE_ERR_HIP;
+  }
+  return GALE_OK;
+}
+
+// rows-per-workgroup choice: enough workgroups to fill 256 CUs several times over,
+// otherwise the smallest tile count.
+static int pick_tiles(int64_t items, int ntiles, uint32_t flags) {
+  const int forced = (int)((flags >> 8) & 0xF);
+  if (forced) return 1 << (forced - 1);
+  const int64_t want = 2048;
+  int r = 4;
+  while (r > 1 && items * ((ntiles + r - 1) / r) < want) r >>= 1;
+  return r;
+}
+
+static int pick_slots(int n_tok) { return n_tok >= 4 ? 4 : (n_tok >= 2 ? 2 : 1); }
+
+// ---- workspace layouts -------------------------------------------------------
+struct GemvWs {
+  size_t ra, total;
+};
+static GemvWs gemv_ws(int cols, int64_t n_x) {
+  GemvWs w;
+  w.ra = 0;
+  w.total = align256(ra_bytes(cols) * (size_t)n_x);
+  return w;
+}
+
+struct FfnWs {
+  size_t ra_x, h, ra_h, total;
+};
+static FfnWs ffn_ws(int hidden, int inter, int64_t n_x, int64_t n_pairs) {
+  FfnWs w;
+  w.ra_x = 0;
+  w.h = align256(ra_bytes(hidden) * (size_t)n_x);
+  w.ra_h = w.h + align256((size_t)4 * inter * n_pairs);
+  w.total = w.ra_h + align256(ra_bytes(inter) * (size_t)n_pairs);
+  return w;
+}
+
+struct MoeWs {
+  size_t idx, w, offsets, perm, items, n_items, ra_x, h, ra_h, yp, total;
+};
+static int64_t moe_item_bound(int T, int E, int k, int slots) {
+  const int64_t P = (int64_t)T * k;
+  return std::min<int64_t>(E, P) + (P + slots - 1) / slots;
+}
+static MoeWs moe_ws(int T, int E, int k, int hidden, int inter) {
+  MoeWs w;
+  const int64_t P = (int64_t)T * k;
+  const int slots = pick_slots(T);
+  size_t o = 0;
+  w.idx = o; o += align256(4 * P);
+  w.w = o; o += align256(4 * P);
+  w.offsets = o; o += align256(4 * (size_t)(E + 1));
+  w.perm = o; o += align256(4 * P);
+  w.items = o; o += align256(sizeof(WorkItem) * (size_t)moe_item_bound(T, E, k, slots));
+  w.n_items = o; o += 256;
+  w.ra_x = o; o += align256(ra_bytes(hidden) * (size_t)T);
+  w.h = o; o += align256((size_t)4 * inter * P);
+  w.ra_h = o; o += align256(ra_bytes(inter) * (size_t)P);
+  w.yp = o; o += align256((size_t)4 * hidden * P);
+  w.total = o;
+  return w;
+}
+
+}  // namespace gale
+
+using namespace gale;
+
+// ============================================================================
+// errors and sizes
+// ============================================================================
+extern "C" const char* gale_status_str(int s) {
+  switch (s) {
+    case GALE_OK: return "ok";
+    case GALE_ERR_NULL: return "null pointer";
+    case GALE_ERR_SHAPE: return "bad shape";
+    case GALE_ERR_DTYPE: return "bad dtype";
+    case GALE_ERR_ALIGN: return "misaligned pointer";
+    case GALE_ERR_WORKSPACE: return "workspace too small";
+    case GALE_ERR_UNSUPPORTED: return "unsupported";
+    case GALE_ERR_FORMAT: return "bad canonical format";
+    case GALE_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+extern "C" const char* gale_last_error(void) { return g_err; }
+
+extern "C" int gale_packed_sizes(int32_t rows, int32_t cols, int64_t nnz, gale_sizes* out) {
+  if (!out) { set_error("gale_packed_sizes: out is NULL"); return GALE_ERR_NULL; }
+  int st = check_matrix_shape("gale_packed_sizes", rows, cols);
+  if (st) return st;
+  if (nnz < 0 || nnz > (int64_t)rows * cols) { set_error("gale_packed_sizes: bad nnz"); return GALE_ERR_SHAPE; }
+  out->signs = (size_t)rows * cols / 8;
+  out->block_scales = (size_t)rows * (cols / 128) * 2;
+  out->row_scales = (size_t)rows * 2;
+  out->row_ptr = (size_t)(rows + 1) * 4;
+  out->out_cols = (size_t)nnz * 2;
+  out->out_vals = (size_t)(nnz + 1) / 2;
+  out->format_bytes = out->signs + out->block_scales + out->row_scales + out->out_cols + out->out_vals;
+  return GALE_OK;
+}
+
+extern "C" int gale_check_canonical(int32_t rows, int32_t cols, const int32_t* row_ptr,
+                                    const uint16_t* out_cols, int64_t nnz) {
+  int st = check_matrix_shape("gale_check_canonical", rows, cols);
+  if (st) return st;
+  if (!row_ptr || (nnz > 0 && !out_cols)) { set_error("gale_check_canonical: NULL pointer"); return GALE_ERR_NULL; }
+  if (row_ptr[0] != 0 || row_ptr[rows] != nnz) {
+    set_error("gale_check_canonical: row_ptr must start at 0 and end at nnz=%lld", (long long)nnz);
+    return GALE_ERR_FORMAT;
+  }
+  for (int n = 0; n < rows; ++n) {
+    if (row_ptr[n + 1] < row_ptr[n]) { set_error("gale_check_canonical: row_ptr decreases at row %d", n); return GALE_ERR_FORMAT; }
+    for (int p = row_ptr[n]; p < row_ptr[n + 1]; ++p) {
+      if (out_cols[p] >= cols) { set_error("gale_check_canonical: column %d >= cols at row %d", out_cols[p], n); return GALE_ERR_FORMAT; }
+      if (p > row_ptr[n] && out_cols[p] <= out_cols[p - 1]) {
+        set_error("gale_check_canonical: columns not strictly ascending at row %d", n);
+        return GALE_ERR_FORMAT;
+      }
+    }
+  }
+  return GALE_OK;
+}
+
+// ============================================================================
+// packing and debug
+// ============================================================================
+extern "C" int gale_pack_device(int32_t rows, int32_t cols, int32_t n_mat, const uint32_t* canon_signs,
+                                const uint16_t* canon_scales, uint32_t* dev_signs, uint16_t* dev_scales,
+                                hipStream_t stream) {
+  int st = check_matrix_shape("gale_pack_device", rows, cols);
+  if (st) return st;
+  if (n_mat < 1) { set_error("gale_pack_device: n_mat=%d", n_mat); return GALE_ERR_SHAPE; }
+  if (!canon_signs || !canon_scales || !dev_signs || !dev_scales) { set_error("gale_pack_device: NULL pointer"); return GALE_ERR_NULL; }
+  if (!aligned(dev_signs, 16) || !aligned(dev_scales, 16) || !aligned(canon_signs, 4) || !aligned(canon_scales, 2)) {
+    set_error("gale_pack_device: misaligned pointer");
+    return GALE_ERR_ALIGN;
+  }
+  return hip_status("gale_pack_device", launch_pack(rows, cols, n_mat, canon_signs, canon_scales, dev_signs, dev_scales, stream));
+}
+
+extern "C" int gale_debug_unpack_signs(int32_t rows, int32_t cols, const uint32_t* dev_signs,
+                                       uint32_t* canon_signs, hipStream_t stream) {
+  int st = check_matrix_shape("gale_debug_unpack_signs", rows, cols);
+  if (st) return st;
+  if (!dev_signs || !canon_signs) { set_error("gale_debug_unpack_signs: NULL pointer"); return GALE_ERR_NULL; }
+  return hip_status("gale_debug_unpack_signs", launch_debug_unpack(rows, cols, dev_signs, canon_signs, stream));
+}
+
+extern "C" int gale_debug_unpack_outliers(int32_t rows, int64_t nnz, const gale_matrix* m_host,
+                                          int32_t* out_row, int32_t* out_col, int32_t* out_val,
+                                          hipStream_t stream) {
+  if (!m_host) { set_error("gale_debug_unpack_outliers: NULL descriptor"); return GALE_ERR_NULL; }
+  if (rows < 1 || nnz < 0) { set_error("gale_debug_unpack_outliers: bad shape"); return GALE_ERR_SHAPE; }
+  if (nnz > 0 && (!m_host->row_ptr || !m_host->out_cols || !m_host->out_vals)) {
+    set_error("gale_debug_unpack_outliers: NULL section");
+    return GALE_ERR_NULL;
+  }
+  return hip_status("gale_debug_unpack_outliers", launch_debug_outliers(rows, nnz, *m_host, out_row, out_col, out_val, stream));
+}
+
+// ============================================================================
+// FWHT
+// ============================================================================
+extern "C" int gale_fwht1024(const void* x, void* y, int64_t n_vec, int32_t len, int32_t in_dtype,
+                             int32_t out_dtype, hipStream_t stream) {
+  if (!x || !y) { set_error("gale_fwht1024: NULL pointer"); return GALE_ERR_NULL; }
+  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) { set_error("gale_fwht1024: bad dtype"); return GALE_ERR_DTYPE; }
+  if (len < 1024 || len % 1024 || n_vec < 0) { set_error("gale_fwht1024: len=%d must be a positive multiple of 1024", len); return GALE_ERR_SHAPE; }
+  if (x == y && in_dtype != out_dtype) { set_error("gale_fwht1024: in place needs equal dtypes"); return GALE_ERR_DTYPE; }
+  if (!aligned(x, 16) || !aligned(y, 16)) { set_error("gale_fwht1024: x and y must be 16-byte aligned"); return GALE_ERR_ALIGN; }
+  return hip_status("gale_fwht1024", launch_fwht(x, y, n_vec, len, in_dtype, out_dtype, stream));
+}
+
+// ============================================================================
+// GEMV
+// ============================================================================
+extern "C" size_t gale_gemv_workspace_bytes(int32_t rows, int32_t cols, int32_t n_mat, int32_t n_tok,
+                                            int32_t x_shared) {
+  (void)rows;
+  if (cols < 1024 || n_mat < 1 || n_tok < 1) return 0;
+  return gemv_ws(cols, (int64_t)(x_shared ? 1 : n_mat) * n_tok).total;
+}
+
+extern "C" int gale_expert_gemv(int32_t rows, int32_t cols, const gale_matrix* mats_dev, int32_t n_mat,
+                                const void* x, int32_t x_dtype, int32_t x_shared, int32_t n_tok,
+                                void* y, int32_t y_dtype, void* ws, size_t ws_bytes, uint32_t flags,
+                                hipStream_t stream) {
+  const char* fn = "gale_expert_gemv";
+  int st = check_matrix_shape(fn, rows, cols);
+  if (st) return st;
+  if (n_mat < 1 || n_tok < 1) { set_error("%s: n_mat=%d n_tok=%d must be >= 1", fn, n_mat, n_tok); return GALE_ERR_SHAPE; }
+  if (!mats_dev || !x || !y || !ws) { set_error("%s: NULL pointer", fn); return GALE_ERR_NULL; }
+  if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype)) { set_error("%s: bad dtype", fn); return GALE_ERR_DTYPE; }
+  if (!aligned(x, 16) || !aligned(ws, 256) || !aligned(y, dsize(y_dtype)) || !aligned(mats_dev, 8)) {
+    set_error("%s: x needs 16-byte, ws 256-byte alignment", fn);
+    return GALE_ERR_ALIGN;
+  }
+  const int64_t n_x = (int64_t)(x_shared ? 1 : n_mat) * n_tok;
+  const GemvWs W = gemv_ws(cols, n_x);
+  if (ws_bytes < W.total) { set_error("%s: workspace %zu < %zu bytes", fn, ws_bytes, W.total); return GALE_ERR_WORKSPACE; }
+  uint8_t* ra = reinterpret_cast<uint8_t*>(ws) + W.ra;
+  st = hip_status(fn, launch_prep(x, x_dtype, cols, (int)n_x, cols, (flags & GALE_X_ROTATED) ? 1 : 0, ra,
+                                  ra_bytes(cols), stream));
+  if (st) return st;
+  const int slots = pick_slots(n_tok);
+  GemvParams P;
+  memset(&P, 0, sizeof(P));
+  P.table = mats_dev;
+  P.mat_stride = 1;
+  P.sel0 = P.sel1 = 0;
+  P.rows = rows;
+  P.cols = cols;
+  P.ra = ra;
+  P.ra_stride = ra_bytes(cols);
+  P.implicit_items = 1;
+  P.n_tok = n_tok;
+  P.n_groups = (n_tok + slots - 1) / slots;
+  P.x_shared = x_shared ? 1 : 0;
+  P.n_items = n_mat * P.n_groups;
+  P.ra_div = 1;
+  P.y = y;
+  P.y_dtype = y_dtype;
+  P.y_stride = rows;
+  P.gateup = 0;
+  const int ntiles = rows / 16;
+  const int R = pick_tiles(P.n_items, ntiles, flags);
+  P.row_groups = (ntiles + R - 1) / R;
+  const int64_t work = (int64_t)P.n_items * P.row_groups;
+  const int grid = (int)std::min<int64_t>(work, 1 << 20);
+  return hip_status(fn, launch_gemv(P, slots, R, grid, stream));
+}
+
+// ============================================================================
+// expert FFN
+// ============================================================================
+extern "C" size_t gale_ffn_workspace_bytes(int32_t hidden, int32_t inter, int32_t n_exp, int32_t n_tok,
+                                           int32_t x_shared) {
+  if (hidden < 1024 || inter < 1024 || n_exp < 1 || n_tok < 1) return 0;
+  return ffn_ws(hidden, inter, (int64_t)(x_shared ? 1 : n_exp) * n_tok, (int64_t)n_exp * n_tok).total;
+}
+
+static int run_gemv_phase(const char* fn, const gale_matrix* table, int stride, int sel0, int sel1,
+                          int rows, int cols, const uint8_t* ra, int implicit, int n_tok, int x_shared,
+                          int n_items, const WorkItem* items, const int32_t* n_items_dev, int ra_div,
+                          int item_bound, void* y, int y_dtype, int gateup, int slots, uint32_t flags,
+                          hipStream_t s) {
+  GemvParams P;
+  memset(&P, 0, sizeof(P));
+  P.table = table;
+  P.mat_stride = stride;
+  P.sel0 = sel0;
+  P.sel1 = sel1;
+  P.rows = rows;
+  P.cols = cols;
+  P.ra = ra;
+  P.ra_stride = ra_bytes(cols);
+  P.implicit_items = implicit;
+  P.n_tok = n_tok;
+  P.n_groups = implicit ? (n_tok + slots - 1) / slots : 0;
+  P.x_shared = x_shared;
+  P.n_items = n_items;
+  P.items = items;
+  P.n_items_dev = n_items_dev;
+  P.ra_div = ra_div;
+  P.y = y;
+  P.y_dtype = y_dtype;
+  P.y_stride = rows;
+  P.gateup = gateup;
+  const int ntiles = rows / 16;
+  const int64_t bound = implicit ? n_items : item_bound;
+  const int R = pick_tiles(bound, ntiles, flags);
+  P.row_groups = (ntiles + R - 1) / R;
+  const int grid = (int)std::min<int64_t>(bound * P.row_groups, 1 << 20);
+  return hip_status(fn, launch_gemv(P, slots, R, grid, s));
+}
+
+extern "C" int gale_expert_ffn(int32_t hidden, int32_t inter, const gale_expert* experts_dev, int32_t n_exp,
+                               const void* x, int32_t x_shared, int32_t n_tok, void* y, void* ws,
+                               size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "gale_expert_ffn";
+  int st = check_matrix_shape(fn, inter, hidden);
+  if (st) return st;
+  st = check_matrix_shape(fn, hidden, inter);
+  if (st) return st;
+  if (n_exp < 1 || n_tok < 1) { set_error("%s: n_exp=%d n_tok=%d must be >= 1", fn, n_exp, n_tok); return GALE_ERR_SHAPE; }
+  if (!experts_dev || !x || !y || !ws) { set_error("%s: NULL pointer", fn); return GALE_ERR_NULL; }
+  if (!aligned(x, 16) || !aligned(ws, 256) || !aligned(y, 2)) { set_error("%s: misaligned pointer", fn); return GALE_ERR_ALIGN; }
+  const int64_t n_x = (int64_t)(x_shared ? 1 : n_exp) * n_tok;
+  const int64_t n_p = (int64_t)n_exp * n_tok;
+  const FfnWs W = ffn_ws(hidden, inter, n_x, n_p);
+  if (ws_bytes < W.total) { set_error("%s: workspace %zu < %zu bytes", fn, ws_bytes, W.total); return GALE_ERR_WORKSPACE; }
+  uint8_t* base = reinterpret_cast<uint8_t*>(ws);
+  uint8_t* ra_x = base + W.ra_x;
+  float* h = reinterpret_cast<float*>(base + W.h);
+  uint8_t* ra_h = base + W.ra_h;
+  const gale_matrix* table = reinterpret_cast<const gale_matrix*>(experts_dev);
+  const int slots = pick_slots(n_tok);
+  st = hip_status(fn, launch_prep(x, GALE_F16, hidden, (int)n_x, hidden, 0, ra_x, ra_bytes(hidden), stream));
+  if (st) return st;
+  const int n_groups = (n_tok + slots - 1) / slots;
+  st = run_gemv_phase(fn, table, 3, 0, 1, inter, hidden, ra_x, 1, n_tok, x_shared ? 1 : 0, n_exp * n_groups,
+                      nullptr, nullptr, 1, 0, h, GALE_F32, 1, slots, 0, stream);
+  if (st) return st;
+  st = hip_status(fn, launch_prep(h, GALE_F32, inter, (int)n_p, inter, 0, ra_h, ra_bytes(inter), stream));
+  if (st) return st;
+  return run_gemv_phase(fn, table, 3, 2, 2, hidden, inter, ra_h, 1, n_tok, 0, n_exp * n_groups, nullptr,
+                        nullptr, 1, 0, y, GALE_F16, 0, slots, 0, stream);
+}
+
+// ============================================================================
+// routed layer
+// ============================================================================
+extern "C" size_t gale_moe_workspace_bytes(int32_t n_tok, int32_t n_experts, int32_t top_k, int32_t hidden,
+                                           int32_t inter, uint32_t flags) {
+  if (n_tok < 1 || n_experts < 1 || top_k < 1 || hidden < 1024 || inter < 1024) return 0;
+  const bool grouped = (flags & GALE_PATH_GROUPED) || (!(flags & GALE_PATH_DECODE) && n_tok > GALE_MAX_DECODE_TOKENS);
+  if (grouped) return prefill_workspace_bytes(n_tok, n_experts, top_k, hidden, inter);
+  return moe_ws(n_tok, n_experts, top_k, hidden, inter).total;
+}
+
+extern "C" int gale_moe_layer_fwd(int32_t hidden, int32_t inter, const gale_expert* experts_dev,
+                                  int32_t n_experts, const float* logits, int32_t top_k, const void* x,
+                                  int32_t n_tok, void* y, int32_t* topk_idx, float* topk_w, void* ws,
+                                  size_t ws_bytes, uint32_t flags, hipStream_t stream) {
+  const char* fn = "gale_moe_layer_fwd";
+  int st = check_matrix_shape(fn, inter, hidden);
+  if (st) return st;
+  st = check_matrix_shape(fn, hidden, inter);
+  if (st) return st;
+  if (n_experts < 1 || n_experts > GALE_MAX_EXPERTS || top_k < 1 || top_k > GALE_MAX_TOPK || top_k > n_experts) {
+    set_error("%s: n_experts=%d top_k=%d out of range", fn, n_experts, top_k);
+    return GALE_ERR_SHAPE;
+  }
+  if (n_tok < 1) { set_error("%s: n_tok=%d", fn, n_tok); return GALE_ERR_SHAPE; }
+  if (!experts_dev || !logits || !x || !y || !ws) { set_error("%s: NULL pointer", fn); return GALE_ERR_NULL; }
+  if (!aligned(x, 16) || !aligned(ws, 256) || !aligned(y, 2) || !aligned(logits, 4)) {
+    set_error("%s: misaligned pointer", fn);
+    return GALE_ERR_ALIGN;
+  }
+  if ((flags & GALE_PATH_DECODE) && (flags & GALE_PATH_GROUPED)) { set_error("%s: both paths forced", fn); return GALE_ERR_SHAPE; }
+  const bool grouped = (flags & GALE_PATH_GROUPED) || (!(flags & GALE_PATH_DECODE) && n_tok > GALE_MAX_DECODE_TOKENS);
+  if (grouped) {
+    const size_t need = prefill_workspace_bytes(n_tok, n_experts, top_k, hidden, inter);
+    if (ws_bytes < need) { set_error("%s: workspace %zu < %zu bytes", fn, ws_bytes, need); return GALE_ERR_WORKSPACE; }
+    return run_prefill(hidden, inter, experts_dev, n_experts, logits, top_k, x, n_tok, y, topk_idx, topk_w, ws,
+                       ws_bytes, stream);
+  }
+  if (n_tok > GALE_MAX_DECODE_TOKENS) {
+    set_error("%s: the decode path takes at most %d tokens", fn, GALE_MAX_DECODE_TOKENS);
+    return GALE_ERR_SHAPE;
+  }
+  const MoeWs W = moe_ws(n_tok, n_experts, top_k, hidden, inter);
+  if (ws_bytes < W.total) { set_error("%s: workspace %zu < %zu bytes", fn, ws_bytes, W.total); return GALE_ERR_WORKSPACE; }
+  uint8_t* base = reinterpret_cast<uint8_t*>(ws);
+  int32_t* idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(base + W.idx);
+  float* wts = topk_w ? topk_w : reinterpret_cast<float*>(base + W.w);
+  WorkItem* items = reinterpret_cast<WorkItem*>(base + W.items);
+  int32_t* n_items = reinterpret_cast<int32_t*>(base + W.n_items);
+  uint8_t* ra_x = base + W.ra_x;
+  float* h = reinterpret_cast<float*>(base + W.h);
+  uint8_t* ra_h = base + W.ra_h;
+  float* yp = reinterpret_cast<float*>(base + W.yp);
+  const int P = n_tok * top_k;
+  const int slots = pick_slots(n_tok);
+  const gale_matrix* table = reinterpret_cast<const gale_matrix*>(experts_dev);
+  st = hip_status(fn, launch_route_small(logits, n_tok, n_experts, top_k, idx, wts, nullptr, nullptr, items, n_items,
+                                         slots, stream));
+  if (st) return st;
+  st = hip_status(fn, launch_prep(x, GALE_F16, hidden, n_tok, hidden, 0, ra_x, ra_bytes(hidden), stream));
+  if (st) return st;
+  const int bound = (int)moe_item_bound(n_tok, n_experts, top_k, slots);
+  st = run_gemv_phase(fn, table, 3, 0, 1, inter, hidden, ra_x, 0, 0, 0, 0, items, n_items, top_k, bound, h,
+                      GALE_F32, 1, slots, flags, stream);
+  if (st) return st;
+  st = hip_status(fn, launch_prep(h, GALE_F32, inter, P, inter, 0, ra_h, ra_bytes(inter), stream));
+  if (st) return st;
+  st = run_gemv_phase(fn, table, 3, 2, 2, hidden, inter, ra_h, 0, 0, 0, 0, items, n_items, 1, bound, yp,
+                      GALE_F32, 0, slots, flags, stream);
+  if (st) return st;
+  return hip_status(fn, launch_combine(yp, wts, n_tok, top_k, hidden, y, GALE_F16, stream));
+}
+
+extern "C" size_t gale_route_workspace_bytes(int32_t n_tok, int32_t n_experts) {
+  if (n_tok < 1 || n_experts < 1) return 0;
+  return align256(route_chunk_count_bytes(n_tok, n_experts));
+}
+
+extern "C" int gale_route_topk(const float* logits, int32_t n_tok, int32_t n_experts, int32_t top_k,
+                               int32_t* topk_idx, float* topk_w, int32_t* offsets, int32_t* perm,
+                               void* ws, size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "gale_route_topk";
+  if (!logits || !topk_idx || !topk_w) { set_error("%s: NULL pointer", fn); return GALE_ERR_NULL; }
+  if (n_tok < 1 || n_experts < 1 || n_experts > GALE_MAX_EXPERTS || top_k < 1 || top_k > GALE_MAX_TOPK ||
+      top_k > n_experts) {
+    set_error("%s: bad sizes n_tok=%d n_experts=%d top_k=%d", fn, n_tok, n_experts, top_k);
+    return GALE_ERR_SHAPE;
+  }
+  if ((offsets == nullptr) != (perm == nullptr)) { set_error("%s: offsets and perm go together", fn); return GALE_ERR_NULL; }
+  if (!aligned(logits, 4)) { set_error("%s: misaligned logits", fn); return GALE_ERR_ALIGN; }
+  if (offsets && n_tok > GALE_MAX_DECODE_TOKENS) {
+    const size_t need = gale_route_workspace_bytes(n_tok, n_experts);
+    if (!ws || ws_bytes < need) { set_error("%s: workspace %zu < %zu bytes", fn, ws_bytes, need); return GALE_ERR_WORKSPACE; }
+    return hip_status(fn, launch_route_large(logits, n_tok, n_experts, top_k, topk_idx, topk_w,
+                                             reinterpret_cast<int32_t*>(ws), offsets, perm, stream));
+  }
+  if (n_tok <= GALE_MAX_DECODE_TOKENS)
+    return hip_status(fn, launch_route_small(logits, n_tok, n_experts, top_k, topk_idx, topk_w, offsets, perm,
+                                             nullptr, nullptr, 1, stream));
+  // top-k only, any number of tokens: the chunked kernel without grouping
+  return hip_status(fn, launch_route_large(logits, n_tok, n_experts, top_k, topk_idx, topk_w, nullptr, nullptr,
+                                           nullptr, stream));
+}

@@ -1,0 +1,126 @@
+// Internal declarations shared by the libgale translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "gale.h"
+
+namespace gale {
+
+// ---------------------------------------------------------------------------
+// Device layout index map (host and device).  A "tile" is 16 rows x 1024
+// columns; C = cols / 1024 chunks per row tile.  Within a tile, lane l of a
+// wavefront owns row (l % 16) and word group g = l / 16; its 8 words
+// q = 8 g + j (j = 0..7) sit at half h = j / 4, element e = j % 4.  Bit
+// (8 i + d) of word q is the sign of column 128 d + 4 q + i of the chunk, so
+// masking one bit position d of every byte selects exactly scale block d.
+// ---------------------------------------------------------------------------
+__host__ __device__ inline int64_t sign_word_index(int t, int c, int C, int h, int l, int e) {
+  return ((((int64_t)t * C + c) * 2 + h) * 64 + l) * 4 + e;
+}
+
+// canonical (n, k) -> (device word index, bit position)
+__host__ __device__ inline void sign_position(int n, int k, int C, int64_t* word, int* bit) {
+  int t = n >> 4, nl = n & 15;
+  int c = k >> 10, kk = k & 1023;
+  int d = kk >> 7, rem = kk & 127;
+  int q = rem >> 2, i = rem & 3;
+  int g = q >> 3, j = q & 7;
+  int l = 16 * g + nl;
+  *word = sign_word_index(t, c, C, j >> 2, l, j & 3);
+  *bit = 8 * i + d;
+}
+
+__host__ __device__ inline int64_t scale_index(int n, int blk, int C) {
+  // s[n][blk], blk = 8 c + d  ->  [n/16][c][n%16][d]
+  int t = n >> 4, r = n & 15, c = blk >> 3, d = blk & 7;
+  return (((int64_t)t * C + c) * 16 + r) * 8 + d;
+}
+
+// ---------------------------------------------------------------------------
+// Rotated-activation record ("RA"): one per activation vector of length K.
+//   [0, 4K)          x~ = blockdiag(H) x, fp32
+//   [4K, 8K)         fp8 e4m3 terms: chunk c, term t at 4K + (4 c + t) * 1024,
+//                    X = x~ * 2^p_c = t0 + t1 + t2 + t3 elementwise
+//   [8K, 8K + 4C)    p_c (int32), one per 1024-chunk
+// padded to a multiple of 256 bytes.
+// ---------------------------------------------------------------------------
+__host__ __device__ inline size_t ra_bytes(int K) {
+  size_t b = (size_t)8 * K + 4 * (size_t)(K / 1024);
+  return (b + 255) & ~(size_t)255;
+}
+__host__ __device__ inline size_t ra_terms_off(int K) { return (size_t)4 * K; }
+__host__ __device__ inline size_t ra_p_off(int K) { return (size_t)8 * K; }
+
+constexpr int kTerms = 4;
+
+// Work item of the explicit (routed) GEMV mode.
+struct WorkItem {
+  int32_t expert;     // item matrix index in the descriptor table (times stride)
+  int32_t n_slots;    // 1..4 activation vectors
+  int32_t pair[4];    // pair ids (RA index = pair / ra_div, output index = pair)
+  int32_t pad[2];
+};
+
+struct GemvParams {
+  const gale_matrix* table;  // descriptor table
+  int mat_stride;            // descriptors per item
+  int sel0, sel1;            // descriptor offsets (sel1: second matrix for gate/up)
+  int rows, cols;
+  const uint8_t* ra;         // RA records
+  size_t ra_stride;
+  // implicit items: item i = (mat i / n_groups, token group i % n_groups)
+  int implicit_items;
+  int n_tok;
+  int n_groups;
+  int x_shared;
+  int n_items;               // implicit item count
+  // explicit items
+  const WorkItem* items;
+  const int32_t* n_items_dev;
+  int ra_div;
+  // output
+  void* y;
+  int y_dtype;
+  int64_t y_stride;          // elements between consecutive output vectors
+  int gateup;                // SwiGLU epilogue (y = fp32 h)
+  int row_groups;            // WGs per item along rows
+};
+
+// launches (return hipError_t of the launch)
+hipError_t launch_prep(const void* x, int x_dtype, int64_t x_stride, int n_vec, int K, int rotated,
+                       uint8_t* ra, size_t ra_stride, hipStream_t s);
+hipError_t launch_fwht(const void* x, void* y, int64_t n_vec, int len, int in_dtype, int out_dtype,
+                       hipStream_t s);
+hipError_t launch_gemv(const GemvParams& p, int slots, int tiles_per_wg, int grid, hipStream_t s);
+hipError_t launch_pack(int rows, int cols, int n_mat, const uint32_t* cs, const uint16_t* csc,
+                       uint32_t* ds, uint16_t* dsc, hipStream_t s);
+hipError_t launch_debug_unpack(int rows, int cols, const uint32_t* ds, uint32_t* cs, hipStream_t s);
+hipError_t launch_debug_outliers(int rows, int64_t nnz, gale_matrix m, int32_t* r, int32_t* c,
+                                 int32_t* v, hipStream_t s);
+
+// routing
+hipError_t launch_route_small(const float* logits, int n_tok, int n_exp, int k, int32_t* idx, float* w,
+                              int32_t* offsets, int32_t* perm, WorkItem* items, int32_t* n_items,
+                              int max_slots, hipStream_t s);
+hipError_t launch_route_large(const float* logits, int n_tok, int n_exp, int k, int32_t* idx, float* w,
+                              int32_t* chunk_cnt, int32_t* offsets, int32_t* perm, hipStream_t s);
+inline size_t route_chunk_count_bytes(int n_tok, int n_exp) {
+  return (size_t)4 * ((n_tok + 63) / 64) * n_exp;
+}
+hipError_t launch_combine(const float* ypairs, const float* w, int n_tok, int k, int hidden,
+                          void* y, int y_dtype, hipStream_t s);
+hipError_t launch_cast(const float* src, void* dst, int dst_dtype, int64_t n, hipStream_t s);
+
+// grouped prefill path
+size_t prefill_workspace_bytes(int n_tok, int n_exp, int k, int hidden, int inter);
+int run_prefill(int hidden, int inter, const gale_expert* experts, int n_exp,
+                       const float* logits, int k, const void* x, int n_tok, void* y,
+                       int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes, hipStream_t s);
+
+void set_error(const char* fmt, ...);
+
+}  // namespace gale

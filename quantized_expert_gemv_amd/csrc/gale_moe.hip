@@ -1,0 +1,264 @@
+// Routing (top-k with softmax-renormalised weights), stable grouping of the
+// (token, slot) pairs by expert, work-item lists for the per-expert GEMVs, and
+// the weighted combine.  DeepSeek-V4-Flash GALE model card, "Measured
+// performance": each token is served by 6 routed experts per layer (258 = 43 x 6).
+//
+// Order rule (needed for exact, checkable routing): experts are ranked by logit
+// descending, ties to the lower expert index; the k weights are the softmax of
+// the k selected logits; the combine sums slots 0..k-1 in that order.
+#include "gale_internal.h"
+
+namespace gale {
+
+// a ranks before b
+__device__ __forceinline__ bool better(float av, int ai, float bv, int bi) {
+  return av > bv || (av == bv && ai < bi);
+}
+
+// Top-k of one token by one wavefront: each lane holds up to 8 logits (E <= 512).
+__device__ void topk_wave(const float* __restrict__ lg, int E, int k, int lane, int32_t* out_idx,
+                          float* out_w, int32_t* lds_idx) {
+  float v[8];
+  int id[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int e = lane + 64 * j;
+    id[j] = e;
+    v[j] = e < E ? lg[e] : -INFINITY;
+  }
+  bool taken[8] = {false, false, false, false, false, false, false, false};
+  float sel_v[GALE_MAX_TOPK];
+  int sel_i[GALE_MAX_TOPK];
+  for (int s = 0; s < k; ++s) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (!taken[j] && id[j] < E && better(v[j], id[j], bv, bi)) { bv = v[j]; bi = id[j]; }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off, 64);
+      const int oi = __shfl_xor(bi, off, 64);
+      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (id[j] == bi) taken[j] = true;
+    sel_v[s] = bv;
+    sel_i[s] = bi;
+  }
+  if (lane == 0) {
+    const float m = sel_v[0];
+    float sum = 0.f, ex[GALE_MAX_TOPK];
+    for (int s = 0; s < k; ++s) { ex[s] = expf(sel_v[s] - m); sum += ex[s]; }
+    for (int s = 0; s < k; ++s) {
+      out_idx[s] = sel_i[s];
+      out_w[s] = ex[s] / sum;
+      lds_idx[s] = sel_i[s];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode routing: one workgroup does top-k for every token, the counting sort
+// and the work-item list (n_tok * k <= 512 pairs).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(512) route_small_kernel(const float* __restrict__ logits, int T, int E,
+                                                          int k, int max_slots, int32_t* __restrict__ idx,
+                                                          float* __restrict__ w, int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ perm, WorkItem* __restrict__ items,
+                                                          int32_t* __restrict__ n_items) {
+  __shared__ int32_t s_idx[GALE_MAX_DECODE_TOKENS * GALE_MAX_TOPK];
+  __shared__ int32_t s_cnt[GALE_MAX_EXPERTS];
+  __shared__ int32_t s_off[GALE_MAX_EXPERTS + 1];
+  __shared__ int32_t s_ioff[GALE_MAX_EXPERTS + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nw = blockDim.x >> 6;
+  for (int e = tid; e < E; e += blockDim.x) s_cnt[e] = 0;
+  for (int t = wave; t < T; t += nw)
+    topk_wave(logits + (int64_t)t * E, E, k, lane, idx + t * k, w + t * k, s_idx + t * k);
+  const int P = T * k;
+  __syncthreads();
+  // per-expert counts (integer atomics: order-free)
+  for (int p = tid; p < P; p += blockDim.x) atomicAdd(&s_cnt[s_idx[p]], 1);
+  __syncthreads();
+  if (tid == 0) {
+    int a = 0, b = 0;
+    for (int e = 0; e < E; ++e) {
+      s_off[e] = a;
+      s_ioff[e] = b;
+      a += s_cnt[e];
+      b += (s_cnt[e] + max_slots - 1) / max_slots;
+    }
+    s_off[E] = a;
+    s_ioff[E] = b;
+    if (n_items) *n_items = b;
+  }
+  __syncthreads();
+  if (offsets)
+    for (int e = tid; e <= E; e += blockDim.x) offsets[e] = s_off[e];
+  // stable scatter: the thread of expert e walks the pairs in order
+  for (int e = tid; e < E; e += blockDim.x) {
+    if (s_cnt[e] == 0) continue;
+    int pos = s_off[e];
+    int it = s_ioff[e], slot = 0;
+    WorkItem cur;
+    cur.expert = e;
+    cur.n_slots = 0;
+    cur.pad[0] = cur.pad[1] = 0;
+    for (int p = 0; p < P; ++p) {
+      if (s_idx[p] != e) continue;
+      if (perm) perm[pos] = p;
+      ++pos;
+      if (!items) continue;
+      cur.pair[slot++] = p;
+      cur.n_slots = slot;
+      if (slot == max_slots) {
+        for (int q = slot; q < 4; ++q) cur.pair[q] = cur.pair[0];
+        items[it++] = cur;
+        slot = 0;
+        cur.n_slots = 0;
+      }
+    }
+    if (items && slot > 0) {
+      for (int q = slot; q < 4; ++q) cur.pair[q] = cur.pair[0];
+      items[it++] = cur;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Large-batch routing: chunks of 64 tokens.
+//  (1) top-k of each token and per-chunk expert counts,
+//  (2) one workgroup scans counts into expert offsets and per-chunk bases,
+//  (3) per chunk, the thread of expert e writes its pairs in token order.
+// ---------------------------------------------------------------------------
+constexpr int kRouteChunk = 64;
+
+__global__ void __launch_bounds__(256) route_topk_count_kernel(const float* __restrict__ logits, int T, int E,
+                                                               int k, int32_t* __restrict__ idx,
+                                                               float* __restrict__ w,
+                                                               int32_t* __restrict__ chunk_cnt) {
+  __shared__ int32_t s_cnt[GALE_MAX_EXPERTS];
+  __shared__ int32_t s_idx[kRouteChunk * GALE_MAX_TOPK];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int chunk = blockIdx.x;
+  const int t0 = chunk * kRouteChunk;
+  const int t1 = min(T, t0 + kRouteChunk);
+  for (int e = tid; e < E; e += blockDim.x) s_cnt[e] = 0;
+  for (int t = t0 + wave; t < t1; t += 4)
+    topk_wave(logits + (int64_t)t * E, E, k, lane, idx + (int64_t)t * k, w + (int64_t)t * k,
+              s_idx + (t - t0) * k);
+  __syncthreads();
+  for (int p = tid; p < (t1 - t0) * k; p += blockDim.x) atomicAdd(&s_cnt[s_idx[p]], 1);
+  __syncthreads();
+  if (chunk_cnt)
+    for (int e = tid; e < E; e += blockDim.x) chunk_cnt[(int64_t)chunk * E + e] = s_cnt[e];
+}
+
+__global__ void __launch_bounds__(512) route_scan_kernel(int n_chunks, int E, int32_t* __restrict__ chunk_cnt,
+                                                         int32_t* __restrict__ offsets) {
+  __shared__ int32_t s_tot[GALE_MAX_EXPERTS];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += blockDim.x) {
+    int a = 0;
+    for (int c = 0; c < n_chunks; ++c) {
+      const int v = chunk_cnt[(int64_t)c * E + e];
+      chunk_cnt[(int64_t)c * E + e] = a;   // becomes the chunk's base within expert e
+      a += v;
+    }
+    s_tot[e] = a;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int a = 0;
+    for (int e = 0; e < E; ++e) { offsets[e] = a; a += s_tot[e]; }
+    offsets[E] = a;
+  }
+}
+
+__global__ void __launch_bounds__(256) route_scatter_kernel(int T, int E, int k,
+                                                            const int32_t* __restrict__ idx,
+                                                            const int32_t* __restrict__ chunk_base,
+                                                            const int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ perm) {
+  __shared__ int32_t s_idx[kRouteChunk * GALE_MAX_TOPK];
+  const int chunk = blockIdx.x;
+  const int t0 = chunk * kRouteChunk;
+  const int t1 = min(T, t0 + kRouteChunk);
+  const int p0 = t0 * k, np = (t1 - t0) * k;
+  for (int p = threadIdx.x; p < np; p += blockDim.x) s_idx[p] = idx[p0 + p];
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int pos = offsets[e] + chunk_base[(int64_t)chunk * E + e];
+    for (int p = 0; p < np; ++p)
+      if (s_idx[p] == e) perm[pos++] = p0 + p;
+  }
+}
+
+hipError_t launch_route_small(const float* logits, int n_tok, int n_exp, int k, int32_t* idx, float* w,
+                              int32_t* offsets, int32_t* perm, WorkItem* items, int32_t* n_items,
+                              int max_slots, hipStream_t s) {
+  hipLaunchKernelGGL(route_small_kernel, dim3(1), dim3(512), 0, s, logits, n_tok, n_exp, k, max_slots, idx, w,
+                     offsets, perm, items, n_items);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_large(const float* logits, int n_tok, int n_exp, int k, int32_t* idx, float* w,
+                              int32_t* chunk_cnt, int32_t* offsets, int32_t* perm, hipStream_t s) {
+  const int nc = (n_tok + kRouteChunk - 1) / kRouteChunk;
+  hipLaunchKernelGGL(route_topk_count_kernel, dim3(nc), dim3(256), 0, s, logits, n_tok, n_exp, k, idx, w,
+                     chunk_cnt);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !chunk_cnt) return e;
+  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(512), 0, s, nc, n_exp, chunk_cnt, offsets);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (perm) {
+    hipLaunchKernelGGL(route_scatter_kernel, dim3(nc), dim3(256), 0, s, n_tok, n_exp, k, idx, chunk_cnt,
+                       offsets, perm);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+// ---------------------------------------------------------------------------
+// combine: y[t][n] = sum_j w[t][j] * ypairs[t k + j][n], slots in order
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ yp, const float* __restrict__ w,
+                                                      int T, int k, int H, void* __restrict__ y, int y_dtype) {
+  const int64_t total = (int64_t)T * H;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int t = (int)(i / H);
+    const int n = (int)(i - (int64_t)t * H);
+    float acc = 0.f;
+    for (int j = 0; j < k; ++j) acc = fmaf(w[t * k + j], yp[((int64_t)t * k + j) * H + n], acc);
+    if (y_dtype == GALE_F16) reinterpret_cast<__half*>(y)[i] = __float2half_rn(acc);
+    else reinterpret_cast<float*>(y)[i] = acc;
+  }
+}
+
+hipError_t launch_combine(const float* ypairs, const float* w, int n_tok, int k, int hidden, void* y,
+                          int y_dtype, hipStream_t s) {
+  const int64_t total = (int64_t)n_tok * hidden;
+  if (total == 0) return hipSuccess;
+  int g = (int)std::min<int64_t>((total + 255) / 256, 16384);
+  hipLaunchKernelGGL(combine_kernel, dim3(g), dim3(256), 0, s, ypairs, w, n_tok, k, hidden, y, y_dtype);
+  return hipGetLastError();
+}
+
+__global__ void cast_kernel(const float* __restrict__ src, void* __restrict__ dst, int dtype, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    if (dtype == GALE_F16) reinterpret_cast<__half*>(dst)[i] = __float2half_rn(src[i]);
+    else reinterpret_cast<float*>(dst)[i] = src[i];
+  }
+}
+
+hipError_t launch_cast(const float* src, void* dst, int dst_dtype, int64_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  int g = (int)std::min<int64_t>((n + 255) / 256, 16384);
+  hipLaunchKernelGGL(cast_kernel, dim3(g), dim3(256), 0, s, src, dst, dst_dtype, n);
+  return hipGetLastError();
+}
+
+}  // namespace gale

@@ -1,0 +1,124 @@
+"""The C ABI on the CPU: the library loads, exports every symbol include/gale.h declares,
+the host packer round-trips, and argument validation rejects bad calls before any
+GPU work (no compute call reaches the GPU here)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import quantized_expert_gemv_amd as q
+from quantized_expert_gemv_amd import binding as B
+from synth import gen_matrix, config_seed
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    txt = open(os.path.join(ROOT, "include", "gale.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(gale_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_exports_every_declared_symbol():
+    L = q.lib()
+    names = header_functions()
+    assert len(names) >= 18
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(q.exported_symbols())
+
+
+def test_status_strings():
+    L = q.lib()
+    for code in range(0, -9, -1):
+        assert L.gale_status_str(code).decode() != "unknown status"
+
+
+def test_packed_sizes_closed_form():
+    s = q.packed_sizes(2048, 4096, 2048 * 41)
+    assert s["format_bytes"] == 1_393_664
+    s2 = q.packed_sizes(4096, 2048, 4096 * 20)
+    assert s2["format_bytes"] == 1_392_640
+    with pytest.raises(q.GaleError):
+        q.packed_sizes(2048, 4000, 0)
+
+
+@pytest.mark.parametrize("rows,cols", [(16, 1024), (48, 2048), (64, 4096)])
+def test_host_pack_roundtrip(rows, cols):
+    m = gen_matrix(config_seed(7), (rows, cols), rows, cols)
+    ds, dsc = q.pack_host(rows, cols, m.signs, m.block_scales)
+    assert not torch.equal(ds, m.signs)                 # the layout really permutes
+    cs, csc = q.unpack_host(rows, cols, ds, dsc)
+    assert torch.equal(cs, m.signs) and torch.equal(csc, m.block_scales)
+
+
+def test_host_pack_plane_structure():
+    # bit (8 i + d) of a device word is column 1024 c + 128 d + 4 q + i: a single canonical
+    # bit must land in the word of lane 16 g + n % 16 at plane position d
+    rows, cols = 16, 1024
+    for (n, k) in [(0, 0), (5, 130), (15, 1023), (3, 4 * 9 + 2 + 128 * 6)]:
+        s = torch.zeros(rows, cols // 32, dtype=torch.int32)
+        s[n, k // 32] = np.int32(np.uint32(1 << (k % 32)).view(np.int32))
+        ds, _ = q.pack_host(rows, cols, s, torch.zeros(rows, cols // 128, dtype=torch.int16))
+        nz = torch.nonzero(ds.view(-1)).flatten()
+        assert nz.numel() == 1
+        w = int(nz[0])
+        word = int(ds.view(-1)[w].item()) & 0xFFFFFFFF
+        d, rem = (k % 1024) // 128, k % 128
+        qq, i = rem // 4, rem % 4
+        g, j = qq // 8, qq % 8
+        lane = 16 * g + n % 16
+        assert w == ((0 * 2 + j // 4) * 64 + lane) * 4 + j % 4
+        assert word == 1 << (8 * i + d)
+
+
+def test_check_canonical_rejects_bad_csr():
+    rp = np.array([0, 2, 3] + [3] * 14, dtype=np.int32)
+    good = np.array([1, 5, 7], dtype=np.uint16)
+    q.check_canonical(16, 1024, rp, good)
+    for bad in (np.array([5, 1, 7], dtype=np.uint16), np.array([1, 1, 7], dtype=np.uint16),
+                np.array([1, 5, 1024], dtype=np.uint16)):
+        with pytest.raises(q.GaleError) as e:
+            q.check_canonical(16, 1024, rp, bad)
+        assert e.value.status == -7
+    with pytest.raises(q.GaleError):
+        q.check_canonical(16, 1024, np.array([0, 2, 1] + [3] * 14, dtype=np.int32), good)
+
+
+def _call(name, *args):
+    return getattr(q.lib(), name)(*args)
+
+
+def test_validation_before_any_gpu_work():
+    # invalid arguments return their specific code without enqueueing (no GPU needed)
+    F = 0x1000  # a fake non-null, 256-aligned pointer value; never dereferenced on these paths
+    assert _call("gale_expert_gemv", 2048, 4000, F, 1, F, 1, 0, 1, F, 1, F, 1 << 30, 0, None) == -2
+    assert _call("gale_expert_gemv", 2040, 4096, F, 1, F, 1, 0, 1, F, 1, F, 1 << 30, 0, None) == -2
+    assert _call("gale_expert_gemv", 2048, 4096, None, 1, F, 1, 0, 1, F, 1, F, 1 << 30, 0, None) == -1
+    assert _call("gale_expert_gemv", 2048, 4096, F, 1, F, 7, 0, 1, F, 1, F, 1 << 30, 0, None) == -3
+    assert _call("gale_expert_gemv", 2048, 4096, F, 1, F + 2, 1, 0, 1, F, 1, F, 1 << 30, 0, None) == -4
+    assert _call("gale_expert_gemv", 2048, 4096, F, 1, F, 1, 0, 1, F, 1, F, 16, 0, None) == -5
+    assert _call("gale_expert_gemv", 2048, 4096, F, 0, F, 1, 0, 1, F, 1, F, 1 << 30, 0, None) == -2
+    assert _call("gale_fwht1024", F, F, 1, 1000, 1, 1, None) == -2
+    assert _call("gale_fwht1024", F, F, 1, 1024, 1, 2, None) == -3        # in place needs equal dtypes
+    assert _call("gale_expert_ffn", 4096, 2048, F, 1, F, 0, 1, F, F, 16, None) == -5
+    assert _call("gale_moe_layer_fwd", 4096, 2048, F, 256, F, 9, F, 1, F, None, None, F, 1 << 30, 0, None) == -2
+    assert _call("gale_moe_layer_fwd", 4096, 2048, F, 600, F, 6, F, 1, F, None, None, F, 1 << 30, 0, None) == -2
+    assert _call("gale_moe_layer_fwd", 4096, 2048, F, 256, F, 6, F, 65, F, None, None, F, 1 << 30,
+                 B.GALE_PATH_DECODE, None) == -2
+    assert _call("gale_moe_layer_fwd", 4096, 2048, F, 256, F, 6, F, 1, F, None, None, F, 16, 0, None) == -5
+    assert _call("gale_route_topk", F, 4, 256, 9, F, F, None, None, None, 0, None) == -2
+    assert _call("gale_route_topk", F, 4, 256, 6, F, F, F, None, None, 0, None) == -1
+    assert _call("gale_route_topk", F, 100, 256, 6, F, F, F, F, None, 0, None) == -5
+    assert "workspace" in q.lib().gale_last_error().decode()
+
+
+def test_workspace_sizes_monotone():
+    a = q.gemv_workspace_bytes(2048, 4096, 1, 1, 0)
+    b = q.gemv_workspace_bytes(2048, 4096, 8, 1, 0)
+    c = q.gemv_workspace_bytes(2048, 4096, 8, 1, 1)
+    assert b > a and c == a and a % 256 == 0
+    assert q.moe_workspace_bytes(32, 256, 6, 4096, 2048) > q.moe_workspace_bytes(1, 256, 6, 4096, 2048)

@@ -1,0 +1,345 @@
+"""GPU parity of every libgale entry point against the fp64 oracle (MI355X only).
+
+Inputs come from the seeded generator (synth); expected values from oracle/.
+Bars: bit-exact for sign unpacking, outlier decoding and routing indices; relative
+L2 <= 2e-3 per output vector for floating point (fp32 accumulation, fp16 output).
+Closed-form cases with fp32 output use CLOSED_TOL = 1e-4: the activation enters the
+matrix cores as four e4m3 terms (exact to ~2^-16 per element) and the MFMA's own
+accumulation of a 128-long block carries ~2^-18 of the block's sum of |products|,
+which for one 1024-column chunk is ~3e-5 of the result.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from synth import CanonicalMatrix, config_seed, gen_logits_normal, gen_matrices, gen_matrix, gen_x
+
+pytestmark = pytest.mark.gpu
+
+REL_L2_BAR = 2e-3
+CLOSED_TOL = 1e-4
+
+
+@pytest.fixture(scope="module")
+def q():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import quantized_expert_gemv_amd as qq
+    qq.lib()
+    return qq
+
+
+DEV = "cuda"
+
+
+def canon_from_dict(d) -> CanonicalMatrix:
+    """oracle-style numpy dict -> CanonicalMatrix on the GPU."""
+    vals = d["out_vals"] if len(d["out_vals"]) else np.zeros(1, dtype=np.uint8)
+    return CanonicalMatrix(
+        rows=d["rows"], cols=d["cols"],
+        signs=torch.from_numpy(np.ascontiguousarray(d["signs"]).view(np.int32)).to(DEV),
+        block_scales=torch.from_numpy(np.ascontiguousarray(d["block_scales"], dtype=np.float16).view(np.int16)).to(DEV),
+        row_scales=torch.from_numpy(np.ascontiguousarray(d["row_scales"], dtype=np.float16).view(np.int16)).to(DEV),
+        row_ptr=torch.from_numpy(np.asarray(d["row_ptr"], dtype=np.int32)).to(DEV),
+        out_cols=torch.from_numpy(np.ascontiguousarray(d["out_cols"], dtype=np.uint16).view(np.int16)).to(DEV),
+        out_vals=torch.from_numpy(np.ascontiguousarray(vals, dtype=np.uint8)).to(DEV),
+    )
+
+
+def hadamard_sign_dict(N, K, scale_num=1.0):
+    i = np.arange(1024, dtype=np.uint64)
+    pc = (O.popcount(i[:, None] & i[None, :]) & 1).astype(np.uint8)
+    bits = np.zeros((N, K), dtype=np.uint8)
+    scales = np.zeros((N, K // 128), dtype=np.float64)
+    for blk in range(min(N, K) // 1024):
+        bits[blk * 1024:(blk + 1) * 1024, blk * 1024:(blk + 1) * 1024] = pc
+        scales[blk * 1024:(blk + 1) * 1024, blk * 8:(blk + 1) * 8] = scale_num / 32.0
+    return {"rows": N, "cols": K, "signs": np.packbits(bits, axis=1, bitorder="little").view(np.uint32),
+            "block_scales": scales.astype(np.float16), "row_scales": np.zeros(N, dtype=np.float16),
+            "row_ptr": np.zeros(N + 1, dtype=np.int64), "out_cols": np.zeros(0, dtype=np.uint16),
+            "out_vals": np.zeros(0, dtype=np.uint8)}
+
+
+def np_of(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+# ----------------------------------------------------------------------------
+# layout and decode: bit-exact
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("rows,cols", [(2048, 4096), (4096, 2048), (48, 1024), (16, 7168)])
+def test_sign_and_outlier_decode_bit_exact(q, rows, cols):
+    m = gen_matrix(config_seed(1), (rows, cols), rows, cols, device=DEV)
+    pm = q.pack_matrix(m)
+    back = q.debug_unpack_signs(pm)
+    assert torch.equal(back, m.signs)
+    # device packer == host packer
+    hs, hsc = q.pack_host(rows, cols, m.signs.cpu(), m.block_scales.cpu())
+    assert torch.equal(pm.signs.view(-1).cpu(), hs.view(-1)) and torch.equal(pm.block_scales.view(-1).cpu(), hsc.view(-1))
+    r, c, v = q.debug_unpack_outliers(pm)
+    orr, occ, ovv = O.outlier_triplets(m.numpy())
+    assert np.array_equal(r.cpu().numpy(), orr) and np.array_equal(c.cpu().numpy(), occ)
+    assert np.array_equal(v.cpu().numpy(), ovv)
+
+
+# ----------------------------------------------------------------------------
+# FWHT
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", [torch.float16, torch.float32])
+def test_fwht_parity(q, dtype):
+    x = gen_x(config_seed(2), (0,), 5, 4096, device=DEV).to(dtype)
+    y = q.fwht1024(x, out_dtype=torch.float32)
+    ref = O.rotate(np_of(x))
+    err = np.abs(np_of(y) - ref).max() / np.abs(ref).max()
+    assert err <= 1e-6, err
+    # involution: H(H x) = x
+    z = q.fwht1024(y)
+    assert np.abs(np_of(z) - np_of(x)).max() <= 1e-5 * np.abs(np_of(x)).max()
+    # fp16 output rounds to nearest
+    y16 = q.fwht1024(x, out_dtype=torch.float16)
+    assert np.abs(np_of(y16) - ref).max() <= np.abs(ref).max() * 2 ** -11
+
+
+# ----------------------------------------------------------------------------
+# GEMV
+# ----------------------------------------------------------------------------
+def test_gemv_single_matrix_config(q):
+    """One [2048 out, 4096 in] matrix, one token (the single-matrix workload)."""
+    m = gen_matrix(config_seed(1), (0,), 2048, 4096, device=DEV)
+    x = gen_x(config_seed(1), (0,), 1, 4096, device=DEV)
+    tab = q.matrix_table([q.pack_matrix(m)])
+    ref = O.gemv(m.numpy(), x.cpu().numpy())
+    y16 = q.expert_gemv(tab, 2048, 4096, x[None])
+    y32 = q.expert_gemv(tab, 2048, 4096, x[None], y_dtype=torch.float32)
+    e16 = O.rel_l2(np_of(y16[0]), ref).max()
+    e32 = O.rel_l2(np_of(y32[0]), ref).max()
+    print(f"gemv rel-L2 fp16 out {e16:.3e}  fp32 out {e32:.3e}")
+    assert e16 <= REL_L2_BAR
+    assert e32 <= 1e-4
+
+
+@pytest.mark.parametrize("n_tok", [1, 2, 3, 4, 5, 7])
+def test_gemv_tokens_and_ragged_tiles(q, n_tok):
+    rows, cols, n_mat = 80, 2048, 3                      # 5 row tiles: ragged against 2 and 4 tiles per WG
+    mats = gen_matrices(config_seed(3), [(i,) for i in range(n_mat)], rows, cols, device=DEV)
+    x = torch.stack([gen_x(config_seed(3), (i, 1), n_tok, cols, device=DEV) for i in range(n_mat)])
+    tab = q.matrix_table([q.pack_matrix(m) for m in mats])
+    outs = {}
+    for r in (1, 2, 4, 8):
+        outs[r] = q.expert_gemv(tab, rows, cols, x, y_dtype=torch.float32, flags=q.gale_tiles_flag(r))
+    for i in range(n_mat):
+        ref = O.gemv(mats[i].numpy(), x[i].cpu().numpy())
+        assert O.rel_l2(np_of(outs[1][i]), ref).max() <= 1e-4
+    for r in (2, 4, 8):
+        assert torch.equal(outs[r], outs[1])             # workgroup shape does not change the arithmetic
+
+
+def test_gemv_shared_x_rotated_input_and_long_k(q):
+    rows, cols = 64, 7168                                # 7 FWHT blocks (non power of two)
+    mats = gen_matrices(config_seed(4), [(0,), (1,)], rows, cols, device=DEV)
+    x = gen_x(config_seed(4), (5,), 2, cols, device=DEV)
+    tab = q.matrix_table([q.pack_matrix(m) for m in mats])
+    y = q.expert_gemv(tab, rows, cols, x, x_shared=True, y_dtype=torch.float32)
+    xt = torch.from_numpy(O.rotate(np_of(x))).float().to(DEV)
+    yr = q.expert_gemv(tab, rows, cols, xt, x_shared=True, y_dtype=torch.float32, flags=q.GALE_X_ROTATED)
+    for i in range(2):
+        ref = O.gemv(mats[i].numpy(), x.cpu().numpy())
+        assert O.rel_l2(np_of(y[i]), ref).max() <= 1e-4
+        assert O.rel_l2(np_of(yr[i]), ref).max() <= 1e-4
+
+
+def test_gemv_hadamard_sign_identity(q):
+    # rows carrying H's sign pattern with scale 1/32 return x itself
+    d = hadamard_sign_dict(2048, 4096)
+    tab = q.matrix_table([q.pack_matrix(canon_from_dict(d))])
+    x = gen_x(config_seed(5), (0,), 3, 4096, device=DEV)
+    y = q.expert_gemv(tab, 2048, 4096, x[None], y_dtype=torch.float32)
+    assert O.rel_l2(np_of(y[0]), np_of(x[:, :2048])).max() <= CLOSED_TOL
+
+
+def test_gemv_zero_bits_closed_form_and_subnormal_scales(q):
+    N, K = 32, 4096
+    m = gen_matrix(config_seed(6), (0,), N, K, device=DEV)
+    d = m.numpy()
+    d["signs"] = np.zeros_like(d["signs"])
+    d["block_scales"] = np.full_like(d["block_scales"], np.float16(0.015625))
+    d["row_scales"] = np.zeros_like(d["row_scales"])
+    x = gen_x(config_seed(6), (1,), 1, K, device=DEV)
+    y = q.expert_gemv(q.matrix_table([q.pack_matrix(canon_from_dict(d))]), N, K, x[None], y_dtype=torch.float32)
+    xs = np_of(x[0])
+    expect = 32.0 * 0.015625 * xs[0::1024].sum()
+    assert np.abs(np_of(y[0]) - expect).max() <= CLOSED_TOL * abs(expect) + 1e-6
+    # subnormal fp16 block scales are honoured, not flushed
+    d2 = m.numpy()
+    sub = np.array([2 ** -24, 3 * 2 ** -24, 2 ** -15, 1023 * 2 ** -24], dtype=np.float16)
+    bs = d2["block_scales"].copy()
+    bs[:, ::2] = sub[np.arange(bs[:, ::2].size).reshape(bs[:, ::2].shape) % 4]
+    d2["block_scales"] = bs
+    d2["row_scales"] = np.zeros_like(d2["row_scales"])
+    y2 = q.expert_gemv(q.matrix_table([q.pack_matrix(canon_from_dict(d2))]), N, K, x[None], y_dtype=torch.float32)
+    ref2 = O.gemv(d2, x.cpu().numpy())
+    assert O.rel_l2(np_of(y2[0]), ref2).max() <= 1e-4
+
+
+def test_gemv_outlier_edges(q):
+    # scales 0: y is the outlier sparse dot alone; rows with 0, 1 and 300 outliers, columns 0 and K-1
+    N, K = 32, 2048
+    rng = np.random.default_rng(11)
+    rp = [0]
+    cols, vals = [], []
+    for n in range(N):
+        cnt = [0, 1, 300, 41][n % 4]
+        cs = np.sort(rng.choice(K, size=cnt, replace=False)) if cnt else np.zeros(0, dtype=np.int64)
+        if n == 5:
+            cs = np.array([0, K - 1])
+        cols.extend(cs.tolist())
+        vals.extend(rng.integers(-8, 8, size=len(cs)).tolist())
+        rp.append(len(cols))
+    nib = [v & 0xF for v in vals] + ([0] if len(vals) % 2 else [])
+    d = {"rows": N, "cols": K, "signs": rng.integers(0, 2 ** 32, size=(N, K // 32), dtype=np.uint64).astype(np.uint32),
+         "block_scales": np.zeros((N, K // 128), dtype=np.float16),
+         "row_scales": np.full(N, 0.05, dtype=np.float16), "row_ptr": np.array(rp),
+         "out_cols": np.array(cols, dtype=np.uint16),
+         "out_vals": np.array([nib[i] | (nib[i + 1] << 4) for i in range(0, len(nib), 2)], dtype=np.uint8)}
+    x = gen_x(config_seed(7), (0,), 2, K, device=DEV)
+    tab = q.matrix_table([q.pack_matrix(canon_from_dict(d))])
+    y = q.expert_gemv(tab, N, K, x[None], y_dtype=torch.float32)
+    ref = O.gemv(d, x.cpu().numpy())
+    err = np.abs(np_of(y[0]) - ref).max()
+    assert err <= 1e-5 * np.abs(ref).max()
+    assert np.all(np_of(y[0])[:, 0::4] == 0.0)           # rows without outliers give exactly 0
+
+
+def test_gemv_many_matrices_sampled(q):
+    """The launch shape of the sustained benchmark: many distinct matrices, one token each;
+    every output checked against the oracle on a sample of matrices."""
+    n_mat = 64
+    mats = gen_matrices(config_seed(1), [(100 + i,) for i in range(n_mat)], 2048, 4096, device=DEV)
+    x = torch.stack([gen_x(config_seed(1), (100 + i,), 1, 4096, device=DEV) for i in range(n_mat)])
+    tab = q.matrix_table([q.pack_matrix(m) for m in mats])
+    y = q.expert_gemv(tab, 2048, 4096, x)
+    y2 = q.expert_gemv(tab, 2048, 4096, x)
+    assert torch.equal(y, y2)                            # deterministic
+    for i in (0, 17, 63):
+        ref = O.gemv(mats[i].numpy(), x[i].cpu().numpy())
+        assert O.rel_l2(np_of(y[i]), ref).max() <= REL_L2_BAR
+
+
+# ----------------------------------------------------------------------------
+# FFN
+# ----------------------------------------------------------------------------
+def _expert(q, seed, e, hidden=4096, inter=2048):
+    w1, w3 = gen_matrices(seed, [(e, 0), (e, 1)], inter, hidden, device=DEV)
+    w2 = gen_matrix(seed, (e, 2), hidden, inter, device=DEV)
+    return (w1, w3, w2), (q.pack_matrix(w1), q.pack_matrix(w3), q.pack_matrix(w2))
+
+
+def test_ffn_one_expert_config(q):
+    (w1, w3, w2), packed = _expert(q, config_seed(2), 0)
+    x = gen_x(config_seed(2), (0,), 1, 4096, device=DEV)
+    y = q.expert_ffn(q.expert_table([packed]), 4096, 2048, x[None])
+    ref = O.ffn(w1.numpy(), w3.numpy(), w2.numpy(), x.cpu().numpy())
+    e = O.rel_l2(np_of(y[0]), ref).max()
+    print(f"ffn rel-L2 {e:.3e}")
+    assert e <= REL_L2_BAR
+
+
+def test_ffn_tokens_and_experts(q):
+    seed = config_seed(12)
+    ex = [_expert(q, seed, e) for e in range(2)]
+    x = gen_x(seed, (3,), 5, 4096, device=DEV)
+    y = q.expert_ffn(q.expert_table([p for _, p in ex]), 4096, 2048, x, x_shared=True)
+    for e in range(2):
+        (w1, w3, w2), _ = ex[e]
+        ref = O.ffn(w1.numpy(), w3.numpy(), w2.numpy(), x.cpu().numpy())
+        assert O.rel_l2(np_of(y[e]), ref).max() <= REL_L2_BAR
+
+
+def test_ffn_closed_form(q):
+    w1 = canon_from_dict(hadamard_sign_dict(2048, 4096))
+    w2 = canon_from_dict(hadamard_sign_dict(4096, 2048))
+    p1, p2 = q.pack_matrix(w1), q.pack_matrix(w2)
+    x = gen_x(config_seed(8), (0,), 2, 4096, device=DEV) * 0.25
+    y = q.expert_ffn(q.expert_table([(p1, p1, p2)]), 4096, 2048, x[None])
+    xs = np_of(x)[:, :2048]
+    ref = np.zeros((2, 4096))
+    ref[:, :2048] = xs * xs / (1 + np.exp(-xs))
+    assert O.rel_l2(np_of(y[0]), ref).max() <= 1e-3     # fp16 output rounding dominates
+
+
+# ----------------------------------------------------------------------------
+# routing and MoE layer (decode path)
+# ----------------------------------------------------------------------------
+def test_route_exact_with_ties(q):
+    lg = gen_logits_normal(config_seed(3), (9,), 40, 256)
+    lg[3, :] = 0.0
+    lg[4, [10, 20, 30, 40, 50, 60, 70]] = 9.0
+    lg[5, :] = -5.0
+    lg[5, 17] = -0.0
+    lg[5, 16] = 0.0
+    idx, w, off, perm = q.route_topk(lg.to(DEV), 6, group=True)
+    ridx, rw = O.route(lg.numpy(), 6)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert np.abs(w.cpu().numpy() - rw).max() <= 1e-6
+    roff, rperm = O.group_by_expert(ridx, 256)
+    assert np.array_equal(off.cpu().numpy(), roff) and np.array_equal(perm.cpu().numpy(), rperm)
+    # large-batch grouping (chunked kernels)
+    lg2 = gen_logits_normal(config_seed(3), (10,), 300, 256)
+    idx2, w2, off2, perm2 = q.route_topk(lg2.to(DEV), 6, group=True)
+    ridx2, _ = O.route(lg2.numpy(), 6)
+    roff2, rperm2 = O.group_by_expert(ridx2, 256)
+    assert np.array_equal(idx2.cpu().numpy(), ridx2)
+    assert np.array_equal(off2.cpu().numpy(), roff2) and np.array_equal(perm2.cpu().numpy(), rperm2)
+
+
+@pytest.fixture(scope="module")
+def layer(q):
+    seed = config_seed(3)
+    E = 256
+    w13 = gen_matrices(seed, [(e, m) for e in range(E) for m in (0, 1)], 2048, 4096, device=DEV)
+    w2 = gen_matrices(seed, [(e, 2) for e in range(E)], 4096, 2048, device=DEV)
+    canon = [(w13[2 * e], w13[2 * e + 1], w2[e]) for e in range(E)]
+    packed = [(q.pack_matrix(a), q.pack_matrix(b), q.pack_matrix(c)) for a, b, c in canon]
+    return seed, canon, q.expert_table(packed)
+
+
+@pytest.mark.parametrize("T", [1, 4, 16, 32])
+def test_moe_decode_layer(q, layer, T):
+    seed, canon, tab = layer
+    x = gen_x(seed, (1000, T), T, 4096, device=DEV)
+    lg = gen_logits_normal(seed, (1000, T), T, 256, device=DEV)
+    y, idx, w = q.moe_layer_fwd(tab, 4096, 2048, lg, x, top_k=6)
+    y_again, _, _ = q.moe_layer_fwd(tab, 4096, 2048, lg, x, top_k=6)
+    assert torch.equal(y, y_again)
+    ridx, rw = O.route(lg.cpu().numpy(), 6)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert np.abs(w.cpu().numpy() - rw).max() <= 1e-6
+    sample = list(range(T)) if T <= 4 else [0, T // 2, T - 1]
+    expert_of = lambda e: tuple(m.numpy() for m in canon[e])  # noqa: E731
+    yref, _, _ = O.moe(expert_of, lg.cpu().numpy()[sample], x.cpu().numpy()[sample], k=6)
+    err = O.rel_l2(np_of(y[sample]), yref).max()
+    print(f"moe T={T} rel-L2 {err:.3e}")
+    assert err <= REL_L2_BAR
+
+
+def test_moe_closed_form(q):
+    E = 16
+    w1 = q.pack_matrix(canon_from_dict(hadamard_sign_dict(2048, 4096)))
+    base2 = hadamard_sign_dict(4096, 2048)
+    experts = []
+    for e in range(E):
+        d = dict(base2)
+        d["block_scales"] = (base2["block_scales"].astype(np.float64) * (1.0 + e / 256.0)).astype(np.float16)
+        experts.append((w1, w1, q.pack_matrix(canon_from_dict(d))))
+    tab = q.expert_table(experts)
+    x = gen_x(config_seed(9), (0,), 3, 4096, device=DEV) * 0.25
+    lg = gen_logits_normal(config_seed(9), (0,), 3, E, device=DEV)
+    y, idx, w = q.moe_layer_fwd(tab, 4096, 2048, lg, x, top_k=6)
+    xs = np_of(x)[:, :2048]
+    coef = (w.cpu().numpy().astype(np.float64) * (1.0 + idx.cpu().numpy() / 256.0)).sum(axis=1)
+    ref = np.zeros((3, 4096))
+    ref[:, :2048] = coef[:, None] * xs * xs / (1 + np.exp(-xs))
+    assert O.rel_l2(np_of(y), ref).max() <= 1e-3
