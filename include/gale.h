@@ -59,6 +59,7 @@ extern "C" {
 #define GALE_F32 2
 
 #define GALE_X_ROTATED    0x1u   /* x is already H.x (fp32 or fp16); skip the rotation */
+#define GALE_X_PREPARED   0x2u   /* gale_expert_gemv: x holds records from gale_prepare_activations */
 #define GALE_PATH_DECODE  0x10u  /* gale_moe_layer_fwd: force the per-expert GEMV path */
 #define GALE_PATH_GROUPED 0x20u  /* gale_moe_layer_fwd: force the grouped MFMA path */
 
@@ -84,6 +85,9 @@ extern "C" {
  *  row_ptr       int32 [rows + 1]            (canonical CSR offsets)
  *  out_cols      uint16 [nnz]                (canonical, ascending within a row)
  *  out_vals      uint8 [ceil(nnz/2)]         (canonical int4, low nibble first)
+ *  out_cols and out_vals start 16-byte aligned and stay readable up to the next
+ *  16-byte boundary past their end (at least 16 bytes, even when nnz == 0): the
+ *  kernels fetch them in whole 16-byte chunks.
  */
 typedef struct gale_matrix {
     const uint32_t* signs;
@@ -159,6 +163,17 @@ int gale_debug_unpack_outliers(int32_t rows, int64_t nnz, const gale_matrix* m_h
 int gale_fwht1024(const void* x, void* y, int64_t n_vec, int32_t len, int32_t in_dtype,
                   int32_t out_dtype, hipStream_t stream);
 
+/* Bytes of one prepared activation record of length len (a multiple of 256). */
+size_t gale_prepared_bytes(int32_t len);
+
+/* Prepare activation vectors for the GEMV: x~ = blockdiag(H) x (skipped with GALE_X_ROTATED),
+ * stored as fp32 plus the matrix-core operand form (four fp8 e4m3 terms per element with a
+ * power-of-two scale per 1024-block).  x: [n_vec][len] (x_dtype); out: n_vec records of
+ * gale_prepared_bytes(len) bytes, 256-byte aligned.  A record can feed any number of GEMVs
+ * (the routed layer shares one per token across its experts' gate and up matrices). */
+int gale_prepare_activations(const void* x, int32_t x_dtype, int64_t n_vec, int32_t len, uint32_t flags,
+                             void* out, size_t out_bytes, hipStream_t stream);
+
 /* Workspace bytes for gale_expert_gemv. */
 size_t gale_gemv_workspace_bytes(int32_t rows, int32_t cols, int32_t n_mat, int32_t n_tok,
                                  int32_t x_shared);
@@ -170,7 +185,8 @@ size_t gale_gemv_workspace_bytes(int32_t rows, int32_t cols, int32_t n_mat, int3
  * x: [n_mat][n_tok][cols] (or [n_tok][cols] shared by all matrices when x_shared != 0),
  *    dtype x_dtype (GALE_F16 / GALE_F32); flags GALE_X_ROTATED means x is already H.x.
  * y: [n_mat][n_tok][rows], dtype y_dtype.  ws: gale_gemv_workspace_bytes(...) bytes,
- * 256-byte aligned.  fp32 accumulation. */
+ * 256-byte aligned.  With GALE_X_PREPARED, x holds the prepared records (same indexing,
+ * x_dtype ignored) and ws may be NULL.  fp32 accumulation. */
 int gale_expert_gemv(int32_t rows, int32_t cols, const gale_matrix* mats_dev, int32_t n_mat,
                      const void* x, int32_t x_dtype, int32_t x_shared, int32_t n_tok,
                      void* y, int32_t y_dtype, void* ws, size_t ws_bytes, uint32_t flags,

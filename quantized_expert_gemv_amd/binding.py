@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libgale.so")
 GALE_OK = 0
 GALE_F16, GALE_F32 = 1, 2
 GALE_X_ROTATED = 0x1
+GALE_X_PREPARED = 0x2
 GALE_PATH_DECODE = 0x10
 GALE_PATH_GROUPED = 0x20
 STATUS = {0: "GALE_OK", -1: "GALE_ERR_NULL", -2: "GALE_ERR_SHAPE", -3: "GALE_ERR_DTYPE", -4: "GALE_ERR_ALIGN",
@@ -65,6 +66,8 @@ _SIGS = {
     "gale_debug_unpack_signs": (_I32, [_I32, _I32, _P, _P, _P]),
     "gale_debug_unpack_outliers": (_I32, [_I32, _I64, ctypes.POINTER(gale_matrix), _P, _P, _P, _P]),
     "gale_fwht1024": (_I32, [_P, _P, _I64, _I32, _I32, _I32, _P]),
+    "gale_prepared_bytes": (_SZ, [_I32]),
+    "gale_prepare_activations": (_I32, [_P, _I32, _I64, _I32, _U32, _P, _SZ, _P]),
     "gale_gemv_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
     "gale_expert_gemv": (_I32, [_I32, _I32, _P, _I32, _P, _I32, _I32, _I32, _P, _I32, _P, _SZ, _U32, _P]),
     "gale_ffn_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
@@ -172,7 +175,10 @@ def unpack_host(rows: int, cols: int, dev_signs: torch.Tensor, dev_scales: torch
 
 @dataclass
 class PackedMatrix:
-    """One matrix in the device layout (all tensors on one GPU)."""
+    """One matrix in the device layout (all tensors on one GPU).
+
+    out_cols / out_vals are the section buffers, which may extend past the nnz
+    entries (whole 16-byte chunks, at least one): the kernels read them in chunks."""
     rows: int
     cols: int
     signs: torch.Tensor
@@ -181,15 +187,20 @@ class PackedMatrix:
     row_ptr: torch.Tensor
     out_cols: torch.Tensor
     out_vals: torch.Tensor
+    nnz: int = -1
 
-    @property
-    def nnz(self) -> int:
-        return int(self.out_cols.numel())
+    def __post_init__(self):
+        if self.nnz < 0:
+            self.nnz = int(self.out_cols.numel())
 
     def descriptor(self) -> gale_matrix:
         d = gale_matrix()
         d.signs, d.block_scales, d.row_scales = _ptr(self.signs), _ptr(self.block_scales), _ptr(self.row_scales)
         d.row_ptr, d.out_cols, d.out_vals = _ptr(self.row_ptr), _ptr(self.out_cols), _ptr(self.out_vals)
+        for name, _ in gale_matrix._fields_:
+            if not getattr(d, name):
+                raise ValueError(f"PackedMatrix section {name} has no storage (NULL pointer); every section, "
+                                 "outliers included, needs a readable buffer")
         return d
 
 
@@ -206,11 +217,23 @@ def pack_device(rows: int, cols: int, n_mat: int, canon_signs: torch.Tensor, can
     return out_signs, out_scales
 
 
+def _padded16(t: torch.Tensor) -> torch.Tensor:
+    """Copy a 1-D section into a fresh buffer padded to whole 16-byte chunks (at least one)."""
+    nbytes = t.numel() * t.element_size()
+    n = max(16, (nbytes + 15) // 16 * 16)
+    out = torch.zeros(n, dtype=torch.uint8, device=t.device)
+    if nbytes:
+        out[:nbytes] = t.reshape(-1).contiguous().view(torch.uint8)
+    return out
+
+
 def pack_matrix(cm) -> PackedMatrix:
-    """synth.CanonicalMatrix (on a GPU) -> PackedMatrix; outliers and row scales are kept as is."""
+    """synth.CanonicalMatrix (on a GPU) -> PackedMatrix.  Signs and block scales are re-laid out;
+    outliers and row scales keep the canonical format (outlier sections padded to 16 bytes)."""
     ds, dsc = pack_device(cm.rows, cm.cols, 1, cm.signs, cm.block_scales)
-    return PackedMatrix(cm.rows, cm.cols, ds, dsc, cm.row_scales, cm.row_ptr.contiguous(), cm.out_cols.contiguous(),
-                        cm.out_vals if cm.out_vals.numel() else torch.zeros(1, dtype=torch.uint8, device=ds.device))
+    # the padded buffers themselves (an empty slice would have a NULL data pointer)
+    return PackedMatrix(cm.rows, cm.cols, ds, dsc, cm.row_scales, cm.row_ptr.contiguous(),
+                        _padded16(cm.out_cols).view(torch.int16), _padded16(cm.out_vals), nnz=cm.nnz)
 
 
 class DescriptorTable:
@@ -282,6 +305,24 @@ def fwht1024(x: torch.Tensor, out_dtype: Optional[torch.dtype] = None, out: Opti
     return out
 
 
+def prepared_bytes(length: int) -> int:
+    return int(lib().gale_prepared_bytes(length))
+
+
+def prepare_activations(x: torch.Tensor, rotated: bool = False, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """x [..., len] -> uint8 [n_vec, prepared_bytes(len)] records for GALE_X_PREPARED GEMVs."""
+    _require_cuda(x)
+    x = x.contiguous()
+    L = x.shape[-1]
+    nv = x.numel() // L
+    rb = prepared_bytes(L)
+    if out is None:
+        out = torch.empty(nv, rb, dtype=torch.uint8, device=x.device)
+    _check("gale_prepare_activations", lib().gale_prepare_activations(
+        x.data_ptr(), _dt(x), nv, L, GALE_X_ROTATED if rotated else 0, out.data_ptr(), out.numel(), _stream()))
+    return out
+
+
 def gemv_workspace_bytes(rows, cols, n_mat, n_tok, x_shared) -> int:
     return int(lib().gale_gemv_workspace_bytes(rows, cols, n_mat, n_tok, int(bool(x_shared))))
 
@@ -292,14 +333,20 @@ def expert_gemv(table: DescriptorTable, rows: int, cols: int, x: torch.Tensor, n
     """y[m, t] = Wq_m . H x[m, t]; x [n_mat, n_tok, cols] (or [n_tok, cols] with x_shared)."""
     _require_cuda(x)
     n_mat = n_mat or table.count
-    n_tok = x.shape[-2]
+    prepared = bool(flags & GALE_X_PREPARED)
+    if prepared:
+        # x: uint8 records [n_x, prepared_bytes(cols)], n_x = (1 if x_shared else n_mat) * n_tok
+        n_tok = x.shape[0] // (1 if x_shared else n_mat)
+    else:
+        n_tok = x.shape[-2]
     if y is None:
         y = torch.empty(n_mat, n_tok, rows, dtype=y_dtype, device=x.device)
-    if ws is None:
+    if ws is None and not prepared:
         ws = _workspace(gemv_workspace_bytes(rows, cols, n_mat, n_tok, x_shared), x.device)
-    _check("gale_expert_gemv", lib().gale_expert_gemv(rows, cols, table.ptr(), n_mat, x.data_ptr(), _dt(x),
-                                                       int(bool(x_shared)), n_tok, y.data_ptr(), _dt(y),
-                                                       ws.data_ptr(), ws.numel(), flags, _stream()))
+    _check("gale_expert_gemv", lib().gale_expert_gemv(rows, cols, table.ptr(), n_mat, x.data_ptr(),
+                                                       GALE_F16 if prepared else _dt(x), int(bool(x_shared)), n_tok,
+                                                       y.data_ptr(), _dt(y), _ptr(ws), 0 if ws is None else ws.numel(),
+                                                       flags, _stream()))
     return y
 
 

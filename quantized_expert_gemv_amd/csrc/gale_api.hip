@@ -46,16 +46,25 @@ static int hip_status(const char* fn, hipError_t e) {
   return GALE_OK;
 }
 
-// rows-per-workgroup choice: enough workgroups to fill 256 CUs several times over,
-// otherwise the smallest tile count.
-static int pick_tiles(int64_t items, int ntiles, uint32_t flags) {
-  const int forced = (int)((flags >> 8) & 0xF);
-  if (forced) return 1 << (forced - 1);
-  const int64_t want = 2048;
+// Row tiles per unit: at most the chunk count (four lanes per row serve the outliers),
+// at most 2 with four activation vectors (register budget), and small enough that the
+// units cover the GPU at least twice; flags bits 8..11 force a value (1, 2 or 4).
+static int pick_tiles(int64_t items, int ntiles, int cols, int slots, uint32_t flags) {
+  const int C = cols / 1024;
   int r = 4;
-  while (r > 1 && items * ((ntiles + r - 1) / r) < want) r >>= 1;
+  const int forced = (int)((flags >> 8) & 0xF);
+  if (forced) r = 1 << (forced - 1);
+  if (r > 4) r = 4;
+  if (slots >= 2 && r > 2) r = 2;
+  while (r > C) r >>= 1;
+  if (!forced) {
+    const int64_t want = 2 * (int64_t)device_cu_count();
+    while (r > 1 && items * ((ntiles + r - 1) / r) < want) r >>= 1;
+  }
   return r;
 }
+
+static int stage_ok(int cols, int slots) { return (int64_t)slots * cols * 4 <= 65536 ? 1 : 0; }
 
 static int pick_slots(int n_tok) { return n_tok >= 4 ? 4 : (n_tok >= 2 ? 2 : 1); }
 
@@ -222,6 +231,26 @@ extern "C" int gale_fwht1024(const void* x, void* y, int64_t n_vec, int32_t len,
 // ============================================================================
 // GEMV
 // ============================================================================
+extern "C" size_t gale_prepared_bytes(int32_t len) {
+  if (len < 1024 || len % 1024) return 0;
+  return ra_bytes(len);
+}
+
+extern "C" int gale_prepare_activations(const void* x, int32_t x_dtype, int64_t n_vec, int32_t len, uint32_t flags,
+                                        void* out, size_t out_bytes, hipStream_t stream) {
+  const char* fn = "gale_prepare_activations";
+  if (!x || !out) { set_error("%s: NULL pointer", fn); return GALE_ERR_NULL; }
+  if (!dtype_ok(x_dtype)) { set_error("%s: bad dtype", fn); return GALE_ERR_DTYPE; }
+  if (len < 1024 || len % 1024 || len > GALE_MAX_COLS || n_vec < 0 || n_vec > (1 << 30)) {
+    set_error("%s: len=%d n_vec=%lld", fn, len, (long long)n_vec);
+    return GALE_ERR_SHAPE;
+  }
+  if (!aligned(x, 16) || !aligned(out, 256)) { set_error("%s: x needs 16-byte, out 256-byte alignment", fn); return GALE_ERR_ALIGN; }
+  if (out_bytes < ra_bytes(len) * (size_t)n_vec) { set_error("%s: out %zu < %zu bytes", fn, out_bytes, ra_bytes(len) * (size_t)n_vec); return GALE_ERR_WORKSPACE; }
+  return hip_status(fn, launch_prep(x, x_dtype, len, (int)n_vec, len, (flags & GALE_X_ROTATED) ? 1 : 0,
+                                    reinterpret_cast<uint8_t*>(out), ra_bytes(len), stream));
+}
+
 extern "C" size_t gale_gemv_workspace_bytes(int32_t rows, int32_t cols, int32_t n_mat, int32_t n_tok,
                                             int32_t x_shared) {
   (void)rows;
@@ -237,19 +266,27 @@ extern "C" int gale_expert_gemv(int32_t rows, int32_t cols, const gale_matrix* m
   int st = check_matrix_shape(fn, rows, cols);
   if (st) return st;
   if (n_mat < 1 || n_tok < 1) { set_error("%s: n_mat=%d n_tok=%d must be >= 1", fn, n_mat, n_tok); return GALE_ERR_SHAPE; }
-  if (!mats_dev || !x || !y || !ws) { set_error("%s: NULL pointer", fn); return GALE_ERR_NULL; }
-  if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype)) { set_error("%s: bad dtype", fn); return GALE_ERR_DTYPE; }
-  if (!aligned(x, 16) || !aligned(ws, 256) || !aligned(y, dsize(y_dtype)) || !aligned(mats_dev, 8)) {
-    set_error("%s: x needs 16-byte, ws 256-byte alignment", fn);
+  const bool prepared = (flags & GALE_X_PREPARED) != 0;
+  if (!mats_dev || !x || !y || (!prepared && !ws)) { set_error("%s: NULL pointer", fn); return GALE_ERR_NULL; }
+  if ((!prepared && !dtype_ok(x_dtype)) || !dtype_ok(y_dtype)) { set_error("%s: bad dtype", fn); return GALE_ERR_DTYPE; }
+  if (!aligned(x, prepared ? 256 : 16) || (!prepared && !aligned(ws, 256)) || !aligned(y, dsize(y_dtype)) ||
+      !aligned(mats_dev, 8)) {
+    set_error("%s: x needs 16-byte (prepared: 256-byte), ws 256-byte alignment", fn);
     return GALE_ERR_ALIGN;
   }
   const int64_t n_x = (int64_t)(x_shared ? 1 : n_mat) * n_tok;
-  const GemvWs W = gemv_ws(cols, n_x);
-  if (ws_bytes < W.total) { set_error("%s: workspace %zu < %zu bytes", fn, ws_bytes, W.total); return GALE_ERR_WORKSPACE; }
-  uint8_t* ra = reinterpret_cast<uint8_t*>(ws) + W.ra;
-  st = hip_status(fn, launch_prep(x, x_dtype, cols, (int)n_x, cols, (flags & GALE_X_ROTATED) ? 1 : 0, ra,
-                                  ra_bytes(cols), stream));
-  if (st) return st;
+  const uint8_t* ra;
+  if (prepared) {
+    ra = reinterpret_cast<const uint8_t*>(x);
+  } else {
+    const GemvWs W = gemv_ws(cols, n_x);
+    if (ws_bytes < W.total) { set_error("%s: workspace %zu < %zu bytes", fn, ws_bytes, W.total); return GALE_ERR_WORKSPACE; }
+    uint8_t* raw = reinterpret_cast<uint8_t*>(ws) + W.ra;
+    st = hip_status(fn, launch_prep(x, x_dtype, cols, (int)n_x, cols, (flags & GALE_X_ROTATED) ? 1 : 0, raw,
+                                    ra_bytes(cols), stream));
+    if (st) return st;
+    ra = raw;
+  }
   const int slots = pick_slots(n_tok);
   GemvParams P;
   memset(&P, 0, sizeof(P));
@@ -271,11 +308,10 @@ extern "C" int gale_expert_gemv(int32_t rows, int32_t cols, const gale_matrix* m
   P.y_stride = rows;
   P.gateup = 0;
   const int ntiles = rows / 16;
-  const int R = pick_tiles(P.n_items, ntiles, flags);
+  const int R = pick_tiles(P.n_items, ntiles, cols, slots, flags);
   P.row_groups = (ntiles + R - 1) / R;
-  const int64_t work = (int64_t)P.n_items * P.row_groups;
-  const int grid = (int)std::min<int64_t>(work, 1 << 20);
-  return hip_status(fn, launch_gemv(P, slots, R, grid, stream));
+  P.stage_xt = stage_ok(cols, slots);
+  return hip_status(fn, launch_gemv(P, slots, R, (int64_t)P.n_items * P.row_groups, stream));
 }
 
 // ============================================================================
@@ -316,10 +352,10 @@ static int run_gemv_phase(const char* fn, const gale_matrix* table, int stride, 
   P.gateup = gateup;
   const int ntiles = rows / 16;
   const int64_t bound = implicit ? n_items : item_bound;
-  const int R = pick_tiles(bound, ntiles, flags);
+  const int R = pick_tiles(bound, ntiles, cols, slots, flags);
   P.row_groups = (ntiles + R - 1) / R;
-  const int grid = (int)std::min<int64_t>(bound * P.row_groups, 1 << 20);
-  return hip_status(fn, launch_gemv(P, slots, R, grid, s));
+  P.stage_xt = stage_ok(cols, slots);
+  return hip_status(fn, launch_gemv(P, slots, R, bound * P.row_groups, s));
 }
 
 extern "C" int gale_expert_ffn(int32_t hidden, int32_t inter, const gale_expert* experts_dev, int32_t n_exp,

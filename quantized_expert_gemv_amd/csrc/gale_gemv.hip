@@ -17,17 +17,32 @@
 //     form (w & 0x80808080) | 0x38383838 = (1 - 2 b) * 1.0;
 //   * the activation enters as A = four e4m3 terms of X = x~ 2^p (rows of A),
 //     up to four tokens sharing the weights (so M = 4 terms x 4 tokens);
-//   * with C = -sum_k X over the block (one extra MFMA against an all -1 operand),
-//     D = -(sum_k (1 - 2 b) X) for planes 0..6 and +sum for plane 7, so
-//     y += -/+ s[n][blk] D: one FMA per 16x128 block of a lane's row.
+//   * the block sums S = sum_k X (one MFMA against an all -1.0 operand when the
+//     activation changes) turn the 0/1 planes into signs: block d adds
+//     s[n][d] (S - 2 sum_k b X).
 // One v_mfma_scale_f32_16x16x128_f8f6f4 therefore consumes one scale block of
-// 16 rows: 2048 weights for 8 ANDs + 1 FMA per lane.
+// 16 rows: 2048 weights for 8 ANDs and two FMAs per lane.
 //
-// Work split: a workgroup owns `R` row tiles (16 rows each) of one work item
-// (a matrix and up to four activation vectors); its NW wavefronts split the
-// 1024-column chunks (split-K) and meet in LDS.  Outliers are applied after the
-// sign pass by all threads of the workgroup (a few lanes per row, CSR order),
-// gathering x~ from the fp32 copy in the activation record.
+// Work split.  A unit is R row tiles (16 rows each) of one work item (a matrix,
+// or the w1/w3 pair of an expert, with up to four activation vectors).  A
+// workgroup has one wavefront per 1024-column chunk of each matrix (split-K);
+// the partial sums meet in LDS.  Workgroups are persistent: each streams a
+// contiguous run of units.
+//
+// Memory pipeline.  Vector-memory completions are counted in issue order, so a
+// wait for any load also waits for every older one.  Each unit therefore
+// consumes only data issued one unit earlier: at the top of unit u the
+// workgroup issues the whole of unit u+1 (sign words, block scales, the outlier
+// entries of its rows as 16-byte chunks, row scales) and the CSR offsets of
+// unit u+2, then computes unit u from registers and LDS.  Descriptors are read
+// with scalar loads; nothing is loaded conditionally (addresses are clamped),
+// so the compiler's wait counts stay exact and one full unit of HBM traffic is
+// always in flight behind the arithmetic.
+//
+// Outliers: each wavefront serves 16 rows of the unit.  Their CSR entries are a
+// contiguous range, fetched as coalesced 16-byte chunks and staged in the
+// wavefront's own LDS slice; four lanes per row then walk the row in CSR order
+// and gather x~ from an LDS copy of the activation.
 #include "gale_internal.h"
 #include "gale_decode.h"
 
@@ -36,6 +51,10 @@ namespace gale {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
+constexpr int kColChunks = 2;    // 16-byte chunks of outlier columns per lane (1024 entries per wave)
+constexpr int kValChunks = 1;    // 16-byte chunks of outlier values per lane (2048 entries per wave)
+constexpr int kWaveOutBytes = 64 * 16 * (kColChunks + kValChunks);
+
 __device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
   __half_raw r;
   r.x = (unsigned short)bits16;
@@ -43,6 +62,22 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
 }
 
 __device__ __forceinline__ float silu_f(float a) { return a / (1.0f + __expf(-a)); }
+
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((address_space(3))) unsigned short lds_u16;
+typedef __attribute__((address_space(3))) u32x4 lds_v4;
+
+__device__ __forceinline__ u32x4 to_v4(const uint4 a) { return u32x4{a.x, a.y, a.z, a.w}; }
+
+// 16-byte streaming load (each sign word is read exactly once)
+__device__ __forceinline__ uint4 stream_load16(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 template <int D>
 __device__ __forceinline__ v8i plane_vec(const uint32_t w[8]) {
@@ -58,272 +93,485 @@ __device__ __forceinline__ v4f plane_mfma(const v8i& a, const uint32_t w[8], con
                                                           plane_scale_e8m0<D>());
 }
 
-template <int NS, int D>
-__device__ __forceinline__ void plane_step(const v8i* A, const v4f* Cm, const uint32_t w[8], float s,
-                                           float* acc) {
-  const v4f zero = {0.f, 0.f, 0.f, 0.f};
-  v4f r = plane_mfma<D>(A[D], w, D < 7 ? Cm[D] : zero);
-  const float sg = D < 7 ? -s : s;
-#pragma unroll
-  for (int i = 0; i < NS; ++i) acc[i] = fmaf(sg, r[i], acc[i]);
-}
-
-struct ItemInfo {
-  int mat;
-  int nslots;
-  int ra_idx[4];
-  int out_idx[4];
+// Item of a unit, decoded without dynamically indexed arrays.
+struct Item {
+  int mat, nslots;
+  int ra0, ra1, ra2, ra3;
+  int out0, out1, out2, out3;
 };
 
+__device__ __forceinline__ int sel4(int i, int a, int b, int c, int d) {
+  return i == 0 ? a : (i == 1 ? b : (i == 2 ? c : d));
+}
+
 template <int NS>
-__device__ __forceinline__ ItemInfo decode_item(const GemvParams& P, int item) {
-  ItemInfo it;
+__device__ __forceinline__ Item decode_item(const GemvParams& P, int item) {
+  Item it;
   if (P.implicit_items) {
     const int mat = item / P.n_groups;
     const int grp = item - mat * P.n_groups;
     it.mat = mat;
-    int ns = P.n_tok - grp * NS;
+    const int ns = P.n_tok - grp * NS;
     it.nslots = ns < NS ? ns : NS;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tok = grp * NS + (i < it.nslots ? i : 0);
-      it.ra_idx[i] = (P.x_shared ? 0 : mat * P.n_tok) + tok;
-      it.out_idx[i] = mat * P.n_tok + tok;
-    }
+    const int base_ra = (P.x_shared ? 0 : mat * P.n_tok) + grp * NS;
+    const int base_out = mat * P.n_tok + grp * NS;
+    it.ra0 = base_ra;
+    it.ra1 = base_ra + (1 < it.nslots ? 1 : 0);
+    it.ra2 = base_ra + (2 < it.nslots ? 2 : 0);
+    it.ra3 = base_ra + (3 < it.nslots ? 3 : 0);
+    it.out0 = base_out;
+    it.out1 = base_out + (1 < it.nslots ? 1 : 0);
+    it.out2 = base_out + (2 < it.nslots ? 2 : 0);
+    it.out3 = base_out + (3 < it.nslots ? 3 : 0);
   } else {
-    const WorkItem w = P.items[item];
-    it.mat = w.expert;
-    it.nslots = w.n_slots < NS ? w.n_slots : NS;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int pr = w.pair[i < it.nslots ? i : 0];
-      it.ra_idx[i] = pr / P.ra_div;
-      it.out_idx[i] = pr;
-    }
+    const auto* w = (const __attribute__((address_space(4))) WorkItem*)(P.items) + item;
+    it.mat = uni(w->expert);
+    const int ns = uni(w->n_slots);
+    it.nslots = ns < NS ? ns : NS;
+    const int p0 = uni(w->pair[0]), p1 = uni(w->pair[1]), p2 = uni(w->pair[2]), p3 = uni(w->pair[3]);
+    it.out0 = p0;
+    it.out1 = 1 < it.nslots ? p1 : p0;
+    it.out2 = 2 < it.nslots ? p2 : p0;
+    it.out3 = 3 < it.nslots ? p3 : p0;
+    it.ra0 = it.out0 / P.ra_div;
+    it.ra1 = it.out1 / P.ra_div;
+    it.ra2 = it.out2 / P.ra_div;
+    it.ra3 = it.out3 / P.ra_div;
   }
   return it;
 }
 
-// NS: activation vectors per item (1, 2 or 4); R: row tiles per workgroup;
-// NW: wavefronts per matrix (split-K); GATEUP: two matrices (w1, w3) and a SwiGLU epilogue.
-template <int NS, int R, int NW, bool GATEUP>
-__global__ void __launch_bounds__(NW * (GATEUP ? 2 : 1) * 64) gemv_kernel(const GemvParams P) {
-  constexpr int HALVES = GATEUP ? 2 : 1;
-  constexpr int THREADS = NW * HALVES * 64;
-  constexpr int RI = HALVES * R * 16;                 // row instances per workgroup
-  // four lanes per row for the outlier pass, whatever the workgroup shape, so that the
-  // summation order (and so the result) does not depend on the launch configuration
-  constexpr int TPR = 4;
-  constexpr int GROUPS = THREADS / TPR;
+struct Geo {
+  int K, C, tid, lane, wave, half, c, g, nl, ntiles, RG;
+  int ohalf, orow0, wr, sub;   // outlier role: rows orow0 + wr of half ohalf, lane sub of four
+  bool orole;
+};
 
-  __shared__ float red[HALVES][NW][R * 16][NS];
-  __shared__ float ored[HALVES][R * 16][NS];
+// Read-only tables are read through the constant address space: scalar loads, which
+// complete on their own counter and never make the vector pipeline wait.
+template <typename T>
+__device__ __forceinline__ const __attribute__((address_space(4))) T* as_const(const T* p) {
+  return (const __attribute__((address_space(4))) T*)(p);
+}
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int half = GATEUP ? wave / NW : 0;
-  const int wl = wave % NW;
-  const int g = lane >> 4, nl = lane & 15;
-  const int C = P.cols >> 10;
-  const int ntiles = P.rows >> 4;
+__device__ __forceinline__ gale_matrix matrix_of(const GemvParams& P, int mat, int hf) {
+  const auto* t = as_const(P.table);
+  const int i = uni(mat * P.mat_stride + (hf ? P.sel1 : P.sel0));
+  gale_matrix m;
+  m.signs = t[i].signs;
+  m.block_scales = t[i].block_scales;
+  m.row_scales = t[i].row_scales;
+  m.row_ptr = t[i].row_ptr;
+  m.out_cols = t[i].out_cols;
+  m.out_vals = t[i].out_vals;
+  return m;
+}
 
-  const int n_items = P.implicit_items ? P.n_items : *P.n_items_dev;
-  const int total = n_items * P.row_groups;
+// Row served by this thread's outlier role in unit rg, clamped to [0, rows].
+template <int R>
+__device__ __forceinline__ int outlier_row(const GemvParams& P, const Geo& G, int rg, bool* valid) {
+  const int n = rg * R * 16 + G.orow0 + G.wr;
+  *valid = G.orole && n < P.rows;
+  return n < P.rows ? n : P.rows;
+}
 
-  for (int work = blockIdx.x; work < total; work += gridDim.x) {
-    const int item = work / P.row_groups;
-    const int rg = work - item * P.row_groups;
-    const ItemInfo it = decode_item<NS>(P, item);
-    const gale_matrix M = P.table[it.mat * P.mat_stride + (half ? P.sel1 : P.sel0)];
+// Everything unit u needs from HBM, issued during unit u-1.
+template <int R>
+struct UnitBuf {
+  uint32_t sw[R][8];     // sign words of the wave's R tiles (its chunk)
+  uint32_t sc[R][4];     // 8 fp16 block scales of the lane's row, per tile
+  uint4 oc[kColChunks];  // outlier column chunks of the wave's 16 rows
+  uint4 ov[kValChunks];  // outlier value chunks
+  int ocf, ovf;          // first chunk index of each (wave-uniform)
+  int rp0, rp1;          // CSR range of this thread's row in this unit
+  int np0, np1;          // CSR range of this thread's row in the next unit
+  uint32_t rsc;          // fp16 row scale of this thread's row
+};
 
-    float rowsum[R][NS];
+// Issue the loads of unit v into b.  rp0/rp1 of unit v must already be in b (from the
+// previous unit's np0/np1).  Also fetches the CSR offsets of unit vnext.
+template <int NS, int R>
+__device__ __forceinline__ void issue_unit(const GemvParams& P, const Geo& G, int v, int vnext, UnitBuf<R>& b) {
+  const int item = uni(v / G.RG);
+  const int rg = uni(v - item * G.RG);
+  const int mat = uni(decode_item<NS>(P, item).mat);
+  const gale_matrix Mw = matrix_of(P, mat, G.half);
+  const gale_matrix Mo = matrix_of(P, mat, G.ohalf);
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+  for (int r = 0; r < R; ++r) {
+    int tile = rg * R + r;
+    tile = tile < G.ntiles ? tile : G.ntiles - 1;
+    const uint4* sw = reinterpret_cast<const uint4*>(Mw.signs + sign_word_index(tile, G.c, G.C, 0, G.lane, 0));
+    const uint4 lo = stream_load16(sw);
+    const uint4 hi = stream_load16(sw + 64);
+    b.sw[r][0] = lo.x; b.sw[r][1] = lo.y; b.sw[r][2] = lo.z; b.sw[r][3] = lo.w;
+    b.sw[r][4] = hi.x; b.sw[r][5] = hi.y; b.sw[r][6] = hi.z; b.sw[r][7] = hi.w;
+    const uint4 sc = stream_load16(Mw.block_scales + scale_index(16 * tile + G.nl, 8 * G.c, G.C));
+    b.sc[r][0] = sc.x; b.sc[r][1] = sc.y; b.sc[r][2] = sc.z; b.sc[r][3] = sc.w;
+  }
+  // outlier entries of the wave's 16 rows: CSR range [e0, e1) from lanes 0 (first row) and 60 (last row)
+  const int e0 = uni(__builtin_amdgcn_readlane(b.rp0, 0));
+  const int e1 = uni(__builtin_amdgcn_readlane(b.rp1, 60));
+  // 16-byte chunks holding the uint16 columns and the packed int4 values of [e0, e1); an
+  // empty range reads chunk 0 (the sections are padded to, and readable in, whole 16-byte chunks)
+  const bool any = e1 > e0;
+  const int cf = any ? (2 * e0) >> 4 : 0;
+  const int cl = any ? (2 * e1 - 1) >> 4 : 0;
+  const int vf = any ? (e0 >> 1) >> 4 : 0;
+  const int vl = any ? ((e1 - 1) >> 1) >> 4 : 0;
+  b.ocf = cf;
+  b.ovf = vf;
+  const uint4* cbase = reinterpret_cast<const uint4*>(Mo.out_cols);
+  const uint4* vbase = reinterpret_cast<const uint4*>(Mo.out_vals);
 #pragma unroll
-      for (int i = 0; i < NS; ++i) rowsum[r][i] = 0.f;
+  for (int k = 0; k < kColChunks; ++k) {
+    int ch = cf + 64 * k + G.lane;
+    ch = ch < cl ? ch : cl;
+    b.oc[k] = cbase[ch];
+  }
+#pragma unroll
+  for (int k = 0; k < kValChunks; ++k) {
+    int ch = vf + 64 * k + G.lane;
+    ch = ch < vl ? ch : vl;
+    b.ov[k] = vbase[ch];
+  }
+  bool ok;
+  const int n = outlier_row<R>(P, G, rg, &ok);
+  b.rsc = Mo.row_scales[n < P.rows ? n : P.rows - 1];
+  // CSR offsets of the next unit's row
+  const int item2 = uni(vnext / G.RG);
+  const int rg2 = uni(vnext - item2 * G.RG);
+  const int mat2 = uni(decode_item<NS>(P, item2).mat);
+  const gale_matrix Mo2 = matrix_of(P, mat2, G.ohalf);
+  const int n2 = outlier_row<R>(P, G, rg2, &ok);
+  b.np0 = Mo2.row_ptr[n2];
+  b.np1 = Mo2.row_ptr[n2 + (n2 < P.rows ? 1 : 0)];
+}
 
-    for (int c = wl; c < C; c += NW) {
-      // ---- sign words and block scales of this wave's R tiles (all loads issued up front)
-      uint32_t w[R][8];
-      uint4 sc[R];
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int tile = rg * R + r;
-        if (tile < ntiles) {
-          const uint4* sw = reinterpret_cast<const uint4*>(M.signs + sign_word_index(tile, c, C, 0, lane, 0));
-          const uint4 lo = sw[0], hi = sw[64];
-          w[r][0] = lo.x; w[r][1] = lo.y; w[r][2] = lo.z; w[r][3] = lo.w;
-          w[r][4] = hi.x; w[r][5] = hi.y; w[r][6] = hi.z; w[r][7] = hi.w;
-          sc[r] = *reinterpret_cast<const uint4*>(M.block_scales + scale_index(16 * tile + nl, 8 * c, C));
-        } else {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) w[r][j] = 0;
-          sc[r] = make_uint4(0, 0, 0, 0);
-        }
-      }
-      // ---- A operand: four e4m3 terms of up to NS activation vectors, 8 planes
-      const int term = nl >> 2, slot = nl & 3;
-      v8i A[8];
-      if (slot < it.nslots) {
-        const uint8_t* tb = P.ra + (size_t)it.ra_idx[slot] * P.ra_stride + ra_terms_off(P.cols) +
-                            ((size_t)c * 4 + term) * 1024 + 32 * g;
-#pragma unroll
-        for (int d = 0; d < 8; ++d) {
-          const uint4 a0 = *reinterpret_cast<const uint4*>(tb + 128 * d);
-          const uint4 a1 = *reinterpret_cast<const uint4*>(tb + 128 * d + 16);
-          A[d] = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-        }
-      } else {
-#pragma unroll
-        for (int d = 0; d < 8; ++d) A[d] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-      }
-      int pexp[NS];
-#pragma unroll
-      for (int i = 0; i < NS; ++i)
-        pexp[i] = i < it.nslots
-                      ? reinterpret_cast<const int32_t*>(P.ra + (size_t)it.ra_idx[i] * P.ra_stride + ra_p_off(P.cols))[c]
-                      : 0;
-      // ---- C operand: -sum over each scale block of each term
-      v4f Cm[8];
-      {
-        const v8i neg1 = {(int)0xB8B8B8B8, (int)0xB8B8B8B8, (int)0xB8B8B8B8, (int)0xB8B8B8B8,
-                          (int)0xB8B8B8B8, (int)0xB8B8B8B8, (int)0xB8B8B8B8, (int)0xB8B8B8B8};
-        const v4f zero = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int d = 0; d < 8; ++d)
-          Cm[d] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[d], neg1, zero, 0, 0, 0, 127, 0, 127);
-      }
-      // ---- sign pass
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        float acc[NS];
-#pragma unroll
-        for (int i = 0; i < NS; ++i) acc[i] = 0.f;
-        const uint32_t s01 = sc[r].x, s23 = sc[r].y, s45 = sc[r].z, s67 = sc[r].w;
-        plane_step<NS, 0>(A, Cm, w[r], half_bits_to_float(s01 & 0xFFFF), acc);
-        plane_step<NS, 1>(A, Cm, w[r], half_bits_to_float(s01 >> 16), acc);
-        plane_step<NS, 2>(A, Cm, w[r], half_bits_to_float(s23 & 0xFFFF), acc);
-        plane_step<NS, 3>(A, Cm, w[r], half_bits_to_float(s23 >> 16), acc);
-        plane_step<NS, 4>(A, Cm, w[r], half_bits_to_float(s45 & 0xFFFF), acc);
-        plane_step<NS, 5>(A, Cm, w[r], half_bits_to_float(s45 >> 16), acc);
-        plane_step<NS, 6>(A, Cm, w[r], half_bits_to_float(s67 & 0xFFFF), acc);
-        plane_step<NS, 7>(A, Cm, w[r], half_bits_to_float(s67 >> 16), acc);
-        // undo 2^p, then sum the four terms (lane groups g = 0..3)
-#pragma unroll
-        for (int i = 0; i < NS; ++i) {
-          float v = ldexpf(acc[i], -pexp[i]);
-          v += __shfl_xor(v, 16, 64);
-          v += __shfl_xor(v, 32, 64);
-          rowsum[r][i] += v;
-        }
-      }
-    }
-    if (lane < 16) {
-#pragma unroll
-      for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int i = 0; i < NS; ++i) red[half][wl][r * 16 + lane][i] = rowsum[r][i];
-    }
+struct Act {
+  v8i A[8];              // e4m3 terms, one operand per scale block of the chunk
+  float S[7][4];         // -sum over each of the blocks 0..6, per slot (plane 7 needs none)
+  int pexp[4];
+};
 
-    // ---- outliers: TPR threads per row, CSR order, x~ gathered from the fp32 record
-    for (int ri = tid / TPR; ri < RI; ri += GROUPS) {
-      const int sub = tid % TPR;
-      const int hf = ri / (R * 16);
-      const int rr = ri - hf * (R * 16);
-      const int n = (rg * R + rr / 16) * 16 + (rr & 15);
-      float o[NS];
+template <int NS>
+__device__ __forceinline__ void load_activation(const GemvParams& P, const Geo& G, const Item& it, Act& a) {
+  const int term = G.nl >> 2, slot = G.nl & 3;
+  const int ra = sel4(slot < it.nslots ? slot : 0, it.ra0, it.ra1, it.ra2, it.ra3);
+  const uint8_t* tb = P.ra + (size_t)ra * P.ra_stride + ra_terms_off(G.K) + ((size_t)G.c * 4 + term) * 1024 + 32 * G.g;
+  const bool live = slot < it.nslots;
 #pragma unroll
-      for (int i = 0; i < NS; ++i) o[i] = 0.f;
-      float rs = 0.f;
-      if (n < P.rows) {
-        const gale_matrix Mo = P.table[it.mat * P.mat_stride + (hf ? P.sel1 : P.sel0)];
-        const int p0 = Mo.row_ptr[n], p1 = Mo.row_ptr[n + 1];
-        for (int p = p0 + sub; p < p1; p += TPR) {
-          const int col = Mo.out_cols[p];
-          const float q = (float)outlier_value(Mo.out_vals, p);
+  for (int d = 0; d < 8; ++d) {
+    const uint4 a0 = *reinterpret_cast<const uint4*>(tb + 128 * d);
+    const uint4 a1 = *reinterpret_cast<const uint4*>(tb + 128 * d + 16);
+    a.A[d] = live ? v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w}
+                  : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+  }
 #pragma unroll
-          for (int i = 0; i < NS; ++i) {
-            if (i < it.nslots) {
-              const float* xt = reinterpret_cast<const float*>(P.ra + (size_t)it.ra_idx[i] * P.ra_stride);
-              o[i] = fmaf(q, xt[col], o[i]);
-            }
-          }
-        }
-        rs = half_bits_to_float(Mo.row_scales[n]);
-      }
+  for (int i = 0; i < NS; ++i) {
+    const int rai = sel4(i < it.nslots ? i : 0, it.ra0, it.ra1, it.ra2, it.ra3);
+    const int pv = reinterpret_cast<const int32_t*>(P.ra + (size_t)rai * P.ra_stride + ra_p_off(G.K))[G.c];
+    a.pexp[i] = i < it.nslots ? pv : 0;
+  }
+  // -S per block and slot: the MFMA against an all -1.0 operand sums each term row
+  const v8i neg1 = {(int)0xB8B8B8B8, (int)0xB8B8B8B8, (int)0xB8B8B8B8, (int)0xB8B8B8B8,
+                    (int)0xB8B8B8B8, (int)0xB8B8B8B8, (int)0xB8B8B8B8, (int)0xB8B8B8B8};
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < NS; ++i) {
+  for (int d = 0; d < 7; ++d) {
+    const v4f s = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a.A[d], neg1, zero, 0, 0, 0, 127, 0, 127);
 #pragma unroll
-        for (int off = TPR / 2; off >= 1; off >>= 1) o[i] += __shfl_xor(o[i], off, 64);
-      }
-      if (sub == 0) {
-#pragma unroll
-        for (int i = 0; i < NS; ++i) ored[hf][rr][i] = o[i] * rs;
-      }
-    }
-    __syncthreads();
-
-    // ---- final: sum the split-K partials in a fixed order, add outliers, store
-    for (int e = tid; e < R * 16 * NS; e += THREADS) {
-      const int rr = e / NS, i = e - rr * NS;
-      const int n = (rg * R + rr / 16) * 16 + (rr & 15);
-      if (n >= P.rows || i >= it.nslots) continue;
-      float v[HALVES];
-#pragma unroll
-      for (int hf = 0; hf < HALVES; ++hf) {
-        float acc = 0.f;
-#pragma unroll
-        for (int q = 0; q < NW; ++q) acc += red[hf][q][rr][i];
-        v[hf] = acc + ored[hf][rr][i];
-      }
-      const int64_t off = (int64_t)it.out_idx[i] * P.y_stride + n;
-      if (GATEUP) {
-        reinterpret_cast<float*>(P.y)[off] = silu_f(v[0]) * v[HALVES - 1];
-      } else if (P.y_dtype == GALE_F16) {
-        reinterpret_cast<__half*>(P.y)[off] = __float2half_rn(v[0]);
-      } else {
-        reinterpret_cast<float*>(P.y)[off] = v[0];
-      }
-    }
-    __syncthreads();
+    for (int i = 0; i < NS; ++i) a.S[d][i] = s[i];
   }
 }
 
-template <int NS, int R, int NW, bool G>
-static hipError_t launch_t(const GemvParams& p, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((gemv_kernel<NS, R, NW, G>), dim3(grid), dim3(NW * (G ? 2 : 1) * 64), 0, s, p);
-  return hipGetLastError();
+// One plane: D = 2 sum_k b X (planes 0..6, via the E8M0 scale) or sum_k (1 - 2 b) X (plane 7).
+// Block contribution s (S - 2 P): acc += -s D - s (-S) for d < 7; acc += s D for d = 7.
+template <int NS, int D>
+__device__ __forceinline__ void plane_step(const Act& a, const uint32_t w[8], float s, float* acc) {
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+  const v4f r = plane_mfma<D>(a.A[D], w, zero);
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    if constexpr (D < 7) {
+      acc[i] = fmaf(-s, r[i], acc[i]);
+      acc[i] = fmaf(-s, a.S[D][i], acc[i]);
+    } else {
+      acc[i] = fmaf(s, r[i], acc[i]);
+    }
+  }
+}
+
+template <int NS, int R, bool GATEUP>
+__device__ __forceinline__ void process_unit(const GemvParams& P, const Geo& G, int u, int u1, UnitBuf<R>& cur,
+                                             UnitBuf<R>& nxt, int& act_item, Act& act, lds_f32* red, lds_f32* ored,
+                                             lds_f32* xt, lds_u8* wout) {
+  constexpr int HALVES = GATEUP ? 2 : 1;
+  constexpr int RR = R * 16;
+  const int item = uni(u / G.RG);
+  const int rg = uni(u - item * G.RG);
+  const Item it = decode_item<NS>(P, item);
+
+  // 1. activation of a new item (A operands, block sums, x~ in LDS); issued before the
+  //    next unit's loads so that waiting for it never waits for them
+  if (item != act_item) {
+    load_activation<NS>(P, G, it, act);
+    if (P.stage_xt) {
+      for (int i = 0; i < NS; ++i) {
+        if (i >= it.nslots) break;
+        const int ra = sel4(i, it.ra0, it.ra1, it.ra2, it.ra3);
+        const u32x4* src = reinterpret_cast<const u32x4*>(P.ra + (size_t)ra * P.ra_stride);
+        lds_v4* dst = reinterpret_cast<lds_v4*>(xt + i * G.K);
+        for (int q = G.tid; q < (G.K >> 2); q += (int)blockDim.x) dst[q] = src[q];
+      }
+    }
+    __syncthreads();
+    act_item = item;
+  }
+
+  // 2. stage this unit's outlier chunks in the wave's LDS slice
+  {
+    lds_v4* oc = reinterpret_cast<lds_v4*>(wout);
+#pragma unroll
+    for (int k = 0; k < kColChunks; ++k) oc[64 * k + G.lane] = to_v4(cur.oc[k]);
+#pragma unroll
+    for (int k = 0; k < kValChunks; ++k) oc[64 * (kColChunks + k) + G.lane] = to_v4(cur.ov[k]);
+  }
+
+  // 3. issue unit u+1 (and the CSR offsets of u+2) behind this unit's arithmetic
+  {
+    const int v = u + 1 < u1 ? u + 1 : u;
+    const int vn = u + 2 < u1 ? u + 2 : v;
+    nxt.rp0 = cur.np0;
+    nxt.rp1 = cur.np1;
+    issue_unit<NS, R>(P, G, v, vn, nxt);
+  }
+
+  // 4. sign pass over the wave's R tiles
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float acc[NS];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) acc[i] = 0.f;
+    const uint32_t s01 = cur.sc[r][0], s23 = cur.sc[r][1], s45 = cur.sc[r][2], s67 = cur.sc[r][3];
+    plane_step<NS, 0>(act, cur.sw[r], half_bits_to_float(s01 & 0xFFFF), acc);
+    plane_step<NS, 1>(act, cur.sw[r], half_bits_to_float(s01 >> 16), acc);
+    plane_step<NS, 2>(act, cur.sw[r], half_bits_to_float(s23 & 0xFFFF), acc);
+    plane_step<NS, 3>(act, cur.sw[r], half_bits_to_float(s23 >> 16), acc);
+    plane_step<NS, 4>(act, cur.sw[r], half_bits_to_float(s45 & 0xFFFF), acc);
+    plane_step<NS, 5>(act, cur.sw[r], half_bits_to_float(s45 >> 16), acc);
+    plane_step<NS, 6>(act, cur.sw[r], half_bits_to_float(s67 & 0xFFFF), acc);
+    plane_step<NS, 7>(act, cur.sw[r], half_bits_to_float(s67 >> 16), acc);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      float v = ldexpf(acc[i], -act.pexp[i]);     // undo 2^p
+      v += __shfl_xor(v, 16, 64);                 // sum the four terms (lane groups)
+      v += __shfl_xor(v, 32, 64);
+      if (G.lane < 16) red[((G.half * G.C + G.c) * RR + r * 16 + G.lane) * NS + i] = v;
+    }
+  }
+
+  // 5. outliers: four lanes per row in CSR order, entries and x~ from LDS
+  {
+    bool valid;
+    (void)outlier_row<R>(P, G, rg, &valid);
+    const lds_u16* lc = reinterpret_cast<const lds_u16*>(wout);
+    const lds_u8* lv = wout + 64 * 16 * kColChunks;
+    float o[NS];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) o[i] = 0.f;
+    const int cbase = 8 * cur.ocf, vbase = 16 * cur.ovf;
+    const int p_begin = cur.rp0 + G.sub, p_end = valid ? cur.rp1 : p_begin;
+    // entries p < p_cap are in the staged chunks
+    const int p_cap = min(cbase + 64 * 8 * kColChunks, 2 * (vbase + 64 * 16 * kValChunks));
+    const int p_mid = min(p_end, p_cap);
+    int p = p_begin;
+    if (P.stage_xt) {
+      for (; p < p_mid; p += 4) {
+        const int col = lc[p - cbase];
+        const int byte = lv[(p >> 1) - vbase];
+        const int nib = (p & 1) ? (byte >> 4) : (byte & 0xF);
+        const float q = (float)(nib - ((nib & 8) << 1));
+#pragma unroll
+        for (int i = 0; i < NS; ++i)
+          if (i < it.nslots) o[i] = fmaf(q, xt[i * G.K + col], o[i]);
+      }
+    } else {
+      for (; p < p_mid; p += 4) {
+        const int col = lc[p - cbase];
+        const int byte = lv[(p >> 1) - vbase];
+        const int nib = (p & 1) ? (byte >> 4) : (byte & 0xF);
+        const float q = (float)(nib - ((nib & 8) << 1));
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+          if (i < it.nslots) {
+            const int ra = sel4(i, it.ra0, it.ra1, it.ra2, it.ra3);
+            o[i] = fmaf(q, reinterpret_cast<const float*>(P.ra + (size_t)ra * P.ra_stride)[col], o[i]);
+          }
+        }
+      }
+    }
+    // rows whose entries run past the staged chunks: the rest straight from memory
+    for (; p < p_end; p += 4) {
+      const gale_matrix* Mo = P.table + it.mat * P.mat_stride + (G.ohalf ? P.sel1 : P.sel0);
+      const int col = Mo->out_cols[p];
+      const float q = (float)outlier_value(Mo->out_vals, p);
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        if (i < it.nslots) {
+          const int ra = sel4(i, it.ra0, it.ra1, it.ra2, it.ra3);
+          o[i] = fmaf(q, reinterpret_cast<const float*>(P.ra + (size_t)ra * P.ra_stride)[col], o[i]);
+        }
+      }
+    }
+    const float rscale = half_bits_to_float(cur.rsc);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      o[i] += __shfl_xor(o[i], 1, 64);
+      o[i] += __shfl_xor(o[i], 2, 64);
+      if (G.orole && G.sub == 0) ored[(G.ohalf * RR + G.orow0 + G.wr) * NS + i] = o[i] * rscale;
+    }
+  }
+  __syncthreads();
+
+  // 6. sum the split-K partials in a fixed order, add the outliers, store
+  for (int e = G.tid; e < RR * NS; e += (int)blockDim.x) {
+    const int rr = e / NS, i = e - rr * NS;
+    const int n = rg * RR + rr;
+    if (n >= P.rows || i >= it.nslots) continue;
+    float v[HALVES];
+#pragma unroll
+    for (int hf = 0; hf < HALVES; ++hf) {
+      float a = 0.f;
+      for (int q = 0; q < G.C; ++q) a += red[((hf * G.C + q) * RR + rr) * NS + i];
+      v[hf] = a + ored[(hf * RR + rr) * NS + i];
+    }
+    const int64_t off = (int64_t)sel4(i, it.out0, it.out1, it.out2, it.out3) * P.y_stride + n;
+    if (GATEUP) {
+      reinterpret_cast<float*>(P.y)[off] = silu_f(v[0]) * v[HALVES - 1];
+    } else if (P.y_dtype == GALE_F16) {
+      reinterpret_cast<__half*>(P.y)[off] = __float2half_rn(v[0]);
+    } else {
+      reinterpret_cast<float*>(P.y)[off] = v[0];
+    }
+  }
+  __syncthreads();
+}
+
+// NS: activation vectors per item (1, 2 or 4); R: row tiles per unit (R <= chunks);
+// GATEUP: two matrices (w1, w3) and a SwiGLU epilogue.  blockDim.x = 64 * C * (GATEUP ? 2 : 1).
+template <int NS, int R, bool GATEUP>
+__global__ void __launch_bounds__(512) gemv_kernel(const GemvParams P) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int HALVES = GATEUP ? 2 : 1;
+  constexpr int RR = R * 16;
+  Geo G;
+  G.K = P.cols;
+  G.C = P.cols >> 10;
+  G.tid = threadIdx.x;
+  G.lane = G.tid & 63;
+  G.wave = uni(G.tid >> 6);
+  G.half = uni(GATEUP ? (G.wave >= G.C ? 1 : 0) : 0);
+  G.c = uni(G.wave - G.half * G.C);
+  G.g = G.lane >> 4;
+  G.nl = G.lane & 15;
+  G.ntiles = P.rows >> 4;
+  G.RG = P.row_groups;
+  // outlier role: wave w serves unit rows 16 w .. 16 w + 15 (across the halves)
+  G.orole = G.wave < HALVES * R;
+  G.ohalf = uni(G.orole ? (16 * G.wave) / RR : 0);
+  G.orow0 = uni(G.orole ? 16 * G.wave - G.ohalf * RR : 0);
+  G.wr = G.lane >> 2;
+  G.sub = G.lane & 3;
+
+  lds_u8* base = (lds_u8*)smem;
+  lds_f32* red = reinterpret_cast<lds_f32*>(base);             // [HALVES][C][RR][NS]
+  lds_f32* ored = red + HALVES * G.C * RR * NS;                // [HALVES][RR][NS]
+  lds_u8* wbase = reinterpret_cast<lds_u8*>(ored + HALVES * RR * NS);
+  lds_u8* wout = wbase + G.wave * kWaveOutBytes;               // this wave's outlier staging slice
+  lds_f32* xt = reinterpret_cast<lds_f32*>(wbase + (size_t)HALVES * G.C * kWaveOutBytes);   // [NS][K] when staged
+
+  const int n_items = P.implicit_items ? P.n_items : *P.n_items_dev;
+  const int total = n_items * G.RG;
+  const int u0 = uni((int)((int64_t)total * blockIdx.x / gridDim.x));
+  const int u1 = uni((int)((int64_t)total * (blockIdx.x + 1) / gridDim.x));
+  if (u0 >= u1) return;
+
+  UnitBuf<R> b0, b1;
+  Act act;
+  int act_item = -1;
+  {
+    // prologue: CSR offsets of u0, then the whole of u0 (with the offsets of u0 + 1)
+    const int item0 = uni(u0 / G.RG);
+    const int mat = uni(decode_item<NS>(P, item0).mat);
+    const gale_matrix Mo = matrix_of(P, mat, G.ohalf);
+    bool ok;
+    const int n = outlier_row<R>(P, G, u0 - item0 * G.RG, &ok);
+    b0.rp0 = Mo.row_ptr[n];
+    b0.rp1 = Mo.row_ptr[n + (n < P.rows ? 1 : 0)];
+    issue_unit<NS, R>(P, G, u0, u0 + 1 < u1 ? u0 + 1 : u0, b0);
+  }
+  for (int u = u0; u < u1; u += 2) {
+    process_unit<NS, R, GATEUP>(P, G, u, u1, b0, b1, act_item, act, red, ored, xt, wout);
+    if (u + 1 >= u1) break;
+    process_unit<NS, R, GATEUP>(P, G, u + 1, u1, b1, b0, act_item, act, red, ored, xt, wout);
+  }
+}
+
+size_t gemv_smem_bytes(int cols, int slots, int tiles, int gateup, int stage_xt) {
+  const int halves = gateup ? 2 : 1;
+  const int C = cols >> 10;
+  size_t f = (size_t)halves * C * tiles * 16 * slots + (size_t)halves * tiles * 16 * slots;
+  size_t b = f * 4 + (size_t)halves * C * kWaveOutBytes;
+  if (stage_xt) b += (size_t)slots * cols * 4;
+  return b;
+}
+
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
 }
 
 template <int NS, int R, bool G>
-static hipError_t launch_nw(const GemvParams& p, int grid, hipStream_t s) {
+static hipError_t launch_t(const GemvParams& p, int64_t max_units, hipStream_t s) {
   const int C = p.cols >> 10;
-  if (C >= 4) return launch_t<NS, R, 4, G>(p, grid, s);
-  if (C >= 2) return launch_t<NS, R, 2, G>(p, grid, s);
-  return launch_t<NS, R, 1, G>(p, grid, s);
+  const int block = 64 * C * (G ? 2 : 1);
+  const size_t smem = gemv_smem_bytes(p.cols, NS, R, G, p.stage_xt);
+  int occ = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemv_kernel<NS, R, G>, block, smem) != hipSuccess || occ < 1)
+    occ = 1;
+  const int64_t grid = std::min<int64_t>(max_units, (int64_t)device_cu_count() * occ);
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL((gemv_kernel<NS, R, G>), dim3((unsigned)grid), dim3(block), smem, s, p);
+  return hipGetLastError();
 }
 
 template <int NS, bool G>
-static hipError_t launch_r(const GemvParams& p, int tiles, int grid, hipStream_t s) {
+static hipError_t launch_r(const GemvParams& p, int tiles, int64_t max_units, hipStream_t s) {
   switch (tiles) {
-    case 1: return launch_nw<NS, 1, G>(p, grid, s);
-    case 2: return launch_nw<NS, 2, G>(p, grid, s);
-    case 4: return launch_nw<NS, 4, G>(p, grid, s);
-    default: return launch_nw<NS, 8, G>(p, grid, s);
+    case 1: return launch_t<NS, 1, G>(p, max_units, s);
+    case 2: return launch_t<NS, 2, G>(p, max_units, s);
+    default: return launch_t<NS, 4, G>(p, max_units, s);
   }
 }
 
-hipError_t launch_gemv(const GemvParams& p, int slots, int tiles_per_wg, int grid, hipStream_t s) {
-  if (grid <= 0) return hipSuccess;
+hipError_t launch_gemv(const GemvParams& p, int slots, int tiles_per_unit, int64_t max_units, hipStream_t s) {
+  if (max_units <= 0) return hipSuccess;
   if (p.gateup) {
-    if (slots == 1) return launch_r<1, true>(p, tiles_per_wg, grid, s);
-    if (slots == 2) return launch_r<2, true>(p, tiles_per_wg, grid, s);
-    return launch_r<4, true>(p, tiles_per_wg, grid, s);
+    if (slots == 1) return launch_r<1, true>(p, tiles_per_unit, max_units, s);
+    if (slots == 2) return launch_r<2, true>(p, tiles_per_unit, max_units, s);
+    return launch_r<4, true>(p, tiles_per_unit, max_units, s);
   }
-  if (slots == 1) return launch_r<1, false>(p, tiles_per_wg, grid, s);
-  if (slots == 2) return launch_r<2, false>(p, tiles_per_wg, grid, s);
-  return launch_r<4, false>(p, tiles_per_wg, grid, s);
+  if (slots == 1) return launch_r<1, false>(p, tiles_per_unit, max_units, s);
+  if (slots == 2) return launch_r<2, false>(p, tiles_per_unit, max_units, s);
+  return launch_r<4, false>(p, tiles_per_unit, max_units, s);
 }
 
 }  // namespace gale

@@ -87,7 +87,8 @@ struct GemvParams {
   int y_dtype;
   int64_t y_stride;          // elements between consecutive output vectors
   int gateup;                // SwiGLU epilogue (y = fp32 h)
-  int row_groups;            // WGs per item along rows
+  int row_groups;            // units per item along rows
+  int stage_xt;              // copy x~ into LDS for the outlier gathers
 };
 
 // launches (return hipError_t of the launch)
@@ -95,7 +96,11 @@ hipError_t launch_prep(const void* x, int x_dtype, int64_t x_stride, int n_vec, 
                        uint8_t* ra, size_t ra_stride, hipStream_t s);
 hipError_t launch_fwht(const void* x, void* y, int64_t n_vec, int len, int in_dtype, int out_dtype,
                        hipStream_t s);
-hipError_t launch_gemv(const GemvParams& p, int slots, int tiles_per_wg, int grid, hipStream_t s);
+// max_units: upper bound of the number of units (items x row groups); the launch is a
+// persistent grid of at most that many workgroups.
+hipError_t launch_gemv(const GemvParams& p, int slots, int tiles_per_unit, int64_t max_units, hipStream_t s);
+size_t gemv_smem_bytes(int cols, int slots, int tiles, int gateup, int stage_xt);
+int device_cu_count();
 hipError_t launch_pack(int rows, int cols, int n_mat, const uint32_t* cs, const uint16_t* csc,
                        uint32_t* ds, uint16_t* dsc, hipStream_t s);
 hipError_t launch_debug_unpack(int rows, int cols, const uint32_t* ds, uint32_t* cs, hipStream_t s);

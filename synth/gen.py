@@ -38,7 +38,7 @@ import torch
 
 __all__ = [
     "GOLDEN", "mix64_int", "stream_key", "bits64", "CanonicalMatrix",
-    "gen_matrix", "gen_matrices", "gen_x", "gen_logits_normal", "gen_logits_zipf",
+    "gen_matrix", "gen_matrices", "gen_matrix_bank", "gen_x", "gen_logits_normal", "gen_logits_zipf",
     "config_seed", "MAT_W1", "MAT_W3", "MAT_W2", "n_outliers",
 ]
 
@@ -214,13 +214,50 @@ class CanonicalMatrix:
         }
 
 
-def _pack_nibbles(v: torch.Tensor) -> torch.Tensor:
-    """int64 nibbles [nnz] (0..15) -> uint8 [ceil(nnz/2)], low nibble first."""
-    nnz = v.shape[0]
-    if nnz % 2:
-        v = torch.cat([v, torch.zeros(1, dtype=v.dtype, device=v.device)])
-    v = v.view(-1, 2)
-    return (v[:, 0] | (v[:, 1] << 4)).to(torch.uint8)
+def gen_matrix_bank(seed: int, ids: Sequence[Sequence[int]], rows: int, cols: int,
+                    outlier_frac: float = 0.01, row_scale: float = 0.05, device="cpu") -> Dict[str, torch.Tensor]:
+    """Canonical sections of several same-shape matrices as stacked tensors; matrix i is keyed
+    by (seed, *ids[i]):
+
+      signs [M, N, K/32] int32, block_scales [M, N, K/128] int16, out_cols [M, N*cnt] int16,
+      out_vals [M, ceil(N*cnt/2)] uint8, and, shared by all M (fixed count per row, fixed
+      scale), row_ptr [N+1] int32 and row_scales [N] int16.
+    """
+    if cols % 1024 != 0:
+        raise ValueError("cols must be a multiple of 1024")
+    M = len(ids)
+    N, K = rows, cols
+    dev = torch.device(device)
+    keys = {sec: torch.tensor([_s64(stream_key(seed, *p, sec)) for p in ids],
+                              dtype=torch.int64, device=dev)
+            for sec in (_SEC_SIGNS, _SEC_SCALES, _SEC_OCOLS, _SEC_OVALS)}
+    nw = N * (K // 32)
+    words = _lo32(bits64(keys[_SEC_SIGNS][:, None], torch.arange(nw, device=dev, dtype=torch.int64)[None, :]))
+    words = words.to(torch.int32).view(M, N, K // 32)   # low 32 bits, two's complement
+    nb = N * (K // 128)
+    sb = bits64(keys[_SEC_SCALES][:, None], torch.arange(nb, device=dev, dtype=torch.int64)[None, :])
+    scales = _table("scale16", dev)[_hi16(sb)].view(M, N, K // 128)
+    del sb
+    rs_bits = int(np.array([row_scale], dtype=np.float16).view(np.int16)[0])
+    cnt = n_outliers(K, outlier_frac)
+    if cnt > 0:
+        row_idx = torch.arange(N, device=dev, dtype=torch.int64)
+        row_keys = bits64(keys[_SEC_OCOLS][:, None], row_idx[None, :]).reshape(-1)
+        cols_all = _distinct_uniform(row_keys, cnt, K).view(M, N * cnt).to(torch.int32).to(torch.int16)
+        vb = bits64(keys[_SEC_OVALS][:, None], torch.arange(N * cnt, device=dev, dtype=torch.int64)[None, :])
+        nib = _lsr(vb, 60)                                      # 4 random bits = int4 two's complement
+        if (N * cnt) % 2:
+            nib = torch.cat([nib, torch.zeros(M, 1, dtype=nib.dtype, device=dev)], dim=1)
+        nib = nib.view(M, -1, 2)
+        vals_all = (nib[:, :, 0] | (nib[:, :, 1] << 4)).to(torch.uint8)
+    else:
+        cols_all = torch.zeros(M, 0, dtype=torch.int16, device=dev)
+        vals_all = torch.zeros(M, 0, dtype=torch.uint8, device=dev)
+    return {
+        "signs": words, "block_scales": scales, "out_cols": cols_all, "out_vals": vals_all,
+        "row_ptr": (torch.arange(N + 1, device=dev, dtype=torch.int64) * cnt).to(torch.int32),
+        "row_scales": torch.full((N,), rs_bits, dtype=torch.int16, device=dev),
+    }
 
 
 def gen_matrices(seed: int, ids: Sequence[Sequence[int]], rows: int, cols: int,
@@ -231,47 +268,17 @@ def gen_matrices(seed: int, ids: Sequence[Sequence[int]], rows: int, cols: int,
     The result for one id path does not depend on which other ids are requested,
     so any single matrix can be regenerated on its own (e.g. by the oracle).
     """
-    if cols % 1024 != 0:
-        raise ValueError("cols must be a multiple of 1024")
-    M = len(ids)
-    N, K = rows, cols
-    dev = torch.device(device)
-    keys = {sec: torch.tensor([_s64(stream_key(seed, *p, sec)) for p in ids],
-                              dtype=torch.int64, device=dev)
-            for sec in (_SEC_SIGNS, _SEC_SCALES, _SEC_OCOLS, _SEC_OVALS)}
-
-    nw = N * (K // 32)
-    words = _lo32(bits64(keys[_SEC_SIGNS][:, None], torch.arange(nw, device=dev, dtype=torch.int64)[None, :]))
-    words = words.to(torch.int32).view(M, N, K // 32)   # low 32 bits, two's complement
-
-    nb = N * (K // 128)
-    sb = bits64(keys[_SEC_SCALES][:, None], torch.arange(nb, device=dev, dtype=torch.int64)[None, :])
-    scales = _table("scale16", dev)[_hi16(sb)].view(M, N, K // 128)
-
-    rs_bits = int(np.array([row_scale], dtype=np.float16).view(np.int16)[0])
-    cnt = n_outliers(K, outlier_frac)
-    if cnt > 0:
-        row_idx = torch.arange(N, device=dev, dtype=torch.int64)
-        row_keys = bits64(keys[_SEC_OCOLS][:, None], row_idx[None, :]).reshape(-1)
-        cols_all = _distinct_uniform(row_keys, cnt, K).view(M, N * cnt)
-        vb = bits64(keys[_SEC_OVALS][:, None], torch.arange(N * cnt, device=dev, dtype=torch.int64)[None, :])
-        nib_all = _lsr(vb, 60)                                  # 4 random bits = int4 two's complement
+    b = gen_matrix_bank(seed, ids, rows, cols, outlier_frac, row_scale, device)
     out = []
-    for m in range(M):
-        if cnt > 0:
-            cols_ = cols_all[m]
-            vals = _pack_nibbles(nib_all[m])
-        else:
-            cols_ = torch.zeros(0, dtype=torch.int64, device=dev)
-            vals = torch.zeros(0, dtype=torch.uint8, device=dev)
+    for m in range(len(ids)):
         out.append(CanonicalMatrix(
-            rows=N, cols=K,
-            signs=words[m].contiguous(),
-            block_scales=scales[m].contiguous(),
-            row_scales=torch.full((N,), rs_bits, dtype=torch.int16, device=dev),
-            row_ptr=(torch.arange(N + 1, device=dev, dtype=torch.int64) * cnt).to(torch.int32),
-            out_cols=cols_.to(torch.int32).to(torch.int16),
-            out_vals=vals,
+            rows=rows, cols=cols,
+            signs=b["signs"][m].contiguous(),
+            block_scales=b["block_scales"][m].contiguous(),
+            row_scales=b["row_scales"].clone(),
+            row_ptr=b["row_ptr"].clone(),
+            out_cols=b["out_cols"][m].contiguous(),
+            out_vals=b["out_vals"][m].contiguous(),
         ))
     return out
 

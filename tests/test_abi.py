@@ -122,3 +122,21 @@ def test_workspace_sizes_monotone():
     c = q.gemv_workspace_bytes(2048, 4096, 8, 1, 1)
     assert b > a and c == a and a % 256 == 0
     assert q.moe_workspace_bytes(32, 256, 6, 4096, 2048) > q.moe_workspace_bytes(1, 256, 6, 4096, 2048)
+
+
+def test_descriptor_refuses_null_sections():
+    # an empty torch slice has a NULL data pointer; the kernels read every outlier
+    # section in whole 16-byte chunks, so a descriptor must never carry one
+    z = torch.zeros(16, dtype=torch.uint8)
+    ok = q.PackedMatrix(16, 1024, torch.zeros(512, dtype=torch.int32), torch.zeros(128, dtype=torch.int16),
+                        torch.zeros(16, dtype=torch.int16), torch.zeros(17, dtype=torch.int32),
+                        z.view(torch.int16), z, nnz=0)
+    d = ok.descriptor()
+    assert d.out_cols and d.out_vals
+    bad = q.PackedMatrix(16, 1024, torch.zeros(512, dtype=torch.int32), torch.zeros(128, dtype=torch.int16),
+                         torch.zeros(16, dtype=torch.int16), torch.zeros(17, dtype=torch.int32),
+                         z.view(torch.int16)[:0], z[:0])
+    with pytest.raises(ValueError):
+        bad.descriptor()
+    assert B._padded16(torch.zeros(0, dtype=torch.int16)).numel() == 16
+    assert B._padded16(torch.zeros(9, dtype=torch.int16)).numel() == 32
