@@ -76,10 +76,13 @@ extern "C" {
  * Device layout of one packed matrix (produced by gale_pack_*), rows % 16 == 0,
  * cols % 1024 == 0, C = cols / 1024:
  *  signs         uint32 [rows/16][C][2][64][4]   (rows*cols/32 words, 16-byte aligned)
- *      word (t, c, h, l, e) holds, for row n = 16 t + (l % 16) and
- *      q = 8 (l / 16) + 4 h + e, bit (8 i + d) = b[n][1024 c + 128 d + 4 q + i],
- *      i in 0..3, d in 0..7.  One 2 KB tile = 16 rows x 1024 columns, read by one
- *      wavefront as two fully coalesced 1 KB dwordx4 loads.
+ *      word (t, c, h, l, e) holds, for row n = 16 t + (l % 16), g = l / 16 and
+ *      scale block d = 4 h + p (p in 0..3), bit (4 i + p) = b[n][1024 c + 128 d + kh],
+ *      kh = 64 (g % 2) + 16 (g / 2) + 32 (e / 2) + 8 (e % 2) + i, i in 0..7
+ *      (the element order of an fp4 operand of the 16x16x128 MFMA, so that one
+ *      AND of a word yields one operand dword of block d).  One 2 KB tile =
+ *      16 rows x 1024 columns, read by one wavefront as two fully coalesced 1 KB
+ *      dwordx4 loads.
  *  block_scales  fp16 [rows/16][C][16][8]: s[16 t + r][8 c + d] (16-byte aligned)
  *  row_scales    fp16 [rows]                 (canonical)
  *  row_ptr       int32 [rows + 1]            (canonical CSR offsets)

@@ -6,26 +6,28 @@
 
 namespace gale {
 
-// Bits of scale block d inside a device sign word: bit (8 i + d), i = 0..3.
+// Bits of scale block d inside one of its device sign words: bit 4 i + (d % 4), i = 0..7.
 __host__ __device__ inline uint32_t plane_bits(uint32_t w, int d) {
-  return w & (0x01010101u << d);
+  return w & (0x11111111u << (d & 3));
 }
 
-// fp8 e4m3 MFMA operand of plane d: four bytes, one per column 128 d + 4 q + i.
-//  d < 7: byte = b << d, the e4m3 pattern of b * 2^e_d (e_d = -9,-8,-7,-6,-5,-3,1);
-//         the MFMA's E8M0 B-scale 2^(1 - e_d) turns it into 2 b.
-//  d = 7: byte = 0x38 | (b << 7) = (1 - 2 b) * 1.0 (sign form, no scale).
+// fp4 e2m1 MFMA operand dword of block d from one of its words: eight nibbles, one per column.
+//  d % 4 < 3: nibble = b << (d % 4), the e2m1 pattern of b * 2^(d % 4 - 1) (0.5, 1, 2);
+//             the MFMA's E8M0 B-scale 2^(2 - d % 4) turns it into 2 b;
+//  d % 4 = 3: nibble = 0x2 | (b << 3) = (1 - 2 b) * 1.0 (sign form, no scale).
 template <int D>
 __device__ __forceinline__ uint32_t plane_operand(uint32_t w) {
-  if constexpr (D < 7) return w & (0x01010101u << D);
-  else return (w & 0x80808080u) | 0x38383838u;
+  if constexpr ((D & 3) < 3) return w & (0x11111111u << (D & 3));
+  else return (w & 0x88888888u) | 0x22222222u;
 }
 
-// E8M0 exponent byte of plane d's B-scale.
+template <int D>
+constexpr bool plane_is_binary() { return (D & 3) < 3; }
+
+// E8M0 exponent byte of block d's B-scale.
 template <int D>
 constexpr int plane_scale_e8m0() {
-  constexpr int e[7] = {-9, -8, -7, -6, -5, -3, 1};
-  if constexpr (D < 7) return 127 + 1 - e[D];
+  if constexpr ((D & 3) < 3) return 127 + 2 - (D & 3);
   else return 127;
 }
 

@@ -9,19 +9,19 @@
 //
 // gfx950 plan.  A 1-bit GEMV has ~1 VALU op per weight of budget at HBM speed,
 // too little for a per-bit select-and-add.  Instead each sign bit becomes one
-// byte of an fp8 MFMA operand with a single AND:
-//   * the device layout puts the 4 columns of scale block d that a byte covers
-//     at bit position d of the word's four bytes, so (w & 0x01010101 << d) is an
-//     fp8 e4m3 operand whose bytes are b * 2^e_d (b = sign bit), and the MFMA's
-//     E8M0 B-scale 2^(1 - e_d) makes them exactly 2 b; plane 7 uses the sign
-//     form (w & 0x80808080) | 0x38383838 = (1 - 2 b) * 1.0;
-//   * the activation enters as A = four e4m3 terms of X = x~ 2^p (rows of A),
-//     up to four tokens sharing the weights (so M = 4 terms x 4 tokens);
+// 4-bit element of an fp4 (e2m1) MFMA operand with a single AND:
+//   * the device layout puts eight columns of scale block d at bit position
+//     d % 4 of the eight nibbles of a word, so (w & 0x11111111 << d % 4) is an
+//     fp4 operand dword whose elements are b * 2^(d % 4 - 1) (b = sign bit), and
+//     the MFMA's E8M0 B-scale 2^(2 - d % 4) makes them exactly 2 b; blocks 3 and
+//     7 use the sign form (w & 0x88888888) | 0x22222222 = (1 - 2 b) * 1.0;
+//   * the activation enters as A = four fp8 e4m3 terms of X = x~ 2^p (rows of
+//     A), up to four tokens sharing the weights (so M = 4 terms x 4 tokens);
 //   * the block sums S = sum_k X (one MFMA against an all -1.0 operand when the
 //     activation changes) turn the 0/1 planes into signs: block d adds
 //     s[n][d] (S - 2 sum_k b X).
 // One v_mfma_scale_f32_16x16x128_f8f6f4 therefore consumes one scale block of
-// 16 rows: 2048 weights for 8 ANDs and two FMAs per lane.
+// 16 rows: 2048 weights for 4 ANDs (8 in sign form) and two FMAs per lane.
 //
 // Work split.  A unit is R row tiles (16 rows each) of one work item (a matrix,
 // or the w1/w3 pair of an expert, with up to four activation vectors).  A
@@ -79,19 +79,24 @@ __device__ __forceinline__ uint4 stream_load16(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// fp4 B operand of block D: the four words of its half, masked (the upper four
+// dwords of the operand are unused for fp4).
 template <int D>
 __device__ __forceinline__ v8i plane_vec(const uint32_t w[8]) {
-  v8i b;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) b[j] = (int)plane_operand<D>(w[j]);
-  return b;
+  constexpr int h = D >> 2;
+  return v8i{(int)plane_operand<D>(w[4 * h + 0]), (int)plane_operand<D>(w[4 * h + 1]),
+             (int)plane_operand<D>(w[4 * h + 2]), (int)plane_operand<D>(w[4 * h + 3]), 0, 0, 0, 0};
 }
 
 template <int D>
 __device__ __forceinline__ v4f plane_mfma(const v8i& a, const uint32_t w[8], const v4f& c) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, plane_vec<D>(w), c, 0, 0, 0, 127, 0,
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, plane_vec<D>(w), c, 0, 4, 0, 127, 0,
                                                           plane_scale_e8m0<D>());
 }
+
+// Index of a 0/1 block among the six that need the block sum (blocks 3 and 7 do not).
+template <int D>
+constexpr int binary_slot() { return D - (D >> 2); }
 
 // Item of a unit, decoded without dynamically indexed arrays.
 struct Item {
@@ -250,7 +255,7 @@ __device__ __forceinline__ void issue_unit(const GemvParams& P, const Geo& G, in
 
 struct Act {
   v8i A[8];              // e4m3 terms, one operand per scale block of the chunk
-  float S[7][4];         // -sum over each of the blocks 0..6, per slot (plane 7 needs none)
+  float S[6][4];         // -sum over each 0/1 block (0, 1, 2, 4, 5, 6), per slot
   int pexp[4];
 };
 
@@ -279,23 +284,24 @@ __device__ __forceinline__ void load_activation(const GemvParams& P, const Geo& 
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int d = 0; d < 7; ++d) {
+    if (d == 3) continue;
     const v4f s = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a.A[d], neg1, zero, 0, 0, 0, 127, 0, 127);
 #pragma unroll
-    for (int i = 0; i < NS; ++i) a.S[d][i] = s[i];
+    for (int i = 0; i < NS; ++i) a.S[d - (d >> 2)][i] = s[i];
   }
 }
 
-// One plane: D = 2 sum_k b X (planes 0..6, via the E8M0 scale) or sum_k (1 - 2 b) X (plane 7).
-// Block contribution s (S - 2 P): acc += -s D - s (-S) for d < 7; acc += s D for d = 7.
+// One block: D = 2 sum_k b X (0/1 blocks, via the E8M0 scale) or sum_k (1 - 2 b) X (sign blocks 3, 7).
+// Block contribution s (S - 2 P): acc += -s D - s (-S) for a 0/1 block; acc += s D for a sign block.
 template <int NS, int D>
 __device__ __forceinline__ void plane_step(const Act& a, const uint32_t w[8], float s, float* acc) {
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
   const v4f r = plane_mfma<D>(a.A[D], w, zero);
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
-    if constexpr (D < 7) {
+    if constexpr (plane_is_binary<D>()) {
       acc[i] = fmaf(-s, r[i], acc[i]);
-      acc[i] = fmaf(-s, a.S[D][i], acc[i]);
+      acc[i] = fmaf(-s, a.S[binary_slot<D>()][i], acc[i]);
     } else {
       acc[i] = fmaf(s, r[i], acc[i]);
     }

@@ -13,25 +13,32 @@ namespace gale {
 // ---------------------------------------------------------------------------
 // Device layout index map (host and device).  A "tile" is 16 rows x 1024
 // columns; C = cols / 1024 chunks per row tile.  Within a tile, lane l of a
-// wavefront owns row (l % 16) and word group g = l / 16; its 8 words
-// q = 8 g + j (j = 0..7) sit at half h = j / 4, element e = j % 4.  Bit
-// (8 i + d) of word q is the sign of column 128 d + 4 q + i of the chunk, so
-// masking one bit position d of every byte selects exactly scale block d.
+// wavefront owns row (l % 16) and lane group g = l / 16; its 8 words sit at
+// half h = 0, 1 (element e = 0..3 of each half).  Word 4 h + j holds four scale
+// blocks d = 4 h + p (p = 0..3) at bit positions 4 i + p, i = 0..7: masking one
+// bit position of every nibble selects exactly one scale block, as the eight
+// 4-bit elements of one dword of an fp4 MFMA operand.  The column of (g, j, i)
+// within block d follows the fp4 operand order of the 16x16x128 MFMA:
+//   kh = 64 (g & 1) + 16 (g >> 1) + 32 (j >> 1) + 8 (j & 1) + i.
 // ---------------------------------------------------------------------------
 __host__ __device__ inline int64_t sign_word_index(int t, int c, int C, int h, int l, int e) {
   return ((((int64_t)t * C + c) * 2 + h) * 64 + l) * 4 + e;
 }
 
+__host__ __device__ inline int fp4_col(int g, int j, int i) {
+  return 64 * (g & 1) + 16 * (g >> 1) + 32 * (j >> 1) + 8 * (j & 1) + i;
+}
+
 // canonical (n, k) -> (device word index, bit position)
 __host__ __device__ inline void sign_position(int n, int k, int C, int64_t* word, int* bit) {
-  int t = n >> 4, nl = n & 15;
-  int c = k >> 10, kk = k & 1023;
-  int d = kk >> 7, rem = kk & 127;
-  int q = rem >> 2, i = rem & 3;
-  int g = q >> 3, j = q & 7;
-  int l = 16 * g + nl;
-  *word = sign_word_index(t, c, C, j >> 2, l, j & 3);
-  *bit = 8 * i + d;
+  const int t = n >> 4, nl = n & 15;
+  const int c = k >> 10, kk = k & 1023;
+  const int d = kk >> 7, kh = kk & 127;
+  const int i = kh & 7;
+  const int j = ((kh >> 3) & 1) | (((kh >> 5) & 1) << 1);
+  const int g = ((kh >> 6) & 1) | (((kh >> 4) & 1) << 1);
+  *word = sign_word_index(t, c, C, d >> 2, 16 * g + nl, j);
+  *bit = 4 * i + (d & 3);
 }
 
 __host__ __device__ inline int64_t scale_index(int n, int blk, int C) {

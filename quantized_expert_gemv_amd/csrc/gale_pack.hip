@@ -27,16 +27,17 @@ __global__ void pack_signs_kernel(int rows, int cols, int n_mat, const uint32_t*
     const int t = (int)(w / C);
     const int n = 16 * t + (l & 15);
     const int g = l >> 4;
-    const int q = 8 * g + 4 * h + e;
     const uint32_t* row = cs + m * words + (int64_t)n * (cols >> 5);
+    // word (h, e) holds blocks d = 4 h + p at bits 4 i + p; its eight columns of block d
+    // are the contiguous run 128 d + fp4_col(g, e, 0) + i, one byte of a canonical word
+    const int base = fp4_col(g, e, 0);
     uint32_t out = 0;
 #pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      // columns 1024 c + 128 d + 4 q + i, i = 0..3: word 32 c + 4 d + q / 8, bits 4 (q % 8) + i
-      const uint32_t cw = row[32 * c + 4 * d + (q >> 3)];
-      const uint32_t nib = (cw >> (4 * (q & 7))) & 0xFu;
+    for (int p = 0; p < 4; ++p) {
+      const int col = 1024 * c + 128 * (4 * h + p) + base;
+      const uint32_t byte = (row[col >> 5] >> (col & 31)) & 0xFFu;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) out |= ((nib >> i) & 1u) << (8 * i + d);
+      for (int i = 0; i < 8; ++i) out |= ((byte >> i) & 1u) << (4 * i + p);
     }
     ds[gid] = out;
   }
@@ -88,15 +89,18 @@ __global__ void debug_unpack_kernel(int rows, int cols, const uint32_t* __restri
   for (int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gid < total;
        gid += (int64_t)gridDim.x * blockDim.x) {
     const int n = (int)(gid / (cols >> 5));
-    const int kw = (int)(gid - (int64_t)n * (cols >> 5));   // = 32 c + 4 d + g
-    const int c = kw >> 5, d = (kw >> 2) & 7, g = kw & 3;
-    const int t = n >> 4, l = 16 * g + (n & 15);
+    const int kw = (int)(gid - (int64_t)n * (cols >> 5));   // = 32 c + 4 d + q
+    const int c = kw >> 5, d = (kw >> 2) & 7, q = kw & 3;
+    const int t = n >> 4;
     uint32_t out = 0;
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t w = ds[sign_word_index(t, c, C, j >> 2, l, j & 3)];
-      const uint32_t bits = plane_bits(w, d);          // the kernel's plane mask, bits at 8 i + d
+    for (int bb = 0; bb < 4; ++bb) {
+      // columns 128 d + 32 q + 8 bb + i: fp4 operand dword j, lane group g, nibble i
+      const int j = (bb & 1) | ((q & 1) << 1);
+      const int g = (q >> 1) | (((bb >> 1) & 1) << 1);
+      const uint32_t w = ds[sign_word_index(t, c, C, d >> 2, 16 * g + (n & 15), j)];
+      const uint32_t bits = plane_bits(w, d);          // the kernel's block mask, bits at 4 i + d % 4
 #pragma unroll
-      for (int i = 0; i < 4; ++i) out |= ((bits >> (8 * i + d)) & 1u) << (4 * j + i);
+      for (int i = 0; i < 8; ++i) out |= ((bits >> (4 * i + (d & 3))) & 1u) << (8 * bb + i);
     }
     cs[gid] = out;
   }

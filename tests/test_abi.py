@@ -55,11 +55,27 @@ def test_host_pack_roundtrip(rows, cols):
     assert torch.equal(cs, m.signs) and torch.equal(csc, m.block_scales)
 
 
+def _fp4_operand_column(g, j, i):
+    # column inside a 128-column block of nibble i of dword j held by lane group g of a
+    # 16x16x128 fp4 MFMA B operand (measured on gfx950 with one-hot operands)
+    return 64 * (g & 1) + 16 * (g >> 1) + 32 * (j >> 1) + 8 * (j & 1) + i
+
+
+def test_fp4_operand_order_is_a_bijection():
+    cols = sorted(_fp4_operand_column(g, j, i) for g in range(4) for j in range(4) for i in range(8))
+    assert cols == list(range(128))
+
+
 def test_host_pack_plane_structure():
-    # bit (8 i + d) of a device word is column 1024 c + 128 d + 4 q + i: a single canonical
-    # bit must land in the word of lane 16 g + n % 16 at plane position d
+    # bit (4 i + d % 4) of word 4 (d // 4) + j of lane 16 g + n % 16 is column
+    # 128 d + kh(g, j, i) of row n: a single canonical bit must land exactly there
     rows, cols = 16, 1024
-    for (n, k) in [(0, 0), (5, 130), (15, 1023), (3, 4 * 9 + 2 + 128 * 6)]:
+    expect = {}
+    for g in range(4):
+        for j in range(4):
+            for i in range(8):
+                expect[_fp4_operand_column(g, j, i)] = (g, j, i)
+    for (n, k) in [(0, 0), (5, 130), (15, 1023), (3, 4 * 9 + 2 + 128 * 6), (9, 128 * 3 + 77)]:
         s = torch.zeros(rows, cols // 32, dtype=torch.int32)
         s[n, k // 32] = np.int32(np.uint32(1 << (k % 32)).view(np.int32))
         ds, _ = q.pack_host(rows, cols, s, torch.zeros(rows, cols // 128, dtype=torch.int16))
@@ -67,12 +83,11 @@ def test_host_pack_plane_structure():
         assert nz.numel() == 1
         w = int(nz[0])
         word = int(ds.view(-1)[w].item()) & 0xFFFFFFFF
-        d, rem = (k % 1024) // 128, k % 128
-        qq, i = rem // 4, rem % 4
-        g, j = qq // 8, qq % 8
+        d = (k % 1024) // 128
+        g, j, i = expect[k % 128]
         lane = 16 * g + n % 16
-        assert w == ((0 * 2 + j // 4) * 64 + lane) * 4 + j % 4
-        assert word == 1 << (8 * i + d)
+        assert w == ((0 * 2 + d // 4) * 64 + lane) * 4 + j
+        assert word == 1 << (4 * i + d % 4)
 
 
 def test_check_canonical_rejects_bad_csr():
