@@ -15,10 +15,18 @@ Reported:
                timed with HIP events; algorithmic bytes 1,405,952 per matrix
   cpu_baseline the fp64 oracle on the host for a bounded sample of the same step
                (its outputs also check the GPU step at full size)
+  stream_ceiling  a plain elementwise kernel (negate, fp32) over a 1 GiB buffer: the
+               HBM rate a trivial streaming kernel reaches on this device; it is also the
+               known-size reference that scales the HBM byte counters behind "traffic"
+
+"traffic" is read from profiles/gemv_kernel_traffic.txt, written from two rocprofv3
+--pmc runs (FETCH_SIZE, WRITE_SIZE) of this script; it is reported only while the
+SHA-256 of the GEMV kernel sources still matches the one recorded there.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -33,6 +41,30 @@ W2_BYTES = 1_392_640           # one [4096, 2048] matrix, 20 outliers per row
 EXPERT_BYTES = 2 * W13_BYTES + W2_BYTES
 GEMV_UNIT_BYTES = W13_BYTES + 2 * HIDDEN + 2 * INTER   # weights + fp16 x + fp16 y
 HBM_PEAK_GBPS = 8000.0
+CEIL_BYTES = 1 << 30            # one side of the streaming-ceiling kernel
+GEMV_SOURCES = ("gale_gemv.hip", "gale_decode.h", "gale_internal.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_kernel_traffic.txt")
+
+
+def gemv_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in GEMV_SOURCES:
+        with open(os.path.join(ROOT, "quantized_expert_gemv_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(n_mats: int):
+    """HBM bytes per sustained-GEMV launch from the committed counter summary, or None
+    when it is absent, was taken at another launch size, or predates the kernel sources."""
+    try:
+        kv = dict(l.split(":", 1) for l in open(TRAFFIC_FILE).read().splitlines() if ":" in l)
+        kv = {k.strip(): v.strip() for k, v in kv.items()}
+        if kv.get("source_sha256") != gemv_source_hash() or int(kv.get("matrices_per_launch", -1)) != n_mats:
+            return None
+        return int(kv["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def log(msg: str) -> None:
@@ -117,7 +149,7 @@ def main() -> int:
     ap.add_argument("--layers", type=int, default=43)
     ap.add_argument("--gemv-mats", type=int, default=1024)
     ap.add_argument("--gemv-reps", type=int, default=20)
-    ap.add_argument("--cpu-layers", type=int, default=2)
+    ap.add_argument("--cpu-layers", type=int, default=16)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     args = ap.parse_args()
@@ -223,6 +255,18 @@ def main() -> int:
     log(f"sustained GEMV: {n} matrices in {ms_gemv * 1e3:.1f} us -> {gemv_gbps:.0f} GB/s "
         f"({100 * gemv_gbps / HBM_PEAK_GBPS:.1f}% of 8 TB/s)")
 
+    # ---- streaming ceiling: a plain elementwise kernel of known size (read 1 GiB, write 1 GiB)
+    src = torch.ones(CEIL_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    ms_ceil = time_events(lambda: torch.neg(src, out=dst), 10)
+    ceil_gbps = 2 * CEIL_BYTES / (ms_ceil * 1e-3) / 1e9
+    del src, dst
+    log(f"streaming ceiling (elementwise negate, 2 x 1 GiB): {ceil_gbps:.0f} GB/s")
+    traffic = recorded_traffic(n)
+
     out = {
         "metric": "packed-weight GB/s & % HBM peak; tokens/s per 43-layer MoE expert stack",
         "value": round(gbps, 2),
@@ -234,7 +278,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8-e4m3 MFMA (4-term activation split), fp32 accumulate, fp16 io",
+        "dtype": "fp8-e4m3 x fp4-e2m1 MFMA (exact 0/1 sign planes, 4-term fp8 activation split), fp32 accumulate, fp16 io",
         "data": "synthetic (seeded DeepSeek-V4-Flash-shaped GALE 1-bit experts; no weights)",
         "config": {"workload": f"decode batch 1 through the resident {L}-layer GALE expert stack "
                                f"({L} x 256 experts x w1/w3 [2048,4096] + w2 [4096,2048], "
@@ -247,10 +291,13 @@ def main() -> int:
         "ms_per_step_graph": None if ms_graph is None else round(ms_graph, 5),
         "bytes_per_token": bytes_per_token,
         "roofline": {"bound": "hbm", "achieved": round(gemv_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(gemv_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "gemv_kernel (sign-plane fp8 MFMA GEMV)",
+                     "frac": round(gemv_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "kernel": "gemv_kernel<1,4,false> (fp4 sign-plane MFMA GEMV)",
                      "launch": f"{n} distinct [2048,4096] matrices x 1 token, prepared activations",
-                     "bytes_per_launch": n * GEMV_UNIT_BYTES, "avg_launch_us": round(ms_gemv * 1e3, 2)},
+                     "bytes_per_launch": n * GEMV_UNIT_BYTES, "avg_launch_us": round(ms_gemv * 1e3, 2),
+                     "source_sha256": gemv_source_hash()[:16]},
+        "stream_ceiling": {"value": round(ceil_gbps, 1), "unit": "GB/s",
+                           "kernel": "torch.neg fp32, read 1 GiB + write 1 GiB"},
     }
 
     if not args.no_cpu:
