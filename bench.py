@@ -41,6 +41,9 @@ W2_BYTES = 1_392_640           # one [4096, 2048] matrix, 20 outliers per row
 EXPERT_BYTES = 2 * W13_BYTES + W2_BYTES
 GEMV_UNIT_BYTES = W13_BYTES + 2 * HIDDEN + 2 * INTER   # weights + fp16 x + fp16 y
 HBM_PEAK_GBPS = 8000.0
+PREFILL_TOKENS = 2048
+PREFILL_FLOP = 2 * TOPK * PREFILL_TOKENS * 3 * INTER * HIDDEN      # dense-equivalent, 618.5 GFLOP
+MFMA_FP16_PEAK_TFLOPS = 2500.0
 CEIL_BYTES = 1 << 30            # one side of the streaming-ceiling kernel
 GEMV_SOURCES = ("gale_gemv.hip", "gale_decode.h", "gale_internal.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_kernel_traffic.txt")
@@ -149,6 +152,7 @@ def main() -> int:
     ap.add_argument("--layers", type=int, default=43)
     ap.add_argument("--gemv-mats", type=int, default=1024)
     ap.add_argument("--gemv-reps", type=int, default=20)
+    ap.add_argument("--prefill-reps", type=int, default=5)
     ap.add_argument("--cpu-layers", type=int, default=16)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
@@ -162,7 +166,7 @@ def main() -> int:
     import torch
     import quantized_expert_gemv_amd as q
     import synth
-    from synth import config_seed, gen_logits_normal, gen_x
+    from synth import config_seed, gen_logits_normal, gen_logits_zipf, gen_x
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -230,6 +234,29 @@ def main() -> int:
     bytes_per_token = 43 * TOPK * EXPERT_BYTES * L // 43
     gbps = bytes_per_token / (ms_step * 1e-3) / 1e9
 
+    # ---- grouped prefill: one layer of the stack, 2048 tokens, Zipf(1.1)-skewed top-6
+    xp = gen_x(seed, (0x40000,), PREFILL_TOKENS, HIDDEN, device=dev)
+    lgp = gen_logits_zipf(seed, (0x40000,), PREFILL_TOKENS, EXPERTS, device=dev)
+    ypf = torch.empty(PREFILL_TOKENS, HIDDEN, dtype=torch.float16, device=dev)
+    wsp = torch.empty(q.moe_workspace_bytes(PREFILL_TOKENS, EXPERTS, TOPK, HIDDEN, INTER, 0), dtype=torch.uint8,
+                      device=dev)
+
+    def prefill():
+        rc = lib.gale_moe_layer_fwd(HIDDEN, INTER, tables[0].ptr(), EXPERTS, lgp.data_ptr(), TOPK, xp.data_ptr(),
+                                    PREFILL_TOKENS, ypf.data_ptr(), None, None, wsp.data_ptr(), wsp.numel(), 0,
+                                    torch.cuda.current_stream().cuda_stream)
+        if rc:
+            raise RuntimeError(lib.gale_last_error().decode())
+
+    for _ in range(2):
+        prefill()
+    torch.cuda.synchronize()
+    ms_prefill = time_events(prefill, args.prefill_reps)
+    prefill_tflops = PREFILL_FLOP / (ms_prefill * 1e-3) / 1e12
+    log(f"grouped prefill: {PREFILL_TOKENS} tokens in {ms_prefill:.3f} ms -> "
+        f"{PREFILL_TOKENS / ms_prefill * 1e3:.0f} tokens/s, {prefill_tflops:.1f} dense-equivalent TFLOP/s")
+    del wsp
+
     # ---- sustained GEMV: one launch over n distinct resident matrices, one token each
     n = min(args.gemv_mats, len(w1_all) // 2)
     sets = [q.matrix_table(w1_all[i * n:(i + 1) * n]) for i in range(2)]     # two disjoint sets, alternated
@@ -296,6 +323,11 @@ def main() -> int:
                      "launch": f"{n} distinct [2048,4096] matrices x 1 token, prepared activations",
                      "bytes_per_launch": n * GEMV_UNIT_BYTES, "avg_launch_us": round(ms_gemv * 1e3, 2),
                      "source_sha256": gemv_source_hash()[:16]},
+        "prefill": {"workload": f"one layer (256 experts), {PREFILL_TOKENS} tokens x hidden {HIDDEN} fp16, "
+                                f"Zipf(1.1) top-6 routing, grouped path",
+                    "ms": round(ms_prefill, 4), "tokens_per_s": round(PREFILL_TOKENS / ms_prefill * 1e3, 1),
+                    "dense_equiv_tflops": round(prefill_tflops, 2),
+                    "frac_of_fp16_mfma_peak": round(prefill_tflops / MFMA_FP16_PEAK_TFLOPS, 4)},
         "stream_ceiling": {"value": round(ceil_gbps, 1), "unit": "GB/s",
                            "kernel": "torch.neg fp32, read 1 GiB + write 1 GiB"},
     }

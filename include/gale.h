@@ -61,7 +61,7 @@ extern "C" {
 #define GALE_X_ROTATED    0x1u   /* x is already H.x (fp32 or fp16); skip the rotation */
 #define GALE_X_PREPARED   0x2u   /* gale_expert_gemv: x holds records from gale_prepare_activations */
 #define GALE_PATH_DECODE  0x10u  /* gale_moe_layer_fwd: force the per-expert GEMV path */
-#define GALE_PATH_GROUPED 0x20u  /* gale_moe_layer_fwd: force the grouped MFMA path */
+#define GALE_PATH_GROUPED 0x20u  /* gale_moe_layer_fwd: force the grouped (token-sorted) path */
 
 /* ---- limits -------------------------------------------------------------- */
 #define GALE_FWHT_N        1024   /* rotation block ("blocked FWHT-1024") */
@@ -216,8 +216,14 @@ size_t gale_moe_workspace_bytes(int32_t n_tok, int32_t n_experts, int32_t top_k,
  *          [n_tok][n_experts]); w[t] = softmax of those k logits (fp32).
  *   y[t] = sum over slots j = 0..top_k-1, in order, of w[t][j] * FFN_{S_t[j]}(x[t]).
  * x, y: fp16 [n_tok][hidden].  topk_idx (int32 [n_tok][top_k]) and topk_w (fp32) are
- * written when non-NULL.  Path: decode (per-expert GEMV) when n_tok <= 64, grouped MFMA
- * otherwise; flags GALE_PATH_DECODE / GALE_PATH_GROUPED force one. */
+ * written when non-NULL.  Two paths, same results bit for bit on any token:
+ *   decode  (n_tok <= 64): one workgroup routes all tokens and lists the work items;
+ *   grouped (n_tok > 64):  chunked top-k, a stable sort of the (token, slot) pairs by
+ *           expert, then work items of up to 4 pairs of one expert each, so that an
+ *           expert's weights are streamed once per 4 of its tokens.
+ * Flags GALE_PATH_DECODE / GALE_PATH_GROUPED force a path (decode takes at most 64
+ * tokens).  The workspace depends on the path (gale_moe_workspace_bytes with the same
+ * flags). */
 int gale_moe_layer_fwd(int32_t hidden, int32_t inter, const gale_expert* experts_dev,
                        int32_t n_experts, const float* logits, int32_t top_k, const void* x,
                        int32_t n_tok, void* y, int32_t* topk_idx, float* topk_w,

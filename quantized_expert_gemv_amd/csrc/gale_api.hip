@@ -92,13 +92,13 @@ static FfnWs ffn_ws(int hidden, int inter, int64_t n_x, int64_t n_pairs) {
 }
 
 struct MoeWs {
-  size_t idx, w, offsets, perm, items, n_items, ra_x, h, ra_h, yp, total;
+  size_t idx, w, offsets, perm, chunk, items, n_items, ra_x, h, ra_h, yp, total;
 };
 static int64_t moe_item_bound(int T, int E, int k, int slots) {
   const int64_t P = (int64_t)T * k;
   return std::min<int64_t>(E, P) + (P + slots - 1) / slots;
 }
-static MoeWs moe_ws(int T, int E, int k, int hidden, int inter) {
+static MoeWs moe_ws(int T, int E, int k, int hidden, int inter, bool grouped) {
   MoeWs w;
   const int64_t P = (int64_t)T * k;
   const int slots = pick_slots(T);
@@ -107,6 +107,7 @@ static MoeWs moe_ws(int T, int E, int k, int hidden, int inter) {
   w.w = o; o += align256(4 * P);
   w.offsets = o; o += align256(4 * (size_t)(E + 1));
   w.perm = o; o += align256(4 * P);
+  w.chunk = o; o += grouped ? align256(route_chunk_count_bytes(T, E)) : 0;
   w.items = o; o += align256(sizeof(WorkItem) * (size_t)moe_item_bound(T, E, k, slots));
   w.n_items = o; o += 256;
   w.ra_x = o; o += align256(ra_bytes(hidden) * (size_t)T);
@@ -398,8 +399,7 @@ extern "C" size_t gale_moe_workspace_bytes(int32_t n_tok, int32_t n_experts, int
                                            int32_t inter, uint32_t flags) {
   if (n_tok < 1 || n_experts < 1 || top_k < 1 || hidden < 1024 || inter < 1024) return 0;
   const bool grouped = (flags & GALE_PATH_GROUPED) || (!(flags & GALE_PATH_DECODE) && n_tok > GALE_MAX_DECODE_TOKENS);
-  if (grouped) return prefill_workspace_bytes(n_tok, n_experts, top_k, hidden, inter);
-  return moe_ws(n_tok, n_experts, top_k, hidden, inter).total;
+  return moe_ws(n_tok, n_experts, top_k, hidden, inter, grouped).total;
 }
 
 extern "C" int gale_moe_layer_fwd(int32_t hidden, int32_t inter, const gale_expert* experts_dev,
@@ -423,17 +423,11 @@ extern "C" int gale_moe_layer_fwd(int32_t hidden, int32_t inter, const gale_expe
   }
   if ((flags & GALE_PATH_DECODE) && (flags & GALE_PATH_GROUPED)) { set_error("%s: both paths forced", fn); return GALE_ERR_SHAPE; }
   const bool grouped = (flags & GALE_PATH_GROUPED) || (!(flags & GALE_PATH_DECODE) && n_tok > GALE_MAX_DECODE_TOKENS);
-  if (grouped) {
-    const size_t need = prefill_workspace_bytes(n_tok, n_experts, top_k, hidden, inter);
-    if (ws_bytes < need) { set_error("%s: workspace %zu < %zu bytes", fn, ws_bytes, need); return GALE_ERR_WORKSPACE; }
-    return run_prefill(hidden, inter, experts_dev, n_experts, logits, top_k, x, n_tok, y, topk_idx, topk_w, ws,
-                       ws_bytes, stream);
-  }
-  if (n_tok > GALE_MAX_DECODE_TOKENS) {
+  if (!grouped && n_tok > GALE_MAX_DECODE_TOKENS) {
     set_error("%s: the decode path takes at most %d tokens", fn, GALE_MAX_DECODE_TOKENS);
     return GALE_ERR_SHAPE;
   }
-  const MoeWs W = moe_ws(n_tok, n_experts, top_k, hidden, inter);
+  const MoeWs W = moe_ws(n_tok, n_experts, top_k, hidden, inter, grouped);
   if (ws_bytes < W.total) { set_error("%s: workspace %zu < %zu bytes", fn, ws_bytes, W.total); return GALE_ERR_WORKSPACE; }
   uint8_t* base = reinterpret_cast<uint8_t*>(ws);
   int32_t* idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(base + W.idx);
@@ -447,8 +441,18 @@ extern "C" int gale_moe_layer_fwd(int32_t hidden, int32_t inter, const gale_expe
   const int P = n_tok * top_k;
   const int slots = pick_slots(n_tok);
   const gale_matrix* table = reinterpret_cast<const gale_matrix*>(experts_dev);
-  st = hip_status(fn, launch_route_small(logits, n_tok, n_experts, top_k, idx, wts, nullptr, nullptr, items, n_items,
-                                         slots, stream));
+  if (grouped) {
+    // chunked top-k, stable sort of the pairs by expert, then the per-expert work items
+    int32_t* offsets = reinterpret_cast<int32_t*>(base + W.offsets);
+    int32_t* perm = reinterpret_cast<int32_t*>(base + W.perm);
+    st = hip_status(fn, launch_route_large(logits, n_tok, n_experts, top_k, idx, wts,
+                                           reinterpret_cast<int32_t*>(base + W.chunk), offsets, perm, stream));
+    if (st) return st;
+    st = hip_status(fn, launch_build_items(offsets, perm, n_experts, slots, items, n_items, stream));
+  } else {
+    st = hip_status(fn, launch_route_small(logits, n_tok, n_experts, top_k, idx, wts, nullptr, nullptr, items,
+                                           n_items, slots, stream));
+  }
   if (st) return st;
   st = hip_status(fn, launch_prep(x, GALE_F16, hidden, n_tok, hidden, 0, ra_x, ra_bytes(hidden), stream));
   if (st) return st;

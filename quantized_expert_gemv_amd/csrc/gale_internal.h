@@ -127,11 +127,9 @@ hipError_t launch_combine(const float* ypairs, const float* w, int n_tok, int k,
                           void* y, int y_dtype, hipStream_t s);
 hipError_t launch_cast(const float* src, void* dst, int dst_dtype, int64_t n, hipStream_t s);
 
-// grouped prefill path
-size_t prefill_workspace_bytes(int n_tok, int n_exp, int k, int hidden, int inter);
-int run_prefill(int hidden, int inter, const gale_expert* experts, int n_exp,
-                       const float* logits, int k, const void* x, int n_tok, void* y,
-                       int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes, hipStream_t s);
+// grouped path: work items of at most `slots` pairs per expert from the sorted pairs
+hipError_t launch_build_items(const int32_t* offsets, const int32_t* perm, int n_exp, int slots, WorkItem* items,
+                              int32_t* n_items, hipStream_t s);
 
 void set_error(const char* fmt, ...);
 

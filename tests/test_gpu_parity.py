@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import oracle as O
-from synth import CanonicalMatrix, config_seed, gen_logits_normal, gen_matrices, gen_matrix, gen_x
+from synth import CanonicalMatrix, config_seed, gen_logits_normal, gen_logits_zipf, gen_matrices, gen_matrix, gen_x
 
 pytestmark = pytest.mark.gpu
 
@@ -323,6 +323,48 @@ def test_moe_decode_layer(q, layer, T):
     err = O.rel_l2(np_of(y[sample]), yref).max()
     print(f"moe T={T} rel-L2 {err:.3e}")
     assert err <= REL_L2_BAR
+
+
+def test_moe_grouped_equals_decode_bitwise(q, layer):
+    # both paths compute each token independently, so forcing the grouped (token-sorted)
+    # path on a decode-sized batch must reproduce the decode path bit for bit
+    seed, canon, tab = layer
+    T = 48
+    x = gen_x(seed, (2000, T), T, 4096, device=DEV)
+    lg = gen_logits_normal(seed, (2000, T), T, 256, device=DEV)
+    yd, idd, wd = q.moe_layer_fwd(tab, 4096, 2048, lg, x, top_k=6, flags=q.GALE_PATH_DECODE)
+    yg, idg, wg = q.moe_layer_fwd(tab, 4096, 2048, lg, x, top_k=6, flags=q.GALE_PATH_GROUPED)
+    assert torch.equal(idd, idg) and torch.equal(wd, wg)
+    assert torch.equal(yd, yg)
+
+
+@pytest.mark.parametrize("T,zipf", [(65, False), (2048, True)])
+def test_moe_grouped_prefill(q, layer, T, zipf):
+    """Grouped path at a ragged size just past the decode limit and at the prefill
+    workload (2048 tokens, Zipf(1.1)-skewed top-6 of 256): routing exact for every
+    token, sampled tokens against the oracle, the leading 64 tokens bit-identical to
+    the decode path run on them alone, and run-to-run determinism."""
+    seed, canon, tab = layer
+    x = gen_x(seed, (3000, T), T, 4096, device=DEV)
+    gen = gen_logits_zipf if zipf else gen_logits_normal
+    lg = gen(seed, (3000, T), T, 256, device=DEV)
+    y, idx, w = q.moe_layer_fwd(tab, 4096, 2048, lg, x, top_k=6)
+    y2, _, _ = q.moe_layer_fwd(tab, 4096, 2048, lg, x, top_k=6)
+    assert torch.equal(y, y2)
+    ridx, rw = O.route(lg.cpu().numpy(), 6)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert np.abs(w.cpu().numpy() - rw).max() <= 1e-6
+    counts = np.bincount(ridx.ravel(), minlength=256)
+    hot = int(np.argmax(counts))
+    t_hot = int(np.nonzero((ridx == hot).any(axis=1))[0][-1])     # last token of the busiest expert
+    sample = sorted({0, T // 2, T - 1, t_hot})
+    expert_of = lambda e: tuple(m.numpy() for m in canon[e])  # noqa: E731
+    yref, _, _ = O.moe(expert_of, lg.cpu().numpy()[sample], x.cpu().numpy()[sample], k=6)
+    err = O.rel_l2(np_of(y[sample]), yref).max()
+    print(f"grouped T={T} max expert load {counts.max()} rel-L2 {err:.3e}")
+    assert err <= REL_L2_BAR
+    yd, _, _ = q.moe_layer_fwd(tab, 4096, 2048, lg[:64].contiguous(), x[:64].contiguous(), top_k=6)
+    assert torch.equal(yd, y[:64])
 
 
 def test_moe_closed_form(q):
