@@ -94,9 +94,11 @@ static FfnWs ffn_ws(int hidden, int inter, int64_t n_x, int64_t n_pairs) {
 struct MoeWs {
   size_t idx, w, offsets, perm, chunk, items, n_items, ra_x, h, ra_h, yp, total;
 };
+// Upper bound on the work items of T tokens: every item holds at least one pair, and
+// each expert's run of pairs ends in at most one partly filled item.
 static int64_t moe_item_bound(int T, int E, int k, int slots) {
   const int64_t P = (int64_t)T * k;
-  return std::min<int64_t>(E, P) + (P + slots - 1) / slots;
+  return std::min<int64_t>(P, std::min<int64_t>(E, P) + (P + slots - 1) / slots);
 }
 static MoeWs moe_ws(int T, int E, int k, int hidden, int inter, bool grouped) {
   MoeWs w;
@@ -449,12 +451,12 @@ extern "C" int gale_moe_layer_fwd(int32_t hidden, int32_t inter, const gale_expe
                                            reinterpret_cast<int32_t*>(base + W.chunk), offsets, perm, stream));
     if (st) return st;
     st = hip_status(fn, launch_build_items(offsets, perm, n_experts, slots, items, n_items, stream));
+    if (st) return st;
+    st = hip_status(fn, launch_prep(x, GALE_F16, hidden, n_tok, hidden, 0, ra_x, ra_bytes(hidden), stream));
   } else {
-    st = hip_status(fn, launch_route_small(logits, n_tok, n_experts, top_k, idx, wts, nullptr, nullptr, items,
-                                           n_items, slots, stream));
+    st = hip_status(fn, launch_route_prep(logits, n_tok, n_experts, top_k, idx, wts, items, n_items, slots, x,
+                                          GALE_F16, hidden, ra_x, ra_bytes(hidden), stream));
   }
-  if (st) return st;
-  st = hip_status(fn, launch_prep(x, GALE_F16, hidden, n_tok, hidden, 0, ra_x, ra_bytes(hidden), stream));
   if (st) return st;
   const int bound = (int)moe_item_bound(n_tok, n_experts, top_k, slots);
   st = run_gemv_phase(fn, table, 3, 0, 1, inter, hidden, ra_x, 0, 0, 0, 0, items, n_items, top_k, bound, h,

@@ -1,87 +1,9 @@
-// Blocked Walsh-Hadamard transform (1024-point blocks) and the activation
-// preparation that feeds the MFMA GEMV.
-//
-// Rotation: DeepSeek-V4-Flash GALE 1-bit model card, "What is in the pack" (signs
-// stored under a blocked FWHT-1024 rotation); the DeepSeek-V4-Pro GALE page
-// (serving knobs, DSV4_FWHT=butterfly) computes it as a single-kernel butterfly.
-// Here one wavefront transforms one 1024-block entirely in registers: each lane
-// holds 16 consecutive elements, the four butterfly stages over the element bits
-// run in-lane and the six stages over the lane bits exchange values across lanes.
-// H is normalised by 1/32 (orthonormal, H.H = I).
-#include "gale_internal.h"
+// Blocked Walsh-Hadamard transform (gale_fwht1024) and the activation record that
+// feeds the MFMA GEMV (gale_prepare_activations).  The wavefront-level transform
+// and the record layout are in gale_rotate.h.
+#include "gale_rotate.h"
 
 namespace gale {
-
-__device__ __forceinline__ float load_elem(const void* base, int dtype, int64_t i) {
-  if (dtype == GALE_F16) return __half2float(reinterpret_cast<const __half*>(base)[i]);
-  return reinterpret_cast<const float*>(base)[i];
-}
-
-// Load 16 consecutive elements [16 l, 16 l + 16) of a 1024-block.
-__device__ __forceinline__ void load16(const void* blk, int dtype, int lane, float v[16]) {
-  if (dtype == GALE_F16) {
-    const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const __half*>(blk) + 16 * lane);
-    uint4 a = p[0], b = p[1];
-    uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __half2 h2 = *reinterpret_cast<__half2*>(&w[i]);
-      v[2 * i] = __low2float(h2);
-      v[2 * i + 1] = __high2float(h2);
-    }
-  } else {
-    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(blk) + 16 * lane);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float4 f = p[i];
-      v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
-    }
-  }
-}
-
-__device__ __forceinline__ void store16(void* blk, int dtype, int lane, const float v[16]) {
-  if (dtype == GALE_F16) {
-    uint32_t w[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __half2 h2 = __floats2half2_rn(v[2 * i], v[2 * i + 1]);
-      w[i] = *reinterpret_cast<uint32_t*>(&h2);
-    }
-    uint4* p = reinterpret_cast<uint4*>(reinterpret_cast<__half*>(blk) + 16 * lane);
-    p[0] = make_uint4(w[0], w[1], w[2], w[3]);
-    p[1] = make_uint4(w[4], w[5], w[6], w[7]);
-  } else {
-    float4* p = reinterpret_cast<float4*>(reinterpret_cast<float*>(blk) + 16 * lane);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
-  }
-}
-
-// In-place normalised Walsh-Hadamard transform of the wavefront's 1024-block.
-__device__ __forceinline__ void fwht1024_wave(float v[16], int lane) {
-#pragma unroll
-  for (int h = 1; h < 16; h <<= 1) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      if ((e & h) == 0) {
-        float a = v[e], b = v[e + h];
-        v[e] = a + b;
-        v[e + h] = a - b;
-      }
-    }
-  }
-#pragma unroll
-  for (int b = 1; b < 64; b <<= 1) {
-    const bool upper = (lane & b) != 0;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      float u = __shfl_xor(v[e], b, 64);
-      v[e] = upper ? (u - v[e]) : (v[e] + u);
-    }
-  }
-#pragma unroll
-  for (int e = 0; e < 16; ++e) v[e] *= 0.03125f;
-}
 
 // ---------------------------------------------------------------------------
 // gale_fwht1024: one wavefront per (vector, block)
@@ -107,74 +29,11 @@ hipError_t launch_fwht(const void* x, void* y, int64_t n_vec, int len, int in_dt
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------
-// Activation preparation (one wavefront per (vector, 1024-chunk)):
-//   x~ = H x (skipped for pre-rotated input), stored in fp32 for the outlier pass;
-//   X = x~ * 2^p with p chosen so that max |X| lies in [128, 256) (well inside
-//   e4m3's 448), split into four e4m3 terms X = t0 + t1 + t2 + t3 by repeated
-//   round-to-nearest on the residual.  Each term carries ~4 significant bits, so
-//   the split is exact to about 2^-16 of each element; the GEMV's MFMA consumes
-//   the terms as four rows of its A operand.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t pack4_fp8(float a, float b, float c, float d) {
-  int p = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  p = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, p, true);
-  return (uint32_t)p;
-}
-
-__device__ __forceinline__ void unpack4_fp8(uint32_t p, float* o) {
-  o[0] = __builtin_amdgcn_cvt_f32_fp8((int)p, 0);
-  o[1] = __builtin_amdgcn_cvt_f32_fp8((int)p, 1);
-  o[2] = __builtin_amdgcn_cvt_f32_fp8((int)p, 2);
-  o[3] = __builtin_amdgcn_cvt_f32_fp8((int)p, 3);
-}
-
 __global__ void __launch_bounds__(256) prep_kernel(const void* __restrict__ x, int x_dtype, int64_t x_stride,
                                                    int n_vec, int K, int rotated, uint8_t* __restrict__ ra,
                                                    size_t ra_stride) {
-  const int lane = threadIdx.x & 63;
-  const int C = K >> 10;
-  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  if (wave >= (int64_t)n_vec * C) return;
-  const int64_t v = wave / C;
-  const int c = (int)(wave - v * C);
-  const size_t isz = x_dtype == GALE_F16 ? 2 : 4;
-  float f[16];
-  load16(reinterpret_cast<const char*>(x) + (v * x_stride + (int64_t)c * 1024) * isz, x_dtype, lane, f);
-  if (!rotated) fwht1024_wave(f, lane);
-
-  uint8_t* rec = ra + v * ra_stride;
-  store16(reinterpret_cast<float*>(rec) + c * 1024, GALE_F32, lane, f);
-
-  float m = 0.f;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(f[e]));
-#pragma unroll
-  for (int b = 1; b < 64; b <<= 1) m = fmaxf(m, __shfl_xor(m, b, 64));
-  int p = 0;
-  if (m > 0.f && m <= 3.0e38f) {
-    int ex;
-    frexpf(m, &ex);          // m = f 2^ex, f in [0.5, 1)
-    p = 8 - ex;              // m 2^p in [128, 256)
-  }
-  float r[16];
-#pragma unroll
-  for (int e = 0; e < 16; ++e) r[e] = ldexpf(f[e], p);
-  uint8_t* terms = rec + ra_terms_off(K) + (size_t)c * 4 * 1024;
-#pragma unroll
-  for (int t = 0; t < kTerms; ++t) {
-    uint32_t w[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      w[q] = pack4_fp8(r[4 * q], r[4 * q + 1], r[4 * q + 2], r[4 * q + 3]);
-      float back[4];
-      unpack4_fp8(w[q], back);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) r[4 * q + i] -= back[i];
-    }
-    *reinterpret_cast<uint4*>(terms + t * 1024 + 16 * lane) = make_uint4(w[0], w[1], w[2], w[3]);
-  }
-  if (lane == 0) reinterpret_cast<int32_t*>(rec + ra_p_off(K))[c] = p;
+  prep_wave(x, x_dtype, x_stride, n_vec, K, rotated, ra, ra_stride,
+            (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));
 }
 
 hipError_t launch_prep(const void* x, int x_dtype, int64_t x_stride, int n_vec, int K, int rotated,

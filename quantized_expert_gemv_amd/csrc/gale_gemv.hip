@@ -264,13 +264,17 @@ __device__ __forceinline__ void load_activation(const GemvParams& P, const Geo& 
   const int term = G.nl >> 2, slot = G.nl & 3;
   const int ra = sel4(slot < it.nslots ? slot : 0, it.ra0, it.ra1, it.ra2, it.ra3);
   const uint8_t* tb = P.ra + (size_t)ra * P.ra_stride + ra_terms_off(G.K) + ((size_t)G.c * 4 + term) * 1024 + 32 * G.g;
+  // lanes of empty slots load nothing (their rows of A are zero)
   const bool live = slot < it.nslots;
 #pragma unroll
-  for (int d = 0; d < 8; ++d) {
-    const uint4 a0 = *reinterpret_cast<const uint4*>(tb + 128 * d);
-    const uint4 a1 = *reinterpret_cast<const uint4*>(tb + 128 * d + 16);
-    a.A[d] = live ? v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w}
-                  : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+  for (int d = 0; d < 8; ++d) a.A[d] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+  if (live) {
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const uint4 a0 = *reinterpret_cast<const uint4*>(tb + 128 * d);
+      const uint4 a1 = *reinterpret_cast<const uint4*>(tb + 128 * d + 16);
+      a.A[d] = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+    }
   }
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
@@ -278,7 +282,11 @@ __device__ __forceinline__ void load_activation(const GemvParams& P, const Geo& 
     const int pv = reinterpret_cast<const int32_t*>(P.ra + (size_t)rai * P.ra_stride + ra_p_off(G.K))[G.c];
     a.pexp[i] = i < it.nslots ? pv : 0;
   }
-  // -S per block and slot: the MFMA against an all -1.0 operand sums each term row
+}
+
+// -S per 0/1 block and slot: the MFMA against an all -1.0 operand sums each term row.
+template <int NS>
+__device__ __forceinline__ void block_sums(Act& a) {
   const v8i neg1 = {(int)0xB8B8B8B8, (int)0xB8B8B8B8, (int)0xB8B8B8B8, (int)0xB8B8B8B8,
                     (int)0xB8B8B8B8, (int)0xB8B8B8B8, (int)0xB8B8B8B8, (int)0xB8B8B8B8};
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
@@ -308,6 +316,19 @@ __device__ __forceinline__ void plane_step(const Act& a, const uint32_t w[8], fl
   }
 }
 
+// fp32 x~ of the item's vectors into LDS for the outlier gather (when it fits)
+template <int NS>
+__device__ __forceinline__ void stage_activation(const GemvParams& P, const Geo& G, const Item& it, lds_f32* xt) {
+  if (!P.stage_xt) return;
+  for (int i = 0; i < NS; ++i) {
+    if (i >= it.nslots) break;
+    const int ra = sel4(i, it.ra0, it.ra1, it.ra2, it.ra3);
+    const u32x4* src = reinterpret_cast<const u32x4*>(P.ra + (size_t)ra * P.ra_stride);
+    lds_v4* dst = reinterpret_cast<lds_v4*>(xt + i * G.K);
+    for (int q = G.tid; q < (G.K >> 2); q += (int)blockDim.x) dst[q] = src[q];
+  }
+}
+
 template <int NS, int R, bool GATEUP>
 __device__ __forceinline__ void process_unit(const GemvParams& P, const Geo& G, int u, int u1, UnitBuf<R>& cur,
                                              UnitBuf<R>& nxt, int& act_item, Act& act, lds_f32* red, lds_f32* ored,
@@ -322,16 +343,9 @@ __device__ __forceinline__ void process_unit(const GemvParams& P, const Geo& G, 
   //    next unit's loads so that waiting for it never waits for them
   if (item != act_item) {
     load_activation<NS>(P, G, it, act);
-    if (P.stage_xt) {
-      for (int i = 0; i < NS; ++i) {
-        if (i >= it.nslots) break;
-        const int ra = sel4(i, it.ra0, it.ra1, it.ra2, it.ra3);
-        const u32x4* src = reinterpret_cast<const u32x4*>(P.ra + (size_t)ra * P.ra_stride);
-        lds_v4* dst = reinterpret_cast<lds_v4*>(xt + i * G.K);
-        for (int q = G.tid; q < (G.K >> 2); q += (int)blockDim.x) dst[q] = src[q];
-      }
-    }
+    stage_activation<NS>(P, G, it, xt);
     __syncthreads();
+    block_sums<NS>(act);
     act_item = item;
   }
 
@@ -507,15 +521,22 @@ __global__ void __launch_bounds__(512) gemv_kernel(const GemvParams P) {
   Act act;
   int act_item = -1;
   {
-    // prologue: CSR offsets of u0, then the whole of u0 (with the offsets of u0 + 1)
+    // prologue: the first item's activation operands (independent of the weight
+    // descriptors, so their latency overlaps the descriptor and CSR loads), the CSR
+    // offsets of u0, the whole of u0 (with the offsets of u0 + 1), then x~ into LDS
     const int item0 = uni(u0 / G.RG);
-    const int mat = uni(decode_item<NS>(P, item0).mat);
-    const gale_matrix Mo = matrix_of(P, mat, G.ohalf);
+    const Item it0 = decode_item<NS>(P, item0);
+    load_activation<NS>(P, G, it0, act);
+    const gale_matrix Mo = matrix_of(P, uni(it0.mat), G.ohalf);
     bool ok;
     const int n = outlier_row<R>(P, G, u0 - item0 * G.RG, &ok);
     b0.rp0 = Mo.row_ptr[n];
     b0.rp1 = Mo.row_ptr[n + (n < P.rows ? 1 : 0)];
     issue_unit<NS, R>(P, G, u0, u0 + 1 < u1 ? u0 + 1 : u0, b0);
+    stage_activation<NS>(P, G, it0, xt);
+    __syncthreads();
+    block_sums<NS>(act);
+    act_item = item0;
   }
   for (int u = u0; u < u1; u += 2) {
     process_unit<NS, R, GATEUP>(P, G, u, u1, b0, b1, act_item, act, red, ored, xt, wout);

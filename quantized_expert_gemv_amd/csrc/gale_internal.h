@@ -118,6 +118,9 @@ hipError_t launch_debug_outliers(int rows, int64_t nnz, gale_matrix m, int32_t* 
 hipError_t launch_route_small(const float* logits, int n_tok, int n_exp, int k, int32_t* idx, float* w,
                               int32_t* offsets, int32_t* perm, WorkItem* items, int32_t* n_items,
                               int max_slots, hipStream_t s);
+hipError_t launch_route_prep(const float* logits, int n_tok, int n_exp, int k, int32_t* idx, float* w,
+                             WorkItem* items, int32_t* n_items, int max_slots, const void* x, int x_dtype, int K,
+                             uint8_t* ra, size_t ra_stride, hipStream_t s);
 hipError_t launch_route_large(const float* logits, int n_tok, int n_exp, int k, int32_t* idx, float* w,
                               int32_t* chunk_cnt, int32_t* offsets, int32_t* perm, hipStream_t s);
 inline size_t route_chunk_count_bytes(int n_tok, int n_exp) {

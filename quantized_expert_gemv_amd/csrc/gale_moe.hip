@@ -7,6 +7,7 @@
 // descending, ties to the lower expert index; the k weights are the softmax of
 // the k selected logits; the combine sums slots 0..k-1 in that order.
 #include "gale_internal.h"
+#include "gale_rotate.h"
 
 namespace gale {
 
@@ -16,7 +17,9 @@ __device__ __forceinline__ bool better(float av, int ai, float bv, int bi) {
 }
 
 // Top-k of one token by one wavefront: each lane holds up to 8 logits (E <= 512).
-__device__ void topk_wave(const float* __restrict__ lg, int E, int k, int lane, int32_t* out_idx,
+// Every selection loop runs to the compile-time bound with a predicate, so the k
+// winners stay in registers.
+__device__ __forceinline__ void topk_wave(const float* __restrict__ lg, int E, int k, int lane, int32_t* out_idx,
                           float* out_w, int32_t* lds_idx) {
   float v[8];
   int id[8];
@@ -27,9 +30,10 @@ __device__ void topk_wave(const float* __restrict__ lg, int E, int k, int lane, 
     v[j] = e < E ? lg[e] : -INFINITY;
   }
   bool taken[8] = {false, false, false, false, false, false, false, false};
-  float sel_v[GALE_MAX_TOPK];
-  int sel_i[GALE_MAX_TOPK];
-  for (int s = 0; s < k; ++s) {
+  float m = 0.f, my_v = 0.f;     // the best logit; lane s keeps winner s
+  int my_i = 0;
+#pragma unroll
+  for (int s = 0; s < GALE_MAX_TOPK; ++s) {
     float bv = -INFINITY;
     int bi = 0x7fffffff;
 #pragma unroll
@@ -41,37 +45,64 @@ __device__ void topk_wave(const float* __restrict__ lg, int E, int k, int lane, 
       const int oi = __shfl_xor(bi, off, 64);
       if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
     }
+    if (s < k) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (id[j] == bi) taken[j] = true;
-    sel_v[s] = bv;
-    sel_i[s] = bi;
-  }
-  if (lane == 0) {
-    const float m = sel_v[0];
-    float sum = 0.f, ex[GALE_MAX_TOPK];
-    for (int s = 0; s < k; ++s) { ex[s] = expf(sel_v[s] - m); sum += ex[s]; }
-    for (int s = 0; s < k; ++s) {
-      out_idx[s] = sel_i[s];
-      out_w[s] = ex[s] / sum;
-      lds_idx[s] = sel_i[s];
+      for (int j = 0; j < 8; ++j)
+        if (id[j] == bi) taken[j] = true;
     }
+    if (s == 0) m = bv;
+    if (lane == s) { my_v = bv; my_i = bi; }
   }
+  // softmax of the k selected logits, one slot per lane
+  const float ex = lane < k ? expf(my_v - m) : 0.f;
+  float sum = 0.f;
+#pragma unroll
+  for (int s = 0; s < GALE_MAX_TOPK; ++s) {
+    const float es = __shfl(ex, s, 64);
+    if (s < k) sum += es;
+  }
+  if (lane < k) {
+    out_idx[lane] = my_i;
+    out_w[lane] = ex / sum;
+    lds_idx[lane] = my_i;
+  }
+}
+
+// Exclusive scan of v over a workgroup of at most 1024 threads; *total gets the sum.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* s_wave, int* total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = (blockDim.x + 63) >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(x, off, 64);
+    if (lane >= off) x += o;
+  }
+  if (lane == 63) s_wave[wave] = x;
+  __syncthreads();
+  int base = 0, all = 0;
+  for (int w = 0; w < nw; ++w) {
+    const int t = s_wave[w];
+    if (w < wave) base += t;
+    all += t;
+  }
+  *total = all;
+  __syncthreads();
+  return base + x - v;
 }
 
 // ---------------------------------------------------------------------------
 // Decode routing: one workgroup does top-k for every token, the counting sort
 // and the work-item list (n_tok * k <= 512 pairs).
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(512) route_small_kernel(const float* __restrict__ logits, int T, int E,
-                                                          int k, int max_slots, int32_t* __restrict__ idx,
-                                                          float* __restrict__ w, int32_t* __restrict__ offsets,
-                                                          int32_t* __restrict__ perm, WorkItem* __restrict__ items,
-                                                          int32_t* __restrict__ n_items) {
+__device__ __forceinline__ void route_small_body(const float* __restrict__ logits, int T, int E, int k,
+                                                 int max_slots, int32_t* __restrict__ idx, float* __restrict__ w,
+                                                 int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+                                                 WorkItem* __restrict__ items, int32_t* __restrict__ n_items) {
   __shared__ int32_t s_idx[GALE_MAX_DECODE_TOKENS * GALE_MAX_TOPK];
   __shared__ int32_t s_cnt[GALE_MAX_EXPERTS];
   __shared__ int32_t s_off[GALE_MAX_EXPERTS + 1];
   __shared__ int32_t s_ioff[GALE_MAX_EXPERTS + 1];
+  __shared__ int s_wave[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nw = blockDim.x >> 6;
   for (int e = tid; e < E; e += blockDim.x) s_cnt[e] = 0;
@@ -82,17 +113,19 @@ __global__ void __launch_bounds__(512) route_small_kernel(const float* __restric
   // per-expert counts (integer atomics: order-free)
   for (int p = tid; p < P; p += blockDim.x) atomicAdd(&s_cnt[s_idx[p]], 1);
   __syncthreads();
-  if (tid == 0) {
-    int a = 0, b = 0;
-    for (int e = 0; e < E; ++e) {
-      s_off[e] = a;
-      s_ioff[e] = b;
-      a += s_cnt[e];
-      b += (s_cnt[e] + max_slots - 1) / max_slots;
+  {
+    // blockDim.x == 512 >= E: thread e owns expert e
+    const int c = tid < E ? s_cnt[tid] : 0;
+    const int ni = (c + max_slots - 1) / max_slots;
+    int tot_p = 0, tot_i = 0;
+    const int op = block_exclusive_scan(c, s_wave, &tot_p);
+    const int oi = block_exclusive_scan(ni, s_wave, &tot_i);
+    if (tid < E) { s_off[tid] = op; s_ioff[tid] = oi; }
+    if (tid == 0) {
+      s_off[E] = tot_p;
+      s_ioff[E] = tot_i;
+      if (n_items) *n_items = tot_i;
     }
-    s_off[E] = a;
-    s_ioff[E] = b;
-    if (n_items) *n_items = b;
   }
   __syncthreads();
   if (offsets)
@@ -111,20 +144,61 @@ __global__ void __launch_bounds__(512) route_small_kernel(const float* __restric
       if (perm) perm[pos] = p;
       ++pos;
       if (!items) continue;
-      cur.pair[slot++] = p;
-      cur.n_slots = slot;
+      cur.pair[0] = slot == 0 ? p : cur.pair[0];
+      cur.pair[1] = slot == 1 ? p : cur.pair[1];
+      cur.pair[2] = slot == 2 ? p : cur.pair[2];
+      cur.pair[3] = slot == 3 ? p : cur.pair[3];
+      cur.n_slots = ++slot;
       if (slot == max_slots) {
-        for (int q = slot; q < 4; ++q) cur.pair[q] = cur.pair[0];
+        cur.pair[1] = slot > 1 ? cur.pair[1] : cur.pair[0];
+        cur.pair[2] = slot > 2 ? cur.pair[2] : cur.pair[0];
+        cur.pair[3] = slot > 3 ? cur.pair[3] : cur.pair[0];
         items[it++] = cur;
         slot = 0;
         cur.n_slots = 0;
       }
     }
     if (items && slot > 0) {
-      for (int q = slot; q < 4; ++q) cur.pair[q] = cur.pair[0];
+      cur.pair[1] = slot > 1 ? cur.pair[1] : cur.pair[0];
+      cur.pair[2] = slot > 2 ? cur.pair[2] : cur.pair[0];
+      cur.pair[3] = slot > 3 ? cur.pair[3] : cur.pair[0];
       items[it++] = cur;
     }
   }
+}
+
+__global__ void __launch_bounds__(512) route_small_kernel(const float* __restrict__ logits, int T, int E,
+                                                          int k, int max_slots, int32_t* __restrict__ idx,
+                                                          float* __restrict__ w, int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ perm, WorkItem* __restrict__ items,
+                                                          int32_t* __restrict__ n_items) {
+  route_small_body(logits, T, E, k, max_slots, idx, w, offsets, perm, items, n_items);
+}
+
+// Decode routing and the activation record of the layer input in one launch: the
+// two are independent, so workgroup 0 routes while the others prepare x.
+__global__ void __launch_bounds__(512) route_prep_kernel(const float* __restrict__ logits, int T, int E, int k,
+                                                         int max_slots, int32_t* __restrict__ idx,
+                                                         float* __restrict__ w, WorkItem* __restrict__ items,
+                                                         int32_t* __restrict__ n_items, const void* __restrict__ x,
+                                                         int x_dtype, int K, uint8_t* __restrict__ ra,
+                                                         size_t ra_stride) {
+  if (blockIdx.x == 0) {
+    route_small_body(logits, T, E, k, max_slots, idx, w, nullptr, nullptr, items, n_items);
+  } else {
+    prep_wave(x, x_dtype, K, T, K, 0, ra, ra_stride,
+              (int64_t)(blockIdx.x - 1) * (blockDim.x >> 6) + (threadIdx.x >> 6));
+  }
+}
+
+hipError_t launch_route_prep(const float* logits, int n_tok, int n_exp, int k, int32_t* idx, float* w,
+                             WorkItem* items, int32_t* n_items, int max_slots, const void* x, int x_dtype, int K,
+                             uint8_t* ra, size_t ra_stride, hipStream_t s) {
+  const int64_t waves = (int64_t)n_tok * (K / 1024);
+  const int64_t grid = 1 + (waves + 7) / 8;
+  hipLaunchKernelGGL(route_prep_kernel, dim3((unsigned)grid), dim3(512), 0, s, logits, n_tok, n_exp, k, max_slots,
+                     idx, w, items, n_items, x, x_dtype, K, ra, ra_stride);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -135,7 +209,7 @@ __global__ void __launch_bounds__(512) route_small_kernel(const float* __restric
 // ---------------------------------------------------------------------------
 constexpr int kRouteChunk = 64;
 
-__global__ void __launch_bounds__(256) route_topk_count_kernel(const float* __restrict__ logits, int T, int E,
+__global__ void __launch_bounds__(1024) route_topk_count_kernel(const float* __restrict__ logits, int T, int E,
                                                                int k, int32_t* __restrict__ idx,
                                                                float* __restrict__ w,
                                                                int32_t* __restrict__ chunk_cnt) {
@@ -146,7 +220,7 @@ __global__ void __launch_bounds__(256) route_topk_count_kernel(const float* __re
   const int t0 = chunk * kRouteChunk;
   const int t1 = min(T, t0 + kRouteChunk);
   for (int e = tid; e < E; e += blockDim.x) s_cnt[e] = 0;
-  for (int t = t0 + wave; t < t1; t += 4)
+  for (int t = t0 + wave; t < t1; t += (int)(blockDim.x >> 6))
     topk_wave(logits + (int64_t)t * E, E, k, lane, idx + (int64_t)t * k, w + (int64_t)t * k,
               s_idx + (t - t0) * k);
   __syncthreads();
@@ -158,23 +232,21 @@ __global__ void __launch_bounds__(256) route_topk_count_kernel(const float* __re
 
 __global__ void __launch_bounds__(512) route_scan_kernel(int n_chunks, int E, int32_t* __restrict__ chunk_cnt,
                                                          int32_t* __restrict__ offsets) {
-  __shared__ int32_t s_tot[GALE_MAX_EXPERTS];
+  __shared__ int s_wave[16];
   const int tid = threadIdx.x;
-  for (int e = tid; e < E; e += blockDim.x) {
-    int a = 0;
+  // blockDim.x == 512 >= E: thread e owns expert e
+  int a = 0;
+  if (tid < E) {
     for (int c = 0; c < n_chunks; ++c) {
-      const int v = chunk_cnt[(int64_t)c * E + e];
-      chunk_cnt[(int64_t)c * E + e] = a;   // becomes the chunk's base within expert e
+      const int v = chunk_cnt[(int64_t)c * E + tid];
+      chunk_cnt[(int64_t)c * E + tid] = a;   // becomes the chunk's base within expert e
       a += v;
     }
-    s_tot[e] = a;
   }
-  __syncthreads();
-  if (tid == 0) {
-    int a = 0;
-    for (int e = 0; e < E; ++e) { offsets[e] = a; a += s_tot[e]; }
-    offsets[E] = a;
-  }
+  int total = 0;
+  const int off = block_exclusive_scan(a, s_wave, &total);
+  if (tid < E) offsets[tid] = off;
+  if (tid == 0) offsets[E] = total;
 }
 
 __global__ void __launch_bounds__(256) route_scatter_kernel(int T, int E, int k,
@@ -207,7 +279,7 @@ hipError_t launch_route_small(const float* logits, int n_tok, int n_exp, int k, 
 hipError_t launch_route_large(const float* logits, int n_tok, int n_exp, int k, int32_t* idx, float* w,
                               int32_t* chunk_cnt, int32_t* offsets, int32_t* perm, hipStream_t s) {
   const int nc = (n_tok + kRouteChunk - 1) / kRouteChunk;
-  hipLaunchKernelGGL(route_topk_count_kernel, dim3(nc), dim3(256), 0, s, logits, n_tok, n_exp, k, idx, w,
+  hipLaunchKernelGGL(route_topk_count_kernel, dim3(nc), dim3(1024), 0, s, logits, n_tok, n_exp, k, idx, w,
                      chunk_cnt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !chunk_cnt) return e;
