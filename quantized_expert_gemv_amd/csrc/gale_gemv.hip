@@ -3,7 +3,7 @@
 // What it computes (DeepSeek-V4-Flash GALE 1-bit model card, "What is in the
 // pack"): y[n] = sum_k Wq[n][k] x~[k], x~ = blockdiag(H_1024) x, with
 //   Wq[n][k] = s[n][k/128] (1 - 2 b[n][k]) + r[n] q at the row's int4 outliers.
-// The DeepSeek-V4-Pro GALE page (serving knobs, DSV4_DIRECT_GEMV) multiplies
+// The DeepSeek-V4-Pro GALE page (serving options, the direct GEMV) multiplies
 // straight out of the packed record with signs, block scales and outliers decoded
 // in registers; this kernel keeps that idea and re-plans it for gfx950.
 //
@@ -21,13 +21,14 @@
 //     activation changes) turn the 0/1 planes into signs: block d adds
 //     s[n][d] (S - 2 sum_k b X).
 // One v_mfma_scale_f32_16x16x128_f8f6f4 therefore consumes one scale block of
-// 16 rows: 2048 weights for 4 ANDs (8 in sign form) and two FMAs per lane.
+// 16 rows: 2048 weights for 4 ANDs (8 in sign form) and two FMAs per token.
 //
 // Work split.  A unit is R row tiles (16 rows each) of one work item (a matrix,
 // or the w1/w3 pair of an expert, with up to four activation vectors).  A
 // workgroup has one wavefront per 1024-column chunk of each matrix (split-K);
-// the partial sums meet in LDS.  Workgroups are persistent: each streams a
-// contiguous run of units.
+// the partial sums meet in LDS, in a fixed order.  Workgroups are persistent:
+// each streams a contiguous run of units, tracking its position incrementally
+// and reloading a work item's descriptors only when the item changes.
 //
 // Memory pipeline.  Vector-memory completions are counted in issue order, so a
 // wait for any load also waits for every older one.  Each unit therefore
@@ -35,9 +36,8 @@
 // workgroup issues the whole of unit u+1 (sign words, block scales, the outlier
 // entries of its rows as 16-byte chunks, row scales) and the CSR offsets of
 // unit u+2, then computes unit u from registers and LDS.  Descriptors are read
-// with scalar loads; nothing is loaded conditionally (addresses are clamped),
-// so the compiler's wait counts stay exact and one full unit of HBM traffic is
-// always in flight behind the arithmetic.
+// with scalar loads; nothing is loaded conditionally (addresses are clamped);
+// every global load is a uniform base plus a 32-bit lane offset.
 //
 // Outliers: each wavefront serves 16 rows of the unit.  Their CSR entries are a
 // contiguous range, fetched as coalesced 16-byte chunks and staged in the
@@ -73,9 +73,14 @@ typedef __attribute__((address_space(3))) u32x4 lds_v4;
 
 __device__ __forceinline__ u32x4 to_v4(const uint4 a) { return u32x4{a.x, a.y, a.z, a.w}; }
 
-// 16-byte streaming load (each sign word is read exactly once)
-__device__ __forceinline__ uint4 stream_load16(const void* p) {
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+// 16-byte load at a wave-uniform base plus a 32-bit lane offset
+__device__ __forceinline__ uint4 ld16(const char* base, uint32_t off) {
+  const u32x4 v = *reinterpret_cast<const u32x4*>(base + off);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+// the same for data read exactly once (sign words, block scales)
+__device__ __forceinline__ uint4 ld16_stream(const char* base, uint32_t off) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + off));
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
@@ -94,9 +99,13 @@ __device__ __forceinline__ v4f plane_mfma(const v8i& a, const uint32_t w[8], con
                                                           plane_scale_e8m0<D>());
 }
 
-// Index of a 0/1 block among the six that need the block sum (blocks 3 and 7 do not).
-template <int D>
-constexpr int binary_slot() { return D - (D >> 2); }
+// Sum over the four lane groups (the four terms of every token): two row swaps.
+__device__ __forceinline__ float term_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float s = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
 // Item of a unit, decoded without dynamically indexed arrays.
 struct Item {
@@ -107,6 +116,13 @@ struct Item {
 
 __device__ __forceinline__ int sel4(int i, int a, int b, int c, int d) {
   return i == 0 ? a : (i == 1 ? b : (i == 2 ? c : d));
+}
+
+// Read-only tables are read through the constant address space: scalar loads, which
+// complete on their own counter and never make the vector pipeline wait.
+template <typename T>
+__device__ __forceinline__ const __attribute__((address_space(4))) T* as_const(const T* p) {
+  return (const __attribute__((address_space(4))) T*)(p);
 }
 
 template <int NS>
@@ -129,7 +145,7 @@ __device__ __forceinline__ Item decode_item(const GemvParams& P, int item) {
     it.out2 = base_out + (2 < it.nslots ? 2 : 0);
     it.out3 = base_out + (3 < it.nslots ? 3 : 0);
   } else {
-    const auto* w = (const __attribute__((address_space(4))) WorkItem*)(P.items) + item;
+    const auto* w = as_const(P.items) + item;
     it.mat = uni(w->expert);
     const int ns = uni(w->n_slots);
     it.nslots = ns < NS ? ns : NS;
@@ -146,33 +162,65 @@ __device__ __forceinline__ Item decode_item(const GemvParams& P, int item) {
   return it;
 }
 
+// Descriptor-table index of an item's matrix group.
+__device__ __forceinline__ int item_mat(const GemvParams& P, int item) {
+  if (P.implicit_items) return uni(item / P.n_groups);
+  return uni(as_const(P.items)[item].expert);
+}
+
 struct Geo {
   int K, C, tid, lane, wave, half, c, g, nl, ntiles, RG;
   int ohalf, orow0, wr, sub;   // outlier role: rows orow0 + wr of half ohalf, lane sub of four
   bool orole;
+  uint32_t sw_lane, sc_lane;   // lane's byte offsets inside one row tile's sign words / scales
+  uint32_t sw_tile, sc_tile;   // bytes per row tile (all chunks)
 };
 
-// Read-only tables are read through the constant address space: scalar loads, which
-// complete on their own counter and never make the vector pipeline wait.
-template <typename T>
-__device__ __forceinline__ const __attribute__((address_space(4))) T* as_const(const T* p) {
-  return (const __attribute__((address_space(4))) T*)(p);
-}
+// The sections of one work item that this wavefront reads: the matrix of its half
+// (signs, block scales) and the matrix whose outliers it serves.
+struct Desc {
+  const char* signs;
+  const char* scales;
+  const char* rsc;
+  const int32_t* rptr;
+  const char* ocols;
+  const char* ovals;
+};
 
-__device__ __forceinline__ gale_matrix matrix_of(const GemvParams& P, int mat, int hf) {
+__device__ __forceinline__ Desc load_desc(const GemvParams& P, const Geo& G, int mat) {
   const auto* t = as_const(P.table);
-  const int i = uni(mat * P.mat_stride + (hf ? P.sel1 : P.sel0));
-  gale_matrix m;
-  m.signs = t[i].signs;
-  m.block_scales = t[i].block_scales;
-  m.row_scales = t[i].row_scales;
-  m.row_ptr = t[i].row_ptr;
-  m.out_cols = t[i].out_cols;
-  m.out_vals = t[i].out_vals;
-  return m;
+  const int iw = uni(mat * P.mat_stride + (G.half ? P.sel1 : P.sel0));
+  const int io = uni(mat * P.mat_stride + (G.ohalf ? P.sel1 : P.sel0));
+  Desc d;
+  d.signs = reinterpret_cast<const char*>(t[iw].signs);
+  d.scales = reinterpret_cast<const char*>(t[iw].block_scales);
+  d.rsc = reinterpret_cast<const char*>(t[io].row_scales);
+  d.rptr = t[io].row_ptr;
+  d.ocols = reinterpret_cast<const char*>(t[io].out_cols);
+  d.ovals = reinterpret_cast<const char*>(t[io].out_vals);
+  return d;
 }
 
-// Row served by this thread's outlier role in unit rg, clamped to [0, rows].
+// Position of a unit: index, work item, row group.
+struct Pos {
+  int u, item, rg;
+};
+
+// The unit after p, or p itself at the end of the workgroup's range.
+__device__ __forceinline__ Pos pos_next(const Pos& p, int u1, int RG) {
+  if (p.u + 1 >= u1) return p;
+  Pos q;
+  q.u = p.u + 1;
+  q.rg = p.rg + 1;
+  q.item = p.item;
+  if (q.rg == RG) {
+    q.rg = 0;
+    q.item = p.item + 1;
+  }
+  return q;
+}
+
+// Row served by this thread's outlier role in row group rg, clamped to [0, rows].
 template <int R>
 __device__ __forceinline__ int outlier_row(const GemvParams& P, const Geo& G, int rg, bool* valid) {
   const int n = rg * R * 16 + G.orow0 + G.wr;
@@ -193,25 +241,22 @@ struct UnitBuf {
   uint32_t rsc;          // fp16 row scale of this thread's row
 };
 
-// Issue the loads of unit v into b.  rp0/rp1 of unit v must already be in b (from the
-// previous unit's np0/np1).  Also fetches the CSR offsets of unit vnext.
-template <int NS, int R>
-__device__ __forceinline__ void issue_unit(const GemvParams& P, const Geo& G, int v, int vnext, UnitBuf<R>& b) {
-  const int item = uni(v / G.RG);
-  const int rg = uni(v - item * G.RG);
-  const int mat = uni(decode_item<NS>(P, item).mat);
-  const gale_matrix Mw = matrix_of(P, mat, G.half);
-  const gale_matrix Mo = matrix_of(P, mat, G.ohalf);
+// Issue the loads of unit v (descriptors dv) into b.  rp0/rp1 of v must already be in
+// b (from the previous unit's np0/np1).  Also fetches the CSR offsets of unit vn.
+template <int R>
+__device__ __forceinline__ void issue_unit(const GemvParams& P, const Geo& G, const Pos& v, const Desc& dv,
+                                           const Pos& vn, const Desc& dn, UnitBuf<R>& b) {
+  const int t0 = v.rg * R;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    int tile = rg * R + r;
+    int tile = t0 + r;
     tile = tile < G.ntiles ? tile : G.ntiles - 1;
-    const uint4* sw = reinterpret_cast<const uint4*>(Mw.signs + sign_word_index(tile, G.c, G.C, 0, G.lane, 0));
-    const uint4 lo = stream_load16(sw);
-    const uint4 hi = stream_load16(sw + 64);
+    const uint32_t o = (uint32_t)tile * G.sw_tile + G.sw_lane;
+    const uint4 lo = ld16_stream(dv.signs, o);
+    const uint4 hi = ld16_stream(dv.signs, o + 1024u);
     b.sw[r][0] = lo.x; b.sw[r][1] = lo.y; b.sw[r][2] = lo.z; b.sw[r][3] = lo.w;
     b.sw[r][4] = hi.x; b.sw[r][5] = hi.y; b.sw[r][6] = hi.z; b.sw[r][7] = hi.w;
-    const uint4 sc = stream_load16(Mw.block_scales + scale_index(16 * tile + G.nl, 8 * G.c, G.C));
+    const uint4 sc = ld16_stream(dv.scales, (uint32_t)tile * G.sc_tile + G.sc_lane);
     b.sc[r][0] = sc.x; b.sc[r][1] = sc.y; b.sc[r][2] = sc.z; b.sc[r][3] = sc.w;
   }
   // outlier entries of the wave's 16 rows: CSR range [e0, e1) from lanes 0 (first row) and 60 (last row)
@@ -226,31 +271,25 @@ __device__ __forceinline__ void issue_unit(const GemvParams& P, const Geo& G, in
   const int vl = any ? ((e1 - 1) >> 1) >> 4 : 0;
   b.ocf = cf;
   b.ovf = vf;
-  const uint4* cbase = reinterpret_cast<const uint4*>(Mo.out_cols);
-  const uint4* vbase = reinterpret_cast<const uint4*>(Mo.out_vals);
 #pragma unroll
   for (int k = 0; k < kColChunks; ++k) {
     int ch = cf + 64 * k + G.lane;
     ch = ch < cl ? ch : cl;
-    b.oc[k] = cbase[ch];
+    b.oc[k] = ld16(dv.ocols, (uint32_t)ch * 16u);
   }
 #pragma unroll
   for (int k = 0; k < kValChunks; ++k) {
     int ch = vf + 64 * k + G.lane;
     ch = ch < vl ? ch : vl;
-    b.ov[k] = vbase[ch];
+    b.ov[k] = ld16(dv.ovals, (uint32_t)ch * 16u);
   }
   bool ok;
-  const int n = outlier_row<R>(P, G, rg, &ok);
-  b.rsc = Mo.row_scales[n < P.rows ? n : P.rows - 1];
+  const int n = outlier_row<R>(P, G, v.rg, &ok);
+  b.rsc = *reinterpret_cast<const uint16_t*>(dv.rsc + 2u * (uint32_t)(n < P.rows ? n : P.rows - 1));
   // CSR offsets of the next unit's row
-  const int item2 = uni(vnext / G.RG);
-  const int rg2 = uni(vnext - item2 * G.RG);
-  const int mat2 = uni(decode_item<NS>(P, item2).mat);
-  const gale_matrix Mo2 = matrix_of(P, mat2, G.ohalf);
-  const int n2 = outlier_row<R>(P, G, rg2, &ok);
-  b.np0 = Mo2.row_ptr[n2];
-  b.np1 = Mo2.row_ptr[n2 + (n2 < P.rows ? 1 : 0)];
+  const int n2 = outlier_row<R>(P, G, vn.rg, &ok);
+  b.np0 = dn.rptr[n2];
+  b.np1 = dn.rptr[n2 + (n2 < P.rows ? 1 : 0)];
 }
 
 struct Act {
@@ -299,23 +338,6 @@ __device__ __forceinline__ void block_sums(Act& a) {
   }
 }
 
-// One block: D = 2 sum_k b X (0/1 blocks, via the E8M0 scale) or sum_k (1 - 2 b) X (sign blocks 3, 7).
-// Block contribution s (S - 2 P): acc += -s D - s (-S) for a 0/1 block; acc += s D for a sign block.
-template <int NS, int D>
-__device__ __forceinline__ void plane_step(const Act& a, const uint32_t w[8], float s, float* acc) {
-  const v4f zero = {0.f, 0.f, 0.f, 0.f};
-  const v4f r = plane_mfma<D>(a.A[D], w, zero);
-#pragma unroll
-  for (int i = 0; i < NS; ++i) {
-    if constexpr (plane_is_binary<D>()) {
-      acc[i] = fmaf(-s, r[i], acc[i]);
-      acc[i] = fmaf(-s, a.S[binary_slot<D>()][i], acc[i]);
-    } else {
-      acc[i] = fmaf(s, r[i], acc[i]);
-    }
-  }
-}
-
 // fp32 x~ of the item's vectors into LDS for the outlier gather (when it fits)
 template <int NS>
 __device__ __forceinline__ void stage_activation(const GemvParams& P, const Geo& G, const Item& it, lds_f32* xt) {
@@ -329,19 +351,56 @@ __device__ __forceinline__ void stage_activation(const GemvParams& P, const Geo&
   }
 }
 
+// One row tile of the sign pass: the eight block products, then the scaled sum.  A 0/1
+// block contributes s (S - 2 P) with 2 P its product; a sign block s times its product.
+template <int NS>
+__device__ __forceinline__ void sign_tile(const Act& a, const uint32_t w[8], const uint32_t sc[4], float* acc) {
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+  const v4f d0 = plane_mfma<0>(a.A[0], w, zero);
+  const v4f d1 = plane_mfma<1>(a.A[1], w, zero);
+  const v4f d2 = plane_mfma<2>(a.A[2], w, zero);
+  const v4f d3 = plane_mfma<3>(a.A[3], w, zero);
+  const v4f d4 = plane_mfma<4>(a.A[4], w, zero);
+  const v4f d5 = plane_mfma<5>(a.A[5], w, zero);
+  const v4f d6 = plane_mfma<6>(a.A[6], w, zero);
+  const v4f d7 = plane_mfma<7>(a.A[7], w, zero);
+  const float s0 = half_bits_to_float(sc[0] & 0xFFFF), s1 = half_bits_to_float(sc[0] >> 16);
+  const float s2 = half_bits_to_float(sc[1] & 0xFFFF), s3 = half_bits_to_float(sc[1] >> 16);
+  const float s4 = half_bits_to_float(sc[2] & 0xFFFF), s5 = half_bits_to_float(sc[2] >> 16);
+  const float s6 = half_bits_to_float(sc[3] & 0xFFFF), s7 = half_bits_to_float(sc[3] >> 16);
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    float v = -s0 * (d0[i] + a.S[0][i]);
+    v = fmaf(-s1, d1[i] + a.S[1][i], v);
+    v = fmaf(-s2, d2[i] + a.S[2][i], v);
+    v = fmaf(s3, d3[i], v);
+    v = fmaf(-s4, d4[i] + a.S[3][i], v);
+    v = fmaf(-s5, d5[i] + a.S[4][i], v);
+    v = fmaf(-s6, d6[i] + a.S[5][i], v);
+    v = fmaf(s7, d7[i], v);
+    acc[i] = v;
+  }
+}
+
+// int4 two's complement value of outlier p from its packed byte
+__device__ __forceinline__ float nibble_value(int byte, int p) {
+  return (float)(((int)((uint32_t)byte << (28 - 4 * (p & 1)))) >> 28);
+}
+
 template <int NS, int R, bool GATEUP>
-__device__ __forceinline__ void process_unit(const GemvParams& P, const Geo& G, int u, int u1, UnitBuf<R>& cur,
-                                             UnitBuf<R>& nxt, int& act_item, Act& act, lds_f32* red, lds_f32* ored,
-                                             lds_f32* xt, lds_u8* wout) {
+__device__ __forceinline__ void process_unit(const GemvParams& P, const Geo& G, const Pos& cur_pos, Item& it,
+                                             UnitBuf<R>& cur, UnitBuf<R>& nxt, const Pos& p1, const Desc& d1,
+                                             const Pos& p2, const Desc& d2, int& act_item, Act& act,
+                                             lds_f32* red, lds_f32* ored, lds_f32* xt, lds_u8* wout) {
   constexpr int HALVES = GATEUP ? 2 : 1;
   constexpr int RR = R * 16;
-  const int item = uni(u / G.RG);
-  const int rg = uni(u - item * G.RG);
-  const Item it = decode_item<NS>(P, item);
+  const int item = cur_pos.item;
+  const int rg = cur_pos.rg;
 
   // 1. activation of a new item (A operands, block sums, x~ in LDS); issued before the
   //    next unit's loads so that waiting for it never waits for them
   if (item != act_item) {
+    it = decode_item<NS>(P, item);
     load_activation<NS>(P, G, it, act);
     stage_activation<NS>(P, G, it, xt);
     __syncthreads();
@@ -359,34 +418,18 @@ __device__ __forceinline__ void process_unit(const GemvParams& P, const Geo& G, 
   }
 
   // 3. issue unit u+1 (and the CSR offsets of u+2) behind this unit's arithmetic
-  {
-    const int v = u + 1 < u1 ? u + 1 : u;
-    const int vn = u + 2 < u1 ? u + 2 : v;
-    nxt.rp0 = cur.np0;
-    nxt.rp1 = cur.np1;
-    issue_unit<NS, R>(P, G, v, vn, nxt);
-  }
+  nxt.rp0 = cur.np0;
+  nxt.rp1 = cur.np1;
+  issue_unit<R>(P, G, p1, d1, p2, d2, nxt);
 
   // 4. sign pass over the wave's R tiles
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     float acc[NS];
-#pragma unroll
-    for (int i = 0; i < NS; ++i) acc[i] = 0.f;
-    const uint32_t s01 = cur.sc[r][0], s23 = cur.sc[r][1], s45 = cur.sc[r][2], s67 = cur.sc[r][3];
-    plane_step<NS, 0>(act, cur.sw[r], half_bits_to_float(s01 & 0xFFFF), acc);
-    plane_step<NS, 1>(act, cur.sw[r], half_bits_to_float(s01 >> 16), acc);
-    plane_step<NS, 2>(act, cur.sw[r], half_bits_to_float(s23 & 0xFFFF), acc);
-    plane_step<NS, 3>(act, cur.sw[r], half_bits_to_float(s23 >> 16), acc);
-    plane_step<NS, 4>(act, cur.sw[r], half_bits_to_float(s45 & 0xFFFF), acc);
-    plane_step<NS, 5>(act, cur.sw[r], half_bits_to_float(s45 >> 16), acc);
-    plane_step<NS, 6>(act, cur.sw[r], half_bits_to_float(s67 & 0xFFFF), acc);
-    plane_step<NS, 7>(act, cur.sw[r], half_bits_to_float(s67 >> 16), acc);
+    sign_tile<NS>(act, cur.sw[r], cur.sc[r], acc);
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
-      float v = ldexpf(acc[i], -act.pexp[i]);     // undo 2^p
-      v += __shfl_xor(v, 16, 64);                 // sum the four terms (lane groups)
-      v += __shfl_xor(v, 32, 64);
+      const float v = term_sum(ldexpf(acc[i], -act.pexp[i]));   // undo 2^p, sum the four terms
       if (G.lane < 16) red[((G.half * G.C + G.c) * RR + r * 16 + G.lane) * NS + i] = v;
     }
   }
@@ -407,11 +450,17 @@ __device__ __forceinline__ void process_unit(const GemvParams& P, const Geo& G, 
     const int p_mid = min(p_end, p_cap);
     int p = p_begin;
     if (P.stage_xt) {
+      for (; p + 4 < p_mid; p += 8) {
+        const int col0 = lc[p - cbase], col1 = lc[p + 4 - cbase];
+        const float q0 = nibble_value(lv[(p >> 1) - vbase], p);
+        const float q1 = nibble_value(lv[((p + 4) >> 1) - vbase], p + 4);
+#pragma unroll
+        for (int i = 0; i < NS; ++i)
+          if (i < it.nslots) o[i] = fmaf(q1, xt[i * G.K + col1], fmaf(q0, xt[i * G.K + col0], o[i]));
+      }
       for (; p < p_mid; p += 4) {
         const int col = lc[p - cbase];
-        const int byte = lv[(p >> 1) - vbase];
-        const int nib = (p & 1) ? (byte >> 4) : (byte & 0xF);
-        const float q = (float)(nib - ((nib & 8) << 1));
+        const float q = nibble_value(lv[(p >> 1) - vbase], p);
 #pragma unroll
         for (int i = 0; i < NS; ++i)
           if (i < it.nslots) o[i] = fmaf(q, xt[i * G.K + col], o[i]);
@@ -419,9 +468,7 @@ __device__ __forceinline__ void process_unit(const GemvParams& P, const Geo& G, 
     } else {
       for (; p < p_mid; p += 4) {
         const int col = lc[p - cbase];
-        const int byte = lv[(p >> 1) - vbase];
-        const int nib = (p & 1) ? (byte >> 4) : (byte & 0xF);
-        const float q = (float)(nib - ((nib & 8) << 1));
+        const float q = nibble_value(lv[(p >> 1) - vbase], p);
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
           if (i < it.nslots) {
@@ -452,6 +499,8 @@ __device__ __forceinline__ void process_unit(const GemvParams& P, const Geo& G, 
       if (G.orole && G.sub == 0) ored[(G.ohalf * RR + G.orow0 + G.wr) * NS + i] = o[i] * rscale;
     }
   }
+  // every wave's partials of this unit are in LDS; the buffers alternate between
+  // units, so the next unit's writes never meet this unit's reads
   __syncthreads();
 
   // 6. sum the split-K partials in a fixed order, add the outliers, store
@@ -475,7 +524,6 @@ __device__ __forceinline__ void process_unit(const GemvParams& P, const Geo& G, 
       reinterpret_cast<float*>(P.y)[off] = v[0];
     }
   }
-  __syncthreads();
 }
 
 // NS: activation vectors per item (1, 2 or 4); R: row tiles per unit (R <= chunks);
@@ -503,15 +551,23 @@ __global__ void __launch_bounds__(512) gemv_kernel(const GemvParams P) {
   G.orow0 = uni(G.orole ? 16 * G.wave - G.ohalf * RR : 0);
   G.wr = G.lane >> 2;
   G.sub = G.lane & 3;
+  // sign words of tile t, chunk c, lane l: byte 2048 (t C + c) + 16 l (and + 1024 for the
+  // second half); block scales: byte 256 (t C + c) + 16 (l % 16)
+  G.sw_tile = (uint32_t)G.C * 2048u;
+  G.sc_tile = (uint32_t)G.C * 256u;
+  G.sw_lane = (uint32_t)G.c * 2048u + 16u * (uint32_t)G.lane;
+  G.sc_lane = (uint32_t)G.c * 256u + 16u * (uint32_t)G.nl;
 
+  // LDS: two alternating sets of partial sums, the waves' outlier slices, x~
   lds_u8* base = (lds_u8*)smem;
-  lds_f32* red = reinterpret_cast<lds_f32*>(base);             // [HALVES][C][RR][NS]
-  lds_f32* ored = red + HALVES * G.C * RR * NS;                // [HALVES][RR][NS]
-  lds_u8* wbase = reinterpret_cast<lds_u8*>(ored + HALVES * RR * NS);
+  const int red_n = HALVES * G.C * RR * NS, ored_n = HALVES * RR * NS;
+  lds_f32* red0 = reinterpret_cast<lds_f32*>(base);            // [2][HALVES][C][RR][NS]
+  lds_f32* ored0 = red0 + 2 * red_n;                            // [2][HALVES][RR][NS]
+  lds_u8* wbase = reinterpret_cast<lds_u8*>(ored0 + 2 * ored_n);
   lds_u8* wout = wbase + G.wave * kWaveOutBytes;               // this wave's outlier staging slice
   lds_f32* xt = reinterpret_cast<lds_f32*>(wbase + (size_t)HALVES * G.C * kWaveOutBytes);   // [NS][K] when staged
 
-  const int n_items = P.implicit_items ? P.n_items : *P.n_items_dev;
+  const int n_items = P.implicit_items ? P.n_items : uni(*as_const(P.n_items_dev));
   const int total = n_items * G.RG;
   const int u0 = uni((int)((int64_t)total * blockIdx.x / gridDim.x));
   const int u1 = uni((int)((int64_t)total * (blockIdx.x + 1) / gridDim.x));
@@ -519,36 +575,57 @@ __global__ void __launch_bounds__(512) gemv_kernel(const GemvParams P) {
 
   UnitBuf<R> b0, b1;
   Act act;
-  int act_item = -1;
+  int act_item;
+  Item it;
+  Pos pc, p1, p2;
+  Desc d1, d2;
   {
     // prologue: the first item's activation operands (independent of the weight
     // descriptors, so their latency overlaps the descriptor and CSR loads), the CSR
     // offsets of u0, the whole of u0 (with the offsets of u0 + 1), then x~ into LDS
-    const int item0 = uni(u0 / G.RG);
-    const Item it0 = decode_item<NS>(P, item0);
-    load_activation<NS>(P, G, it0, act);
-    const gale_matrix Mo = matrix_of(P, uni(it0.mat), G.ohalf);
+    pc.u = u0;
+    pc.item = uni(u0 / G.RG);
+    pc.rg = uni(u0 - pc.item * G.RG);
+    it = decode_item<NS>(P, pc.item);
+    load_activation<NS>(P, G, it, act);
+    const Desc d0 = load_desc(P, G, uni(it.mat));
+    p1 = pos_next(pc, u1, G.RG);
+    d1 = p1.item == pc.item ? d0 : load_desc(P, G, item_mat(P, p1.item));
     bool ok;
-    const int n = outlier_row<R>(P, G, u0 - item0 * G.RG, &ok);
-    b0.rp0 = Mo.row_ptr[n];
-    b0.rp1 = Mo.row_ptr[n + (n < P.rows ? 1 : 0)];
-    issue_unit<NS, R>(P, G, u0, u0 + 1 < u1 ? u0 + 1 : u0, b0);
-    stage_activation<NS>(P, G, it0, xt);
+    const int n = outlier_row<R>(P, G, pc.rg, &ok);
+    b0.rp0 = d0.rptr[n];
+    b0.rp1 = d0.rptr[n + (n < P.rows ? 1 : 0)];
+    issue_unit<R>(P, G, pc, d0, p1, d1, b0);
+    stage_activation<NS>(P, G, it, xt);
     __syncthreads();
     block_sums<NS>(act);
-    act_item = item0;
+    act_item = pc.item;
+    p2 = pos_next(p1, u1, G.RG);
+    d2 = p2.item == p1.item ? d1 : load_desc(P, G, item_mat(P, p2.item));
   }
-  for (int u = u0; u < u1; u += 2) {
-    process_unit<NS, R, GATEUP>(P, G, u, u1, b0, b1, act_item, act, red, ored, xt, wout);
-    if (u + 1 >= u1) break;
-    process_unit<NS, R, GATEUP>(P, G, u + 1, u1, b1, b0, act_item, act, red, ored, xt, wout);
+  for (;;) {
+    process_unit<NS, R, GATEUP>(P, G, pc, it, b0, b1, p1, d1, p2, d2, act_item, act, red0, ored0, xt, wout);
+    if (pc.u + 1 >= u1) break;
+    pc = p1;
+    p1 = p2;
+    d1 = d2;
+    p2 = pos_next(p2, u1, G.RG);
+    d2 = p2.item == p1.item ? d1 : load_desc(P, G, item_mat(P, p2.item));
+    process_unit<NS, R, GATEUP>(P, G, pc, it, b1, b0, p1, d1, p2, d2, act_item, act, red0 + red_n,
+                                ored0 + ored_n, xt, wout);
+    if (pc.u + 1 >= u1) break;
+    pc = p1;
+    p1 = p2;
+    d1 = d2;
+    p2 = pos_next(p2, u1, G.RG);
+    d2 = p2.item == p1.item ? d1 : load_desc(P, G, item_mat(P, p2.item));
   }
 }
 
 size_t gemv_smem_bytes(int cols, int slots, int tiles, int gateup, int stage_xt) {
   const int halves = gateup ? 2 : 1;
   const int C = cols >> 10;
-  size_t f = (size_t)halves * C * tiles * 16 * slots + (size_t)halves * tiles * 16 * slots;
+  const size_t f = 2 * ((size_t)halves * C * tiles * 16 * slots + (size_t)halves * tiles * 16 * slots);
   size_t b = f * 4 + (size_t)halves * C * kWaveOutBytes;
   if (stage_xt) b += (size_t)slots * cols * 4;
   return b;
@@ -585,7 +662,10 @@ static hipError_t launch_r(const GemvParams& p, int tiles, int64_t max_units, hi
   switch (tiles) {
     case 1: return launch_t<NS, 1, G>(p, max_units, s);
     case 2: return launch_t<NS, 2, G>(p, max_units, s);
-    default: return launch_t<NS, 4, G>(p, max_units, s);
+    default:
+      // four tiles per unit only for single-token items (more slots would spill)
+      if constexpr (NS == 1) return launch_t<NS, 4, G>(p, max_units, s);
+      else return launch_t<NS, 2, G>(p, max_units, s);
   }
 }
 
