@@ -18,7 +18,9 @@ __host__ __device__ inline uint32_t plane_bits(uint32_t w, int d) {
 template <int D>
 __device__ __forceinline__ uint32_t plane_operand(uint32_t w) {
   if constexpr ((D & 3) < 3) return w & (0x11111111u << (D & 3));
-  else return (w & 0x88888888u) | 0x22222222u;
+  // (w & 0x88888888) | 0x22222222 in one three-input bit operation: truth table 0xEA
+  // is (S0 & S1) | S2 for the index 4 S0 + 2 S1 + S2
+  else return __builtin_amdgcn_bitop3_b32(w, 0x88888888u, 0x22222222u, 0xEA);
 }
 
 template <int D>

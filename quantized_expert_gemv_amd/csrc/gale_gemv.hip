@@ -450,6 +450,35 @@ __device__ __forceinline__ void process_unit(const GemvParams& P, const Geo& G, 
     const int p_mid = min(p_end, p_cap);
     int p = p_begin;
     if (P.stage_xt) {
+      // eight entries per step: all their LDS reads issue before the first FMA waits
+      for (; p + 28 < p_mid; p += 32) {
+        int col[8], by[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) { col[j] = lc[p + 4 * j - cbase]; by[j] = lv[((p + 4 * j) >> 1) - vbase]; }
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+          if (i < it.nslots) {
+            float x[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) x[j] = xt[i * G.K + col[j]];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) o[i] = fmaf(nibble_value(by[j], p), x[j], o[i]);
+          }
+        }
+      }
+      for (; p + 12 < p_mid; p += 16) {
+        const int col0 = lc[p - cbase], col1 = lc[p + 4 - cbase], col2 = lc[p + 8 - cbase], col3 = lc[p + 12 - cbase];
+        const int by0 = lv[(p >> 1) - vbase], by1 = lv[((p + 4) >> 1) - vbase];
+        const int by2 = lv[((p + 8) >> 1) - vbase], by3 = lv[((p + 12) >> 1) - vbase];
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+          if (i < it.nslots) {
+            const float x0 = xt[i * G.K + col0], x1 = xt[i * G.K + col1], x2 = xt[i * G.K + col2], x3 = xt[i * G.K + col3];
+            o[i] = fmaf(nibble_value(by3, p), x3, fmaf(nibble_value(by2, p), x2,
+                   fmaf(nibble_value(by1, p), x1, fmaf(nibble_value(by0, p), x0, o[i]))));
+          }
+        }
+      }
       for (; p + 4 < p_mid; p += 8) {
         const int col0 = lc[p - cbase], col1 = lc[p + 4 - cbase];
         const float q0 = nibble_value(lv[(p >> 1) - vbase], p);
@@ -663,8 +692,8 @@ static hipError_t launch_r(const GemvParams& p, int tiles, int64_t max_units, hi
     case 1: return launch_t<NS, 1, G>(p, max_units, s);
     case 2: return launch_t<NS, 2, G>(p, max_units, s);
     default:
-      // four tiles per unit only for single-token items (more slots would spill)
-      if constexpr (NS == 1) return launch_t<NS, 4, G>(p, max_units, s);
+      // four tiles per unit only for single-token, single-matrix items (more would spill)
+      if constexpr (NS == 1 && !G) return launch_t<NS, 4, G>(p, max_units, s);
       else return launch_t<NS, 2, G>(p, max_units, s);
   }
 }
