@@ -62,6 +62,8 @@ extern "C" {
 #define GALE_X_PREPARED   0x2u   /* gale_expert_gemv: x holds records from gale_prepare_activations */
 #define GALE_PATH_DECODE  0x10u  /* gale_moe_layer_fwd: force the per-expert GEMV path */
 #define GALE_PATH_GROUPED 0x20u  /* gale_moe_layer_fwd: force the grouped (token-sorted) path */
+#define GALE_GROUPED_ITEMS 0x40u /* gale_moe_layer_fwd grouped path: GEMV work items only */
+#define GALE_GROUPED_GEMM  0x80u /* gale_moe_layer_fwd grouped path: fp16 MFMA tile GEMM only */
 
 /* ---- limits -------------------------------------------------------------- */
 #define GALE_FWHT_N        1024   /* rotation block ("blocked FWHT-1024") */
@@ -218,9 +220,15 @@ size_t gale_moe_workspace_bytes(int32_t n_tok, int32_t n_experts, int32_t top_k,
  * x, y: fp16 [n_tok][hidden].  topk_idx (int32 [n_tok][top_k]) and topk_w (fp32) are
  * written when non-NULL.  Two paths, same results bit for bit on any token:
  *   decode  (n_tok <= 64): one workgroup routes all tokens and lists the work items;
- *   grouped (n_tok > 64):  chunked top-k, a stable sort of the (token, slot) pairs by
- *           expert, then work items of up to 4 pairs of one expert each, so that an
- *           expert's weights are streamed once per 4 of its tokens.
+ *   grouped (n_tok > 64):  chunked top-k and a stable sort of the (token, slot) pairs
+ *           by expert; then experts with many pairs run a tiled GEMM on the matrix
+ *           cores (128 pairs x 128 weight rows per workgroup, the weights dequantized to
+ *           fp16 in LDS -- sign times block scale, plus the outliers -- and the rotated
+ *           activations in fp16: each rounding ~2^-12 relative, results within the
+ *           rel-L2 bar, not bit-equal to the decode path), and the others run work
+ *           items of up to 4 pairs of one expert through the decode GEMV (bit-equal to
+ *           the decode path).  GALE_GROUPED_ITEMS / GALE_GROUPED_GEMM force one kind
+ *           for every expert.
  * Flags GALE_PATH_DECODE / GALE_PATH_GROUPED force a path (decode takes at most 64
  * tokens).  The workspace depends on the path (gale_moe_workspace_bytes with the same
  * flags). */

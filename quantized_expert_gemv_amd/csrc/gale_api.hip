@@ -3,6 +3,7 @@
 // between host and device; every launch goes on the caller's stream.
 #include <cstdarg>
 #include <cstdio>
+#include <climits>
 #include <cstring>
 
 #include "gale_internal.h"
@@ -92,7 +93,9 @@ static FfnWs ffn_ws(int hidden, int inter, int64_t n_x, int64_t n_pairs) {
 }
 
 struct MoeWs {
-  size_t idx, w, offsets, perm, chunk, items, n_items, ra_x, h, ra_h, yp, total;
+  size_t idx, w, offsets, perm, chunk, items, n_items, ra_x, h, ra_h, yp;   // decode / items
+  size_t tiles, xt16, ht16;                                                 // grouped GEMM
+  size_t total;
 };
 // Upper bound on the work items of T tokens: every item holds at least one pair, and
 // each expert's run of pairs ends in at most one partly filled item.
@@ -100,8 +103,24 @@ static int64_t moe_item_bound(int T, int E, int k, int slots) {
   const int64_t P = (int64_t)T * k;
   return std::min<int64_t>(P, std::min<int64_t>(E, P) + (P + slots - 1) / slots);
 }
-static MoeWs moe_ws(int T, int E, int k, int hidden, int inter, bool grouped) {
+// The same for the GEMM tiles of kGemmBM pairs.
+static int64_t moe_tile_bound(int T, int E, int k) {
+  const int64_t P = (int64_t)T * k;
+  return std::min<int64_t>(P, std::min<int64_t>(E, P) + (P + kGemmBM - 1) / kGemmBM);
+}
+enum MoePath { kDecode = 0, kGroupedItems = 1, kGroupedGemm = 2, kGroupedHybrid = 3 };
+// Experts with at least this many pairs take the tile GEMM in the hybrid grouped path.
+constexpr int kGemmMinPairs = 64;
+static MoePath moe_path(int n_tok, uint32_t flags) {
+  const bool grouped = (flags & GALE_PATH_GROUPED) || (!(flags & GALE_PATH_DECODE) && n_tok > GALE_MAX_DECODE_TOKENS);
+  if (!grouped) return kDecode;
+  if (flags & GALE_GROUPED_ITEMS) return kGroupedItems;
+  if (flags & GALE_GROUPED_GEMM) return kGroupedGemm;
+  return kGroupedHybrid;
+}
+static MoeWs moe_ws(int T, int E, int k, int hidden, int inter, MoePath path) {
   MoeWs w;
+  memset(&w, 0, sizeof(w));
   const int64_t P = (int64_t)T * k;
   const int slots = pick_slots(T);
   size_t o = 0;
@@ -109,13 +128,20 @@ static MoeWs moe_ws(int T, int E, int k, int hidden, int inter, bool grouped) {
   w.w = o; o += align256(4 * P);
   w.offsets = o; o += align256(4 * (size_t)(E + 1));
   w.perm = o; o += align256(4 * P);
-  w.chunk = o; o += grouped ? align256(route_chunk_count_bytes(T, E)) : 0;
-  w.items = o; o += align256(sizeof(WorkItem) * (size_t)moe_item_bound(T, E, k, slots));
+  w.chunk = o; o += path != kDecode ? align256(route_chunk_count_bytes(T, E)) : 0;
   w.n_items = o; o += 256;
-  w.ra_x = o; o += align256(ra_bytes(hidden) * (size_t)T);
   w.h = o; o += align256((size_t)4 * inter * P);
-  w.ra_h = o; o += align256(ra_bytes(inter) * (size_t)P);
   w.yp = o; o += align256((size_t)4 * hidden * P);
+  if (path == kGroupedGemm || path == kGroupedHybrid) {
+    w.tiles = o; o += align256(sizeof(GemmTile) * (size_t)moe_tile_bound(T, E, k));
+    w.xt16 = o; o += align256((size_t)2 * hidden * T);
+    w.ht16 = o; o += align256((size_t)2 * inter * P);
+  }
+  if (path != kGroupedGemm) {
+    w.items = o; o += align256(sizeof(WorkItem) * (size_t)moe_item_bound(T, E, k, slots));
+    w.ra_x = o; o += align256(ra_bytes(hidden) * (size_t)T);
+    w.ra_h = o; o += align256(ra_bytes(inter) * (size_t)P);
+  }
   w.total = o;
   return w;
 }
@@ -400,8 +426,7 @@ extern "C" int gale_expert_ffn(int32_t hidden, int32_t inter, const gale_expert*
 extern "C" size_t gale_moe_workspace_bytes(int32_t n_tok, int32_t n_experts, int32_t top_k, int32_t hidden,
                                            int32_t inter, uint32_t flags) {
   if (n_tok < 1 || n_experts < 1 || top_k < 1 || hidden < 1024 || inter < 1024) return 0;
-  const bool grouped = (flags & GALE_PATH_GROUPED) || (!(flags & GALE_PATH_DECODE) && n_tok > GALE_MAX_DECODE_TOKENS);
-  return moe_ws(n_tok, n_experts, top_k, hidden, inter, grouped).total;
+  return moe_ws(n_tok, n_experts, top_k, hidden, inter, moe_path(n_tok, flags)).total;
 }
 
 extern "C" int gale_moe_layer_fwd(int32_t hidden, int32_t inter, const gale_expert* experts_dev,
@@ -424,49 +449,87 @@ extern "C" int gale_moe_layer_fwd(int32_t hidden, int32_t inter, const gale_expe
     return GALE_ERR_ALIGN;
   }
   if ((flags & GALE_PATH_DECODE) && (flags & GALE_PATH_GROUPED)) { set_error("%s: both paths forced", fn); return GALE_ERR_SHAPE; }
-  const bool grouped = (flags & GALE_PATH_GROUPED) || (!(flags & GALE_PATH_DECODE) && n_tok > GALE_MAX_DECODE_TOKENS);
-  if (!grouped && n_tok > GALE_MAX_DECODE_TOKENS) {
+  const MoePath path = moe_path(n_tok, flags);
+  if (path == kDecode && n_tok > GALE_MAX_DECODE_TOKENS) {
     set_error("%s: the decode path takes at most %d tokens", fn, GALE_MAX_DECODE_TOKENS);
     return GALE_ERR_SHAPE;
   }
-  const MoeWs W = moe_ws(n_tok, n_experts, top_k, hidden, inter, grouped);
+  const MoeWs W = moe_ws(n_tok, n_experts, top_k, hidden, inter, path);
   if (ws_bytes < W.total) { set_error("%s: workspace %zu < %zu bytes", fn, ws_bytes, W.total); return GALE_ERR_WORKSPACE; }
   uint8_t* base = reinterpret_cast<uint8_t*>(ws);
   int32_t* idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(base + W.idx);
   float* wts = topk_w ? topk_w : reinterpret_cast<float*>(base + W.w);
-  WorkItem* items = reinterpret_cast<WorkItem*>(base + W.items);
+  int32_t* offsets = reinterpret_cast<int32_t*>(base + W.offsets);
+  int32_t* perm = reinterpret_cast<int32_t*>(base + W.perm);
   int32_t* n_items = reinterpret_cast<int32_t*>(base + W.n_items);
-  uint8_t* ra_x = base + W.ra_x;
   float* h = reinterpret_cast<float*>(base + W.h);
-  uint8_t* ra_h = base + W.ra_h;
   float* yp = reinterpret_cast<float*>(base + W.yp);
   const int P = n_tok * top_k;
   const int slots = pick_slots(n_tok);
   const gale_matrix* table = reinterpret_cast<const gale_matrix*>(experts_dev);
-  if (grouped) {
-    // chunked top-k, stable sort of the pairs by expert, then the per-expert work items
-    int32_t* offsets = reinterpret_cast<int32_t*>(base + W.offsets);
-    int32_t* perm = reinterpret_cast<int32_t*>(base + W.perm);
+  if (path != kDecode) {
+    // chunked top-k and a stable sort of the pairs by expert
     st = hip_status(fn, launch_route_large(logits, n_tok, n_experts, top_k, idx, wts,
                                            reinterpret_cast<int32_t*>(base + W.chunk), offsets, perm, stream));
     if (st) return st;
-    st = hip_status(fn, launch_build_items(offsets, perm, n_experts, slots, items, n_items, stream));
-    if (st) return st;
-    st = hip_status(fn, launch_prep(x, GALE_F16, hidden, n_tok, hidden, 0, ra_x, ra_bytes(hidden), stream));
-  } else {
+  }
+  const bool use_items = path != kGroupedGemm;
+  const bool use_gemm = path == kGroupedGemm || path == kGroupedHybrid;
+  WorkItem* items = reinterpret_cast<WorkItem*>(base + W.items);
+  uint8_t* ra_x = base + W.ra_x;
+  uint8_t* ra_h = base + W.ra_h;
+  GemmTile* tiles = reinterpret_cast<GemmTile*>(base + W.tiles);
+  int32_t* n_tiles = n_items + 16;
+  uint16_t* xt16 = reinterpret_cast<uint16_t*>(base + W.xt16);
+  uint16_t* ht16 = reinterpret_cast<uint16_t*>(base + W.ht16);
+  const int max_tiles = use_gemm ? (int)moe_tile_bound(n_tok, n_experts, top_k) : 0;
+  // hybrid: experts with at least kGemmMinPairs pairs run as GEMM tiles, the rest as items
+  const int split = path == kGroupedHybrid ? kGemmMinPairs : (path == kGroupedGemm ? 1 : INT_MAX);
+  if (path == kDecode) {
     st = hip_status(fn, launch_route_prep(logits, n_tok, n_experts, top_k, idx, wts, items, n_items, slots, x,
                                           GALE_F16, hidden, ra_x, ra_bytes(hidden), stream));
+    if (st) return st;
+  } else {
+    if (use_items) {
+      st = hip_status(fn, launch_build_items(offsets, perm, n_experts, slots, split, items, n_items, stream));
+      if (st) return st;
+      st = hip_status(fn, launch_prep(x, GALE_F16, hidden, n_tok, hidden, 0, ra_x, ra_bytes(hidden), stream));
+      if (st) return st;
+    }
+    if (use_gemm) {
+      st = hip_status(fn, launch_build_tiles(offsets, n_experts, split, tiles, n_tiles, stream));
+      if (st) return st;
+      st = hip_status(fn, launch_rotate_f16(x, GALE_F16, n_tok, hidden, xt16, stream));
+      if (st) return st;
+    }
   }
-  if (st) return st;
   const int bound = (int)moe_item_bound(n_tok, n_experts, top_k, slots);
-  st = run_gemv_phase(fn, table, 3, 0, 1, inter, hidden, ra_x, 0, 0, 0, 0, items, n_items, top_k, bound, h,
-                      GALE_F32, 1, slots, flags, stream);
-  if (st) return st;
-  st = hip_status(fn, launch_prep(h, GALE_F32, inter, P, inter, 0, ra_h, ra_bytes(inter), stream));
-  if (st) return st;
-  st = run_gemv_phase(fn, table, 3, 2, 2, hidden, inter, ra_h, 0, 0, 0, 0, items, n_items, 1, bound, yp,
-                      GALE_F32, 0, slots, flags, stream);
-  if (st) return st;
+  // gate/up + SwiGLU: h[pair]
+  if (use_items) {
+    st = run_gemv_phase(fn, table, 3, 0, 1, inter, hidden, ra_x, 0, 0, 0, 0, items, n_items, top_k, bound, h,
+                        GALE_F32, 1, slots, flags, stream);
+    if (st) return st;
+  }
+  if (use_gemm) {
+    st = hip_status(fn, launch_grouped_gemm(table, 1, inter, hidden, offsets, perm, top_k, tiles, n_tiles, max_tiles,
+                                            xt16, h, inter, stream));
+    if (st) return st;
+  }
+  // rotate h; down: yp[pair]
+  if (use_items) {
+    st = hip_status(fn, launch_prep(h, GALE_F32, inter, P, inter, 0, ra_h, ra_bytes(inter), stream));
+    if (st) return st;
+    st = run_gemv_phase(fn, table, 3, 2, 2, hidden, inter, ra_h, 0, 0, 0, 0, items, n_items, 1, bound, yp,
+                        GALE_F32, 0, slots, flags, stream);
+    if (st) return st;
+  }
+  if (use_gemm) {
+    st = hip_status(fn, launch_rotate_f16(h, GALE_F32, P, inter, ht16, stream));
+    if (st) return st;
+    st = hip_status(fn, launch_grouped_gemm(table, 0, hidden, inter, offsets, perm, top_k, tiles, n_tiles,
+                                            max_tiles, ht16, yp, hidden, stream));
+    if (st) return st;
+  }
   return hip_status(fn, launch_combine(yp, wts, n_tok, top_k, hidden, y, GALE_F16, stream));
 }
 

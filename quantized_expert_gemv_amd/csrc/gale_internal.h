@@ -131,8 +131,22 @@ hipError_t launch_combine(const float* ypairs, const float* w, int n_tok, int k,
 hipError_t launch_cast(const float* src, void* dst, int dst_dtype, int64_t n, hipStream_t s);
 
 // grouped path: work items of at most `slots` pairs per expert from the sorted pairs
-hipError_t launch_build_items(const int32_t* offsets, const int32_t* perm, int n_exp, int slots, WorkItem* items,
-                              int32_t* n_items, hipStream_t s);
+hipError_t launch_build_items(const int32_t* offsets, const int32_t* perm, int n_exp, int slots, int max_pairs,
+                              WorkItem* items, int32_t* n_items, hipStream_t s);
+// grouped GEMM: tiles of kGemmBM sorted pairs of one expert
+constexpr int kGemmBM = 128;
+struct GemmTile {
+  int32_t expert, m0;
+};
+hipError_t launch_build_tiles(const int32_t* offsets, int n_exp, int min_pairs, GemmTile* tiles, int32_t* n_tiles,
+                              hipStream_t s);
+// rows of K rotated into fp16 with every 8-column group in MFMA operand order
+hipError_t launch_rotate_f16(const void* x, int x_dtype, int64_t n_rows, int K, uint16_t* out, hipStream_t s);
+// gateup: out[pair][inter] = silu(w1 x~) * (w3 x~), A = rotated x by token; else out[pair][hidden] = w2 h~,
+// A = rotated h by pair (fp32 outputs)
+hipError_t launch_grouped_gemm(const gale_matrix* table, int gateup, int rows, int K, const int32_t* offsets,
+                               const int32_t* perm, int top_k, const GemmTile* tiles, const int32_t* n_tiles,
+                               int max_tiles, const uint16_t* A, float* out, int out_stride, hipStream_t s);
 
 void set_error(const char* fmt, ...);
 

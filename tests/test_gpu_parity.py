@@ -325,25 +325,27 @@ def test_moe_decode_layer(q, layer, T):
     assert err <= REL_L2_BAR
 
 
-def test_moe_grouped_equals_decode_bitwise(q, layer):
-    # both paths compute each token independently, so forcing the grouped (token-sorted)
-    # path on a decode-sized batch must reproduce the decode path bit for bit
+def test_moe_grouped_items_equal_decode_bitwise(q, layer):
+    # the grouped path's GEMV work items compute each token independently, so on a
+    # decode-sized batch they must reproduce the decode path bit for bit
     seed, canon, tab = layer
     T = 48
     x = gen_x(seed, (2000, T), T, 4096, device=DEV)
     lg = gen_logits_normal(seed, (2000, T), T, 256, device=DEV)
     yd, idd, wd = q.moe_layer_fwd(tab, 4096, 2048, lg, x, top_k=6, flags=q.GALE_PATH_DECODE)
-    yg, idg, wg = q.moe_layer_fwd(tab, 4096, 2048, lg, x, top_k=6, flags=q.GALE_PATH_GROUPED)
+    yg, idg, wg = q.moe_layer_fwd(tab, 4096, 2048, lg, x, top_k=6,
+                                  flags=q.GALE_PATH_GROUPED | q.GALE_GROUPED_ITEMS)
     assert torch.equal(idd, idg) and torch.equal(wd, wg)
     assert torch.equal(yd, yg)
 
 
 @pytest.mark.parametrize("T,zipf", [(65, False), (2048, True)])
 def test_moe_grouped_prefill(q, layer, T, zipf):
-    """Grouped path at a ragged size just past the decode limit and at the prefill
-    workload (2048 tokens, Zipf(1.1)-skewed top-6 of 256): routing exact for every
-    token, sampled tokens against the oracle, the leading 64 tokens bit-identical to
-    the decode path run on them alone, and run-to-run determinism."""
+    """Grouped path (tile GEMM for the busy experts, GEMV items for the rest) at a ragged
+    size just past the decode limit and at the prefill workload (2048 tokens,
+    Zipf(1.1)-skewed top-6 of 256): routing exact for every token, sampled tokens
+    against the oracle, every token against the all-items and all-GEMM variants, and
+    run-to-run determinism."""
     seed, canon, tab = layer
     x = gen_x(seed, (3000, T), T, 4096, device=DEV)
     gen = gen_logits_zipf if zipf else gen_logits_normal
@@ -361,10 +363,60 @@ def test_moe_grouped_prefill(q, layer, T, zipf):
     expert_of = lambda e: tuple(m.numpy() for m in canon[e])  # noqa: E731
     yref, _, _ = O.moe(expert_of, lg.cpu().numpy()[sample], x.cpu().numpy()[sample], k=6)
     err = O.rel_l2(np_of(y[sample]), yref).max()
-    print(f"grouped T={T} max expert load {counts.max()} rel-L2 {err:.3e}")
+    # every expert through the items path, and every expert through the tile GEMM
+    yi, _, _ = q.moe_layer_fwd(tab, 4096, 2048, lg, x, top_k=6, flags=q.GALE_PATH_GROUPED | q.GALE_GROUPED_ITEMS)
+    yg, _, _ = q.moe_layer_fwd(tab, 4096, 2048, lg, x, top_k=6, flags=q.GALE_PATH_GROUPED | q.GALE_GROUPED_GEMM)
+    err_items = O.rel_l2(np_of(y), np_of(yi)).max()
+    err_gemm = O.rel_l2(np_of(yg), np_of(yi)).max()
+    err_gemm_ref = O.rel_l2(np_of(yg[sample]), yref).max()
+    print(f"grouped T={T} max expert load {counts.max()} rel-L2 vs oracle {err:.3e} (GEMM only {err_gemm_ref:.3e}), "
+          f"vs items path {err_items:.3e} (GEMM only {err_gemm:.3e})")
+    assert err <= REL_L2_BAR and err_gemm_ref <= REL_L2_BAR
+    assert err_items <= REL_L2_BAR and err_gemm <= REL_L2_BAR
+
+
+def outlier_edge_dict(N, K, seed):
+    """Random signs and block scales; outliers per row cycling through 0, 1, 300 and
+    round(0.01 K), one row with columns 0 and K - 1 only."""
+    rng = np.random.default_rng(seed)
+    rp, cols, vals = [0], [], []
+    for n in range(N):
+        cnt = [0, 1, 300, int(0.01 * K + 0.5)][n % 4]
+        cs = np.sort(rng.choice(K, size=cnt, replace=False)) if cnt else np.zeros(0, dtype=np.int64)
+        if n == 5:
+            cs = np.array([0, K - 1])
+        cols.extend(cs.tolist())
+        vals.extend(rng.integers(-8, 8, size=len(cs)).tolist())
+        rp.append(len(cols))
+    nib = [v & 0xF for v in vals] + ([0] if len(vals) % 2 else [])
+    return {"rows": N, "cols": K, "signs": rng.integers(0, 2 ** 32, size=(N, K // 32), dtype=np.uint64).astype(np.uint32),
+            "block_scales": (np.abs(rng.standard_normal((N, K // 128))) * 0.02).astype(np.float16),
+            "row_scales": np.full(N, 0.05, dtype=np.float16), "row_ptr": np.array(rp),
+            "out_cols": np.array(cols, dtype=np.uint16),
+            "out_vals": np.array([nib[i] | (nib[i + 1] << 4) for i in range(0, len(nib), 2)], dtype=np.uint8)}
+
+
+def test_moe_grouped_gemm_outlier_edges(q):
+    # w2 rows carry 0, 1, 300 or 20 outliers (too many for the GEMM's LDS staging, so
+    # the tiles read them from HBM); w1/w3 are standard (staged); tiles partly filled
+    E, T = 4, 80
+    seed = config_seed(12)
+    w13 = gen_matrices(seed, [(e, m) for e in range(E) for m in (0, 1)], 2048, 4096)
+    experts_np, packed = [], []
+    for e in range(E):
+        d2 = outlier_edge_dict(4096, 2048, 100 + e)
+        m1, m3 = w13[2 * e], w13[2 * e + 1]
+        experts_np.append((m1.numpy(), m3.numpy(), d2))
+        packed.append((q.pack_matrix(m1.to(DEV)), q.pack_matrix(m3.to(DEV)), q.pack_matrix(canon_from_dict(d2))))
+    tab = q.expert_table(packed)
+    x = gen_x(seed, (1,), T, 4096, device=DEV)
+    lg = gen_logits_normal(seed, (2,), T, E, device=DEV)
+    y, idx, w = q.moe_layer_fwd(tab, 4096, 2048, lg, x, top_k=2, flags=q.GALE_PATH_GROUPED | q.GALE_GROUPED_GEMM)
+    yref, ridx, _ = O.moe(lambda e: experts_np[e], lg.cpu().numpy(), x.cpu().numpy(), k=2)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    err = O.rel_l2(np_of(y), yref).max()
+    print(f"grouped GEMM outlier edges rel-L2 {err:.3e}")
     assert err <= REL_L2_BAR
-    yd, _, _ = q.moe_layer_fwd(tab, 4096, 2048, lg[:64].contiguous(), x[:64].contiguous(), top_k=6)
-    assert torch.equal(yd, y[:64])
 
 
 def test_moe_closed_form(q):
