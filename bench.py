@@ -47,7 +47,7 @@ PREFILL_TOKENS = 2048
 PREFILL_FLOP = 2 * TOPK * PREFILL_TOKENS * 3 * INTER * HIDDEN      # dense-equivalent, 618.5 GFLOP
 MFMA_FP16_PEAK_TFLOPS = 2500.0
 CEIL_BYTES = 1 << 30            # one side of the streaming-ceiling kernel
-GEMV_SOURCES = ("gale_gemv.hip", "gale_decode.h", "gale_internal.h")
+GEMV_SOURCES = ("gale_gemv.hip", "gale_gemv_core.h", "gale_decode.h", "gale_internal.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_kernel_traffic.txt")
 
 

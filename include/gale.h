@@ -64,6 +64,8 @@ extern "C" {
 #define GALE_PATH_GROUPED 0x20u  /* gale_moe_layer_fwd: force the grouped (token-sorted) path */
 #define GALE_GROUPED_ITEMS 0x40u /* gale_moe_layer_fwd grouped path: GEMV work items only */
 #define GALE_GROUPED_GEMM  0x80u /* gale_moe_layer_fwd grouped path: fp16 MFMA tile GEMM only */
+#define GALE_DECODE_STAGED 0x1000u /* gale_moe_layer_fwd, one token: the five-launch decode sequence
+                                      instead of the one-launch layer kernel */
 
 /* ---- limits -------------------------------------------------------------- */
 #define GALE_FWHT_N        1024   /* rotation block ("blocked FWHT-1024") */
@@ -220,6 +222,15 @@ size_t gale_moe_workspace_bytes(int32_t n_tok, int32_t n_experts, int32_t top_k,
  * x, y: fp16 [n_tok][hidden].  topk_idx (int32 [n_tok][top_k]) and topk_w (fp32) are
  * written when non-NULL.  Two paths, same results bit for bit on any token:
  *   decode  (n_tok <= 64): one workgroup routes all tokens and lists the work items;
+ *           with one token the whole layer is a single persistent launch (the
+ *           DeepSeek-V4-Pro GALE page's batch-1 notes put the floor in launches):
+ *           every workgroup routes the token itself, the gate/up and down units run
+ *           back to back, and counters in the workspace hand each finished block of
+ *           h and each finished row group of y to the workgroup that completes it.
+ *           The counters need no initialisation (they carry a generation number),
+ *           so the workspace stays plain scratch, but calls sharing one workspace
+ *           must not overlap in time (true of every workspace).  GALE_DECODE_STAGED
+ *           selects the five-launch sequence instead (same results bit for bit);
  *   grouped (n_tok > 64):  chunked top-k and a stable sort of the (token, slot) pairs
  *           by expert; then experts with many pairs run a tiled GEMM on the matrix
  *           cores (128 pairs x 128 weight rows per workgroup, the weights dequantized to

@@ -6,7 +6,7 @@ memory and streams only.
 """
 from .binding import (  # noqa: F401
     GALE_F16, GALE_F32, GALE_X_ROTATED, GALE_X_PREPARED, prepared_bytes, prepare_activations, GALE_PATH_DECODE, GALE_PATH_GROUPED,
-    GALE_GROUPED_ITEMS, GALE_GROUPED_GEMM, GaleError, PackedMatrix,
+    GALE_GROUPED_ITEMS, GALE_GROUPED_GEMM, GALE_DECODE_STAGED, GaleError, PackedMatrix,
     DescriptorTable, lib, exported_symbols, packed_sizes, check_canonical, pack_host, unpack_host, pack_device,
     pack_matrix, matrix_table, expert_table, debug_unpack_signs, debug_unpack_outliers, fwht1024,
     expert_gemv, expert_ffn, moe_layer_fwd, route_topk, gemv_workspace_bytes, ffn_workspace_bytes,

@@ -25,6 +25,7 @@ GALE_PATH_DECODE = 0x10
 GALE_PATH_GROUPED = 0x20
 GALE_GROUPED_ITEMS = 0x40
 GALE_GROUPED_GEMM = 0x80
+GALE_DECODE_STAGED = 0x1000
 STATUS = {0: "GALE_OK", -1: "GALE_ERR_NULL", -2: "GALE_ERR_SHAPE", -3: "GALE_ERR_DTYPE", -4: "GALE_ERR_ALIGN",
           -5: "GALE_ERR_WORKSPACE", -6: "GALE_ERR_UNSUPPORTED", -7: "GALE_ERR_FORMAT", -8: "GALE_ERR_HIP"}
 

@@ -11,7 +11,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libgale.so")
-SOURCES = ["gale_api.hip", "gale_pack.hip", "gale_fwht.hip", "gale_gemv.hip", "gale_moe.hip", "gale_prefill.hip"]
+SOURCES = ["gale_api.hip", "gale_pack.hip", "gale_fwht.hip", "gale_gemv.hip", "gale_moe.hip", "gale_prefill.hip",
+           "gale_decode_layer.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # packed-fp32 VALU forms are disabled for correctness on this hardware

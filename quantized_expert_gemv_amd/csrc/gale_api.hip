@@ -95,6 +95,7 @@ static FfnWs ffn_ws(int hidden, int inter, int64_t n_x, int64_t n_pairs) {
 struct MoeWs {
   size_t idx, w, offsets, perm, chunk, items, n_items, ra_x, h, ra_h, yp;   // decode / items
   size_t tiles, xt16, ht16;                                                 // grouped GEMM
+  size_t sync;                                                              // one-launch decode
   size_t total;
 };
 // Upper bound on the work items of T tokens: every item holds at least one pair, and
@@ -141,6 +142,9 @@ static MoeWs moe_ws(int T, int E, int k, int hidden, int inter, MoePath path) {
     w.items = o; o += align256(sizeof(WorkItem) * (size_t)moe_item_bound(T, E, k, slots));
     w.ra_x = o; o += align256(ra_bytes(hidden) * (size_t)T);
     w.ra_h = o; o += align256(ra_bytes(inter) * (size_t)P);
+  }
+  if (path == kDecode && T == 1) {
+    w.sync = o; o += align256(decode_layer_sync_bytes(hidden, inter));
   }
   w.total = o;
   return w;
@@ -485,6 +489,13 @@ extern "C" int gale_moe_layer_fwd(int32_t hidden, int32_t inter, const gale_expe
   const int max_tiles = use_gemm ? (int)moe_tile_bound(n_tok, n_experts, top_k) : 0;
   // hybrid: experts with at least kGemmMinPairs pairs run as GEMM tiles, the rest as items
   const int split = path == kGroupedHybrid ? kGemmMinPairs : (path == kGroupedGemm ? 1 : INT_MAX);
+  if (path == kDecode && n_tok == 1 && !(flags & GALE_DECODE_STAGED) && decode_layer_supported(hidden, inter)) {
+    // one launch for the whole layer; the counters live in the workspace
+    const int forced = (int)((flags >> 8) & 0xF);
+    return hip_status(fn, launch_decode_layer(table, n_experts, logits, top_k, x, hidden, inter, y, topk_idx, topk_w,
+                                              h, yp, reinterpret_cast<uint64_t*>(base + W.sync),
+                                              forced ? 1 << (forced - 1) : 2, stream));
+  }
   if (path == kDecode) {
     st = hip_status(fn, launch_route_prep(logits, n_tok, n_experts, top_k, idx, wts, items, n_items, slots, x,
                                           GALE_F16, hidden, ra_x, ra_bytes(hidden), stream));

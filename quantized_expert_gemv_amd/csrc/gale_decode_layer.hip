@@ -1,0 +1,648 @@
+// One-launch decode of a routed-expert MoE layer for a single token.
+//
+// What it computes is the decode MoE layer of the DeepSeek-V4-Flash GALE model
+// card ("What is in the pack": w1/w3/w2 per expert; "Measured performance": 6
+// routed experts per token and layer): top-k routing with softmax-renormalised
+// weights, the SwiGLU FFN of every selected expert out of its three GALE
+// matrices, and the weighted combine.  The DeepSeek-V4-Pro GALE page (its
+// "Measured" notes on batch-1 decode) puts the batch-1 floor in kernel launches
+// and per-expert unpacks, not in data movement; here the whole layer is one
+// persistent launch instead of five.
+//
+// Plan.  The grid is one workgroup per CU, all resident together.  Each
+// workgroup, with no help from the others:
+//   * routes the token (one wavefront; every workgroup gets the same answer) and
+//     prepares x's activation record in LDS (rotation, fp8 terms) while routing;
+//   * streams its share of the gate/up units (R row tiles of w1 and w3 of one
+//     selected expert), writing h = silu(w1 x~) * (w3 x~);
+//   * streams its share of the down units (Q x R row tiles of w2).
+// Two global dependencies are resolved with counters in the workspace:
+//   * a down unit waits until every gate/up unit of its pair has stored its rows
+//     of h, then rotates h into its own LDS record (one wavefront per 1024-block);
+//   * the down unit that completes a row group for the last of the k pairs sums
+//     the k partial outputs in slot order into y ("last arriver").
+// The down units' weight loads go out before the wait, so they are in flight while
+// the workgroup waits.  Only down units wait, only on gate/up work, and every
+// workgroup is resident, so the waits end; each is also bounded in time and records
+// a timeout in the workspace's error word rather than spinning on.
+//
+// Counters carry the call's generation in their upper 32 bits.  The workgroup that
+// combines the last down row group (after which no counter is touched again in the
+// call) re-arms every counter for the next generation; an arrival that finds a word
+// of another generation (a workspace's first use) re-tags it with a compare-and-swap,
+// so the workspace needs no initialisation.
+//
+// The per-unit arithmetic is the sign-plane GEMV's (gale_gemv_core.h) in the same
+// order, so the outputs equal those of the multi-launch decode sequence.
+#include "gale_internal.h"
+#include "gale_decode.h"
+#include "gale_gemv_core.h"
+#include "gale_rotate.h"
+#include "gale_route.h"
+
+namespace gale {
+
+// ---- synchronisation words (uint64, in the workspace) -----------------------
+// sync words (each counter is spread over kSubs words, so that few arrivals meet
+// on one word):
+//   [0] generation, [1] row-group subsets combined, [2] error bits (sticky);
+//   [8 + kSubs j + s] gate/up units of pair j with row group = s (mod kSubs) done;
+//   [72 + s] down row groups = s (mod kSubs) combined;
+//   [80 + g] pairs done in down row group g.
+constexpr int kSubs = 8;
+constexpr int kSyncTop = 1;
+constexpr int kSyncErr = 2;
+constexpr int kSyncReady = 8;
+constexpr int kSyncRowSub = kSyncReady + GALE_MAX_TOPK * kSubs;
+constexpr int kSyncRows = kSyncRowSub + kSubs;
+
+// Units of a phase with RG row groups per pair that land on sub-counter s.
+__host__ __device__ inline int sub_count(int RG, int s) { return s < RG ? (RG - s + kSubs - 1) / kSubs : 0; }
+
+__device__ __forceinline__ uint64_t sync_load(uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One arrival at a generation-tagged counter; returns the count including it.
+__device__ __forceinline__ uint32_t arrive(uint64_t* ctr, uint32_t gen) {
+  const uint64_t old = __hip_atomic_fetch_add(ctr, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if ((uint32_t)(old >> 32) == gen) return (uint32_t)old + 1u;
+  // a word of another generation: count this arrival against the word re-tagged
+  // with this generation (the add above went to the stale value and is dropped)
+  uint64_t cur = sync_load(ctr);
+  for (;;) {
+    const uint64_t want = (uint32_t)(cur >> 32) == gen ? cur + 1u : (((uint64_t)gen << 32) | 1u);
+    if (__hip_atomic_compare_exchange_strong(ctr, &cur, want, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT))
+      return (uint32_t)want;
+  }
+}
+
+// Wave 0 polls the kSubs sub-counters of one count until each reads (gen, its
+// share of RG); about 0.1 s at most, then the error word records the timeout and
+// the caller proceeds.
+constexpr int kWaitPolls = 1 << 17;
+__device__ __forceinline__ void wait_subs(uint64_t* base, uint32_t gen, int RG, uint64_t* err, int lane) {
+  const bool watch = lane < kSubs && lane < RG;
+  const uint64_t want = ((uint64_t)gen << 32) | (uint32_t)sub_count(RG, lane);
+  for (int i = 0;; ++i) {
+    const bool ok = !watch || sync_load(base + (watch ? lane : 0)) == want;
+    if (__all(ok)) break;
+    if (i == kWaitPolls) {
+      if (lane == 0) __hip_atomic_fetch_or(err, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// ---- data handed between workgroups --------------------------------------------
+// The workgroups of one XCD share an L2 that the other XCDs' L2s do not see, and a
+// device-scope fence would write back or drop a whole L2.  So every value that one
+// workgroup hands to another (h, its rotated records, the partial outputs) is stored
+// and loaded with device-scope (coherent) accesses, and a producer only waits for its
+// own stores to complete before it counts them.
+__device__ __forceinline__ void cst_f32(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float cld_f32(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void cst_u64(void* p, uint64_t v) {
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t cld_u64(const void* p) {
+  return __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<void*>(p)), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t pack2(uint32_t lo, uint32_t hi) { return ((uint64_t)hi << 32) | lo; }
+
+// Wait until this wavefront's stores (and loads) have completed, with no compiler
+// reordering of memory accesses across the wait.
+__device__ __forceinline__ void stores_done() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// ---- geometry of one phase for this thread ------------------------------------
+// Gate/up: wave w = (matrix half w / C, chunk w % C); a unit is R row tiles of both
+// matrices; waves 0 .. 2R-1 serve the outliers of its 2 x 16 R rows.
+// Down: wave w = (row group w / C, chunk w % C); a unit is Q row groups of R tiles;
+// waves 0 .. QR-1 serve the outliers of its 16 Q R rows.
+struct PhaseGeo {
+  int K, C, rows, ntiles;
+  int unit_tiles, grp_tile, unit_rows, orow;
+  int smat, omat;
+  bool orole;
+  uint32_t sw_tile, sc_tile, sw_lane, sc_lane;
+};
+
+template <int R>
+__device__ __forceinline__ PhaseGeo phase_geo(bool down, int K, int rows, int wave, int lane, int Q) {
+  PhaseGeo G;
+  G.K = K;
+  G.C = K >> 10;
+  G.rows = rows;
+  G.ntiles = rows >> 4;
+  const int grp = uni(wave / G.C), c = uni(wave - grp * G.C);
+  if (down) {
+    G.unit_tiles = Q * R;
+    G.grp_tile = grp * R;
+    G.unit_rows = Q * R * 16;
+    G.orow = 16 * wave;
+    G.smat = 2;
+    G.omat = 2;
+    G.orole = wave < Q * R;
+  } else {
+    G.unit_tiles = R;
+    G.grp_tile = 0;
+    G.unit_rows = R * 16;
+    G.orow = 16 * (wave % R);
+    G.smat = grp;
+    G.omat = uni(wave < 2 * R ? wave / R : 0);
+    G.orole = wave < 2 * R;
+  }
+  G.sw_tile = (uint32_t)G.C * 2048u;
+  G.sc_tile = (uint32_t)G.C * 256u;
+  G.sw_lane = (uint32_t)c * 2048u + 16u * (uint32_t)lane;
+  G.sc_lane = (uint32_t)c * 256u + 16u * (uint32_t)(lane & 15);
+  return G;
+}
+
+// Row of this thread's outlier role in row group rg, clamped to [0, rows].
+__device__ __forceinline__ int role_row(const PhaseGeo& G, int lane, int rg, bool* valid) {
+  const int n = rg * G.unit_rows + G.orow + (lane >> 2);
+  *valid = G.orole && n < G.rows;
+  return n < G.rows ? n : G.rows;
+}
+
+struct LayerDesc {
+  const char* signs;
+  const char* scales;
+  const char* rsc;
+  const int32_t* rptr;
+  const char* ocols;
+  const char* ovals;
+};
+
+__device__ __forceinline__ LayerDesc layer_desc(const gale_matrix* table, const PhaseGeo& G, int expert) {
+  const auto* t = as_const(table) + expert * 3;
+  LayerDesc d;
+  d.signs = reinterpret_cast<const char*>(t[G.smat].signs);
+  d.scales = reinterpret_cast<const char*>(t[G.smat].block_scales);
+  d.rsc = reinterpret_cast<const char*>(t[G.omat].row_scales);
+  d.rptr = t[G.omat].row_ptr;
+  d.ocols = reinterpret_cast<const char*>(t[G.omat].out_cols);
+  d.ovals = reinterpret_cast<const char*>(t[G.omat].out_vals);
+  return d;
+}
+
+// Issue the loads of a unit at row group rg (rp0/rp1 of its row already in b), and
+// the CSR offsets of the row of the unit after it (geometry Gn, row group rgn).
+template <int R>
+__device__ __forceinline__ void issue_layer_unit(const PhaseGeo& G, int lane, int rg, const LayerDesc& dv,
+                                                 const PhaseGeo& Gn, int rgn, const LayerDesc& dn, UnitBuf<R>& b) {
+  const int t0 = rg * G.unit_tiles + G.grp_tile;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    int tile = t0 + r;
+    tile = tile < G.ntiles ? tile : G.ntiles - 1;
+    const uint32_t o = (uint32_t)tile * G.sw_tile + G.sw_lane;
+    const uint4 lo = ld16_stream(dv.signs, o);
+    const uint4 hi = ld16_stream(dv.signs, o + 1024u);
+    b.sw[r][0] = lo.x; b.sw[r][1] = lo.y; b.sw[r][2] = lo.z; b.sw[r][3] = lo.w;
+    b.sw[r][4] = hi.x; b.sw[r][5] = hi.y; b.sw[r][6] = hi.z; b.sw[r][7] = hi.w;
+    const uint4 sc = ld16_stream(dv.scales, (uint32_t)tile * G.sc_tile + G.sc_lane);
+    b.sc[r][0] = sc.x; b.sc[r][1] = sc.y; b.sc[r][2] = sc.z; b.sc[r][3] = sc.w;
+  }
+  // outlier entries of the wave's 16 rows: CSR range [e0, e1) from lanes 0 and 60
+  const int e0 = uni(__builtin_amdgcn_readlane(b.rp0, 0));
+  const int e1 = uni(__builtin_amdgcn_readlane(b.rp1, 60));
+  const bool any = e1 > e0;
+  const int cf = any ? (2 * e0) >> 4 : 0;
+  const int cl = any ? (2 * e1 - 1) >> 4 : 0;
+  const int vf = any ? (e0 >> 1) >> 4 : 0;
+  const int vl = any ? ((e1 - 1) >> 1) >> 4 : 0;
+  b.ocf = cf;
+  b.ovf = vf;
+#pragma unroll
+  for (int k = 0; k < kColChunks; ++k) {
+    int ch = cf + 64 * k + lane;
+    ch = ch < cl ? ch : cl;
+    b.oc[k] = ld16(dv.ocols, (uint32_t)ch * 16u);
+  }
+#pragma unroll
+  for (int k = 0; k < kValChunks; ++k) {
+    int ch = vf + 64 * k + lane;
+    ch = ch < vl ? ch : vl;
+    b.ov[k] = ld16(dv.ovals, (uint32_t)ch * 16u);
+  }
+  bool ok;
+  const int n = role_row(G, lane, rg, &ok);
+  b.rsc = *reinterpret_cast<const uint16_t*>(dv.rsc + 2u * (uint32_t)(n < G.rows ? n : G.rows - 1));
+  const int n2 = role_row(Gn, lane, rgn, &ok);
+  b.np0 = dn.rptr[n2];
+  b.np1 = dn.rptr[n2 + (n2 < Gn.rows ? 1 : 0)];
+}
+
+// A operands and exponent of chunk c from an activation record (LDS or global).
+__device__ __forceinline__ void record_activation(const uint8_t* rec, int K, int c, int lane, Act& a) {
+  const int nl = lane & 15, g = lane >> 4;
+  const int term = nl >> 2;
+  const uint8_t* tb = rec + ra_terms_off(K) + ((size_t)c * 4 + term) * 1024 + 32 * g;
+#pragma unroll
+  for (int d = 0; d < 8; ++d) a.A[d] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+  if ((nl & 3) == 0) {
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const uint4 a0 = *reinterpret_cast<const uint4*>(tb + 128 * d);
+      const uint4 a1 = *reinterpret_cast<const uint4*>(tb + 128 * d + 16);
+      a.A[d] = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+    }
+  }
+  a.pexp[0] = reinterpret_cast<const int32_t*>(rec + ra_p_off(K))[c];
+}
+
+// One wavefront rotates 1024-block c of h (written by other workgroups; coherent
+// loads) into an activation record in LDS: the arithmetic of prep_wave.
+__device__ __forceinline__ void prep_block_to_lds(const float* hv, int K, int c, uint8_t* rec, int lane) {
+  float f[16];
+  const float* src = hv + (size_t)c * 1024 + 16 * lane;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint64_t q = cld_u64(src + 2 * i);
+    f[2 * i] = __uint_as_float((uint32_t)q);
+    f[2 * i + 1] = __uint_as_float((uint32_t)(q >> 32));
+  }
+  PrepLane o;
+  prep_lane(f, lane, true, o);
+  float4* xo = reinterpret_cast<float4*>(reinterpret_cast<float*>(rec) + (size_t)c * 1024 + 16 * lane);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) xo[i] = make_float4(o.x[4 * i], o.x[4 * i + 1], o.x[4 * i + 2], o.x[4 * i + 3]);
+  uint8_t* terms = rec + ra_terms_off(K) + (size_t)c * 4 * 1024 + 16 * lane;
+#pragma unroll
+  for (int t = 0; t < kTerms; ++t)
+    *reinterpret_cast<uint4*>(terms + t * 1024) = make_uint4(o.t[t][0], o.t[t][1], o.t[t][2], o.t[t][3]);
+  if (lane == 0) reinterpret_cast<int32_t*>(rec + ra_p_off(K))[c] = o.p;
+}
+
+struct LayerParams {
+  const gale_matrix* table;  // [E][3]: w1, w3, w2
+  const float* logits;       // [E]
+  const void* x;             // fp16 [H]
+  __half* y;                 // fp16 [H]
+  int32_t* topk_idx;         // [k] or NULL
+  float* topk_w;             // [k] or NULL
+  float* h;                  // fp32 [k][I]
+  float* yp;                 // fp32 [k][H]
+  uint64_t* sync;            // counters, layout below
+  int E, k, H, I, Q;
+  int RGg, RGd;              // row groups per pair: gate/up and down
+};
+
+// LDS: the activation record of the current phase (x's, then each pair's h~), two
+// alternating sets of split-K and outlier sums, the waves' outlier slices, routing.
+template <int R>
+struct LayerLds {
+  static constexpr int RR = 16 * R;
+  __host__ __device__ static size_t red_off(int H, int I) { return ra_bytes(H > I ? H : I); }
+  __host__ __device__ static size_t ored_off(int H, int I) { return red_off(H, I) + 2 * 8 * RR * 4; }
+  __host__ __device__ static size_t wout_off(int H, int I) { return ored_off(H, I) + 2 * 128 * 4; }
+  __host__ __device__ static size_t misc_off(int H, int I) { return wout_off(H, I) + 8 * (size_t)kWaveOutBytes; }
+  __host__ __device__ static size_t bytes(int H, int I) { return misc_off(H, I) + 128; }
+};
+
+template <int R, bool DOWN>
+__device__ __forceinline__ void layer_unit(const LayerParams& L, const PhaseGeo& G, int wave, int lane, int pair,
+                                           int rg, UnitBuf<R>& cur, UnitBuf<R>& nxt, bool issue, int n_rg,
+                                           const LayerDesc& d1, int nn_rg, const LayerDesc& d2, int& act_key,
+                                           Act& act, uint8_t* rec, lds_f32* red, lds_f32* ored, lds_u8* wout,
+                                           const int32_t* s_exp, const float* s_w, uint32_t gen, bool armed) {
+  constexpr int RR = 16 * R;
+  const int tid = threadIdx.x;
+  lds_f32* xt = (lds_f32*)rec;
+
+  // 1. activation: x's record (LDS) for every gate/up unit; pair's h~ record for
+  //    down units, once its ready flag has counted all of its blocks
+  const int key = DOWN ? pair : -2;
+  if (key != act_key) {
+    if (DOWN) {
+      // every gate/up unit of the pair has stored its rows of h: rotate h into this
+      // workgroup's record (one wavefront per 1024-block)
+      if (wave == 0) wait_subs(L.sync + kSyncReady + kSubs * pair, gen, L.RGg, L.sync + kSyncErr, lane);
+      __syncthreads();
+      if (wave < G.C) prep_block_to_lds(L.h + (size_t)pair * L.I, G.K, wave, rec, lane);
+      __syncthreads();
+      record_activation(rec, G.K, uni(wave % G.C), lane, act);
+    } else {
+      record_activation(rec, G.K, uni(wave % G.C), lane, act);
+    }
+    __syncthreads();
+    block_sums<1>(act);
+    act_key = key;
+  }
+
+  // 2. this unit's outlier chunks into the wave's LDS slice
+  {
+    lds_v4* oc = reinterpret_cast<lds_v4*>(wout);
+#pragma unroll
+    for (int k = 0; k < kColChunks; ++k) oc[64 * k + lane] = to_v4(cur.oc[k]);
+#pragma unroll
+    for (int k = 0; k < kValChunks; ++k) oc[64 * (kColChunks + k) + lane] = to_v4(cur.ov[k]);
+  }
+
+  // 3. the next unit's loads behind this unit's arithmetic
+  if (issue) {
+    nxt.rp0 = cur.np0;
+    nxt.rp1 = cur.np1;
+    issue_layer_unit<R>(G, lane, n_rg, d1, G, nn_rg, d2, nxt);
+  }
+
+  // 4. sign pass over the wave's R tiles
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float acc[1];
+    sign_tile<1>(act, cur.sw[r], cur.sc[r], acc);
+    const float v = term_sum(ldexpf(acc[0], -act.pexp[0]));
+    if (lane < 16) red[wave * RR + r * 16 + lane] = v;
+  }
+
+  // 5. outliers: four lanes per row in CSR order, entries and x~ from LDS
+  {
+    bool valid;
+    const int n = role_row(G, lane, rg, &valid);
+    const int sub = lane & 3;
+    const lds_u16* lc = reinterpret_cast<const lds_u16*>(wout);
+    const lds_u8* lv = wout + 64 * 16 * kColChunks;
+    float o = 0.f;
+    const int cbase = 8 * cur.ocf, vbase = 16 * cur.ovf;
+    const int p_begin = cur.rp0 + sub, p_end = valid ? cur.rp1 : p_begin;
+    const int p_cap = min(cbase + 64 * 8 * kColChunks, 2 * (vbase + 64 * 16 * kValChunks));
+    const int p_mid = min(p_end, p_cap);
+    int p = p_begin;
+    for (; p + 28 < p_mid; p += 32) {
+      int col[8], by[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) { col[j] = lc[p + 4 * j - cbase]; by[j] = lv[((p + 4 * j) >> 1) - vbase]; }
+      float xv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xv[j] = xt[col[j]];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o = fmaf(nibble_value(by[j], p), xv[j], o);
+    }
+    for (; p < p_mid; p += 4) {
+      const int col = lc[p - cbase];
+      const float q = nibble_value(lv[(p >> 1) - vbase], p);
+      o = fmaf(q, xt[col], o);
+    }
+    if (p < p_end) {
+      // rows whose entries run past the staged chunks: the rest straight from memory
+      const LayerDesc dm = layer_desc(L.table, G, uni(s_exp[pair]));
+      for (; p < p_end; p += 4) {
+        const int col = reinterpret_cast<const uint16_t*>(dm.ocols)[p];
+        const float q = (float)outlier_value(reinterpret_cast<const uint8_t*>(dm.ovals), p);
+        o = fmaf(q, xt[col], o);
+      }
+    }
+    (void)n;
+    const float rscale = half_bits_to_float(cur.rsc);
+    o += __shfl_xor(o, 1, 64);
+    o += __shfl_xor(o, 2, 64);
+    if (G.orole && sub == 0) ored[16 * wave + (lane >> 2)] = o * rscale;
+  }
+  // every wave's partials are in LDS; the buffers alternate between units
+  __syncthreads();
+
+  // 6. wave 0: sum the split-K partials in a fixed order, add the outliers, store,
+  //    count the unit, and run the follow-up work of a last arrival
+  if (wave != 0) return;
+  if (!DOWN) {
+    for (int rr = lane; rr < RR; rr += 64) {
+      float a = 0.f, g = 0.f;
+      for (int q = 0; q < G.C; ++q) a += red[q * RR + rr];
+      for (int q = 0; q < G.C; ++q) g += red[(G.C + q) * RR + rr];
+      a = a + ored[rr];
+      g = g + ored[RR + rr];
+      cst_f32(L.h + (size_t)pair * L.I + rg * RR + rr, silu_f(a) * g);
+    }
+    stores_done();
+    if (lane == 0) {
+      uint64_t* w = L.sync + kSyncReady + kSubs * pair + rg % kSubs;
+      if (armed) (void)__hip_atomic_fetch_add(w, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else (void)arrive(w, gen);
+    }
+  } else {
+    const int Q = L.Q;
+    for (int e = lane; e < Q * RR; e += 64) {
+      const int q = e / RR, rr = e - q * RR;
+      float a = 0.f;
+      for (int c = 0; c < G.C; ++c) a += red[(q * G.C + c) * RR + rr];
+      a = a + ored[q * RR + rr];
+      cst_f32(L.yp + (size_t)pair * L.H + rg * Q * RR + e, a);
+    }
+    stores_done();
+    uint32_t cnt = 0;
+    if (lane == 0) cnt = arrive(L.sync + kSyncRows + rg, gen);
+    cnt = (uint32_t)__builtin_amdgcn_readfirstlane((int)cnt);
+    if (cnt == (uint32_t)L.k) {
+      // the last pair of this row group: y = sum over slots in order of w_j yp_j
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      for (int e = lane; e < Q * RR; e += 64) {
+        const int n = rg * Q * RR + e;
+        float v[GALE_MAX_TOPK];
+#pragma unroll
+        for (int j = 0; j < GALE_MAX_TOPK; ++j) v[j] = j < L.k ? cld_f32(L.yp + (size_t)j * L.H + n) : 0.f;
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < GALE_MAX_TOPK; ++j)
+          if (j < L.k) acc = fmaf(s_w[j], v[j], acc);
+        L.y[n] = __float2half_rn(acc);
+      }
+      const int sub = rg % kSubs;
+      uint32_t c1 = 0, c2 = 0;
+      if (lane == 0) {
+        c1 = arrive(L.sync + kSyncRowSub + sub, gen);
+        if (c1 == (uint32_t)sub_count(L.RGd, sub)) c2 = arrive(L.sync + kSyncTop, gen);
+      }
+      c2 = (uint32_t)__builtin_amdgcn_readfirstlane((int)c2);
+      if (c2 == (uint32_t)(L.RGd < kSubs ? L.RGd : kSubs)) {
+        const int words = kSyncRows + L.RGd;
+        const uint64_t next = (uint64_t)(gen + 1u) << 32;
+        for (int i = lane; i < words; i += 64)
+          if (i != 0 && i != kSyncErr) __hip_atomic_store(L.sync + i, next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) __hip_atomic_store(L.sync, (uint64_t)(gen + 1u), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+}
+
+// Descriptors of expert e's matrices that this wavefront reads in phase G.
+__device__ __forceinline__ LayerDesc phase_desc(const LayerParams& L, const PhaseGeo& G, const int32_t* s_exp,
+                                                int pair) {
+  return layer_desc(L.table, G, uni(s_exp[pair]));
+}
+
+// Units [u0, u1) of one phase (unit u = pair u / RG, row group u % RG), pipelined one
+// unit ahead.  The first unit's loads go out before its activation is waited for.
+template <int R, bool DOWN>
+__device__ __forceinline__ void run_phase(const LayerParams& L, const PhaseGeo& G, int wave, int lane, int u0,
+                                          int u1, int RG, uint8_t* rec, lds_f32* red0, lds_f32* ored0,
+                                          lds_u8* wout, const int32_t* s_exp, const float* s_w, uint32_t gen,
+                                          bool armed) {
+  constexpr int RR = 16 * R;
+  if (u0 >= u1) return;
+  UnitBuf<R> b0, b1;
+  Act act;
+  int act_key = -1;
+  int u = u0;
+  int pair = uni(u / RG), rg = uni(u - pair * RG);
+  int u_1 = u + 1 < u1 ? u + 1 : u;
+  int pair1 = uni(u_1 / RG), rg1 = uni(u_1 - pair1 * RG);
+  int u_2 = u + 2 < u1 ? u + 2 : u_1;
+  int pair2 = uni(u_2 / RG), rg2 = uni(u_2 - pair2 * RG);
+  LayerDesc dc = phase_desc(L, G, s_exp, pair);
+  LayerDesc d1 = pair1 == pair ? dc : phase_desc(L, G, s_exp, pair1);
+  LayerDesc d2 = pair2 == pair1 ? d1 : phase_desc(L, G, s_exp, pair2);
+  {
+    bool ok;
+    const int r0 = role_row(G, lane, rg, &ok);
+    b0.rp0 = dc.rptr[r0];
+    b0.rp1 = dc.rptr[r0 + (r0 < G.rows ? 1 : 0)];
+    issue_layer_unit<R>(G, lane, rg, dc, G, rg1, d1, b0);
+  }
+  for (;;) {
+    layer_unit<R, DOWN>(L, G, wave, lane, pair, rg, b0, b1, u + 1 < u1, rg1, d1, rg2, d2, act_key, act, rec, red0,
+                        ored0, wout, s_exp, s_w, gen, armed);
+    if (++u >= u1) break;
+    pair = pair1; rg = rg1; pair1 = pair2; rg1 = rg2; d1 = d2;
+    u_2 = u + 2 < u1 ? u + 2 : u1 - 1;
+    { const int pn = uni(u_2 / RG); rg2 = uni(u_2 - pn * RG); if (pn != pair2) d2 = phase_desc(L, G, s_exp, pn); pair2 = pn; }
+    layer_unit<R, DOWN>(L, G, wave, lane, pair, rg, b1, b0, u + 1 < u1, rg1, d1, rg2, d2, act_key, act, rec,
+                        red0 + 8 * RR, ored0 + 128, wout, s_exp, s_w, gen, armed);
+    if (++u >= u1) break;
+    pair = pair1; rg = rg1; pair1 = pair2; rg1 = rg2; d1 = d2;
+    u_2 = u + 2 < u1 ? u + 2 : u1 - 1;
+    { const int pn = uni(u_2 / RG); rg2 = uni(u_2 - pn * RG); if (pn != pair2) d2 = phase_desc(L, G, s_exp, pn); pair2 = pn; }
+  }
+}
+
+template <int R>
+__global__ void __launch_bounds__(512) decode_layer_kernel(const LayerParams L) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  using LL = LayerLds<R>;
+  constexpr int RR = 16 * R;
+  const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
+  uint8_t* rec = reinterpret_cast<uint8_t*>(smem);
+  lds_f32* red0 = (lds_f32*)(smem + LL::red_off(L.H, L.I));
+  lds_f32* ored0 = (lds_f32*)(smem + LL::ored_off(L.H, L.I));
+  lds_u8* wout = (lds_u8*)(smem + LL::wout_off(L.H, L.I)) + wave * kWaveOutBytes;
+  int32_t* s_exp = reinterpret_cast<int32_t*>(smem + LL::misc_off(L.H, L.I));
+  float* s_w = reinterpret_cast<float*>(s_exp + 8);
+  uint32_t* s_gen = reinterpret_cast<uint32_t*>(s_exp + 16);
+
+  // route (wave 0) while waves 1 .. C_H prepare x's record in LDS.  Wave 0 also
+  // reads the generation and the gate/up counters: when every one this call uses
+  // already carries the generation (re-armed by the previous call), gate/up units
+  // count themselves without waiting for the atomic's reply.
+  const int C_H = L.H >> 10;
+  bool armed = false;
+  if (wave == 0) {
+    const uint64_t g64 = sync_load(L.sync);
+    const uint64_t rw = sync_load(L.sync + kSyncReady + lane);
+    topk_wave(L.logits, L.E, L.k, lane, s_exp, s_w, s_exp);
+    const uint32_t g = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)g64);
+    const bool used = lane / kSubs < L.k && lane % kSubs < L.RGg;
+    armed = __all(!used || (uint32_t)(rw >> 32) == g);
+    if (lane == 0) *s_gen = g;
+  } else if (wave <= C_H) {
+    prep_wave(L.x, GALE_F16, L.H, 1, L.H, 0, rec, ra_bytes(L.H), wave - 1);
+  }
+  __syncthreads();
+  const uint32_t gen = *s_gen;
+  if (blockIdx.x == 0 && tid < L.k) {
+    if (L.topk_idx) L.topk_idx[tid] = s_exp[tid];
+    if (L.topk_w) L.topk_w[tid] = s_w[tid];
+  }
+
+  // gate/up units, then down units: contiguous shares of each phase
+  const int GU = L.k * L.RGg, DN = L.k * L.RGd;
+  const int nb = (int)gridDim.x, b = (int)blockIdx.x;
+  {
+    const PhaseGeo GG = phase_geo<R>(false, L.H, L.I, wave, lane, L.Q);
+    run_phase<R, false>(L, GG, wave, lane, (int)((int64_t)GU * b / nb), (int)((int64_t)GU * (b + 1) / nb), L.RGg,
+                        rec, red0, ored0, wout, s_exp, s_w, gen, armed);
+  }
+  {
+    const PhaseGeo GD = phase_geo<R>(true, L.I, L.H, wave, lane, L.Q);
+    run_phase<R, true>(L, GD, wave, lane, (int)((int64_t)DN * b / nb), (int)((int64_t)DN * (b + 1) / nb), L.RGd,
+                       rec, red0, ored0, wout, s_exp, s_w, gen, armed);
+  }
+}
+
+size_t decode_layer_sync_bytes(int hidden, int inter) {
+  // the largest layout: one tile per unit (the most down row groups)
+  (void)inter;
+  const int words = kSyncRows + hidden / 16;
+  static_assert(kSyncReady + GALE_MAX_TOPK * kSubs <= kSyncRowSub, "sync layout");
+  return (size_t)8 * words;
+}
+
+// Shapes the kernel's wave layout covers: 2 C_H wavefronts per workgroup (at most 8),
+// split evenly into down row groups of C_I wavefronts.
+bool decode_layer_supported(int hidden, int inter) {
+  if (hidden % 1024 || inter % 1024) return false;
+  const int C_H = hidden >> 10, C_I = inter >> 10;
+  return C_H >= 1 && C_H <= 4 && C_I >= 1 && C_I <= 2 * C_H && (2 * C_H) % C_I == 0;
+}
+
+template <int R>
+static hipError_t launch_layer_r(LayerParams L, hipStream_t s) {
+  const int W = 2 * (L.H >> 10);
+  L.Q = W / (L.I >> 10);
+  L.RGg = L.I / (16 * R);
+  L.RGd = L.H / (16 * R * L.Q);
+  const size_t smem = LayerLds<R>::bytes(L.H, L.I);
+  const int block = 64 * W;
+  if (smem > 65536) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_layer_kernel<R>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+  }
+  int occ = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, decode_layer_kernel<R>, block, smem) != hipSuccess ||
+      occ < 1)
+    occ = 1;
+  // every workgroup must be resident at once (down units wait on gate/up units)
+  const int64_t units = std::max<int64_t>((int64_t)L.k * L.RGg, (int64_t)L.k * L.RGd);
+  const int64_t grid = std::min<int64_t>(units, (int64_t)device_cu_count() * occ);
+  hipLaunchKernelGGL(decode_layer_kernel<R>, dim3((unsigned)grid), dim3(block), smem, s, L);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_layer(const gale_matrix* table, int E, const float* logits, int k, const void* x,
+                               int hidden, int inter, void* y, int32_t* topk_idx, float* topk_w, float* h,
+                               float* yp, uint64_t* sync, int tiles, hipStream_t s) {
+  LayerParams L;
+  L.table = table;
+  L.logits = logits;
+  L.x = x;
+  L.y = reinterpret_cast<__half*>(y);
+  L.topk_idx = topk_idx;
+  L.topk_w = topk_w;
+  L.h = h;
+  L.yp = yp;
+  L.sync = sync;
+  L.E = E;
+  L.k = k;
+  L.H = hidden;
+  L.I = inter;
+  L.Q = 1;
+  L.RGg = L.RGd = 1;
+  // R tiles per unit need R <= C_H (gate/up outlier roles) and R <= C_I (down)
+  if (tiles >= 2 && (inter >> 10) >= 2 && (hidden >> 10) >= 2) return launch_layer_r<2>(L, s);
+  return launch_layer_r<1>(L, s);
+}
+
+}  // namespace gale

@@ -148,6 +148,14 @@ hipError_t launch_grouped_gemm(const gale_matrix* table, int gateup, int rows, i
                                const int32_t* perm, int top_k, const GemmTile* tiles, const int32_t* n_tiles,
                                int max_tiles, const uint16_t* A, float* out, int out_stride, hipStream_t s);
 
+// one-launch decode MoE layer for a single token (route, gate/up + SwiGLU, rotate h,
+// down, combine); sync: decode_layer_sync_bytes(hidden, inter) bytes of counters
+bool decode_layer_supported(int hidden, int inter);
+size_t decode_layer_sync_bytes(int hidden, int inter);
+hipError_t launch_decode_layer(const gale_matrix* table, int E, const float* logits, int k, const void* x,
+                               int hidden, int inter, void* y, int32_t* topk_idx, float* topk_w, float* h,
+                               float* yp, uint64_t* sync, int tiles, hipStream_t s);
+
 void set_error(const char* fmt, ...);
 
 }  // namespace gale

@@ -8,65 +8,9 @@
 // the k selected logits; the combine sums slots 0..k-1 in that order.
 #include "gale_internal.h"
 #include "gale_rotate.h"
+#include "gale_route.h"
 
 namespace gale {
-
-// a ranks before b
-__device__ __forceinline__ bool better(float av, int ai, float bv, int bi) {
-  return av > bv || (av == bv && ai < bi);
-}
-
-// Top-k of one token by one wavefront: each lane holds up to 8 logits (E <= 512).
-// Every selection loop runs to the compile-time bound with a predicate, so the k
-// winners stay in registers.
-__device__ __forceinline__ void topk_wave(const float* __restrict__ lg, int E, int k, int lane, int32_t* out_idx,
-                          float* out_w, int32_t* lds_idx) {
-  float v[8];
-  int id[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int e = lane + 64 * j;
-    id[j] = e;
-    v[j] = e < E ? lg[e] : -INFINITY;
-  }
-  bool taken[8] = {false, false, false, false, false, false, false, false};
-  float m = 0.f, my_v = 0.f;     // the best logit; lane s keeps winner s
-  int my_i = 0;
-#pragma unroll
-  for (int s = 0; s < GALE_MAX_TOPK; ++s) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (!taken[j] && id[j] < E && better(v[j], id[j], bv, bi)) { bv = v[j]; bi = id[j]; }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off, 64);
-      const int oi = __shfl_xor(bi, off, 64);
-      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-    }
-    if (s < k) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (id[j] == bi) taken[j] = true;
-    }
-    if (s == 0) m = bv;
-    if (lane == s) { my_v = bv; my_i = bi; }
-  }
-  // softmax of the k selected logits, one slot per lane
-  const float ex = lane < k ? expf(my_v - m) : 0.f;
-  float sum = 0.f;
-#pragma unroll
-  for (int s = 0; s < GALE_MAX_TOPK; ++s) {
-    const float es = __shfl(ex, s, 64);
-    if (s < k) sum += es;
-  }
-  if (lane < k) {
-    out_idx[lane] = my_i;
-    out_w[lane] = ex / sum;
-    lds_idx[lane] = my_i;
-  }
-}
 
 // Exclusive scan of v over a workgroup of at most 1024 threads; *total gets the sum.
 __device__ __forceinline__ int block_exclusive_scan(int v, int* s_wave, int* total) {

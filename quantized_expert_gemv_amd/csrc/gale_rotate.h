@@ -11,6 +11,7 @@
 // H is normalised by 1/32 (orthonormal, H.H = I).
 #pragma once
 #include "gale_internal.h"
+#include "gale_lanes.h"
 
 namespace gale {
 
@@ -59,6 +60,18 @@ __device__ __forceinline__ void store16(void* blk, int dtype, int lane, const fl
   }
 }
 
+// One butterfly stage over lane bit B: with a the lower lane's value and b the upper
+// lane's, the lower lane becomes a + b and the upper lane a - b.
+template <int B>
+__device__ __forceinline__ void fwht_lane_stage(float v[16], int lane) {
+  const bool upper = (lane & B) != 0;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const float u = lane_xor<B>(v[e]);
+    v[e] = upper ? (u - v[e]) : (v[e] + u);
+  }
+}
+
 // In-place normalised Walsh-Hadamard transform of the wavefront's 1024-block.
 __device__ __forceinline__ void fwht1024_wave(float v[16], int lane) {
 #pragma unroll
@@ -72,15 +85,12 @@ __device__ __forceinline__ void fwht1024_wave(float v[16], int lane) {
       }
     }
   }
-#pragma unroll
-  for (int b = 1; b < 64; b <<= 1) {
-    const bool upper = (lane & b) != 0;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      float u = __shfl_xor(v[e], b, 64);
-      v[e] = upper ? (u - v[e]) : (v[e] + u);
-    }
-  }
+  fwht_lane_stage<1>(v, lane);
+  fwht_lane_stage<2>(v, lane);
+  fwht_lane_stage<4>(v, lane);
+  fwht_lane_stage<8>(v, lane);
+  fwht_lane_stage<16>(v, lane);
+  fwht_lane_stage<32>(v, lane);
 #pragma unroll
   for (int e = 0; e < 16; ++e) v[e] *= 0.03125f;
 }
@@ -107,6 +117,51 @@ __device__ __forceinline__ void unpack4_fp8(uint32_t p, float* o) {
   o[3] = __builtin_amdgcn_cvt_f32_fp8((int)p, 3);
 }
 
+// The record pieces of one lane's 16 elements (x~, four fp8 terms, the chunk
+// exponent), from its 16 input values; the wavefront's lanes together hold one
+// 1024-chunk.
+struct PrepLane {
+  float x[16];
+  uint32_t t[kTerms][4];
+  int p;
+};
+
+__device__ __forceinline__ void prep_lane(const float in[16], int lane, bool rotate, PrepLane& o) {
+#pragma unroll
+  for (int e = 0; e < 16; ++e) o.x[e] = in[e];
+  if (rotate) fwht1024_wave(o.x, lane);
+  float m = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(o.x[e]));
+  m = fmaxf(m, lane_xor<1>(m));
+  m = fmaxf(m, lane_xor<2>(m));
+  m = fmaxf(m, lane_xor<4>(m));
+  m = fmaxf(m, lane_xor<8>(m));
+  m = fmaxf(m, lane_xor<16>(m));
+  m = fmaxf(m, lane_xor<32>(m));
+  int p = 0;
+  if (m > 0.f && m <= 3.0e38f) {
+    int ex;
+    frexpf(m, &ex);          // m = f 2^ex, f in [0.5, 1)
+    p = 8 - ex;              // m 2^p in [128, 256)
+  }
+  float r[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) r[e] = ldexpf(o.x[e], p);
+#pragma unroll
+  for (int t = 0; t < kTerms; ++t) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      o.t[t][q] = pack4_fp8(r[4 * q], r[4 * q + 1], r[4 * q + 2], r[4 * q + 3]);
+      float back[4];
+      unpack4_fp8(o.t[t][q], back);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[4 * q + i] -= back[i];
+    }
+  }
+  o.p = p;
+}
+
 // One wavefront prepares one (vector, 1024-chunk) of the activation record.
 __device__ __forceinline__ void prep_wave(const void* __restrict__ x, int x_dtype, int64_t x_stride, int n_vec,
                                           int K, int rotated, uint8_t* __restrict__ ra, size_t ra_stride,
@@ -119,40 +174,15 @@ __device__ __forceinline__ void prep_wave(const void* __restrict__ x, int x_dtyp
   const size_t isz = x_dtype == GALE_F16 ? 2 : 4;
   float f[16];
   load16(reinterpret_cast<const char*>(x) + (v * x_stride + (int64_t)c * 1024) * isz, x_dtype, lane, f);
-  if (!rotated) fwht1024_wave(f, lane);
-
+  PrepLane o;
+  prep_lane(f, lane, !rotated, o);
   uint8_t* rec = ra + v * ra_stride;
-  store16(reinterpret_cast<float*>(rec) + c * 1024, GALE_F32, lane, f);
-
-  float m = 0.f;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(f[e]));
-#pragma unroll
-  for (int b = 1; b < 64; b <<= 1) m = fmaxf(m, __shfl_xor(m, b, 64));
-  int p = 0;
-  if (m > 0.f && m <= 3.0e38f) {
-    int ex;
-    frexpf(m, &ex);          // m = f 2^ex, f in [0.5, 1)
-    p = 8 - ex;              // m 2^p in [128, 256)
-  }
-  float r[16];
-#pragma unroll
-  for (int e = 0; e < 16; ++e) r[e] = ldexpf(f[e], p);
+  store16(reinterpret_cast<float*>(rec) + c * 1024, GALE_F32, lane, o.x);
   uint8_t* terms = rec + ra_terms_off(K) + (size_t)c * 4 * 1024;
 #pragma unroll
-  for (int t = 0; t < kTerms; ++t) {
-    uint32_t w[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      w[q] = pack4_fp8(r[4 * q], r[4 * q + 1], r[4 * q + 2], r[4 * q + 3]);
-      float back[4];
-      unpack4_fp8(w[q], back);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) r[4 * q + i] -= back[i];
-    }
-    *reinterpret_cast<uint4*>(terms + t * 1024 + 16 * lane) = make_uint4(w[0], w[1], w[2], w[3]);
-  }
-  if (lane == 0) reinterpret_cast<int32_t*>(rec + ra_p_off(K))[c] = p;
+  for (int t = 0; t < kTerms; ++t)
+    *reinterpret_cast<uint4*>(terms + t * 1024 + 16 * lane) = make_uint4(o.t[t][0], o.t[t][1], o.t[t][2], o.t[t][3]);
+  if (lane == 0) reinterpret_cast<int32_t*>(rec + ra_p_off(K))[c] = o.p;
 }
 
 }  // namespace gale

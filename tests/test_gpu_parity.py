@@ -339,6 +339,56 @@ def test_moe_grouped_items_equal_decode_bitwise(q, layer):
     assert torch.equal(yd, yg)
 
 
+@pytest.mark.parametrize("tiles", [1, 2])
+def test_moe_one_launch_equals_staged_bitwise(q, layer, tiles):
+    """One token: the one-launch layer kernel against the five-launch sequence, bit for
+    bit, over consecutive calls on one workspace (its counters carry a generation from
+    call to call) that starts out filled with random bytes (first use re-tags them)."""
+    seed, canon, tab = layer
+    ws = torch.randint(0, 256, (q.moe_workspace_bytes(1, 256, 6, 4096, 2048),), dtype=torch.uint8, device=DEV)
+    for i in range(4):
+        print(f"one-launch decode tiles={tiles} call {i}", flush=True)
+        x = gen_x(seed, (3000 + i,), 1, 4096, device=DEV)
+        lg = gen_logits_normal(seed, (3000 + i,), 1, 256, device=DEV)
+        yf, idf, wf = q.moe_layer_fwd(tab, 4096, 2048, lg, x, top_k=6, ws=ws, flags=q.gale_tiles_flag(tiles))
+        ys, ids, wss = q.moe_layer_fwd(tab, 4096, 2048, lg, x, top_k=6, flags=q.GALE_DECODE_STAGED)
+        assert torch.equal(idf, ids) and torch.equal(wf, wss)
+        assert torch.equal(yf, ys)
+    ridx, _ = O.route(lg.cpu().numpy(), 6)
+    assert np.array_equal(idf.cpu().numpy(), ridx)
+    expert_of = lambda e: tuple(m.numpy() for m in canon[e])  # noqa: E731
+    yref, _, _ = O.moe(expert_of, lg.cpu().numpy(), x.cpu().numpy(), k=6)
+    assert O.rel_l2(np_of(yf), yref).max() <= REL_L2_BAR
+
+
+def test_moe_one_launch_top_k_and_outlier_edges(q):
+    """One token through experts whose rows carry 0, 1, 300 (past the staged outlier
+    chunks) or 41 / 20 outliers, with top_k 1, 8 and 3 in turn on one workspace (the
+    counter layout moves with top_k): equal to the staged sequence and to the oracle."""
+    E = 8
+    seed = config_seed(13)
+    experts_np, packed = [], []
+    for e in range(E):
+        d1, d3, d2 = outlier_edge_dict(2048, 4096, 200 + e), outlier_edge_dict(2048, 4096, 300 + e), \
+            outlier_edge_dict(4096, 2048, 400 + e)
+        experts_np.append((d1, d3, d2))
+        packed.append(tuple(q.pack_matrix(canon_from_dict(d)) for d in (d1, d3, d2)))
+    tab = q.expert_table(packed)
+    ws = torch.empty(q.moe_workspace_bytes(1, E, 8, 4096, 2048), dtype=torch.uint8, device=DEV)
+    for i, k in enumerate([1, 8, 3]):
+        print(f"one-launch decode edges top_k={k}", flush=True)
+        x = gen_x(seed, (10 + i,), 1, 4096, device=DEV)
+        lg = gen_logits_normal(seed, (10 + i,), 1, E, device=DEV)
+        yf, idf, wf = q.moe_layer_fwd(tab, 4096, 2048, lg, x, top_k=k, ws=ws)
+        ys, ids, _ = q.moe_layer_fwd(tab, 4096, 2048, lg, x, top_k=k, flags=q.GALE_DECODE_STAGED)
+        assert torch.equal(idf, ids) and torch.equal(yf, ys)
+        yref, ridx, _ = O.moe(lambda e: experts_np[e], lg.cpu().numpy(), x.cpu().numpy(), k=k)
+        assert np.array_equal(idf.cpu().numpy(), ridx)
+        err = O.rel_l2(np_of(yf), yref).max()
+        print(f"one-launch decode edges top_k={k} rel-L2 {err:.3e}")
+        assert err <= REL_L2_BAR
+
+
 @pytest.mark.parametrize("T,zipf", [(65, False), (2048, True)])
 def test_moe_grouped_prefill(q, layer, T, zipf):
     """Grouped path (tile GEMM for the busy experts, GEMV items for the rest) at a ragged
