@@ -66,6 +66,11 @@ extern "C" {
 #define GALE_GROUPED_GEMM  0x80u /* gale_moe_layer_fwd grouped path: fp16 MFMA tile GEMM only */
 #define GALE_DECODE_STAGED 0x1000u /* gale_moe_layer_fwd, one token: the five-launch decode sequence
                                       instead of the one-launch layer kernel */
+/* Tuning knob, bits 8..11: a value v != 0 fixes the row tiles (16 rows each) per work unit
+ * instead of the built-in choice.  GEMV kernels: 2^(v-1) (capped where registers run out).
+ * One-token layer kernel, (gate/up, down) tiles per unit: v = 1: (1, 1); 2: (2, 2); 3: (1, 2);
+ * 4: (2, 1); 5: (3, 2); 6: (3, 1).  Results do not depend on it. */
+#define GALE_TILES_SHIFT 8
 
 /* ---- limits -------------------------------------------------------------- */
 #define GALE_FWHT_N        1024   /* rotation block ("blocked FWHT-1024") */

@@ -31,8 +31,13 @@ STATUS = {0: "GALE_OK", -1: "GALE_ERR_NULL", -2: "GALE_ERR_SHAPE", -3: "GALE_ERR
 
 
 def gale_tiles_flag(r: int) -> int:
-    """flags bits 8..11 force the row tiles per workgroup (1, 2, 4 or 8)."""
+    """flags bits 8..11 force the GEMV kernels' row tiles per unit (1, 2, 4 or 8)."""
     return ((r.bit_length()) & 0xF) << 8
+
+
+def gale_layer_tiles_flag(gate_up: int, down: int) -> int:
+    """flags bits 8..11 for the one-token layer kernel: row tiles per gate/up and per down unit."""
+    return {(1, 1): 1, (2, 2): 2, (1, 2): 3, (2, 1): 4, (3, 2): 5, (3, 1): 6}[(gate_up, down)] << 8
 
 
 class GaleError(RuntimeError):

@@ -53,7 +53,7 @@ static int hip_status(const char* fn, hipError_t e) {
 static int pick_tiles(int64_t items, int ntiles, int cols, int slots, int gateup, uint32_t flags) {
   const int C = cols / 1024;
   int r = 4;
-  const int forced = (int)((flags >> 8) & 0xF);
+  const int forced = (int)((flags >> GALE_TILES_SHIFT) & 0xF);
   if (forced) r = 1 << (forced - 1);
   if (r > 4) r = 4;
   if ((slots >= 2 || gateup) && r > 2) r = 2;    // the kernel's register budget
@@ -112,6 +112,8 @@ static int64_t moe_tile_bound(int T, int E, int k) {
 enum MoePath { kDecode = 0, kGroupedItems = 1, kGroupedGemm = 2, kGroupedHybrid = 3 };
 // Experts with at least this many pairs take the tile GEMM in the hybrid grouped path.
 constexpr int kGemmMinPairs = 64;
+// Row tiles per unit of the one-token layer kernel, (gate/up, down) as decimal digits.
+constexpr int kDecodeLayerTiles = 32;
 static MoePath moe_path(int n_tok, uint32_t flags) {
   const bool grouped = (flags & GALE_PATH_GROUPED) || (!(flags & GALE_PATH_DECODE) && n_tok > GALE_MAX_DECODE_TOKENS);
   if (!grouped) return kDecode;
@@ -491,10 +493,12 @@ extern "C" int gale_moe_layer_fwd(int32_t hidden, int32_t inter, const gale_expe
   const int split = path == kGroupedHybrid ? kGemmMinPairs : (path == kGroupedGemm ? 1 : INT_MAX);
   if (path == kDecode && n_tok == 1 && !(flags & GALE_DECODE_STAGED) && decode_layer_supported(hidden, inter)) {
     // one launch for the whole layer; the counters live in the workspace
-    const int forced = (int)((flags >> 8) & 0xF);
+    // tiles per unit of (gate/up, down), as decimal digits; see GALE_TILES_SHIFT
+    static const int kLayerTiles[7] = {kDecodeLayerTiles, 11, 22, 12, 21, 32, 31};
+    const int forced = (int)((flags >> GALE_TILES_SHIFT) & 0xF);
     return hip_status(fn, launch_decode_layer(table, n_experts, logits, top_k, x, hidden, inter, y, topk_idx, topk_w,
                                               h, yp, reinterpret_cast<uint64_t*>(base + W.sync),
-                                              forced ? 1 << (forced - 1) : 2, stream));
+                                              kLayerTiles[forced <= 6 ? forced : 0], stream));
   }
   if (path == kDecode) {
     st = hip_status(fn, launch_route_prep(logits, n_tok, n_experts, top_k, idx, wts, items, n_items, slots, x,

@@ -10,89 +10,85 @@
 
 namespace gale {
 
-// a ranks before b
-__device__ __forceinline__ bool better(float av, int ai, float bv, int bi) {
-  return av > bv || (av == bv && ai < bi);
+// Ranking key of (logit v, expert e): larger key = ranks first.  The high word maps the
+// float order onto unsigned order (-0 is folded into +0 first, so equal logits stay
+// equal); the low word is ~e, so equal logits rank by ascending index.  Key 0 is never
+// the key of a candidate and stands for "none".
+__device__ __forceinline__ uint64_t rank_key(float v, int e) {
+  uint32_t u = __float_as_uint(v + 0.0f);
+  u ^= (u >> 31) ? 0xFFFFFFFFu : 0x80000000u;
+  return ((uint64_t)u << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
 }
+__device__ __forceinline__ float key_logit(uint64_t k) {
+  uint32_t u = (uint32_t)(k >> 32);
+  u ^= (u >> 31) ? 0x80000000u : 0xFFFFFFFFu;
+  return __uint_as_float(u);
+}
+__device__ __forceinline__ int key_expert(uint64_t k) { return (int)(0xFFFFFFFFu - (uint32_t)k); }
 
-// Keep the better of this lane's candidate and the one of lane ^ OFF (OFF = 1, 2, 16,
-// 32) or of the mirrored lane (OFF = 8: within 8, 16: within 16; see lane_mirror_u32).
+// Keep the larger of this lane's key and the one of lane ^ OFF (OFF = 1, 2, 16, 32) or
+// of the mirrored lane (OFF = 8: within 8, 16: within 16; see lane_mirror_u32).
 template <int OFF, bool MIRROR = false>
-__device__ __forceinline__ void arg_best(float& bv, int& bi) {
-  uint32_t ov, oi;
+__device__ __forceinline__ void key_best(uint64_t& k) {
+  uint32_t lo, hi;
   if constexpr (MIRROR) {
-    ov = lane_mirror_u32<OFF>(__float_as_uint(bv));
-    oi = lane_mirror_u32<OFF>((uint32_t)bi);
+    lo = lane_mirror_u32<OFF>((uint32_t)k);
+    hi = lane_mirror_u32<OFF>((uint32_t)(k >> 32));
   } else {
-    ov = lane_xor_u32<OFF>(__float_as_uint(bv));
-    oi = lane_xor_u32<OFF>((uint32_t)bi);
+    lo = lane_xor_u32<OFF>((uint32_t)k);
+    hi = lane_xor_u32<OFF>((uint32_t)(k >> 32));
   }
-  const bool take = better(__uint_as_float(ov), (int)oi, bv, bi);
-  bv = take ? __uint_as_float(ov) : bv;
-  bi = take ? (int)oi : bi;
+  const uint64_t o = ((uint64_t)hi << 32) | lo;
+  k = o > k ? o : k;
 }
 
-// Best (logit, expert) of the wavefront, in every lane: quads, groups of 8 and 16
-// through DPP, rows through the permlane swaps.
-__device__ __forceinline__ void wave_best(float& bv, int& bi) {
-  arg_best<1>(bv, bi);
-  arg_best<2>(bv, bi);
-  arg_best<8, true>(bv, bi);
-  arg_best<16, true>(bv, bi);
-  arg_best<16>(bv, bi);
-  arg_best<32>(bv, bi);
+// Largest key of the wavefront, in every lane: quads, groups of 8 and 16 through DPP,
+// rows through the permlane swaps.
+__device__ __forceinline__ uint64_t wave_best(uint64_t k) {
+  key_best<1>(k);
+  key_best<2>(k);
+  key_best<8, true>(k);
+  key_best<16, true>(k);
+  key_best<16>(k);
+  key_best<32>(k);
+  return k;
 }
 
-// The best candidate of this lane (experts lane + 64 j, j < NJ) not yet taken.
+// Top-k of one token by one wavefront: each lane holds the keys of up to 8 logits
+// (E <= 512, experts lane + 64 j) and offers its largest untaken one; each round takes
+// the largest of the wavefront, and the lane that owned it zeroes that key.  Lane s
+// keeps winner s.  The largest of a set of distinct keys is unique, so the pairing of
+// lanes in each round does not change the result.
 template <int NJ>
-__device__ __forceinline__ void lane_best(const float v[8], int lane, int E, uint32_t taken, float& bv, int& bi) {
-  bv = -INFINITY;
-  bi = 0x7fffffff;
+__device__ __forceinline__ void topk_rounds(const float* __restrict__ lg, int E, int k, int lane, float& m,
+                                            float& my_v, int& my_i) {
+  uint64_t key[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int e = lane + 64 * j;
-    const bool take = e < E && !((taken >> j) & 1u) && better(v[j], e, bv, bi);
-    bv = take ? v[j] : bv;
-    bi = take ? e : bi;
+    key[j] = e < E ? rank_key(lg[e], e) : 0;
   }
-}
-
-template <int NJ>
-__device__ __forceinline__ void topk_rounds(const float v[8], int lane, int E, int k, float& m, float& my_v,
-                                            int& my_i) {
-  uint32_t taken = 0;
-  float bv;
-  int bi;
-  lane_best<NJ>(v, lane, E, taken, bv, bi);
+  uint64_t mk = 0;
   for (int s = 0; s < k; ++s) {
-    float wv = bv;
-    int wi = bi;
-    wave_best(wv, wi);
-    m = s == 0 ? wv : m;
-    my_v = lane == s ? wv : my_v;
-    my_i = lane == s ? wi : my_i;
-    taken |= (wi & 63) == lane ? 1u << (wi >> 6) : 0u;
-    lane_best<NJ>(v, lane, E, taken, bv, bi);
+    uint64_t b = key[0];
+#pragma unroll
+    for (int j = 1; j < NJ; ++j) b = key[j] > b ? key[j] : b;
+    const uint64_t w = wave_best(b);
+    mk = s == 0 ? w : mk;
+    my_v = lane == s ? key_logit(w) : my_v;
+    my_i = lane == s ? key_expert(w) : my_i;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) key[j] = key[j] == w ? 0 : key[j];
   }
+  m = key_logit(mk);
 }
 
-// Top-k of one token by one wavefront: each lane holds up to 8 logits (E <= 512) and
-// keeps its best untaken one; each round takes the best of the wavefront, and the
-// lane that owned it moves on to its next best.  Lane s keeps winner s.  The best of
-// a set is unique under the order rule, so the pairing of lanes in each round does
-// not change the result.
 __device__ __forceinline__ void topk_wave(const float* __restrict__ lg, int E, int k, int lane, int32_t* out_idx,
                           float* out_w, int32_t* lds_idx) {
-  float v[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int e = lane + 64 * j;
-    v[j] = e < E ? lg[e] : -INFINITY;
-  }
   float m = 0.f, my_v = 0.f;
   int my_i = 0;
-  if (E <= 256) topk_rounds<4>(v, lane, E, k, m, my_v, my_i);
-  else topk_rounds<8>(v, lane, E, k, m, my_v, my_i);
+  if (E <= 256) topk_rounds<4>(lg, E, k, lane, m, my_v, my_i);
+  else topk_rounds<8>(lg, E, k, lane, m, my_v, my_i);
   // softmax of the k selected logits, one slot per lane, summed in slot order
   const float ex = lane < k ? expf(my_v - m) : 0.f;
   float sum = 0.f;

@@ -339,7 +339,7 @@ def test_moe_grouped_items_equal_decode_bitwise(q, layer):
     assert torch.equal(yd, yg)
 
 
-@pytest.mark.parametrize("tiles", [1, 2])
+@pytest.mark.parametrize("tiles", [(1, 1), (2, 2), (1, 2), (2, 1), (3, 2), (3, 1)])
 def test_moe_one_launch_equals_staged_bitwise(q, layer, tiles):
     """One token: the one-launch layer kernel against the five-launch sequence, bit for
     bit, over consecutive calls on one workspace (its counters carry a generation from
@@ -350,7 +350,7 @@ def test_moe_one_launch_equals_staged_bitwise(q, layer, tiles):
         print(f"one-launch decode tiles={tiles} call {i}", flush=True)
         x = gen_x(seed, (3000 + i,), 1, 4096, device=DEV)
         lg = gen_logits_normal(seed, (3000 + i,), 1, 256, device=DEV)
-        yf, idf, wf = q.moe_layer_fwd(tab, 4096, 2048, lg, x, top_k=6, ws=ws, flags=q.gale_tiles_flag(tiles))
+        yf, idf, wf = q.moe_layer_fwd(tab, 4096, 2048, lg, x, top_k=6, ws=ws, flags=q.gale_layer_tiles_flag(*tiles))
         ys, ids, wss = q.moe_layer_fwd(tab, 4096, 2048, lg, x, top_k=6, flags=q.GALE_DECODE_STAGED)
         assert torch.equal(idf, ids) and torch.equal(wf, wss)
         assert torch.equal(yf, ys)
