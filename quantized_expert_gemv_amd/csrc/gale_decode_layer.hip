@@ -63,9 +63,13 @@ __device__ __forceinline__ uint64_t sync_load(uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// One arrival at a generation-tagged counter; returns the count including it.
-__device__ __forceinline__ uint32_t arrive(uint64_t* ctr, uint32_t gen) {
-  const uint64_t old = __hip_atomic_fetch_add(ctr, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// One arrival at a generation-tagged counter, in two halves so that other work can
+// overlap the atomic's round trip: arrive_add issues the add, arrive_count turns its
+// reply into the count including this arrival.
+__device__ __forceinline__ uint64_t arrive_add(uint64_t* ctr) {
+  return __hip_atomic_fetch_add(ctr, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t arrive_count(uint64_t* ctr, uint64_t old, uint32_t gen) {
   if ((uint32_t)(old >> 32) == gen) return (uint32_t)old + 1u;
   // a word of another generation: count this arrival against the word re-tagged
   // with this generation (the add above went to the stale value and is dropped)
@@ -77,6 +81,8 @@ __device__ __forceinline__ uint32_t arrive(uint64_t* ctr, uint32_t gen) {
       return (uint32_t)want;
   }
 }
+// One arrival at a generation-tagged counter; returns the count including it.
+__device__ __forceinline__ uint32_t arrive(uint64_t* ctr, uint32_t gen) { return arrive_count(ctr, arrive_add(ctr), gen); }
 
 // Wave 0 polls the kSubs sub-counters of one count until each reads (gen, its
 // share of RG); about 0.1 s at most, then the error word records the timeout and
@@ -596,7 +602,13 @@ __device__ __forceinline__ void down_unit(const LayerParams& L, const PhaseGeo& 
   if (lane == 0) cnt = arrive(L.sync + kSyncRows + rg, gen);
   cnt = (uint32_t)__builtin_amdgcn_readfirstlane((int)cnt);
   if (cnt != (uint32_t)L.k) return;
-  // the last pair of this row group: y = sum over slots in order of w_j yp_j
+  // the last pair of this row group.  Every unit of the call has now made its last
+  // access to the gate/up and row-group counters, so this row group is counted towards
+  // the re-arm straight away (the count's round trip overlaps the combine); then
+  // y = sum over slots in order of w_j yp_j.
+  const int sub = rg % kSubs;
+  uint64_t sub_old = 0;
+  if (lane == 0) sub_old = arrive_add(L.sync + kSyncRowSub + sub);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   for (int e = lane; e < Q * RR; e += 64) {
     const int n = rg * Q * RR + e;
@@ -609,12 +621,10 @@ __device__ __forceinline__ void down_unit(const LayerParams& L, const PhaseGeo& 
       if (j < L.k) acc = fmaf(s_w[j], v[j], acc);
     L.y[n] = __float2half_rn(acc);
   }
-  // the last row group to be combined: every unit of every workgroup has made its last
-  // counter access, so re-arm the counters for the next generation
-  const int sub = rg % kSubs;
+  // the last row group to be combined re-arms the counters for the next generation
   uint32_t c1 = 0, c2 = 0;
   if (lane == 0) {
-    c1 = arrive(L.sync + kSyncRowSub + sub, gen);
+    c1 = arrive_count(L.sync + kSyncRowSub + sub, sub_old, gen);
     if (c1 == (uint32_t)sub_count(L.RGd, sub)) c2 = arrive(L.sync + kSyncTop, gen);
   }
   c2 = (uint32_t)__builtin_amdgcn_readfirstlane((int)c2);
