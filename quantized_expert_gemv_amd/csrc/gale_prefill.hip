@@ -170,13 +170,24 @@ hipError_t launch_rotate_f16(const void* x, int x_dtype, int64_t n_rows, int K, 
 //      shift, AND and XOR per two weights: the sign bit goes straight into the fp16
 //      sign of the block scale), then the block's outliers added in place.
 // LDS rows are 272 bytes (128 fp16 + 16 pad), so the 16 rows a 16-byte operand
-// read touches start on 16 different bank quads.  The outlier entries of the 128
-// rows are staged in LDS once per workgroup (columns and int4 values).
+// read touches start on 16 different bank quads.
+//
+// Outliers.  At the start, the workgroup sorts the outlier entries of its 128 rows
+// into buckets of (group of 16 rows, block) in LDS, one 16-bit entry each (int4
+// value, row within the group, column within the block).  The wavefront that
+// unpacks a group of 16 rows also patches them: after its sign stores, lane i adds
+// the bucket's entry i into its weight (LDS operations of one wavefront complete in
+// order, so no barrier is needed).  Rows whose entries exceed the staging space,
+// or K beyond the bucket table, take a per-lane walk over the CSR lists in HBM.
 // ---------------------------------------------------------------------------
 constexpr int kRowBytes = 272;
 constexpr int kTileBytes = 128 * kRowBytes;
 constexpr int kOutStage = 6144;                       // staged outlier entries per workgroup
-constexpr int kStageBytes = 2 * kOutStage + kOutStage + 4 * 132;
+constexpr int kStageBlocks = 56;                      // bucket table: K <= 7168
+constexpr int kBuckets = 8 * kStageBlocks;
+// entries u16 [kOutStage]; bucket starts i32 [kBuckets + 1]; fill cursors i32 [kBuckets];
+// row scales f32 [128]; eight i32 for the total and the scan; output rows i32 [128]
+constexpr int kStageBytes = 2 * kOutStage + 4 * (kBuckets + 1) + 4 * kBuckets + 4 * 128 + 4 * 8 + 4 * 128;
 constexpr size_t kGemmSmem = 4 * (size_t)kTileBytes + kStageBytes;
 
 struct GemmParams {
@@ -201,8 +212,8 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) unsigned char lds_b;
 typedef __attribute__((address_space(3))) u32x4 lds_q;
 typedef __attribute__((address_space(3))) unsigned short lds_h;
-typedef __attribute__((address_space(3))) signed char lds_i8;
 typedef __attribute__((address_space(3))) int lds_i32;
+typedef __attribute__((address_space(3))) float lds_f32;
 
 __device__ __forceinline__ v8h as_v8h(const u32x4 v) {
   union { u32x4 u; v8h h; } c;
@@ -217,11 +228,17 @@ __device__ __forceinline__ int group_of(int g, int e) {
   return 8 * (g & 1) + 2 * (g >> 1) + 4 * (e >> 1) + (e & 1);
 }
 
+// Byte offset in a B tile of (row, column cb of the block): the 16-byte group of cb
+// holds its 8 columns in the order (c0, c4, c1, c5, c2, c6, c3, c7).
+__device__ __forceinline__ int b_offset(int row, int cb) {
+  return row * kRowBytes + 16 * (cb >> 3) + 2 * (2 * (cb & 3) + ((cb >> 2) & 1));
+}
+
 // One B unpack item: a 16-row group of the device sign layout seen by one lane, i.e.
 // B-tile row 16 tt + l % 16 and lane group l / 16 (32 of the row's columns per block).
 struct BItem {
   int brow, bg;                 // B-tile row, lane group
-  int cur, cend;                // outlier cursor and end (staged or CSR index)
+  int cur, cend;                // unstaged outliers: CSR cursor and end
   int ncol, nq;                 // column and value of entry cur (column INT_MAX past the end)
   int gsrc;                     // descriptor index of the row's matrix
   float rscale;                 // the row's outlier scale
@@ -229,13 +246,21 @@ struct BItem {
   const uint16_t* scale;        // the row's scales of chunk 0
 };
 
-// The item's sign words (both halves) and block scales of one 1024-column chunk.
-struct ChunkRegs {
-  uint4 wlo, whi, sc;
-};
+// Global-memory views of device pointers: a load through them is a global load, which
+// only the vector-memory counter tracks (a load through a generic pointer is a flat
+// load, and every wait for LDS results would wait for it as well).  The 16-byte load
+// goes through the builtin vector type: uint4's copy constructor takes a generic
+// reference and would turn it back into a flat load.
+typedef const __attribute__((address_space(1))) u32x4 g_u4;
+typedef const __attribute__((address_space(1))) uint32_t g_u32;
 
-__device__ __forceinline__ BItem make_item(const GemmParams& P, int e, int n0, int C, int item, bool staged,
-                                           const lds_i32* st_off, const lds_h* st_col, const lds_i8* st_val) {
+__device__ __forceinline__ uint4 gload16(const void* p) {
+  const u32x4 v = *(g_u4*)p;
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t gload4(const void* p) { return *(g_u32*)p; }
+
+__device__ __forceinline__ BItem make_item(const GemmParams& P, int e, int n0, int C, int item, bool staged) {
   BItem b;
   const int tt = item >> 6, l = item & 63;
   const int r0 = 16 * tt;
@@ -247,19 +272,18 @@ __device__ __forceinline__ BItem make_item(const GemmParams& P, int e, int n0, i
   b.bg = l >> 4;
   b.sign = M->signs + sign_word_index(tg, 0, C, 0, l, 0);
   b.scale = M->block_scales + scale_index(16 * tg + nl, 0, C);
-  const int grow = n0 + (r0 + nl) % P.half_rows;
-  __half_raw hr;
-  hr.x = M->row_scales[grow];
-  b.rscale = __half2float(__half(hr));
-  b.cur = staged ? st_off[r0 + nl] : M->row_ptr[grow];
-  b.cend = staged ? st_off[r0 + nl + 1] : M->row_ptr[grow + 1];
+  b.cur = b.cend = 0;
   b.ncol = 0x7fffffff;
   b.nq = 0;
-  if (b.cur < b.cend) {
-    if (staged) {
-      b.ncol = st_col[b.cur];
-      b.nq = st_val[b.cur];
-    } else {
+  b.rscale = 0.f;
+  if (!staged) {
+    const int grow = n0 + (r0 + nl) % P.half_rows;
+    __half_raw hr;
+    hr.x = M->row_scales[grow];
+    b.rscale = __half2float(__half(hr));
+    b.cur = M->row_ptr[grow];
+    b.cend = M->row_ptr[grow + 1];
+    if (b.cur < b.cend) {
       b.ncol = M->out_cols[b.cur];
       b.nq = outlier_value(M->out_vals, b.cur);
     }
@@ -267,87 +291,241 @@ __device__ __forceinline__ BItem make_item(const GemmParams& P, int e, int n0, i
   return b;
 }
 
-__device__ __forceinline__ ChunkRegs item_load_chunk(const BItem& b, int c) {
-  const uint4* w = reinterpret_cast<const uint4*>(b.sign + (int64_t)c * 512);
-  ChunkRegs r;
-  r.wlo = w[0];
-  r.whi = w[64];
-  r.sc = *reinterpret_cast<const uint4*>(b.scale + (int64_t)c * 128);
-  return r;
+// A staging: chunk q = tid + 256 j -> tile row q / 16, 16-byte column group q % 16.
+// Rows past the tile's pairs read the first pair's row: those MFMA rows are never stored.
+struct AStage {
+  int row[8];
+};
+
+// Everything block j of the K loop takes from global memory, loaded two blocks ahead of
+// its store into LDS: the thread's eight A chunks and, for each of its two B items, the
+// sign words of the block's half-chunk and the word holding the block's scale.  The
+// loads are unconditional, so the wait before the store counts exactly the newer set.
+struct BlockRegs {
+  uint4 a[8];
+  uint4 w[2];
+  uint32_t s[2];
+};
+
+__device__ __forceinline__ void block_load(BlockRegs& r, const AStage& as, const BItem& b0, const BItem& b1,
+                                           const uint16_t* A, int K, int j, int acg) {
+#pragma unroll
+  for (int q = 0; q < 8; ++q) r.a[q] = gload16(A + (int64_t)as.row[q] * K + 128 * j + 8 * acg);
+  const int c = j >> 3, d = j & 7;
+  const int64_t wo = (int64_t)c * 512 + 256 * (d >> 2);   // words of half d / 4 of chunk c
+  const int64_t so = (int64_t)c * 128 + 2 * (d >> 1);     // scales of blocks d & ~1 and d | 1
+  r.w[0] = gload16(b0.sign + wo);
+  r.w[1] = gload16(b1.sign + wo);
+  r.s[0] = gload4(b0.scale + so);
+  r.s[1] = gload4(b1.scale + so);
 }
 
-// Unpack block bd of the item into B-tile rows (Bt), then add the row's outliers of
-// the block that fall in the item's columns.
-__device__ __forceinline__ void item_store(BItem& b, const ChunkRegs cr, lds_b* Bt, int bd, bool staged,
-                                           const lds_h* st_col, const lds_i8* st_val, const gale_matrix* table) {
-  const int d = bd & 7, h = d >> 2, p = d & 3;
-  // element-wise selects keep the item in registers (a select of two aggregates goes
-  // through memory)
-  const uint32_t w0 = h ? cr.whi.x : cr.wlo.x, w1 = h ? cr.whi.y : cr.wlo.y;
-  const uint32_t w2 = h ? cr.whi.z : cr.wlo.z, w3 = h ? cr.whi.w : cr.wlo.w;
-  const uint32_t sw = (d >> 1) == 0 ? cr.sc.x : ((d >> 1) == 1 ? cr.sc.y : ((d >> 1) == 2 ? cr.sc.z : cr.sc.w));
-  const uint32_t s16 = (d & 1) ? (sw >> 16) : (sw & 0xFFFFu);
-  const uint32_t s_pair = s16 | (s16 << 16);
+__device__ __forceinline__ void a_store(const BlockRegs& r, lds_b* At, int tid, int acg) {
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int row = (tid >> 4) + 16 * q;
+    *reinterpret_cast<lds_q*>(At + row * kRowBytes + 16 * acg) = u32x4{r.a[q].x, r.a[q].y, r.a[q].z, r.a[q].w};
+  }
+}
+
+// Unpack block bd of the item into B-tile rows (Bt).  w: the sign words of the block's
+// half, sw: the scale word holding the block's scale.
+__device__ __forceinline__ void sign_store(const BItem& b, const uint4 w, const uint32_t sw, lds_b* Bt, int bd) {
+  const int p = bd & 3;
+  // the block's fp16 scale in both halves of a dword.  The asm statement keeps this
+  // step here: folded back onto the loop-carried load, it would wait for the newest loads.
+  uint32_t s_pair;
+  const uint32_t sel = (bd & 1) ? 0x03020302u : 0x01000100u;
+  asm volatile("v_perm_b32 %0, %1, %1, %2" : "=v"(s_pair) : "v"(sw), "v"(sel));
   lds_b* rowp = Bt + b.brow * kRowBytes;
 #pragma unroll
   for (int ee = 0; ee < 4; ++ee) {
-    const uint32_t W = ee == 0 ? w0 : (ee == 1 ? w1 : (ee == 2 ? w2 : w3));
+    const uint32_t W = ee == 0 ? w.x : (ee == 1 ? w.y : (ee == 2 ? w.z : w.w));
     uint32_t dw[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) dw[j] = s_pair ^ ((W << (15 - 4 * j - p)) & 0x80008000u);
     *reinterpret_cast<lds_q*>(rowp + 16 * group_of(b.bg, ee)) = u32x4{dw[0], dw[1], dw[2], dw[3]};
   }
+}
+
+// Add one outlier into the fp16 weight at byte offset off of the tile: the sum is
+// taken in fp32 and rounded to fp16 once.
+__device__ __forceinline__ void add_outlier(lds_b* Bt, int off, float add) {
+  lds_h* hp = reinterpret_cast<lds_h*>(Bt + off);
+  __half_raw hr;
+  hr.x = *hp;
+  hr = __half_raw(__float2half_rn(__half2float(__half(hr)) + add));
+  *hp = hr.x;
+}
+
+// Unstaged outliers: the item's own walk over its row's CSR list in HBM, adding the
+// entries of block bd that fall in the item's columns.
+__device__ __forceinline__ void walk_outliers(BItem& b, lds_b* Bt, int bd, const gale_matrix* table) {
   const int k0 = 128 * bd, k1 = k0 + 128;
   // b.ncol / b.nq hold entry b.cur (or a column past the end), so the test never waits
   while (b.ncol < k1) {
     const int col = b.ncol, q = b.nq;
     ++b.cur;
     if (b.cur < b.cend) {
-      if (staged) {
-        b.ncol = st_col[b.cur];
-        b.nq = st_val[b.cur];
-      } else {
-        const gale_matrix* M = table + b.gsrc;
-        b.ncol = M->out_cols[b.cur];
-        b.nq = outlier_value(M->out_vals, b.cur);
-      }
+      const gale_matrix* M = table + b.gsrc;
+      b.ncol = M->out_cols[b.cur];
+      b.nq = outlier_value(M->out_vals, b.cur);
     } else {
       b.ncol = 0x7fffffff;
     }
     const int cb = col - k0;
-    if ((((cb >> 6) & 1) | (((cb >> 4) & 1) << 1)) == b.bg) {
-      const int i = cb & 7;
-      lds_h* hp = reinterpret_cast<lds_h*>(rowp + 16 * (cb >> 3) + 2 * (2 * (i & 3) + (i >> 2)));
-      __half_raw hr;
-      hr.x = *hp;
-      const float v = __half2float(__half(hr)) + b.rscale * (float)q;
-      hr = __half_raw(__float2half_rn(v));
-      *hp = hr.x;
+    if ((((cb >> 6) & 1) | (((cb >> 4) & 1) << 1)) == b.bg) add_outlier(Bt, b_offset(b.brow, cb), b.rscale * (float)q);
+  }
+}
+
+// Staged outliers of bucket (row group tt, block j) for one wavefront: lane i takes
+// entry i.  starts: lane l holds the start of bucket (tt, l), l <= NB.
+struct Patch {
+  int s0, s1;                   // the bucket's entry range (uniform)
+  int off;                      // lane's entry: byte offset in the tile (-1: none)
+  float add;                    // ... and the value to add
+};
+
+struct PatchEntry {
+  int off;
+  float add;
+};
+
+__device__ __forceinline__ PatchEntry patch_entry(const lds_h* st_ent, const lds_f32* st_rs, int tt, int i) {
+  const uint32_t ent = st_ent[i];
+  const int rl = (ent >> 7) & 15, cb = ent & 127;
+  const int q = (int)(ent << 17) >> 28;                      // int4 in bits 11..14
+  const int row = 16 * tt + rl;
+  PatchEntry pe;
+  pe.off = b_offset(row, cb);
+  pe.add = st_rs[row] * (float)q;
+  return pe;
+}
+
+// j < NB: bucket (tt, j); j == NB: no entries
+__device__ __forceinline__ Patch patch_prep(const lds_h* st_ent, const lds_f32* st_rs, int starts, int tt, int j,
+                                            int NB, int lane) {
+  Patch pt;
+  const int jj = j < NB ? j : NB - 1;
+  pt.s0 = __builtin_amdgcn_readlane(starts, jj);
+  pt.s1 = j < NB ? __builtin_amdgcn_readlane(starts, jj + 1) : pt.s0;
+  pt.off = -1;
+  pt.add = 0.f;
+  if (pt.s0 + lane < pt.s1) {
+    const PatchEntry pe = patch_entry(st_ent, st_rs, tt, pt.s0 + lane);
+    pt.off = pe.off;
+    pt.add = pe.add;
+  }
+  return pt;
+}
+
+// After the wavefront's own sign stores of the bucket's rows.  Entries past the first
+// 64 (dense buckets) are read and added here.
+__device__ __forceinline__ void patch_apply(const Patch pt, lds_b* Bt, const lds_h* st_ent, const lds_f32* st_rs,
+                                            int tt, int lane) {
+  asm volatile("" ::: "memory");   // the sign stores stay before the reads below
+  if (pt.off >= 0) add_outlier(Bt, pt.off, pt.add);
+  for (int base = pt.s0 + 64; base < pt.s1; base += 64) {
+    const int i = base + lane;
+    if (i < pt.s1) {
+      const PatchEntry pe = patch_entry(st_ent, st_rs, tt, i);
+      add_outlier(Bt, pe.off, pe.add);
     }
   }
 }
 
-// A staging: chunk q = tid + 256 j -> row q / 16, 16-byte column group q % 16.
-struct AStage {
-  int row[8];                   // source row per chunk (-1: beyond the tile's pairs)
-  uint4 reg[8];
-};
-
-__device__ __forceinline__ void a_load(AStage& a, const uint16_t* A, int K, int bd, int acg) {
+// The 16 products of one 128-column block for one wavefront: four K-steps of 32, each
+// reading four B and four A fragments (16 bytes per lane) from LDS.  nfm (uniform):
+// fragments of 16 pairs that hold pairs; the rest are skipped.
+__device__ __forceinline__ void mfma_block(v4f (&acc)[4][4], const lds_b* At, const lds_b* Bt, int wm, int wn,
+                                           int nfm, int ml, int lg) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (a.row[j] >= 0)
-      a.reg[j] = *reinterpret_cast<const uint4*>(A + (int64_t)a.row[j] * K + 128 * bd + 8 * acg);
-    else
-      a.reg[j] = make_uint4(0, 0, 0, 0);
+  for (int ee = 0; ee < 4; ++ee) {
+    const int goff = 16 * group_of(lg, ee);
+    v8h bf[4], af[4];
+#pragma unroll
+    for (int nf = 0; nf < 4; ++nf)
+      bf[nf] = as_v8h(*reinterpret_cast<const lds_q*>(Bt + (64 * wn + 16 * nf + ml) * kRowBytes + goff));
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+      af[f] = as_v8h(*reinterpret_cast<const lds_q*>(At + (64 * wm + 16 * f + ml) * kRowBytes + goff));
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      if (f < nfm) {
+#pragma unroll
+        for (int nf = 0; nf < 4; ++nf)
+          acc[f][nf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[f], bf[nf], acc[f][nf], 0, 0, 0);
+      }
+    }
   }
 }
 
-__device__ __forceinline__ void a_store(const AStage& a, lds_b* At, int tid, int acg) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = (tid >> 4) + 16 * j;
-    *reinterpret_cast<lds_q*>(At + r * kRowBytes + 16 * acg) = u32x4{a.reg[j].x, a.reg[j].y, a.reg[j].z, a.reg[j].w};
+// Stores block j into the B buffer Bt (and A into At): A chunks, sign unpack, outliers.
+template <bool STAGED>
+__device__ __forceinline__ void store_block(const BlockRegs& r, BItem& b0, BItem& b1, lds_b* At, lds_b* Bt, int j,
+                                            int tid, int acg, const Patch p0, const Patch p1, int tt0,
+                                            const lds_h* st_ent, const lds_f32* st_rs, const gale_matrix* table) {
+  a_store(r, At, tid, acg);
+  sign_store(b0, r.w[0], r.s[0], Bt, j);
+  sign_store(b1, r.w[1], r.s[1], Bt, j);
+  if (STAGED) {
+    const int lane = tid & 63;
+    patch_apply(p0, Bt, st_ent, st_rs, tt0, lane);
+    patch_apply(p1, Bt, st_ent, st_rs, tt0 + 4, lane);
+  } else {
+    walk_outliers(b0, Bt, j, table);
+    walk_outliers(b1, Bt, j, table);
+  }
+}
+
+// The K loop over blocks of 128 columns, two LDS buffers: while the products of block
+// bd run on one buffer, block bd + 1 is stored into the other from registers, and the
+// registers are refilled with block bd + 3.  NB (blocks) is a multiple of 8, so the
+// loop takes blocks in pairs and each register set serves one parity.  The last pass
+// also stores a block NB (a copy of block NB - 1's words, no outliers left) that
+// nothing reads.
+template <bool STAGED>
+__device__ __forceinline__ void gemm_k_loop(const GemmParams& P, v4f (&acc)[4][4], lds_b* A0, lds_b* B0,
+                                            const AStage& as, BItem& b0, BItem& b1, int NB, int tid, int acg,
+                                            int wm, int wn, int nfm, int ml, int lg, const lds_h* st_ent,
+                                            const lds_f32* st_rs, int starts0, int starts1) {
+  lds_b* const A1 = A0 + kTileBytes;
+  lds_b* const B1 = B0 + kTileBytes;
+  const int lane = tid & 63, tt0 = b0.brow >> 4;
+  Patch p0 = {0, 0, -1, 0.f}, p1 = {0, 0, -1, 0.f};
+  BlockRegs re, ro;   // blocks of even and of odd index
+  block_load(re, as, b0, b1, P.A, P.K, 0, acg);
+  if (STAGED) {
+    p0 = patch_prep(st_ent, st_rs, starts0, tt0, 0, NB, lane);
+    p1 = patch_prep(st_ent, st_rs, starts1, tt0 + 4, 0, NB, lane);
+  }
+  store_block<STAGED>(re, b0, b1, A0, B0, 0, tid, acg, p0, p1, tt0, st_ent, st_rs, P.table);
+  // the two sets issue in order (no interleaving): the loop's waits count whole sets
+  __builtin_amdgcn_sched_barrier(0);
+  block_load(ro, as, b0, b1, P.A, P.K, 1, acg);
+  __builtin_amdgcn_sched_barrier(0);
+  block_load(re, as, b0, b1, P.A, P.K, 2, acg);
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+  for (int bd = 0; bd < NB; bd += 2) {
+    // block bd (buffer 0) runs; block bd + 1 into buffer 1
+    if (STAGED) {
+      p0 = patch_prep(st_ent, st_rs, starts0, tt0, bd + 1, NB, lane);
+      p1 = patch_prep(st_ent, st_rs, starts1, tt0 + 4, bd + 1, NB, lane);
+    }
+    mfma_block(acc, A0, B0, wm, wn, nfm, ml, lg);
+    store_block<STAGED>(ro, b0, b1, A1, B1, bd + 1, tid, acg, p0, p1, tt0, st_ent, st_rs, P.table);
+    block_load(ro, as, b0, b1, P.A, P.K, min(bd + 3, NB - 1), acg);
+    __syncthreads();
+    // block bd + 1 (buffer 1) runs; block bd + 2 into buffer 0
+    if (STAGED) {
+      p0 = patch_prep(st_ent, st_rs, starts0, tt0, bd + 2, NB, lane);
+      p1 = patch_prep(st_ent, st_rs, starts1, tt0 + 4, bd + 2, NB, lane);
+    }
+    mfma_block(acc, A1, B1, wm, wn, nfm, ml, lg);
+    store_block<STAGED>(re, b0, b1, A0, B0, bd + 2, tid, acg, p0, p1, tt0, st_ent, st_rs, P.table);
+    block_load(re, as, b0, b1, P.A, P.K, min(bd + 4, NB - 1), acg);
+    __syncthreads();
   }
 }
 
@@ -361,74 +539,88 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(const GemmParams P) {
   const int pair0 = P.offsets[e] + m0;
   const int valid = min(kGemmBM, P.offsets[e + 1] - pair0);
   const int n0 = blockIdx.x * P.half_rows;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int C = P.K >> 10;
   const int NB = P.K >> 7;
 
   lds_b* const base = (lds_b*)smem;
   lds_b* const A0 = base;
   lds_b* const B0 = base + 2 * kTileBytes;
-  lds_h* const st_col = reinterpret_cast<lds_h*>(base + 4 * kTileBytes);
-  lds_i8* const st_val = reinterpret_cast<lds_i8*>(base + 4 * kTileBytes + 2 * kOutStage);
-  lds_i32* const st_off = reinterpret_cast<lds_i32*>(base + 4 * kTileBytes + 3 * kOutStage);
+  lds_h* const st_ent = reinterpret_cast<lds_h*>(base + 4 * kTileBytes);
+  lds_i32* const st_start = reinterpret_cast<lds_i32*>(base + 4 * kTileBytes + 2 * kOutStage);
+  lds_i32* const st_fill = st_start + kBuckets + 1;
+  lds_f32* const st_rs = reinterpret_cast<lds_f32*>(st_fill + kBuckets);
+  lds_i32* const st_misc = reinterpret_cast<lds_i32*>(st_rs + 128);
+  lds_i32* const s_orow = st_misc + 8;                       // output row of tile pair m
 
-  // ---- stage the outlier entries of the 128 B-tile rows: counts, scan, copy.  B-tile
-  //      row r belongs to matrix (r < half_rows ? sel_a : sel_b), global row n0 + r % half_rows.
-  {
-    int cnt = 0;
-    if (tid < 128) {
-      const gale_matrix* M = P.table + 3 * e + (tid >= P.half_rows ? P.sel_b : P.sel_a);
-      const int g = n0 + tid % P.half_rows;
-      cnt = M->row_ptr[g + 1] - M->row_ptr[g];
-    }
-    // exclusive scan over the first 128 threads (two wavefronts)
-    int v = cnt;
+  // ---- outlier staging.  Row r = tid / 2 of the B tile (matrix sel_a for r < half_rows,
+  //      else sel_b; global row n0 + r % half_rows) is walked by two threads, entries of
+  //      parity tid & 1: count per bucket, scan, then place each entry.
+  const int r = tid >> 1, par = tid & 1;
+  const gale_matrix* Mr = P.table + 3 * e + (r >= P.half_rows ? P.sel_b : P.sel_a);
+  const int gr = n0 + r % P.half_rows;
+  const int rp0 = Mr->row_ptr[gr], rp1 = Mr->row_ptr[gr + 1];
+  const int nbk = 8 * NB;                                    // buckets in use
+  if (tid == 0) st_misc[0] = 0;
+  if (tid < kGemmBM) s_orow[tid] = tid < valid ? P.perm[pair0 + tid] : 0;
+  for (int b = tid; b < kBuckets; b += 256) st_fill[b] = 0;
+  if (par == 0) {
+    __half_raw hr;
+    hr.x = Mr->row_scales[gr];
+    st_rs[r] = __half2float(__half(hr));
+  }
+  __syncthreads();
+  if (par == 0) __atomic_fetch_add(st_misc, rp1 - rp0, __ATOMIC_RELAXED);
+  __syncthreads();
+  const bool staged = st_misc[0] <= kOutStage && NB <= kStageBlocks;
+  const int bucket0 = (r >> 4) * NB;
+  if (staged) {
+    for (int p = rp0 + par; p < rp1; p += 2)
+      __atomic_fetch_add(st_fill + bucket0 + (Mr->out_cols[p] >> 7), 1, __ATOMIC_RELAXED);
+    __syncthreads();
+    // exclusive scan of the bucket counts, two per thread
+    const int c0 = 2 * tid < nbk ? st_fill[2 * tid] : 0;
+    const int c1 = 2 * tid + 1 < nbk ? st_fill[2 * tid + 1] : 0;
+    int v = c0 + c1;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const int o = __shfl_up(v, off, 64);
       if (lane >= off) v += o;
     }
-    if (tid == 63) st_off[129] = v;       // the first wavefront's total
+    if (lane == 63) st_misc[1 + wave] = v;
     __syncthreads();
-    if (tid < 128) st_off[tid] = v - cnt + (wave == 1 ? st_off[129] : 0);
-    if (tid == 127) st_off[128] = v + st_off[129];
+    int ex = v - c0 - c1;
+    for (int w = 0; w < wave; ++w) ex += st_misc[1 + w];
+    if (2 * tid < nbk) st_start[2 * tid] = st_fill[2 * tid] = ex;
+    if (2 * tid + 1 < nbk) st_start[2 * tid + 1] = st_fill[2 * tid + 1] = ex + c0;
+    if (tid == 255) st_start[nbk] = ex + c0 + c1;
     __syncthreads();
-    const int total = st_off[128];
-    if (total <= kOutStage) {
-      // B-tile rows [0, half_rows) and [half_rows, 128) are consecutive rows of one matrix
-      // each, so their entries are (at most) two contiguous CSR ranges: copy them as such
-      const gale_matrix* Ma = P.table + 3 * e + P.sel_a;
-      const gale_matrix* Mb = P.table + 3 * e + P.sel_b;
-      const int na = st_off[P.half_rows];
-      const int ba = Ma->row_ptr[n0];
-      const int bb = P.half_rows < 128 ? Mb->row_ptr[n0] : 0;
-      for (int i = tid; i < total; i += 256) {
-        const bool in_a = i < na;
-        const gale_matrix* M = in_a ? Ma : Mb;
-        const int src = in_a ? ba + i : bb + (i - na);
-        st_col[i] = M->out_cols[src];
-        st_val[i] = (signed char)outlier_value(M->out_vals, src);
-      }
+    for (int p = rp0 + par; p < rp1; p += 2) {
+      const int col = Mr->out_cols[p];
+      const int q = outlier_value(Mr->out_vals, p);
+      const int slot = __atomic_fetch_add(st_fill + bucket0 + (col >> 7), 1, __ATOMIC_RELAXED);
+      st_ent[slot] = (unsigned short)(((q & 15) << 11) | ((r & 15) << 7) | (col & 127));
     }
     __syncthreads();
   }
-  const bool staged = st_off[128] <= kOutStage;
 
   AStage as;
+  const int first_row = P.a_by_token ? P.perm[pair0] / P.top_k : P.perm[pair0];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int r = (tid >> 4) + 16 * j;
-    int src = -1;
-    if (r < valid) {
-      const int s = pair0 + r;
+    const int rr = (tid >> 4) + 16 * j;
+    int src = first_row;
+    if (rr < valid) {
+      const int s = pair0 + rr;
       src = P.a_by_token ? P.perm[s] / P.top_k : P.perm[s];
     }
     as.row[j] = src;
   }
   const int acg = tid & 15;
 
-  BItem b0 = make_item(P, e, n0, C, tid, staged, st_off, st_col, st_val);
-  BItem b1 = make_item(P, e, n0, C, tid + 256, staged, st_off, st_col, st_val);
+  BItem b0 = make_item(P, e, n0, C, tid, staged);
+  BItem b1 = make_item(P, e, n0, C, tid + 256, staged);
 
   // ---- accumulators: wave (wm, wn) = pairs [64 wm, +64) x B rows [64 wn, +64)
   const int wm = wave & 1, wn = wave >> 1;
@@ -437,55 +629,18 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(const GemmParams P) {
   for (int f = 0; f < 4; ++f)
 #pragma unroll
     for (int nf = 0; nf < 4; ++nf) acc[f][nf] = v4f{0.f, 0.f, 0.f, 0.f};
-  const int nfrag_m = max(0, min(4, (valid - 64 * wm + 15) >> 4));   // fragments holding pairs
+  // fragments of 16 pairs that hold pairs (uniform in the wavefront)
+  const int nfm = __builtin_amdgcn_readfirstlane(max(0, min(4, (valid - 64 * wm + 15) >> 4)));
   const int ml = lane & 15, lg = lane >> 4;
 
-  // ---- prologue: block 0
-  ChunkRegs c0 = item_load_chunk(b0, 0);
-  ChunkRegs c1 = item_load_chunk(b1, 0);
-  a_load(as, P.A, P.K, 0, acg);
-  a_store(as, A0, tid, acg);
-  item_store(b0, c0, B0, 0, staged, st_col, st_val, P.table);
-  item_store(b1, c1, B0, 0, staged, st_col, st_val, P.table);
-  __syncthreads();
-
-  for (int bd = 0; bd < NB; ++bd) {
-    const int buf = bd & 1;
-    const bool more = bd + 1 < NB;
-    if (more) {
-      if (((bd + 1) & 7) == 0) {
-        c0 = item_load_chunk(b0, (bd + 1) >> 3);
-        c1 = item_load_chunk(b1, (bd + 1) >> 3);
-      }
-      a_load(as, P.A, P.K, bd + 1, acg);
-    }
-    const lds_b* At = A0 + buf * kTileBytes;
-    const lds_b* Bt = B0 + buf * kTileBytes;
-    // four K-steps of 32
-#pragma unroll
-    for (int ee = 0; ee < 4; ++ee) {
-      const int goff = 16 * group_of(lg, ee);
-      v8h bf[4];
-#pragma unroll
-      for (int nf = 0; nf < 4; ++nf)
-        bf[nf] = as_v8h(*reinterpret_cast<const lds_q*>(Bt + (64 * wn + 16 * nf + ml) * kRowBytes + goff));
-#pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        if (f < nfrag_m) {
-          const v8h af = as_v8h(*reinterpret_cast<const lds_q*>(At + (64 * wm + 16 * f + ml) * kRowBytes + goff));
-#pragma unroll
-          for (int nf = 0; nf < 4; ++nf)
-            acc[f][nf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[nf], acc[f][nf], 0, 0, 0);
-        }
-      }
-    }
-    if (more) {
-      lds_b* Bn = B0 + (buf ^ 1) * kTileBytes;
-      a_store(as, A0 + (buf ^ 1) * kTileBytes, tid, acg);
-      item_store(b0, c0, Bn, bd + 1, staged, st_col, st_val, P.table);
-      item_store(b1, c1, Bn, bd + 1, staged, st_col, st_val, P.table);
-    }
-    __syncthreads();
+  if (staged) {
+    // bucket starts of the wavefront's two row groups, lane l: block l (l <= NB)
+    const int starts0 = lane <= NB ? st_start[wave * NB + lane] : 0;
+    const int starts1 = lane <= NB ? st_start[(wave + 4) * NB + lane] : 0;
+    gemm_k_loop<true>(P, acc, A0, B0, as, b0, b1, NB, tid, acg, wm, wn, nfm, ml, lg, st_ent, st_rs, starts0,
+                      starts1);
+  } else {
+    gemm_k_loop<false>(P, acc, A0, B0, as, b0, b1, NB, tid, acg, wm, wn, nfm, ml, lg, st_ent, st_rs, 0, 0);
   }
 
   // ---- epilogue.  Fragment layout: lane l, register i -> pair 16 f + 4 (l / 16) + i,
@@ -514,8 +669,7 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(const GemmParams P) {
             const int m = 64 * wm + 16 * f + 4 * lg + i;
             if (m >= valid) continue;
             const float g = acc[f][nf][i];
-            const int s = pair0 + m;
-            const int orow = P.perm[s];
+            const int orow = s_orow[m];
             P.out[(int64_t)orow * P.out_stride + n0 + 16 * nf + ml] = g / (1.0f + __expf(-g)) * uu[i];
           }
         }
@@ -530,8 +684,7 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(const GemmParams P) {
         for (int i = 0; i < 4; ++i) {
           const int m = 64 * wm + 16 * f + 4 * lg + i;
           if (m >= valid) continue;
-          const int s = pair0 + m;
-          const int orow = P.perm[s];
+          const int orow = s_orow[m];
           P.out[(int64_t)orow * P.out_stride + n0 + 64 * wn + 16 * nf + ml] = acc[f][nf][i];
         }
       }

@@ -469,6 +469,49 @@ def test_moe_grouped_gemm_outlier_edges(q):
     assert err <= REL_L2_BAR
 
 
+def clustered_outlier_dict(N, K, seed):
+    """Random signs and block scales; every row has 12 outliers in its first 128 columns
+    and 2 in its last 128, so a group of 16 rows holds 192 entries in block 0."""
+    rng = np.random.default_rng(seed)
+    rp, cols, vals = [0], [], []
+    for n in range(N):
+        cs = np.concatenate([np.sort(rng.choice(128, size=12, replace=False)),
+                             K - 128 + np.sort(rng.choice(128, size=2, replace=False))])
+        cols.extend(cs.tolist())
+        vals.extend(rng.integers(-8, 8, size=len(cs)).tolist())
+        rp.append(len(cols))
+    nib = [v & 0xF for v in vals] + ([0] if len(vals) % 2 else [])
+    return {"rows": N, "cols": K, "signs": rng.integers(0, 2 ** 32, size=(N, K // 32), dtype=np.uint64).astype(np.uint32),
+            "block_scales": (np.abs(rng.standard_normal((N, K // 128))) * 0.02).astype(np.float16),
+            "row_scales": np.full(N, 0.05, dtype=np.float16), "row_ptr": np.array(rp),
+            "out_cols": np.array(cols, dtype=np.uint16),
+            "out_vals": np.array([nib[i] | (nib[i + 1] << 4) for i in range(0, len(nib), 2)], dtype=np.uint8)}
+
+
+def test_moe_grouped_gemm_dense_buckets(q):
+    # w1 and w2 rows carry their outliers in the first and last blocks: staged, with
+    # more than 64 entries in one (row group, block) bucket
+    E, T = 3, 70
+    seed = config_seed(13)
+    w3s = gen_matrices(seed, [(e, 1) for e in range(E)], 2048, 4096)
+    experts_np, packed = [], []
+    for e in range(E):
+        d1 = clustered_outlier_dict(2048, 4096, 200 + e)
+        d2 = clustered_outlier_dict(4096, 2048, 300 + e)
+        m3 = w3s[e]
+        experts_np.append((d1, m3.numpy(), d2))
+        packed.append((q.pack_matrix(canon_from_dict(d1)), q.pack_matrix(m3.to(DEV)), q.pack_matrix(canon_from_dict(d2))))
+    tab = q.expert_table(packed)
+    x = gen_x(seed, (1,), T, 4096, device=DEV)
+    lg = gen_logits_normal(seed, (2,), T, E, device=DEV)
+    y, idx, w = q.moe_layer_fwd(tab, 4096, 2048, lg, x, top_k=2, flags=q.GALE_PATH_GROUPED | q.GALE_GROUPED_GEMM)
+    yref, ridx, _ = O.moe(lambda e: experts_np[e], lg.cpu().numpy(), x.cpu().numpy(), k=2)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    err = O.rel_l2(np_of(y), yref).max()
+    print(f"grouped GEMM dense outlier buckets rel-L2 {err:.3e}")
+    assert err <= REL_L2_BAR
+
+
 def test_moe_closed_form(q):
     E = 16
     w1 = q.pack_matrix(canon_from_dict(hadamard_sign_dict(2048, 4096)))
