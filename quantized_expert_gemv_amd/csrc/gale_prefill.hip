@@ -173,8 +173,10 @@ hipError_t launch_rotate_f16(const void* x, int x_dtype, int64_t n_rows, int K, 
 // read touches start on 16 different bank quads.
 //
 // Outliers.  At the start, the workgroup sorts the outlier entries of its 128 rows
-// into buckets of (group of 16 rows, block) in LDS, one 16-bit entry each (int4
-// value, row within the group, column within the block).  The wavefront that
+// into buckets of (group of 16 rows, block) in LDS, one 32-bit entry each (column
+// within the block, row within the group, int4 value, and the row's fp16 scale).
+// The counting tables of the sort live in the second A buffer, which the K loop
+// fills only after them.  The wavefront that
 // unpacks a group of 16 rows also patches them: after its sign stores, lane i adds
 // the bucket's entry i into its weight (LDS operations of one wavefront complete in
 // order, so no barrier is needed).  Rows whose entries exceed the staging space,
@@ -182,12 +184,14 @@ hipError_t launch_rotate_f16(const void* x, int x_dtype, int64_t n_rows, int K, 
 // ---------------------------------------------------------------------------
 constexpr int kRowBytes = 272;
 constexpr int kTileBytes = 128 * kRowBytes;
-constexpr int kOutStage = 6144;                       // staged outlier entries per workgroup
+constexpr int kOutStage = 6000;                       // staged outlier entries per workgroup
 constexpr int kStageBlocks = 56;                      // bucket table: K <= 7168
 constexpr int kBuckets = 8 * kStageBlocks;
-// entries u16 [kOutStage]; bucket starts i32 [kBuckets + 1]; fill cursors i32 [kBuckets];
-// row scales f32 [128]; eight i32 for the total and the scan; output rows i32 [128]
-constexpr int kStageBytes = 2 * kOutStage + 4 * (kBuckets + 1) + 4 * kBuckets + 4 * 128 + 4 * 8 + 4 * 128;
+// entries u32 [kOutStage]; eight i32 for the total and the scan; output rows i32 [128].
+// In the second A buffer during the sort: bucket starts i32 [kBuckets + 1], fill cursors
+// i32 [kBuckets].
+constexpr int kStageBytes = 4 * kOutStage + 4 * 8 + 4 * 128;
+static_assert(4 * (2 * kBuckets + 1) <= kTileBytes, "sort tables fit the second A buffer");
 constexpr size_t kGemmSmem = 4 * (size_t)kTileBytes + kStageBytes;
 
 struct GemmParams {
@@ -212,8 +216,12 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) unsigned char lds_b;
 typedef __attribute__((address_space(3))) u32x4 lds_q;
 typedef __attribute__((address_space(3))) unsigned short lds_h;
+// fp16 weights patched in place: may alias the 16-byte sign stores of the same tile, so the
+// compiler keeps each patch after the stores before it
+typedef __attribute__((address_space(3), may_alias)) unsigned short lds_h_alias;
 typedef __attribute__((address_space(3))) int lds_i32;
 typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
 
 __device__ __forceinline__ v8h as_v8h(const u32x4 v) {
   union { u32x4 u; v8h h; } c;
@@ -260,7 +268,7 @@ __device__ __forceinline__ uint4 gload16(const void* p) {
 }
 __device__ __forceinline__ uint32_t gload4(const void* p) { return *(g_u32*)p; }
 
-__device__ __forceinline__ BItem make_item(const GemmParams& P, int e, int n0, int C, int item, bool staged) {
+__device__ __forceinline__ BItem make_item(const GemmParams& P, int e, int n0, int C, int item) {
   BItem b;
   const int tt = item >> 6, l = item & 63;
   const int r0 = 16 * tt;
@@ -276,19 +284,22 @@ __device__ __forceinline__ BItem make_item(const GemmParams& P, int e, int n0, i
   b.ncol = 0x7fffffff;
   b.nq = 0;
   b.rscale = 0.f;
-  if (!staged) {
-    const int grow = n0 + (r0 + nl) % P.half_rows;
-    __half_raw hr;
-    hr.x = M->row_scales[grow];
-    b.rscale = __half2float(__half(hr));
-    b.cur = M->row_ptr[grow];
-    b.cend = M->row_ptr[grow + 1];
-    if (b.cur < b.cend) {
-      b.ncol = M->out_cols[b.cur];
-      b.nq = outlier_value(M->out_vals, b.cur);
-    }
-  }
   return b;
+}
+
+// Unstaged outliers: the item's cursor on its row's CSR list.
+__device__ __forceinline__ void item_walk_init(const GemmParams& P, int e, int n0, BItem& b) {
+  const gale_matrix* M = P.table + b.gsrc;
+  const int grow = n0 + b.brow % P.half_rows;
+  __half_raw hr;
+  hr.x = M->row_scales[grow];
+  b.rscale = __half2float(__half(hr));
+  b.cur = M->row_ptr[grow];
+  b.cend = M->row_ptr[grow + 1];
+  if (b.cur < b.cend) {
+    b.ncol = M->out_cols[b.cur];
+    b.nq = outlier_value(M->out_vals, b.cur);
+  }
 }
 
 // A staging: chunk q = tid + 256 j -> tile row q / 16, 16-byte column group q % 16.
@@ -351,7 +362,7 @@ __device__ __forceinline__ void sign_store(const BItem& b, const uint4 w, const 
 // Add one outlier into the fp16 weight at byte offset off of the tile: the sum is
 // taken in fp32 and rounded to fp16 once.
 __device__ __forceinline__ void add_outlier(lds_b* Bt, int off, float add) {
-  lds_h* hp = reinterpret_cast<lds_h*>(Bt + off);
+  lds_h_alias* hp = reinterpret_cast<lds_h_alias*>(Bt + off);
   __half_raw hr;
   hr.x = *hp;
   hr = __half_raw(__float2half_rn(__half2float(__half(hr)) + add));
@@ -379,84 +390,91 @@ __device__ __forceinline__ void walk_outliers(BItem& b, lds_b* Bt, int bd, const
 }
 
 // Staged outliers of bucket (row group tt, block j) for one wavefront: lane i takes
-// entry i.  starts: lane l holds the start of bucket (tt, l), l <= NB.
+// entry i.  starts: lane l holds the start of bucket (tt, l), l <= NB.  The entry is read
+// one block ahead of its use, so its LDS latency is hidden behind a block of products.
+constexpr uint32_t kNoEntry = 0x8000u;   // bit 15 is never set in an entry
+
 struct Patch {
   int s0, s1;                   // the bucket's entry range (uniform)
-  int off;                      // lane's entry: byte offset in the tile (-1: none)
-  float add;                    // ... and the value to add
+  uint32_t ent;                 // the lane's entry (kNoEntry: none)
 };
 
-struct PatchEntry {
-  int off;
-  float add;
-};
-
-__device__ __forceinline__ PatchEntry patch_entry(const lds_h* st_ent, const lds_f32* st_rs, int tt, int i) {
-  const uint32_t ent = st_ent[i];
-  const int rl = (ent >> 7) & 15, cb = ent & 127;
-  const int q = (int)(ent << 17) >> 28;                      // int4 in bits 11..14
-  const int row = 16 * tt + rl;
-  PatchEntry pe;
-  pe.off = b_offset(row, cb);
-  pe.add = st_rs[row] * (float)q;
-  return pe;
+// entry: column in the block (bits 0..6), row in the group (7..10), int4 value (11..14),
+// the row's fp16 outlier scale (16..31)
+__device__ __forceinline__ uint32_t pack_entry(int cb, int rl, int q, uint16_t rs) {
+  return (uint32_t)cb | ((uint32_t)rl << 7) | ((uint32_t)(q & 15) << 11) | ((uint32_t)rs << 16);
 }
 
-// j < NB: bucket (tt, j); j == NB: no entries
-__device__ __forceinline__ Patch patch_prep(const lds_h* st_ent, const lds_f32* st_rs, int starts, int tt, int j,
-                                            int NB, int lane) {
+// Byte offset and addend of an entry.  A lane without an entry patches its own pad
+// bytes of the row group (bytes 256..271 of a row, which no operand read touches) with
+// 0, so the patch needs no branch.
+__device__ __forceinline__ void decode_entry(uint32_t ent, int tt, int lane, int& off, float& add) {
+  const int rl = (ent >> 7) & 15, cb = ent & 127;
+  const int q = (int)(ent << 17) >> 28;                      // int4 in bits 11..14
+  __half_raw hr;
+  hr.x = (unsigned short)(ent >> 16);
+  const bool none = (ent & kNoEntry) != 0;
+  off = none ? (16 * tt + (lane & 15)) * kRowBytes + 256 + 2 * (lane >> 4) : b_offset(16 * tt + rl, cb);
+  add = none ? 0.f : __half2float(__half(hr)) * (float)q;
+}
+
+// j < NB: bucket (tt, j); j >= NB: no entries
+__device__ __forceinline__ Patch patch_prep(const lds_u32* st_ent, int starts, int tt, int j, int NB, int lane) {
   Patch pt;
   const int jj = j < NB ? j : NB - 1;
   pt.s0 = __builtin_amdgcn_readlane(starts, jj);
   pt.s1 = j < NB ? __builtin_amdgcn_readlane(starts, jj + 1) : pt.s0;
-  pt.off = -1;
-  pt.add = 0.f;
-  if (pt.s0 + lane < pt.s1) {
-    const PatchEntry pe = patch_entry(st_ent, st_rs, tt, pt.s0 + lane);
-    pt.off = pe.off;
-    pt.add = pe.add;
-  }
+  pt.ent = pt.s0 + lane < pt.s1 ? st_ent[pt.s0 + lane] : kNoEntry;
   return pt;
 }
 
-// After the wavefront's own sign stores of the bucket's rows.  Entries past the first
-// 64 (dense buckets) are read and added here.
-__device__ __forceinline__ void patch_apply(const Patch pt, lds_b* Bt, const lds_h* st_ent, const lds_f32* st_rs,
-                                            int tt, int lane) {
-  asm volatile("" ::: "memory");   // the sign stores stay before the reads below
-  if (pt.off >= 0) add_outlier(Bt, pt.off, pt.add);
+// After the wavefront's own sign stores of the bucket's rows: the first 64 entries,
+// without a branch.
+__device__ __forceinline__ void patch_apply(const Patch pt, lds_b* Bt, int tt, int lane) {
+  int off;
+  float add;
+  decode_entry(pt.ent, tt, lane, off, add);
+  add_outlier(Bt, off, add);
+}
+
+// Entries past the first 64 of a dense bucket (a uniform branch, after the block's region).
+__device__ __forceinline__ void patch_rest(const Patch pt, lds_b* Bt, const lds_u32* st_ent, int tt, int lane) {
+  int off;
+  float add;
   for (int base = pt.s0 + 64; base < pt.s1; base += 64) {
     const int i = base + lane;
-    if (i < pt.s1) {
-      const PatchEntry pe = patch_entry(st_ent, st_rs, tt, i);
-      add_outlier(Bt, pe.off, pe.add);
-    }
+    decode_entry(i < pt.s1 ? st_ent[i] : kNoEntry, tt, lane, off, add);
+    add_outlier(Bt, off, add);
   }
 }
 
 // The 16 products of one 128-column block for one wavefront: four K-steps of 32, each
-// reading four B and four A fragments (16 bytes per lane) from LDS.  nfm (uniform):
-// fragments of 16 pairs that hold pairs; the rest are skipped.
+// reading four B and four A fragments (16 bytes per lane) from LDS.  Fragments of pairs
+// past the tile's end run too (their A rows repeat the first pair; nothing stores them):
+// without branches, the products and the next block's stores form one scheduling region.
+__device__ __forceinline__ void mfma_frags(v8h (&af)[4], v8h (&bf)[4], const lds_b* At, const lds_b* Bt, int wm,
+                                           int wn, int ml, int goff) {
+#pragma unroll
+  for (int nf = 0; nf < 4; ++nf)
+    bf[nf] = as_v8h(*reinterpret_cast<const lds_q*>(Bt + (64 * wn + 16 * nf + ml) * kRowBytes + goff));
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+    af[f] = as_v8h(*reinterpret_cast<const lds_q*>(At + (64 * wm + 16 * f + ml) * kRowBytes + goff));
+}
+
+// The fragments of K-step ee + 1 are read while the products of step ee run.
 __device__ __forceinline__ void mfma_block(v4f (&acc)[4][4], const lds_b* At, const lds_b* Bt, int wm, int wn,
-                                           int nfm, int ml, int lg) {
+                                           int ml, int lg) {
+  v8h af[2][4], bf[2][4];
+  mfma_frags(af[0], bf[0], At, Bt, wm, wn, ml, 16 * group_of(lg, 0));
 #pragma unroll
   for (int ee = 0; ee < 4; ++ee) {
-    const int goff = 16 * group_of(lg, ee);
-    v8h bf[4], af[4];
-#pragma unroll
-    for (int nf = 0; nf < 4; ++nf)
-      bf[nf] = as_v8h(*reinterpret_cast<const lds_q*>(Bt + (64 * wn + 16 * nf + ml) * kRowBytes + goff));
+    if (ee < 3) mfma_frags(af[(ee + 1) & 1], bf[(ee + 1) & 1], At, Bt, wm, wn, ml, 16 * group_of(lg, ee + 1));
 #pragma unroll
     for (int f = 0; f < 4; ++f)
-      af[f] = as_v8h(*reinterpret_cast<const lds_q*>(At + (64 * wm + 16 * f + ml) * kRowBytes + goff));
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      if (f < nfm) {
-#pragma unroll
-        for (int nf = 0; nf < 4; ++nf)
-          acc[f][nf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[f], bf[nf], acc[f][nf], 0, 0, 0);
-      }
-    }
+      for (int nf = 0; nf < 4; ++nf)
+        acc[f][nf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[ee & 1][f], bf[ee & 1][nf], acc[f][nf], 0, 0, 0);
   }
 }
 
@@ -464,14 +482,14 @@ __device__ __forceinline__ void mfma_block(v4f (&acc)[4][4], const lds_b* At, co
 template <bool STAGED>
 __device__ __forceinline__ void store_block(const BlockRegs& r, BItem& b0, BItem& b1, lds_b* At, lds_b* Bt, int j,
                                             int tid, int acg, const Patch p0, const Patch p1, int tt0,
-                                            const lds_h* st_ent, const lds_f32* st_rs, const gale_matrix* table) {
+                                            const lds_u32* st_ent, const gale_matrix* table) {
   a_store(r, At, tid, acg);
   sign_store(b0, r.w[0], r.s[0], Bt, j);
   sign_store(b1, r.w[1], r.s[1], Bt, j);
   if (STAGED) {
     const int lane = tid & 63;
-    patch_apply(p0, Bt, st_ent, st_rs, tt0, lane);
-    patch_apply(p1, Bt, st_ent, st_rs, tt0 + 4, lane);
+    patch_apply(p0, Bt, tt0, lane);
+    patch_apply(p1, Bt, tt0 + 4, lane);
   } else {
     walk_outliers(b0, Bt, j, table);
     walk_outliers(b1, Bt, j, table);
@@ -487,22 +505,26 @@ __device__ __forceinline__ void store_block(const BlockRegs& r, BItem& b0, BItem
 template <bool STAGED>
 __device__ __forceinline__ void gemm_k_loop(const GemmParams& P, v4f (&acc)[4][4], lds_b* A0, lds_b* B0,
                                             const AStage& as, BItem& b0, BItem& b1, int NB, int tid, int acg,
-                                            int wm, int wn, int nfm, int ml, int lg, const lds_h* st_ent,
-                                            const lds_f32* st_rs, int starts0, int starts1) {
+                                            int wm, int wn, int ml, int lg, const lds_u32* st_ent,
+                                            int starts0, int starts1, BlockRegs& re, BlockRegs& ro) {
   lds_b* const A1 = A0 + kTileBytes;
   lds_b* const B1 = B0 + kTileBytes;
   const int lane = tid & 63, tt0 = b0.brow >> 4;
-  Patch p0 = {0, 0, -1, 0.f}, p1 = {0, 0, -1, 0.f};
-  BlockRegs re, ro;   // blocks of even and of odd index
-  block_load(re, as, b0, b1, P.A, P.K, 0, acg);
+  const Patch none = {0, 0, kNoEntry};
+  // patch entries of the block stored next (x) and of the one after (y)
+  Patch px0 = none, px1 = none, py0 = none, py1 = none;
+  // re holds block 0 and ro block 1 (loaded before the outlier staging)
   if (STAGED) {
-    p0 = patch_prep(st_ent, st_rs, starts0, tt0, 0, NB, lane);
-    p1 = patch_prep(st_ent, st_rs, starts1, tt0 + 4, 0, NB, lane);
+    px0 = patch_prep(st_ent, starts0, tt0, 0, NB, lane);
+    px1 = patch_prep(st_ent, starts1, tt0 + 4, 0, NB, lane);
+    py0 = patch_prep(st_ent, starts0, tt0, 1, NB, lane);
+    py1 = patch_prep(st_ent, starts1, tt0 + 4, 1, NB, lane);
   }
-  store_block<STAGED>(re, b0, b1, A0, B0, 0, tid, acg, p0, p1, tt0, st_ent, st_rs, P.table);
-  // the two sets issue in order (no interleaving): the loop's waits count whole sets
-  __builtin_amdgcn_sched_barrier(0);
-  block_load(ro, as, b0, b1, P.A, P.K, 1, acg);
+  store_block<STAGED>(re, b0, b1, A0, B0, 0, tid, acg, px0, px1, tt0, st_ent, P.table);
+  if (STAGED) {
+    patch_rest(px0, B0, st_ent, tt0, lane);
+    patch_rest(px1, B0, st_ent, tt0 + 4, lane);
+  }
   __builtin_amdgcn_sched_barrier(0);
   block_load(re, as, b0, b1, P.A, P.K, 2, acg);
   __builtin_amdgcn_sched_barrier(0);
@@ -510,21 +532,29 @@ __device__ __forceinline__ void gemm_k_loop(const GemmParams& P, v4f (&acc)[4][4
   for (int bd = 0; bd < NB; bd += 2) {
     // block bd (buffer 0) runs; block bd + 1 into buffer 1
     if (STAGED) {
-      p0 = patch_prep(st_ent, st_rs, starts0, tt0, bd + 1, NB, lane);
-      p1 = patch_prep(st_ent, st_rs, starts1, tt0 + 4, bd + 1, NB, lane);
+      px0 = patch_prep(st_ent, starts0, tt0, bd + 2, NB, lane);
+      px1 = patch_prep(st_ent, starts1, tt0 + 4, bd + 2, NB, lane);
     }
-    mfma_block(acc, A0, B0, wm, wn, nfm, ml, lg);
-    store_block<STAGED>(ro, b0, b1, A1, B1, bd + 1, tid, acg, p0, p1, tt0, st_ent, st_rs, P.table);
+    mfma_block(acc, A0, B0, wm, wn, ml, lg);
+    store_block<STAGED>(ro, b0, b1, A1, B1, bd + 1, tid, acg, py0, py1, tt0, st_ent, P.table);
     block_load(ro, as, b0, b1, P.A, P.K, min(bd + 3, NB - 1), acg);
+    if (STAGED) {
+      patch_rest(py0, B1, st_ent, tt0, lane);
+      patch_rest(py1, B1, st_ent, tt0 + 4, lane);
+    }
     __syncthreads();
     // block bd + 1 (buffer 1) runs; block bd + 2 into buffer 0
     if (STAGED) {
-      p0 = patch_prep(st_ent, st_rs, starts0, tt0, bd + 2, NB, lane);
-      p1 = patch_prep(st_ent, st_rs, starts1, tt0 + 4, bd + 2, NB, lane);
+      py0 = patch_prep(st_ent, starts0, tt0, bd + 3, NB, lane);
+      py1 = patch_prep(st_ent, starts1, tt0 + 4, bd + 3, NB, lane);
     }
-    mfma_block(acc, A1, B1, wm, wn, nfm, ml, lg);
-    store_block<STAGED>(re, b0, b1, A0, B0, bd + 2, tid, acg, p0, p1, tt0, st_ent, st_rs, P.table);
+    mfma_block(acc, A1, B1, wm, wn, ml, lg);
+    store_block<STAGED>(re, b0, b1, A0, B0, bd + 2, tid, acg, px0, px1, tt0, st_ent, P.table);
     block_load(re, as, b0, b1, P.A, P.K, min(bd + 4, NB - 1), acg);
+    if (STAGED) {
+      patch_rest(px0, B0, st_ent, tt0, lane);
+      patch_rest(px1, B0, st_ent, tt0 + 4, lane);
+    }
     __syncthreads();
   }
 }
@@ -547,12 +577,37 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(const GemmParams P) {
   lds_b* const base = (lds_b*)smem;
   lds_b* const A0 = base;
   lds_b* const B0 = base + 2 * kTileBytes;
-  lds_h* const st_ent = reinterpret_cast<lds_h*>(base + 4 * kTileBytes);
-  lds_i32* const st_start = reinterpret_cast<lds_i32*>(base + 4 * kTileBytes + 2 * kOutStage);
-  lds_i32* const st_fill = st_start + kBuckets + 1;
-  lds_f32* const st_rs = reinterpret_cast<lds_f32*>(st_fill + kBuckets);
-  lds_i32* const st_misc = reinterpret_cast<lds_i32*>(st_rs + 128);
+  lds_u32* const st_ent = reinterpret_cast<lds_u32*>(base + 4 * kTileBytes);
+  lds_i32* const st_misc = reinterpret_cast<lds_i32*>(base + 4 * kTileBytes + 4 * kOutStage);
   lds_i32* const s_orow = st_misc + 8;                       // output row of tile pair m
+  lds_i32* const st_start = reinterpret_cast<lds_i32*>(A0 + kTileBytes);   // during the sort
+  lds_i32* const st_fill = st_start + kBuckets + 1;
+
+  AStage as;
+  const int first_row = P.a_by_token ? P.perm[pair0] / P.top_k : P.perm[pair0];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int rr = (tid >> 4) + 16 * j;
+    int src = first_row;
+    if (rr < valid) {
+      const int s = pair0 + rr;
+      src = P.a_by_token ? P.perm[s] / P.top_k : P.perm[s];
+    }
+    as.row[j] = src;
+  }
+  const int acg = tid & 15;
+
+  BItem b0 = make_item(P, e, n0, C, tid);
+  BItem b1 = make_item(P, e, n0, C, tid + 256);
+  // blocks 0 and 1 load while the outliers are staged; the two sets issue in order (no
+  // interleaving), so the K loop's waits count whole sets
+  BlockRegs re, ro;   // blocks of even and of odd index
+  __builtin_amdgcn_sched_barrier(0);
+  block_load(re, as, b0, b1, P.A, P.K, 0, acg);
+  __builtin_amdgcn_sched_barrier(0);
+  block_load(ro, as, b0, b1, P.A, P.K, 1, acg);
+  __builtin_amdgcn_sched_barrier(0);
+
 
   // ---- outlier staging.  Row r = tid / 2 of the B tile (matrix sel_a for r < half_rows,
   //      else sel_b; global row n0 + r % half_rows) is walked by two threads, entries of
@@ -565,19 +620,23 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(const GemmParams P) {
   if (tid == 0) st_misc[0] = 0;
   if (tid < kGemmBM) s_orow[tid] = tid < valid ? P.perm[pair0 + tid] : 0;
   for (int b = tid; b < kBuckets; b += 256) st_fill[b] = 0;
-  if (par == 0) {
-    __half_raw hr;
-    hr.x = Mr->row_scales[gr];
-    st_rs[r] = __half2float(__half(hr));
-  }
   __syncthreads();
   if (par == 0) __atomic_fetch_add(st_misc, rp1 - rp0, __ATOMIC_RELAXED);
   __syncthreads();
   const bool staged = st_misc[0] <= kOutStage && NB <= kStageBlocks;
   const int bucket0 = (r >> 4) * NB;
+  int starts0 = 0, starts1 = 0;
   if (staged) {
-    for (int p = rp0 + par; p < rp1; p += 2)
-      __atomic_fetch_add(st_fill + bucket0 + (Mr->out_cols[p] >> 7), 1, __ATOMIC_RELAXED);
+    // the walks take the thread's entries eight at a time, loads first (clamped into the
+    // row's range) so that eight are in flight
+    for (int p0 = rp0 + par; p0 < rp1; p0 += 16) {
+      int col[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) col[k] = Mr->out_cols[min(p0 + 2 * k, rp1 - 1)];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (p0 + 2 * k < rp1) __atomic_fetch_add(st_fill + bucket0 + (col[k] >> 7), 1, __ATOMIC_RELAXED);
+    }
     __syncthreads();
     // exclusive scan of the bucket counts, two per thread
     const int c0 = 2 * tid < nbk ? st_fill[2 * tid] : 0;
@@ -596,31 +655,33 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(const GemmParams P) {
     if (2 * tid + 1 < nbk) st_start[2 * tid + 1] = st_fill[2 * tid + 1] = ex + c0;
     if (tid == 255) st_start[nbk] = ex + c0 + c1;
     __syncthreads();
-    for (int p = rp0 + par; p < rp1; p += 2) {
-      const int col = Mr->out_cols[p];
-      const int q = outlier_value(Mr->out_vals, p);
-      const int slot = __atomic_fetch_add(st_fill + bucket0 + (col >> 7), 1, __ATOMIC_RELAXED);
-      st_ent[slot] = (unsigned short)(((q & 15) << 11) | ((r & 15) << 7) | (col & 127));
+    const uint16_t rs = Mr->row_scales[gr];
+    for (int p0 = rp0 + par; p0 < rp1; p0 += 16) {
+      int col[8], q[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int p = min(p0 + 2 * k, rp1 - 1);
+        col[k] = Mr->out_cols[p];
+        q[k] = outlier_value(Mr->out_vals, p);
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (p0 + 2 * k < rp1) {
+          const int slot = __atomic_fetch_add(st_fill + bucket0 + (col[k] >> 7), 1, __ATOMIC_RELAXED);
+          st_ent[slot] = pack_entry(col[k] & 127, r & 15, q[k], rs);
+        }
+      }
     }
+    // bucket starts of the wavefront's two row groups, lane l: block l (l <= NB)
+    starts0 = lane <= NB ? st_start[wave * NB + lane] : 0;
+    starts1 = lane <= NB ? st_start[(wave + 4) * NB + lane] : 0;
     __syncthreads();
   }
 
-  AStage as;
-  const int first_row = P.a_by_token ? P.perm[pair0] / P.top_k : P.perm[pair0];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int rr = (tid >> 4) + 16 * j;
-    int src = first_row;
-    if (rr < valid) {
-      const int s = pair0 + rr;
-      src = P.a_by_token ? P.perm[s] / P.top_k : P.perm[s];
-    }
-    as.row[j] = src;
+  if (!staged) {
+    item_walk_init(P, e, n0, b0);
+    item_walk_init(P, e, n0, b1);
   }
-  const int acg = tid & 15;
-
-  BItem b0 = make_item(P, e, n0, C, tid, staged);
-  BItem b1 = make_item(P, e, n0, C, tid + 256, staged);
 
   // ---- accumulators: wave (wm, wn) = pairs [64 wm, +64) x B rows [64 wn, +64)
   const int wm = wave & 1, wn = wave >> 1;
@@ -629,19 +690,12 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(const GemmParams P) {
   for (int f = 0; f < 4; ++f)
 #pragma unroll
     for (int nf = 0; nf < 4; ++nf) acc[f][nf] = v4f{0.f, 0.f, 0.f, 0.f};
-  // fragments of 16 pairs that hold pairs (uniform in the wavefront)
-  const int nfm = __builtin_amdgcn_readfirstlane(max(0, min(4, (valid - 64 * wm + 15) >> 4)));
   const int ml = lane & 15, lg = lane >> 4;
 
-  if (staged) {
-    // bucket starts of the wavefront's two row groups, lane l: block l (l <= NB)
-    const int starts0 = lane <= NB ? st_start[wave * NB + lane] : 0;
-    const int starts1 = lane <= NB ? st_start[(wave + 4) * NB + lane] : 0;
-    gemm_k_loop<true>(P, acc, A0, B0, as, b0, b1, NB, tid, acg, wm, wn, nfm, ml, lg, st_ent, st_rs, starts0,
-                      starts1);
-  } else {
-    gemm_k_loop<false>(P, acc, A0, B0, as, b0, b1, NB, tid, acg, wm, wn, nfm, ml, lg, st_ent, st_rs, 0, 0);
-  }
+  if (staged)
+    gemm_k_loop<true>(P, acc, A0, B0, as, b0, b1, NB, tid, acg, wm, wn, ml, lg, st_ent, starts0, starts1, re, ro);
+  else
+    gemm_k_loop<false>(P, acc, A0, B0, as, b0, b1, NB, tid, acg, wm, wn, ml, lg, st_ent, 0, 0, re, ro);
 
   // ---- epilogue.  Fragment layout: lane l, register i -> pair 16 f + 4 (l / 16) + i,
   //      B row 16 nf + l % 16 of the wave's range.
