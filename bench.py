@@ -147,6 +147,76 @@ def cpu_baseline(synth, O, seed, xs, logits, gpu_y, n_layers):
     return per_token, threads, max(errs)
 
 
+SWEEP_SHAPES = ((2048, 4096, 0.01), (2048, 4096, 0.02), (2048, 4096, 0.03), (2048, 4096, 0.05),
+                (3072, 7168, 0.01), (7168, 3072, 0.01))
+
+
+def packed_matrix_bytes(rows: int, cols: int, frac: float) -> int:
+    """Bytes of one packed matrix: signs, fp16 block scales, uint16 outlier columns,
+    int4 outlier values, fp16 row scales (round(frac * cols) outliers per row)."""
+    import synth
+    nnz = rows * synth.n_outliers(cols, frac)
+    return rows * cols // 8 + rows * cols // 128 * 2 + 2 * nnz + (nnz + 1) // 2 + 2 * rows
+
+
+def sweep_gemv(q, synth, lib, dev, seed, reps: int, warm_s: float):
+    """Sustained GEMV (one launch over >= 1 GB of distinct matrices, one token each) across
+    outlier budgets and matrix shapes: GB/s of algorithmic bytes against bits per weight."""
+    import torch
+    res = []
+    for rows, cols, frac in SWEEP_SHAPES:
+        unit = packed_matrix_bytes(rows, cols, frac)
+        # a power of two of at least 512 matrices and 1 GB per set: the persistent workgroups'
+        # runs of units then start on matrix boundaries, as in the main measurement
+        n = 512
+        while n * unit < (1 << 30):
+            n *= 2
+        sets = []
+        for k in range(2):                       # two disjoint sets, alternated
+            b = synth.gen_matrix_bank(seed, [(0x50000 + k, rows, int(frac * 1000), i) for i in range(n)], rows, cols,
+                                      outlier_frac=frac, device=dev)
+            sg, sc = q.pack_device(rows, cols, n, b["signs"], b["block_scales"])
+            del b["signs"], b["block_scales"]
+            nw, ns = rows * cols // 32, rows * cols // 128
+            mats = [q.PackedMatrix(rows, cols, sg[i * nw:(i + 1) * nw], sc[i * ns:(i + 1) * ns], b["row_scales"],
+                                   b["row_ptr"], b["out_cols"][i], b["out_vals"][i]) for i in range(n)]
+            sets.append((q.matrix_table(mats), mats, sg, sc, b))
+        from synth import gen_x
+        xg = torch.stack([gen_x(seed, (0x51000 + i,), 1, cols, device=dev) for i in range(n)])
+        rec = q.prepare_activations(xg)
+        yg = torch.empty(n, 1, rows, dtype=torch.float16, device=dev)
+        flip = [0]
+
+        def call():
+            t = sets[flip[0]][0]
+            flip[0] ^= 1
+            rc = lib.gale_expert_gemv(rows, cols, t.ptr(), n, rec.data_ptr(), q.GALE_F16, 0, 1, yg.data_ptr(),
+                                      q.GALE_F16, None, 0, q.GALE_X_PREPARED, torch.cuda.current_stream().cuda_stream)
+            if rc:
+                raise RuntimeError(lib.gale_last_error().decode())
+
+        t_w = time.time()                       # steady clocks first, as for the main measurement
+        while time.time() - t_w < warm_s:
+            for _ in range(8):
+                call()
+            torch.cuda.synchronize()
+        for _ in range(GEMV_WARM_CALLS):
+            call()
+        torch.cuda.synchronize()
+        ms = time_events(call, reps)
+        bytes_launch = n * (unit + 2 * cols + 2 * rows)
+        gbps = bytes_launch / (ms * 1e-3) / 1e9
+        bpw = 8.0 * unit / (rows * cols)
+        log(f"sweep: [{rows}, {cols}] outliers {frac:.0%} ({bpw:.3f} b/w): {n} matrices in {ms * 1e3:.1f} us -> "
+            f"{gbps:.0f} GB/s ({100 * gbps / HBM_PEAK_GBPS:.1f}% of 8 TB/s)")
+        res.append({"rows": rows, "cols": cols, "outlier_frac": frac, "bits_per_weight": round(bpw, 4),
+                    "matrices_per_launch": n, "avg_launch_us": round(ms * 1e3, 2), "gbps": round(gbps, 1),
+                    "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)})
+        del sets, rec, yg, xg
+        torch.cuda.empty_cache()
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -160,6 +230,8 @@ def main() -> int:
     ap.add_argument("--cpu-layers", type=int, default=16)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="also time the sustained GEMV at outlier budgets 1/2/3/5 %% and the DeepSeek-V4-Pro shapes")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -215,6 +287,7 @@ def main() -> int:
     gemv_gbps = n * GEMV_UNIT_BYTES / (ms_gemv * 1e-3) / 1e9
     log(f"sustained GEMV: {n} matrices in {ms_gemv * 1e3:.1f} us -> {gemv_gbps:.0f} GB/s "
         f"({100 * gemv_gbps / HBM_PEAK_GBPS:.1f}% of 8 TB/s)")
+    sweep = sweep_gemv(q, synth, lib, dev, seed, args.gemv_reps, args.device_warm_s) if args.sweep else None
 
 
     xs = [gen_x(seed, (0x10000 + l,), 1, HIDDEN, device=dev) for l in range(L)]
@@ -329,7 +402,7 @@ def main() -> int:
         "bytes_per_token": bytes_per_token,
         "roofline": {"bound": "hbm", "achieved": round(gemv_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gemv_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "kernel": "gemv_kernel<1,4,false> (fp4 sign-plane MFMA GEMV)",
+                     "kernel": "gemv_kernel<1,4,false,512> (fp4 sign-plane MFMA GEMV)",
                      "launch": f"{n} distinct [2048,4096] matrices (w1, w3 of {n // 2} experts) x 1 token, "
                                f"prepared activations; two disjoint sets alternated",
                      "bytes_per_launch": n * GEMV_UNIT_BYTES, "avg_launch_us": round(ms_gemv * 1e3, 2),
@@ -339,6 +412,7 @@ def main() -> int:
                     "ms": round(ms_prefill, 4), "tokens_per_s": round(PREFILL_TOKENS / ms_prefill * 1e3, 1),
                     "dense_equiv_tflops": round(prefill_tflops, 2),
                     "frac_of_fp16_mfma_peak": round(prefill_tflops / MFMA_FP16_PEAK_TFLOPS, 4)},
+        "gemv_sweep": sweep,
         "stream_ceiling": {"value": round(ceil_gbps, 1), "unit": "GB/s",
                            "kernel": "torch.neg fp32, read 1 GiB + write 1 GiB"},
     }

@@ -77,6 +77,9 @@ extern "C" {
 #define GALE_SCALE_BLOCK    128   /* weights per fp16 block scale */
 #define GALE_MAX_COLS     16384   /* cols: multiple of 1024, at most this */
 #define GALE_MAX_ROWS   1048576   /* rows: multiple of 16, at most this */
+#define GALE_MAX_HIDDEN    8192   /* expert FFN / MoE hidden size: the w1/w3 GEMV runs one wavefront
+                                   per 1024 columns of each matrix in one workgroup of at most
+                                   1024 threads */
 #define GALE_MAX_TOPK         8
 #define GALE_MAX_EXPERTS    512
 #define GALE_MAX_DECODE_TOKENS 64 /* gale_moe_layer_fwd decode path limit */
@@ -211,7 +214,7 @@ size_t gale_ffn_workspace_bytes(int32_t hidden, int32_t inter, int32_t n_exp, in
 /* Expert FFN for n_exp experts (model card naming: w1 gate, w3 up, w2 down):
  *   y[e][t] = w2_e . H( silu(w1_e . H x) * (w3_e . H x) ),  x = x[e][t] (or x[t] if x_shared).
  * experts_dev: device array of n_exp gale_expert.  x, y fp16 [.. ][n_tok][hidden];
- * intermediate h and every sum in fp32. */
+ * intermediate h and every sum in fp32.  hidden <= GALE_MAX_HIDDEN (else GALE_ERR_SHAPE). */
 int gale_expert_ffn(int32_t hidden, int32_t inter, const gale_expert* experts_dev, int32_t n_exp,
                     const void* x, int32_t x_shared, int32_t n_tok, void* y,
                     void* ws, size_t ws_bytes, hipStream_t stream);
@@ -247,7 +250,9 @@ size_t gale_moe_workspace_bytes(int32_t n_tok, int32_t n_experts, int32_t top_k,
  *           for every expert.
  * Flags GALE_PATH_DECODE / GALE_PATH_GROUPED force a path (decode takes at most 64
  * tokens).  The workspace depends on the path (gale_moe_workspace_bytes with the same
- * flags). */
+ * flags).  hidden <= GALE_MAX_HIDDEN (else GALE_ERR_SHAPE); the single-launch layer
+ * takes hidden <= 4096 with inter dividing 2 hidden in whole 1024-column blocks, other
+ * shapes run the five-launch sequence. */
 int gale_moe_layer_fwd(int32_t hidden, int32_t inter, const gale_expert* experts_dev,
                        int32_t n_experts, const float* logits, int32_t top_k, const void* x,
                        int32_t n_tok, void* y, int32_t* topk_idx, float* topk_w,

@@ -401,6 +401,10 @@ extern "C" int gale_expert_ffn(int32_t hidden, int32_t inter, const gale_expert*
   if (st) return st;
   st = check_matrix_shape(fn, hidden, inter);
   if (st) return st;
+  if (hidden > GALE_MAX_HIDDEN) {
+    set_error("%s: hidden=%d above %d", fn, hidden, GALE_MAX_HIDDEN);
+    return GALE_ERR_SHAPE;
+  }
   if (n_exp < 1 || n_tok < 1) { set_error("%s: n_exp=%d n_tok=%d must be >= 1", fn, n_exp, n_tok); return GALE_ERR_SHAPE; }
   if (!experts_dev || !x || !y || !ws) { set_error("%s: NULL pointer", fn); return GALE_ERR_NULL; }
   if (!aligned(x, 16) || !aligned(ws, 256) || !aligned(y, 2)) { set_error("%s: misaligned pointer", fn); return GALE_ERR_ALIGN; }
@@ -444,6 +448,10 @@ extern "C" int gale_moe_layer_fwd(int32_t hidden, int32_t inter, const gale_expe
   if (st) return st;
   st = check_matrix_shape(fn, hidden, inter);
   if (st) return st;
+  if (hidden > GALE_MAX_HIDDEN) {
+    set_error("%s: hidden=%d above %d", fn, hidden, GALE_MAX_HIDDEN);
+    return GALE_ERR_SHAPE;
+  }
   if (n_experts < 1 || n_experts > GALE_MAX_EXPERTS || top_k < 1 || top_k > GALE_MAX_TOPK || top_k > n_experts) {
     set_error("%s: n_experts=%d top_k=%d out of range", fn, n_experts, top_k);
     return GALE_ERR_SHAPE;

@@ -377,11 +377,19 @@ __device__ __forceinline__ void outlier_pass(const LayerParams& L, const PhaseGe
     o = fmaf(q, xt[col], o);
   }
   if (p < p_end) {
+    // eight entries of the lane per step, all loads issued before the first use
     const LayerDesc dm = layer_desc(L.table, G, uni(s_exp[role_pair]));
-    for (; p < p_end; p += 4) {
-      const int col = reinterpret_cast<const uint16_t*>(dm.ocols)[p];
-      const float q = (float)outlier_value(reinterpret_cast<const uint8_t*>(dm.ovals), p);
-      o = fmaf(q, xt[col], o);
+    for (; p < p_end; p += 32) {
+      int col[8];
+      float q[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int pj = min(p + 4 * j, p_end - 1);
+        col[j] = reinterpret_cast<const uint16_t*>(dm.ocols)[pj];
+        q[j] = p + 4 * j < p_end ? (float)outlier_value(reinterpret_cast<const uint8_t*>(dm.ovals), pj) : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o = fmaf(q[j], xt[col[j]], o);
     }
   }
   const float rscale = half_bits_to_float(cur.rsc);

@@ -368,16 +368,28 @@ __device__ __forceinline__ void process_unit(const GemvParams& P, const Geo& G, 
         }
       }
     }
-    // rows whose entries run past the staged chunks: the rest straight from memory
-    for (; p < p_end; p += 4) {
+    // rows whose entries run past the staged chunks (more than 64 per row on average over
+    // the wave's 16 rows): the rest straight from memory, eight entries of the lane per
+    // step with all their loads issued before the first use
+    if (p < p_end) {
       const gale_matrix* Mo = P.table + it.mat * P.mat_stride + (G.ohalf ? P.sel1 : P.sel0);
-      const int col = Mo->out_cols[p];
-      const float q = (float)outlier_value(Mo->out_vals, p);
+      for (; p < p_end; p += 32) {
+        int col[8];
+        float q[8];
 #pragma unroll
-      for (int i = 0; i < NS; ++i) {
-        if (i < it.nslots) {
-          const int ra = sel4(i, it.ra0, it.ra1, it.ra2, it.ra3);
-          o[i] = fmaf(q, reinterpret_cast<const float*>(P.ra + (size_t)ra * P.ra_stride)[col], o[i]);
+        for (int j = 0; j < 8; ++j) {
+          const int pj = min(p + 4 * j, p_end - 1);
+          col[j] = Mo->out_cols[pj];
+          q[j] = p + 4 * j < p_end ? (float)outlier_value(Mo->out_vals, pj) : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+          if (i < it.nslots) {
+            const int ra = sel4(i, it.ra0, it.ra1, it.ra2, it.ra3);
+            const float* xg = reinterpret_cast<const float*>(P.ra + (size_t)ra * P.ra_stride);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) o[i] = fmaf(q[j], P.stage_xt ? xt[i * G.K + col[j]] : xg[col[j]], o[i]);
+          }
         }
       }
     }
@@ -417,9 +429,10 @@ __device__ __forceinline__ void process_unit(const GemvParams& P, const Geo& G, 
 }
 
 // NS: activation vectors per item (1, 2 or 4); R: row tiles per unit (R <= chunks);
-// GATEUP: two matrices (w1, w3) and a SwiGLU epilogue.  blockDim.x = 64 * C * (GATEUP ? 2 : 1).
-template <int NS, int R, bool GATEUP>
-__global__ void __launch_bounds__(512) gemv_kernel(const GemvParams P) {
+// GATEUP: two matrices (w1, w3) and a SwiGLU epilogue.  blockDim.x = 64 * C * (GATEUP ? 2 : 1)
+// <= MAXT: 512 for up to eight wavefronts, 1024 (half the registers per lane) beyond.
+template <int NS, int R, bool GATEUP, int MAXT>
+__global__ void __launch_bounds__(MAXT) gemv_kernel(const GemvParams P) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int HALVES = GATEUP ? 2 : 1;
   constexpr int RR = R * 16;
@@ -533,18 +546,25 @@ int device_cu_count() {
   return cached[dev];
 }
 
-template <int NS, int R, bool G>
-static hipError_t launch_t(const GemvParams& p, int64_t max_units, hipStream_t s) {
-  const int C = p.cols >> 10;
-  const int block = 64 * C * (G ? 2 : 1);
+template <int NS, int R, bool G, int MAXT>
+static hipError_t launch_b(const GemvParams& p, int block, int64_t max_units, hipStream_t s) {
   const size_t smem = gemv_smem_bytes(p.cols, NS, R, G, p.stage_xt);
   int occ = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemv_kernel<NS, R, G>, block, smem) != hipSuccess || occ < 1)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemv_kernel<NS, R, G, MAXT>, block, smem) != hipSuccess ||
+      occ < 1)
     occ = 1;
   const int64_t grid = std::min<int64_t>(max_units, (int64_t)device_cu_count() * occ);
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemv_kernel<NS, R, G>), dim3((unsigned)grid), dim3(block), smem, s, p);
+  hipLaunchKernelGGL((gemv_kernel<NS, R, G, MAXT>), dim3((unsigned)grid), dim3(block), smem, s, p);
   return hipGetLastError();
+}
+
+template <int NS, int R, bool G>
+static hipError_t launch_t(const GemvParams& p, int64_t max_units, hipStream_t s) {
+  const int block = 64 * (p.cols >> 10) * (G ? 2 : 1);
+  if (block > kGemvMaxThreads) return hipErrorInvalidConfiguration;   // the host checks first
+  if (block <= 512) return launch_b<NS, R, G, 512>(p, block, max_units, s);
+  return launch_b<NS, R, G, 1024>(p, block, max_units, s);
 }
 
 template <int NS, bool G>

@@ -105,6 +105,8 @@ hipError_t launch_fwht(const void* x, void* y, int64_t n_vec, int len, int in_dt
                        hipStream_t s);
 // max_units: upper bound of the number of units (items x row groups); the launch is a
 // persistent grid of at most that many workgroups.
+// threads of a GEMV workgroup: 64 per 1024-column chunk of each matrix
+constexpr int kGemvMaxThreads = 1024;
 hipError_t launch_gemv(const GemvParams& p, int slots, int tiles_per_unit, int64_t max_units, hipStream_t s);
 size_t gemv_smem_bytes(int cols, int slots, int tiles, int gateup, int stage_xt);
 int device_cu_count();
