@@ -258,6 +258,26 @@ int gale_moe_layer_fwd(int32_t hidden, int32_t inter, const gale_expert* experts
                        int32_t n_tok, void* y, int32_t* topk_idx, float* topk_w,
                        void* ws, size_t ws_bytes, uint32_t flags, hipStream_t stream);
 
+/* The same layer with two of DeepSeek's routing variants:
+ *   select_bias (fp32 [n_experts], or NULL): a per-expert term added to the logits for the
+ *          choice of the top_k experts only; the weights stay the softmax of the chosen
+ *          experts' own logits (the aux-loss-free balancing bias, DeepSeek-V4-Pro GALE page,
+ *          serving notes on the tier bias).  The choice compares fp32 sums logit + bias,
+ *          ties to the lower expert index.
+ *   fixed_idx (int32 [n_tok][top_k], or NULL): the experts of each token are given, in slot
+ *          order (hash-routed layers that read a token-to-expert table, DeepSeek-V4-Flash
+ *          180B REAP card); the weights are again the softmax of those experts' logits.
+ *          Entries must be distinct experts in [0, n_experts); an entry outside that range
+ *          is clamped into it (memory-safe, result unspecified).
+ * At most one of the two may be given (GALE_ERR_SHAPE otherwise); with neither, the call is
+ * gale_moe_layer_fwd.  Both pointers are device memory, 4-byte aligned.  Same workspace,
+ * paths and flags as gale_moe_layer_fwd. */
+int gale_moe_layer_fwd_routed(int32_t hidden, int32_t inter, const gale_expert* experts_dev,
+                              int32_t n_experts, const float* logits, const float* select_bias,
+                              const int32_t* fixed_idx, int32_t top_k, const void* x, int32_t n_tok,
+                              void* y, int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
+                              uint32_t flags, hipStream_t stream);
+
 /* Workspace bytes for gale_route_topk with grouping of more than GALE_MAX_DECODE_TOKENS tokens. */
 size_t gale_route_workspace_bytes(int32_t n_tok, int32_t n_experts);
 

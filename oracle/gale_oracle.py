@@ -21,6 +21,11 @@ Sources (cited by page title and section):
            DSV4_DIRECT_GEMV / DSV4_FWHT: a GEMV straight out of the packed record
            (signs, block scales, int4 outliers decoded in registers) and a
            single-kernel Walsh-Hadamard transform exact to 1e-8 of the matmul form.
+           Same page, serving notes on the tier bias: a per-expert selection bias
+           (DeepSeek's aux-loss-free balancing term) changes which experts are chosen,
+           never the routing weights.
+  [REAP]   DeepSeek-V4-Flash 180B REAP W4A16 card, lineage notes: layers 0-2 route
+           by hash, reading the experts of each token from a token-to-expert table.
 
 Readings taken where the pages are silent (each also listed in the design notes):
   * H is the Sylvester-ordered Walsh-Hadamard matrix normalised by 1/sqrt(1024)
@@ -32,6 +37,9 @@ Readings taken where the pages are silent (each also listed in the design notes)
   * FFN: h = silu(w1 x~) * (w3 x~), y = w2 . (blockdiag(H) . h), silu(a) = a / (1 + e^-a).
   * Routing: top-k by (logit descending, expert index ascending); weights are the
     softmax of the k selected logits.
+  * Selection bias: added to the fp32 logits (an fp32 sum) for the ordering only.
+  * Hash routing: the pages give the token-to-expert table but not the weights; they
+    are taken as the softmax of the given experts' logits, as on the other layers.
 """
 from __future__ import annotations
 
@@ -159,19 +167,31 @@ def ffn(w1: Dict, w3: Dict, w2: Dict, x: np.ndarray) -> np.ndarray:
 # --------------------------------------------------------------------------
 # O6, O7: routing and combine
 # --------------------------------------------------------------------------
-def route(logits: np.ndarray, k: int) -> Tuple[np.ndarray, np.ndarray]:
+def route(logits: np.ndarray, k: int, select_bias: Optional[np.ndarray] = None,
+          fixed_idx: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
     """Top-k experts per token ordered by (logit desc, index asc); softmax over the k chosen logits.
 
     logits: fp32 [T, E].  Returns idx int64 [T, k] and weights fp64 [T, k].
+
+    Routing variants ([Pro] serving notes on the tier bias; [REAP] hash-routed layers):
+      select_bias fp32 [E]: DeepSeek's balancing term, added to the logits for the choice of
+        the k experts only -- the order is taken on the fp32 sums logit + bias (same ties
+        rule) and the weights remain the softmax of the chosen experts' own logits.
+      fixed_idx [T, k]: the experts come from a token-to-expert table (hash routing), in slot
+        order; the weights are the softmax of those experts' logits.
     """
     lg = np.asarray(logits, dtype=np.float32)
     T, E = lg.shape
     idx = np.empty((T, k), dtype=np.int64)
     w = np.empty((T, k), dtype=np.float64)
     ar = np.arange(E)
+    score = lg if select_bias is None else lg + np.asarray(select_bias, dtype=np.float32)[None, :]   # fp32 sums
     for t in range(T):
-        order = np.lexsort((ar, -lg[t].astype(np.float64)))   # primary: -logit, secondary: index
-        sel = order[:k]
+        if fixed_idx is not None:
+            sel = np.asarray(fixed_idx[t], dtype=np.int64)
+        else:
+            order = np.lexsort((ar, -score[t].astype(np.float64)))   # primary: -score, secondary: index
+            sel = order[:k]
         idx[t] = sel
         v = lg[t, sel].astype(np.float64)
         e = np.exp(v - v.max())
@@ -179,14 +199,16 @@ def route(logits: np.ndarray, k: int) -> Tuple[np.ndarray, np.ndarray]:
     return idx, w
 
 
-def moe(expert_of, logits: np.ndarray, x: np.ndarray, k: int = 6):
+def moe(expert_of, logits: np.ndarray, x: np.ndarray, k: int = 6, select_bias: Optional[np.ndarray] = None,
+        fixed_idx: Optional[np.ndarray] = None):
     """y_t = sum over the k routed experts e of w[t, e] * FFN_e(x_t).
 
     ``expert_of(e)`` returns the canonical (w1, w3, w2) of expert e.  Returns
-    (y fp64 [T, hidden], idx, weights).
+    (y fp64 [T, hidden], idx, weights).  select_bias / fixed_idx: the routing variants of
+    ``route``.
     """
     x = np.atleast_2d(np.asarray(x).astype(np.float64))
-    idx, w = route(logits, k)
+    idx, w = route(logits, k, select_bias, fixed_idx)
     y = np.zeros_like(x)
     for e in np.unique(idx):
         toks = np.nonzero((idx == e).any(axis=1))[0]

@@ -82,6 +82,8 @@ _SIGS = {
     "gale_expert_ffn": (_I32, [_I32, _I32, _P, _I32, _P, _I32, _I32, _P, _P, _SZ, _P]),
     "gale_moe_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _U32]),
     "gale_moe_layer_fwd": (_I32, [_I32, _I32, _P, _I32, _P, _I32, _P, _I32, _P, _P, _P, _P, _SZ, _U32, _P]),
+    "gale_moe_layer_fwd_routed": (_I32, [_I32, _I32, _P, _I32, _P, _P, _P, _I32, _P, _I32, _P, _P, _P, _P, _SZ, _U32,
+                                         _P]),
     "gale_route_workspace_bytes": (_SZ, [_I32, _I32]),
     "gale_route_topk": (_I32, [_P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
 }
@@ -384,7 +386,10 @@ def moe_workspace_bytes(n_tok, n_experts, top_k, hidden, inter, flags=0) -> int:
 def moe_layer_fwd(table: DescriptorTable, hidden: int, inter: int, logits: torch.Tensor, x: torch.Tensor,
                   top_k: int = 6, flags: int = 0, y: Optional[torch.Tensor] = None,
                   topk_idx: Optional[torch.Tensor] = None, topk_w: Optional[torch.Tensor] = None,
-                  ws: Optional[torch.Tensor] = None):
+                  ws: Optional[torch.Tensor] = None, select_bias: Optional[torch.Tensor] = None,
+                  fixed_idx: Optional[torch.Tensor] = None):
+    """One routed-expert layer; select_bias (fp32 [E]) or fixed_idx (int32 [T, top_k]) select the
+    routing variants of gale_moe_layer_fwd_routed."""
     _require_cuda(x, logits)
     n_tok = x.shape[0]
     E = logits.shape[1]
@@ -396,10 +401,24 @@ def moe_layer_fwd(table: DescriptorTable, hidden: int, inter: int, logits: torch
         topk_w = torch.empty(n_tok, top_k, dtype=torch.float32, device=x.device)
     if ws is None:
         ws = _workspace(moe_workspace_bytes(n_tok, E, top_k, hidden, inter, flags), x.device)
-    _check("gale_moe_layer_fwd", lib().gale_moe_layer_fwd(hidden, inter, table.ptr(), E, logits.data_ptr(), top_k,
-                                                           x.data_ptr(), n_tok, y.data_ptr(), topk_idx.data_ptr(),
-                                                           topk_w.data_ptr(), ws.data_ptr(), ws.numel(), flags,
-                                                           _stream()))
+    if select_bias is None and fixed_idx is None:
+        _check("gale_moe_layer_fwd", lib().gale_moe_layer_fwd(hidden, inter, table.ptr(), E, logits.data_ptr(), top_k,
+                                                               x.data_ptr(), n_tok, y.data_ptr(), topk_idx.data_ptr(),
+                                                               topk_w.data_ptr(), ws.data_ptr(), ws.numel(), flags,
+                                                               _stream()))
+        return y, topk_idx, topk_w
+    if select_bias is not None:
+        _require_cuda(select_bias)
+        if select_bias.dtype != torch.float32 or select_bias.numel() != E or not select_bias.is_contiguous():
+            raise ValueError("select_bias must be a contiguous fp32 tensor of n_experts entries")
+    if fixed_idx is not None:
+        _require_cuda(fixed_idx)
+        if fixed_idx.dtype != torch.int32 or tuple(fixed_idx.shape) != (n_tok, top_k) or not fixed_idx.is_contiguous():
+            raise ValueError("fixed_idx must be a contiguous int32 tensor [n_tok, top_k]")
+    _check("gale_moe_layer_fwd_routed", lib().gale_moe_layer_fwd_routed(
+        hidden, inter, table.ptr(), E, logits.data_ptr(), None if select_bias is None else select_bias.data_ptr(),
+        None if fixed_idx is None else fixed_idx.data_ptr(), top_k, x.data_ptr(), n_tok, y.data_ptr(),
+        topk_idx.data_ptr(), topk_w.data_ptr(), ws.data_ptr(), ws.numel(), flags, _stream()))
     return y, topk_idx, topk_w
 
 

@@ -439,11 +439,10 @@ extern "C" size_t gale_moe_workspace_bytes(int32_t n_tok, int32_t n_experts, int
   return moe_ws(n_tok, n_experts, top_k, hidden, inter, moe_path(n_tok, flags)).total;
 }
 
-extern "C" int gale_moe_layer_fwd(int32_t hidden, int32_t inter, const gale_expert* experts_dev,
-                                  int32_t n_experts, const float* logits, int32_t top_k, const void* x,
-                                  int32_t n_tok, void* y, int32_t* topk_idx, float* topk_w, void* ws,
-                                  size_t ws_bytes, uint32_t flags, hipStream_t stream) {
-  const char* fn = "gale_moe_layer_fwd";
+static int moe_layer(const char* fn, int32_t hidden, int32_t inter, const gale_expert* experts_dev,
+                     int32_t n_experts, const float* logits, const float* select_bias, const int32_t* fixed_idx,
+                     int32_t top_k, const void* x, int32_t n_tok, void* y, int32_t* topk_idx, float* topk_w,
+                     void* ws, size_t ws_bytes, uint32_t flags, hipStream_t stream) {
   int st = check_matrix_shape(fn, inter, hidden);
   if (st) return st;
   st = check_matrix_shape(fn, hidden, inter);
@@ -458,10 +457,13 @@ extern "C" int gale_moe_layer_fwd(int32_t hidden, int32_t inter, const gale_expe
   }
   if (n_tok < 1) { set_error("%s: n_tok=%d", fn, n_tok); return GALE_ERR_SHAPE; }
   if (!experts_dev || !logits || !x || !y || !ws) { set_error("%s: NULL pointer", fn); return GALE_ERR_NULL; }
-  if (!aligned(x, 16) || !aligned(ws, 256) || !aligned(y, 2) || !aligned(logits, 4)) {
+  if (!aligned(x, 16) || !aligned(ws, 256) || !aligned(y, 2) || !aligned(logits, 4) || !aligned(select_bias, 4) ||
+      !aligned(fixed_idx, 4)) {
     set_error("%s: misaligned pointer", fn);
     return GALE_ERR_ALIGN;
   }
+  if (select_bias && fixed_idx) { set_error("%s: a selection bias and fixed experts exclude each other", fn); return GALE_ERR_SHAPE; }
+  const RouteIn rin = {logits, select_bias, fixed_idx};
   if ((flags & GALE_PATH_DECODE) && (flags & GALE_PATH_GROUPED)) { set_error("%s: both paths forced", fn); return GALE_ERR_SHAPE; }
   const MoePath path = moe_path(n_tok, flags);
   if (path == kDecode && n_tok > GALE_MAX_DECODE_TOKENS) {
@@ -483,7 +485,7 @@ extern "C" int gale_moe_layer_fwd(int32_t hidden, int32_t inter, const gale_expe
   const gale_matrix* table = reinterpret_cast<const gale_matrix*>(experts_dev);
   if (path != kDecode) {
     // chunked top-k and a stable sort of the pairs by expert
-    st = hip_status(fn, launch_route_large(logits, n_tok, n_experts, top_k, idx, wts,
+    st = hip_status(fn, launch_route_large(rin, n_tok, n_experts, top_k, idx, wts,
                                            reinterpret_cast<int32_t*>(base + W.chunk), offsets, perm, stream));
     if (st) return st;
   }
@@ -504,12 +506,12 @@ extern "C" int gale_moe_layer_fwd(int32_t hidden, int32_t inter, const gale_expe
     // tiles per unit of (gate/up, down), as decimal digits; see GALE_TILES_SHIFT
     static const int kLayerTiles[7] = {kDecodeLayerTiles, 11, 22, 12, 21, 32, 31};
     const int forced = (int)((flags >> GALE_TILES_SHIFT) & 0xF);
-    return hip_status(fn, launch_decode_layer(table, n_experts, logits, top_k, x, hidden, inter, y, topk_idx, topk_w,
+    return hip_status(fn, launch_decode_layer(table, n_experts, rin, top_k, x, hidden, inter, y, topk_idx, topk_w,
                                               h, yp, reinterpret_cast<uint64_t*>(base + W.sync),
                                               kLayerTiles[forced <= 6 ? forced : 0], stream));
   }
   if (path == kDecode) {
-    st = hip_status(fn, launch_route_prep(logits, n_tok, n_experts, top_k, idx, wts, items, n_items, slots, x,
+    st = hip_status(fn, launch_route_prep(rin, n_tok, n_experts, top_k, idx, wts, items, n_items, slots, x,
                                           GALE_F16, hidden, ra_x, ra_bytes(hidden), stream));
     if (st) return st;
   } else {
@@ -556,6 +558,23 @@ extern "C" int gale_moe_layer_fwd(int32_t hidden, int32_t inter, const gale_expe
   return hip_status(fn, launch_combine(yp, wts, n_tok, top_k, hidden, y, GALE_F16, stream));
 }
 
+extern "C" int gale_moe_layer_fwd(int32_t hidden, int32_t inter, const gale_expert* experts_dev,
+                                  int32_t n_experts, const float* logits, int32_t top_k, const void* x,
+                                  int32_t n_tok, void* y, int32_t* topk_idx, float* topk_w, void* ws,
+                                  size_t ws_bytes, uint32_t flags, hipStream_t stream) {
+  return moe_layer("gale_moe_layer_fwd", hidden, inter, experts_dev, n_experts, logits, nullptr, nullptr, top_k, x,
+                   n_tok, y, topk_idx, topk_w, ws, ws_bytes, flags, stream);
+}
+
+extern "C" int gale_moe_layer_fwd_routed(int32_t hidden, int32_t inter, const gale_expert* experts_dev,
+                                         int32_t n_experts, const float* logits, const float* select_bias,
+                                         const int32_t* fixed_idx, int32_t top_k, const void* x, int32_t n_tok,
+                                         void* y, int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
+                                         uint32_t flags, hipStream_t stream) {
+  return moe_layer("gale_moe_layer_fwd_routed", hidden, inter, experts_dev, n_experts, logits, select_bias, fixed_idx,
+                   top_k, x, n_tok, y, topk_idx, topk_w, ws, ws_bytes, flags, stream);
+}
+
 extern "C" size_t gale_route_workspace_bytes(int32_t n_tok, int32_t n_experts) {
   if (n_tok < 1 || n_experts < 1) return 0;
   return align256(route_chunk_count_bytes(n_tok, n_experts));
@@ -576,13 +595,13 @@ extern "C" int gale_route_topk(const float* logits, int32_t n_tok, int32_t n_exp
   if (offsets && n_tok > GALE_MAX_DECODE_TOKENS) {
     const size_t need = gale_route_workspace_bytes(n_tok, n_experts);
     if (!ws || ws_bytes < need) { set_error("%s: workspace %zu < %zu bytes", fn, ws_bytes, need); return GALE_ERR_WORKSPACE; }
-    return hip_status(fn, launch_route_large(logits, n_tok, n_experts, top_k, topk_idx, topk_w,
-                                             reinterpret_cast<int32_t*>(ws), offsets, perm, stream));
+    return hip_status(fn, launch_route_large(RouteIn{logits, nullptr, nullptr}, n_tok, n_experts, top_k, topk_idx,
+                                             topk_w, reinterpret_cast<int32_t*>(ws), offsets, perm, stream));
   }
   if (n_tok <= GALE_MAX_DECODE_TOKENS)
-    return hip_status(fn, launch_route_small(logits, n_tok, n_experts, top_k, topk_idx, topk_w, offsets, perm,
-                                             nullptr, nullptr, 1, stream));
+    return hip_status(fn, launch_route_small(RouteIn{logits, nullptr, nullptr}, n_tok, n_experts, top_k, topk_idx,
+                                             topk_w, offsets, perm, nullptr, nullptr, 1, stream));
   // top-k only, any number of tokens: the chunked kernel without grouping
-  return hip_status(fn, launch_route_large(logits, n_tok, n_experts, top_k, topk_idx, topk_w, nullptr, nullptr,
-                                           nullptr, stream));
+  return hip_status(fn, launch_route_large(RouteIn{logits, nullptr, nullptr}, n_tok, n_experts, top_k, topk_idx,
+                                           topk_w, nullptr, nullptr, nullptr, stream));
 }

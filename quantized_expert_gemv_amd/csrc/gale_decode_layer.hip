@@ -299,6 +299,8 @@ __device__ __forceinline__ void prep_block_to_lds(const float* hv, int K, int c,
 struct LayerParams {
   const gale_matrix* table;  // [E][3]: w1, w3, w2
   const float* logits;       // [E]
+  const float* bias;         // [E] selection bias, or NULL
+  const int32_t* fixed;      // [k] given experts, or NULL
   const void* x;             // fp16 [H]
   __half* y;                 // fp16 [H]
   int32_t* topk_idx;         // [k] or NULL
@@ -712,7 +714,7 @@ __global__ void __launch_bounds__(512) decode_layer_kernel(const LayerParams L) 
   const int C_H = L.H >> 10;
   const int W = (int)(blockDim.x >> 6);
   if (wave == 0) {
-    topk_wave(L.logits, L.E, L.k, lane, s_exp, s_w, s_exp);
+    topk_wave(RouteIn{L.logits, L.bias, L.fixed}, 0, L.E, L.k, lane, s_exp, s_w, s_exp);
   } else if (wave <= C_H) {
     prep_wave(L.x, GALE_F16, L.H, 1, L.H, 0, rec, ra_bytes(L.H), wave - 1);
   }
@@ -816,12 +818,14 @@ static hipError_t launch_layer_r(LayerParams L, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_decode_layer(const gale_matrix* table, int E, const float* logits, int k, const void* x,
+hipError_t launch_decode_layer(const gale_matrix* table, int E, const RouteIn& rin, int k, const void* x,
                                int hidden, int inter, void* y, int32_t* topk_idx, float* topk_w, float* h,
                                float* yp, uint64_t* sync, int tiles, hipStream_t s) {
   LayerParams L;
   L.table = table;
-  L.logits = logits;
+  L.logits = rin.logits;
+  L.bias = rin.bias;
+  L.fixed = rin.fixed;
   L.x = x;
   L.y = reinterpret_cast<__half*>(y);
   L.topk_idx = topk_idx;

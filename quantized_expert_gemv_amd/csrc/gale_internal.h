@@ -117,13 +117,24 @@ hipError_t launch_debug_outliers(int rows, int64_t nnz, gale_matrix m, int32_t* 
                                  int32_t* v, hipStream_t s);
 
 // routing
-hipError_t launch_route_small(const float* logits, int n_tok, int n_exp, int k, int32_t* idx, float* w,
+// Routing inputs of a batch: logits [T][E]; an optional selection bias [E], added to the
+// logits for the choice of the k experts only (the balancing term of the DeepSeek-V4-Pro
+// GALE page's serving notes, which never enters the weights); optional fixed experts [T][k]
+// (hash-routed layers, DeepSeek-V4-Flash 180B REAP card: the experts come from a table, in
+// slot order).  The k weights are always the softmax of the chosen experts' own logits.
+struct RouteIn {
+  const float* logits;
+  const float* bias;      // NULL: none
+  const int32_t* fixed;   // NULL: top-k
+};
+
+hipError_t launch_route_small(const RouteIn& rin, int n_tok, int n_exp, int k, int32_t* idx, float* w,
                               int32_t* offsets, int32_t* perm, WorkItem* items, int32_t* n_items,
                               int max_slots, hipStream_t s);
-hipError_t launch_route_prep(const float* logits, int n_tok, int n_exp, int k, int32_t* idx, float* w,
+hipError_t launch_route_prep(const RouteIn& rin, int n_tok, int n_exp, int k, int32_t* idx, float* w,
                              WorkItem* items, int32_t* n_items, int max_slots, const void* x, int x_dtype, int K,
                              uint8_t* ra, size_t ra_stride, hipStream_t s);
-hipError_t launch_route_large(const float* logits, int n_tok, int n_exp, int k, int32_t* idx, float* w,
+hipError_t launch_route_large(const RouteIn& rin, int n_tok, int n_exp, int k, int32_t* idx, float* w,
                               int32_t* chunk_cnt, int32_t* offsets, int32_t* perm, hipStream_t s);
 inline size_t route_chunk_count_bytes(int n_tok, int n_exp) {
   return (size_t)4 * ((n_tok + 63) / 64) * n_exp;
@@ -154,7 +165,7 @@ hipError_t launch_grouped_gemm(const gale_matrix* table, int gateup, int rows, i
 // down, combine); sync: decode_layer_sync_bytes(hidden, inter) bytes of counters
 bool decode_layer_supported(int hidden, int inter);
 size_t decode_layer_sync_bytes(int hidden, int inter);
-hipError_t launch_decode_layer(const gale_matrix* table, int E, const float* logits, int k, const void* x,
+hipError_t launch_decode_layer(const gale_matrix* table, int E, const RouteIn& rin, int k, const void* x,
                                int hidden, int inter, void* y, int32_t* topk_idx, float* topk_w, float* h,
                                float* yp, uint64_t* sync, int tiles, hipStream_t s);
 

@@ -38,7 +38,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* s_wave, int* tot
 // Decode routing: one workgroup does top-k for every token, the counting sort
 // and the work-item list (n_tok * k <= 512 pairs).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void route_small_body(const float* __restrict__ logits, int T, int E, int k,
+__device__ __forceinline__ void route_small_body(const RouteIn& rin, int T, int E, int k,
                                                  int max_slots, int32_t* __restrict__ idx, float* __restrict__ w,
                                                  int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
                                                  WorkItem* __restrict__ items, int32_t* __restrict__ n_items) {
@@ -51,7 +51,7 @@ __device__ __forceinline__ void route_small_body(const float* __restrict__ logit
   const int nw = blockDim.x >> 6;
   for (int e = tid; e < E; e += blockDim.x) s_cnt[e] = 0;
   for (int t = wave; t < T; t += nw)
-    topk_wave(logits + (int64_t)t * E, E, k, lane, idx + t * k, w + t * k, s_idx + t * k);
+    topk_wave(rin, t, E, k, lane, idx + t * k, w + t * k, s_idx + t * k);
   const int P = T * k;
   __syncthreads();
   // per-expert counts (integer atomics: order-free)
@@ -111,36 +111,36 @@ __device__ __forceinline__ void route_small_body(const float* __restrict__ logit
   }
 }
 
-__global__ void __launch_bounds__(512) route_small_kernel(const float* __restrict__ logits, int T, int E,
+__global__ void __launch_bounds__(512) route_small_kernel(const RouteIn rin, int T, int E,
                                                           int k, int max_slots, int32_t* __restrict__ idx,
                                                           float* __restrict__ w, int32_t* __restrict__ offsets,
                                                           int32_t* __restrict__ perm, WorkItem* __restrict__ items,
                                                           int32_t* __restrict__ n_items) {
-  route_small_body(logits, T, E, k, max_slots, idx, w, offsets, perm, items, n_items);
+  route_small_body(rin, T, E, k, max_slots, idx, w, offsets, perm, items, n_items);
 }
 
 // Decode routing and the activation record of the layer input in one launch: the
 // two are independent, so workgroup 0 routes while the others prepare x.
-__global__ void __launch_bounds__(512) route_prep_kernel(const float* __restrict__ logits, int T, int E, int k,
+__global__ void __launch_bounds__(512) route_prep_kernel(const RouteIn rin, int T, int E, int k,
                                                          int max_slots, int32_t* __restrict__ idx,
                                                          float* __restrict__ w, WorkItem* __restrict__ items,
                                                          int32_t* __restrict__ n_items, const void* __restrict__ x,
                                                          int x_dtype, int K, uint8_t* __restrict__ ra,
                                                          size_t ra_stride) {
   if (blockIdx.x == 0) {
-    route_small_body(logits, T, E, k, max_slots, idx, w, nullptr, nullptr, items, n_items);
+    route_small_body(rin, T, E, k, max_slots, idx, w, nullptr, nullptr, items, n_items);
   } else {
     prep_wave(x, x_dtype, K, T, K, 0, ra, ra_stride,
               (int64_t)(blockIdx.x - 1) * (blockDim.x >> 6) + (threadIdx.x >> 6));
   }
 }
 
-hipError_t launch_route_prep(const float* logits, int n_tok, int n_exp, int k, int32_t* idx, float* w,
+hipError_t launch_route_prep(const RouteIn& rin, int n_tok, int n_exp, int k, int32_t* idx, float* w,
                              WorkItem* items, int32_t* n_items, int max_slots, const void* x, int x_dtype, int K,
                              uint8_t* ra, size_t ra_stride, hipStream_t s) {
   const int64_t waves = (int64_t)n_tok * (K / 1024);
   const int64_t grid = 1 + (waves + 7) / 8;
-  hipLaunchKernelGGL(route_prep_kernel, dim3((unsigned)grid), dim3(512), 0, s, logits, n_tok, n_exp, k, max_slots,
+  hipLaunchKernelGGL(route_prep_kernel, dim3((unsigned)grid), dim3(512), 0, s, rin, n_tok, n_exp, k, max_slots,
                      idx, w, items, n_items, x, x_dtype, K, ra, ra_stride);
   return hipGetLastError();
 }
@@ -153,7 +153,7 @@ hipError_t launch_route_prep(const float* logits, int n_tok, int n_exp, int k, i
 // ---------------------------------------------------------------------------
 constexpr int kRouteChunk = 64;
 
-__global__ void __launch_bounds__(1024) route_topk_count_kernel(const float* __restrict__ logits, int T, int E,
+__global__ void __launch_bounds__(1024) route_topk_count_kernel(const RouteIn rin, int T, int E,
                                                                int k, int32_t* __restrict__ idx,
                                                                float* __restrict__ w,
                                                                int32_t* __restrict__ chunk_cnt) {
@@ -165,7 +165,7 @@ __global__ void __launch_bounds__(1024) route_topk_count_kernel(const float* __r
   const int t1 = min(T, t0 + kRouteChunk);
   for (int e = tid; e < E; e += blockDim.x) s_cnt[e] = 0;
   for (int t = t0 + wave; t < t1; t += (int)(blockDim.x >> 6))
-    topk_wave(logits + (int64_t)t * E, E, k, lane, idx + (int64_t)t * k, w + (int64_t)t * k,
+    topk_wave(rin, t, E, k, lane, idx + (int64_t)t * k, w + (int64_t)t * k,
               s_idx + (t - t0) * k);
   __syncthreads();
   for (int p = tid; p < (t1 - t0) * k; p += blockDim.x) atomicAdd(&s_cnt[s_idx[p]], 1);
@@ -212,18 +212,18 @@ __global__ void __launch_bounds__(256) route_scatter_kernel(int T, int E, int k,
   }
 }
 
-hipError_t launch_route_small(const float* logits, int n_tok, int n_exp, int k, int32_t* idx, float* w,
+hipError_t launch_route_small(const RouteIn& rin, int n_tok, int n_exp, int k, int32_t* idx, float* w,
                               int32_t* offsets, int32_t* perm, WorkItem* items, int32_t* n_items,
                               int max_slots, hipStream_t s) {
-  hipLaunchKernelGGL(route_small_kernel, dim3(1), dim3(512), 0, s, logits, n_tok, n_exp, k, max_slots, idx, w,
+  hipLaunchKernelGGL(route_small_kernel, dim3(1), dim3(512), 0, s, rin, n_tok, n_exp, k, max_slots, idx, w,
                      offsets, perm, items, n_items);
   return hipGetLastError();
 }
 
-hipError_t launch_route_large(const float* logits, int n_tok, int n_exp, int k, int32_t* idx, float* w,
+hipError_t launch_route_large(const RouteIn& rin, int n_tok, int n_exp, int k, int32_t* idx, float* w,
                               int32_t* chunk_cnt, int32_t* offsets, int32_t* perm, hipStream_t s) {
   const int nc = (n_tok + kRouteChunk - 1) / kRouteChunk;
-  hipLaunchKernelGGL(route_topk_count_kernel, dim3(nc), dim3(1024), 0, s, logits, n_tok, n_exp, k, idx, w,
+  hipLaunchKernelGGL(route_topk_count_kernel, dim3(nc), dim3(1024), 0, s, rin, n_tok, n_exp, k, idx, w,
                      chunk_cnt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !chunk_cnt) return e;

@@ -2,8 +2,8 @@
 // the one-launch decode layer.
 //
 // Order rule (needed for exact, checkable routing): experts are ranked by logit
-// descending, ties to the lower expert index; the k weights are the softmax of
-// the k selected logits.
+// (plus the selection bias, when given) descending, ties to the lower expert index;
+// the k weights are the softmax of the k selected experts' own logits.
 #pragma once
 #include "gale_internal.h"
 #include "gale_lanes.h"
@@ -83,12 +83,50 @@ __device__ __forceinline__ void topk_rounds(const float* __restrict__ lg, int E,
   m = key_logit(mk);
 }
 
-__device__ __forceinline__ void topk_wave(const float* __restrict__ lg, int E, int k, int lane, int32_t* out_idx,
-                          float* out_w, int32_t* lds_idx) {
+// Top-k of (logit + bias) for the choice only: keys of the biased values (fp32 sums), the
+// winners' own logits for the weights.
+template <int NJ>
+__device__ __forceinline__ void topk_rounds_biased(const float* __restrict__ lg, const float* __restrict__ bias,
+                                                   int E, int k, int lane, int& my_i) {
+  uint64_t key[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int e = lane + 64 * j;
+    key[j] = e < E ? rank_key(lg[e] + bias[e], e) : 0;
+  }
+  for (int s = 0; s < k; ++s) {
+    uint64_t b = key[0];
+#pragma unroll
+    for (int j = 1; j < NJ; ++j) b = key[j] > b ? key[j] : b;
+    const uint64_t w = wave_best(b);
+    my_i = lane == s ? key_expert(w) : my_i;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) key[j] = key[j] == w ? 0 : key[j];
+  }
+}
+
+__device__ __forceinline__ void topk_wave(const RouteIn& in, int t, int E, int k, int lane, int32_t* out_idx,
+                                          float* out_w, int32_t* lds_idx) {
+  const float* __restrict__ lg = in.logits + (int64_t)t * E;
   float m = 0.f, my_v = 0.f;
   int my_i = 0;
-  if (E <= 256) topk_rounds<4>(lg, E, k, lane, m, my_v, my_i);
-  else topk_rounds<8>(lg, E, k, lane, m, my_v, my_i);
+  if (in.fixed == nullptr && in.bias == nullptr) {
+    if (E <= 256) topk_rounds<4>(lg, E, k, lane, m, my_v, my_i);
+    else topk_rounds<8>(lg, E, k, lane, m, my_v, my_i);
+  } else {
+    if (in.fixed != nullptr) {
+      // given experts (clamped into range, so a bad table cannot reach past the logits)
+      const int e = lane < k ? in.fixed[(int64_t)t * k + lane] : 0;
+      my_i = e < 0 ? 0 : (e >= E ? E - 1 : e);
+    } else if (E <= 256) {
+      topk_rounds_biased<4>(lg, in.bias, E, k, lane, my_i);
+    } else {
+      topk_rounds_biased<8>(lg, in.bias, E, k, lane, my_i);
+    }
+    my_v = lane < k ? lg[my_i] : 0.f;
+    m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_v), 0));
+    for (int s = 1; s < k; ++s) m = fmaxf(m, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_v), s)));
+  }
   // softmax of the k selected logits, one slot per lane, summed in slot order
   const float ex = lane < k ? expf(my_v - m) : 0.f;
   float sum = 0.f;

@@ -325,6 +325,39 @@ def test_moe_decode_layer(q, layer, T):
     assert err <= REL_L2_BAR
 
 
+@pytest.mark.parametrize("variant", ["bias", "fixed"])
+@pytest.mark.parametrize("T,flags", [(1, 0), (5, 0), (1, "staged"), (300, 0)])
+def test_moe_routing_variants(q, layer, variant, T, flags):
+    """Selection bias (moves the choice, not the weights) and fixed experts per token (hash
+    routing) through the one-launch layer (T = 1), the five-launch decode sequence and the
+    grouped path: routing exact against the oracle for every token, outputs on a sample."""
+    seed, canon, tab = layer
+    rng = np.random.default_rng(40 + T)
+    x = gen_x(seed, (4000, T), T, 4096, device=DEV)
+    lg = gen_logits_normal(seed, (4000, T), T, 256, device=DEV)
+    lgn = lg.cpu().numpy()
+    fl = q.GALE_DECODE_STAGED if flags == "staged" else 0
+    if variant == "bias":
+        bias_np = (rng.standard_normal(256) * 0.5).astype(np.float32)
+        kw = {"select_bias": torch.from_numpy(bias_np).to(DEV)}
+        ridx, rw = O.route(lgn, 6, select_bias=bias_np)
+        assert not np.array_equal(ridx, O.route(lgn, 6)[0])          # the bias does move the choice
+    else:
+        fixed_np = np.stack([rng.permutation(256)[:6] for _ in range(T)]).astype(np.int32)
+        kw = {"fixed_idx": torch.from_numpy(fixed_np).to(DEV)}
+        ridx, rw = O.route(lgn, 6, fixed_idx=fixed_np)
+    y, idx, w = q.moe_layer_fwd(tab, 4096, 2048, lg, x, top_k=6, flags=fl, **kw)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert np.abs(w.cpu().numpy() - rw).max() <= 1e-6
+    sample = sorted({0, T - 1})
+    expert_of = lambda e: tuple(m.numpy() for m in canon[e])  # noqa: E731
+    okw = {"select_bias": bias_np} if variant == "bias" else {"fixed_idx": fixed_np[sample]}
+    yref, _, _ = O.moe(expert_of, lgn[sample], x.cpu().numpy()[sample], k=6, **okw)
+    err = O.rel_l2(np_of(y[sample]), yref).max()
+    print(f"routing {variant} T={T} {flags or ''}: rel-L2 {err:.3e}")
+    assert err <= REL_L2_BAR
+
+
 def test_moe_grouped_items_equal_decode_bitwise(q, layer):
     # the grouped path's GEMV work items compute each token independently, so on a
     # decode-sized batch they must reproduce the decode path bit for bit
