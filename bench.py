@@ -43,6 +43,7 @@ EXPERT_BYTES = 2 * W13_BYTES + W2_BYTES
 GEMV_UNIT_BYTES = W13_BYTES + 2 * HIDDEN + 2 * INTER   # weights + fp16 x + fp16 y
 HBM_PEAK_GBPS = 8000.0
 GEMV_WARM_CALLS = 10
+DECODE_BATCHES = (1, 4, 16, 32)
 PREFILL_TOKENS = 2048
 PREFILL_FLOP = 2 * TOPK * PREFILL_TOKENS * 3 * INTER * HIDDEN      # dense-equivalent, 618.5 GFLOP
 MFMA_FP16_PEAK_TFLOPS = 2500.0
@@ -342,6 +343,42 @@ def main() -> int:
     bytes_per_token = 43 * TOPK * EXPERT_BYTES * L // 43
     gbps = bytes_per_token / (ms_step * 1e-3) / 1e9
 
+    # ---- one MoE layer at decode batches of 1, 4, 16 and 32 tokens (N(0,1) logits, top-6):
+    #      the layers of the stack in turn, so every call streams its experts from HBM
+    import numpy as np
+    batches = []
+    for T in DECODE_BATCHES:
+        xb = [gen_x(seed, (0x60000 + T, l), T, HIDDEN, device=dev) for l in range(L)]
+        lb = [gen_logits_normal(seed, (0x60000 + T, l), T, EXPERTS, device=dev) for l in range(L)]
+        yb = torch.empty(T, HIDDEN, dtype=torch.float16, device=dev)
+        wsb = torch.empty(q.moe_workspace_bytes(T, EXPERTS, TOPK, HIDDEN, INTER), dtype=torch.uint8, device=dev)
+        uniq = [int(np.unique(torch.topk(lb[l], TOPK, dim=1).indices.cpu().numpy()).size) for l in range(L)]
+        cur = [0]
+
+        def layer_call():
+            l = cur[0]
+            cur[0] = (l + 1) % L
+            rc = lib.gale_moe_layer_fwd(HIDDEN, INTER, tables[l].ptr(), EXPERTS, lb[l].data_ptr(), TOPK,
+                                        xb[l].data_ptr(), T, yb.data_ptr(), None, None, wsb.data_ptr(), wsb.numel(),
+                                        0, torch.cuda.current_stream().cuda_stream)
+            if rc:
+                raise RuntimeError(lib.gale_last_error().decode())
+
+        for _ in range(L):
+            layer_call()
+        torch.cuda.synchronize()
+        cur[0] = 0
+        reps = 2 * L
+        ms_layer = time_events(layer_call, reps)
+        u_mean = sum(uniq[i % L] for i in range(reps)) / reps
+        gb = u_mean * EXPERT_BYTES / (ms_layer * 1e-3) / 1e9
+        batches.append({"tokens": T, "us_per_layer": round(ms_layer * 1e3, 2), "unique_experts": round(u_mean, 1),
+                        "gbps": round(gb, 1), "frac_of_peak": round(gb / HBM_PEAK_GBPS, 4),
+                        "tokens_per_s_per_layer": round(T / (ms_layer * 1e-3), 1)})
+        log(f"decode layer T={T}: {ms_layer * 1e3:.1f} us, {u_mean:.1f} experts -> {gb:.0f} GB/s "
+            f"({100 * gb / HBM_PEAK_GBPS:.1f}% of 8 TB/s)")
+        del wsb
+
     # ---- grouped prefill: one layer of the stack, 2048 tokens, Zipf(1.1)-skewed top-6
     xp = gen_x(seed, (0x40000,), PREFILL_TOKENS, HIDDEN, device=dev)
     lgp = gen_logits_zipf(seed, (0x40000,), PREFILL_TOKENS, EXPERTS, device=dev)
@@ -407,6 +444,8 @@ def main() -> int:
                                f"prepared activations; two disjoint sets alternated",
                      "bytes_per_launch": n * GEMV_UNIT_BYTES, "avg_launch_us": round(ms_gemv * 1e3, 2),
                      "source_sha256": gemv_source_hash()[:16]},
+        "decode_batches": {"workload": "one MoE layer (256 experts, N(0,1) logits, top-6), the stack's layers in "
+                                       "turn; GB/s on the unique experts' packed bytes", "batches": batches},
         "prefill": {"workload": f"one layer (256 experts), {PREFILL_TOKENS} tokens x hidden {HIDDEN} fp16, "
                                 f"Zipf(1.1) top-6 routing, grouped path",
                     "ms": round(ms_prefill, 4), "tokens_per_s": round(PREFILL_TOKENS / ms_prefill * 1e3, 1),
