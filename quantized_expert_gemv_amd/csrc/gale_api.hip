@@ -57,7 +57,8 @@ static int pick_tiles(int64_t items, int ntiles, int cols, int slots, int gateup
   if (forced) r = 1 << (forced - 1);
   if (r > 4) r = 4;
   if ((slots >= 2 || gateup) && r > 2) r = 2;    // the kernel's register budget
-  while (r > C) r >>= 1;
+  if (r > C) r = C >= 3 ? 3 : C;                  // three chunks: units of three tiles
+  if (r == 3 && forced) r = 2;
   if (!forced) {
     const int64_t want = 2 * (int64_t)device_cu_count();
     while (r > 1 && items * ((ntiles + r - 1) / r) < want) r >>= 1;

@@ -125,6 +125,17 @@ def test_validation_before_any_gpu_work():
     assert _call("gale_moe_layer_fwd", 4096, 2048, F, 256, F, 6, F, 65, F, None, None, F, 1 << 30,
                  B.GALE_PATH_DECODE, None) == -2
     assert _call("gale_moe_layer_fwd", 4096, 2048, F, 256, F, 6, F, 1, F, None, None, F, 16, 0, None) == -5
+    # hidden above GALE_MAX_HIDDEN (the w1/w3 workgroup would exceed 1024 threads)
+    assert _call("gale_expert_ffn", 9216, 2048, F, 1, F, 0, 1, F, F, 1 << 30, None) == -2
+    assert _call("gale_moe_layer_fwd", 9216, 2048, F, 256, F, 6, F, 1, F, None, None, F, 1 << 30, 0, None) == -2
+    assert "above" in q.lib().gale_last_error().decode()
+    # routing variants: a selection bias and fixed experts exclude each other; alignment
+    assert _call("gale_moe_layer_fwd_routed", 4096, 2048, F, 256, F, F, F, 6, F, 1, F, None, None, F, 1 << 30, 0,
+                 None) == -2
+    assert _call("gale_moe_layer_fwd_routed", 4096, 2048, F, 256, F, F + 2, None, 6, F, 1, F, None, None, F,
+                 1 << 30, 0, None) == -4
+    assert _call("gale_moe_layer_fwd_routed", 4096, 2048, F, 256, F, None, F + 1, 6, F, 1, F, None, None, F,
+                 1 << 30, 0, None) == -4
     assert _call("gale_route_topk", F, 4, 256, 9, F, F, None, None, None, 0, None) == -2
     assert _call("gale_route_topk", F, 4, 256, 6, F, F, F, None, None, 0, None) == -1
     assert _call("gale_route_topk", F, 100, 256, 6, F, F, F, F, None, 0, None) == -5

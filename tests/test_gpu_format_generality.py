@@ -99,6 +99,21 @@ def test_pro_geometry_gemv(q, rows, cols):
         assert err <= 1e-4
 
 
+def test_gemv_three_chunk_units(q):
+    # 3072 columns with one vector per matrix: units of three row tiles (448 tiles per
+    # matrix: the last unit is ragged), equal bit for bit to one-tile units, and to the oracle
+    seed = config_seed(25)
+    rows, cols = PRO_HIDDEN, PRO_INTER
+    mats = gen_matrices(seed, [(7, i) for i in range(3)], rows, cols, device=DEV)
+    x = torch.stack([gen_x(seed, (8, i), 1, cols, device=DEV) for i in range(3)])
+    tab = q.matrix_table([q.pack_matrix(m) for m in mats])
+    y3 = q.expert_gemv(tab, rows, cols, x, y_dtype=torch.float32)
+    y1 = q.expert_gemv(tab, rows, cols, x, y_dtype=torch.float32, flags=q.gale_tiles_flag(1))
+    assert torch.equal(y3, y1)
+    for i, m in enumerate(mats):
+        assert O.rel_l2(np_of(y3[i]), O.gemv(m.numpy(), x[i].cpu().numpy())).max() <= 1e-4
+
+
 def test_pro_geometry_ffn(q):
     seed = config_seed(23)
     canon, packed = experts(q, seed, 1, PRO_HIDDEN, PRO_INTER)
