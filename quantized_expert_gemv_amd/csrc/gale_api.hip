@@ -48,15 +48,15 @@ static int hip_status(const char* fn, hipError_t e) {
 }
 
 // Row tiles per unit: at most the chunk count (four lanes per row serve the outliers),
-// at most 2 with four activation vectors (register budget), and small enough that the
-// units cover the GPU at least twice; flags bits 8..11 force a value (1, 2 or 4).
-static int pick_tiles(int64_t items, int ntiles, int cols, int slots, int gateup, uint32_t flags) {
+// at most 2 with two or more activation vectors (register budget), and small enough that
+// the units cover the GPU at least twice; flags bits 8..11 force a value (1, 2 or 4).
+static int pick_tiles(int64_t items, int ntiles, int cols, int slots, uint32_t flags) {
   const int C = cols / 1024;
   int r = 4;
   const int forced = (int)((flags >> GALE_TILES_SHIFT) & 0xF);
   if (forced) r = 1 << (forced - 1);
   if (r > 4) r = 4;
-  if ((slots >= 2 || gateup) && r > 2) r = 2;    // the kernel's register budget
+  if (slots >= 2 && r > 2) r = 2;                // the kernel's register budget
   if (r > C) r = C >= 3 ? 3 : C;                  // three chunks: units of three tiles
   if (r == 3 && forced) r = 2;
   if (!forced) {
@@ -357,7 +357,7 @@ extern "C" int gale_expert_gemv(int32_t rows, int32_t cols, const gale_matrix* m
   P.y_stride = rows;
   P.gateup = 0;
   const int ntiles = rows / 16;
-  const int R = pick_tiles(P.n_items, ntiles, cols, slots, 0, flags);
+  const int R = pick_tiles(P.n_items, ntiles, cols, slots, flags);
   P.row_groups = (ntiles + R - 1) / R;
   P.stage_xt = stage_ok(cols, slots);
   return hip_status(fn, launch_gemv(P, slots, R, (int64_t)P.n_items * P.row_groups, stream));
@@ -401,7 +401,7 @@ static int run_gemv_phase(const char* fn, const gale_matrix* table, int stride, 
   P.gateup = gateup;
   const int ntiles = rows / 16;
   const int64_t bound = implicit ? n_items : item_bound;
-  const int R = pick_tiles(bound, ntiles, cols, slots, gateup, flags);
+  const int R = pick_tiles(bound, ntiles, cols, slots, flags);
   P.row_groups = (ntiles + R - 1) / R;
   P.stage_xt = stage_ok(cols, slots);
   return hip_status(fn, launch_gemv(P, slots, R, bound * P.row_groups, s));

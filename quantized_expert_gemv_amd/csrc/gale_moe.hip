@@ -50,8 +50,12 @@ __device__ __forceinline__ void route_small_body(const RouteIn& rin, int T, int 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nw = blockDim.x >> 6;
   for (int e = tid; e < E; e += blockDim.x) s_cnt[e] = 0;
-  for (int t = wave; t < T; t += nw)
-    topk_wave(rin, t, E, k, lane, idx + t * k, w + t * k, s_idx + t * k);
+  if (rin.bias == nullptr && rin.fixed == nullptr && E <= 256) {
+    if (wave < T) topk_tokens(rin.logits, wave, T, nw, E, k, lane, idx, w, s_idx);
+  } else {
+    for (int t = wave; t < T; t += nw)
+      topk_wave(rin, t, E, k, lane, idx + t * k, w + t * k, s_idx + t * k);
+  }
   const int P = T * k;
   __syncthreads();
   // per-expert counts (integer atomics: order-free)

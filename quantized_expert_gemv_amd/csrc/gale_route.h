@@ -105,6 +105,24 @@ __device__ __forceinline__ void topk_rounds_biased(const float* __restrict__ lg,
   }
 }
 
+// Softmax of the k selected logits (lane s holds slot s: its logit my_v and expert my_i),
+// summed in slot order, and the k outputs.
+__device__ __forceinline__ void topk_softmax_store(float m, float my_v, int my_i, int k, int lane, int32_t* out_idx,
+                                                   float* out_w, int32_t* lds_idx) {
+  const float ex = lane < k ? expf(my_v - m) : 0.f;
+  float sum = 0.f;
+#pragma unroll
+  for (int s = 0; s < GALE_MAX_TOPK; ++s) {
+    const float es = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), s));
+    sum += s < k ? es : 0.f;
+  }
+  if (lane < k) {
+    out_idx[lane] = my_i;
+    out_w[lane] = ex / sum;
+    lds_idx[lane] = my_i;
+  }
+}
+
 __device__ __forceinline__ void topk_wave(const RouteIn& in, int t, int E, int k, int lane, int32_t* out_idx,
                                           float* out_w, int32_t* lds_idx) {
   const float* __restrict__ lg = in.logits + (int64_t)t * E;
@@ -127,18 +145,41 @@ __device__ __forceinline__ void topk_wave(const RouteIn& in, int t, int E, int k
     m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_v), 0));
     for (int s = 1; s < k; ++s) m = fmaxf(m, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_v), s)));
   }
-  // softmax of the k selected logits, one slot per lane, summed in slot order
-  const float ex = lane < k ? expf(my_v - m) : 0.f;
-  float sum = 0.f;
+  topk_softmax_store(m, my_v, my_i, k, lane, out_idx, out_w, lds_idx);
+}
+
+// Plain top-k of several tokens by one wavefront: each token's logits are loaded one token
+// ahead of its selection, so only the first load's latency is exposed (E <= 256).
+__device__ __forceinline__ void topk_tokens(const float* __restrict__ logits, int t0, int T, int step, int E,
+                                            int k, int lane, int32_t* idx, float* w, int32_t* lds_idx) {
+  float v[4], vn[4];
 #pragma unroll
-  for (int s = 0; s < GALE_MAX_TOPK; ++s) {
-    const float es = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), s));
-    sum += s < k ? es : 0.f;
-  }
-  if (lane < k) {
-    out_idx[lane] = my_i;
-    out_w[lane] = ex / sum;
-    lds_idx[lane] = my_i;
+  for (int j = 0; j < 4; ++j) v[j] = lane + 64 * j < E ? logits[(int64_t)t0 * E + lane + 64 * j] : 0.f;
+  for (int t = t0; t < T; t += step) {
+    const int tn = t + step < T ? t + step : t;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) vn[j] = lane + 64 * j < E ? logits[(int64_t)tn * E + lane + 64 * j] : 0.f;
+    uint64_t key[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) key[j] = lane + 64 * j < E ? rank_key(v[j], lane + 64 * j) : 0;
+    float m = 0.f, my_v = 0.f;
+    int my_i = 0;
+    uint64_t mk = 0;
+    for (int s = 0; s < k; ++s) {
+      uint64_t b = key[0];
+#pragma unroll
+      for (int j = 1; j < 4; ++j) b = key[j] > b ? key[j] : b;
+      const uint64_t win = wave_best(b);
+      mk = s == 0 ? win : mk;
+      my_v = lane == s ? key_logit(win) : my_v;
+      my_i = lane == s ? key_expert(win) : my_i;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) key[j] = key[j] == win ? 0 : key[j];
+    }
+    m = key_logit(mk);
+    topk_softmax_store(m, my_v, my_i, k, lane, idx + (int64_t)t * k, w + (int64_t)t * k, lds_idx + t * k);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = vn[j];
   }
 }
 

@@ -114,6 +114,26 @@ def test_gemv_three_chunk_units(q):
         assert O.rel_l2(np_of(y3[i]), O.gemv(m.numpy(), x[i].cpu().numpy())).max() <= 1e-4
 
 
+@pytest.mark.parametrize("n_tok", [1, 2])
+def test_ffn_three_chunk_hidden(q, n_tok):
+    # hidden 3072: the w1/w3 pair runs units of three row tiles with one vector per item,
+    # two with two vectors; the one-launch layer and the five-launch sequence agree bit for bit
+    seed = config_seed(26)
+    canon, packed = experts(q, seed, 2, 3072, 2048)
+    x = gen_x(seed, (1,), n_tok, 3072, device=DEV)
+    y = q.expert_ffn(q.expert_table(packed), 3072, 2048, x[None].expand(2, n_tok, 3072).contiguous())
+    for e in range(2):
+        w1, w3, w2 = (m.numpy() for m in canon[e])
+        err = O.rel_l2(np_of(y[e]), O.ffn(w1, w3, w2, x.cpu().numpy())).max()
+        print(f"ffn hidden 3072 tokens {n_tok} expert {e}: rel-L2 {err:.3e}")
+        assert err <= REL_L2_BAR
+    tab = q.expert_table(packed * 4)
+    lg = gen_logits_normal(seed, (2,), 1, 8, device=DEV)
+    y1, _, _ = q.moe_layer_fwd(tab, 3072, 2048, lg, x[:1], top_k=3)
+    ys, _, _ = q.moe_layer_fwd(tab, 3072, 2048, lg, x[:1], top_k=3, flags=q.GALE_DECODE_STAGED)
+    assert torch.equal(y1, ys)
+
+
 def test_pro_geometry_ffn(q):
     seed = config_seed(23)
     canon, packed = experts(q, seed, 1, PRO_HIDDEN, PRO_INTER)
