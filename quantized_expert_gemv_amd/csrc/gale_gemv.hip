@@ -569,16 +569,15 @@ static hipError_t launch_t(const GemvParams& p, int64_t max_units, hipStream_t s
 
 template <int NS, bool G>
 static hipError_t launch_r(const GemvParams& p, int tiles, int64_t max_units, hipStream_t s) {
-  // three and four tiles per unit only for single-token items (more would spill); the
-  // host's row groups are counted with the same tile count, so no other value is taken
+  // four tiles per unit for items of up to two vectors, three for four vectors (four would
+  // spill); the host's row groups are counted with the same tile count, so no other value
+  // is taken
   switch (tiles) {
     case 1: return launch_t<NS, 1, G>(p, max_units, s);
     case 2: return launch_t<NS, 2, G>(p, max_units, s);
-    case 3:
-      if constexpr (NS == 1) return launch_t<NS, 3, G>(p, max_units, s);
-      else return hipErrorInvalidValue;
+    case 3: return launch_t<NS, 3, G>(p, max_units, s);
     case 4:
-      if constexpr (NS == 1) return launch_t<NS, 4, G>(p, max_units, s);
+      if constexpr (NS <= 2) return launch_t<NS, 4, G>(p, max_units, s);
       else return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }

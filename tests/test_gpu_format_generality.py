@@ -114,6 +114,25 @@ def test_gemv_three_chunk_units(q):
         assert O.rel_l2(np_of(y3[i]), O.gemv(m.numpy(), x[i].cpu().numpy())).max() <= 1e-4
 
 
+@pytest.mark.parametrize("n_tok", [2, 3, 4])
+def test_gemv_multi_vector_units(q, n_tok):
+    # several vectors per matrix: two per item run units of four row tiles, four per item
+    # units of three (the last of the 128 tiles ragged); bit for bit the same as one-tile
+    # units, and the oracle's on two of the matrices
+    seed = config_seed(27)
+    rows, cols, n = 2048, 4096, 24
+    mats = gen_matrices(seed, [(9, i) for i in range(n)], rows, cols, device=DEV)
+    x = torch.stack([gen_x(seed, (10, i), n_tok, cols, device=DEV) for i in range(n)])
+    tab = q.matrix_table([q.pack_matrix(m) for m in mats])
+    yw = q.expert_gemv(tab, rows, cols, x, y_dtype=torch.float32)
+    y1 = q.expert_gemv(tab, rows, cols, x, y_dtype=torch.float32, flags=q.gale_tiles_flag(1))
+    assert torch.equal(yw, y1)
+    for i in (0, n - 1):
+        err = O.rel_l2(np_of(yw[i]), O.gemv(mats[i].numpy(), x[i].cpu().numpy())).max()
+        print(f"gemv {n_tok} vectors, matrix {i}: rel-L2 {err:.3e}")
+        assert err <= 1e-4
+
+
 @pytest.mark.parametrize("n_tok", [1, 2])
 def test_ffn_three_chunk_hidden(q, n_tok):
     # hidden 3072: the w1/w3 pair runs units of three row tiles with one vector per item,
