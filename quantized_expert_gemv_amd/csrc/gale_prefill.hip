@@ -162,9 +162,10 @@ hipError_t launch_rotate_f16(const void* x, int x_dtype, int64_t n_rows, int K, 
 // ---------------------------------------------------------------------------
 // Grouped GEMM.  Workgroup = (tile of kGemmBM pairs of one expert) x (128 weight rows):
 // gate/up takes 64 rows of w1 and the same 64 rows of w3 (SwiGLU in the epilogue),
-// down 128 rows of w2.  Four wavefronts in a 2 x 2 arrangement, 64 pairs x 64 rows
-// each.  K advances one 128-column scale block at a time through double-buffered
-// LDS tiles:
+// down 128 rows of w2.  Eight wavefronts in two roles, two per SIMD: four producers
+// load and unpack, four consumers run the products in a 2 x 2 arrangement, 64 pairs x
+// 64 rows each, so one role's waits overlap the other's work.  K advances one
+// 128-column scale block at a time through double-buffered LDS tiles:
 //   A: 128 pairs x 128 fp16 rotated activations (copied from HBM);
 //   B: 128 rows x 128 fp16 weights, unpacked from the device sign layout (one
 //      shift, AND and XOR per two weights: the sign bit goes straight into the fp16
@@ -496,17 +497,17 @@ __device__ __forceinline__ void store_block(const BlockRegs& r, BItem& b0, BItem
   }
 }
 
-// The K loop over blocks of 128 columns, two LDS buffers: while the products of block
-// bd run on one buffer, block bd + 1 is stored into the other from registers, and the
-// registers are refilled with block bd + 3.  NB (blocks) is a multiple of 8, so the
-// loop takes blocks in pairs and each register set serves one parity.  The last pass
-// also stores a block NB (a copy of block NB - 1's words, no outliers left) that
-// nothing reads.
+// The K loop over blocks of 128 columns, two LDS buffers, split by role.  Producers
+// (wavefronts 0..3) fill the buffers: while the consumers run block bd from one buffer,
+// block bd + 1 is stored into the other from registers, and the registers are refilled
+// with block bd + 3.  NB (blocks) is a multiple of 8, so the loop takes blocks in pairs
+// and each register set serves one parity.  The last pass also stores a block NB (a
+// copy of block NB - 1's words, no outliers left) that nothing reads.  Both roles pass
+// the same 1 + NB barriers.
 template <bool STAGED>
-__device__ __forceinline__ void gemm_k_loop(const GemmParams& P, v4f (&acc)[4][4], lds_b* A0, lds_b* B0,
-                                            const AStage& as, BItem& b0, BItem& b1, int NB, int tid, int acg,
-                                            int wm, int wn, int ml, int lg, const lds_u32* st_ent,
-                                            int starts0, int starts1, BlockRegs& re, BlockRegs& ro) {
+__device__ __forceinline__ void producer_loop(const GemmParams& P, lds_b* A0, lds_b* B0, const AStage& as, BItem& b0,
+                                              BItem& b1, int NB, int tid, int acg, const lds_u32* st_ent,
+                                              int starts0, int starts1, BlockRegs& re, BlockRegs& ro) {
   lds_b* const A1 = A0 + kTileBytes;
   lds_b* const B1 = B0 + kTileBytes;
   const int lane = tid & 63, tt0 = b0.brow >> 4;
@@ -535,7 +536,6 @@ __device__ __forceinline__ void gemm_k_loop(const GemmParams& P, v4f (&acc)[4][4
       px0 = patch_prep(st_ent, starts0, tt0, bd + 2, NB, lane);
       px1 = patch_prep(st_ent, starts1, tt0 + 4, bd + 2, NB, lane);
     }
-    mfma_block(acc, A0, B0, wm, wn, ml, lg);
     store_block<STAGED>(ro, b0, b1, A1, B1, bd + 1, tid, acg, py0, py1, tt0, st_ent, P.table);
     block_load(ro, as, b0, b1, P.A, P.K, min(bd + 3, NB - 1), acg);
     if (STAGED) {
@@ -548,7 +548,6 @@ __device__ __forceinline__ void gemm_k_loop(const GemmParams& P, v4f (&acc)[4][4
       py0 = patch_prep(st_ent, starts0, tt0, bd + 3, NB, lane);
       py1 = patch_prep(st_ent, starts1, tt0 + 4, bd + 3, NB, lane);
     }
-    mfma_block(acc, A1, B1, wm, wn, ml, lg);
     store_block<STAGED>(re, b0, b1, A0, B0, bd + 2, tid, acg, px0, px1, tt0, st_ent, P.table);
     block_load(re, as, b0, b1, P.A, P.K, min(bd + 4, NB - 1), acg);
     if (STAGED) {
@@ -559,8 +558,22 @@ __device__ __forceinline__ void gemm_k_loop(const GemmParams& P, v4f (&acc)[4][4
   }
 }
 
+// Consumers (wavefronts 4..7): the products of each block, alternating buffers.
+__device__ __forceinline__ void consumer_loop(v4f (&acc)[4][4], const lds_b* A0, const lds_b* B0, int NB, int wm,
+                                              int wn, int ml, int lg) {
+  const lds_b* const A1 = A0 + kTileBytes;
+  const lds_b* const B1 = B0 + kTileBytes;
+  __syncthreads();
+  for (int bd = 0; bd < NB; bd += 2) {
+    mfma_block(acc, A0, B0, wm, wn, ml, lg);
+    __syncthreads();
+    mfma_block(acc, A1, B1, wm, wn, ml, lg);
+    __syncthreads();
+  }
+}
+
 template <bool GATEUP>
-__global__ void __launch_bounds__(256) grouped_gemm_kernel(const GemmParams P) {
+__global__ void __launch_bounds__(512) grouped_gemm_kernel(const GemmParams P) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int n_tiles = *P.n_tiles;
   if ((int)blockIdx.y >= n_tiles) return;
@@ -569,8 +582,11 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(const GemmParams P) {
   const int pair0 = P.offsets[e] + m0;
   const int valid = min(kGemmBM, P.offsets[e + 1] - pair0);
   const int n0 = blockIdx.x * P.half_rows;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  // wavefronts 0..3 load, unpack and patch (tid 0..255); 4..7 run the products
+  const bool producer = wave < 4;
+  const int tid = threadIdx.x & 255;
   const int C = P.K >> 10;
   const int NB = P.K >> 7;
 
@@ -584,44 +600,50 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(const GemmParams P) {
   lds_i32* const st_fill = st_start + kBuckets + 1;
 
   AStage as;
-  const int first_row = P.a_by_token ? P.perm[pair0] / P.top_k : P.perm[pair0];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int rr = (tid >> 4) + 16 * j;
-    int src = first_row;
-    if (rr < valid) {
-      const int s = pair0 + rr;
-      src = P.a_by_token ? P.perm[s] / P.top_k : P.perm[s];
-    }
-    as.row[j] = src;
-  }
   const int acg = tid & 15;
-
-  BItem b0 = make_item(P, e, n0, C, tid);
-  BItem b1 = make_item(P, e, n0, C, tid + 256);
-  // blocks 0 and 1 load while the outliers are staged; the two sets issue in order (no
-  // interleaving), so the K loop's waits count whole sets
+  BItem b0, b1;
   BlockRegs re, ro;   // blocks of even and of odd index
-  __builtin_amdgcn_sched_barrier(0);
-  block_load(re, as, b0, b1, P.A, P.K, 0, acg);
-  __builtin_amdgcn_sched_barrier(0);
-  block_load(ro, as, b0, b1, P.A, P.K, 1, acg);
-  __builtin_amdgcn_sched_barrier(0);
+  if (producer) {
+    const int first_row = P.a_by_token ? P.perm[pair0] / P.top_k : P.perm[pair0];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int rr = (tid >> 4) + 16 * j;
+      int src = first_row;
+      if (rr < valid) {
+        const int s = pair0 + rr;
+        src = P.a_by_token ? P.perm[s] / P.top_k : P.perm[s];
+      }
+      as.row[j] = src;
+    }
+    b0 = make_item(P, e, n0, C, tid);
+    b1 = make_item(P, e, n0, C, tid + 256);
+    // blocks 0 and 1 load while the outliers are staged; the two sets issue in order (no
+    // interleaving), so the K loop's waits count whole sets
+    __builtin_amdgcn_sched_barrier(0);
+    block_load(re, as, b0, b1, P.A, P.K, 0, acg);
+    __builtin_amdgcn_sched_barrier(0);
+    block_load(ro, as, b0, b1, P.A, P.K, 1, acg);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 
-
-  // ---- outlier staging.  Row r = tid / 2 of the B tile (matrix sel_a for r < half_rows,
-  //      else sel_b; global row n0 + r % half_rows) is walked by two threads, entries of
-  //      parity tid & 1: count per bucket, scan, then place each entry.
+  // ---- outlier staging (producers; the consumers pass the same barriers).  Row r =
+  //      tid / 2 of the B tile (matrix sel_a for r < half_rows, else sel_b; global row
+  //      n0 + r % half_rows) is walked by two threads, entries of parity tid & 1: count
+  //      per bucket, scan, then place each entry.
   const int r = tid >> 1, par = tid & 1;
   const gale_matrix* Mr = P.table + 3 * e + (r >= P.half_rows ? P.sel_b : P.sel_a);
   const int gr = n0 + r % P.half_rows;
-  const int rp0 = Mr->row_ptr[gr], rp1 = Mr->row_ptr[gr + 1];
+  int rp0 = 0, rp1 = 0;
+  if (producer) {
+    rp0 = Mr->row_ptr[gr];
+    rp1 = Mr->row_ptr[gr + 1];
+  }
   const int nbk = 8 * NB;                                    // buckets in use
-  if (tid == 0) st_misc[0] = 0;
-  if (tid < kGemmBM) s_orow[tid] = tid < valid ? P.perm[pair0 + tid] : 0;
-  for (int b = tid; b < kBuckets; b += 256) st_fill[b] = 0;
+  if (threadIdx.x == 0) st_misc[0] = 0;
+  if (threadIdx.x < kGemmBM) s_orow[threadIdx.x] = (int)threadIdx.x < valid ? P.perm[pair0 + threadIdx.x] : 0;
+  for (int b = threadIdx.x; b < kBuckets; b += 512) st_fill[b] = 0;
   __syncthreads();
-  if (par == 0) __atomic_fetch_add(st_misc, rp1 - rp0, __ATOMIC_RELAXED);
+  if (producer && par == 0) __atomic_fetch_add(st_misc, rp1 - rp0, __ATOMIC_RELAXED);
   __syncthreads();
   const bool staged = st_misc[0] <= kOutStage && NB <= kStageBlocks;
   const int bucket0 = (r >> 4) * NB;
@@ -629,80 +651,92 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(const GemmParams P) {
   if (staged) {
     // the walks take the thread's entries eight at a time, loads first (clamped into the
     // row's range) so that eight are in flight
-    for (int p0 = rp0 + par; p0 < rp1; p0 += 16) {
-      int col[8];
+    if (producer) {
+      for (int p0 = rp0 + par; p0 < rp1; p0 += 16) {
+        int col[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) col[k] = Mr->out_cols[min(p0 + 2 * k, rp1 - 1)];
+        for (int k = 0; k < 8; ++k) col[k] = Mr->out_cols[min(p0 + 2 * k, rp1 - 1)];
 #pragma unroll
-      for (int k = 0; k < 8; ++k)
-        if (p0 + 2 * k < rp1) __atomic_fetch_add(st_fill + bucket0 + (col[k] >> 7), 1, __ATOMIC_RELAXED);
+        for (int k = 0; k < 8; ++k)
+          if (p0 + 2 * k < rp1) __atomic_fetch_add(st_fill + bucket0 + (col[k] >> 7), 1, __ATOMIC_RELAXED);
+      }
     }
     __syncthreads();
     // exclusive scan of the bucket counts, two per thread
-    const int c0 = 2 * tid < nbk ? st_fill[2 * tid] : 0;
-    const int c1 = 2 * tid + 1 < nbk ? st_fill[2 * tid + 1] : 0;
-    int v = c0 + c1;
+    int c0 = 0, c1 = 0, v = 0;
+    if (producer) {
+      c0 = 2 * tid < nbk ? st_fill[2 * tid] : 0;
+      c1 = 2 * tid + 1 < nbk ? st_fill[2 * tid + 1] : 0;
+      v = c0 + c1;
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int o = __shfl_up(v, off, 64);
-      if (lane >= off) v += o;
-    }
-    if (lane == 63) st_misc[1 + wave] = v;
-    __syncthreads();
-    int ex = v - c0 - c1;
-    for (int w = 0; w < wave; ++w) ex += st_misc[1 + w];
-    if (2 * tid < nbk) st_start[2 * tid] = st_fill[2 * tid] = ex;
-    if (2 * tid + 1 < nbk) st_start[2 * tid + 1] = st_fill[2 * tid + 1] = ex + c0;
-    if (tid == 255) st_start[nbk] = ex + c0 + c1;
-    __syncthreads();
-    const uint16_t rs = Mr->row_scales[gr];
-    for (int p0 = rp0 + par; p0 < rp1; p0 += 16) {
-      int col[8], q[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int p = min(p0 + 2 * k, rp1 - 1);
-        col[k] = Mr->out_cols[p];
-        q[k] = outlier_value(Mr->out_vals, p);
+      for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(v, off, 64);
+        if (lane >= off) v += o;
       }
+      if (lane == 63) st_misc[1 + wave] = v;
+    }
+    __syncthreads();
+    if (producer) {
+      int ex = v - c0 - c1;
+      for (int w = 0; w < wave; ++w) ex += st_misc[1 + w];
+      if (2 * tid < nbk) st_start[2 * tid] = st_fill[2 * tid] = ex;
+      if (2 * tid + 1 < nbk) st_start[2 * tid + 1] = st_fill[2 * tid + 1] = ex + c0;
+      if (tid == 255) st_start[nbk] = ex + c0 + c1;
+    }
+    __syncthreads();
+    if (producer) {
+      // each entry carries its patched weight: the sign bit and block scale of its
+      // position are read here, once per tile
+      const uint16_t rs = Mr->row_scales[gr];
+      for (int p0 = rp0 + par; p0 < rp1; p0 += 16) {
+        int col[8], q[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        if (p0 + 2 * k < rp1) {
-          const int slot = __atomic_fetch_add(st_fill + bucket0 + (col[k] >> 7), 1, __ATOMIC_RELAXED);
-          st_ent[slot] = pack_entry(col[k] & 127, r & 15, q[k], rs);
+        for (int k = 0; k < 8; ++k) {
+          const int p = min(p0 + 2 * k, rp1 - 1);
+          col[k] = Mr->out_cols[p];
+          q[k] = outlier_value(Mr->out_vals, p);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          if (p0 + 2 * k < rp1) {
+            const int slot = __atomic_fetch_add(st_fill + bucket0 + (col[k] >> 7), 1, __ATOMIC_RELAXED);
+            st_ent[slot] = pack_entry(col[k] & 127, r & 15, q[k], rs);
+          }
         }
       }
+      // bucket starts of the wavefront's two row groups, lane l: block l (l <= NB)
+      starts0 = lane <= NB ? st_start[wave * NB + lane] : 0;
+      starts1 = lane <= NB ? st_start[(wave + 4) * NB + lane] : 0;
     }
-    // bucket starts of the wavefront's two row groups, lane l: block l (l <= NB)
-    starts0 = lane <= NB ? st_start[wave * NB + lane] : 0;
-    starts1 = lane <= NB ? st_start[(wave + 4) * NB + lane] : 0;
     __syncthreads();
   }
 
-  if (!staged) {
-    item_walk_init(P, e, n0, b0);
-    item_walk_init(P, e, n0, b1);
+  // ---- accumulators of consumer (wm, wn) = pairs [64 wm, +64) x B rows [64 wn, +64)
+  const int wm = wave & 1, wn = (wave >> 1) & 1;
+  const int ml = lane & 15, lg = lane >> 4;
+  v4f acc[4][4];
+  if (producer) {
+    if (staged) {
+      producer_loop<true>(P, A0, B0, as, b0, b1, NB, tid, acg, st_ent, starts0, starts1, re, ro);
+    } else {
+      item_walk_init(P, e, n0, b0);
+      item_walk_init(P, e, n0, b1);
+      producer_loop<false>(P, A0, B0, as, b0, b1, NB, tid, acg, st_ent, 0, 0, re, ro);
+    }
+  } else {
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+      for (int nf = 0; nf < 4; ++nf) acc[f][nf] = v4f{0.f, 0.f, 0.f, 0.f};
+    consumer_loop(acc, A0, B0, NB, wm, wn, ml, lg);
   }
 
-  // ---- accumulators: wave (wm, wn) = pairs [64 wm, +64) x B rows [64 wn, +64)
-  const int wm = wave & 1, wn = wave >> 1;
-  v4f acc[4][4];
-#pragma unroll
-  for (int f = 0; f < 4; ++f)
-#pragma unroll
-    for (int nf = 0; nf < 4; ++nf) acc[f][nf] = v4f{0.f, 0.f, 0.f, 0.f};
-  const int ml = lane & 15, lg = lane >> 4;
-
-  if (staged)
-    gemm_k_loop<true>(P, acc, A0, B0, as, b0, b1, NB, tid, acg, wm, wn, ml, lg, st_ent, starts0, starts1, re, ro);
-  else
-    gemm_k_loop<false>(P, acc, A0, B0, as, b0, b1, NB, tid, acg, wm, wn, ml, lg, st_ent, 0, 0, re, ro);
-
-  // ---- epilogue.  Fragment layout: lane l, register i -> pair 16 f + 4 (l / 16) + i,
-  //      B row 16 nf + l % 16 of the wave's range.
+  // ---- epilogue (consumers).  Fragment layout: lane l, register i -> pair 16 f + 4 (l / 16)
+  //      + i, B row 16 nf + l % 16 of the wave's range.
   if (GATEUP) {
     // the waves of w3 rows hand their products to the waves of the same w1 rows
     float* U = reinterpret_cast<float*>(smem);
-    if (wn == 1) {
+    if (!producer && wn == 1) {
 #pragma unroll
       for (int f = 0; f < 4; ++f)
 #pragma unroll
@@ -711,7 +745,7 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(const GemmParams P) {
               make_float4(acc[f][nf][0], acc[f][nf][1], acc[f][nf][2], acc[f][nf][3]);
     }
     __syncthreads();
-    if (wn == 0) {
+    if (!producer && wn == 0) {
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
 #pragma unroll
@@ -729,7 +763,7 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(const GemmParams P) {
         }
       }
     }
-  } else {
+  } else if (!producer) {
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
 #pragma unroll
@@ -773,12 +807,12 @@ hipError_t launch_grouped_gemm(const gale_matrix* table, int gateup, int rows, i
     err = hipFuncSetAttribute((const void*)grouped_gemm_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)kGemmSmem);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(grouped_gemm_kernel<true>, grid, dim3(256), kGemmSmem, s, P);
+    hipLaunchKernelGGL(grouped_gemm_kernel<true>, grid, dim3(512), kGemmSmem, s, P);
   } else {
     err = hipFuncSetAttribute((const void*)grouped_gemm_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)kGemmSmem);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(grouped_gemm_kernel<false>, grid, dim3(256), kGemmSmem, s, P);
+    hipLaunchKernelGGL(grouped_gemm_kernel<false>, grid, dim3(512), kGemmSmem, s, P);
   }
   return hipGetLastError();
 }
