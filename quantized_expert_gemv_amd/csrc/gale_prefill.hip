@@ -303,39 +303,42 @@ __device__ __forceinline__ void item_walk_init(const GemmParams& P, int e, int n
   }
 }
 
-// A staging: chunk q = tid + 256 j -> tile row q / 16, 16-byte column group q % 16.
+// Producer threads of a workgroup (eight wavefronts): each stages four A chunks and
+// unpacks one B item per block.
+constexpr int kProducerThreads = 512;
+constexpr int kAChunks = kGemmBM * 16 / kProducerThreads;
+
+// A staging: chunk q = tid + 512 j -> tile row q / 16, 16-byte column group q % 16.
 // Rows past the tile's pairs read the first pair's row: those MFMA rows are never stored.
 struct AStage {
-  int row[8];
+  int row[kAChunks];
 };
 
 // Everything block j of the K loop takes from global memory, loaded two blocks ahead of
-// its store into LDS: the thread's eight A chunks and, for each of its two B items, the
-// sign words of the block's half-chunk and the word holding the block's scale.  The
-// loads are unconditional, so the wait before the store counts exactly the newer set.
+// its store into LDS: the thread's four A chunks and, for its B item, the sign words of
+// the block's half-chunk and the word holding the block's scale.  The loads are
+// unconditional, so the wait before the store counts exactly the newer set.
 struct BlockRegs {
-  uint4 a[8];
-  uint4 w[2];
-  uint32_t s[2];
+  uint4 a[kAChunks];
+  uint4 w;
+  uint32_t s;
 };
 
-__device__ __forceinline__ void block_load(BlockRegs& r, const AStage& as, const BItem& b0, const BItem& b1,
-                                           const uint16_t* A, int K, int j, int acg) {
+__device__ __forceinline__ void block_load(BlockRegs& r, const AStage& as, const BItem& b, const uint16_t* A, int K,
+                                           int j, int acg) {
 #pragma unroll
-  for (int q = 0; q < 8; ++q) r.a[q] = gload16(A + (int64_t)as.row[q] * K + 128 * j + 8 * acg);
+  for (int q = 0; q < kAChunks; ++q) r.a[q] = gload16(A + (int64_t)as.row[q] * K + 128 * j + 8 * acg);
   const int c = j >> 3, d = j & 7;
   const int64_t wo = (int64_t)c * 512 + 256 * (d >> 2);   // words of half d / 4 of chunk c
   const int64_t so = (int64_t)c * 128 + 2 * (d >> 1);     // scales of blocks d & ~1 and d | 1
-  r.w[0] = gload16(b0.sign + wo);
-  r.w[1] = gload16(b1.sign + wo);
-  r.s[0] = gload4(b0.scale + so);
-  r.s[1] = gload4(b1.scale + so);
+  r.w = gload16(b.sign + wo);
+  r.s = gload4(b.scale + so);
 }
 
 __device__ __forceinline__ void a_store(const BlockRegs& r, lds_b* At, int tid, int acg) {
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int row = (tid >> 4) + 16 * q;
+  for (int q = 0; q < kAChunks; ++q) {
+    const int row = (tid >> 4) + (kProducerThreads / 16) * q;
     *reinterpret_cast<lds_q*>(At + row * kRowBytes + 16 * acg) = u32x4{r.a[q].x, r.a[q].y, r.a[q].z, r.a[q].w};
   }
 }
@@ -481,84 +484,59 @@ __device__ __forceinline__ void mfma_block(v4f (&acc)[4][4], const lds_b* At, co
 
 // Stores block j into the B buffer Bt (and A into At): A chunks, sign unpack, outliers.
 template <bool STAGED>
-__device__ __forceinline__ void store_block(const BlockRegs& r, BItem& b0, BItem& b1, lds_b* At, lds_b* Bt, int j,
-                                            int tid, int acg, const Patch p0, const Patch p1, int tt0,
-                                            const lds_u32* st_ent, const gale_matrix* table) {
+__device__ __forceinline__ void store_block(const BlockRegs& r, BItem& b, lds_b* At, lds_b* Bt, int j, int tid, int acg,
+                                            const Patch pt, int tt, const gale_matrix* table) {
   a_store(r, At, tid, acg);
-  sign_store(b0, r.w[0], r.s[0], Bt, j);
-  sign_store(b1, r.w[1], r.s[1], Bt, j);
-  if (STAGED) {
-    const int lane = tid & 63;
-    patch_apply(p0, Bt, tt0, lane);
-    patch_apply(p1, Bt, tt0 + 4, lane);
-  } else {
-    walk_outliers(b0, Bt, j, table);
-    walk_outliers(b1, Bt, j, table);
-  }
+  sign_store(b, r.w, r.s, Bt, j);
+  if (STAGED) patch_apply(pt, Bt, tt, tid & 63);
+  else walk_outliers(b, Bt, j, table);
 }
 
 // The K loop over blocks of 128 columns, two LDS buffers, split by role.  Producers
-// (wavefronts 0..3) fill the buffers: while the consumers run block bd from one buffer,
+// (wavefronts 0..7) fill the buffers: while the consumers run block bd from one buffer,
 // block bd + 1 is stored into the other from registers, and the registers are refilled
 // with block bd + 3.  NB (blocks) is a multiple of 8, so the loop takes blocks in pairs
 // and each register set serves one parity.  The last pass also stores a block NB (a
 // copy of block NB - 1's words, no outliers left) that nothing reads.  Both roles pass
-// the same 1 + NB barriers.
+// the same 1 + NB barriers.  Producer wavefront w unpacks and patches B row group w.
 template <bool STAGED>
-__device__ __forceinline__ void producer_loop(const GemmParams& P, lds_b* A0, lds_b* B0, const AStage& as, BItem& b0,
-                                              BItem& b1, int NB, int tid, int acg, const lds_u32* st_ent,
-                                              int starts0, int starts1, BlockRegs& re, BlockRegs& ro) {
+__device__ __forceinline__ void producer_loop(const GemmParams& P, lds_b* A0, lds_b* B0, const AStage& as, BItem& b,
+                                              int NB, int tid, int acg, const lds_u32* st_ent, int starts,
+                                              BlockRegs& re, BlockRegs& ro) {
   lds_b* const A1 = A0 + kTileBytes;
   lds_b* const B1 = B0 + kTileBytes;
-  const int lane = tid & 63, tt0 = b0.brow >> 4;
+  const int lane = tid & 63, tt = b.brow >> 4;
   const Patch none = {0, 0, kNoEntry};
   // patch entries of the block stored next (x) and of the one after (y)
-  Patch px0 = none, px1 = none, py0 = none, py1 = none;
+  Patch px = none, py = none;
   // re holds block 0 and ro block 1 (loaded before the outlier staging)
   if (STAGED) {
-    px0 = patch_prep(st_ent, starts0, tt0, 0, NB, lane);
-    px1 = patch_prep(st_ent, starts1, tt0 + 4, 0, NB, lane);
-    py0 = patch_prep(st_ent, starts0, tt0, 1, NB, lane);
-    py1 = patch_prep(st_ent, starts1, tt0 + 4, 1, NB, lane);
+    px = patch_prep(st_ent, starts, tt, 0, NB, lane);
+    py = patch_prep(st_ent, starts, tt, 1, NB, lane);
   }
-  store_block<STAGED>(re, b0, b1, A0, B0, 0, tid, acg, px0, px1, tt0, st_ent, P.table);
-  if (STAGED) {
-    patch_rest(px0, B0, st_ent, tt0, lane);
-    patch_rest(px1, B0, st_ent, tt0 + 4, lane);
-  }
+  store_block<STAGED>(re, b, A0, B0, 0, tid, acg, px, tt, P.table);
+  if (STAGED) patch_rest(px, B0, st_ent, tt, lane);
   __builtin_amdgcn_sched_barrier(0);
-  block_load(re, as, b0, b1, P.A, P.K, 2, acg);
+  block_load(re, as, b, P.A, P.K, 2, acg);
   __builtin_amdgcn_sched_barrier(0);
   __syncthreads();
   for (int bd = 0; bd < NB; bd += 2) {
     // block bd (buffer 0) runs; block bd + 1 into buffer 1
-    if (STAGED) {
-      px0 = patch_prep(st_ent, starts0, tt0, bd + 2, NB, lane);
-      px1 = patch_prep(st_ent, starts1, tt0 + 4, bd + 2, NB, lane);
-    }
-    store_block<STAGED>(ro, b0, b1, A1, B1, bd + 1, tid, acg, py0, py1, tt0, st_ent, P.table);
-    block_load(ro, as, b0, b1, P.A, P.K, min(bd + 3, NB - 1), acg);
-    if (STAGED) {
-      patch_rest(py0, B1, st_ent, tt0, lane);
-      patch_rest(py1, B1, st_ent, tt0 + 4, lane);
-    }
+    if (STAGED) px = patch_prep(st_ent, starts, tt, bd + 2, NB, lane);
+    store_block<STAGED>(ro, b, A1, B1, bd + 1, tid, acg, py, tt, P.table);
+    block_load(ro, as, b, P.A, P.K, min(bd + 3, NB - 1), acg);
+    if (STAGED) patch_rest(py, B1, st_ent, tt, lane);
     __syncthreads();
     // block bd + 1 (buffer 1) runs; block bd + 2 into buffer 0
-    if (STAGED) {
-      py0 = patch_prep(st_ent, starts0, tt0, bd + 3, NB, lane);
-      py1 = patch_prep(st_ent, starts1, tt0 + 4, bd + 3, NB, lane);
-    }
-    store_block<STAGED>(re, b0, b1, A0, B0, bd + 2, tid, acg, px0, px1, tt0, st_ent, P.table);
-    block_load(re, as, b0, b1, P.A, P.K, min(bd + 4, NB - 1), acg);
-    if (STAGED) {
-      patch_rest(px0, B0, st_ent, tt0, lane);
-      patch_rest(px1, B0, st_ent, tt0 + 4, lane);
-    }
+    if (STAGED) py = patch_prep(st_ent, starts, tt, bd + 3, NB, lane);
+    store_block<STAGED>(re, b, A0, B0, bd + 2, tid, acg, px, tt, P.table);
+    block_load(re, as, b, P.A, P.K, min(bd + 4, NB - 1), acg);
+    if (STAGED) patch_rest(px, B0, st_ent, tt, lane);
     __syncthreads();
   }
 }
 
-// Consumers (wavefronts 4..7): the products of each block, alternating buffers.
+// Consumers (wavefronts 8..11): the products of each block, alternating buffers.
 __device__ __forceinline__ void consumer_loop(v4f (&acc)[4][4], const lds_b* A0, const lds_b* B0, int NB, int wm,
                                               int wn, int ml, int lg) {
   const lds_b* const A1 = A0 + kTileBytes;
@@ -573,7 +551,7 @@ __device__ __forceinline__ void consumer_loop(v4f (&acc)[4][4], const lds_b* A0,
 }
 
 template <bool GATEUP>
-__global__ void __launch_bounds__(512) grouped_gemm_kernel(const GemmParams P) {
+__global__ void __launch_bounds__(kProducerThreads + 256) grouped_gemm_kernel(const GemmParams P) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int n_tiles = *P.n_tiles;
   if ((int)blockIdx.y >= n_tiles) return;
@@ -584,9 +562,9 @@ __global__ void __launch_bounds__(512) grouped_gemm_kernel(const GemmParams P) {
   const int n0 = blockIdx.x * P.half_rows;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-  // wavefronts 0..3 load, unpack and patch (tid 0..255); 4..7 run the products
-  const bool producer = wave < 4;
-  const int tid = threadIdx.x & 255;
+  // wavefronts 0..7 load, unpack and patch (tid 0..511); 8..11 run the products
+  const bool producer = wave < kProducerThreads / 64;
+  const int tid = threadIdx.x & (kProducerThreads - 1);
   const int C = P.K >> 10;
   const int NB = P.K >> 7;
 
@@ -601,13 +579,13 @@ __global__ void __launch_bounds__(512) grouped_gemm_kernel(const GemmParams P) {
 
   AStage as;
   const int acg = tid & 15;
-  BItem b0, b1;
+  BItem b;
   BlockRegs re, ro;   // blocks of even and of odd index
   if (producer) {
     const int first_row = P.a_by_token ? P.perm[pair0] / P.top_k : P.perm[pair0];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int rr = (tid >> 4) + 16 * j;
+    for (int j = 0; j < kAChunks; ++j) {
+      const int rr = (tid >> 4) + (kProducerThreads / 16) * j;
       int src = first_row;
       if (rr < valid) {
         const int s = pair0 + rr;
@@ -615,43 +593,43 @@ __global__ void __launch_bounds__(512) grouped_gemm_kernel(const GemmParams P) {
       }
       as.row[j] = src;
     }
-    b0 = make_item(P, e, n0, C, tid);
-    b1 = make_item(P, e, n0, C, tid + 256);
+    b = make_item(P, e, n0, C, tid);
     // blocks 0 and 1 load while the outliers are staged; the two sets issue in order (no
     // interleaving), so the K loop's waits count whole sets
     __builtin_amdgcn_sched_barrier(0);
-    block_load(re, as, b0, b1, P.A, P.K, 0, acg);
+    block_load(re, as, b, P.A, P.K, 0, acg);
     __builtin_amdgcn_sched_barrier(0);
-    block_load(ro, as, b0, b1, P.A, P.K, 1, acg);
+    block_load(ro, as, b, P.A, P.K, 1, acg);
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // ---- outlier staging (producers; the consumers pass the same barriers).  Row r =
-  //      tid / 2 of the B tile (matrix sel_a for r < half_rows, else sel_b; global row
+  // ---- outlier staging by wavefronts 0..3 (the others pass the same barriers).  Row
+  //      r = tid / 2 of the B tile (matrix sel_a for r < half_rows, else sel_b; global row
   //      n0 + r % half_rows) is walked by two threads, entries of parity tid & 1: count
   //      per bucket, scan, then place each entry.
-  const int r = tid >> 1, par = tid & 1;
+  const bool stager = threadIdx.x < 256;
+  const int r = (tid >> 1) & 127, par = tid & 1;
   const gale_matrix* Mr = P.table + 3 * e + (r >= P.half_rows ? P.sel_b : P.sel_a);
   const int gr = n0 + r % P.half_rows;
   int rp0 = 0, rp1 = 0;
-  if (producer) {
+  if (stager) {
     rp0 = Mr->row_ptr[gr];
     rp1 = Mr->row_ptr[gr + 1];
   }
   const int nbk = 8 * NB;                                    // buckets in use
   if (threadIdx.x == 0) st_misc[0] = 0;
   if (threadIdx.x < kGemmBM) s_orow[threadIdx.x] = (int)threadIdx.x < valid ? P.perm[pair0 + threadIdx.x] : 0;
-  for (int b = threadIdx.x; b < kBuckets; b += 512) st_fill[b] = 0;
+  for (int i = threadIdx.x; i < kBuckets; i += blockDim.x) st_fill[i] = 0;
   __syncthreads();
-  if (producer && par == 0) __atomic_fetch_add(st_misc, rp1 - rp0, __ATOMIC_RELAXED);
+  if (stager && par == 0) __atomic_fetch_add(st_misc, rp1 - rp0, __ATOMIC_RELAXED);
   __syncthreads();
   const bool staged = st_misc[0] <= kOutStage && NB <= kStageBlocks;
   const int bucket0 = (r >> 4) * NB;
-  int starts0 = 0, starts1 = 0;
+  int starts = 0;
   if (staged) {
     // the walks take the thread's entries eight at a time, loads first (clamped into the
     // row's range) so that eight are in flight
-    if (producer) {
+    if (stager) {
       for (int p0 = rp0 + par; p0 < rp1; p0 += 16) {
         int col[8];
 #pragma unroll
@@ -664,7 +642,7 @@ __global__ void __launch_bounds__(512) grouped_gemm_kernel(const GemmParams P) {
     __syncthreads();
     // exclusive scan of the bucket counts, two per thread
     int c0 = 0, c1 = 0, v = 0;
-    if (producer) {
+    if (stager) {
       c0 = 2 * tid < nbk ? st_fill[2 * tid] : 0;
       c1 = 2 * tid + 1 < nbk ? st_fill[2 * tid + 1] : 0;
       v = c0 + c1;
@@ -676,7 +654,7 @@ __global__ void __launch_bounds__(512) grouped_gemm_kernel(const GemmParams P) {
       if (lane == 63) st_misc[1 + wave] = v;
     }
     __syncthreads();
-    if (producer) {
+    if (stager) {
       int ex = v - c0 - c1;
       for (int w = 0; w < wave; ++w) ex += st_misc[1 + w];
       if (2 * tid < nbk) st_start[2 * tid] = st_fill[2 * tid] = ex;
@@ -684,9 +662,7 @@ __global__ void __launch_bounds__(512) grouped_gemm_kernel(const GemmParams P) {
       if (tid == 255) st_start[nbk] = ex + c0 + c1;
     }
     __syncthreads();
-    if (producer) {
-      // each entry carries its patched weight: the sign bit and block scale of its
-      // position are read here, once per tile
+    if (stager) {
       const uint16_t rs = Mr->row_scales[gr];
       for (int p0 = rp0 + par; p0 < rp1; p0 += 16) {
         int col[8], q[8];
@@ -704,24 +680,22 @@ __global__ void __launch_bounds__(512) grouped_gemm_kernel(const GemmParams P) {
           }
         }
       }
-      // bucket starts of the wavefront's two row groups, lane l: block l (l <= NB)
-      starts0 = lane <= NB ? st_start[wave * NB + lane] : 0;
-      starts1 = lane <= NB ? st_start[(wave + 4) * NB + lane] : 0;
     }
+    // bucket starts of the producer wavefront's row group, lane l: block l (l <= NB)
+    if (producer) starts = lane <= NB ? st_start[wave * NB + lane] : 0;
     __syncthreads();
   }
 
   // ---- accumulators of consumer (wm, wn) = pairs [64 wm, +64) x B rows [64 wn, +64)
-  const int wm = wave & 1, wn = (wave >> 1) & 1;
+  const int wm = wave & 1, wn = (wave >> 1) & 1;   // consumer wavefronts 8..11
   const int ml = lane & 15, lg = lane >> 4;
   v4f acc[4][4];
   if (producer) {
     if (staged) {
-      producer_loop<true>(P, A0, B0, as, b0, b1, NB, tid, acg, st_ent, starts0, starts1, re, ro);
+      producer_loop<true>(P, A0, B0, as, b, NB, tid, acg, st_ent, starts, re, ro);
     } else {
-      item_walk_init(P, e, n0, b0);
-      item_walk_init(P, e, n0, b1);
-      producer_loop<false>(P, A0, B0, as, b0, b1, NB, tid, acg, st_ent, 0, 0, re, ro);
+      item_walk_init(P, e, n0, b);
+      producer_loop<false>(P, A0, B0, as, b, NB, tid, acg, st_ent, 0, re, ro);
     }
   } else {
 #pragma unroll
@@ -807,12 +781,12 @@ hipError_t launch_grouped_gemm(const gale_matrix* table, int gateup, int rows, i
     err = hipFuncSetAttribute((const void*)grouped_gemm_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)kGemmSmem);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(grouped_gemm_kernel<true>, grid, dim3(512), kGemmSmem, s, P);
+    hipLaunchKernelGGL(grouped_gemm_kernel<true>, grid, dim3(kProducerThreads + 256), kGemmSmem, s, P);
   } else {
     err = hipFuncSetAttribute((const void*)grouped_gemm_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)kGemmSmem);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(grouped_gemm_kernel<false>, grid, dim3(512), kGemmSmem, s, P);
+    hipLaunchKernelGGL(grouped_gemm_kernel<false>, grid, dim3(kProducerThreads + 256), kGemmSmem, s, P);
   }
   return hipGetLastError();
 }
