@@ -187,12 +187,14 @@ def sweep_gemv(q, synth, lib, dev, seed, reps: int, warm_s: float):
         rec = q.prepare_activations(xg)
         yg = torch.empty(n, 1, rows, dtype=torch.float16, device=dev)
         flip = [0]
+        stage = q.gale_outlier_stage_flag(sets[0][0].outliers_per_row)
 
         def call():
             t = sets[flip[0]][0]
             flip[0] ^= 1
             rc = lib.gale_expert_gemv(rows, cols, t.ptr(), n, rec.data_ptr(), q.GALE_F16, 0, 1, yg.data_ptr(),
-                                      q.GALE_F16, None, 0, q.GALE_X_PREPARED, torch.cuda.current_stream().cuda_stream)
+                                      q.GALE_F16, None, 0, q.GALE_X_PREPARED | stage,
+                                      torch.cuda.current_stream().cuda_stream)
             if rc:
                 raise RuntimeError(lib.gale_last_error().decode())
 
@@ -211,6 +213,7 @@ def sweep_gemv(q, synth, lib, dev, seed, reps: int, warm_s: float):
         log(f"sweep: [{rows}, {cols}] outliers {frac:.0%} ({bpw:.3f} b/w): {n} matrices in {ms * 1e3:.1f} us -> "
             f"{gbps:.0f} GB/s ({100 * gbps / HBM_PEAK_GBPS:.1f}% of 8 TB/s)")
         res.append({"rows": rows, "cols": cols, "outlier_frac": frac, "bits_per_weight": round(bpw, 4),
+                    "outlier_stage": stage >> q.GALE_OUTLIER_STAGE_SHIFT,
                     "matrices_per_launch": n, "avg_launch_us": round(ms * 1e3, 2), "gbps": round(gbps, 1),
                     "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)})
         del sets, rec, yg, xg
@@ -439,7 +442,7 @@ def main() -> int:
         "bytes_per_token": bytes_per_token,
         "roofline": {"bound": "hbm", "achieved": round(gemv_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gemv_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "kernel": "gemv_kernel<1,4,false,512> (fp4 sign-plane MFMA GEMV)",
+                     "kernel": "gemv_kernel<1,4,false,512,2> (fp4 sign-plane MFMA GEMV)",
                      "launch": f"{n} distinct [2048,4096] matrices (w1, w3 of {n // 2} experts) x 1 token, "
                                f"prepared activations; two disjoint sets alternated",
                      "bytes_per_launch": n * GEMV_UNIT_BYTES, "avg_launch_us": round(ms_gemv * 1e3, 2),

@@ -71,6 +71,13 @@ extern "C" {
  * One-token layer kernel, (gate/up, down) tiles per unit: v = 1: (1, 1); 2: (2, 2); 3: (1, 2);
  * 4: (2, 1); 5: (3, 2); 6: (3, 1).  Results do not depend on it. */
 #define GALE_TILES_SHIFT 8
+/* Tuning knob, bits 14..15: outlier entries that a GEMV wavefront stages per work unit for
+ * its 16 rows.  v = 0: 1024 (64 per row on average, the 1 % budget's 41 fit); 1: 2048;
+ * 2: 4096 (one activation vector per item only; with more, as 1).  Entries past the staged
+ * ones are read from HBM one by one, which is slow; a larger staging takes registers from the
+ * row tiles per unit.  For budgets of 2 to 3 % take 1, from 4 % take 2.  The one-token
+ * layer kernel ignores it.  Results do not depend on it. */
+#define GALE_OUTLIER_STAGE_SHIFT 14
 
 /* ---- limits -------------------------------------------------------------- */
 #define GALE_FWHT_N        1024   /* rotation block ("blocked FWHT-1024") */

@@ -10,5 +10,5 @@ from .binding import (  # noqa: F401
     DescriptorTable, lib, exported_symbols, packed_sizes, check_canonical, pack_host, unpack_host, pack_device,
     pack_matrix, matrix_table, expert_table, debug_unpack_signs, debug_unpack_outliers, fwht1024,
     expert_gemv, expert_ffn, moe_layer_fwd, route_topk, gemv_workspace_bytes, ffn_workspace_bytes,
-    moe_workspace_bytes, gale_tiles_flag, gale_layer_tiles_flag,
+    moe_workspace_bytes, gale_tiles_flag, gale_layer_tiles_flag, GALE_OUTLIER_STAGE_SHIFT, gale_outlier_stage_flag,
 )

@@ -35,6 +35,25 @@ def gale_tiles_flag(r: int) -> int:
     return ((r.bit_length()) & 0xF) << 8
 
 
+GALE_OUTLIER_STAGE_SHIFT = 14
+
+
+def gale_outlier_stage_flag(per_row: float) -> int:
+    """flags bits 14..15 for a mean outlier count per row: the GEMV staging (1024, 2048 or
+    4096 entries per 16-row group) that holds a 16-row group's entries.  Measured on
+    [2048, 4096]: 1 % (41 per row) streams fastest with 1024, 2 and 3 % (82, 123) with 2048,
+    5 % (205) with 4096."""
+    v = 0 if per_row <= 48 else (1 if per_row <= 128 else 2)
+    return v << GALE_OUTLIER_STAGE_SHIFT
+
+
+def _with_stage(flags: int, table: "DescriptorTable") -> int:
+    """flags with the outlier staging of the table's densest matrix, unless the caller set it."""
+    if (flags >> GALE_OUTLIER_STAGE_SHIFT) & 3:
+        return flags
+    return flags | gale_outlier_stage_flag(table.outliers_per_row)
+
+
 def gale_layer_tiles_flag(gate_up: int, down: int) -> int:
     """flags bits 8..11 for the one-token layer kernel: row tiles per gate/up and per down unit."""
     return {(1, 1): 1, (2, 2): 2, (1, 2): 3, (2, 1): 4, (3, 2): 5, (3, 1): 6}[(gate_up, down)] << 8
@@ -249,7 +268,8 @@ def pack_matrix(cm) -> PackedMatrix:
 class DescriptorTable:
     """A device array of gale_matrix or gale_expert descriptors, keeping the matrices alive."""
 
-    def __init__(self, structs: Sequence[ctypes.Structure], keep: Sequence, device):
+    def __init__(self, structs: Sequence[ctypes.Structure], keep: Sequence, device, outliers_per_row: float = 0.0):
+        self.outliers_per_row = outliers_per_row   # mean outliers per row of the densest matrix
         n = len(structs)
         size = ctypes.sizeof(structs[0]) if n else 8
         raw = (ctypes.c_uint8 * (size * max(n, 1)))()
@@ -266,7 +286,8 @@ class DescriptorTable:
 
 def matrix_table(mats: Sequence[PackedMatrix], device=None) -> DescriptorTable:
     device = device or mats[0].signs.device
-    return DescriptorTable([m.descriptor() for m in mats], mats, device)
+    return DescriptorTable([m.descriptor() for m in mats], mats, device,
+                           max((m.nnz / m.rows for m in mats), default=0.0))
 
 
 def expert_table(experts: Sequence[Sequence[PackedMatrix]], device=None) -> DescriptorTable:
@@ -276,7 +297,8 @@ def expert_table(experts: Sequence[Sequence[PackedMatrix]], device=None) -> Desc
         e = gale_expert()
         e.w1, e.w3, e.w2 = w1.descriptor(), w3.descriptor(), w2.descriptor()
         structs.append(e)
-    return DescriptorTable(structs, experts, device)
+    return DescriptorTable(structs, experts, device,
+                           max((m.nnz / m.rows for ex in experts for m in ex), default=0.0))
 
 
 # ----------------------------------------------------------------------------
@@ -353,6 +375,7 @@ def expert_gemv(table: DescriptorTable, rows: int, cols: int, x: torch.Tensor, n
         y = torch.empty(n_mat, n_tok, rows, dtype=y_dtype, device=x.device)
     if ws is None and not prepared:
         ws = _workspace(gemv_workspace_bytes(rows, cols, n_mat, n_tok, x_shared), x.device)
+    flags = _with_stage(flags, table)
     _check("gale_expert_gemv", lib().gale_expert_gemv(rows, cols, table.ptr(), n_mat, x.data_ptr(),
                                                        GALE_F16 if prepared else _dt(x), int(bool(x_shared)), n_tok,
                                                        y.data_ptr(), _dt(y), _ptr(ws), 0 if ws is None else ws.numel(),
@@ -401,6 +424,7 @@ def moe_layer_fwd(table: DescriptorTable, hidden: int, inter: int, logits: torch
         topk_w = torch.empty(n_tok, top_k, dtype=torch.float32, device=x.device)
     if ws is None:
         ws = _workspace(moe_workspace_bytes(n_tok, E, top_k, hidden, inter, flags), x.device)
+    flags = _with_stage(flags, table)
     if select_bias is None and fixed_idx is None:
         _check("gale_moe_layer_fwd", lib().gale_moe_layer_fwd(hidden, inter, table.ptr(), E, logits.data_ptr(), top_k,
                                                                x.data_ptr(), n_tok, y.data_ptr(), topk_idx.data_ptr(),

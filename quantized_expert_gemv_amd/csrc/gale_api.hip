@@ -47,18 +47,32 @@ static int hip_status(const char* fn, hipError_t e) {
   return GALE_OK;
 }
 
+static int stage_ok(int cols, int slots) { return (int64_t)slots * cols * 4 <= 65536 ? 1 : 0; }
+
+// Outlier column chunks staged per wavefront and unit, from flags bits 14..15 (2, 4 or 8;
+// eight only with one vector per item, else four), fewer where the workgroup's staging
+// would not fit the LDS next to its other buffers.
+static int pick_out_chunks(uint32_t flags, int slots, int cols, int gateup) {
+  const int v = (int)((flags >> GALE_OUTLIER_STAGE_SHIFT) & 3);
+  int oc = v == 0 ? 2 : (v == 1 || slots > 1 ? 4 : 8);
+  while (oc > 2 && gemv_smem_bytes(cols, slots, 4, gateup, stage_ok(cols, slots), oc) > kGemvMaxLds) oc >>= 1;
+  return oc;
+}
+
 // Row tiles per unit: at most the chunk count (four lanes per row serve the outliers),
-// at most 3 with four activation vectors (register budget), and small enough that the
-// units cover the GPU at least twice; flags bits 8..11 force a value (1, 2 or 4).  A
-// unit's loads are issued one unit ahead, so wider units keep more bytes in flight per
-// CU: with one or two vectors, four tiles stream ~1.4x faster than two.
-static int pick_tiles(int64_t items, int ntiles, int cols, int slots, uint32_t flags) {
+// at most what the registers hold next to the outlier staging (two chunks: 4, or 3 with
+// four activation vectors; four chunks: 3, or 2 with four vectors; eight chunks: 1), and
+// small enough that the units cover the GPU at least twice; flags bits 8..11 force a value
+// (1, 2 or 4).  A unit's loads are issued one unit ahead, so wider units keep more bytes in
+// flight per CU: with one or two vectors, four tiles stream ~1.4x faster than two.
+static int pick_tiles(int64_t items, int ntiles, int cols, int slots, int out_chunks, uint32_t flags) {
   const int C = cols / 1024;
   int r = 4;
   const int forced = (int)((flags >> GALE_TILES_SHIFT) & 0xF);
   if (forced) r = 1 << (forced - 1);
   if (r > 4) r = 4;
-  if (slots >= 4 && r > 3) r = 3;                // the kernel's register budget
+  const int cap = out_chunks == 8 ? 1 : (out_chunks == 4 ? (slots >= 4 ? 2 : 3) : (slots >= 4 ? 3 : 4));
+  if (r > cap) r = cap;                           // the kernel's register budget
   if (r > C) r = C >= 3 ? 3 : C;                  // three chunks: units of three tiles
   if (r == 3 && forced) r = 2;
   if (!forced) {
@@ -68,7 +82,6 @@ static int pick_tiles(int64_t items, int ntiles, int cols, int slots, uint32_t f
   return r;
 }
 
-static int stage_ok(int cols, int slots) { return (int64_t)slots * cols * 4 <= 65536 ? 1 : 0; }
 
 static int pick_slots(int n_tok) { return n_tok >= 4 ? 4 : (n_tok >= 2 ? 2 : 1); }
 
@@ -359,7 +372,8 @@ extern "C" int gale_expert_gemv(int32_t rows, int32_t cols, const gale_matrix* m
   P.y_stride = rows;
   P.gateup = 0;
   const int ntiles = rows / 16;
-  const int R = pick_tiles(P.n_items, ntiles, cols, slots, flags);
+  P.out_chunks = pick_out_chunks(flags, slots, cols, 0);
+  const int R = pick_tiles(P.n_items, ntiles, cols, slots, P.out_chunks, flags);
   P.row_groups = (ntiles + R - 1) / R;
   P.stage_xt = stage_ok(cols, slots);
   return hip_status(fn, launch_gemv(P, slots, R, (int64_t)P.n_items * P.row_groups, stream));
@@ -403,7 +417,8 @@ static int run_gemv_phase(const char* fn, const gale_matrix* table, int stride, 
   P.gateup = gateup;
   const int ntiles = rows / 16;
   const int64_t bound = implicit ? n_items : item_bound;
-  const int R = pick_tiles(bound, ntiles, cols, slots, flags);
+  P.out_chunks = pick_out_chunks(flags, slots, cols, gateup);
+  const int R = pick_tiles(bound, ntiles, cols, slots, P.out_chunks, flags);
   P.row_groups = (ntiles + R - 1) / R;
   P.stage_xt = stage_ok(cols, slots);
   return hip_status(fn, launch_gemv(P, slots, R, bound * P.row_groups, s));

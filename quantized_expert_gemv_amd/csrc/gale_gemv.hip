@@ -161,9 +161,9 @@ __device__ __forceinline__ int outlier_row(const GemvParams& P, const Geo& G, in
 
 // Issue the loads of unit v (descriptors dv) into b.  rp0/rp1 of v must already be in
 // b (from the previous unit's np0/np1).  Also fetches the CSR offsets of unit vn.
-template <int R>
+template <int R, int OC>
 __device__ __forceinline__ void issue_unit(const GemvParams& P, const Geo& G, const Pos& v, const Desc& dv,
-                                           const Pos& vn, const Desc& dn, UnitBuf<R>& b) {
+                                           const Pos& vn, const Desc& dn, UnitBuf<R, OC>& b) {
   const int t0 = v.rg * R;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -190,13 +190,13 @@ __device__ __forceinline__ void issue_unit(const GemvParams& P, const Geo& G, co
   b.ocf = cf;
   b.ovf = vf;
 #pragma unroll
-  for (int k = 0; k < kColChunks; ++k) {
+  for (int k = 0; k < OC; ++k) {
     int ch = cf + 64 * k + G.lane;
     ch = ch < cl ? ch : cl;
     b.oc[k] = ld16(dv.ocols, (uint32_t)ch * 16u);
   }
 #pragma unroll
-  for (int k = 0; k < kValChunks; ++k) {
+  for (int k = 0; k < val_chunks(OC); ++k) {
     int ch = vf + 64 * k + G.lane;
     ch = ch < vl ? ch : vl;
     b.ov[k] = ld16(dv.ovals, (uint32_t)ch * 16u);
@@ -248,9 +248,9 @@ __device__ __forceinline__ void stage_activation(const GemvParams& P, const Geo&
   }
 }
 
-template <int NS, int R, bool GATEUP>
+template <int NS, int R, bool GATEUP, int OC>
 __device__ __forceinline__ void process_unit(const GemvParams& P, const Geo& G, const Pos& cur_pos, Item& it,
-                                             UnitBuf<R>& cur, UnitBuf<R>& nxt, const Pos& p1, const Desc& d1,
+                                             UnitBuf<R, OC>& cur, UnitBuf<R, OC>& nxt, const Pos& p1, const Desc& d1,
                                              const Pos& p2, const Desc& d2, int& act_item, Act& act,
                                              lds_f32* red, lds_f32* ored, lds_f32* xt, lds_u8* wout) {
   constexpr int HALVES = GATEUP ? 2 : 1;
@@ -273,15 +273,15 @@ __device__ __forceinline__ void process_unit(const GemvParams& P, const Geo& G, 
   {
     lds_v4* oc = reinterpret_cast<lds_v4*>(wout);
 #pragma unroll
-    for (int k = 0; k < kColChunks; ++k) oc[64 * k + G.lane] = to_v4(cur.oc[k]);
+    for (int k = 0; k < OC; ++k) oc[64 * k + G.lane] = to_v4(cur.oc[k]);
 #pragma unroll
-    for (int k = 0; k < kValChunks; ++k) oc[64 * (kColChunks + k) + G.lane] = to_v4(cur.ov[k]);
+    for (int k = 0; k < val_chunks(OC); ++k) oc[64 * (OC + k) + G.lane] = to_v4(cur.ov[k]);
   }
 
   // 3. issue unit u+1 (and the CSR offsets of u+2) behind this unit's arithmetic
   nxt.rp0 = cur.np0;
   nxt.rp1 = cur.np1;
-  issue_unit<R>(P, G, p1, d1, p2, d2, nxt);
+  issue_unit<R, OC>(P, G, p1, d1, p2, d2, nxt);
 
   // 4. sign pass over the wave's R tiles
 #pragma unroll
@@ -300,14 +300,14 @@ __device__ __forceinline__ void process_unit(const GemvParams& P, const Geo& G, 
     bool valid;
     (void)outlier_row<R>(P, G, rg, &valid);
     const lds_u16* lc = reinterpret_cast<const lds_u16*>(wout);
-    const lds_u8* lv = wout + 64 * 16 * kColChunks;
+    const lds_u8* lv = wout + 64 * 16 * OC;
     float o[NS];
 #pragma unroll
     for (int i = 0; i < NS; ++i) o[i] = 0.f;
     const int cbase = 8 * cur.ocf, vbase = 16 * cur.ovf;
     const int p_begin = cur.rp0 + G.sub, p_end = valid ? cur.rp1 : p_begin;
     // entries p < p_cap are in the staged chunks
-    const int p_cap = min(cbase + 64 * 8 * kColChunks, 2 * (vbase + 64 * 16 * kValChunks));
+    const int p_cap = min(cbase + 64 * 8 * OC, 2 * (vbase + 64 * 16 * val_chunks(OC)));
     const int p_mid = min(p_end, p_cap);
     int p = p_begin;
     if (P.stage_xt) {
@@ -431,7 +431,7 @@ __device__ __forceinline__ void process_unit(const GemvParams& P, const Geo& G, 
 // NS: activation vectors per item (1, 2 or 4); R: row tiles per unit (R <= chunks);
 // GATEUP: two matrices (w1, w3) and a SwiGLU epilogue.  blockDim.x = 64 * C * (GATEUP ? 2 : 1)
 // <= MAXT: 512 for up to eight wavefronts, 1024 (half the registers per lane) beyond.
-template <int NS, int R, bool GATEUP, int MAXT>
+template <int NS, int R, bool GATEUP, int MAXT, int OC>
 __global__ void __launch_bounds__(MAXT) gemv_kernel(const GemvParams P) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int HALVES = GATEUP ? 2 : 1;
@@ -467,8 +467,8 @@ __global__ void __launch_bounds__(MAXT) gemv_kernel(const GemvParams P) {
   lds_f32* red0 = reinterpret_cast<lds_f32*>(base);            // [2][HALVES][C][RR][NS]
   lds_f32* ored0 = red0 + 2 * red_n;                            // [2][HALVES][RR][NS]
   lds_u8* wbase = reinterpret_cast<lds_u8*>(ored0 + 2 * ored_n);
-  lds_u8* wout = wbase + G.wave * kWaveOutBytes;               // this wave's outlier staging slice
-  lds_f32* xt = reinterpret_cast<lds_f32*>(wbase + (size_t)HALVES * G.C * kWaveOutBytes);   // [NS][K] when staged
+  lds_u8* wout = wbase + G.wave * wave_out_bytes(OC);          // this wave's outlier staging slice
+  lds_f32* xt = reinterpret_cast<lds_f32*>(wbase + (size_t)HALVES * G.C * wave_out_bytes(OC));   // [NS][K] when staged
 
   const int n_items = P.implicit_items ? P.n_items : uni(*as_const(P.n_items_dev));
   const int total = n_items * G.RG;
@@ -476,7 +476,7 @@ __global__ void __launch_bounds__(MAXT) gemv_kernel(const GemvParams P) {
   const int u1 = uni((int)((int64_t)total * (blockIdx.x + 1) / gridDim.x));
   if (u0 >= u1) return;
 
-  UnitBuf<R> b0, b1;
+  UnitBuf<R, OC> b0, b1;
   Act act;
   int act_item;
   Item it;
@@ -498,7 +498,7 @@ __global__ void __launch_bounds__(MAXT) gemv_kernel(const GemvParams P) {
     const int n = outlier_row<R>(P, G, pc.rg, &ok);
     b0.rp0 = d0.rptr[n];
     b0.rp1 = d0.rptr[n + (n < P.rows ? 1 : 0)];
-    issue_unit<R>(P, G, pc, d0, p1, d1, b0);
+    issue_unit<R, OC>(P, G, pc, d0, p1, d1, b0);
     stage_activation<NS>(P, G, it, xt);
     __syncthreads();
     block_sums<NS>(act);
@@ -507,14 +507,14 @@ __global__ void __launch_bounds__(MAXT) gemv_kernel(const GemvParams P) {
     d2 = p2.item == p1.item ? d1 : load_desc(P, G, item_mat(P, p2.item));
   }
   for (;;) {
-    process_unit<NS, R, GATEUP>(P, G, pc, it, b0, b1, p1, d1, p2, d2, act_item, act, red0, ored0, xt, wout);
+    process_unit<NS, R, GATEUP, OC>(P, G, pc, it, b0, b1, p1, d1, p2, d2, act_item, act, red0, ored0, xt, wout);
     if (pc.u + 1 >= u1) break;
     pc = p1;
     p1 = p2;
     d1 = d2;
     p2 = pos_next(p2, u1, G.RG);
     d2 = p2.item == p1.item ? d1 : load_desc(P, G, item_mat(P, p2.item));
-    process_unit<NS, R, GATEUP>(P, G, pc, it, b1, b0, p1, d1, p2, d2, act_item, act, red0 + red_n,
+    process_unit<NS, R, GATEUP, OC>(P, G, pc, it, b1, b0, p1, d1, p2, d2, act_item, act, red0 + red_n,
                                 ored0 + ored_n, xt, wout);
     if (pc.u + 1 >= u1) break;
     pc = p1;
@@ -525,11 +525,11 @@ __global__ void __launch_bounds__(MAXT) gemv_kernel(const GemvParams P) {
   }
 }
 
-size_t gemv_smem_bytes(int cols, int slots, int tiles, int gateup, int stage_xt) {
+size_t gemv_smem_bytes(int cols, int slots, int tiles, int gateup, int stage_xt, int out_chunks) {
   const int halves = gateup ? 2 : 1;
   const int C = cols >> 10;
   const size_t f = 2 * ((size_t)halves * C * tiles * 16 * slots + (size_t)halves * tiles * 16 * slots);
-  size_t b = f * 4 + (size_t)halves * C * kWaveOutBytes;
+  size_t b = f * 4 + (size_t)halves * C * (size_t)(64 * 16 * (out_chunks + out_chunks / 4 + 1));
   if (stage_xt) b += (size_t)slots * cols * 4;
   return b;
 }
@@ -546,53 +546,72 @@ int device_cu_count() {
   return cached[dev];
 }
 
-template <int NS, int R, bool G, int MAXT>
+template <int NS, int R, bool G, int MAXT, int OC>
 static hipError_t launch_b(const GemvParams& p, int block, int64_t max_units, hipStream_t s) {
-  const size_t smem = gemv_smem_bytes(p.cols, NS, R, G, p.stage_xt);
+  const size_t smem = gemv_smem_bytes(p.cols, NS, R, G, p.stage_xt, OC);
   int occ = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemv_kernel<NS, R, G, MAXT>, block, smem) != hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemv_kernel<NS, R, G, MAXT, OC>, block, smem) != hipSuccess ||
       occ < 1)
     occ = 1;
   const int64_t grid = std::min<int64_t>(max_units, (int64_t)device_cu_count() * occ);
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemv_kernel<NS, R, G, MAXT>), dim3((unsigned)grid), dim3(block), smem, s, p);
+  hipLaunchKernelGGL((gemv_kernel<NS, R, G, MAXT, OC>), dim3((unsigned)grid), dim3(block), smem, s, p);
   return hipGetLastError();
 }
 
-template <int NS, int R, bool G>
+template <int NS, int R, bool G, int OC>
 static hipError_t launch_t(const GemvParams& p, int64_t max_units, hipStream_t s) {
   const int block = 64 * (p.cols >> 10) * (G ? 2 : 1);
   if (block > kGemvMaxThreads) return hipErrorInvalidConfiguration;   // the host checks first
-  if (block <= 512) return launch_b<NS, R, G, 512>(p, block, max_units, s);
-  return launch_b<NS, R, G, 1024>(p, block, max_units, s);
+  if (block <= 512) return launch_b<NS, R, G, 512, OC>(p, block, max_units, s);
+  return launch_b<NS, R, G, 1024, OC>(p, block, max_units, s);
 }
 
-template <int NS, bool G>
+// Row tiles per unit by outlier staging.  Two chunks: four tiles for items of up to two
+// vectors, three for four vectors (four would spill).  Four chunks (twice the staged
+// entries): three tiles for up to two vectors, two for four.  Eight chunks: one tile, one
+// vector.  The host's row groups are counted with the same tile count, so no other value
+// is taken.
+template <int NS, bool G, int OC>
 static hipError_t launch_r(const GemvParams& p, int tiles, int64_t max_units, hipStream_t s) {
-  // four tiles per unit for items of up to two vectors, three for four vectors (four would
-  // spill); the host's row groups are counted with the same tile count, so no other value
-  // is taken
-  switch (tiles) {
-    case 1: return launch_t<NS, 1, G>(p, max_units, s);
-    case 2: return launch_t<NS, 2, G>(p, max_units, s);
-    case 3: return launch_t<NS, 3, G>(p, max_units, s);
-    case 4:
-      if constexpr (NS <= 2) return launch_t<NS, 4, G>(p, max_units, s);
-      else return hipErrorInvalidValue;
-    default: return hipErrorInvalidValue;
+  if constexpr (OC == 8) {
+    if (NS == 1 && tiles == 1) return launch_t<1, 1, G, 8>(p, max_units, s);
+    return hipErrorInvalidValue;
+  } else {
+    constexpr int kMax = OC == 2 ? (NS <= 2 ? 4 : 3) : (NS <= 2 ? 3 : 2);
+    switch (tiles) {
+      case 1: return launch_t<NS, 1, G, OC>(p, max_units, s);
+      case 2: return launch_t<NS, 2, G, OC>(p, max_units, s);
+      case 3:
+        if constexpr (kMax >= 3) return launch_t<NS, 3, G, OC>(p, max_units, s);
+        else return hipErrorInvalidValue;
+      case 4:
+        if constexpr (kMax >= 4) return launch_t<NS, 4, G, OC>(p, max_units, s);
+        else return hipErrorInvalidValue;
+      default: return hipErrorInvalidValue;
+    }
   }
+}
+
+template <bool G, int OC>
+static hipError_t launch_s(const GemvParams& p, int slots, int tiles, int64_t max_units, hipStream_t s) {
+  if (slots == 1) return launch_r<1, G, OC>(p, tiles, max_units, s);
+  if (slots == 2) return launch_r<2, G, OC>(p, tiles, max_units, s);
+  return launch_r<4, G, OC>(p, tiles, max_units, s);
+}
+
+template <bool G>
+static hipError_t launch_o(const GemvParams& p, int slots, int tiles, int64_t max_units, hipStream_t s) {
+  if (p.out_chunks == 8) return launch_s<G, 8>(p, slots, tiles, max_units, s);
+  if (p.out_chunks == 4) return launch_s<G, 4>(p, slots, tiles, max_units, s);
+  if (p.out_chunks == 2) return launch_s<G, 2>(p, slots, tiles, max_units, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemv(const GemvParams& p, int slots, int tiles_per_unit, int64_t max_units, hipStream_t s) {
   if (max_units <= 0) return hipSuccess;
-  if (p.gateup) {
-    if (slots == 1) return launch_r<1, true>(p, tiles_per_unit, max_units, s);
-    if (slots == 2) return launch_r<2, true>(p, tiles_per_unit, max_units, s);
-    return launch_r<4, true>(p, tiles_per_unit, max_units, s);
-  }
-  if (slots == 1) return launch_r<1, false>(p, tiles_per_unit, max_units, s);
-  if (slots == 2) return launch_r<2, false>(p, tiles_per_unit, max_units, s);
-  return launch_r<4, false>(p, tiles_per_unit, max_units, s);
+  if (p.gateup) return launch_o<true>(p, slots, tiles_per_unit, max_units, s);
+  return launch_o<false>(p, slots, tiles_per_unit, max_units, s);
 }
 
 }  // namespace gale

@@ -14,6 +14,9 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 constexpr int kColChunks = 2;    // 16-byte chunks of outlier columns per lane (1024 entries per wave)
 constexpr int kValChunks = 1;    // 16-byte chunks of outlier values per lane (2048 entries per wave)
 constexpr int kWaveOutBytes = 64 * 16 * (kColChunks + kValChunks);
+// The same for a staging of OC column chunks (OC * 512 entries per wave)
+constexpr int val_chunks(int OC) { return OC / 4 + 1; }   // 2048 entries each, one more for the offset
+constexpr int wave_out_bytes(int OC) { return 64 * 16 * (OC + val_chunks(OC)); }
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
   __half_raw r;
@@ -78,13 +81,13 @@ __device__ __forceinline__ const __attribute__((address_space(4))) T* as_const(c
   return (const __attribute__((address_space(4))) T*)(p);
 }
 
-// Everything unit u needs from HBM, issued during unit u-1.
-template <int R>
+// Everything unit u needs from HBM, issued during unit u-1.  OC: outlier column chunks.
+template <int R, int OC = kColChunks>
 struct UnitBuf {
   uint32_t sw[R][8];     // sign words of the wave's R tiles (its chunk)
   uint32_t sc[R][4];     // 8 fp16 block scales of the lane's row, per tile
-  uint4 oc[kColChunks];  // outlier column chunks of the wave's 16 rows
-  uint4 ov[kValChunks];  // outlier value chunks
+  uint4 oc[OC];          // outlier column chunks of the wave's 16 rows
+  uint4 ov[val_chunks(OC)];  // outlier value chunks
   int ocf, ovf;          // first chunk index of each (wave-uniform)
   int rp0, rp1;          // CSR range of this thread's row in this unit
   int np0, np1;          // CSR range of this thread's row in the next unit

@@ -96,6 +96,7 @@ struct GemvParams {
   int gateup;                // SwiGLU epilogue (y = fp32 h)
   int row_groups;            // units per item along rows
   int stage_xt;              // copy x~ into LDS for the outlier gathers
+  int out_chunks;            // outlier column chunks staged per wavefront and unit (2, 4 or 8)
 };
 
 // launches (return hipError_t of the launch)
@@ -108,7 +109,8 @@ hipError_t launch_fwht(const void* x, void* y, int64_t n_vec, int len, int in_dt
 // threads of a GEMV workgroup: 64 per 1024-column chunk of each matrix
 constexpr int kGemvMaxThreads = 1024;
 hipError_t launch_gemv(const GemvParams& p, int slots, int tiles_per_unit, int64_t max_units, hipStream_t s);
-size_t gemv_smem_bytes(int cols, int slots, int tiles, int gateup, int stage_xt);
+size_t gemv_smem_bytes(int cols, int slots, int tiles, int gateup, int stage_xt, int out_chunks);
+constexpr size_t kGemvMaxLds = 160 * 1024;   // LDS per workgroup on gfx950
 int device_cu_count();
 hipError_t launch_pack(int rows, int cols, int n_mat, const uint32_t* cs, const uint16_t* csc,
                        uint32_t* ds, uint16_t* dsc, hipStream_t s);

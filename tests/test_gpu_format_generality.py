@@ -61,6 +61,24 @@ def test_gemv_outlier_budgets(q, frac):
     assert err <= 1e-4
 
 
+@pytest.mark.parametrize("frac", [0.01, 0.03, 0.05])
+def test_gemv_outlier_stagings(q, frac):
+    # each outlier staging (1024, 2048, 4096 entries per 16-row group, with its own row tiles
+    # per unit; entries past the staging read from HBM) gives the same bits, and the oracle's
+    seed = config_seed(28)
+    # 16 matrices: units of four row tiles with the smallest staging, three with 2048 entries
+    mats = gen_matrices(seed, [(int(frac * 100), i) for i in range(16)], 2048, 4096, outlier_frac=frac, device=DEV)
+    x = gen_x(seed, (1,), 1, 4096, device=DEV)
+    tab = q.matrix_table([q.pack_matrix(m) for m in mats])
+    ys = [q.expert_gemv(tab, 2048, 4096, x, x_shared=True, y_dtype=torch.float32, flags=v << q.GALE_OUTLIER_STAGE_SHIFT)
+          for v in (0, 1, 2)]
+    assert torch.equal(ys[0], ys[1]) and torch.equal(ys[0], ys[2])
+    for i in (0, 15):
+        err = O.rel_l2(np_of(ys[0][i]), O.gemv(mats[i].numpy(), x.cpu().numpy())).max()
+        print(f"gemv outliers {frac:.0%} matrix {i}, three stagings: rel-L2 {err:.3e}")
+        assert err <= 1e-4
+
+
 @pytest.mark.parametrize("frac", [0.02, 0.05])
 def test_moe_outlier_budgets_decode_and_grouped(q, frac):
     # 8 experts at the budget; decode (one launch), the grouped path with every expert on
