@@ -61,7 +61,7 @@ static int pick_out_chunks(uint32_t flags, int slots, int cols, int gateup) {
 
 // Row tiles per unit: at most the chunk count (four lanes per row serve the outliers),
 // at most what the registers hold next to the outlier staging (two chunks: 4, or 3 with
-// four activation vectors; four chunks: 3, or 2 with four vectors; eight chunks: 1), and
+// four activation vectors; four chunks: 3, or 2 with four vectors; eight chunks: 2), and
 // small enough that the units cover the GPU at least twice; flags bits 8..11 force a value
 // (1, 2 or 4).  A unit's loads are issued one unit ahead, so wider units keep more bytes in
 // flight per CU: with one or two vectors, four tiles stream ~1.4x faster than two.
@@ -71,7 +71,7 @@ static int pick_tiles(int64_t items, int ntiles, int cols, int slots, int out_ch
   const int forced = (int)((flags >> GALE_TILES_SHIFT) & 0xF);
   if (forced) r = 1 << (forced - 1);
   if (r > 4) r = 4;
-  const int cap = out_chunks == 8 ? 1 : (out_chunks == 4 ? (slots >= 4 ? 2 : 3) : (slots >= 4 ? 3 : 4));
+  const int cap = out_chunks == 8 ? 2 : (out_chunks == 4 ? (slots >= 4 ? 2 : 3) : (slots >= 4 ? 3 : 4));
   if (r > cap) r = cap;                           // the kernel's register budget
   if (r > C) r = C >= 3 ? 3 : C;                  // three chunks: units of three tiles
   if (r == 3 && forced) r = 2;
