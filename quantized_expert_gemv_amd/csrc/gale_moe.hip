@@ -43,7 +43,9 @@ __device__ __forceinline__ void route_small_body(const RouteIn& rin, int T, int 
                                                  int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
                                                  WorkItem* __restrict__ items, int32_t* __restrict__ n_items) {
   __shared__ int32_t s_idx[GALE_MAX_DECODE_TOKENS * GALE_MAX_TOPK];
+  __shared__ int32_t s_pairs[GALE_MAX_DECODE_TOKENS * GALE_MAX_TOPK];   // pairs grouped by expert
   __shared__ int32_t s_cnt[GALE_MAX_EXPERTS];
+  __shared__ int32_t s_fill[GALE_MAX_EXPERTS];
   __shared__ int32_t s_off[GALE_MAX_EXPERTS + 1];
   __shared__ int32_t s_ioff[GALE_MAX_EXPERTS + 1];
   __shared__ int s_wave[16];
@@ -68,7 +70,7 @@ __device__ __forceinline__ void route_small_body(const RouteIn& rin, int T, int 
     int tot_p = 0, tot_i = 0;
     const int op = block_exclusive_scan(c, s_wave, &tot_p);
     const int oi = block_exclusive_scan(ni, s_wave, &tot_i);
-    if (tid < E) { s_off[tid] = op; s_ioff[tid] = oi; }
+    if (tid < E) { s_off[tid] = op; s_fill[tid] = op; s_ioff[tid] = oi; }
     if (tid == 0) {
       s_off[E] = tot_p;
       s_ioff[E] = tot_i;
@@ -76,21 +78,34 @@ __device__ __forceinline__ void route_small_body(const RouteIn& rin, int T, int 
     }
   }
   __syncthreads();
+  // each pair into its expert's range, in any order
+  for (int p = tid; p < P; p += blockDim.x) s_pairs[atomicAdd(&s_fill[s_idx[p]], 1)] = p;
+  __syncthreads();
   if (offsets)
     for (int e = tid; e <= E; e += blockDim.x) offsets[e] = s_off[e];
-  // stable scatter: the thread of expert e walks the pairs in order
+  // stable order: the thread of expert e sorts its few pairs by index (insertion sort),
+  // then writes them and its work items
   for (int e = tid; e < E; e += blockDim.x) {
-    if (s_cnt[e] == 0) continue;
-    int pos = s_off[e];
+    const int c = s_cnt[e];
+    if (c == 0) continue;
+    const int base = s_off[e];
+    for (int i = 1; i < c; ++i) {
+      const int v = s_pairs[base + i];
+      int j = i - 1;
+      while (j >= 0 && s_pairs[base + j] > v) {
+        s_pairs[base + j + 1] = s_pairs[base + j];
+        --j;
+      }
+      s_pairs[base + j + 1] = v;
+    }
     int it = s_ioff[e], slot = 0;
     WorkItem cur;
     cur.expert = e;
     cur.n_slots = 0;
     cur.pad[0] = cur.pad[1] = 0;
-    for (int p = 0; p < P; ++p) {
-      if (s_idx[p] != e) continue;
-      if (perm) perm[pos] = p;
-      ++pos;
+    for (int i = 0; i < c; ++i) {
+      const int p = s_pairs[base + i];
+      if (perm) perm[base + i] = p;
       if (!items) continue;
       cur.pair[0] = slot == 0 ? p : cur.pair[0];
       cur.pair[1] = slot == 1 ? p : cur.pair[1];
