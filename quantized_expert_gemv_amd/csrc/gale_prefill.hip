@@ -452,30 +452,33 @@ __device__ __forceinline__ void patch_rest(const Patch pt, lds_b* Bt, const lds_
   }
 }
 
-// The 16 products of one 128-column block for one wavefront: four K-steps of 32, each
-// reading four B and four A fragments (16 bytes per lane) from LDS.  Fragments of pairs
-// past the tile's end run too (their A rows repeat the first pair; nothing stores them):
-// without branches, the products and the next block's stores form one scheduling region.
+// The products of one 128-column block for one wavefront: four K-steps of 32, each
+// reading four B and NF A fragments (16 bytes per lane) from LDS.  NF is the number of
+// 16-pair fragments of the wave's 64 pairs that hold tile pairs (the last tile of an expert
+// is partly empty); the others are neither read nor multiplied.  The count is uniform per
+// wavefront, so the products run without branches.
+template <int NF>
 __device__ __forceinline__ void mfma_frags(v8h (&af)[4], v8h (&bf)[4], const lds_b* At, const lds_b* Bt, int wm,
                                            int wn, int ml, int goff) {
 #pragma unroll
   for (int nf = 0; nf < 4; ++nf)
     bf[nf] = as_v8h(*reinterpret_cast<const lds_q*>(Bt + (64 * wn + 16 * nf + ml) * kRowBytes + goff));
 #pragma unroll
-  for (int f = 0; f < 4; ++f)
+  for (int f = 0; f < NF; ++f)
     af[f] = as_v8h(*reinterpret_cast<const lds_q*>(At + (64 * wm + 16 * f + ml) * kRowBytes + goff));
 }
 
 // The fragments of K-step ee + 1 are read while the products of step ee run.
+template <int NF>
 __device__ __forceinline__ void mfma_block(v4f (&acc)[4][4], const lds_b* At, const lds_b* Bt, int wm, int wn,
                                            int ml, int lg) {
   v8h af[2][4], bf[2][4];
-  mfma_frags(af[0], bf[0], At, Bt, wm, wn, ml, 16 * group_of(lg, 0));
+  mfma_frags<NF>(af[0], bf[0], At, Bt, wm, wn, ml, 16 * group_of(lg, 0));
 #pragma unroll
   for (int ee = 0; ee < 4; ++ee) {
-    if (ee < 3) mfma_frags(af[(ee + 1) & 1], bf[(ee + 1) & 1], At, Bt, wm, wn, ml, 16 * group_of(lg, ee + 1));
+    if (ee < 3) mfma_frags<NF>(af[(ee + 1) & 1], bf[(ee + 1) & 1], At, Bt, wm, wn, ml, 16 * group_of(lg, ee + 1));
 #pragma unroll
-    for (int f = 0; f < 4; ++f)
+    for (int f = 0; f < NF; ++f)
 #pragma unroll
       for (int nf = 0; nf < 4; ++nf)
         acc[f][nf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[ee & 1][f], bf[ee & 1][nf], acc[f][nf], 0, 0, 0);
@@ -537,15 +540,16 @@ __device__ __forceinline__ void producer_loop(const GemmParams& P, lds_b* A0, ld
 }
 
 // Consumers (wavefronts 8..11): the products of each block, alternating buffers.
+template <int NF>
 __device__ __forceinline__ void consumer_loop(v4f (&acc)[4][4], const lds_b* A0, const lds_b* B0, int NB, int wm,
                                               int wn, int ml, int lg) {
   const lds_b* const A1 = A0 + kTileBytes;
   const lds_b* const B1 = B0 + kTileBytes;
   __syncthreads();
   for (int bd = 0; bd < NB; bd += 2) {
-    mfma_block(acc, A0, B0, wm, wn, ml, lg);
+    if (NF > 0) mfma_block<NF>(acc, A0, B0, wm, wn, ml, lg);
     __syncthreads();
-    mfma_block(acc, A1, B1, wm, wn, ml, lg);
+    if (NF > 0) mfma_block<NF>(acc, A1, B1, wm, wn, ml, lg);
     __syncthreads();
   }
 }
@@ -702,7 +706,15 @@ __global__ void __launch_bounds__(kProducerThreads + 256) grouped_gemm_kernel(co
     for (int f = 0; f < 4; ++f)
 #pragma unroll
       for (int nf = 0; nf < 4; ++nf) acc[f][nf] = v4f{0.f, 0.f, 0.f, 0.f};
-    consumer_loop(acc, A0, B0, NB, wm, wn, ml, lg);
+    // 16-pair fragments of this wave's 64 pairs that hold tile pairs
+    const int nfrag = __builtin_amdgcn_readfirstlane(max(0, min(4, (valid - 64 * wm + 15) >> 4)));
+    switch (nfrag) {
+      case 4: consumer_loop<4>(acc, A0, B0, NB, wm, wn, ml, lg); break;
+      case 3: consumer_loop<3>(acc, A0, B0, NB, wm, wn, ml, lg); break;
+      case 2: consumer_loop<2>(acc, A0, B0, NB, wm, wn, ml, lg); break;
+      case 1: consumer_loop<1>(acc, A0, B0, NB, wm, wn, ml, lg); break;
+      default: consumer_loop<0>(acc, A0, B0, NB, wm, wn, ml, lg); break;
+    }
   }
 
   // ---- epilogue (consumers).  Fragment layout: lane l, register i -> pair 16 f + 4 (l / 16)
