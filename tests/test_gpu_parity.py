@@ -358,6 +358,34 @@ def test_moe_routing_variants(q, layer, variant, T, flags):
     assert err <= REL_L2_BAR
 
 
+def test_moe_grouped_gemm_partial_tiles(q, layer):
+    """Experts whose pair counts end a tile at every fragment boundary (1, 15, 16, 17, 63, 64,
+    65, 127, 128, 129 pairs; fixed experts, one per token): the tile GEMM runs only the
+    16-pair fragments that hold pairs.  Against the GEMV items and the oracle."""
+    seed, canon, tab = layer
+    counts = [1, 15, 16, 17, 63, 64, 65, 127, 128, 129]
+    exps = [3 + 7 * i for i in range(len(counts))]
+    rng = np.random.default_rng(77)
+    fixed_np = np.concatenate([np.full(c, e, np.int32) for c, e in zip(counts, exps)])
+    rng.shuffle(fixed_np)
+    T = fixed_np.size
+    fixed_np = fixed_np.reshape(T, 1)
+    x = gen_x(seed, (5000,), T, 4096, device=DEV)
+    lg = gen_logits_normal(seed, (5000,), T, 256, device=DEV)
+    kw = {"fixed_idx": torch.from_numpy(fixed_np).to(DEV)}
+    yg, idx, _ = q.moe_layer_fwd(tab, 4096, 2048, lg, x, top_k=1, flags=q.GALE_PATH_GROUPED | q.GALE_GROUPED_GEMM, **kw)
+    yi, _, _ = q.moe_layer_fwd(tab, 4096, 2048, lg, x, top_k=1, flags=q.GALE_PATH_GROUPED | q.GALE_GROUPED_ITEMS, **kw)
+    assert np.array_equal(idx.cpu().numpy(), fixed_np)
+    e_gi = O.rel_l2(np_of(yg), np_of(yi)).max()
+    # the last token of each expert's pairs (in token order: the tile's last valid row)
+    sample = sorted(int(np.nonzero(fixed_np[:, 0] == e)[0][-1]) for e in exps)
+    expert_of = lambda e: tuple(m.numpy() for m in canon[e])  # noqa: E731
+    yref, _, _ = O.moe(expert_of, lg.cpu().numpy()[sample], x.cpu().numpy()[sample], k=1, fixed_idx=fixed_np[sample])
+    e_or = O.rel_l2(np_of(yg[sample]), yref).max()
+    print(f"grouped GEMM partial tiles: vs items {e_gi:.3e}, vs oracle {e_or:.3e}")
+    assert max(e_gi, e_or) <= REL_L2_BAR
+
+
 def test_moe_grouped_items_equal_decode_bitwise(q, layer):
     # the grouped path's GEMV work items compute each token independently, so on a
     # decode-sized batch they must reproduce the decode path bit for bit
