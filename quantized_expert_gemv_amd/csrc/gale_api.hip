@@ -532,6 +532,16 @@ static int moe_layer(const char* fn, int32_t hidden, int32_t inter, const gale_e
   const int max_tiles = use_gemm ? (int)moe_tile_bound(n_tok, n_experts, top_k) : 0;
   // hybrid: experts with at least kGemmMinPairs pairs run as GEMM tiles, the rest as items
   const int split = path == kGroupedHybrid ? kGemmMinPairs : (path == kGroupedGemm ? 1 : INT_MAX);
+  // hybrid: each side rotates only the tokens and pairs it reads
+  VecFilter tok_items, tok_gemm, pair_items, pair_gemm;
+  if (path == kGroupedHybrid) {
+    tok_items.idx = tok_gemm.idx = pair_items.idx = pair_gemm.idx = idx;
+    tok_items.offsets = tok_gemm.offsets = pair_items.offsets = pair_gemm.offsets = offsets;
+    tok_items.top_k = tok_gemm.top_k = top_k;
+    tok_items.per_token = tok_gemm.per_token = 1;
+    tok_items.split = tok_gemm.split = pair_items.split = pair_gemm.split = split;
+    tok_items.items_side = pair_items.items_side = 1;
+  }
   if (path == kDecode && n_tok == 1 && !(flags & GALE_DECODE_STAGED) && decode_layer_supported(hidden, inter)) {
     // one launch for the whole layer; the counters live in the workspace
     // tiles per unit of (gate/up, down), as decimal digits; see GALE_TILES_SHIFT
@@ -549,13 +559,13 @@ static int moe_layer(const char* fn, int32_t hidden, int32_t inter, const gale_e
     if (use_items) {
       st = hip_status(fn, launch_build_items(offsets, perm, n_experts, slots, split, items, n_items, stream));
       if (st) return st;
-      st = hip_status(fn, launch_prep(x, GALE_F16, hidden, n_tok, hidden, 0, ra_x, ra_bytes(hidden), stream));
+      st = hip_status(fn, launch_prep(x, GALE_F16, hidden, n_tok, hidden, 0, ra_x, ra_bytes(hidden), stream, tok_items));
       if (st) return st;
     }
     if (use_gemm) {
       st = hip_status(fn, launch_build_tiles(offsets, n_experts, split, tiles, n_tiles, stream));
       if (st) return st;
-      st = hip_status(fn, launch_rotate_f16(x, GALE_F16, n_tok, hidden, xt16, stream));
+      st = hip_status(fn, launch_rotate_f16(x, GALE_F16, n_tok, hidden, xt16, stream, tok_gemm));
       if (st) return st;
     }
   }
@@ -573,14 +583,14 @@ static int moe_layer(const char* fn, int32_t hidden, int32_t inter, const gale_e
   }
   // rotate h; down: yp[pair]
   if (use_items) {
-    st = hip_status(fn, launch_prep(h, GALE_F32, inter, P, inter, 0, ra_h, ra_bytes(inter), stream));
+    st = hip_status(fn, launch_prep(h, GALE_F32, inter, P, inter, 0, ra_h, ra_bytes(inter), stream, pair_items));
     if (st) return st;
     st = run_gemv_phase(fn, table, 3, 2, 2, hidden, inter, ra_h, 0, 0, 0, 0, items, n_items, 1, bound, yp,
                         GALE_F32, 0, slots, flags, stream);
     if (st) return st;
   }
   if (use_gemm) {
-    st = hip_status(fn, launch_rotate_f16(h, GALE_F32, P, inter, ht16, stream));
+    st = hip_status(fn, launch_rotate_f16(h, GALE_F32, P, inter, ht16, stream, pair_gemm));
     if (st) return st;
     st = hip_status(fn, launch_grouped_gemm(table, 0, hidden, inter, offsets, perm, top_k, tiles, n_tiles,
                                             max_tiles, ht16, yp, hidden, stream));

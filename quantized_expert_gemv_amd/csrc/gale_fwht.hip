@@ -31,18 +31,19 @@ hipError_t launch_fwht(const void* x, void* y, int64_t n_vec, int len, int in_dt
 
 __global__ void __launch_bounds__(256) prep_kernel(const void* __restrict__ x, int x_dtype, int64_t x_stride,
                                                    int n_vec, int K, int rotated, uint8_t* __restrict__ ra,
-                                                   size_t ra_stride) {
-  prep_wave(x, x_dtype, x_stride, n_vec, K, rotated, ra, ra_stride,
-            (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));
+                                                   size_t ra_stride, const VecFilter filt) {
+  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (wave >= (int64_t)n_vec * (K >> 10) || !filter_keep(filt, wave / (K >> 10))) return;
+  prep_wave(x, x_dtype, x_stride, n_vec, K, rotated, ra, ra_stride, wave);
 }
 
 hipError_t launch_prep(const void* x, int x_dtype, int64_t x_stride, int n_vec, int K, int rotated,
-                       uint8_t* ra, size_t ra_stride, hipStream_t s) {
+                       uint8_t* ra, size_t ra_stride, hipStream_t s, const VecFilter& filt) {
   const int64_t nw = (int64_t)n_vec * (K / 1024);
   if (nw == 0) return hipSuccess;
   const int64_t grid = (nw + 3) / 4;
   hipLaunchKernelGGL(prep_kernel, dim3((unsigned)grid), dim3(256), 0, s, x, x_dtype, x_stride, n_vec, K,
-                     rotated, ra, ra_stride);
+                     rotated, ra, ra_stride, filt);
   return hipGetLastError();
 }
 

@@ -99,9 +99,32 @@ struct GemvParams {
   int out_chunks;            // outlier column chunks staged per wavefront and unit (2, 4 or 8)
 };
 
+// Which vectors of a grouped layer a side needs.  Vector v is a token (per_token: its
+// top_k experts idx[v k + s]) or a pair (its expert idx[v]).  An expert with fewer than
+// split pairs runs as GEMV items, the others as GEMM tiles; a vector is kept when one of its
+// experts runs on the side asked for (items_side).  idx == nullptr keeps every vector.
+struct VecFilter {
+  const int32_t* idx = nullptr;
+  const int32_t* offsets = nullptr;   // pair offsets per expert [E + 1]
+  int top_k = 1, per_token = 0, split = 0, items_side = 0;
+};
+
+__device__ __forceinline__ bool filter_keep(const VecFilter& f, int64_t v) {
+  if (f.idx == nullptr) return true;
+  const int n = f.per_token ? f.top_k : 1;
+  const int32_t* ex = f.idx + (f.per_token ? v * f.top_k : v);
+  bool keep = false;
+  for (int s = 0; s < n; ++s) {
+    const int e = __builtin_amdgcn_readfirstlane(ex[s]);
+    const bool items = f.offsets[e + 1] - f.offsets[e] < f.split;
+    keep = keep || (items == (f.items_side != 0));
+  }
+  return keep;
+}
+
 // launches (return hipError_t of the launch)
 hipError_t launch_prep(const void* x, int x_dtype, int64_t x_stride, int n_vec, int K, int rotated,
-                       uint8_t* ra, size_t ra_stride, hipStream_t s);
+                       uint8_t* ra, size_t ra_stride, hipStream_t s, const VecFilter& filt = VecFilter());
 hipError_t launch_fwht(const void* x, void* y, int64_t n_vec, int len, int in_dtype, int out_dtype,
                        hipStream_t s);
 // max_units: upper bound of the number of units (items x row groups); the launch is a
@@ -156,7 +179,8 @@ struct GemmTile {
 hipError_t launch_build_tiles(const int32_t* offsets, int n_exp, int min_pairs, GemmTile* tiles, int32_t* n_tiles,
                               hipStream_t s);
 // rows of K rotated into fp16 with every 8-column group in MFMA operand order
-hipError_t launch_rotate_f16(const void* x, int x_dtype, int64_t n_rows, int K, uint16_t* out, hipStream_t s);
+hipError_t launch_rotate_f16(const void* x, int x_dtype, int64_t n_rows, int K, uint16_t* out, hipStream_t s,
+                             const VecFilter& filt = VecFilter());
 // gateup: out[pair][inter] = silu(w1 x~) * (w3 x~), A = rotated x by token; else out[pair][hidden] = w2 h~,
 // A = rotated h by pair (fp32 outputs)
 hipError_t launch_grouped_gemm(const gale_matrix* table, int gateup, int rows, int K, const int32_t* offsets,

@@ -223,11 +223,19 @@ __global__ void __launch_bounds__(256) route_scatter_kernel(int T, int E, int k,
   const int t1 = min(T, t0 + kRouteChunk);
   const int p0 = t0 * k, np = (t1 - t0) * k;
   for (int p = threadIdx.x; p < np; p += blockDim.x) s_idx[p] = idx[p0 + p];
+  for (int p = np + threadIdx.x; p < ((np + 7) & ~7); p += blockDim.x) s_idx[p] = -1;   // pad to 8
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     int pos = offsets[e] + chunk_base[(int64_t)chunk * E + e];
-    for (int p = 0; p < np; ++p)
-      if (s_idx[p] == e) perm[pos++] = p0 + p;
+    // eight entries per step, read together (broadcast reads: every thread scans the same list)
+    for (int p = 0; p < np; p += 8) {
+      int v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = s_idx[p + j];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (v[j] == e) perm[pos++] = p0 + p + j;
+    }
   }
 }
 

@@ -126,12 +126,13 @@ hipError_t launch_build_tiles(const int32_t* offsets, int n_exp, int min_pairs, 
 // (row, 1024-chunk).
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) rotate_f16_kernel(const void* __restrict__ x, int x_dtype, int64_t n_rows,
-                                                         int K, uint16_t* __restrict__ out) {
+                                                         int K, uint16_t* __restrict__ out, const VecFilter filt) {
   const int lane = threadIdx.x & 63;
   const int C = K >> 10;
   const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   if (wave >= n_rows * C) return;
   const int64_t row = wave / C;
+  if (!filter_keep(filt, row)) return;
   const int c = (int)(wave - row * C);
   const size_t isz = x_dtype == GALE_F16 ? 2 : 4;
   float v[16];
@@ -151,11 +152,12 @@ __global__ void __launch_bounds__(256) rotate_f16_kernel(const void* __restrict_
   dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
 }
 
-hipError_t launch_rotate_f16(const void* x, int x_dtype, int64_t n_rows, int K, uint16_t* out, hipStream_t s) {
+hipError_t launch_rotate_f16(const void* x, int x_dtype, int64_t n_rows, int K, uint16_t* out, hipStream_t s,
+                             const VecFilter& filt) {
   const int64_t waves = n_rows * (K / 1024);
   if (waves == 0) return hipSuccess;
   hipLaunchKernelGGL(rotate_f16_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, x, x_dtype, n_rows, K,
-                     out);
+                     out, filt);
   return hipGetLastError();
 }
 
