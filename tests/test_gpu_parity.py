@@ -306,7 +306,7 @@ def layer(q):
     return seed, canon, q.expert_table(packed)
 
 
-@pytest.mark.parametrize("T", [1, 4, 16, 32])
+@pytest.mark.parametrize("T", [1, 2, 4, 16, 32, 63, 64])
 def test_moe_decode_layer(q, layer, T):
     seed, canon, tab = layer
     x = gen_x(seed, (1000, T), T, 4096, device=DEV)
