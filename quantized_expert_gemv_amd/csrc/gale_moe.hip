@@ -268,22 +268,45 @@ hipError_t launch_route_large(const RouteIn& rin, int n_tok, int n_exp, int k, i
 // ---------------------------------------------------------------------------
 // combine: y[t][n] = sum_j w[t][j] * ypairs[t k + j][n], slots in order
 // ---------------------------------------------------------------------------
+// Four columns per thread: the partial rows (workspace, 16-byte aligned, H % 4 == 0) are read
+// as float4.  Each element's sum is the same fp32 sequence as before: fma over the k slots in
+// order from 0.
 __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ yp, const float* __restrict__ w,
                                                       int T, int k, int H, void* __restrict__ y, int y_dtype) {
-  const int64_t total = (int64_t)T * H;
+  const int H4 = H >> 2;
+  const int64_t total = (int64_t)T * H4;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
-    const int t = (int)(i / H);
-    const int n = (int)(i - (int64_t)t * H);
-    float acc = 0.f;
-    for (int j = 0; j < k; ++j) acc = fmaf(w[t * k + j], yp[((int64_t)t * k + j) * H + n], acc);
-    if (y_dtype == GALE_F16) reinterpret_cast<__half*>(y)[i] = __float2half_rn(acc);
-    else reinterpret_cast<float*>(y)[i] = acc;
+    const int t = (int)(i / H4);
+    const int n = 4 * (int)(i - (int64_t)t * H4);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < k; ++j) {
+      const float wj = w[t * k + j];
+      const float4 v = *reinterpret_cast<const float4*>(yp + ((int64_t)t * k + j) * H + n);
+      acc.x = fmaf(wj, v.x, acc.x);
+      acc.y = fmaf(wj, v.y, acc.y);
+      acc.z = fmaf(wj, v.z, acc.z);
+      acc.w = fmaf(wj, v.w, acc.w);
+    }
+    const int64_t o = (int64_t)t * H + n;
+    if (y_dtype == GALE_F16) {
+      __half* yh = reinterpret_cast<__half*>(y) + o;
+      yh[0] = __float2half_rn(acc.x);
+      yh[1] = __float2half_rn(acc.y);
+      yh[2] = __float2half_rn(acc.z);
+      yh[3] = __float2half_rn(acc.w);
+    } else {
+      float* yf = reinterpret_cast<float*>(y) + o;
+      yf[0] = acc.x;
+      yf[1] = acc.y;
+      yf[2] = acc.z;
+      yf[3] = acc.w;
+    }
   }
 }
 
 hipError_t launch_combine(const float* ypairs, const float* w, int n_tok, int k, int hidden, void* y,
                           int y_dtype, hipStream_t s) {
-  const int64_t total = (int64_t)n_tok * hidden;
+  const int64_t total = (int64_t)n_tok * (hidden / 4);
   if (total == 0) return hipSuccess;
   int g = (int)std::min<int64_t>((total + 255) / 256, 16384);
   hipLaunchKernelGGL(combine_kernel, dim3(g), dim3(256), 0, s, ypairs, w, n_tok, k, hidden, y, y_dtype);
