@@ -75,8 +75,10 @@ extern "C" {
  * its 16 rows.  v = 0: 1024 (64 per row on average, the 1 % budget's 41 fit); 1: 2048;
  * 2: 4096 (one activation vector per item only; with more, as 1).  Entries past the staged
  * ones are read from HBM one by one, which is slow; a larger staging takes registers from the
- * row tiles per unit.  For budgets of 2 to 3 % take 1, from 4 % take 2.  The one-token
- * layer kernel ignores it.  Results do not depend on it. */
+ * row tiles per unit.  For budgets of 2 to 3 % take 1, from 4 % take 2.  In the expert FFN
+ * and MoE layer the value describes w1/w3; the down phase stages half as many entries for
+ * each halving of its columns (a budget is a share of each row).  The one-token layer
+ * kernel ignores it.  Results do not depend on it. */
 #define GALE_OUTLIER_STAGE_SHIFT 14
 
 /* ---- limits -------------------------------------------------------------- */

@@ -52,16 +52,29 @@ static int stage_ok(int cols, int slots) { return (int64_t)slots * cols * 4 <= 6
 // Outlier column chunks staged per wavefront and unit, from flags bits 14..15 (2, 4 or 8;
 // eight only with one vector per item, else four), fewer where the workgroup's staging
 // would not fit the LDS next to its other buffers.
-static int pick_out_chunks(uint32_t flags, int slots, int cols, int gateup) {
+//
+// The flag describes the matrices of ref_cols columns (an expert's w1/w3: hidden).  The
+// budget is a share of each row, so a phase over fewer columns (w2: inter) stages
+// proportionally fewer entries: with the default, 512 per 16 rows for inter = hidden / 2,
+// which frees LDS (one more workgroup per CU for four-vector items) and registers.
+static int pick_out_chunks(uint32_t flags, int slots, int cols, int gateup, int ref_cols) {
   const int v = (int)((flags >> GALE_OUTLIER_STAGE_SHIFT) & 3);
   int oc = v == 0 ? 2 : (v == 1 || slots > 1 ? 4 : 8);
+  if (!gateup) {
+    // oc * cols / ref_cols chunks, at least one
+    int64_t c = cols;
+    while (oc > 1 && 2 * c <= ref_cols) {
+      oc >>= 1;
+      c *= 2;
+    }
+  }
   while (oc > 2 && gemv_smem_bytes(cols, slots, 4, gateup, stage_ok(cols, slots), oc) > kGemvMaxLds) oc >>= 1;
   return oc;
 }
 
 // Row tiles per unit: at most the chunk count (four lanes per row serve the outliers),
 // at most what the registers hold next to the outlier staging (two chunks: 4, or 3 with
-// four activation vectors; four chunks: 3, or 2 with four vectors; eight chunks: 2), and
+// four activation vectors; one or four chunks: 3, or 2 with four vectors; eight chunks: 2), and
 // small enough that the units cover the GPU at least twice; flags bits 8..11 force a value
 // (1, 2 or 4).  A unit's loads are issued one unit ahead, so wider units keep more bytes in
 // flight per CU: with one or two vectors, four tiles stream ~1.4x faster than two.
@@ -71,7 +84,7 @@ static int pick_tiles(int64_t items, int ntiles, int cols, int slots, int out_ch
   const int forced = (int)((flags >> GALE_TILES_SHIFT) & 0xF);
   if (forced) r = 1 << (forced - 1);
   if (r > 4) r = 4;
-  const int cap = out_chunks == 8 ? 2 : (out_chunks == 4 ? (slots >= 4 ? 2 : 3) : (slots >= 4 ? 3 : 4));
+  const int cap = out_chunks == 8 ? 2 : (out_chunks == 4 || out_chunks == 1 ? (slots >= 4 ? 2 : 3) : (slots >= 4 ? 3 : 4));
   if (r > cap) r = cap;                           // the kernel's register budget
   if (r > C) r = C >= 3 ? 3 : C;                  // three chunks: units of three tiles
   if (r == 3 && forced) r = 2;
@@ -372,7 +385,7 @@ extern "C" int gale_expert_gemv(int32_t rows, int32_t cols, const gale_matrix* m
   P.y_stride = rows;
   P.gateup = 0;
   const int ntiles = rows / 16;
-  P.out_chunks = pick_out_chunks(flags, slots, cols, 0);
+  P.out_chunks = pick_out_chunks(flags, slots, cols, 0, cols);
   const int R = pick_tiles(P.n_items, ntiles, cols, slots, P.out_chunks, flags);
   P.row_groups = (ntiles + R - 1) / R;
   P.stage_xt = stage_ok(cols, slots);
@@ -392,7 +405,7 @@ static int run_gemv_phase(const char* fn, const gale_matrix* table, int stride, 
                           int rows, int cols, const uint8_t* ra, int implicit, int n_tok, int x_shared,
                           int n_items, const WorkItem* items, const int32_t* n_items_dev, int ra_div,
                           int item_bound, void* y, int y_dtype, int gateup, int slots, uint32_t flags,
-                          hipStream_t s) {
+                          hipStream_t s, int ref_cols) {
   GemvParams P;
   memset(&P, 0, sizeof(P));
   P.table = table;
@@ -417,7 +430,7 @@ static int run_gemv_phase(const char* fn, const gale_matrix* table, int stride, 
   P.gateup = gateup;
   const int ntiles = rows / 16;
   const int64_t bound = implicit ? n_items : item_bound;
-  P.out_chunks = pick_out_chunks(flags, slots, cols, gateup);
+  P.out_chunks = pick_out_chunks(flags, slots, cols, gateup, ref_cols);
   const int R = pick_tiles(bound, ntiles, cols, slots, P.out_chunks, flags);
   P.row_groups = (ntiles + R - 1) / R;
   P.stage_xt = stage_ok(cols, slots);
@@ -453,12 +466,12 @@ extern "C" int gale_expert_ffn(int32_t hidden, int32_t inter, const gale_expert*
   if (st) return st;
   const int n_groups = (n_tok + slots - 1) / slots;
   st = run_gemv_phase(fn, table, 3, 0, 1, inter, hidden, ra_x, 1, n_tok, x_shared ? 1 : 0, n_exp * n_groups,
-                      nullptr, nullptr, 1, 0, h, GALE_F32, 1, slots, 0, stream);
+                      nullptr, nullptr, 1, 0, h, GALE_F32, 1, slots, 0, stream, hidden);
   if (st) return st;
   st = hip_status(fn, launch_prep(h, GALE_F32, inter, (int)n_p, inter, 0, ra_h, ra_bytes(inter), stream));
   if (st) return st;
   return run_gemv_phase(fn, table, 3, 2, 2, hidden, inter, ra_h, 1, n_tok, 0, n_exp * n_groups, nullptr,
-                        nullptr, 1, 0, y, GALE_F16, 0, slots, 0, stream);
+                        nullptr, 1, 0, y, GALE_F16, 0, slots, 0, stream, hidden);
 }
 
 // ============================================================================
@@ -573,7 +586,7 @@ static int moe_layer(const char* fn, int32_t hidden, int32_t inter, const gale_e
   // gate/up + SwiGLU: h[pair]
   if (use_items) {
     st = run_gemv_phase(fn, table, 3, 0, 1, inter, hidden, ra_x, 0, 0, 0, 0, items, n_items, top_k, bound, h,
-                        GALE_F32, 1, slots, flags, stream);
+                        GALE_F32, 1, slots, flags, stream, hidden);
     if (st) return st;
   }
   if (use_gemm) {
@@ -586,7 +599,7 @@ static int moe_layer(const char* fn, int32_t hidden, int32_t inter, const gale_e
     st = hip_status(fn, launch_prep(h, GALE_F32, inter, P, inter, 0, ra_h, ra_bytes(inter), stream, pair_items));
     if (st) return st;
     st = run_gemv_phase(fn, table, 3, 2, 2, hidden, inter, ra_h, 0, 0, 0, 0, items, n_items, 1, bound, yp,
-                        GALE_F32, 0, slots, flags, stream);
+                        GALE_F32, 0, slots, flags, stream, hidden);
     if (st) return st;
   }
   if (use_gemm) {

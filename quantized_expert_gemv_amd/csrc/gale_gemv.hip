@@ -567,7 +567,9 @@ static hipError_t launch_t(const GemvParams& p, int64_t max_units, hipStream_t s
   return launch_b<NS, R, G, 1024, OC>(p, block, max_units, s);
 }
 
-// Row tiles per unit by outlier staging.  Two chunks: four tiles for items of up to two
+// Row tiles per unit by outlier staging.  One chunk (the down phase of a layer whose
+// intermediate size is at most half the hidden size): as four chunks.  Two chunks: four
+// tiles for items of up to two
 // vectors, three for four vectors (four would spill).  Four chunks (twice the staged
 // entries): three tiles for up to two vectors, two for four.  Eight chunks: one vector,
 // up to two tiles (two spill a few registers, and still stream 1.4x faster than one).
@@ -603,6 +605,9 @@ static hipError_t launch_s(const GemvParams& p, int slots, int tiles, int64_t ma
 
 template <bool G>
 static hipError_t launch_o(const GemvParams& p, int slots, int tiles, int64_t max_units, hipStream_t s) {
+  if constexpr (!G) {
+    if (p.out_chunks == 1) return launch_s<G, 1>(p, slots, tiles, max_units, s);
+  }
   if (p.out_chunks == 8) return launch_s<G, 8>(p, slots, tiles, max_units, s);
   if (p.out_chunks == 4) return launch_s<G, 4>(p, slots, tiles, max_units, s);
   if (p.out_chunks == 2) return launch_s<G, 2>(p, slots, tiles, max_units, s);
