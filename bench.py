@@ -239,7 +239,7 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on exactly one GPU (the whole 46 GB stack fits one MI355X); "
+        print(f"bench.py: the benchmark runs on exactly one GPU (the whole 46 GB stack fits one MI355X); "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
         return 2
 

@@ -50,7 +50,7 @@ extern "C" {
 #define GALE_ERR_DTYPE       (-3)  /* unknown dtype code */
 #define GALE_ERR_ALIGN       (-4)  /* a pointer is not aligned as required */
 #define GALE_ERR_WORKSPACE   (-5)  /* workspace missing or too small */
-#define GALE_ERR_UNSUPPORTED (-6)  /* valid request this build does not implement */
+#define GALE_ERR_UNSUPPORTED (-6)  /* valid request the library does not implement */
 #define GALE_ERR_FORMAT      (-7)  /* canonical data violates the format */
 #define GALE_ERR_HIP         (-8)  /* a HIP runtime call failed */
 
