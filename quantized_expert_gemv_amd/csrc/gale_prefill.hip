@@ -311,7 +311,9 @@ constexpr int kProducerThreads = 512;
 constexpr int kAChunks = kGemmBM * 16 / kProducerThreads;
 
 // A staging: chunk q = tid + 512 j -> tile row q / 16, 16-byte column group q % 16.
-// Rows past the tile's pairs read the first pair's row: those MFMA rows are never stored.
+// Rows past the tile's pairs load the first pair's row (so every load is unconditional) and
+// are not stored into LDS.  Their LDS rows keep older data, which only reaches MFMA output
+// rows of the same pairs (a product row depends on its own A row alone), never stored.
 struct AStage {
   int row[kAChunks];
 };
@@ -337,11 +339,12 @@ __device__ __forceinline__ void block_load(BlockRegs& r, const AStage& as, const
   r.s = gload4(b.scale + so);
 }
 
-__device__ __forceinline__ void a_store(const BlockRegs& r, lds_b* At, int tid, int acg) {
+__device__ __forceinline__ void a_store(const BlockRegs& r, lds_b* At, int tid, int acg, int valid) {
 #pragma unroll
   for (int q = 0; q < kAChunks; ++q) {
     const int row = (tid >> 4) + (kProducerThreads / 16) * q;
-    *reinterpret_cast<lds_q*>(At + row * kRowBytes + 16 * acg) = u32x4{r.a[q].x, r.a[q].y, r.a[q].z, r.a[q].w};
+    if (row < valid)
+      *reinterpret_cast<lds_q*>(At + row * kRowBytes + 16 * acg) = u32x4{r.a[q].x, r.a[q].y, r.a[q].z, r.a[q].w};
   }
 }
 
@@ -490,8 +493,8 @@ __device__ __forceinline__ void mfma_block(v4f (&acc)[4][4], const lds_b* At, co
 // Stores block j into the B buffer Bt (and A into At): A chunks, sign unpack, outliers.
 template <bool STAGED>
 __device__ __forceinline__ void store_block(const BlockRegs& r, BItem& b, lds_b* At, lds_b* Bt, int j, int tid, int acg,
-                                            const Patch pt, int tt, const gale_matrix* table) {
-  a_store(r, At, tid, acg);
+                                            const Patch pt, int tt, const gale_matrix* table, int valid) {
+  a_store(r, At, tid, acg, valid);
   sign_store(b, r.w, r.s, Bt, j);
   if (STAGED) patch_apply(pt, Bt, tt, tid & 63);
   else walk_outliers(b, Bt, j, table);
@@ -507,7 +510,7 @@ __device__ __forceinline__ void store_block(const BlockRegs& r, BItem& b, lds_b*
 template <bool STAGED>
 __device__ __forceinline__ void producer_loop(const GemmParams& P, lds_b* A0, lds_b* B0, const AStage& as, BItem& b,
                                               int NB, int tid, int acg, const lds_u32* st_ent, int starts,
-                                              BlockRegs& re, BlockRegs& ro) {
+                                              BlockRegs& re, BlockRegs& ro, int valid) {
   lds_b* const A1 = A0 + kTileBytes;
   lds_b* const B1 = B0 + kTileBytes;
   const int lane = tid & 63, tt = b.brow >> 4;
@@ -519,7 +522,7 @@ __device__ __forceinline__ void producer_loop(const GemmParams& P, lds_b* A0, ld
     px = patch_prep(st_ent, starts, tt, 0, NB, lane);
     py = patch_prep(st_ent, starts, tt, 1, NB, lane);
   }
-  store_block<STAGED>(re, b, A0, B0, 0, tid, acg, px, tt, P.table);
+  store_block<STAGED>(re, b, A0, B0, 0, tid, acg, px, tt, P.table, valid);
   if (STAGED) patch_rest(px, B0, st_ent, tt, lane);
   __builtin_amdgcn_sched_barrier(0);
   block_load(re, as, b, P.A, P.K, 2, acg);
@@ -528,13 +531,13 @@ __device__ __forceinline__ void producer_loop(const GemmParams& P, lds_b* A0, ld
   for (int bd = 0; bd < NB; bd += 2) {
     // block bd (buffer 0) runs; block bd + 1 into buffer 1
     if (STAGED) px = patch_prep(st_ent, starts, tt, bd + 2, NB, lane);
-    store_block<STAGED>(ro, b, A1, B1, bd + 1, tid, acg, py, tt, P.table);
+    store_block<STAGED>(ro, b, A1, B1, bd + 1, tid, acg, py, tt, P.table, valid);
     block_load(ro, as, b, P.A, P.K, min(bd + 3, NB - 1), acg);
     if (STAGED) patch_rest(py, B1, st_ent, tt, lane);
     __syncthreads();
     // block bd + 1 (buffer 1) runs; block bd + 2 into buffer 0
     if (STAGED) py = patch_prep(st_ent, starts, tt, bd + 3, NB, lane);
-    store_block<STAGED>(re, b, A0, B0, bd + 2, tid, acg, px, tt, P.table);
+    store_block<STAGED>(re, b, A0, B0, bd + 2, tid, acg, px, tt, P.table, valid);
     block_load(re, as, b, P.A, P.K, min(bd + 4, NB - 1), acg);
     if (STAGED) patch_rest(px, B0, st_ent, tt, lane);
     __syncthreads();
@@ -698,10 +701,10 @@ __global__ void __launch_bounds__(kProducerThreads + 256) grouped_gemm_kernel(co
   v4f acc[4][4];
   if (producer) {
     if (staged) {
-      producer_loop<true>(P, A0, B0, as, b, NB, tid, acg, st_ent, starts, re, ro);
+      producer_loop<true>(P, A0, B0, as, b, NB, tid, acg, st_ent, starts, re, ro, valid);
     } else {
       item_walk_init(P, e, n0, b);
-      producer_loop<false>(P, A0, B0, as, b, NB, tid, acg, st_ent, 0, re, ro);
+      producer_loop<false>(P, A0, B0, as, b, NB, tid, acg, st_ent, 0, re, ro, valid);
     }
   } else {
 #pragma unroll
