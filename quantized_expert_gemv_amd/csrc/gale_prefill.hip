@@ -612,16 +612,16 @@ __global__ void __launch_bounds__(kProducerThreads + 256) grouped_gemm_kernel(co
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // ---- outlier staging by wavefronts 0..3 (the others pass the same barriers).  Row
-  //      r = tid / 2 of the B tile (matrix sel_a for r < half_rows, else sel_b; global row
-  //      n0 + r % half_rows) is walked by two threads, entries of parity tid & 1: count
-  //      per bucket, scan, then place each entry.
-  const bool stager = threadIdx.x < 256;
-  const int r = (tid >> 1) & 127, par = tid & 1;
+  // ---- outlier staging by the producers (the consumers pass the same barriers).  Row
+  //      r = tid / 4 of the B tile (matrix sel_a for r < half_rows, else sel_b; global row
+  //      n0 + r % half_rows) is walked by four threads, entries p with p % 4 = tid % 4: count
+  //      per bucket, scan (wavefronts 0..3, two buckets per thread), then place each entry.
+  const int r = tid >> 2, par = tid & 3;
+  const bool scanner = threadIdx.x < 256;
   const gale_matrix* Mr = P.table + 3 * e + (r >= P.half_rows ? P.sel_b : P.sel_a);
   const int gr = n0 + r % P.half_rows;
   int rp0 = 0, rp1 = 0;
-  if (stager) {
+  if (producer) {
     rp0 = Mr->row_ptr[gr];
     rp1 = Mr->row_ptr[gr + 1];
   }
@@ -630,7 +630,7 @@ __global__ void __launch_bounds__(kProducerThreads + 256) grouped_gemm_kernel(co
   if (threadIdx.x < kGemmBM) s_orow[threadIdx.x] = (int)threadIdx.x < valid ? P.perm[pair0 + threadIdx.x] : 0;
   for (int i = threadIdx.x; i < kBuckets; i += blockDim.x) st_fill[i] = 0;
   __syncthreads();
-  if (stager && par == 0) __atomic_fetch_add(st_misc, rp1 - rp0, __ATOMIC_RELAXED);
+  if (producer && par == 0) __atomic_fetch_add(st_misc, rp1 - rp0, __ATOMIC_RELAXED);
   __syncthreads();
   const bool staged = st_misc[0] <= kOutStage && NB <= kStageBlocks;
   const int bucket0 = (r >> 4) * NB;
@@ -638,20 +638,20 @@ __global__ void __launch_bounds__(kProducerThreads + 256) grouped_gemm_kernel(co
   if (staged) {
     // the walks take the thread's entries eight at a time, loads first (clamped into the
     // row's range) so that eight are in flight
-    if (stager) {
-      for (int p0 = rp0 + par; p0 < rp1; p0 += 16) {
+    if (producer) {
+      for (int p0 = rp0 + par; p0 < rp1; p0 += 32) {
         int col[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) col[k] = Mr->out_cols[min(p0 + 2 * k, rp1 - 1)];
+        for (int k = 0; k < 8; ++k) col[k] = Mr->out_cols[min(p0 + 4 * k, rp1 - 1)];
 #pragma unroll
         for (int k = 0; k < 8; ++k)
-          if (p0 + 2 * k < rp1) __atomic_fetch_add(st_fill + bucket0 + (col[k] >> 7), 1, __ATOMIC_RELAXED);
+          if (p0 + 4 * k < rp1) __atomic_fetch_add(st_fill + bucket0 + (col[k] >> 7), 1, __ATOMIC_RELAXED);
       }
     }
     __syncthreads();
     // exclusive scan of the bucket counts, two per thread
     int c0 = 0, c1 = 0, v = 0;
-    if (stager) {
+    if (scanner) {
       c0 = 2 * tid < nbk ? st_fill[2 * tid] : 0;
       c1 = 2 * tid + 1 < nbk ? st_fill[2 * tid + 1] : 0;
       v = c0 + c1;
@@ -663,7 +663,7 @@ __global__ void __launch_bounds__(kProducerThreads + 256) grouped_gemm_kernel(co
       if (lane == 63) st_misc[1 + wave] = v;
     }
     __syncthreads();
-    if (stager) {
+    if (scanner) {
       int ex = v - c0 - c1;
       for (int w = 0; w < wave; ++w) ex += st_misc[1 + w];
       if (2 * tid < nbk) st_start[2 * tid] = st_fill[2 * tid] = ex;
@@ -671,19 +671,19 @@ __global__ void __launch_bounds__(kProducerThreads + 256) grouped_gemm_kernel(co
       if (tid == 255) st_start[nbk] = ex + c0 + c1;
     }
     __syncthreads();
-    if (stager) {
+    if (producer) {
       const uint16_t rs = Mr->row_scales[gr];
-      for (int p0 = rp0 + par; p0 < rp1; p0 += 16) {
+      for (int p0 = rp0 + par; p0 < rp1; p0 += 32) {
         int col[8], q[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          const int p = min(p0 + 2 * k, rp1 - 1);
+          const int p = min(p0 + 4 * k, rp1 - 1);
           col[k] = Mr->out_cols[p];
           q[k] = outlier_value(Mr->out_vals, p);
         }
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          if (p0 + 2 * k < rp1) {
+          if (p0 + 4 * k < rp1) {
             const int slot = __atomic_fetch_add(st_fill + bucket0 + (col[k] >> 7), 1, __ATOMIC_RELAXED);
             st_ent[slot] = pack_entry(col[k] & 127, r & 15, q[k], rs);
           }
