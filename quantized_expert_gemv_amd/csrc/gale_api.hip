@@ -153,7 +153,7 @@ static int64_t moe_tile_bound(int T, int E, int k) {
 }
 enum MoePath { kDecode = 0, kGroupedItems = 1, kGroupedGemm = 2, kGroupedHybrid = 3 };
 // Experts with at least this many pairs take the tile GEMM in the hybrid grouped path.
-constexpr int kGemmMinPairs = 24;
+constexpr int kGemmMinPairs = 20;
 // Row tiles per unit of the one-token layer kernel, (gate/up, down) as decimal digits.
 constexpr int kDecodeLayerTiles = 32;
 static MoePath moe_path(int n_tok, uint32_t flags) {
