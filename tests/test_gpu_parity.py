@@ -530,6 +530,30 @@ def test_moe_grouped_gemm_outlier_edges(q):
     assert err <= REL_L2_BAR
 
 
+def test_moe_grouped_gemm_hidden_8192(q):
+    # hidden 8192 (64 scale blocks): past the GEMM's bucket table, so its tiles walk the CSR
+    # lists in HBM; the GEMV items run 16 wavefronts per workgroup.  GEMM and items against
+    # each other and against the oracle on a sample.
+    E, T, H, I = 2, 80, 8192, 2048
+    seed = config_seed(13)
+    w13 = gen_matrices(seed, [(e, m) for e in range(E) for m in (0, 1)], I, H)
+    w2 = gen_matrices(seed, [(e, 2) for e in range(E)], H, I)
+    canon = [(w13[2 * e], w13[2 * e + 1], w2[e]) for e in range(E)]
+    tab = q.expert_table([tuple(q.pack_matrix(m.to(DEV)) for m in ex) for ex in canon])
+    x = gen_x(seed, (1,), T, H, device=DEV)
+    lg = gen_logits_normal(seed, (2,), T, E, device=DEV)
+    yg, idx, _ = q.moe_layer_fwd(tab, H, I, lg, x, top_k=1, flags=q.GALE_PATH_GROUPED | q.GALE_GROUPED_GEMM)
+    yi, _, _ = q.moe_layer_fwd(tab, H, I, lg, x, top_k=1, flags=q.GALE_PATH_GROUPED | q.GALE_GROUPED_ITEMS)
+    sample = [0, T - 1]
+    yref, ridx, _ = O.moe(lambda e: tuple(m.numpy() for m in canon[e]), lg.cpu().numpy()[sample],
+                          x.cpu().numpy()[sample], k=1)
+    assert np.array_equal(idx.cpu().numpy()[sample], ridx)
+    e_or = O.rel_l2(np_of(yg[sample]), yref).max()
+    e_gi = O.rel_l2(np_of(yg), np_of(yi)).max()
+    print(f"grouped GEMM hidden 8192: vs oracle {e_or:.3e}, vs items {e_gi:.3e}")
+    assert max(e_or, e_gi) <= REL_L2_BAR
+
+
 def clustered_outlier_dict(N, K, seed):
     """Random signs and block scales; every row has 12 outliers in its first 128 columns
     and 2 in its last 128, so a group of 16 rows holds 192 entries in block 0."""
