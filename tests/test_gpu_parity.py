@@ -554,6 +554,26 @@ def test_moe_grouped_gemm_hidden_8192(q):
     assert max(e_or, e_gi) <= REL_L2_BAR
 
 
+@pytest.mark.parametrize("T", [1, 4])
+def test_moe_decode_hidden_8192(q, T):
+    # the decode path at hidden 8192: the five-launch sequence (the one-launch layer takes
+    # hidden <= 4096), gate/up workgroups of 16 wavefronts
+    E, H, I = 8, 8192, 2048
+    seed = config_seed(14)
+    w13 = gen_matrices(seed, [(e, m) for e in range(E) for m in (0, 1)], I, H)
+    w2 = gen_matrices(seed, [(e, 2) for e in range(E)], H, I)
+    canon = [(w13[2 * e], w13[2 * e + 1], w2[e]) for e in range(E)]
+    tab = q.expert_table([tuple(q.pack_matrix(m.to(DEV)) for m in ex) for ex in canon])
+    x = gen_x(seed, (1, T), T, H, device=DEV)
+    lg = gen_logits_normal(seed, (2, T), T, E, device=DEV)
+    y, idx, _ = q.moe_layer_fwd(tab, H, I, lg, x, top_k=2)
+    yref, ridx, _ = O.moe(lambda e: tuple(m.numpy() for m in canon[e]), lg.cpu().numpy(), x.cpu().numpy(), k=2)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    err = O.rel_l2(np_of(y), yref).max()
+    print(f"decode hidden 8192 T={T}: rel-L2 {err:.3e}")
+    assert err <= REL_L2_BAR
+
+
 def clustered_outlier_dict(N, K, seed):
     """Random signs and block scales; every row has 12 outliers in its first 128 columns
     and 2 in its last 128, so a group of 16 rows holds 192 entries in block 0."""
