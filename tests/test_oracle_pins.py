@@ -259,6 +259,45 @@ def test_ffn_closed_form():
     assert np.abs(y[:, 2048:]).max() == 0.0
 
 
+@pytest.mark.parametrize("gate_scale,up_scale", [(1.0, 2.0), (2.0, 1.0)])
+def test_ffn_closed_form_gate_and_up_differ(gate_scale, up_scale):
+    # w1 (gate) = Hadamard-sign pattern with scales gate_scale/32, w3 (up) the same with
+    # up_scale/32, w2 the plain pattern: a = gate_scale x, g = up_scale x on the first 2048
+    # features, so y = silu(gate_scale x) * up_scale x there.  With the roles swapped the
+    # result would be silu(up_scale x) * gate_scale x, which differs for every x != 0.
+    w1 = hadamard_sign_matrix(2048, 4096, scale_num=gate_scale)
+    w3 = hadamard_sign_matrix(2048, 4096, scale_num=up_scale)
+    w2 = hadamard_sign_matrix(4096, 2048)
+    x = np.random.default_rng(16).standard_normal((2, 4096))
+    y = O.ffn(w1, w3, w2, x)
+    for t in range(2):
+        ref = [silu_py(gate_scale * v) * up_scale * v for v in x[t, :2048]]
+        swapped = [silu_py(up_scale * v) * gate_scale * v for v in x[t, :2048]]
+        assert np.abs(y[t, :2048] - np.array(ref)).max() <= 1e-12
+        assert np.abs(np.array(ref) - np.array(swapped)).max() > 1e-2
+    assert np.abs(y[:, 2048:]).max() == 0.0
+
+
+def test_rel_l2_is_per_vector():
+    # two token vectors whose norms differ by 100x: the metric is the norm of the error over
+    # the norm of the reference for each vector on its own (hand-computed values)
+    ref = np.array([[3.0, 4.0], [300.0, 400.0]])
+    y = np.array([[3.0, 4.5], [300.0, 401.0]])
+    e = O.rel_l2(y, ref)
+    assert e.shape == (2,)
+    assert abs(e[0] - 0.5 / 5.0) <= 1e-15
+    assert abs(e[1] - 1.0 / 500.0) <= 1e-15
+    # a global norm would give sqrt(0.25 + 1) / sqrt(25 + 250000) ~ 2.2e-3 for both
+    assert abs(e.max() - 0.1) <= 1e-15
+    # along the other axis the vectors are the columns
+    ec = O.rel_l2(y, ref, axis=0)
+    assert abs(ec[0] - 0.0) <= 1e-15
+    assert abs(ec[1] - math.sqrt(0.25 + 1.0) / math.sqrt(16.0 + 160000.0)) <= 1e-15
+    # a zero reference vector gives the absolute error
+    z = O.rel_l2(np.array([[0.0, 1e-7]]), np.zeros((1, 2)))
+    assert abs(z[0] - 1e-7) <= 1e-22
+
+
 def brute_route(row, k):
     order = sorted(range(len(row)), key=lambda e: (-float(row[e]), e))
     return order[:k]
