@@ -6,16 +6,27 @@ DeepSeek-V4-Flash-shaped routed experts: 43 layers x 256 experts x {w1, w3, w2}
 (33,024 packed matrices, 46.0 GB in HBM), each layer routing the token to its
 top-6 experts and combining their SwiGLU FFN outputs.  Inputs are seeded
 synthetic data of the model card's shapes (no weights or datasets are used).
+Every timed region starts with its inputs resident in HBM.
 
 Reported:
-  value        packed expert-weight bytes touched per token (258 experts) / step time, GB/s
+  value        packed expert-weight bytes touched per token (258 experts) / step time, GB/s;
+               the step is timed three ways -- 43 one-launch layer calls (eager and as a
+               HIP graph) and one launch for the whole stack -- and the fastest is the value
+               (all three give the same outputs bit for bit; checked here)
   tokens_per_s steps per second
   roofline     the GEMV kernel at its sustained launch shape: one launch over 1024
                distinct [2048, 4096] matrices of the resident stack (w1 and w3 of 512
-               experts), one token each, timed with HIP events; algorithmic bytes
-               1,405,952 per matrix
-  cpu_baseline the fp64 oracle on the host for a bounded sample of the same step
-               (its outputs also check the GPU step at full size)
+               experts), one token each, prepared activations, timed with HIP events on the
+               launch stream; algorithmic bytes 1,405,952 per matrix
+  gemv_single_matrix  the single-matrix workload as configured: FWHT-1024 of each matrix's
+               own x and the activation split, then the GEMV (two launches), over the same
+               1024 matrices; and one matrix per call (launch-latency bound)
+  ffn          one expert FFN, one token: one expert per call, and 256 distinct experts per
+               launch (each its own x), GB/s of 4,196,352 algorithmic bytes per expert
+  decode_batches, prefill  one MoE layer at 1/4/16/32 tokens; the 2048-token grouped prefill
+  gemv_sweep   the sustained GEMV at outlier budgets 1/2/3/5 % and the DeepSeek-V4-Pro shapes
+  cpu_baseline the fp64 oracle on the host cores, single thread and all cores, per workload,
+               on bounded samples (scaled as stated); its outputs also check the GPU step
   stream_ceiling  a plain elementwise kernel (negate, fp32) over a 1 GiB buffer: the
                HBM rate a trivial streaming kernel reaches on this device; it is also the
                known-size reference that scales the HBM byte counters behind "traffic"
@@ -41,6 +52,8 @@ W13_BYTES = 1_393_664          # one [2048, 4096] matrix, 41 outliers per row
 W2_BYTES = 1_392_640           # one [4096, 2048] matrix, 20 outliers per row
 EXPERT_BYTES = 2 * W13_BYTES + W2_BYTES
 GEMV_UNIT_BYTES = W13_BYTES + 2 * HIDDEN + 2 * INTER   # weights + fp16 x + fp16 y
+FFN_UNIT_BYTES = EXPERT_BYTES + 2 * HIDDEN + 2 * HIDDEN  # weights + fp16 x + fp16 y (4,196,352)
+EXPERT_DESC_BYTES = 3 * 48                              # one gale_expert in a descriptor table
 HBM_PEAK_GBPS = 8000.0
 GEMV_WARM_CALLS = 10
 DECODE_BATCHES = (1, 4, 16, 32)
@@ -125,27 +138,136 @@ def time_events(fn, reps: int):
     return s.elapsed_time(e) / reps
 
 
-def cpu_baseline(synth, O, seed, xs, logits, gpu_y, n_layers):
-    """Oracle on the host for the first n_layers of the step; returns timing and parity."""
+def time_isolated(fn, reps: int):
+    """Median milliseconds of one call of fn on an otherwise idle stream (HIP events around
+    each call, synchronised between calls): the latency of a single launch sequence."""
+    import torch
+    out = []
+    for _ in range(reps):
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        e.synchronize()
+        out.append(s.elapsed_time(e))
+    out.sort()
+    return out[len(out) // 2]
+
+
+def host_cpu():
+    """(cores this process may use, CPU model name)."""
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return cores, model
+
+
+def cpu_baselines(synth, O, seed, dev, xs, logits, gpu_y, layers: int):
+    """The fp64 oracle on the host, untuned, per workload: one thread (numpy's BLAS limited to
+    one) and all cores (the oracle's independent per-matrix or per-expert evaluations spread over
+    a thread pool of every core; numpy works outside the interpreter lock).  Each is timed on a
+    bounded sample and scaled to the workload as stated.  Matrices are generated on the GPU
+    (synth is bit-identical on both) and copied to the host before the timed region.  Also
+    returns the oracle's check of the GPU step on the sampled layers."""
     import numpy as np
-    from threadpoolctl import threadpool_info
-    t_total, errs = 0.0, []
-    for l in range(n_layers):
-        lg = logits[l].cpu().numpy()
-        x = xs[l].cpu().numpy()
-        idx, _ = O.route(lg, TOPK)
-        mats = {}
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    cores, model = host_cpu()
+    pool = ThreadPoolExecutor(cores)
+    # numpy's BLAS held to one thread per worker throughout: the all-core runs spread work
+    # over the pool instead (BLAS threads inside every worker would oversubscribe the cores)
+    limit = threadpool_limits(1)
+
+    def canon(ids, r, c):
+        return synth.gen_matrix(seed, ids, r, c, device=dev).numpy()
+
+    def expert(l, e):
+        return (canon((l, e, 0), INTER, HIDDEN), canon((l, e, 1), INTER, HIDDEN), canon((l, e, 2), HIDDEN, INTER))
+
+    res = {}
+    # d1: one [2048, 4096] matrix, one token: rotation + dequantize + matvec
+    mats = [canon((0, e, m), INTER, HIDDEN) for e in range(cores) for m in (0, 1)][:2 * cores]
+    xv = [xs[0][0].float().cpu().numpy() for _ in mats]
+    t0 = time.perf_counter()
+    for i in range(4):
+        O.gemv(mats[i], xv[i])
+    t1 = (time.perf_counter() - t0) / 4
+    t0 = time.perf_counter()
+    list(pool.map(lambda i: O.gemv(mats[i], xv[i]), range(len(mats))))
+    tn = (time.perf_counter() - t0) / len(mats)
+    res["single_matrix"] = {"s_per_matrix_1_thread": round(t1, 4), "s_per_matrix_all_cores": round(tn, 5),
+                            "gbps_all_cores": round(GEMV_UNIT_BYTES / tn / 1e9, 4),
+                            "sample": f"4 matrices on one thread; {len(mats)} distinct matrices on {cores} threads"}
+    del mats
+    # d2: one expert FFN, one token
+    exps = [expert(0, e) for e in range(cores)]
+    t0 = time.perf_counter()
+    for i in range(2):
+        O.ffn(*exps[i], xv[0])
+    t1 = (time.perf_counter() - t0) / 2
+    t0 = time.perf_counter()
+    list(pool.map(lambda i: O.ffn(*exps[i], xv[0]), range(len(exps))))
+    tn = (time.perf_counter() - t0) / len(exps)
+    res["ffn"] = {"s_per_expert_1_thread": round(t1, 4), "s_per_expert_all_cores": round(tn, 5),
+                  "gbps_all_cores": round(FFN_UNIT_BYTES / tn / 1e9, 4),
+                  "sample": f"2 experts on one thread; {len(exps)} distinct experts on {cores} threads"}
+    del exps
+    # d4: one token through the stack (43 layers x route + 6 FFNs + combine), sampled layers
+    n_l = min(layers, cores)
+    ex = {}
+    for l in range(n_l):
+        idx, _ = O.route(logits[l].cpu().numpy(), TOPK)
         for e in idx[0]:
-            e = int(e)
-            mats[e] = tuple(synth.gen_matrix(seed, (l, e, m), r, c).numpy()
-                            for m, r, c in ((0, INTER, HIDDEN), (1, INTER, HIDDEN), (2, HIDDEN, INTER)))
+            ex[(l, int(e))] = expert(l, int(e))
+    lg_np = [logits[l].cpu().numpy() for l in range(n_l)]
+    x_np = [xs[l].float().cpu().numpy() for l in range(n_l)]
+    t0 = time.perf_counter()
+    O.moe(lambda e: ex[(0, e)], lg_np[0], x_np[0], k=TOPK)
+    t1 = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    outs = list(pool.map(lambda l: O.moe(lambda e: ex[(l, e)], lg_np[l], x_np[l], k=TOPK)[0], range(n_l)))
+    tn = (time.perf_counter() - t0) / n_l
+    errs = [float(O.rel_l2(gpu_y[l].float().cpu().numpy().astype(np.float64), outs[l]).max()) for l in range(n_l)]
+    res["stack_token"] = {"s_per_token_1_thread": round(t1 * 43, 2), "s_per_token_all_cores": round(tn * 43, 3),
+                          "gbps_all_cores": round(43 * TOPK * EXPERT_BYTES / (tn * 43) / 1e9, 4),
+                          "sample": f"1 layer on one thread, {n_l} layers (one per thread) on {cores} threads; "
+                                    f"scaled to 43 layers"}
+    del ex
+    # d3: one layer at 4 / 16 / 32 tokens (all cores: the touched experts in parallel), and d5
+    # grouped prefill: a sample of the touched experts with all their tokens, scaled by the count
+    def layer_sample(lg, xb, n_exp_sample, l_id):
+        idx, _ = O.route(lg, TOPK)
+        uniq = [int(e) for e in np.unique(idx)]
+        take = uniq[:n_exp_sample]
+        exs = {e: expert(l_id, e) for e in take}
+        tok = {e: np.nonzero((idx == e).any(axis=1))[0] for e in take}
         t0 = time.perf_counter()
-        yref, _, _ = O.moe(lambda e: mats[e], lg, x, k=TOPK)
-        t_total += time.perf_counter() - t0
-        errs.append(float(O.rel_l2(gpu_y[l].float().cpu().numpy().astype(np.float64), yref).max()))
-    per_token = t_total / n_layers * 43
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return per_token, threads, max(errs)
+        list(pool.map(lambda e: O.ffn(*exs[e], xb[tok[e]]), take))
+        return (time.perf_counter() - t0) * len(uniq) / len(take), len(uniq), len(take)
+
+    for T in (4, 16, 32):
+        lg = synth.gen_logits_normal(seed, (0x60000 + T, 0), T, EXPERTS).numpy()
+        xb = synth.gen_x(seed, (0x60000 + T, 0), T, HIDDEN).float().numpy()
+        tt, u, k_s = layer_sample(lg, xb, 2 * cores, 0)
+        res[f"decode_layer_T{T}"] = {"s_per_layer_all_cores": round(tt, 3), "unique_experts": u,
+                                     "gbps_all_cores": round(u * EXPERT_BYTES / tt / 1e9, 4),
+                                     "sample": f"{k_s} of {u} touched experts on {cores} threads, scaled"}
+    lgp = synth.gen_logits_zipf(seed, (0x40000,), PREFILL_TOKENS, EXPERTS).numpy()
+    xp = synth.gen_x(seed, (0x40000,), PREFILL_TOKENS, HIDDEN).float().numpy()
+    tt, u, k_s = layer_sample(lgp, xp, 2 * cores, 0)
+    res["prefill"] = {"s_per_layer_all_cores": round(tt, 2), "unique_experts": u,
+                      "tflops_all_cores": round(PREFILL_FLOP / tt / 1e12, 5),
+                      "sample": f"{k_s} of {u} touched experts with all their tokens on {cores} threads, scaled"}
+    pool.shutdown()
+    limit.restore_original_limits()
+    return res, cores, model, max(errs), n_l
 
 
 SWEEP_SHAPES = ((2048, 4096, 0.01), (2048, 4096, 0.02), (2048, 4096, 0.03), (2048, 4096, 0.05),
@@ -231,11 +353,10 @@ def main() -> int:
     ap.add_argument("--gemv-reps", type=int, default=50)
     ap.add_argument("--device-warm-s", type=float, default=1.0)
     ap.add_argument("--prefill-reps", type=int, default=5)
-    ap.add_argument("--cpu-layers", type=int, default=16)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
-    ap.add_argument("--sweep", action="store_true",
-                    help="also time the sustained GEMV at outlier budgets 1/2/3/5 %% and the DeepSeek-V4-Pro shapes")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the sustained GEMV at outlier budgets 1/2/3/5 %% and the DeepSeek-V4-Pro shapes")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -291,15 +412,93 @@ def main() -> int:
     gemv_gbps = n * GEMV_UNIT_BYTES / (ms_gemv * 1e-3) / 1e9
     log(f"sustained GEMV: {n} matrices in {ms_gemv * 1e3:.1f} us -> {gemv_gbps:.0f} GB/s "
         f"({100 * gemv_gbps / HBM_PEAK_GBPS:.1f}% of 8 TB/s)")
-    sweep = sweep_gemv(q, synth, lib, dev, seed, args.gemv_reps, args.device_warm_s) if args.sweep else None
 
+    # ---- the single-matrix workload as configured: FWHT-1024 and the activation split of each
+    #      matrix's own fp16 x, then the GEMV (gale_expert_gemv on raw x: two launches)
+    wsg = torch.empty(max(q.gemv_workspace_bytes(INTER, HIDDEN, n, 1, 0), 256), dtype=torch.uint8, device=dev)
+    e2e_args = [(INTER, HIDDEN, t.ptr(), n, xg.data_ptr(), q.GALE_F16, 0, 1, yg.data_ptr(), q.GALE_F16,
+                 wsg.data_ptr(), wsg.numel(), 0) for t in sets]
+
+    def gemv_e2e_call():
+        a = e2e_args[flip[0]]
+        flip[0] ^= 1
+        rc = lib.gale_expert_gemv(*a, torch.cuda.current_stream().cuda_stream)
+        if rc:
+            raise RuntimeError(lib.gale_last_error().decode())
+
+    for _ in range(GEMV_WARM_CALLS):
+        gemv_e2e_call()
+    torch.cuda.synchronize()
+    ms_e2e = time_events(gemv_e2e_call, args.gemv_reps)
+    e2e_gbps = n * GEMV_UNIT_BYTES / (ms_e2e * 1e-3) / 1e9
+    log(f"single-matrix workload as configured (rotation + GEMV, {n} distinct matrices): {ms_e2e * 1e3:.1f} us "
+        f"-> {e2e_gbps:.0f} GB/s ({100 * e2e_gbps / HBM_PEAK_GBPS:.1f}% of 8 TB/s)")
+    # one matrix per call (a different one each time), FWHT + GEMV: launch-latency bound
+    one_tabs = [q.matrix_table([w13_all[i]]) for i in range(0, 2 * n, 2 * n // 64)]
+    ws1 = torch.empty(max(q.gemv_workspace_bytes(INTER, HIDDEN, 1, 1, 0), 256), dtype=torch.uint8, device=dev)
+    y1 = torch.empty(1, 1, INTER, dtype=torch.float16, device=dev)
+    cur1 = [0]
+
+    def gemv_one_call():
+        t = one_tabs[cur1[0] % len(one_tabs)]
+        cur1[0] += 1
+        rc = lib.gale_expert_gemv(INTER, HIDDEN, t.ptr(), 1, xg.data_ptr(), q.GALE_F16, 0, 1, y1.data_ptr(),
+                                  q.GALE_F16, ws1.data_ptr(), ws1.numel(), 0, torch.cuda.current_stream().cuda_stream)
+        if rc:
+            raise RuntimeError(lib.gale_last_error().decode())
+
+    for _ in range(10):
+        gemv_one_call()
+    ms_one_iso = time_isolated(gemv_one_call, 64)
+    ms_one_tp = time_events(gemv_one_call, 256)
+    log(f"one matrix per call: {ms_one_iso * 1e3:.2f} us isolated, {ms_one_tp * 1e3:.2f} us back to back")
+    del one_tabs
+
+    # ---- one expert FFN, one token: one expert per call, and 256 distinct experts per launch
+    x256 = torch.stack([gen_x(seed, (0x70000 + i,), 1, HIDDEN, device=dev) for i in range(EXPERTS)])
+    y256 = torch.empty(EXPERTS, 1, HIDDEN, dtype=torch.float16, device=dev)
+    wsf = torch.empty(q.ffn_workspace_bytes(HIDDEN, INTER, EXPERTS, 1, 0), dtype=torch.uint8, device=dev)
+    fcur = [0]
+
+    def ffn_many_call():
+        t = tables[fcur[0] % min(L, 2)]
+        fcur[0] += 1
+        rc = lib.gale_expert_ffn(HIDDEN, INTER, t.ptr(), EXPERTS, x256.data_ptr(), 0, 1, y256.data_ptr(),
+                                 wsf.data_ptr(), wsf.numel(), torch.cuda.current_stream().cuda_stream)
+        if rc:
+            raise RuntimeError(lib.gale_last_error().decode())
+
+    def ffn_one_call():
+        i = fcur[0]
+        fcur[0] += 1
+        t = tables[i % L]
+        rc = lib.gale_expert_ffn(HIDDEN, INTER, t.ptr() + EXPERT_DESC_BYTES * (i % EXPERTS), 1, x256.data_ptr(), 0, 1,
+                                 y256.data_ptr(), wsf.data_ptr(), wsf.numel(), torch.cuda.current_stream().cuda_stream)
+        if rc:
+            raise RuntimeError(lib.gale_last_error().decode())
+
+    for _ in range(4):
+        ffn_many_call()
+    torch.cuda.synchronize()
+    ms_ffn_many = time_events(ffn_many_call, 20)
+    ffn_gbps = EXPERTS * FFN_UNIT_BYTES / (ms_ffn_many * 1e-3) / 1e9
+    for _ in range(10):
+        ffn_one_call()
+    ms_ffn_one = time_isolated(ffn_one_call, 64)
+    ms_ffn_one_tp = time_events(ffn_one_call, 256)
+    log(f"expert FFN: {EXPERTS} experts per launch in {ms_ffn_many * 1e3:.1f} us -> {ffn_gbps:.0f} GB/s "
+        f"({100 * ffn_gbps / HBM_PEAK_GBPS:.1f}% of 8 TB/s); one expert {ms_ffn_one * 1e3:.2f} us isolated, "
+        f"{ms_ffn_one_tp * 1e3:.2f} us back to back")
+    del x256, y256, wsf
+
+    sweep = None if args.no_sweep else sweep_gemv(q, synth, lib, dev, seed, args.gemv_reps, args.device_warm_s)
 
     xs = [gen_x(seed, (0x10000 + l,), 1, HIDDEN, device=dev) for l in range(L)]
     logits = [gen_logits_normal(seed, (0x20000 + l,), 1, EXPERTS, device=dev) for l in range(L)]
     ys = [torch.empty(1, HIDDEN, dtype=torch.float16, device=dev) for _ in range(L)]
     idxs = [torch.empty(1, TOPK, dtype=torch.int32, device=dev) for _ in range(L)]
     wts = [torch.empty(1, TOPK, dtype=torch.float32, device=dev) for _ in range(L)]
-    ws = torch.empty(q.moe_workspace_bytes(1, EXPERTS, TOPK, HIDDEN, INTER), dtype=torch.uint8, device=dev)
+    ws = q.moe_workspace(q.moe_workspace_bytes(1, EXPERTS, TOPK, HIDDEN, INTER), dev)
     args_per_layer = [(HIDDEN, INTER, tables[l].ptr(), EXPERTS, logits[l].data_ptr(), TOPK, xs[l].data_ptr(), 1,
                        ys[l].data_ptr(), idxs[l].data_ptr(), wts[l].data_ptr(), ws.data_ptr(), ws.numel(), 0)
                       for l in range(L)]
@@ -342,7 +541,33 @@ def main() -> int:
             log("graph replay differs from eager: graph timing not used")
     torch.cuda.synchronize()
 
-    ms_step = min(ms_eager, ms_graph) if ms_graph is not None else ms_eager
+    # ---- the same step as one launch for the whole stack (layer l reads its inputs only after
+    #      layer l-1's y is stored, as separate launches order them); outputs bit-equal
+    ys_stack = [torch.empty(1, HIDDEN, dtype=torch.float16, device=dev) for _ in range(L)]
+    ltab = q.layer_table([dict(experts=tables[l], logits=logits[l], x=xs[l], y=ys_stack[l]) for l in range(L)])
+    wss = q.moe_workspace(q.decode_stack_workspace_bytes(HIDDEN, INTER, TOPK), dev)
+
+    def stack_step():
+        rc = lib.gale_moe_decode_stack(HIDDEN, INTER, EXPERTS, TOPK, L, ltab.ptr(), wss.data_ptr(), wss.numel(), 0,
+                                       torch.cuda.current_stream().cuda_stream)
+        if rc:
+            raise RuntimeError(lib.gale_last_error().decode())
+
+    for _ in range(args.warmup):
+        stack_step()
+    torch.cuda.synchronize()
+    stack_ok = all(torch.equal(a, b) for a, b in zip(ys_stack, y_eager))
+    ms_stack = time_events(stack_step, args.steps)
+    torch.cuda.synchronize()
+    sync_ok = q.sync_status(ws)[0] == 0 and q.sync_status(wss)[0] == 0
+    log(f"stack launch: {ms_stack * 1e3:.1f} us/token (outputs equal to the per-layer calls: {stack_ok}; "
+        f"synchronisation words clean: {sync_ok})")
+    if not (stack_ok and sync_ok):
+        raise RuntimeError("the stack launch differs from the per-layer calls, or a cross-workgroup wait gave up")
+
+    modes = {"layer_calls_eager": ms_eager, "layer_calls_graph": ms_graph, "stack_launch": ms_stack}
+    best_mode = min((m for m in modes if modes[m] is not None), key=lambda m: modes[m])
+    ms_step = modes[best_mode]
     bytes_per_token = 43 * TOPK * EXPERT_BYTES * L // 43
     gbps = bytes_per_token / (ms_step * 1e-3) / 1e9
 
@@ -354,7 +579,7 @@ def main() -> int:
         xb = [gen_x(seed, (0x60000 + T, l), T, HIDDEN, device=dev) for l in range(L)]
         lb = [gen_logits_normal(seed, (0x60000 + T, l), T, EXPERTS, device=dev) for l in range(L)]
         yb = torch.empty(T, HIDDEN, dtype=torch.float16, device=dev)
-        wsb = torch.empty(q.moe_workspace_bytes(T, EXPERTS, TOPK, HIDDEN, INTER), dtype=torch.uint8, device=dev)
+        wsb = q.moe_workspace(q.moe_workspace_bytes(T, EXPERTS, TOPK, HIDDEN, INTER), dev)
         uniq = [int(np.unique(torch.topk(lb[l], TOPK, dim=1).indices.cpu().numpy()).size) for l in range(L)]
         cur = [0]
 
@@ -437,6 +662,8 @@ def main() -> int:
                    "inter": INTER, "parallelism": "none (1 GPU)"},
         "tokens_per_s": round(1e3 / ms_step, 2),
         "hbm_frac_step": round(gbps / HBM_PEAK_GBPS, 4),
+        "step_mode": best_mode,
+        "ms_per_step_modes": {m: (None if v is None else round(v, 5)) for m, v in modes.items()},
         "ms_per_step_eager": round(ms_eager, 5),
         "ms_per_step_graph": None if ms_graph is None else round(ms_graph, 5),
         "bytes_per_token": bytes_per_token,
@@ -447,6 +674,21 @@ def main() -> int:
                                f"prepared activations; two disjoint sets alternated",
                      "bytes_per_launch": n * GEMV_UNIT_BYTES, "avg_launch_us": round(ms_gemv * 1e3, 2),
                      "source_sha256": gemv_source_hash()[:16]},
+        "gemv_single_matrix": {
+            "workload": "one [2048 out, 4096 in] matrix, 1 token: FWHT-1024 of x and the fp8 activation split, "
+                        "then the GEMV (two launches)",
+            "sustained": {"matrices_per_call": n, "avg_call_us": round(ms_e2e * 1e3, 2),
+                          "gbps": round(e2e_gbps, 1), "frac_of_peak": round(e2e_gbps / HBM_PEAK_GBPS, 4),
+                          "note": "each matrix with its own x; rotation + split + GEMV inside the timed call"},
+            "one_matrix_per_call": {"isolated_us": round(ms_one_iso * 1e3, 2),
+                                    "back_to_back_us": round(ms_one_tp * 1e3, 2),
+                                    "note": "launch-latency bound (two launches per call)"}},
+        "ffn": {"workload": "one expert FFN (w1, w3 [2048,4096], w2 [4096,2048]), 1 token",
+                "sustained": {"experts_per_launch": EXPERTS, "avg_launch_us": round(ms_ffn_many * 1e3, 2),
+                              "gbps": round(ffn_gbps, 1), "frac_of_peak": round(ffn_gbps / HBM_PEAK_GBPS, 4),
+                              "bytes_per_expert": FFN_UNIT_BYTES},
+                "one_expert_per_call": {"isolated_us": round(ms_ffn_one * 1e3, 2),
+                                        "back_to_back_us": round(ms_ffn_one_tp * 1e3, 2)}},
         "decode_batches": {"workload": "one MoE layer (256 experts, N(0,1) logits, top-6), the stack's layers in "
                                        "turn; GB/s on the unique experts' packed bytes", "batches": batches},
         "prefill": {"workload": f"one layer (256 experts), {PREFILL_TOKENS} tokens x hidden {HIDDEN} fp16, "
@@ -461,13 +703,17 @@ def main() -> int:
 
     if not args.no_cpu:
         import oracle as O
-        per_tok, threads, err = cpu_baseline(synth, O, seed, xs, logits, ys, min(args.cpu_layers, L))
-        out["cpu_baseline"] = {"value": round(bytes_per_token / per_tok / 1e9, 4), "unit": "GB/s", "cores": threads,
-                               "kind": "oracle", "tokens_per_s": round(1.0 / per_tok, 5),
-                               "sample": f"1 token through {min(args.cpu_layers, L)} layers (route + 6 fp64 "
-                                         f"dequantize/matvec FFNs each), scaled to 43 layers"}
+        t_cpu = time.time()
+        per_cfg, cores, model, err, n_l = cpu_baselines(synth, O, seed, dev, xs, logits, ys, L)
+        st = per_cfg["stack_token"]
+        out["cpu_baseline"] = {"value": st["gbps_all_cores"], "unit": "GB/s", "cores": cores, "kind": "oracle",
+                               "cpu_model": model, "tokens_per_s": round(1.0 / st["s_per_token_all_cores"], 5),
+                               "sample": st["sample"] + " (route + 6 fp64 dequantize/matvec FFNs per layer)",
+                               "per_workload": per_cfg}
         out["parity_rel_l2_sampled_layers"] = err
-        log(f"cpu oracle: {per_tok:.1f} s/token; GPU vs oracle rel-L2 {err:.2e}")
+        log(f"cpu oracle ({cores} cores, {model}): {st['s_per_token_all_cores']:.2f} s/token all cores, "
+            f"{st['s_per_token_1_thread']:.1f} s/token one thread; GPU step vs oracle on {n_l} layers rel-L2 "
+            f"{err:.2e}; {time.time() - t_cpu:.0f} s")
     print(json.dumps(out), flush=True)
     return 0
 

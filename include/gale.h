@@ -53,6 +53,8 @@ extern "C" {
 #define GALE_ERR_UNSUPPORTED (-6)  /* valid request the library does not implement */
 #define GALE_ERR_FORMAT      (-7)  /* canonical data violates the format */
 #define GALE_ERR_HIP         (-8)  /* a HIP runtime call failed */
+#define GALE_ERR_SYNC        (-9)  /* gale_sync_status: the one-launch decode's synchronisation words
+                                      were never zeroed, or a wait in an earlier call gave up */
 
 /* ---- dtype codes and flags ---------------------------------------------- */
 #define GALE_F16 1
@@ -68,8 +70,8 @@ extern "C" {
                                       instead of the one-launch layer kernel */
 /* Tuning knob, bits 8..11: a value v != 0 fixes the row tiles (16 rows each) per work unit
  * instead of the built-in choice.  GEMV kernels: 2^(v-1) (capped where registers run out).
- * One-token layer kernel, (gate/up, down) tiles per unit: v = 1: (1, 1); 2: (2, 2); 3: (1, 2);
- * 4: (2, 1); 5: (3, 2); 6: (3, 1).  Results do not depend on it. */
+ * One-launch decode (one token): v = 1, 2 or 3 gate/up tiles per unit (at most hidden / 1024).
+ * Results do not depend on it. */
 #define GALE_TILES_SHIFT 8
 /* Tuning knob, bits 14..15: outlier entries that a GEMV wavefront stages per work unit for
  * its 16 rows.  v = 0: 1024 (64 per row on average, the 1 % budget's 41 fit); 1: 2048;
@@ -80,6 +82,10 @@ extern "C" {
  * each halving of its columns (a budget is a share of each row).  The one-token layer
  * kernel ignores it.  Results do not depend on it. */
 #define GALE_OUTLIER_STAGE_SHIFT 14
+/* Test knob for the one-launch decode: every cross-workgroup wait gives up at once, as one whose
+ * time budget ran out would (the call then records the give-up in its synchronisation words and
+ * its outputs are unspecified).  Every kernel still ends normally. */
+#define GALE_SYNC_NO_WAIT 0x10000u
 
 /* ---- limits -------------------------------------------------------------- */
 #define GALE_FWHT_N        1024   /* rotation block ("blocked FWHT-1024") */
@@ -126,6 +132,19 @@ typedef struct gale_matrix {
 typedef struct gale_expert {
     gale_matrix w1, w3, w2;
 } gale_expert;
+
+/* The inputs and outputs of one routed-expert layer for one token (gale_moe_decode_stack).
+ * All pointers are device pointers. */
+typedef struct gale_layer_io {
+    const gale_expert* experts;  /* descriptor table of the layer's n_experts experts */
+    const float* logits;         /* fp32 [n_experts] router logits */
+    const float* select_bias;    /* fp32 [n_experts] selection bias, or NULL (as gale_moe_layer_fwd_routed) */
+    const int32_t* fixed_idx;    /* int32 [top_k] given experts, or NULL (as gale_moe_layer_fwd_routed) */
+    const void* x;               /* fp16 [hidden]; may be the previous layer's y */
+    void* y;                     /* fp16 [hidden] */
+    int32_t* topk_idx;           /* int32 [top_k], or NULL */
+    float* topk_w;               /* fp32 [top_k], or NULL */
+} gale_layer_io;
 
 /* Bytes of each packed section of one matrix. */
 typedef struct gale_sizes {
@@ -240,14 +259,16 @@ size_t gale_moe_workspace_bytes(int32_t n_tok, int32_t n_experts, int32_t top_k,
  * written when non-NULL.  Two paths, same results bit for bit on any token:
  *   decode  (n_tok <= 64): one workgroup routes all tokens and lists the work items;
  *           with one token the whole layer is a single persistent launch (the
- *           DeepSeek-V4-Pro GALE page's batch-1 notes put the floor in launches):
- *           every workgroup routes the token itself, the gate/up and down units run
- *           back to back, and counters in the workspace hand each finished block of
- *           h and each finished row group of y to the workgroup that completes it.
- *           The counters need no initialisation (they carry a generation number),
- *           so the workspace stays plain scratch, but calls sharing one workspace
- *           must not overlap in time (true of every workspace).  GALE_DECODE_STAGED
- *           selects the five-launch sequence instead (same results bit for bit);
+ *           DeepSeek-V4-Pro GALE page's batch-1 notes put the floor in launches), the
+ *           layer of gale_moe_decode_stack: every workgroup routes the token itself,
+ *           runs its gate/up units, and after a grid barrier owns 16 rows of y for all
+ *           top_k experts.  This needs the workspace's synchronisation words (its first
+ *           GALE_SYNC_BYTES bytes) zero-filled once before the first such call
+ *           (gale_sync_init, or any zero fill) and calls sharing a workspace must not
+ *           overlap in time (true of every workspace).  When the words are not valid
+ *           the call computes nothing (y is left as it was); gale_sync_status() reports
+ *           it.  GALE_DECODE_STAGED selects the five-launch sequence instead (same
+ *           results bit for bit; it does not use the synchronisation words);
  *   grouped (n_tok > 64):  chunked top-k and a stable sort of the (token, slot) pairs
  *           by expert; then experts with many pairs run a tiled GEMM on the matrix
  *           cores (128 pairs x 128 weight rows per workgroup, the weights dequantized to
@@ -260,8 +281,9 @@ size_t gale_moe_workspace_bytes(int32_t n_tok, int32_t n_experts, int32_t top_k,
  * Flags GALE_PATH_DECODE / GALE_PATH_GROUPED force a path (decode takes at most 64
  * tokens).  The workspace depends on the path (gale_moe_workspace_bytes with the same
  * flags).  hidden <= GALE_MAX_HIDDEN (else GALE_ERR_SHAPE); the single-launch layer
- * takes hidden <= 4096 with inter dividing 2 hidden in whole 1024-column blocks, other
- * shapes run the five-launch sequence. */
+ * takes hidden <= 4096 (whole 1024-column blocks; the down tasks of top_k x inter / 1024
+ * must fit its wavefronts, true of every shape with inter <= 2 hidden), other shapes run
+ * the five-launch sequence. */
 int gale_moe_layer_fwd(int32_t hidden, int32_t inter, const gale_expert* experts_dev,
                        int32_t n_experts, const float* logits, int32_t top_k, const void* x,
                        int32_t n_tok, void* y, int32_t* topk_idx, float* topk_w,
@@ -286,6 +308,46 @@ int gale_moe_layer_fwd_routed(int32_t hidden, int32_t inter, const gale_expert* 
                               const int32_t* fixed_idx, int32_t top_k, const void* x, int32_t n_tok,
                               void* y, int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
                               uint32_t flags, hipStream_t stream);
+
+/* ---- one token through a stack of layers in one launch -------------------------- */
+
+/* Bytes at the start of a one-launch decode workspace that hold its synchronisation words. */
+#define GALE_SYNC_BYTES 4608
+
+/* Workspace bytes for gale_moe_decode_stack (the synchronisation words, then fp32 h). */
+size_t gale_decode_stack_workspace_bytes(int32_t hidden, int32_t inter, int32_t top_k);
+
+/* One decode token through n_layers routed-expert layers, in one persistent launch
+ * (DeepSeek-V4-Flash GALE model card, "Measured performance": 43 layers x 6 routed experts
+ * per token; the DeepSeek-V4-Pro GALE page's batch-1 notes put the floor in launches).
+ * Layer l computes exactly gale_moe_layer_fwd of one token on layers_dev[l] (same results
+ * bit for bit), and reads its logits and x only after every row of layer l-1's y has been
+ * stored, as separate launches in stream order would: x of layer l may be y of layer l-1.
+ * layers_dev: device array of n_layers gale_layer_io (read by the kernel); at most one of
+ * select_bias / fixed_idx per layer.  hidden and inter as the one-launch layer takes them
+ * (gale_moe_layer_fwd); n_experts <= GALE_MAX_EXPERTS, top_k <= GALE_MAX_TOPK.
+ * ws: gale_decode_stack_workspace_bytes() bytes, 256-byte aligned, whose first
+ * GALE_SYNC_BYTES must have been zero-filled once (gale_sync_init) before the first call
+ * on it; if they are not valid, or a wait in an earlier call gave up, the call computes
+ * nothing and gale_sync_status() says why.  Every workgroup of the launch must be resident
+ * at once (one per CU): a wait gives up after about 10 ms, records that in the words and
+ * the kernel carries on, so it always ends.  flags: GALE_TILES_SHIFT, GALE_SYNC_NO_WAIT. */
+int gale_moe_decode_stack(int32_t hidden, int32_t inter, int32_t n_experts, int32_t top_k, int32_t n_layers,
+                          const gale_layer_io* layers_dev, void* ws, size_t ws_bytes, uint32_t flags,
+                          hipStream_t stream);
+
+/* Zero the synchronisation words at the start of ws (GALE_SYNC_BYTES; a kernel on `stream`,
+ * so it can be captured in a graph).  Needed once before the first one-launch decode call on
+ * a workspace, and again after gale_sync_status() reported GALE_ERR_SYNC. */
+int gale_sync_init(void* ws, hipStream_t stream);
+
+/* State of the synchronisation words at the start of ws, for the caller to check after its
+ * own synchronisation: copies the three header words to the host (a blocking copy, not for
+ * graph capture).  GALE_OK: valid and no wait has given up.  GALE_ERR_SYNC: the words were
+ * never zeroed, or a wait of an earlier call gave up (gale_last_error() says which); the
+ * outputs of that call are unspecified and later calls compute nothing until gale_sync_init.
+ * words_host (3 x uint64, may be NULL): generation, check word, error bits. */
+int gale_sync_status(const void* ws, uint64_t* words_host);
 
 /* Workspace bytes for gale_route_topk with grouping of more than GALE_MAX_DECODE_TOKENS tokens. */
 size_t gale_route_workspace_bytes(int32_t n_tok, int32_t n_experts);

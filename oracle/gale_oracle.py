@@ -200,21 +200,27 @@ def route(logits: np.ndarray, k: int, select_bias: Optional[np.ndarray] = None,
 
 
 def moe(expert_of, logits: np.ndarray, x: np.ndarray, k: int = 6, select_bias: Optional[np.ndarray] = None,
-        fixed_idx: Optional[np.ndarray] = None):
+        fixed_idx: Optional[np.ndarray] = None, map_fn=map):
     """y_t = sum over the k routed experts e of w[t, e] * FFN_e(x_t).
 
     ``expert_of(e)`` returns the canonical (w1, w3, w2) of expert e.  Returns
     (y fp64 [T, hidden], idx, weights).  select_bias / fixed_idx: the routing variants of
-    ``route``.
+    ``route``.  ``map_fn`` evaluates the per-expert FFNs (each an independent call of
+    ``ffn`` on that expert's tokens); a thread pool's map runs them side by side without
+    changing any result.
     """
     x = np.atleast_2d(np.asarray(x).astype(np.float64))
     idx, w = route(logits, k, select_bias, fixed_idx)
     y = np.zeros_like(x)
-    for e in np.unique(idx):
-        toks = np.nonzero((idx == e).any(axis=1))[0]
-        w1, w3, w2 = expert_of(int(e))
-        ye = ffn(w1, w3, w2, x[toks])
-        for j, t in enumerate(toks):
+    experts = [int(e) for e in np.unique(idx)]
+    toks_of = {e: np.nonzero((idx == e).any(axis=1))[0] for e in experts}
+
+    def expert_ffn(e):
+        w1, w3, w2 = expert_of(e)
+        return ffn(w1, w3, w2, x[toks_of[e]])
+
+    for e, ye in zip(experts, map_fn(expert_ffn, experts)):
+        for j, t in enumerate(toks_of[e]):
             slot = int(np.nonzero(idx[t] == e)[0][0])
             y[t] += w[t, slot] * ye[j]
     return y, idx, w

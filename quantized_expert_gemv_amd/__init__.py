@@ -11,4 +11,6 @@ from .binding import (  # noqa: F401
     pack_matrix, matrix_table, expert_table, debug_unpack_signs, debug_unpack_outliers, fwht1024,
     expert_gemv, expert_ffn, moe_layer_fwd, route_topk, gemv_workspace_bytes, ffn_workspace_bytes,
     moe_workspace_bytes, gale_tiles_flag, gale_layer_tiles_flag, GALE_OUTLIER_STAGE_SHIFT, gale_outlier_stage_flag,
+    GALE_SYNC_NO_WAIT, GALE_SYNC_BYTES, GALE_ERR_SYNC, moe_workspace, sync_init, sync_status,
+    decode_stack_workspace_bytes, layer_table, moe_decode_stack,
 )

@@ -26,8 +26,12 @@ GALE_PATH_GROUPED = 0x20
 GALE_GROUPED_ITEMS = 0x40
 GALE_GROUPED_GEMM = 0x80
 GALE_DECODE_STAGED = 0x1000
+GALE_SYNC_NO_WAIT = 0x10000
+GALE_SYNC_BYTES = 4608
+GALE_ERR_SYNC = -9
 STATUS = {0: "GALE_OK", -1: "GALE_ERR_NULL", -2: "GALE_ERR_SHAPE", -3: "GALE_ERR_DTYPE", -4: "GALE_ERR_ALIGN",
-          -5: "GALE_ERR_WORKSPACE", -6: "GALE_ERR_UNSUPPORTED", -7: "GALE_ERR_FORMAT", -8: "GALE_ERR_HIP"}
+          -5: "GALE_ERR_WORKSPACE", -6: "GALE_ERR_UNSUPPORTED", -7: "GALE_ERR_FORMAT", -8: "GALE_ERR_HIP",
+          -9: "GALE_ERR_SYNC"}
 
 
 def gale_tiles_flag(r: int) -> int:
@@ -54,9 +58,11 @@ def _with_stage(flags: int, table: "DescriptorTable") -> int:
     return flags | gale_outlier_stage_flag(table.outliers_per_row)
 
 
-def gale_layer_tiles_flag(gate_up: int, down: int) -> int:
-    """flags bits 8..11 for the one-token layer kernel: row tiles per gate/up and per down unit."""
-    return {(1, 1): 1, (2, 2): 2, (1, 2): 3, (2, 1): 4, (3, 2): 5, (3, 1): 6}[(gate_up, down)] << 8
+def gale_layer_tiles_flag(gate_up: int) -> int:
+    """flags bits 8..11 for the one-launch decode: row tiles per gate/up unit (1, 2 or 3)."""
+    if gate_up not in (1, 2, 3):
+        raise ValueError("the one-launch decode takes 1, 2 or 3 gate/up tiles per unit")
+    return gate_up << 8
 
 
 class GaleError(RuntimeError):
@@ -72,6 +78,12 @@ class gale_matrix(ctypes.Structure):
 
 class gale_expert(ctypes.Structure):
     _fields_ = [("w1", gale_matrix), ("w3", gale_matrix), ("w2", gale_matrix)]
+
+
+class gale_layer_io(ctypes.Structure):
+    _fields_ = [("experts", ctypes.c_void_p), ("logits", ctypes.c_void_p), ("select_bias", ctypes.c_void_p),
+                ("fixed_idx", ctypes.c_void_p), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("topk_idx", ctypes.c_void_p), ("topk_w", ctypes.c_void_p)]
 
 
 class gale_sizes(ctypes.Structure):
@@ -105,6 +117,10 @@ _SIGS = {
                                          _P]),
     "gale_route_workspace_bytes": (_SZ, [_I32, _I32]),
     "gale_route_topk": (_I32, [_P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
+    "gale_decode_stack_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
+    "gale_moe_decode_stack": (_I32, [_I32, _I32, _I32, _I32, _I32, _P, _P, _SZ, _U32, _P]),
+    "gale_sync_init": (_I32, [_P, _P]),
+    "gale_sync_status": (_I32, [_P, ctypes.POINTER(ctypes.c_uint64)]),
 }
 
 _lib = None
@@ -164,6 +180,14 @@ def _tdt(code: int) -> torch.dtype:
 def _workspace(nbytes: int, device) -> torch.Tensor:
     # torch's caching allocator hands out 512-byte aligned blocks
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def moe_workspace(nbytes: int, device) -> torch.Tensor:
+    """A workspace for gale_moe_layer_fwd / gale_moe_decode_stack whose synchronisation words
+    (its first GALE_SYNC_BYTES) are zeroed, as the one-launch decode needs before its first call."""
+    ws = _workspace(max(int(nbytes), GALE_SYNC_BYTES), device)
+    sync_init(ws)
+    return ws
 
 
 # ----------------------------------------------------------------------------
@@ -423,7 +447,7 @@ def moe_layer_fwd(table: DescriptorTable, hidden: int, inter: int, logits: torch
     if topk_w is None:
         topk_w = torch.empty(n_tok, top_k, dtype=torch.float32, device=x.device)
     if ws is None:
-        ws = _workspace(moe_workspace_bytes(n_tok, E, top_k, hidden, inter, flags), x.device)
+        ws = moe_workspace(moe_workspace_bytes(n_tok, E, top_k, hidden, inter, flags), x.device)
     flags = _with_stage(flags, table)
     if select_bias is None and fixed_idx is None:
         _check("gale_moe_layer_fwd", lib().gale_moe_layer_fwd(hidden, inter, table.ptr(), E, logits.data_ptr(), top_k,
@@ -461,3 +485,67 @@ def route_topk(logits: torch.Tensor, top_k: int, group: bool = False):
                                                      w.data_ptr(), _ptr(offsets), _ptr(perm), _ptr(ws),
                                                      0 if ws is None else ws.numel(), _stream()))
     return (idx, w, offsets, perm) if group else (idx, w)
+
+
+# ----------------------------------------------------------------------------
+# one token through a stack of layers; synchronisation words
+# ----------------------------------------------------------------------------
+def sync_init(ws: torch.Tensor) -> None:
+    """Zero the synchronisation words at the start of ws (a kernel on the current stream)."""
+    _require_cuda(ws)
+    _check("gale_sync_init", lib().gale_sync_init(ws.data_ptr(), _stream()))
+
+
+def sync_status(ws: torch.Tensor):
+    """(status, (generation, check, error bits), detail) of the synchronisation words of ws.
+    Blocking: call after the stream's work is done."""
+    _require_cuda(ws)
+    words = (ctypes.c_uint64 * 3)()
+    st = lib().gale_sync_status(ws.data_ptr(), words)
+    detail = lib().gale_last_error().decode() if st != GALE_OK else ""
+    if st not in (GALE_OK, GALE_ERR_SYNC):
+        raise GaleError("gale_sync_status", st, detail)
+    return st, (words[0], words[1], words[2]), detail
+
+
+def decode_stack_workspace_bytes(hidden: int, inter: int, top_k: int) -> int:
+    return int(lib().gale_decode_stack_workspace_bytes(hidden, inter, top_k))
+
+
+class LayerTable:
+    """Device array of gale_layer_io records for gale_moe_decode_stack (keeps the tensors alive)."""
+
+    def __init__(self, records: Sequence[dict], device):
+        self.keep = records
+        arr = (gale_layer_io * len(records))()
+        for i, r in enumerate(records):
+            arr[i] = gale_layer_io(*[_ptr(r.get(n)) for n, _ in gale_layer_io._fields_])
+        host = torch.frombuffer(bytearray(bytes(arr)), dtype=torch.uint8)
+        self.dev = host.to(device)
+        self.n = len(records)
+
+    def ptr(self) -> int:
+        return self.dev.data_ptr()
+
+
+def layer_table(layers: Sequence[dict], device=None) -> LayerTable:
+    """layers: per layer a dict of tensors with keys experts (DescriptorTable), logits, x, y and
+    optionally select_bias, fixed_idx, topk_idx, topk_w."""
+    recs = []
+    for r in layers:
+        d = dict(r)
+        d["experts"] = r["experts"].tensor if isinstance(r["experts"], DescriptorTable) else r["experts"]
+        recs.append(d)
+    dev = device if device is not None else recs[0]["x"].device
+    return LayerTable(recs, dev)
+
+
+def moe_decode_stack(hidden: int, inter: int, n_experts: int, top_k: int, layers: LayerTable,
+                     ws: Optional[torch.Tensor] = None, flags: int = 0) -> torch.Tensor:
+    """One token through the layers of `layers` in one launch; returns the workspace used."""
+    if ws is None:
+        ws = moe_workspace(decode_stack_workspace_bytes(hidden, inter, top_k), layers.dev.device)
+    _check("gale_moe_decode_stack", lib().gale_moe_decode_stack(hidden, inter, n_experts, top_k, layers.n,
+                                                                 layers.ptr(), ws.data_ptr(), ws.numel(), flags,
+                                                                 _stream()))
+    return ws

@@ -137,7 +137,7 @@ static FfnWs ffn_ws(int hidden, int inter, int64_t n_x, int64_t n_pairs) {
 struct MoeWs {
   size_t idx, w, offsets, perm, chunk, items, n_items, ra_x, h, ra_h, yp;   // decode / items
   size_t tiles, xt16, ht16;                                                 // grouped GEMM
-  size_t sync;                                                              // one-launch decode
+  size_t sync;                                                              // one-launch decode (offset 0)
   size_t total;
 };
 // Upper bound on the work items of T tokens: every item holds at least one pair, and
@@ -156,6 +156,9 @@ enum MoePath { kDecode = 0, kGroupedItems = 1, kGroupedGemm = 2, kGroupedHybrid 
 constexpr int kGemmMinPairs = 20;
 // Row tiles per unit of the one-token layer kernel, (gate/up, down) as decimal digits.
 constexpr int kDecodeLayerTiles = 32;
+// Give-up time of a one-launch decode wait (100 MHz ticks): 10 ms, far beyond any healthy
+// barrier (~2 us) and short enough that a launch whose workgroups are not all resident ends.
+static int64_t decode_wait_ticks(uint32_t flags) { return (flags & GALE_SYNC_NO_WAIT) ? 0 : 1000000; }
 static MoePath moe_path(int n_tok, uint32_t flags) {
   const bool grouped = (flags & GALE_PATH_GROUPED) || (!(flags & GALE_PATH_DECODE) && n_tok > GALE_MAX_DECODE_TOKENS);
   if (!grouped) return kDecode;
@@ -169,6 +172,7 @@ static MoeWs moe_ws(int T, int E, int k, int hidden, int inter, MoePath path) {
   const int64_t P = (int64_t)T * k;
   const int slots = pick_moe_slots(T, k, E, path != kDecode);
   size_t o = 0;
+  w.sync = o; o += align256(kDecodeSyncBytes);   // first, at a fixed place (gale_sync_init / _status)
   w.idx = o; o += align256(4 * P);
   w.w = o; o += align256(4 * P);
   w.offsets = o; o += align256(4 * (size_t)(E + 1));
@@ -186,9 +190,6 @@ static MoeWs moe_ws(int T, int E, int k, int hidden, int inter, MoePath path) {
     w.items = o; o += align256(sizeof(WorkItem) * (size_t)moe_item_bound(T, E, k, slots));
     w.ra_x = o; o += align256(ra_bytes(hidden) * (size_t)T);
     w.ra_h = o; o += align256(ra_bytes(inter) * (size_t)P);
-  }
-  if (path == kDecode && T == 1) {
-    w.sync = o; o += align256(decode_layer_sync_bytes(hidden, inter));
   }
   w.total = o;
   return w;
@@ -212,6 +213,7 @@ extern "C" const char* gale_status_str(int s) {
     case GALE_ERR_UNSUPPORTED: return "unsupported";
     case GALE_ERR_FORMAT: return "bad canonical format";
     case GALE_ERR_HIP: return "HIP runtime error";
+    case GALE_ERR_SYNC: return "decode synchronisation words not valid";
     default: return "unknown status";
   }
 }
@@ -555,14 +557,21 @@ static int moe_layer(const char* fn, int32_t hidden, int32_t inter, const gale_e
     tok_items.split = tok_gemm.split = pair_items.split = pair_gemm.split = split;
     tok_items.items_side = pair_items.items_side = 1;
   }
-  if (path == kDecode && n_tok == 1 && !(flags & GALE_DECODE_STAGED) && decode_layer_supported(hidden, inter)) {
-    // one launch for the whole layer; the counters live in the workspace
-    // tiles per unit of (gate/up, down), as decimal digits; see GALE_TILES_SHIFT
-    static const int kLayerTiles[7] = {kDecodeLayerTiles, 11, 22, 12, 21, 32, 31};
+  if (path == kDecode && n_tok == 1 && !(flags & GALE_DECODE_STAGED) && decode_layer_supported(hidden, inter, top_k)) {
+    // one launch for the whole layer; its synchronisation words start the workspace
+    gale_layer_io io;
+    io.experts = experts_dev;
+    io.logits = logits;
+    io.select_bias = select_bias;
+    io.fixed_idx = fixed_idx;
+    io.x = x;
+    io.y = y;
+    io.topk_idx = topk_idx;
+    io.topk_w = topk_w;
     const int forced = (int)((flags >> GALE_TILES_SHIFT) & 0xF);
-    return hip_status(fn, launch_decode_layer(table, n_experts, rin, top_k, x, hidden, inter, y, topk_idx, topk_w,
-                                              h, yp, reinterpret_cast<uint64_t*>(base + W.sync),
-                                              kLayerTiles[forced <= 6 ? forced : 0], stream));
+    return hip_status(fn, launch_decode_stack(io, nullptr, 1, n_experts, top_k, hidden, inter, h,
+                                              reinterpret_cast<uint64_t*>(base + W.sync), forced,
+                                              decode_wait_ticks(flags), stream));
   }
   if (path == kDecode) {
     st = hip_status(fn, launch_route_prep(rin, n_tok, n_experts, top_k, idx, wts, items, n_items, slots, x,
@@ -658,4 +667,79 @@ extern "C" int gale_route_topk(const float* logits, int32_t n_tok, int32_t n_exp
   // top-k only, any number of tokens: the chunked kernel without grouping
   return hip_status(fn, launch_route_large(RouteIn{logits, nullptr, nullptr}, n_tok, n_experts, top_k, topk_idx,
                                            topk_w, nullptr, nullptr, nullptr, stream));
+}
+
+// ============================================================================
+// one token through a stack of layers; the synchronisation words
+// ============================================================================
+extern "C" size_t gale_decode_stack_workspace_bytes(int32_t hidden, int32_t inter, int32_t top_k) {
+  if (hidden < 1024 || inter < 1024 || top_k < 1 || top_k > GALE_MAX_TOPK) return 0;
+  return align256(kDecodeSyncBytes) + align256(decode_stack_h_bytes(inter, top_k));
+}
+
+// Host validation shared by the two stack entry points (ws == NULL is checked by the caller).
+static int decode_stack_check(const char* fn, int32_t hidden, int32_t inter, int32_t n_experts, int32_t top_k,
+                              int32_t n_layers, const gale_layer_io* layers_dev) {
+  int st = check_matrix_shape(fn, inter, hidden);
+  if (st) return st;
+  st = check_matrix_shape(fn, hidden, inter);
+  if (st) return st;
+  if (n_layers < 1) { set_error("%s: n_layers=%d", fn, n_layers); return GALE_ERR_SHAPE; }
+  if (n_experts < 1 || n_experts > GALE_MAX_EXPERTS || top_k < 1 || top_k > GALE_MAX_TOPK || top_k > n_experts) {
+    set_error("%s: n_experts=%d top_k=%d out of range", fn, n_experts, top_k);
+    return GALE_ERR_SHAPE;
+  }
+  if (!decode_layer_supported(hidden, inter, top_k)) {
+    set_error("%s: hidden=%d inter=%d top_k=%d is not a shape of the one-launch decode", fn, hidden, inter, top_k);
+    return GALE_ERR_UNSUPPORTED;
+  }
+  if (!layers_dev) { set_error("%s: NULL pointer", fn); return GALE_ERR_NULL; }
+  if (!aligned(layers_dev, 8)) { set_error("%s: misaligned pointer", fn); return GALE_ERR_ALIGN; }
+  return GALE_OK;
+}
+
+extern "C" int gale_moe_decode_stack(int32_t hidden, int32_t inter, int32_t n_experts, int32_t top_k,
+                                     int32_t n_layers, const gale_layer_io* layers_dev, void* ws, size_t ws_bytes,
+                                     uint32_t flags, hipStream_t stream) {
+  const char* fn = "gale_moe_decode_stack";
+  int st = decode_stack_check(fn, hidden, inter, n_experts, top_k, n_layers, layers_dev);
+  if (st) return st;
+  if (!ws) { set_error("%s: NULL pointer", fn); return GALE_ERR_NULL; }
+  if (!aligned(ws, 256)) { set_error("%s: misaligned pointer", fn); return GALE_ERR_ALIGN; }
+  const size_t need = gale_decode_stack_workspace_bytes(hidden, inter, top_k);
+  if (ws_bytes < need) { set_error("%s: workspace %zu < %zu bytes", fn, ws_bytes, need); return GALE_ERR_WORKSPACE; }
+  uint8_t* base = reinterpret_cast<uint8_t*>(ws);
+  float* h = reinterpret_cast<float*>(base + align256(kDecodeSyncBytes));
+  gale_layer_io none;
+  memset(&none, 0, sizeof(none));
+  const int forced = (int)((flags >> GALE_TILES_SHIFT) & 0xF);
+  return hip_status(fn, launch_decode_stack(none, layers_dev, n_layers, n_experts, top_k, hidden, inter, h,
+                                            reinterpret_cast<uint64_t*>(base), forced, decode_wait_ticks(flags),
+                                            stream));
+}
+
+extern "C" int gale_sync_init(void* ws, hipStream_t stream) {
+  const char* fn = "gale_sync_init";
+  if (!ws) { set_error("%s: NULL pointer", fn); return GALE_ERR_NULL; }
+  if (!aligned(ws, 256)) { set_error("%s: misaligned workspace", fn); return GALE_ERR_ALIGN; }
+  return hip_status(fn, launch_sync_init(ws, stream));
+}
+
+extern "C" int gale_sync_status(const void* ws, uint64_t* words_host) {
+  const char* fn = "gale_sync_status";
+  if (!ws) { set_error("%s: NULL pointer", fn); return GALE_ERR_NULL; }
+  uint64_t w[3] = {0, 0, 0};
+  const hipError_t e = hipMemcpy(w, ws, sizeof(w), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_status(fn, e);
+  if (words_host) memcpy(words_host, w, sizeof(w));
+  switch (sync_words_state(w)) {
+    case 0: return GALE_OK;
+    case 1:
+      set_error("%s: the synchronisation words were never zeroed (gale_sync_init)", fn);
+      return GALE_ERR_SYNC;
+    default:
+      set_error("%s: a cross-workgroup wait gave up in an earlier call (error bits 0x%llx); outputs of that "
+                "call are unspecified, calls compute nothing until gale_sync_init", fn, (unsigned long long)w[2]);
+      return GALE_ERR_SYNC;
+  }
 }

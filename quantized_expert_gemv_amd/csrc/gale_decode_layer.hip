@@ -1,39 +1,63 @@
-// One-launch decode of a routed-expert MoE layer for a single token.
+// One-launch decode of routed-expert MoE layers for a single token.
 //
 // What it computes is the decode MoE layer of the DeepSeek-V4-Flash GALE model
 // card ("What is in the pack": w1/w3/w2 per expert; "Measured performance": 6
-// routed experts per token and layer): top-k routing with softmax-renormalised
-// weights, the SwiGLU FFN of every selected expert out of its three GALE
-// matrices, and the weighted combine.  The DeepSeek-V4-Pro GALE page (its
-// "Measured" notes on batch-1 decode) puts the batch-1 floor in kernel launches
-// and per-expert unpacks, not in data movement; here the whole layer is one
-// persistent launch instead of five.
+// routed experts per token and layer, 43 layers): top-k routing with
+// softmax-renormalised weights, the SwiGLU FFN of every selected expert out of its
+// three GALE matrices, and the weighted combine -- for one layer, or for a stack of
+// layers run strictly one after another.  The DeepSeek-V4-Pro GALE page (its
+// "Measured" notes on batch-1 decode) puts the batch-1 floor in kernel launches and
+// per-expert unpacks, not in data movement; here each layer is two phases of one
+// persistent launch, and a stack of layers is one launch.
 //
-// Plan.  The grid is one workgroup per CU, all resident together.  Each
-// workgroup, with no help from the others:
-//   * routes the token (one wavefront; every workgroup gets the same answer) and
-//     prepares x's activation record in LDS (rotation, fp8 terms) while routing;
-//   * streams its share of the gate/up units (R row tiles of w1 and w3 of one
-//     selected expert), writing h = silu(w1 x~) * (w3 x~);
-//   * streams its share of the down units (Q x R row tiles of w2).
-// Two global dependencies are resolved with counters in the workspace:
-//   * a down unit waits until every gate/up unit of its pair has stored its rows
-//     of h, then rotates h into its own LDS record (one wavefront per 1024-block);
-//   * the down unit that completes a row group for the last of the k pairs sums
-//     the k partial outputs in slot order into y ("last arriver").
-// The down units' weight loads go out before the wait, so they are in flight while
-// the workgroup waits.  Only down units wait, only on gate/up work, and every
-// workgroup is resident, so the waits end; each is also bounded in time and records
-// a timeout in the workspace's error word rather than spinning on.
+// Plan.  The grid is one workgroup per CU, all resident together.  Per layer:
+//   R  every workgroup routes the token itself (one wavefront; the same answer
+//      everywhere) while other wavefronts rotate x into an activation record in LDS;
+//   G  gate/up: the workgroup's share of units of R row tiles of w1 and w3 of a
+//      selected expert (split-K over the 1024-column chunks, one wavefront each),
+//      writing h = silu(w1 x~) * (w3 x~); meanwhile the weights of its down tile are
+//      already on their way (issued right behind the gate/up loads);
+//   -- grid barrier: every h row is stored --
+//   D  down: the workgroup owns one row tile (16 rows of y) for ALL k pairs, so the
+//      combine needs no other workgroup: it rotates every pair's h into LDS records
+//      (each 1024-block is independent), runs the k x C_I sign tasks and the k
+//      outlier rows, and wavefront 0 sums the k outputs in slot order into y;
+//   -- grid barrier (between layers only): y is stored; the next layer may read it --
 //
-// Counters carry the call's generation in their upper 32 bits.  The workgroup that
-// combines the last down row group (after which no counter is touched again in the
-// call) re-arms every counter for the next generation; an arrival that finds a word
-// of another generation (a workspace's first use) re-tags it with a compare-and-swap,
-// so the workspace needs no initialisation.
+// A stack of layers is one token through the layers in order: layer l reads its
+// logits and x only after every row of layer l-1's y is stored, exactly as separate
+// launches would order them (x of layer l may be layer l-1's y).
+//
+// Barriers.  A workgroup arrives after its own stores have completed (s_waitcnt
+// vmcnt(0)) with one fire-and-forget device-scope atomic add on one of kSubs
+// sub-counters (workgroup b on counter b % kSubs, 128 bytes apart); wavefront 0 of
+// every workgroup polls the kSubs counters until each holds its arrivals for the
+// barrier.  Counts only grow within a call (barrier p waits for p arrivals per
+// workgroup), so a slow poller can never miss a barrier.  Measured on this part: a
+// 16-way barrier takes 1.5 us against 3.8 us for one counter and 2.6 us for a
+// kernel boundary.  Values handed between workgroups (h, y) are stored and loaded
+// with device-scope accesses; there are no device-scope fences, which would write
+// back or drop a whole XCD's L2.
+//
+// Synchronisation words (the first kDecodeSyncBytes of the workspace) and their contract:
+//   [0] G  the generation of the last call that ran on these words
+//   [1] C  check word, sync_check(G); sync_check(0) = 0, so all-zero words are a
+//          valid start (generation 1 comes next)
+//   [2] E  error bits, sticky: bit 0 = a barrier wait gave up (its time budget ran
+//          out: workgroups that were not all resident, or a forced zero budget)
+//   two sets of kSubs counters: call g counts on set g % 2 and zeroes set (g+1) % 2
+//   (last used by call g-1, which has completed) for call g+1.
+// Every workgroup reads G, C, E at its start; when C != sync_check(G) (the words were
+// never zeroed) or E != 0 (an earlier wait gave up), the call does nothing at all:
+// y is not written and the host query reports the state.  Workgroup 0 writes the new
+// G and C at its end; it has then passed the first barrier, so every workgroup has
+// read the old values.  A wait that gives up sets E and the kernel carries on (it
+// always ends); the generation moves on, so nothing of a failed call satisfies a
+// later call's waits, and the sticky E makes later calls refuse until the words are
+// zeroed again.
 //
 // The per-unit arithmetic is the sign-plane GEMV's (gale_gemv_core.h) in the same
-// order, so the outputs equal those of the multi-launch decode sequence.
+// order, so every output equals that of the five-launch decode sequence bit for bit.
 #include "gale_internal.h"
 #include "gale_decode.h"
 #include "gale_gemv_core.h"
@@ -42,87 +66,40 @@
 
 namespace gale {
 
-// ---- synchronisation words (uint64, in the workspace) -----------------------
-// sync words (each counter is spread over kSubs words, so that few arrivals meet
-// on one word):
-//   [0] generation, [1] row-group subsets combined, [2] error bits (sticky);
-//   [8 + kSubs j + s] gate/up units of pair j with row group = s (mod kSubs) done;
-//   [72 + s] down row groups = s (mod kSubs) combined;
-//   [80 + g] pairs done in down row group g.
-constexpr int kSubs = 8;
-constexpr int kSyncTop = 1;
-constexpr int kSyncErr = 2;
-constexpr int kSyncReady = 8;
-constexpr int kSyncRowSub = kSyncReady + GALE_MAX_TOPK * kSubs;
-constexpr int kSyncRows = kSyncRowSub + kSubs;
+// ---- synchronisation words --------------------------------------------------------
+constexpr int kSubs = 16;          // arrival sub-counters per set
+constexpr int kSubStride = 16;     // uint64 words between sub-counters (128 bytes)
+constexpr int kSetBase = 16;       // word of set 0, counter 0
+__host__ __device__ constexpr int sub_word(int set, int i) { return kSetBase + (set * kSubs + i) * kSubStride; }
+constexpr int kSyncWordCount = kSetBase + 2 * kSubs * kSubStride;
+static_assert((size_t)8 * kSyncWordCount <= kDecodeSyncBytes, "sync region");
+constexpr uint64_t kErrWaitGaveUp = 1;
 
-// Units of a phase with RG row groups per pair that land on sub-counter s.
-__host__ __device__ inline int sub_count(int RG, int s) { return s < RG ? (RG - s + kSubs - 1) / kSubs : 0; }
-
-__device__ __forceinline__ uint64_t sync_load(uint64_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// A bijective 64-bit mix (the finaliser of Appleby's MurmurHash3); 0 maps to 0.
+__host__ __device__ inline uint64_t sync_check(uint64_t g) {
+  g ^= g >> 33;
+  g *= 0xFF51AFD7ED558CCDull;
+  g ^= g >> 33;
+  g *= 0xC4CEB9FE1A85EC53ull;
+  g ^= g >> 33;
+  return g;
 }
 
-// One arrival at a generation-tagged counter, in two halves so that other work can
-// overlap the atomic's round trip: arrive_add issues the add, arrive_count turns its
-// reply into the count including this arrival.
-__device__ __forceinline__ uint64_t arrive_add(uint64_t* ctr) {
-  return __hip_atomic_fetch_add(ctr, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t arrive_count(uint64_t* ctr, uint64_t old, uint32_t gen) {
-  if ((uint32_t)(old >> 32) == gen) return (uint32_t)old + 1u;
-  // a word of another generation: count this arrival against the word re-tagged
-  // with this generation (the add above went to the stale value and is dropped)
-  uint64_t cur = sync_load(ctr);
-  for (;;) {
-    const uint64_t want = (uint32_t)(cur >> 32) == gen ? cur + 1u : (((uint64_t)gen << 32) | 1u);
-    if (__hip_atomic_compare_exchange_strong(ctr, &cur, want, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT))
-      return (uint32_t)want;
-  }
-}
-// One arrival at a generation-tagged counter; returns the count including it.
-__device__ __forceinline__ uint32_t arrive(uint64_t* ctr, uint32_t gen) { return arrive_count(ctr, arrive_add(ctr), gen); }
-
-// Wave 0 polls the kSubs sub-counters of one count until each reads (gen, its
-// share of RG); about 0.1 s at most, then the error word records the timeout and
-// the caller proceeds.
-constexpr int kWaitPolls = 1 << 17;
-__device__ __forceinline__ void wait_subs(uint64_t* base, uint32_t gen, int RG, uint64_t* err, int lane) {
-  const bool watch = lane < kSubs && lane < RG;
-  const uint64_t want = ((uint64_t)gen << 32) | (uint32_t)sub_count(RG, lane);
-  for (int i = 0;; ++i) {
-    const bool ok = !watch || sync_load(base + (watch ? lane : 0)) == want;
-    if (__all(ok)) break;
-    if (i == kWaitPolls) {
-      if (lane == 0) __hip_atomic_fetch_or(err, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      break;
-    }
-    __builtin_amdgcn_s_sleep(2);
-  }
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+__device__ __forceinline__ uint64_t sync_load(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// ---- data handed between workgroups --------------------------------------------
-// The workgroups of one XCD share an L2 that the other XCDs' L2s do not see, and a
-// device-scope fence would write back or drop a whole L2.  So every value that one
-// workgroup hands to another (h, its rotated records, the partial outputs) is stored
-// and loaded with device-scope (coherent) accesses, and a producer only waits for its
-// own stores to complete before it counts them.
+// ---- data handed between workgroups ----------------------------------------------
 __device__ __forceinline__ void cst_f32(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float cld_f32(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void cst_u64(void* p, uint64_t v) {
-  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void cst_u32(void* p, uint32_t v) {
+  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint64_t cld_u64(const void* p) {
   return __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<void*>(p)), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint64_t pack2(uint32_t lo, uint32_t hi) { return ((uint64_t)hi << 32) | lo; }
 
 // Wait until this wavefront's stores (and loads) have completed, with no compiler
 // reordering of memory accesses across the wait.
@@ -132,130 +109,95 @@ __device__ __forceinline__ void stores_done() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// ---- geometry of one phase for this thread ------------------------------------
-// Gate/up: wave w = (matrix half w / C, chunk w % C); a unit is R row tiles of both
-// matrices; waves 0 .. 2R-1 serve the outliers of its 2 x 16 R rows.
-// Down: wave w = (row group w / C, chunk w % C); a unit is Q row groups of R tiles;
-// waves 0 .. QR-1 serve the outliers of its 16 Q R rows.
-struct PhaseGeo {
-  int K, C, rows, ntiles;
-  int unit_tiles, grp_tile, unit_rows, orow;
-  int smat, omat;
-  bool orole;
-  uint32_t sw_tile, sc_tile, sw_lane, sc_lane;
+struct StackParams {
+  gale_layer_io io0;               // the layer of a one-layer call
+  const gale_layer_io* layers;     // [L] (device), or NULL for a one-layer call
+  int L, E, k, H, I;
+  int gu_units;                    // gate/up units per layer (R row tiles of w1 and w3 each)
+  int down_tiles;                  // 16-row tiles of y per layer
+  int kp;                          // pairs whose h records fit in LDS at once
+  float* h;                        // fp32 [k][I]
+  uint64_t* sync;                  // kDecodeSyncBytes of synchronisation words
+  int64_t wait_ticks;              // give-up time of a barrier wait (100 MHz ticks)
 };
 
-template <int R>
-__device__ __forceinline__ PhaseGeo phase_geo(bool down, int K, int rows, int wave, int lane, int Q) {
-  PhaseGeo G;
-  G.K = K;
-  G.C = K >> 10;
-  G.rows = rows;
-  G.ntiles = rows >> 4;
-  const int grp = uni(wave / G.C), c = uni(wave - grp * G.C);
-  if (down) {
-    G.unit_tiles = Q * R;
-    G.grp_tile = grp * R;
-    G.unit_rows = Q * R * 16;
-    G.orow = 16 * wave;
-    G.smat = 2;
-    G.omat = 2;
-    G.orole = wave < Q * R;
-  } else {
-    G.unit_tiles = R;
-    G.grp_tile = 0;
-    G.unit_rows = R * 16;
-    G.orow = 16 * (wave % R);
-    G.smat = grp;
-    G.omat = uni(wave < 2 * R ? wave / R : 0);
-    G.orole = wave < 2 * R;
+__device__ __forceinline__ gale_layer_io layer_io(const StackParams& P, int l) {
+  if (P.layers == nullptr) return P.io0;
+  const auto* a = as_const(P.layers) + l;
+  gale_layer_io io;
+  io.experts = a->experts;
+  io.logits = a->logits;
+  io.select_bias = a->select_bias;
+  io.fixed_idx = a->fixed_idx;
+  io.x = a->x;
+  io.y = a->y;
+  io.topk_idx = a->topk_idx;
+  io.topk_w = a->topk_w;
+  return io;
+}
+
+// Arrival of this workgroup at the next barrier of set `set` (wavefront 0, after its
+// stores have completed).
+__device__ __forceinline__ void arrive(const StackParams& P, int set, int lane) {
+  stores_done();
+  if (lane == 0)
+    (void)__hip_atomic_fetch_add(P.sync + sub_word(set, (int)(blockIdx.x % kSubs)), (uint64_t)1, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wavefront 0 waits until every workgroup has arrived at barrier `phase` (1, 2, ...)
+// of set `set`, or the time budget runs out (then E records it and the wait ends).
+__device__ __forceinline__ void wait_barrier(const StackParams& P, int set, int phase, int lane) {
+  const int nb = (int)gridDim.x;
+  const bool watch = lane < kSubs && lane < nb;
+  const uint64_t target = watch ? (uint64_t)phase * (uint64_t)((nb - lane + kSubs - 1) / kSubs) : 0;
+  const uint64_t* w = P.sync + sub_word(set, watch ? lane : 0);
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  for (;;) {
+    const bool ok = !watch || sync_load(w) >= target;
+    if (__all(ok)) break;
+    if ((int64_t)(__builtin_amdgcn_s_memrealtime() - t0) >= P.wait_ticks) {
+      if (lane == 0)
+        (void)__hip_atomic_fetch_or(P.sync + 2, kErrWaitGaveUp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
   }
-  G.sw_tile = (uint32_t)G.C * 2048u;
-  G.sc_tile = (uint32_t)G.C * 256u;
-  G.sw_lane = (uint32_t)c * 2048u + 16u * (uint32_t)lane;
-  G.sc_lane = (uint32_t)c * 256u + 16u * (uint32_t)(lane & 15);
-  return G;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// Row of this thread's outlier role in row group rg, clamped to [0, rows].
-__device__ __forceinline__ int role_row(const PhaseGeo& G, int lane, int rg, bool* valid) {
-  const int n = rg * G.unit_rows + G.orow + (lane >> 2);
-  *valid = G.orole && n < G.rows;
-  return n < G.rows ? n : G.rows;
-}
-
-struct LayerDesc {
-  const char* signs;
-  const char* scales;
-  const char* rsc;
-  const int32_t* rptr;
-  const char* ocols;
-  const char* ovals;
-};
-
-__device__ __forceinline__ LayerDesc layer_desc(const gale_matrix* table, const PhaseGeo& G, int expert) {
-  const auto* t = as_const(table) + expert * 3;
-  LayerDesc d;
-  d.signs = reinterpret_cast<const char*>(t[G.smat].signs);
-  d.scales = reinterpret_cast<const char*>(t[G.smat].block_scales);
-  d.rsc = reinterpret_cast<const char*>(t[G.omat].row_scales);
-  d.rptr = t[G.omat].row_ptr;
-  d.ocols = reinterpret_cast<const char*>(t[G.omat].out_cols);
-  d.ovals = reinterpret_cast<const char*>(t[G.omat].out_vals);
-  return d;
-}
-
-// Issue the loads of a unit at row group rg (rp0/rp1 of its row already in b), and
-// the CSR offsets of the row of the unit after it (geometry Gn, row group rgn).
-template <int R>
-__device__ __forceinline__ void issue_layer_unit(const PhaseGeo& G, int lane, int rg, const LayerDesc& dv,
-                                                 const PhaseGeo& Gn, int rgn, const LayerDesc& dn, UnitBuf<R>& b) {
-  // CSR offsets of the next unit's row first: a wait for them (at the next issue) then
-  // never waits for this unit's sign words
-  bool ok;
-  const int n2 = role_row(Gn, lane, rgn, &ok);
-  b.np0 = dn.rptr[n2];
-  b.np1 = dn.rptr[n2 + (n2 < Gn.rows ? 1 : 0)];
-  const int t0 = rg * G.unit_tiles + G.grp_tile;
+// ---- activation records -------------------------------------------------------------
+// One wavefront rotates chunk c of x (fp16; device-scope loads: x may be the previous
+// layer's y) into the record, in the coalesced layout of prep_wave, so that the record is
+// the one prep_wave makes bit for bit.
+__device__ __forceinline__ void prep_x_chunk(const void* x, int K, int c, uint8_t* rec, int lane) {
+  float f[16];
+  const uint64_t* src = reinterpret_cast<const uint64_t*>(reinterpret_cast<const char*>(x) + (size_t)c * 2048);
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    int tile = t0 + r;
-    tile = tile < G.ntiles ? tile : G.ntiles - 1;
-    const uint32_t o = (uint32_t)tile * G.sw_tile + G.sw_lane;
-    const uint4 lo = ld16_stream(dv.signs, o);
-    const uint4 hi = ld16_stream(dv.signs, o + 1024u);
-    b.sw[r][0] = lo.x; b.sw[r][1] = lo.y; b.sw[r][2] = lo.z; b.sw[r][3] = lo.w;
-    b.sw[r][4] = hi.x; b.sw[r][5] = hi.y; b.sw[r][6] = hi.z; b.sw[r][7] = hi.w;
-    const uint4 sc = ld16_stream(dv.scales, (uint32_t)tile * G.sc_tile + G.sc_lane);
-    b.sc[r][0] = sc.x; b.sc[r][1] = sc.y; b.sc[r][2] = sc.z; b.sc[r][3] = sc.w;
-  }
-  // outlier entries of the wave's 16 rows: CSR range [e0, e1) from lanes 0 and 60
-  const int e0 = uni(__builtin_amdgcn_readlane(b.rp0, 0));
-  const int e1 = uni(__builtin_amdgcn_readlane(b.rp1, 60));
-  const bool any = e1 > e0;
-  const int cf = any ? (2 * e0) >> 4 : 0;
-  const int cl = any ? (2 * e1 - 1) >> 4 : 0;
-  const int vf = any ? (e0 >> 1) >> 4 : 0;
-  const int vl = any ? ((e1 - 1) >> 1) >> 4 : 0;
-  b.ocf = cf;
-  b.ovf = vf;
-#pragma unroll
-  for (int k = 0; k < kColChunks; ++k) {
-    int ch = cf + 64 * k + lane;
-    ch = ch < cl ? ch : cl;
-    b.oc[k] = ld16(dv.ocols, (uint32_t)ch * 16u);
-  }
-#pragma unroll
-  for (int k = 0; k < kValChunks; ++k) {
-    int ch = vf + 64 * k + lane;
-    ch = ch < vl ? ch : vl;
-    b.ov[k] = ld16(dv.ovals, (uint32_t)ch * 16u);
-  }
-  const int n = role_row(G, lane, rg, &ok);
-  b.rsc = *reinterpret_cast<const uint16_t*>(dv.rsc + 2u * (uint32_t)(n < G.rows ? n : G.rows - 1));
+  for (int i = 0; i < 4; ++i) unpack_f16x4(cld_u64(src + 64 * i + lane), f + 4 * i);
+  PrepLane o;
+  prep_lane(f, lane, true, o);
+  store_record_chunk(o, GALE_F16, rec, K, c, lane);
 }
 
-// A operands and exponent of chunk c from an activation record (LDS or global).
+// Rotation of one pair's h (fp32, written by other workgroups) into an activation record
+// in LDS, as prep_wave would: the block's device-scope loads, then the record chunk.
+__device__ __forceinline__ void load_h_block(const float* hv, int c, int lane, float f[16]) {
+  const uint64_t* src = reinterpret_cast<const uint64_t*>(hv + (size_t)c * 1024);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint64_t q = cld_u64(src + 64 * j + lane);
+    f[2 * j] = __uint_as_float((uint32_t)q);
+    f[2 * j + 1] = __uint_as_float((uint32_t)(q >> 32));
+  }
+}
+__device__ __forceinline__ void rotate_h_block(const float f[16], int K, int c, uint8_t* rec, int lane) {
+  PrepLane o;
+  prep_lane(f, lane, true, o);
+  store_record_chunk(o, GALE_F32, rec, K, c, lane);
+}
+
+// A operands and exponent of chunk c from an activation record in LDS.
 __device__ __forceinline__ void record_activation(const uint8_t* rec, int K, int c, int lane, Act& a) {
   const int nl = lane & 15, g = lane >> 4;
   const int term = nl >> 2;
@@ -273,93 +215,69 @@ __device__ __forceinline__ void record_activation(const uint8_t* rec, int K, int
   a.pexp[0] = reinterpret_cast<const int32_t*>(rec + ra_p_off(K))[c];
 }
 
-// One wavefront rotates 1024-block c of h (written by other workgroups; coherent
-// loads) into an activation record in LDS: the arithmetic of prep_wave.
-__device__ __forceinline__ void prep_block_to_lds(const float* hv, int K, int c, uint8_t* rec, int lane) {
-  float f[16];
-  const float* src = hv + (size_t)c * 1024 + 16 * lane;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint64_t q = cld_u64(src + 2 * i);
-    f[2 * i] = __uint_as_float((uint32_t)q);
-    f[2 * i + 1] = __uint_as_float((uint32_t)(q >> 32));
-  }
-  PrepLane o;
-  prep_lane(f, lane, true, o);
-  float4* xo = reinterpret_cast<float4*>(reinterpret_cast<float*>(rec) + (size_t)c * 1024 + 16 * lane);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) xo[i] = make_float4(o.x[4 * i], o.x[4 * i + 1], o.x[4 * i + 2], o.x[4 * i + 3]);
-  uint8_t* terms = rec + ra_terms_off(K) + (size_t)c * 4 * 1024 + 16 * lane;
-#pragma unroll
-  for (int t = 0; t < kTerms; ++t)
-    *reinterpret_cast<uint4*>(terms + t * 1024) = make_uint4(o.t[t][0], o.t[t][1], o.t[t][2], o.t[t][3]);
-  if (lane == 0) reinterpret_cast<int32_t*>(rec + ra_p_off(K))[c] = o.p;
-}
-
-struct LayerParams {
-  const gale_matrix* table;  // [E][3]: w1, w3, w2
-  const float* logits;       // [E]
-  const float* bias;         // [E] selection bias, or NULL
-  const int32_t* fixed;      // [k] given experts, or NULL
-  const void* x;             // fp16 [H]
-  __half* y;                 // fp16 [H]
-  int32_t* topk_idx;         // [k] or NULL
-  float* topk_w;             // [k] or NULL
-  float* h;                  // fp32 [k][I]
-  float* yp;                 // fp32 [k][H]
-  uint64_t* sync;            // counters, layout below
-  int E, k, H, I, Q;
-  int RGd;                   // down row groups per pair
+// ---- outliers of one 16-row group (shared by both phases) ----------------------------
+// Loads of a group's CSR entries: the 16-byte chunks holding the uint16 columns and
+// packed int4 values of [e0, e1) (e0 from lane 0's rp0, e1 from lane 60's rp1), and
+// the row scale of the lane's row.
+struct OutBuf {
+  uint4 oc[kColChunks];
+  uint4 ov[kValChunks];
+  int ocf, ovf;
+  int rp0, rp1;
+  uint32_t rsc;
 };
 
-// LDS: the activation record of the current phase (x's, then each pair's h~), two
-// alternating sets of split-K and outlier sums, the waves' outlier slices, routing.
-template <int R>   // R: the larger of the two phases' tiles per unit
-struct LayerLds {
-  static constexpr int RR = 16 * R;
-  __host__ __device__ static size_t red_off(int H, int I) { return ra_bytes(H > I ? H : I); }
-  __host__ __device__ static size_t ored_off(int H, int I) { return red_off(H, I) + 2 * 8 * RR * 4; }
-  __host__ __device__ static size_t wout_off(int H, int I) { return ored_off(H, I) + 2 * 128 * 4; }
-  __host__ __device__ static size_t misc_off(int H, int I) { return wout_off(H, I) + 8 * (size_t)kWaveOutBytes; }
-  __host__ __device__ static size_t bytes(int H, int I) { return misc_off(H, I) + 128; }
-};
-
-// ---- the steps of a unit shared by both phases ------------------------------------
-// This unit's outlier chunks into the wave's LDS slice.
-template <int R>
-__device__ __forceinline__ void stage_outliers(const UnitBuf<R>& cur, lds_u8* wout, int lane) {
-  lds_v4* oc = reinterpret_cast<lds_v4*>(wout);
-#pragma unroll
-  for (int k = 0; k < kColChunks; ++k) oc[64 * k + lane] = to_v4(cur.oc[k]);
-#pragma unroll
-  for (int k = 0; k < kValChunks; ++k) oc[64 * (kColChunks + k) + lane] = to_v4(cur.ov[k]);
+__device__ __forceinline__ void out_issue_rp(const gale_matrix* m, int n, OutBuf& o) {
+  const int32_t* rp = as_const(m)->row_ptr;
+  o.rp0 = rp[n];
+  o.rp1 = rp[n + 1];
 }
 
-// Sign pass over the wave's R tiles: one partial sum per row into red.
-template <int R>
-__device__ __forceinline__ void sign_pass(const Act& act, const UnitBuf<R>& cur, lds_f32* red, int wave, int lane) {
-  constexpr int RR = 16 * R;
+__device__ __forceinline__ void out_issue_chunks(const gale_matrix* m, int n, int lane, OutBuf& o) {
+  const auto* mm = as_const(m);
+  const char* ocols = reinterpret_cast<const char*>(mm->out_cols);
+  const char* ovals = reinterpret_cast<const char*>(mm->out_vals);
+  const char* rsc = reinterpret_cast<const char*>(mm->row_scales);
+  const int e0 = uni(__builtin_amdgcn_readlane(o.rp0, 0));
+  const int e1 = uni(__builtin_amdgcn_readlane(o.rp1, 60));
+  const bool any = e1 > e0;
+  const int cf = any ? (2 * e0) >> 4 : 0;
+  const int cl = any ? (2 * e1 - 1) >> 4 : 0;
+  const int vf = any ? (e0 >> 1) >> 4 : 0;
+  const int vl = any ? ((e1 - 1) >> 1) >> 4 : 0;
+  o.ocf = cf;
+  o.ovf = vf;
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    float acc[1];
-    sign_tile<1>(act, cur.sw[r], cur.sc[r], acc);
-    const float v = term_sum(ldexpf(acc[0], -act.pexp[0]));
-    if (lane < 16) red[wave * RR + r * 16 + lane] = v;
+  for (int k = 0; k < kColChunks; ++k) {
+    int ch = cf + 64 * k + lane;
+    ch = ch < cl ? ch : cl;
+    o.oc[k] = ld16(ocols, (uint32_t)ch * 16u);
   }
+#pragma unroll
+  for (int k = 0; k < kValChunks; ++k) {
+    int ch = vf + 64 * k + lane;
+    ch = ch < vl ? ch : vl;
+    o.ov[k] = ld16(ovals, (uint32_t)ch * 16u);
+  }
+  o.rsc = *reinterpret_cast<const uint16_t*>(rsc + 2u * (uint32_t)n);
 }
 
-// Outliers of the wave's role rows: four lanes per row in CSR order, entries and x~
-// from LDS (entries past the staged chunks straight from the role matrix in memory).
-template <int R>
-__device__ __forceinline__ void outlier_pass(const LayerParams& L, const PhaseGeo& G, const UnitBuf<R>& cur,
-                                             bool valid, int role_pair, const int32_t* s_exp, const lds_f32* xt,
-                                             const lds_u8* wout, lds_f32* ored, int wave, int lane) {
+// Sum of r[n] q_p x~[c_p] over the row's outliers: four lanes per row walk its entries in
+// CSR order (entries from the wave's LDS slice; past the staged chunks, from memory),
+// x~ gathered from LDS.  Returns the row sum in every lane of the row (valid rows).
+__device__ __forceinline__ float outlier_row_sum(const gale_matrix* m, const OutBuf& o, bool valid, const lds_f32* xt,
+                                                 lds_u8* wout, int lane) {
+  lds_v4* st = reinterpret_cast<lds_v4*>(wout);
+#pragma unroll
+  for (int k = 0; k < kColChunks; ++k) st[64 * k + lane] = to_v4(o.oc[k]);
+#pragma unroll
+  for (int k = 0; k < kValChunks; ++k) st[64 * (kColChunks + k) + lane] = to_v4(o.ov[k]);
   const int sub = lane & 3;
   const lds_u16* lc = reinterpret_cast<const lds_u16*>(wout);
   const lds_u8* lv = wout + 64 * 16 * kColChunks;
-  float o = 0.f;
-  const int cbase = 8 * cur.ocf, vbase = 16 * cur.ovf;
-  const int p_begin = cur.rp0 + sub, p_end = valid ? cur.rp1 : p_begin;
+  float s = 0.f;
+  const int cbase = 8 * o.ocf, vbase = 16 * o.ovf;
+  const int p_begin = o.rp0 + sub, p_end = valid ? o.rp1 : p_begin;
   const int p_cap = min(cbase + 64 * 8 * kColChunks, 2 * (vbase + 64 * 16 * kValChunks));
   const int p_mid = min(p_end, p_cap);
   int p = p_begin;
@@ -371,481 +289,539 @@ __device__ __forceinline__ void outlier_pass(const LayerParams& L, const PhaseGe
 #pragma unroll
     for (int j = 0; j < 8; ++j) xv[j] = xt[col[j]];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) o = fmaf(nibble_value(by[j], p), xv[j], o);
+    for (int j = 0; j < 8; ++j) s = fmaf(nibble_value(by[j], p), xv[j], s);
   }
   for (; p < p_mid; p += 4) {
     const int col = lc[p - cbase];
     const float q = nibble_value(lv[(p >> 1) - vbase], p);
-    o = fmaf(q, xt[col], o);
+    s = fmaf(q, xt[col], s);
   }
   if (p < p_end) {
     // eight entries of the lane per step, all loads issued before the first use
-    const LayerDesc dm = layer_desc(L.table, G, uni(s_exp[role_pair]));
+    const auto* mm = as_const(m);
+    const uint16_t* gc = mm->out_cols;
+    const uint8_t* gv = mm->out_vals;
     for (; p < p_end; p += 32) {
       int col[8];
       float q[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int pj = min(p + 4 * j, p_end - 1);
-        col[j] = reinterpret_cast<const uint16_t*>(dm.ocols)[pj];
-        q[j] = p + 4 * j < p_end ? (float)outlier_value(reinterpret_cast<const uint8_t*>(dm.ovals), pj) : 0.f;
+        col[j] = gc[pj];
+        q[j] = p + 4 * j < p_end ? (float)outlier_value(gv, pj) : 0.f;
       }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) o = fmaf(q[j], xt[col[j]], o);
+      for (int j = 0; j < 8; ++j) s = fmaf(q[j], xt[col[j]], s);
     }
   }
-  const float rscale = half_bits_to_float(cur.rsc);
-  o += __shfl_xor(o, 1, 64);
-  o += __shfl_xor(o, 2, 64);
-  if (G.orole && sub == 0) ored[16 * wave + (lane >> 2)] = o * rscale;
+  s += __shfl_xor(s, 1, 64);
+  s += __shfl_xor(s, 2, 64);
+  return s * half_bits_to_float(o.rsc);
 }
 
-// ---- gate/up: units of R tiles over the flattened (pair, tile) space -------------
-// Gate/up tile t of the T = k TI tiles (TI = I / 16 per expert) is tile t % TI of pair
-// t / TI; unit u covers tiles [R u, R u + R) and may span two pairs, so that the
-// units spread evenly over the workgroups.  Readiness is counted per tile.
+// ---- phase G: gate/up units ----------------------------------------------------------
+// Tile t of the T = k TI gate/up tiles (TI = I / 16 per expert) is row tile t % TI of
+// pair t / TI; unit u covers tiles [R u, R u + R) and may span two pairs.  Wavefront w
+// reads chunk w % C_H of matrix w / C_H (w1, w3) for all R tiles; wavefronts w < 2 R
+// serve the outliers of tile w % R of matrix w / R.
+template <int R>
+struct GuBuf {
+  uint32_t sw[R][8];
+  uint32_t sc[R][4];
+  OutBuf o;
+};
+
 struct GuRole {
-  int pair, n;
+  const gale_matrix* m;   // matrix whose outliers the wave serves
+  int n;                  // the lane's row in it
   bool valid;
 };
 
-// The pair and row of this thread's outlier role in unit u (row = rows: no role).
-__device__ __forceinline__ GuRole gu_role(const PhaseGeo& G, int lane, int u, int T, int TI) {
+template <int R>
+__device__ __forceinline__ GuRole gu_role(const gale_matrix* table, const int32_t* s_exp, int wave, int lane, int u,
+                                          int T, int TI) {
   GuRole r;
-  const int t = u * G.unit_tiles + (G.orow >> 4);
-  r.valid = G.orole && t < T;
+  const int half = uni(wave < 2 * R ? wave / R : 0);
+  const int t = u * R + (wave < 2 * R ? wave % R : 0);
+  r.valid = wave < 2 * R && t < T;
   const int tc = t < T ? t : T - 1;
-  r.pair = uni(tc / TI);
-  r.n = r.valid ? (tc - r.pair * TI) * 16 + (lane >> 2) : G.rows;
+  const int pr = uni(tc / TI);
+  r.m = table + uni(s_exp[pr]) * 3 + half;
+  r.n = (tc - pr * TI) * 16 + (lane >> 2);
   return r;
 }
 
-// Issue the loads of gate/up unit u (the CSR offsets of its role row already in b) and
-// the CSR offsets of the role row of unit un.
 template <int R>
-__device__ __forceinline__ void gu_issue(const LayerParams& L, const PhaseGeo& G, const int32_t* s_exp, int lane,
-                                         int u, int un, int T, int TI, UnitBuf<R>& b) {
-  const GuRole rn = gu_role(G, lane, un, T, TI);
-  const LayerDesc dn = layer_desc(L.table, G, uni(s_exp[rn.pair]));
-  b.np0 = dn.rptr[rn.n];
-  b.np1 = dn.rptr[rn.n + (rn.n < G.rows ? 1 : 0)];
-  // sign words and block scales: the unit's tiles come from at most two pairs
-  const int tA = u * R < T ? u * R : T - 1;
-  const int tB = u * R + R - 1 < T ? u * R + R - 1 : T - 1;
-  const int pA = uni(tA / TI), pB = uni(tB / TI);
-  const auto* mA = as_const(L.table) + uni(s_exp[pA]) * 3 + G.smat;
-  const auto* mB = as_const(L.table) + uni(s_exp[pB]) * 3 + G.smat;
-  const char* sgA = reinterpret_cast<const char*>(mA->signs);
-  const char* scA = reinterpret_cast<const char*>(mA->block_scales);
-  const char* sgB = reinterpret_cast<const char*>(mB->signs);
-  const char* scB = reinterpret_cast<const char*>(mB->block_scales);
+__device__ __forceinline__ void gu_issue_weights(const gale_matrix* table, const int32_t* s_exp, int half, int c,
+                                                 int C, int lane, int u, int T, int TI, GuBuf<R>& b) {
+  const uint32_t sw_tile = (uint32_t)C * 2048u, sc_tile = (uint32_t)C * 256u;
+  const uint32_t sw_lane = (uint32_t)c * 2048u + 16u * (uint32_t)lane;
+  const uint32_t sc_lane = (uint32_t)c * 256u + 16u * (uint32_t)(lane & 15);
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     int t = u * R + r;
     t = t < T ? t : T - 1;
     const int pr = uni(t / TI);
     const int tile = t - pr * TI;
-    const char* sg = pr == pA ? sgA : sgB;
-    const char* scl = pr == pA ? scA : scB;
-    const uint32_t o = (uint32_t)tile * G.sw_tile + G.sw_lane;
+    const auto* m = as_const(table) + uni(s_exp[pr]) * 3 + half;
+    const char* sg = reinterpret_cast<const char*>(m->signs);
+    const char* scl = reinterpret_cast<const char*>(m->block_scales);
+    const uint32_t o = (uint32_t)tile * sw_tile + sw_lane;
     const uint4 lo = ld16_stream(sg, o);
     const uint4 hi = ld16_stream(sg, o + 1024u);
     b.sw[r][0] = lo.x; b.sw[r][1] = lo.y; b.sw[r][2] = lo.z; b.sw[r][3] = lo.w;
     b.sw[r][4] = hi.x; b.sw[r][5] = hi.y; b.sw[r][6] = hi.z; b.sw[r][7] = hi.w;
-    const uint4 sc = ld16_stream(scl, (uint32_t)tile * G.sc_tile + G.sc_lane);
+    const uint4 sc = ld16_stream(scl, (uint32_t)tile * sc_tile + sc_lane);
     b.sc[r][0] = sc.x; b.sc[r][1] = sc.y; b.sc[r][2] = sc.z; b.sc[r][3] = sc.w;
   }
-  // outlier entries of the wave's 16 role rows
-  const GuRole rc = gu_role(G, lane, u, T, TI);
-  const LayerDesc dc = layer_desc(L.table, G, uni(s_exp[rc.pair]));
-  const int e0 = uni(__builtin_amdgcn_readlane(b.rp0, 0));
-  const int e1 = uni(__builtin_amdgcn_readlane(b.rp1, 60));
-  const bool any = e1 > e0;
-  const int cf = any ? (2 * e0) >> 4 : 0;
-  const int cl = any ? (2 * e1 - 1) >> 4 : 0;
-  const int vf = any ? (e0 >> 1) >> 4 : 0;
-  const int vl = any ? ((e1 - 1) >> 1) >> 4 : 0;
-  b.ocf = cf;
-  b.ovf = vf;
-#pragma unroll
-  for (int k = 0; k < kColChunks; ++k) {
-    int ch = cf + 64 * k + lane;
-    ch = ch < cl ? ch : cl;
-    b.oc[k] = ld16(dc.ocols, (uint32_t)ch * 16u);
-  }
-#pragma unroll
-  for (int k = 0; k < kValChunks; ++k) {
-    int ch = vf + 64 * k + lane;
-    ch = ch < vl ? ch : vl;
-    b.ov[k] = ld16(dc.ovals, (uint32_t)ch * 16u);
-  }
-  b.rsc = *reinterpret_cast<const uint16_t*>(dc.rsc + 2u * (uint32_t)(rc.n < G.rows ? rc.n : G.rows - 1));
 }
 
-template <int R>
-__device__ __forceinline__ void gu_unit(const LayerParams& L, const PhaseGeo& G, int wave, int lane, int u, int T,
-                                        int TI, UnitBuf<R>& cur, UnitBuf<R>& nxt, bool issue, int un, int unn,
-                                        bool& act_ready, Act& act, uint8_t* rec, lds_f32* red, lds_f32* ored,
-                                        lds_u8* wout, const int32_t* s_exp) {
-  constexpr int RR = 16 * R;
-  // 1. x's activation record (LDS), once
-  if (!act_ready) {
-    record_activation(rec, G.K, uni(wave % G.C), lane, act);
-    __syncthreads();
-    block_sums<1>(act);
-    act_ready = true;
-  }
-  // 2-5. outlier staging, the next unit's loads, sign pass, outliers
-  stage_outliers<R>(cur, wout, lane);
-  if (issue) {
-    nxt.rp0 = cur.np0;
-    nxt.rp1 = cur.np1;
-    gu_issue<R>(L, G, s_exp, lane, un, unn, T, TI, nxt);
-  }
-  sign_pass<R>(act, cur, red, wave, lane);
-  const GuRole role = gu_role(G, lane, u, T, TI);
-  outlier_pass<R>(L, G, cur, role.valid, role.pair, s_exp, (const lds_f32*)rec, wout, ored, wave, lane);
-  // every wave's partials are in LDS; the buffers alternate between units
-  __syncthreads();
-  // 6. wave 0: split-K sums in a fixed order plus outliers, h = silu(a) g per row
-  if (wave != 0) return;
-  for (int rr = lane; rr < RR; rr += 64) {
-    const int t = u * R + (rr >> 4);
-    if (t >= T) continue;
-    const int pr = t / TI;
-    const int n = (t - pr * TI) * 16 + (rr & 15);
-    float a = 0.f, g = 0.f;
-    for (int q = 0; q < G.C; ++q) a += red[q * RR + rr];
-    for (int q = 0; q < G.C; ++q) g += red[(G.C + q) * RR + rr];
-    a = a + ored[rr];
-    g = g + ored[RR + rr];
-    cst_f32(L.h + (size_t)pr * L.I + n, silu_f(a) * g);
+// ---- phase D: the down tasks of one workgroup ---------------------------------------
+// Wavefronts 1 .. W-1 (Wd of them) take the k C_I sign tasks (pair s / C_I, chunk
+// s % C_I) round robin, slot s / Wd; the k outlier rows (one 16-row group per pair) go
+// round robin from the last wavefront down, slot j / Wd.  Wavefront 0 combines.
+template <int NT, int NO>
+struct DownBuf {
+  uint32_t sw[NT][8];
+  uint32_t sc[NT][4];
+  OutBuf o[NO];
+};
+
+__device__ __forceinline__ int sign_task(int wd, int slot, int Wd) { return wd + slot * Wd; }
+__device__ __forceinline__ int out_task(int wd, int slot, int Wd) { return (Wd - 1 - wd) + slot * Wd; }
+
+template <int NT, int NO>
+__device__ __forceinline__ void down_issue_rp(const gale_matrix* table, const int32_t* s_exp, int k, int Wd, int wd,
+                                              int tile, int lane, DownBuf<NT, NO>& b) {
+#pragma unroll
+  for (int i = 0; i < NO; ++i) {
+    const int j = out_task(wd, i, Wd);
+    if (j < k) out_issue_rp(table + uni(s_exp[j]) * 3 + 2, tile * 16 + (lane >> 2), b.o[i]);
   }
 }
 
-// Gate/up units [u0, u1), pipelined one unit ahead; then wave 0 waits for its stores of
-// h and counts every tile of its units on the tile's pair (sub-counter tile % kSubs).
-template <int R>
-__device__ __forceinline__ void run_gu(const LayerParams& L, const PhaseGeo& G, int wave, int lane, int u0, int u1,
-                                       int T, int TI, uint8_t* rec, lds_f32* red0, lds_f32* ored0, lds_u8* wout,
-                                       const int32_t* s_exp, uint32_t gen, bool armed) {
-  constexpr int RR = 16 * R;
-  if (u0 < u1) {
-    UnitBuf<R> b0, b1;
-    Act act;
-    bool act_ready = false;
-    {
-      const GuRole r0 = gu_role(G, lane, u0, T, TI);
-      const LayerDesc d0 = layer_desc(L.table, G, uni(s_exp[r0.pair]));
-      b0.rp0 = d0.rptr[r0.n];
-      b0.rp1 = d0.rptr[r0.n + (r0.n < G.rows ? 1 : 0)];
-      gu_issue<R>(L, G, s_exp, lane, u0, u0 + 1 < u1 ? u0 + 1 : u0, T, TI, b0);
-    }
-    for (int u = u0;;) {
-      gu_unit<R>(L, G, wave, lane, u, T, TI, b0, b1, u + 1 < u1, u + 1, u + 2 < u1 ? u + 2 : u1 - 1, act_ready, act,
-                 rec, red0, ored0, wout, s_exp);
-      if (++u >= u1) break;
-      gu_unit<R>(L, G, wave, lane, u, T, TI, b1, b0, u + 1 < u1, u + 1, u + 2 < u1 ? u + 2 : u1 - 1, act_ready, act,
-                 rec, red0 + 8 * RR, ored0 + 128, wout, s_exp);
-      if (++u >= u1) break;
-    }
-  }
-  if (wave == 0) {
-    stores_done();
-    for (int v = lane; v < (u1 - u0) * R; v += 64) {
-      const int t = u0 * R + v;
-      if (t >= T) continue;
-      const int pr = t / TI;
-      uint64_t* w = L.sync + kSyncReady + kSubs * pr + (t - pr * TI) % kSubs;
-      if (armed) (void)__hip_atomic_fetch_add(w, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      else (void)arrive(w, gen);
+template <int NT, int NO>
+__device__ __forceinline__ void down_issue_weights(const gale_matrix* table, const int32_t* s_exp, int k, int C,
+                                                   int Wd, int wd, int tile, int lane, DownBuf<NT, NO>& b) {
+  const uint32_t sw_lane = 16u * (uint32_t)lane, sc_lane = 16u * (uint32_t)(lane & 15);
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    const int s = sign_task(wd, i, Wd);
+    if (s < k * C) {
+      const int j = uni(s / C), c = uni(s - j * C);
+      const auto* m = as_const(table) + uni(s_exp[j]) * 3 + 2;
+      const char* sg = reinterpret_cast<const char*>(m->signs);
+      const char* scl = reinterpret_cast<const char*>(m->block_scales);
+      const uint32_t o = ((uint32_t)tile * C + c) * 2048u + sw_lane;
+      const uint4 lo = ld16_stream(sg, o);
+      const uint4 hi = ld16_stream(sg, o + 1024u);
+      b.sw[i][0] = lo.x; b.sw[i][1] = lo.y; b.sw[i][2] = lo.z; b.sw[i][3] = lo.w;
+      b.sw[i][4] = hi.x; b.sw[i][5] = hi.y; b.sw[i][6] = hi.z; b.sw[i][7] = hi.w;
+      const uint4 sc = ld16_stream(scl, ((uint32_t)tile * C + c) * 256u + sc_lane);
+      b.sc[i][0] = sc.x; b.sc[i][1] = sc.y; b.sc[i][2] = sc.z; b.sc[i][3] = sc.w;
     }
   }
 }
 
-// ---- down: units of Q row groups of R tiles of one pair's w2 ------------------------
-template <int R>
-__device__ __forceinline__ void down_unit(const LayerParams& L, const PhaseGeo& G, int wave, int lane, int pair,
-                                          int rg, UnitBuf<R>& cur, UnitBuf<R>& nxt, bool issue, int n_rg,
-                                          const LayerDesc& d1, int nn_rg, const LayerDesc& d2, int& act_key,
-                                          Act& act, uint8_t* rec, lds_f32* red, lds_f32* ored, lds_u8* wout,
-                                          const int32_t* s_exp, const float* s_w, uint32_t gen, int TI) {
-  constexpr int RR = 16 * R;
-  // 1. the pair's h~ record: once every gate/up tile of the pair has stored its rows of
-  //    h, rotate h into this workgroup's LDS record (one wavefront per 1024-block)
-  if (pair != act_key) {
-    if (wave == 0) wait_subs(L.sync + kSyncReady + kSubs * pair, gen, TI, L.sync + kSyncErr, lane);
-    __syncthreads();
-    if (wave < G.C) prep_block_to_lds(L.h + (size_t)pair * L.I, G.K, wave, rec, lane);
-    __syncthreads();
-    record_activation(rec, G.K, uni(wave % G.C), lane, act);
-    __syncthreads();
-    block_sums<1>(act);
-    act_key = pair;
-  }
-  // 2-5. outlier staging, the next unit's loads, sign pass, outliers
-  stage_outliers<R>(cur, wout, lane);
-  if (issue) {
-    nxt.rp0 = cur.np0;
-    nxt.rp1 = cur.np1;
-    issue_layer_unit<R>(G, lane, n_rg, d1, G, nn_rg, d2, nxt);
-  }
-  sign_pass<R>(act, cur, red, wave, lane);
-  bool valid;
-  (void)role_row(G, lane, rg, &valid);
-  outlier_pass<R>(L, G, cur, valid, pair, s_exp, (const lds_f32*)rec, wout, ored, wave, lane);
-  __syncthreads();
-
-  // 6. wave 0: split-K sums plus outliers into the pair's partial output; the last pair
-  //    of a row group to arrive combines the row group
-  if (wave != 0) return;
-  const int Q = L.Q;
-  for (int e = lane; e < Q * RR; e += 64) {
-    const int q = e / RR, rr = e - q * RR;
-    float a = 0.f;
-    for (int c = 0; c < G.C; ++c) a += red[(q * G.C + c) * RR + rr];
-    a = a + ored[q * RR + rr];
-    cst_f32(L.yp + (size_t)pair * L.H + rg * Q * RR + e, a);
-  }
-  stores_done();
-  uint32_t cnt = 0;
-  if (lane == 0) cnt = arrive(L.sync + kSyncRows + rg, gen);
-  cnt = (uint32_t)__builtin_amdgcn_readfirstlane((int)cnt);
-  if (cnt != (uint32_t)L.k) return;
-  // the last pair of this row group.  Every unit of the call has now made its last
-  // access to the gate/up and row-group counters, so this row group is counted towards
-  // the re-arm straight away (the count's round trip overlaps the combine); then
-  // y = sum over slots in order of w_j yp_j.
-  const int sub = rg % kSubs;
-  uint64_t sub_old = 0;
-  if (lane == 0) sub_old = arrive_add(L.sync + kSyncRowSub + sub);
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  for (int e = lane; e < Q * RR; e += 64) {
-    const int n = rg * Q * RR + e;
-    float v[GALE_MAX_TOPK];
+template <int NT, int NO>
+__device__ __forceinline__ void down_issue_chunks(const gale_matrix* table, const int32_t* s_exp, int k, int Wd,
+                                                  int wd, int tile, int lane, DownBuf<NT, NO>& b) {
 #pragma unroll
-    for (int j = 0; j < GALE_MAX_TOPK; ++j) v[j] = j < L.k ? cld_f32(L.yp + (size_t)j * L.H + n) : 0.f;
-    float acc = 0.f;
-#pragma unroll
-    for (int j = 0; j < GALE_MAX_TOPK; ++j)
-      if (j < L.k) acc = fmaf(s_w[j], v[j], acc);
-    L.y[n] = __float2half_rn(acc);
-  }
-  // the last row group to be combined re-arms the counters for the next generation
-  uint32_t c1 = 0, c2 = 0;
-  if (lane == 0) {
-    c1 = arrive_count(L.sync + kSyncRowSub + sub, sub_old, gen);
-    if (c1 == (uint32_t)sub_count(L.RGd, sub)) c2 = arrive(L.sync + kSyncTop, gen);
-  }
-  c2 = (uint32_t)__builtin_amdgcn_readfirstlane((int)c2);
-  if (c2 == (uint32_t)(L.RGd < kSubs ? L.RGd : kSubs)) {
-    const int words = kSyncRows + L.RGd;
-    const uint64_t next = (uint64_t)(gen + 1u) << 32;
-    for (int i = lane; i < words; i += 64)
-      if (i != 0 && i != kSyncErr) __hip_atomic_store(L.sync + i, next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (lane == 0) __hip_atomic_store(L.sync, (uint64_t)(gen + 1u), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int i = 0; i < NO; ++i) {
+    const int j = out_task(wd, i, Wd);
+    if (j < k) out_issue_chunks(table + uni(s_exp[j]) * 3 + 2, tile * 16 + (lane >> 2), lane, b.o[i]);
   }
 }
 
-// Descriptors of expert e's matrices that this wavefront reads in phase G.
-__device__ __forceinline__ LayerDesc phase_desc(const LayerParams& L, const PhaseGeo& G, const int32_t* s_exp,
-                                                int pair) {
-  return layer_desc(L.table, G, uni(s_exp[pair]));
+// LDS of the kernel.  The record region holds x's activation record during phases R and
+// G, then the h records of up to kp pairs during phase D.
+struct StackLds {
+  size_t rec, red, ored, dpart, dout, wout, misc, total;
+};
+__host__ __device__ inline StackLds stack_lds(int H, int I, int k, int kp, int W, int R) {
+  StackLds s;
+  const size_t rb = ra_bytes(H), rh = (size_t)kp * ra_bytes(I);
+  s.rec = 0;
+  s.red = (rb > rh ? rb : rh);
+  s.ored = s.red + (size_t)2 * W * 16 * R * 4;          // two alternating sets
+  s.dpart = s.ored + (size_t)2 * 2 * 16 * R * 4;
+  s.dout = s.dpart + (size_t)2 * k * (I >> 10) * 16 * 4;
+  s.wout = s.dout + (size_t)2 * k * 16 * 4;
+  s.misc = s.wout + (size_t)W * kWaveOutBytes;
+  s.total = s.misc + 128;
+  return s;
 }
 
-// Down units [u0, u1) (unit u = pair u / RG, row group u % RG), pipelined one unit
-// ahead; rp0/rp1: the CSR offsets of unit u0's role row.  The first unit's loads go out
-// before its activation is waited for.
-template <int R>
-__device__ __forceinline__ void run_down(const LayerParams& L, const PhaseGeo& G, int wave, int lane, int u0, int u1,
-                                         int RG, uint8_t* rec, lds_f32* red0, lds_f32* ored0, lds_u8* wout,
-                                         const int32_t* s_exp, const float* s_w, uint32_t gen, int TI, int rp0,
-                                         int rp1) {
-  constexpr int RR = 16 * R;
-  if (u0 >= u1) return;
-  UnitBuf<R> b0, b1;
-  Act act;
-  int act_key = -1;
-  int u = u0;
-  int pair = uni(u / RG), rg = uni(u - pair * RG);
-  int u_1 = u + 1 < u1 ? u + 1 : u;
-  int pair1 = uni(u_1 / RG), rg1 = uni(u_1 - pair1 * RG);
-  int u_2 = u + 2 < u1 ? u + 2 : u_1;
-  int pair2 = uni(u_2 / RG), rg2 = uni(u_2 - pair2 * RG);
-  LayerDesc dc = phase_desc(L, G, s_exp, pair);
-  LayerDesc d1 = pair1 == pair ? dc : phase_desc(L, G, s_exp, pair1);
-  LayerDesc d2 = pair2 == pair1 ? d1 : phase_desc(L, G, s_exp, pair2);
-  b0.rp0 = rp0;   // the CSR offsets of unit u0's role row, fetched by the caller
-  b0.rp1 = rp1;
-  issue_layer_unit<R>(G, lane, rg, dc, G, rg1, d1, b0);
-  for (;;) {
-    down_unit<R>(L, G, wave, lane, pair, rg, b0, b1, u + 1 < u1, rg1, d1, rg2, d2, act_key, act, rec, red0, ored0,
-                 wout, s_exp, s_w, gen, TI);
-    if (++u >= u1) break;
-    pair = pair1; rg = rg1; pair1 = pair2; rg1 = rg2; d1 = d2;
-    u_2 = u + 2 < u1 ? u + 2 : u1 - 1;
-    { const int pn = uni(u_2 / RG); rg2 = uni(u_2 - pn * RG); if (pn != pair2) d2 = phase_desc(L, G, s_exp, pn); pair2 = pn; }
-    down_unit<R>(L, G, wave, lane, pair, rg, b1, b0, u + 1 < u1, rg1, d1, rg2, d2, act_key, act, rec, red0 + 8 * RR,
-                 ored0 + 128, wout, s_exp, s_w, gen, TI);
-    if (++u >= u1) break;
-    pair = pair1; rg = rg1; pair1 = pair2; rg1 = rg2; d1 = d2;
-    u_2 = u + 2 < u1 ? u + 2 : u1 - 1;
-    { const int pn = uni(u_2 / RG); rg2 = uni(u_2 - pn * RG); if (pn != pair2) d2 = phase_desc(L, G, s_exp, pn); pair2 = pn; }
-  }
+// Warm the L2 of this workgroup's XCD with its share of a layer's descriptor table (the
+// workgroups of an XCD split it), so that the descriptor reads after routing hit it.
+__device__ __forceinline__ void warm_table(const gale_matrix* table, int E, int lane, uint32_t* sink) {
+  const int per_xcd = ((int)gridDim.x + 7) / 8;
+  const int lines = (int)((3 * (size_t)E * sizeof(gale_matrix) + 127) / 128);
+  const int share = (lines + per_xcd - 1) / per_xcd;
+  const int first = (int)(blockIdx.x / 8) * share;
+  uint32_t v = 0;
+  for (int i = lane; i < share && first + i < lines; i += 64)
+    v ^= *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(table) + (size_t)(first + i) * 128);
+  if (v == 0x9E3779B9u) *sink = v;   // keeps the loads; the value itself is unused
 }
 
-template <int RG, int RD>
-__global__ void __launch_bounds__(512) decode_layer_kernel(const LayerParams L) {
+template <int R, int NT, int NO>
+__global__ void __launch_bounds__(512) decode_stack_kernel(const StackParams P) {
   extern __shared__ __align__(16) unsigned char smem[];
-  using LL = LayerLds<(RG > RD ? RG : RD)>;
   const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
-  uint8_t* rec = reinterpret_cast<uint8_t*>(smem);
-  lds_f32* red0 = (lds_f32*)(smem + LL::red_off(L.H, L.I));
-  lds_f32* ored0 = (lds_f32*)(smem + LL::ored_off(L.H, L.I));
-  lds_u8* wout = (lds_u8*)(smem + LL::wout_off(L.H, L.I)) + wave * kWaveOutBytes;
-  int32_t* s_exp = reinterpret_cast<int32_t*>(smem + LL::misc_off(L.H, L.I));
+  const int W = (int)(blockDim.x >> 6), Wd = W - 1, wd = wave - 1;
+  const int C_H = P.H >> 10, C_I = P.I >> 10;
+  const int TI = P.I >> 4, T = P.k * TI;
+  constexpr int RR = 16 * R;
+  const StackLds LL = stack_lds(P.H, P.I, P.k, P.kp, W, R);
+  uint8_t* rec = smem + LL.rec;
+  lds_f32* red0 = (lds_f32*)(smem + LL.red);
+  lds_f32* ored0 = (lds_f32*)(smem + LL.ored);
+  lds_f32* dpart0 = (lds_f32*)(smem + LL.dpart);
+  lds_f32* dout0 = (lds_f32*)(smem + LL.dout);
+  lds_u8* wout = (lds_u8*)(smem + LL.wout) + wave * kWaveOutBytes;
+  int32_t* s_exp = reinterpret_cast<int32_t*>(smem + LL.misc);
   float* s_w = reinterpret_cast<float*>(s_exp + 8);
-  uint32_t* s_gen = reinterpret_cast<uint32_t*>(s_exp + 16);
+  uint32_t* s_hdr = reinterpret_cast<uint32_t*>(s_exp + 16);
 
-  // route (wave 0) while waves 1 .. C_H prepare x's record in LDS.  Wave 0 also
-  // reads the generation and the gate/up counters: when every one this call uses
-  // already carries the generation (re-armed by the previous call), gate/up units
-  // count themselves without waiting for the atomic's reply.
-  const int C_H = L.H >> 10;
-  const int W = (int)(blockDim.x >> 6);
+  // the generation of this call, or nothing at all when the words are not valid
   if (wave == 0) {
-    topk_wave(RouteIn{L.logits, L.bias, L.fixed}, 0, L.E, L.k, lane, s_exp, s_w, s_exp);
-  } else if (wave <= C_H) {
-    prep_wave(L.x, GALE_F16, L.H, 1, L.H, 0, rec, ra_bytes(L.H), wave - 1);
-  }
-  if (wave == W - 2 && W - 2 > C_H) {
-    // warm this XCD's L2 with its share of the layer's descriptor table, so that the
-    // descriptor reads after routing hit it (workgroups are dispatched to the XCDs in
-    // turn; a different placement only makes this prefetch less useful)
-    const int per_xcd = ((int)gridDim.x + 7) / 8;
-    const int lines = (int)((3 * (size_t)L.E * sizeof(gale_matrix) + 127) / 128);
-    const int share = (lines + per_xcd - 1) / per_xcd;
-    const int first = (int)(blockIdx.x / 8) * share;
-    uint32_t sink = 0;
-    for (int i = lane; i < share && first + i < lines; i += 64)
-      sink ^= *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(L.table) + (size_t)(first + i) * 128);
-    if (sink == 0x9E3779B9u) s_gen[3] = sink;   // keeps the loads; the value itself is unused
-  }
-  if (wave == W - 1) {
-    const uint64_t g64 = sync_load(L.sync);
-    const uint64_t rw = sync_load(L.sync + kSyncReady + lane);
-    const uint32_t g = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)g64);
-    const bool used = lane / kSubs < L.k && lane % kSubs < (L.I >> 4);
-    const bool all_armed = __all(!used || (uint32_t)(rw >> 32) == g);
+    const uint64_t v = lane < 3 ? sync_load(P.sync + lane) : 0;
+    const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+    const uint64_t G = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, 0) << 32) |
+                       (uint32_t)__builtin_amdgcn_readlane((int)lo, 0);
+    const uint64_t C = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, 1) << 32) |
+                       (uint32_t)__builtin_amdgcn_readlane((int)lo, 1);
+    const uint64_t E = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, 2) << 32) |
+                       (uint32_t)__builtin_amdgcn_readlane((int)lo, 2);
     if (lane == 0) {
-      s_gen[0] = g;
-      s_gen[1] = all_armed ? 1u : 0u;
+      const uint64_t g = G + 1;
+      s_hdr[0] = (uint32_t)g;
+      s_hdr[1] = (uint32_t)(g >> 32);
+      s_hdr[2] = (C == sync_check(G) && E == 0) ? 1u : 0u;
     }
   }
   __syncthreads();
-  const uint32_t gen = s_gen[0];
-  const bool armed = s_gen[1] != 0;
-  if (blockIdx.x == 0 && tid < L.k) {
-    if (L.topk_idx) L.topk_idx[tid] = s_exp[tid];
-    if (L.topk_w) L.topk_w[tid] = s_w[tid];
-  }
+  if (s_hdr[2] == 0) return;
+  const uint64_t gen = ((uint64_t)s_hdr[1] << 32) | s_hdr[0];
+  const int set = (int)(gen & 1);
+  // zero the other set for the next call (the previous call, its last user, has ended)
+  if (wave == 1 && lane < kSubs)
+    __hip_atomic_store(P.sync + sub_word(set ^ 1, lane), (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-  // gate/up units, then down units: contiguous shares of each phase
-  const int TI = L.I >> 4, T = L.k * TI;
-  const int GU = (T + RG - 1) / RG, DN = L.k * L.RGd;
   const int nb = (int)gridDim.x, b = (int)blockIdx.x;
-  const int d0 = (int)((int64_t)DN * b / nb), d1 = (int)((int64_t)DN * (b + 1) / nb);
-  // the CSR offsets of the first down unit's role row, fetched now so that they are in
-  // registers when the down phase starts
-  int dn_rp0 = 0, dn_rp1 = 0;
-  if (d0 < d1) {
-    const PhaseGeo GD = phase_geo<RD>(true, L.I, L.H, wave, lane, L.Q);
-    const int pair = uni(d0 / L.RGd), rg = uni(d0 - pair * L.RGd);
-    const LayerDesc dd = phase_desc(L, GD, s_exp, pair);
-    bool ok;
-    const int r0 = role_row(GD, lane, rg, &ok);
-    dn_rp0 = dd.rptr[r0];
-    dn_rp1 = dd.rptr[r0 + (r0 < GD.rows ? 1 : 0)];
+  const int gu0 = (int)((int64_t)P.gu_units * b / nb), gu1 = (int)((int64_t)P.gu_units * (b + 1) / nb);
+  const int dt0 = (int)((int64_t)P.down_tiles * b / nb), dt1 = (int)((int64_t)P.down_tiles * (b + 1) / nb);
+  const int half = uni(wave / C_H), cq = uni(wave - half * C_H);
+  int phase = 0;
+
+  for (int l = 0; l < P.L; ++l) {
+    const gale_layer_io io = layer_io(P, l);
+    const gale_matrix* table = reinterpret_cast<const gale_matrix*>(io.experts);
+    if (l > 0) {
+      // the previous layer's y is complete before this layer reads anything
+      if (wave == 0) wait_barrier(P, set, phase, lane);
+      __syncthreads();
+    }
+    // ---- R: route (wave 0) while waves 1 .. C_H rotate x into the record
+    if (wave == 0) {
+      topk_wave(RouteIn{io.logits, io.select_bias, io.fixed_idx}, 0, P.E, P.k, lane, s_exp, s_w, s_exp);
+    } else if (wave <= C_H) {
+      prep_x_chunk(io.x, P.H, wave - 1, rec, lane);
+    } else if (wave == W - 1 && l == 0) {
+      warm_table(table, P.E, lane, s_hdr + 3);
+    }
+    __syncthreads();
+    if (b == 0 && tid < P.k) {
+      if (io.topk_idx) io.topk_idx[tid] = s_exp[tid];
+      if (io.topk_w) io.topk_w[tid] = s_w[tid];
+    }
+
+    // ---- G: gate/up units, then (waves 1 ..) the first down tile's loads.
+    // the down tasks' loads (prefetched during gate/up when a wave has at most two sign
+    // tasks and one outlier row; the larger task sets load each task when it runs)
+    constexpr bool kPrefetch = NT <= 2 && NO <= 1;
+    GuBuf<R> gb;
+    DownBuf<NT, NO> db;
+    const bool down_tasks = kPrefetch && wave >= 1 && dt0 < dt1;
+    if (gu0 < gu1) {
+      Act act;
+      record_activation(rec, P.H, cq, lane, act);
+      block_sums<1>(act);
+      for (int u = gu0; u < gu1; ++u) {
+        const int par = (u - gu0) & 1;
+        lds_f32* red = red0 + par * (W * RR);
+        lds_f32* ored = ored0 + par * (2 * RR);
+        const GuRole r = gu_role<R>(table, s_exp, wave, lane, u, T, TI);
+        if (wave < 2 * R) out_issue_rp(r.m, r.n, gb.o);
+        gu_issue_weights<R>(table, s_exp, half, cq, C_H, lane, u, T, TI, gb);
+        if (wave < 2 * R) out_issue_chunks(r.m, r.n, lane, gb.o);
+        // sign pass over the wave's R tiles: one partial per row
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          float acc[1];
+          sign_tile<1>(act, gb.sw[r], gb.sc[r], acc);
+          const float v = term_sum(ldexpf(acc[0], -act.pexp[0]));
+          if (lane < 16) red[wave * RR + r * 16 + lane] = v;
+          __builtin_amdgcn_sched_barrier(0);   // one tile's eight products in registers at a time
+        }
+        if (wave < 2 * R) {
+          const float s = outlier_row_sum(r.m, gb.o, r.valid, (const lds_f32*)rec, wout, lane);
+          if ((lane & 3) == 0) ored[16 * wave + (lane >> 2)] = s;
+        }
+        __syncthreads();
+        // wave 0: split-K sums in a fixed order plus outliers, h = silu(a) g per row
+        if (wave == 0) {
+          for (int rr = lane; rr < RR; rr += 64) {
+            const int t = u * R + (rr >> 4);
+            if (t >= T) continue;
+            const int pr = t / TI;
+            const int n = (t - pr * TI) * 16 + (rr & 15);
+            float a = 0.f, g = 0.f;
+            for (int q = 0; q < C_H; ++q) a += red[q * RR + rr];
+            for (int q = 0; q < C_H; ++q) g += red[(C_H + q) * RR + rr];
+            a = a + ored[rr];
+            g = g + ored[RR + rr];
+            cst_f32(P.h + (size_t)pr * P.I + n, silu_f(a) * g);
+          }
+        }
+      }
+    }
+    // the first down tile's loads (waves 1 ..; wave 0 holds no loads at its arrival): they travel
+    // while the h stores complete and the barrier fills
+    if (down_tasks) {
+      down_issue_rp<NT, NO>(table, s_exp, P.k, Wd, wd, dt0, lane, db);
+      down_issue_weights<NT, NO>(table, s_exp, P.k, C_I, Wd, wd, dt0, lane, db);
+      down_issue_chunks<NT, NO>(table, s_exp, P.k, Wd, wd, dt0, lane, db);
+    }
+    ++phase;
+    if (wave == 0) arrive(P, set, lane);
+    if (wave == W - 1 && W - 1 > 0 && l + 1 < P.L) {
+      // the next layer's descriptors into L2 while the barrier completes
+      const gale_layer_io nio = layer_io(P, l + 1);
+      warm_table(reinterpret_cast<const gale_matrix*>(nio.experts), P.E, lane, s_hdr + 3);
+    }
+    if (wave == 0) wait_barrier(P, set, phase, lane);
+    __syncthreads();
+
+    // ---- D: this workgroup's down tiles, all k pairs each
+    const int npass = (P.k + P.kp - 1) / P.kp;
+    for (int tile = dt0; tile < dt1; ++tile) {
+      const int par = (tile - dt0) & 1;
+      lds_f32* dpart = dpart0 + par * (P.k * C_I * 16);
+      lds_f32* dout = dout0 + par * (P.k * 16);
+      if (kPrefetch && tile > dt0 && wave >= 1) {
+        down_issue_rp<NT, NO>(table, s_exp, P.k, Wd, wd, tile, lane, db);
+        down_issue_weights<NT, NO>(table, s_exp, P.k, C_I, Wd, wd, tile, lane, db);
+        down_issue_chunks<NT, NO>(table, s_exp, P.k, Wd, wd, tile, lane, db);
+      }
+      for (int ps = 0; ps < npass; ++ps) {
+        const int j0 = ps * P.kp, j1 = min(P.k, j0 + P.kp);
+        // rotate the pass's pairs once per layer when they all fit, else once per tile and pass
+        if (npass > 1 || tile == dt0) {
+          if (npass > 1 && (tile > dt0 || ps > 0)) __syncthreads();   // the previous pass's reads are done
+          // blocks wave, wave + W, ...: two at a time, both blocks' loads in flight together
+          const int nblk = (j1 - j0) * C_I;
+          for (int blk = wave; blk < nblk; blk += 2 * W) {
+            const int blk2 = blk + W;
+            const int jl = blk / C_I, c = blk - jl * C_I;
+            const int jl2 = blk2 / C_I, c2 = blk2 - jl2 * C_I;
+            float fa[16], fb[16];
+            load_h_block(P.h + (size_t)(j0 + jl) * P.I, c, lane, fa);
+            if (blk2 < nblk) load_h_block(P.h + (size_t)(j0 + jl2) * P.I, c2, lane, fb);
+            rotate_h_block(fa, P.I, c, rec + (size_t)jl * ra_bytes(P.I), lane);
+            __builtin_amdgcn_sched_barrier(0);   // one block's transform at a time (registers)
+            if (blk2 < nblk) rotate_h_block(fb, P.I, c2, rec + (size_t)jl2 * ra_bytes(P.I), lane);
+          }
+          __syncthreads();
+        }
+        if (wave >= 1) {
+          // one task at a time (a rolled loop: the registers of one task's operands and
+          // products); the slot's weights are picked from the prefetched set
+#pragma unroll 1
+          for (int i = 0; i < NT; ++i) {
+            const int s = sign_task(wd, i, Wd);
+            const int j = s / C_I;
+            if (s < P.k * C_I && j >= j0 && j < j1) {
+              const int c = s - j * C_I;
+              uint32_t w[8], sc[4];
+              if constexpr (kPrefetch) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) w[e] = i == 0 ? db.sw[0][e] : db.sw[NT - 1][e];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sc[e] = i == 0 ? db.sc[0][e] : db.sc[NT - 1][e];
+              } else {
+                // the larger task sets load each task's weights when it runs
+                const int sj = s / C_I;
+                const auto* m = as_const(table) + uni(s_exp[sj]) * 3 + 2;
+                const char* sg = reinterpret_cast<const char*>(m->signs);
+                const char* scl = reinterpret_cast<const char*>(m->block_scales);
+                const uint32_t o = ((uint32_t)tile * C_I + c) * 2048u + 16u * (uint32_t)lane;
+                const uint4 lo = ld16_stream(sg, o);
+                const uint4 hi = ld16_stream(sg, o + 1024u);
+                const uint4 sv = ld16_stream(scl, ((uint32_t)tile * C_I + c) * 256u + 16u * (uint32_t)(lane & 15));
+                w[0] = lo.x; w[1] = lo.y; w[2] = lo.z; w[3] = lo.w; w[4] = hi.x; w[5] = hi.y; w[6] = hi.z; w[7] = hi.w;
+                sc[0] = sv.x; sc[1] = sv.y; sc[2] = sv.z; sc[3] = sv.w;
+              }
+              Act act;
+              record_activation(rec + (size_t)(j - j0) * ra_bytes(P.I), P.I, c, lane, act);
+              block_sums<1>(act);
+              float acc[1];
+              sign_tile<1>(act, w, sc, acc);
+              const float v = term_sum(ldexpf(acc[0], -act.pexp[0]));
+              if (lane < 16) dpart[s * 16 + lane] = v;
+            }
+          }
+#pragma unroll 1
+          for (int i = 0; i < NO; ++i) {
+            const int j = out_task(wd, i, Wd);
+            if (j < P.k && j >= j0 && j < j1) {
+              OutBuf o;
+              if constexpr (kPrefetch) {
+                o = db.o[0];
+              } else {
+                const gale_matrix* m2 = table + uni(s_exp[j]) * 3 + 2;
+                out_issue_rp(m2, tile * 16 + (lane >> 2), o);
+                out_issue_chunks(m2, tile * 16 + (lane >> 2), lane, o);
+              }
+              const lds_f32* xt = (const lds_f32*)(rec + (size_t)(j - j0) * ra_bytes(P.I));
+              const float s = outlier_row_sum(table + uni(s_exp[j]) * 3 + 2, o, true, xt, wout, lane);
+              if ((lane & 3) == 0) dout[j * 16 + (lane >> 2)] = s;
+            }
+          }
+        }
+      }
+      __syncthreads();
+      // wave 0: y = sum over slots in order of w_j (sum over chunks in order + outliers)
+      if (wave == 0 && lane < 16) {
+        float acc = 0.f;
+        for (int j = 0; j < P.k; ++j) {
+          float a = 0.f;
+          for (int c = 0; c < C_I; ++c) a += dpart[(j * C_I + c) * 16 + lane];
+          a = a + dout[j * 16 + lane];
+          acc = fmaf(s_w[j], a, acc);
+        }
+        const __half yh = __float2half_rn(acc);
+        const uint32_t bits = (uint32_t)__half_as_ushort(yh);
+        const uint32_t other = (uint32_t)__builtin_amdgcn_ds_swizzle((int)bits, 0x041F);   // lane ^ 1
+        if ((lane & 1) == 0)
+          cst_u32(reinterpret_cast<__half*>(io.y) + tile * 16 + lane, bits | (other << 16));
+      }
+    }
+    if (l + 1 < P.L) {
+      ++phase;
+      if (wave == 0) arrive(P, set, lane);
+    }
   }
-  {
-    const PhaseGeo GG = phase_geo<RG>(false, L.H, L.I, wave, lane, L.Q);
-    run_gu<RG>(L, GG, wave, lane, (int)((int64_t)GU * b / nb), (int)((int64_t)GU * (b + 1) / nb), T, TI, rec, red0,
-               ored0, wout, s_exp, gen, armed);
-  }
-  {
-    const PhaseGeo GD = phase_geo<RD>(true, L.I, L.H, wave, lane, L.Q);
-    run_down<RD>(L, GD, wave, lane, d0, d1, L.RGd, rec, red0, ored0, wout, s_exp, s_w, gen, TI, dn_rp0, dn_rp1);
+  // workgroup 0 (which passed the first barrier, so every workgroup has read the
+  // words) records this call's generation for the next call
+  if (b == 0 && tid == 0) {
+    __hip_atomic_store(P.sync + 1, sync_check(gen), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(P.sync + 0, gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
-size_t decode_layer_sync_bytes(int hidden, int inter) {
-  // the largest layout: one tile per unit (the most down row groups)
-  (void)inter;
-  const int words = kSyncRows + hidden / 16;
-  static_assert(kSyncReady + GALE_MAX_TOPK * kSubs <= kSyncRowSub, "sync layout");
-  return (size_t)8 * words;
+// ---- host side ----------------------------------------------------------------------
+// Down tasks per wavefront of a shape, or 0 when they do not fit the built variants.
+static int down_slots(int hidden, int inter, int k, int* nt, int* no) {
+  const int W = 2 * (hidden >> 10), Wd = W - 1, C_I = inter >> 10;
+  if (Wd < 1) return 0;
+  const int need_t = (k * C_I + Wd - 1) / Wd, need_o = (k + Wd - 1) / Wd;
+  if (need_t <= 2 && need_o <= 1) { *nt = 2; *no = 1; return 1; }   // prefetched during gate/up
+  if (need_t <= 4 && need_o <= 2) { *nt = 4; *no = 2; return 1; }   // loaded task by task
+  return 0;
 }
 
-// Shapes the kernel's wave layout covers: 2 C_H wavefronts per workgroup (at most 8),
-// split evenly into down row groups of C_I wavefronts.
-bool decode_layer_supported(int hidden, int inter) {
-  if (hidden % 1024 || inter % 1024) return false;
-  const int C_H = hidden >> 10, C_I = inter >> 10;
-  return C_H >= 1 && C_H <= 4 && C_I >= 1 && C_I <= 2 * C_H && (2 * C_H) % C_I == 0;
+static int pairs_per_pass(int hidden, int inter, int k, int R) {
+  const int W = 2 * (hidden >> 10);
+  for (int kp = k; kp >= 1; --kp)
+    if (stack_lds(hidden, inter, k, kp, W, R).total <= kGemvMaxLds) return kp;
+  return 0;
 }
 
-template <int RG, int RD>
-static hipError_t launch_layer_r(LayerParams L, hipStream_t s) {
-  const int W = 2 * (L.H >> 10);
-  L.Q = W / (L.I >> 10);
-  L.RGd = L.H / (16 * RD * L.Q);
-  const int64_t gu_units = ((int64_t)L.k * (L.I >> 4) + RG - 1) / RG;
-  const size_t smem = LayerLds<(RG > RD ? RG : RD)>::bytes(L.H, L.I);
-  const int block = 64 * W;
+bool decode_layer_supported(int hidden, int inter, int top_k) {
+  if (hidden % 1024 || inter % 1024 || hidden < 1024 || hidden > 4096 || inter < 1024) return false;
+  if (top_k < 1 || top_k > GALE_MAX_TOPK) return false;
+  int nt, no;
+  if (!down_slots(hidden, inter, top_k, &nt, &no)) return false;
+  return pairs_per_pass(hidden, inter, top_k, 1) >= 1;
+}
+
+size_t decode_stack_h_bytes(int inter, int top_k) { return (size_t)4 * inter * top_k; }
+
+template <int R, int NT, int NO>
+static hipError_t launch_stack_r(StackParams P, hipStream_t s) {
+  const int W = 2 * (P.H >> 10);
+  const size_t smem = stack_lds(P.H, P.I, P.k, P.kp, W, R).total;
+  auto kern = &decode_stack_kernel<R, NT, NO>;
   if (smem > 65536) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_layer_kernel<RG, RD>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
   }
   int occ = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, decode_layer_kernel<RG, RD>, block, smem) != hipSuccess ||
-      occ < 1)
-    occ = 1;
-  // every workgroup must be resident at once (down units wait on gate/up units)
-  const int64_t units = std::max<int64_t>(gu_units, (int64_t)L.k * L.RGd);
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, 64 * W, smem) != hipSuccess || occ < 1) occ = 1;
+  // every workgroup must be resident at once (the barriers wait for all of them)
+  const int64_t units = std::max<int64_t>(P.gu_units, P.down_tiles);
   const int64_t grid = std::min<int64_t>(units, (int64_t)device_cu_count() * occ);
-  hipLaunchKernelGGL((decode_layer_kernel<RG, RD>), dim3((unsigned)grid), dim3(block), smem, s, L);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * W), smem, s, P);
   return hipGetLastError();
 }
 
-hipError_t launch_decode_layer(const gale_matrix* table, int E, const RouteIn& rin, int k, const void* x,
-                               int hidden, int inter, void* y, int32_t* topk_idx, float* topk_w, float* h,
-                               float* yp, uint64_t* sync, int tiles, hipStream_t s) {
-  LayerParams L;
-  L.table = table;
-  L.logits = rin.logits;
-  L.bias = rin.bias;
-  L.fixed = rin.fixed;
-  L.x = x;
-  L.y = reinterpret_cast<__half*>(y);
-  L.topk_idx = topk_idx;
-  L.topk_w = topk_w;
-  L.h = h;
-  L.yp = yp;
-  L.sync = sync;
-  L.E = E;
-  L.k = k;
-  L.H = hidden;
-  L.I = inter;
-  L.Q = 1;
-  L.RGd = 1;
-  // tiles = 10 x (gate/up tiles per unit) + (down tiles per unit), each 1 or 2; R tiles
-  // need R <= C_H (gate/up outlier roles) and R <= C_I (down)
+template <int R>
+static hipError_t launch_stack_t(StackParams P, int nt, int no, hipStream_t s) {
+  if (nt == 2 && no == 1) return launch_stack_r<R, 2, 1>(P, s);
+  return launch_stack_r<R, 4, 2>(P, s);
+}
+
+hipError_t launch_decode_stack(const gale_layer_io& io0, const gale_layer_io* layers_dev, int L, int E, int k,
+                               int hidden, int inter, float* h, uint64_t* sync, int tiles, int64_t wait_ticks,
+                               hipStream_t s) {
+  StackParams P;
+  P.io0 = io0;
+  P.layers = layers_dev;
+  P.L = L;
+  P.E = E;
+  P.k = k;
+  P.H = hidden;
+  P.I = inter;
+  P.h = h;
+  P.sync = sync;
+  P.wait_ticks = wait_ticks;
   const int C_H = hidden >> 10;
-  const int tg = tiles / 10 <= C_H ? tiles / 10 : C_H, td = (inter >> 10) >= 2 ? tiles % 10 : 1;
-  if (tg >= 3) return td == 2 ? launch_layer_r<3, 2>(L, s) : launch_layer_r<3, 1>(L, s);
-  if (tg == 2) return td == 2 ? launch_layer_r<2, 2>(L, s) : launch_layer_r<2, 1>(L, s);
-  return td == 2 ? launch_layer_r<1, 2>(L, s) : launch_layer_r<1, 1>(L, s);
+  int R = tiles >= 1 && tiles <= 3 ? tiles : 3;   // gate/up tiles per unit; 2 R wavefronts serve the outliers
+  R = R <= C_H ? R : C_H;
+  P.gu_units = (k * (inter >> 4) + R - 1) / R;
+  P.down_tiles = hidden >> 4;
+  P.kp = pairs_per_pass(hidden, inter, k, R);
+  int nt = 0, no = 0;
+  if (P.kp < 1 || !down_slots(hidden, inter, k, &nt, &no)) return hipErrorInvalidValue;
+  if (R == 3) return launch_stack_t<3>(P, nt, no, s);
+  if (R == 2) return launch_stack_t<2>(P, nt, no, s);
+  return launch_stack_t<1>(P, nt, no, s);
+}
+
+}  // namespace gale
+
+namespace gale {
+
+// Zero the synchronisation words (a kernel rather than a memset, so that a captured
+// graph replays it faithfully).
+__global__ void sync_init_kernel(uint64_t* w, int n) {
+  for (int i = (int)threadIdx.x; i < n; i += (int)blockDim.x) w[i] = 0;
+}
+
+hipError_t launch_sync_init(void* sync, hipStream_t s) {
+  hipLaunchKernelGGL(sync_init_kernel, dim3(1), dim3(256), 0, s, reinterpret_cast<uint64_t*>(sync),
+                     (int)(kDecodeSyncBytes / 8));
+  return hipGetLastError();
+}
+
+// Host check of the three header words read back by the caller.
+int sync_words_state(const uint64_t words[3]) {
+  if (words[1] != sync_check(words[0])) return 1;   // never zeroed (or overwritten)
+  if (words[2] != 0) return 2;                      // a wait gave up
+  return 0;
 }
 
 }  // namespace gale

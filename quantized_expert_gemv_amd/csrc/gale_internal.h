@@ -187,13 +187,18 @@ hipError_t launch_grouped_gemm(const gale_matrix* table, int gateup, int rows, i
                                const int32_t* perm, int top_k, const GemmTile* tiles, const int32_t* n_tiles,
                                int max_tiles, const uint16_t* A, float* out, int out_stride, hipStream_t s);
 
-// one-launch decode MoE layer for a single token (route, gate/up + SwiGLU, rotate h,
-// down, combine); sync: decode_layer_sync_bytes(hidden, inter) bytes of counters
-bool decode_layer_supported(int hidden, int inter);
-size_t decode_layer_sync_bytes(int hidden, int inter);
-hipError_t launch_decode_layer(const gale_matrix* table, int E, const RouteIn& rin, int k, const void* x,
-                               int hidden, int inter, void* y, int32_t* topk_idx, float* topk_w, float* h,
-                               float* yp, uint64_t* sync, int tiles, hipStream_t s);
+// one-launch decode of one token through one MoE layer or a stack of layers (route, gate/up +
+// SwiGLU, rotate h, down, combine per layer); sync: kDecodeSyncBytes of synchronisation words
+// (zero-filled before the first call), h: decode_stack_h_bytes(inter, top_k) of fp32 h
+constexpr size_t kDecodeSyncBytes = GALE_SYNC_BYTES;
+bool decode_layer_supported(int hidden, int inter, int top_k);
+size_t decode_stack_h_bytes(int inter, int top_k);
+hipError_t launch_decode_stack(const gale_layer_io& io0, const gale_layer_io* layers_dev, int L, int E, int k,
+                               int hidden, int inter, float* h, uint64_t* sync, int tiles, int64_t wait_ticks,
+                               hipStream_t s);
+hipError_t launch_sync_init(void* sync, hipStream_t s);
+// 0: valid and no error; 1: the words were never zeroed; 2: a barrier wait gave up
+int sync_words_state(const uint64_t words[3]);
 
 void set_error(const char* fmt, ...);
 

@@ -61,14 +61,16 @@ __device__ __forceinline__ void store16(void* blk, int dtype, int lane, const fl
 }
 
 // One butterfly stage over lane bit B: with a the lower lane's value and b the upper
-// lane's, the lower lane becomes a + b and the upper lane a - b.
+// lane's, the lower lane becomes a + b and the upper lane a - b, each as one fused
+// multiply-add by +-1 of the own value onto the partner's (exact multiply, one rounding:
+// the same result as the separate add or subtract).
 template <int B>
 __device__ __forceinline__ void fwht_lane_stage(float v[16], int lane) {
-  const bool upper = (lane & B) != 0;
+  const float sgn = (lane & B) != 0 ? -1.0f : 1.0f;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
     const float u = lane_xor<B>(v[e]);
-    v[e] = upper ? (u - v[e]) : (v[e] + u);
+    v[e] = fmaf(sgn, v[e], u);
   }
 }
 
@@ -162,6 +164,71 @@ __device__ __forceinline__ void prep_lane(const float in[16], int lane, bool rot
   o.p = p;
 }
 
+// ---------------------------------------------------------------------------
+// Coalesced lane layout of a 1024-block for the activation record: every load moves
+// 8-byte granules, consecutive lanes on consecutive granules, so one load instruction
+// covers 512 contiguous bytes.  The butterfly is a product over the ten index bits, so
+// any assignment of index bits to (register, lane) bits computes the same transform; the
+// order of the stages, and so the rounding, depends on the layout, which is therefore
+// fixed per input dtype and shared by every path that prepares records:
+//   fp32: register r of lane l holds element 128 (r >> 1) + 2 l + (r & 1)
+//   fp16: register r of lane l holds element 256 (r >> 2) + 4 l + (r & 3)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void unpack_f16x4(uint64_t q, float* f) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    __half_raw r;
+    r.x = (unsigned short)(q >> (16 * e));
+    f[e] = __half2float(__half(r));
+  }
+}
+
+// Plain loads of a block in the coalesced layout of its dtype.
+__device__ __forceinline__ void load_block_coalesced(const void* blk, int dtype, int lane, float v[16]) {
+  const uint64_t* g = reinterpret_cast<const uint64_t*>(blk);
+  if (dtype == GALE_F16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) unpack_f16x4(g[64 * i + lane], v + 4 * i);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint64_t q = g[64 * j + lane];
+      v[2 * j] = __uint_as_float((uint32_t)q);
+      v[2 * j + 1] = __uint_as_float((uint32_t)(q >> 32));
+    }
+  }
+}
+
+// Store chunk c of a record from one lane's prepared values, in the layout of `dtype`
+// (the dtype the block was loaded in).  rec may be global memory or LDS.
+__device__ __forceinline__ void store_record_chunk(const PrepLane& o, int dtype, uint8_t* rec, int K, int c,
+                                                   int lane) {
+  float* xo = reinterpret_cast<float*>(rec) + (size_t)c * 1024;
+  uint8_t* terms = rec + ra_terms_off(K) + (size_t)c * 4 * 1024;
+  if (dtype == GALE_F16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      reinterpret_cast<float4*>(xo)[64 * i + lane] = make_float4(o.x[4 * i], o.x[4 * i + 1], o.x[4 * i + 2],
+                                                                 o.x[4 * i + 3]);
+#pragma unroll
+    for (int t = 0; t < kTerms; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) reinterpret_cast<uint32_t*>(terms + t * 1024)[64 * i + lane] = o.t[t][i];
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) reinterpret_cast<float2*>(xo)[64 * j + lane] = make_float2(o.x[2 * j], o.x[2 * j + 1]);
+#pragma unroll
+    for (int t = 0; t < kTerms; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        // the word of registers 4q .. 4q+3 holds elements of granules 2q (low half) and 2q + 1
+        reinterpret_cast<uint16_t*>(terms + t * 1024)[64 * (2 * q) + lane] = (uint16_t)(o.t[t][q] & 0xFFFF);
+        reinterpret_cast<uint16_t*>(terms + t * 1024)[64 * (2 * q + 1) + lane] = (uint16_t)(o.t[t][q] >> 16);
+      }
+  }
+  if (lane == 0) reinterpret_cast<int32_t*>(rec + ra_p_off(K))[c] = o.p;
+}
+
 // One wavefront prepares one (vector, 1024-chunk) of the activation record.
 __device__ __forceinline__ void prep_wave(const void* __restrict__ x, int x_dtype, int64_t x_stride, int n_vec,
                                           int K, int rotated, uint8_t* __restrict__ ra, size_t ra_stride,
@@ -173,16 +240,10 @@ __device__ __forceinline__ void prep_wave(const void* __restrict__ x, int x_dtyp
   const int c = (int)(wave - v * C);
   const size_t isz = x_dtype == GALE_F16 ? 2 : 4;
   float f[16];
-  load16(reinterpret_cast<const char*>(x) + (v * x_stride + (int64_t)c * 1024) * isz, x_dtype, lane, f);
+  load_block_coalesced(reinterpret_cast<const char*>(x) + (v * x_stride + (int64_t)c * 1024) * isz, x_dtype, lane, f);
   PrepLane o;
   prep_lane(f, lane, !rotated, o);
-  uint8_t* rec = ra + v * ra_stride;
-  store16(reinterpret_cast<float*>(rec) + c * 1024, GALE_F32, lane, o.x);
-  uint8_t* terms = rec + ra_terms_off(K) + (size_t)c * 4 * 1024;
-#pragma unroll
-  for (int t = 0; t < kTerms; ++t)
-    *reinterpret_cast<uint4*>(terms + t * 1024 + 16 * lane) = make_uint4(o.t[t][0], o.t[t][1], o.t[t][2], o.t[t][3]);
-  if (lane == 0) reinterpret_cast<int32_t*>(rec + ra_p_off(K))[c] = o.p;
+  store_record_chunk(o, x_dtype, ra + v * ra_stride, K, c, lane);
 }
 
 }  // namespace gale

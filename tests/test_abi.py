@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
 
 def test_status_strings():
     L = q.lib()
-    for code in range(0, -9, -1):
+    for code in range(0, -10, -1):
         assert L.gale_status_str(code).decode() != "unknown status"
 
 
@@ -166,3 +166,20 @@ def test_descriptor_refuses_null_sections():
         bad.descriptor()
     assert B._padded16(torch.zeros(0, dtype=torch.int16)).numel() == 16
     assert B._padded16(torch.zeros(9, dtype=torch.int16)).numel() == 32
+
+
+def test_decode_stack_validation_before_gpu_work():
+    """gale_moe_decode_stack rejects bad requests on the host, before anything is enqueued."""
+    L = q.lib()
+    ws_bytes = q.decode_stack_workspace_bytes(4096, 2048, 6)
+    assert ws_bytes >= q.GALE_SYNC_BYTES + 4 * 2048 * 6
+    assert q.decode_stack_workspace_bytes(4096, 2048, 9) == 0
+    fake = 1 << 40                      # never dereferenced: every call below fails validation
+    assert L.gale_moe_decode_stack(4096, 2048, 256, 6, 0, fake, fake, ws_bytes, 0, None) == -2      # no layers
+    assert L.gale_moe_decode_stack(4096, 2048, 256, 6, 2, None, fake, ws_bytes, 0, None) == -1      # NULL table
+    assert L.gale_moe_decode_stack(4096, 2048, 256, 6, 2, fake, fake, ws_bytes - 1, 0, None) == -5  # workspace
+    assert L.gale_moe_decode_stack(4096, 2048, 256, 6, 2, fake, fake + 8, ws_bytes, 0, None) == -4  # alignment
+    assert L.gale_moe_decode_stack(8192, 2048, 256, 6, 2, fake, fake, 1 << 30, 0, None) == -6       # shape
+    assert L.gale_moe_decode_stack(4096, 2048, 256, 9, 2, fake, fake, 1 << 30, 0, None) == -2      # top_k
+    assert L.gale_sync_init(None, None) == -1
+    assert L.gale_sync_init(fake + 8, None) == -4
