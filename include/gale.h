@@ -336,6 +336,22 @@ int gale_moe_decode_stack(int32_t hidden, int32_t inter, int32_t n_experts, int3
                           const gale_layer_io* layers_dev, void* ws, size_t ws_bytes, uint32_t flags,
                           hipStream_t stream);
 
+/* For callers that cannot allocate -- code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc: gale_moe_decode_stack with its workspace in a device array
+ * of GALE_STATIC_SCRATCH_BYTES that the library holds for each GPU it runs on, from its first
+ * call on that GPU until the process ends.  The call allocates nothing and frees nothing.
+ * Every call zeroes the array's synchronisation words before its kernel (a fill kernel on
+ * `stream`), so each call starts clean and a wait that gave up in an earlier call does not
+ * carry over (nor can it be queried: use gale_moe_decode_stack with gale_sync_status for
+ * that).  Calls on one GPU share its array: calls that overlap in time on one GPU (two streams,
+ * two threads) race and must not be made.  The arguments are those of gale_moe_decode_stack;
+ * a shape whose workspace (gale_decode_stack_workspace_bytes) exceeds
+ * GALE_STATIC_SCRATCH_BYTES returns GALE_ERR_WORKSPACE before anything is enqueued. */
+#define GALE_STATIC_SCRATCH_BYTES (GALE_SYNC_BYTES + 65536)
+int gale_moe_decode_stack_static(int32_t hidden, int32_t inter, int32_t n_experts, int32_t top_k,
+                                 int32_t n_layers, const gale_layer_io* layers_dev, uint32_t flags,
+                                 hipStream_t stream);
+
 /* Zero the synchronisation words at the start of ws (GALE_SYNC_BYTES; a kernel on `stream`,
  * so it can be captured in a graph).  Needed once before the first one-launch decode call on
  * a workspace, and again after gale_sync_status() reported GALE_ERR_SYNC. */

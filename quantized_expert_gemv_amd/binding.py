@@ -28,6 +28,7 @@ GALE_GROUPED_GEMM = 0x80
 GALE_DECODE_STAGED = 0x1000
 GALE_SYNC_NO_WAIT = 0x10000
 GALE_SYNC_BYTES = 4608
+GALE_STATIC_SCRATCH_BYTES = GALE_SYNC_BYTES + 65536
 GALE_ERR_SYNC = -9
 STATUS = {0: "GALE_OK", -1: "GALE_ERR_NULL", -2: "GALE_ERR_SHAPE", -3: "GALE_ERR_DTYPE", -4: "GALE_ERR_ALIGN",
           -5: "GALE_ERR_WORKSPACE", -6: "GALE_ERR_UNSUPPORTED", -7: "GALE_ERR_FORMAT", -8: "GALE_ERR_HIP",
@@ -119,6 +120,7 @@ _SIGS = {
     "gale_route_topk": (_I32, [_P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
     "gale_decode_stack_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
     "gale_moe_decode_stack": (_I32, [_I32, _I32, _I32, _I32, _I32, _P, _P, _SZ, _U32, _P]),
+    "gale_moe_decode_stack_static": (_I32, [_I32, _I32, _I32, _I32, _I32, _P, _U32, _P]),
     "gale_sync_init": (_I32, [_P, _P]),
     "gale_sync_status": (_I32, [_P, ctypes.POINTER(ctypes.c_uint64)]),
 }

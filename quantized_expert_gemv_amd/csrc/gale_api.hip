@@ -743,3 +743,31 @@ extern "C" int gale_sync_status(const void* ws, uint64_t* words_host) {
       return GALE_ERR_SYNC;
   }
 }
+
+extern "C" int gale_moe_decode_stack_static(int32_t hidden, int32_t inter, int32_t n_experts, int32_t top_k,
+                                            int32_t n_layers, const gale_layer_io* layers_dev, uint32_t flags,
+                                            hipStream_t stream) {
+  const char* fn = "gale_moe_decode_stack_static";
+  int st = decode_stack_check(fn, hidden, inter, n_experts, top_k, n_layers, layers_dev);
+  if (st) return st;
+  const size_t need = gale_decode_stack_workspace_bytes(hidden, inter, top_k);
+  if (need > (size_t)GALE_STATIC_SCRATCH_BYTES) {
+    set_error("%s: hidden=%d inter=%d top_k=%d needs %zu workspace bytes, above the static array's %d", fn, hidden,
+              inter, top_k, need, GALE_STATIC_SCRATCH_BYTES);
+    return GALE_ERR_WORKSPACE;
+  }
+  void* ws = nullptr;
+  st = hip_status(fn, static_scratch(&ws));
+  if (st) return st;
+  uint8_t* base = reinterpret_cast<uint8_t*>(ws);
+  // every call starts from zeroed synchronisation words (the array keeps the last call's)
+  st = hip_status(fn, launch_sync_init(base, stream));
+  if (st) return st;
+  float* h = reinterpret_cast<float*>(base + align256(kDecodeSyncBytes));
+  gale_layer_io none;
+  memset(&none, 0, sizeof(none));
+  const int forced = (int)((flags >> GALE_TILES_SHIFT) & 0xF);
+  return hip_status(fn, launch_decode_stack(none, layers_dev, n_layers, n_experts, top_k, hidden, inter, h,
+                                            reinterpret_cast<uint64_t*>(base), forced, decode_wait_ticks(flags),
+                                            stream));
+}

@@ -825,3 +825,31 @@ int sync_words_state(const uint64_t words[3]) {
 }
 
 }  // namespace gale
+
+#include <mutex>
+
+namespace gale {
+
+// The workspace of gale_moe_decode_stack_static: one per GPU, in the library's code object,
+// held until the process ends.  Host code never uses this name as an address: it is a
+// host-side stand-in, and the device address comes from hipGetSymbolAddress (per device).
+static __device__ __align__(256) unsigned char scratch[GALE_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+hipError_t static_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  static std::once_flag once[kMaxDevices];
+  static void* ptr[kMaxDevices];
+  static hipError_t status[kMaxDevices];
+  // once per device, with that device current (it is: hipGetDevice above)
+  std::call_once(once[dev], [dev] { status[dev] = hipGetSymbolAddress(&ptr[dev], HIP_SYMBOL(scratch)); });
+  if (status[dev] != hipSuccess) return status[dev];
+  *out = ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace gale

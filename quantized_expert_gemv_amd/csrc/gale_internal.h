@@ -199,6 +199,8 @@ hipError_t launch_decode_stack(const gale_layer_io& io0, const gale_layer_io* la
 hipError_t launch_sync_init(void* sync, hipStream_t s);
 // 0: valid and no error; 1: the words were never zeroed; 2: a barrier wait gave up
 int sync_words_state(const uint64_t words[3]);
+// device address of this GPU's GALE_STATIC_SCRATCH_BYTES array (looked up once per device)
+hipError_t static_scratch(void** out);
 
 void set_error(const char* fmt, ...);
 
