@@ -261,8 +261,8 @@ size_t gale_moe_workspace_bytes(int32_t n_tok, int32_t n_experts, int32_t top_k,
  *           with one token the whole layer is a single persistent launch (the
  *           DeepSeek-V4-Pro GALE page's batch-1 notes put the floor in launches), the
  *           layer of gale_moe_decode_stack: every workgroup routes the token itself,
- *           runs its gate/up units, and after a grid barrier owns 16 rows of y for all
- *           top_k experts.  This needs the workspace's synchronisation words (its first
+ *           runs its gate/up units, and then owns 16 rows of y for all top_k experts,
+ *           waiting only for the rotated 1024-blocks of h it reads.  This needs the workspace's synchronisation words (its first
  *           GALE_SYNC_BYTES bytes) zero-filled once before the first such call
  *           (gale_sync_init, or any zero fill) and calls sharing a workspace must not
  *           overlap in time (true of every workspace).  When the words are not valid
@@ -312,9 +312,10 @@ int gale_moe_layer_fwd_routed(int32_t hidden, int32_t inter, const gale_expert* 
 /* ---- one token through a stack of layers in one launch -------------------------- */
 
 /* Bytes at the start of a one-launch decode workspace that hold its synchronisation words. */
-#define GALE_SYNC_BYTES 4608
+#define GALE_SYNC_BYTES 40960
 
-/* Workspace bytes for gale_moe_decode_stack (the synchronisation words, then fp32 h). */
+/* Workspace bytes for gale_moe_decode_stack (the synchronisation words, then fp32 h and the
+ * rotated h's activation records). */
 size_t gale_decode_stack_workspace_bytes(int32_t hidden, int32_t inter, int32_t top_k);
 
 /* One decode token through n_layers routed-expert layers, in one persistent launch
@@ -347,7 +348,7 @@ int gale_moe_decode_stack(int32_t hidden, int32_t inter, int32_t n_experts, int3
  * two threads) race and must not be made.  The arguments are those of gale_moe_decode_stack;
  * a shape whose workspace (gale_decode_stack_workspace_bytes) exceeds
  * GALE_STATIC_SCRATCH_BYTES returns GALE_ERR_WORKSPACE before anything is enqueued. */
-#define GALE_STATIC_SCRATCH_BYTES (GALE_SYNC_BYTES + 65536)
+#define GALE_STATIC_SCRATCH_BYTES (GALE_SYNC_BYTES + 196608)
 int gale_moe_decode_stack_static(int32_t hidden, int32_t inter, int32_t n_experts, int32_t top_k,
                                  int32_t n_layers, const gale_layer_io* layers_dev, uint32_t flags,
                                  hipStream_t stream);

@@ -27,8 +27,8 @@ GALE_GROUPED_ITEMS = 0x40
 GALE_GROUPED_GEMM = 0x80
 GALE_DECODE_STAGED = 0x1000
 GALE_SYNC_NO_WAIT = 0x10000
-GALE_SYNC_BYTES = 4608
-GALE_STATIC_SCRATCH_BYTES = GALE_SYNC_BYTES + 65536
+GALE_SYNC_BYTES = 40960
+GALE_STATIC_SCRATCH_BYTES = GALE_SYNC_BYTES + 196608
 GALE_ERR_SYNC = -9
 STATUS = {0: "GALE_OK", -1: "GALE_ERR_NULL", -2: "GALE_ERR_SHAPE", -3: "GALE_ERR_DTYPE", -4: "GALE_ERR_ALIGN",
           -5: "GALE_ERR_WORKSPACE", -6: "GALE_ERR_UNSUPPORTED", -7: "GALE_ERR_FORMAT", -8: "GALE_ERR_HIP",

@@ -569,7 +569,7 @@ static int moe_layer(const char* fn, int32_t hidden, int32_t inter, const gale_e
     io.topk_idx = topk_idx;
     io.topk_w = topk_w;
     const int forced = (int)((flags >> GALE_TILES_SHIFT) & 0xF);
-    return hip_status(fn, launch_decode_stack(io, nullptr, 1, n_experts, top_k, hidden, inter, h,
+    return hip_status(fn, launch_decode_stack(io, nullptr, 1, n_experts, top_k, hidden, inter, h, ra_h,
                                               reinterpret_cast<uint64_t*>(base + W.sync), forced,
                                               decode_wait_ticks(flags), stream));
   }
@@ -674,7 +674,8 @@ extern "C" int gale_route_topk(const float* logits, int32_t n_tok, int32_t n_exp
 // ============================================================================
 extern "C" size_t gale_decode_stack_workspace_bytes(int32_t hidden, int32_t inter, int32_t top_k) {
   if (hidden < 1024 || inter < 1024 || top_k < 1 || top_k > GALE_MAX_TOPK) return 0;
-  return align256(kDecodeSyncBytes) + align256(decode_stack_h_bytes(inter, top_k));
+  return align256(kDecodeSyncBytes) + align256(decode_stack_h_bytes(inter, top_k)) +
+         align256(decode_stack_rec_bytes(inter, top_k));
 }
 
 // Host validation shared by the two stack entry points (ws == NULL is checked by the caller).
@@ -710,10 +711,11 @@ extern "C" int gale_moe_decode_stack(int32_t hidden, int32_t inter, int32_t n_ex
   if (ws_bytes < need) { set_error("%s: workspace %zu < %zu bytes", fn, ws_bytes, need); return GALE_ERR_WORKSPACE; }
   uint8_t* base = reinterpret_cast<uint8_t*>(ws);
   float* h = reinterpret_cast<float*>(base + align256(kDecodeSyncBytes));
+  uint8_t* rec = base + align256(kDecodeSyncBytes) + align256(decode_stack_h_bytes(inter, top_k));
   gale_layer_io none;
   memset(&none, 0, sizeof(none));
   const int forced = (int)((flags >> GALE_TILES_SHIFT) & 0xF);
-  return hip_status(fn, launch_decode_stack(none, layers_dev, n_layers, n_experts, top_k, hidden, inter, h,
+  return hip_status(fn, launch_decode_stack(none, layers_dev, n_layers, n_experts, top_k, hidden, inter, h, rec,
                                             reinterpret_cast<uint64_t*>(base), forced, decode_wait_ticks(flags),
                                             stream));
 }
@@ -764,10 +766,11 @@ extern "C" int gale_moe_decode_stack_static(int32_t hidden, int32_t inter, int32
   st = hip_status(fn, launch_sync_init(base, stream));
   if (st) return st;
   float* h = reinterpret_cast<float*>(base + align256(kDecodeSyncBytes));
+  uint8_t* rec = base + align256(kDecodeSyncBytes) + align256(decode_stack_h_bytes(inter, top_k));
   gale_layer_io none;
   memset(&none, 0, sizeof(none));
   const int forced = (int)((flags >> GALE_TILES_SHIFT) & 0xF);
-  return hip_status(fn, launch_decode_stack(none, layers_dev, n_layers, n_experts, top_k, hidden, inter, h,
+  return hip_status(fn, launch_decode_stack(none, layers_dev, n_layers, n_experts, top_k, hidden, inter, h, rec,
                                             reinterpret_cast<uint64_t*>(base), forced, decode_wait_ticks(flags),
                                             stream));
 }

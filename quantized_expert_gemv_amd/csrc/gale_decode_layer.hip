@@ -7,8 +7,8 @@
 // three GALE matrices, and the weighted combine -- for one layer, or for a stack of
 // layers run strictly one after another.  The DeepSeek-V4-Pro GALE page (its
 // "Measured" notes on batch-1 decode) puts the batch-1 floor in kernel launches and
-// per-expert unpacks, not in data movement; here each layer is two phases of one
-// persistent launch, and a stack of layers is one launch.
+// per-expert unpacks, not in data movement; here a layer is one persistent launch with
+// no grid barrier inside, and a stack of layers is one launch.
 //
 // Plan.  The grid is one workgroup per CU, all resident together.  Per layer:
 //   R  every workgroup routes the token itself (one wavefront; the same answer
@@ -17,11 +17,15 @@
 //      selected expert (split-K over the 1024-column chunks, one wavefront each),
 //      writing h = silu(w1 x~) * (w3 x~); meanwhile the weights of its down tile are
 //      already on their way (issued right behind the gate/up loads);
-//   -- grid barrier: every h row is stored --
+//   H  hand-off: each (pair, 1024-block) of h is 64 row tiles.  A workgroup adds the
+//      tiles it stored to the block's counter; the one whose addition completes the
+//      block rotates it (FWHT-1024 and the fp8 split) once for the whole grid into a
+//      shared activation record and raises the block's flag.  The rotation is
+//      blockwise, so no block waits for any other;
 //   D  down: the workgroup owns one row tile (16 rows of y) for ALL k pairs, so the
-//      combine needs no other workgroup: it rotates every pair's h into LDS records
-//      (each 1024-block is independent), runs the k x C_I sign tasks and the k
-//      outlier rows, and wavefront 0 sums the k outputs in slot order into y;
+//      combine needs no other workgroup: each wavefront waits for the flags of its
+//      blocks and copies their records into LDS, then the k x C_I sign tasks and the
+//      k outlier rows run, and wavefront 0 sums the k outputs in slot order into y;
 //   -- grid barrier (between layers only): y is stored; the next layer may read it --
 //
 // A stack of layers is one token through the layers in order: layer l reads its
@@ -43,15 +47,19 @@
 //   [0] G  the generation of the last call that ran on these words
 //   [1] C  check word, sync_check(G); sync_check(0) = 0, so all-zero words are a
 //          valid start (generation 1 comes next)
-//   [2] E  error bits, sticky: bit 0 = a barrier wait gave up (its time budget ran
-//          out: workgroups that were not all resident, or a forced zero budget)
-//   two sets of kSubs counters: call g counts on set g % 2 and zeroes set (g+1) % 2
-//   (last used by call g-1, which has completed) for call g+1.
+//   [2] E  error bits, sticky: bit 0 = a wait gave up (its time budget ran out:
+//          workgroups that were not all resident, or a forced zero budget)
+//   two sets of {kSubs barrier counters, kMaxBlocks block counters, kMaxBlocks block
+//   flags}: call g counts on set g % 2 and workgroup 0 zeroes set (g+1) % 2 (last used
+//   by call g-1, which has completed) for call g+1.  Within a call every count only
+//   grows: barrier p waits for p arrivals per workgroup (barrier 1 = every workgroup
+//   has read the header), a block's counter reaches 64 (l + 1) in layer l, and its
+//   flag is set to l + 1 once layer l's record of the block is stored.
 // Every workgroup reads G, C, E at its start; when C != sync_check(G) (the words were
 // never zeroed) or E != 0 (an earlier wait gave up), the call does nothing at all:
 // y is not written and the host query reports the state.  Workgroup 0 writes the new
-// G and C at its end; it has then passed the first barrier, so every workgroup has
-// read the old values.  A wait that gives up sets E and the kernel carries on (it
+// G and C at its end, after barrier 1, so every workgroup has read the old values
+// before they change.  A wait that gives up sets E and the kernel carries on (it
 // always ends); the generation moves on, so nothing of a failed call satisfies a
 // later call's waits, and the sticky E makes later calls refuse until the words are
 // zeroed again.
@@ -68,10 +76,22 @@ namespace gale {
 
 // ---- synchronisation words --------------------------------------------------------
 constexpr int kSubs = 16;          // arrival sub-counters per set
-constexpr int kSubStride = 16;     // uint64 words between sub-counters (128 bytes)
+constexpr int kSubStride = 16;     // uint64 words between counters (128 bytes)
 constexpr int kSetBase = 16;       // word of set 0, counter 0
-__host__ __device__ constexpr int sub_word(int set, int i) { return kSetBase + (set * kSubs + i) * kSubStride; }
-constexpr int kSyncWordCount = kSetBase + 2 * kSubs * kSubStride;
+constexpr int kMaxBlocks = 64;     // (pair, 1024-block) pieces of h per layer
+constexpr int kMaxChunksH = 4;     // 1024-chunks of the hidden size (hidden <= 4096)
+constexpr int kMaxChunksI = 4;     // 1024-chunks of the intermediate size (inter <= 4096)
+// A set: kSubs barrier sub-counters, kMaxBlocks block counters and kMaxBlocks block flags,
+// one 128-byte line each (polled lines are spread over the memory channels).
+constexpr int kSetWords = (kSubs + 2 * kMaxBlocks) * kSubStride;
+__host__ __device__ constexpr int sub_word(int set, int i) { return kSetBase + set * kSetWords + i * kSubStride; }
+__host__ __device__ constexpr int cnt_word(int set, int b) {
+  return kSetBase + set * kSetWords + (kSubs + b) * kSubStride;
+}
+__host__ __device__ constexpr int flag_word(int set, int b) {
+  return kSetBase + set * kSetWords + (kSubs + kMaxBlocks + b) * kSubStride;
+}
+constexpr int kSyncWordCount = kSetBase + 2 * kSetWords;
 static_assert((size_t)8 * kSyncWordCount <= kDecodeSyncBytes, "sync region");
 constexpr uint64_t kErrWaitGaveUp = 1;
 
@@ -100,6 +120,11 @@ __device__ __forceinline__ uint64_t cld_u64(const void* p) {
   return __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<void*>(p)), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
 }
+// Cache-policy bits of a device-scope access (sc1) for the global-to-LDS loads and buffer
+// stores, and the last word of a raw buffer resource (32-bit data format).
+constexpr int kDeviceScope = 16;
+constexpr int kBufferWord3 = 0x00020000;
+typedef __attribute__((address_space(1))) const unsigned char g_cu8;
 
 // Wait until this wavefront's stores (and loads) have completed, with no compiler
 // reordering of memory accesses across the wait.
@@ -117,6 +142,7 @@ struct StackParams {
   int down_tiles;                  // 16-row tiles of y per layer
   int kp;                          // pairs whose h records fit in LDS at once
   float* h;                        // fp32 [k][I]
+  uint8_t* rec;                    // [k] activation records of the rotated h (ra_bytes(I) each)
   uint64_t* sync;                  // kDecodeSyncBytes of synchronisation words
   int64_t wait_ticks;              // give-up time of a barrier wait (100 MHz ticks)
 };
@@ -147,23 +173,62 @@ __device__ __forceinline__ void arrive(const StackParams& P, int set, int lane) 
 
 // Wavefront 0 waits until every workgroup has arrived at barrier `phase` (1, 2, ...)
 // of set `set`, or the time budget runs out (then E records it and the wait ends).
+// Polls keep four loads in flight, issued a short sleep apart (kPollSleep x 64 clocks), so
+// that a change is seen sooner after it lands than with one load at a time.
+constexpr int kPollSleep = 3;
+__device__ __forceinline__ void gave_up(const StackParams& P, int lane) {
+  if (lane == 0) (void)__hip_atomic_fetch_or(P.sync + 2, kErrWaitGaveUp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Poll the lane's word w until ok(value) holds (a wavefront-uniform test) or the time budget
+// runs out (then E records it).  Four loads stay in flight; every exit leaves the loop
+// directly, so each test waits only for its own load.
+template <typename Ok>
+__device__ __forceinline__ void poll_until(const StackParams& P, const uint64_t* w, Ok ok, int lane) {
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  uint64_t v0 = sync_load(w);
+  __builtin_amdgcn_s_sleep(kPollSleep);
+  uint64_t v1 = sync_load(w);
+  __builtin_amdgcn_s_sleep(kPollSleep);
+  uint64_t v2 = sync_load(w);
+  __builtin_amdgcn_s_sleep(kPollSleep);
+  uint64_t v3 = sync_load(w);
+  __builtin_amdgcn_s_sleep(kPollSleep);
+  for (;;) {
+    if (ok(v0)) goto done;
+    v0 = sync_load(w);
+    __builtin_amdgcn_s_sleep(kPollSleep);
+    if (ok(v1)) goto done;
+    v1 = sync_load(w);
+    __builtin_amdgcn_s_sleep(kPollSleep);
+    if (ok(v2)) goto done;
+    v2 = sync_load(w);
+    __builtin_amdgcn_s_sleep(kPollSleep);
+    if (ok(v3)) goto done;
+    v3 = sync_load(w);
+    __builtin_amdgcn_s_sleep(kPollSleep);
+    if ((int64_t)(__builtin_amdgcn_s_memrealtime() - t0) >= P.wait_ticks) {
+      gave_up(P, lane);
+      goto done;
+    }
+  }
+done:
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 __device__ __forceinline__ void wait_barrier(const StackParams& P, int set, int phase, int lane) {
   const int nb = (int)gridDim.x;
   const bool watch = lane < kSubs && lane < nb;
   const uint64_t target = watch ? (uint64_t)phase * (uint64_t)((nb - lane + kSubs - 1) / kSubs) : 0;
   const uint64_t* w = P.sync + sub_word(set, watch ? lane : 0);
-  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-  for (;;) {
-    const bool ok = !watch || sync_load(w) >= target;
-    if (__all(ok)) break;
-    if ((int64_t)(__builtin_amdgcn_s_memrealtime() - t0) >= P.wait_ticks) {
-      if (lane == 0)
-        (void)__hip_atomic_fetch_or(P.sync + 2, kErrWaitGaveUp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      break;
-    }
-    __builtin_amdgcn_s_sleep(1);
-  }
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  poll_until(P, w, [&](uint64_t v) { return __all(!watch || v >= target) != 0; }, lane);
+}
+
+// The wavefront waits until block flag `b` of set `set` reaches `target`, or the time
+// budget runs out (then E records it and the wait ends).
+__device__ __forceinline__ void wait_flag(const StackParams& P, int set, int b, uint64_t target, int lane) {
+  // one address for the whole wavefront: one request per poll
+  poll_until(P, P.sync + flag_word(set, b), [&](uint64_t v) { return __all(v >= target) != 0; }, lane);
 }
 
 // ---- activation records -------------------------------------------------------------
@@ -191,10 +256,60 @@ __device__ __forceinline__ void load_h_block(const float* hv, int c, int lane, f
     f[2 * j + 1] = __uint_as_float((uint32_t)(q >> 32));
   }
 }
-__device__ __forceinline__ void rotate_h_block(const float f[16], int K, int c, uint8_t* rec, int lane) {
-  PrepLane o;
-  prep_lane(f, lane, true, o);
-  store_record_chunk(o, GALE_F32, rec, K, c, lane);
+
+// The same record chunk as store_record_chunk makes for fp32 input, written with
+// device-scope stores into a record in global memory (read by workgroups on other XCDs).
+// Neighbouring lanes (2m, 2m + 1) swap halves so that every store is 16 bytes (x~) or 4
+// bytes (terms) per lane, with device-scope (sc1) buffer stores:
+//   x~, registers 2j, 2j+1 (elements 128 j + 2 l, + 1), for j = 0, 2, 4, 6: the even lane
+//       stores its own pair and its partner's for j (elements 128 j + 4 m .. + 3), the odd
+//       lane its partner's pair and its own for j + 1 (elements 128 (j + 1) + 4 m .. + 3);
+//   terms, word q of term t (low half: granule 2q, high half: granule 2q + 1): the even
+//       lane stores both lanes' low halves (uint16 128 q + 2 m, + 1), the odd lane both
+//       high halves (uint16 128 q + 64 + 2 m, + 1).
+__device__ __forceinline__ void store_record_chunk_dev(const PrepLane& o, uint8_t* rec, int K, int c, int lane) {
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(rec, 0, (int)ra_bytes(K), kBufferWord3);
+  const bool odd = (lane & 1) != 0;
+  const int m = lane >> 1;
+#pragma unroll
+  for (int j = 0; j < 8; j += 2) {
+    const float p0 = lane_xor<1>(o.x[2 * j]), p1 = lane_xor<1>(o.x[2 * j + 1]);
+    const float p2 = lane_xor<1>(o.x[2 * j + 2]), p3 = lane_xor<1>(o.x[2 * j + 3]);
+    const u32x4 v = odd ? u32x4{__float_as_uint(p2), __float_as_uint(p3), __float_as_uint(o.x[2 * j + 2]),
+                                __float_as_uint(o.x[2 * j + 3])}
+                        : u32x4{__float_as_uint(o.x[2 * j]), __float_as_uint(o.x[2 * j + 1]), __float_as_uint(p0),
+                                __float_as_uint(p1)};
+    const int elem = 128 * (odd ? j + 1 : j) + 4 * m;
+    __builtin_amdgcn_raw_buffer_store_b128(v, rs, c * 4096 + 4 * elem, 0, kDeviceScope);
+  }
+  const int toff = (int)ra_terms_off(K) + c * 4096;
+#pragma unroll
+  for (int t = 0; t < kTerms; ++t)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t w = o.t[t][q], pw = lane_xor_u32<1>(w);
+      const uint32_t v = odd ? ((pw >> 16) | (w & 0xFFFF0000u)) : ((w & 0xFFFFu) | (pw << 16));
+      __builtin_amdgcn_raw_buffer_store_b32(v, rs, toff + t * 1024 + 4 * (64 * q + (odd ? 32 : 0) + m), 0, kDeviceScope);
+    }
+  if (lane == 0) cst_u32(rec + ra_p_off(K) + 4 * (size_t)c, (uint32_t)o.p);
+}
+
+// Chunk c of a record in global memory (written by another workgroup) into the same
+// place of a record in LDS: x~ and the four terms by device-scope global-to-LDS loads,
+// the exponent through a register.  The caller waits for the loads (vmcnt) before use.
+__device__ __forceinline__ void stage_record_chunk(const uint8_t* grec, lds_u8* lrec, int K, int c, int lane) {
+  const char* gx = reinterpret_cast<const char*>(grec) + (size_t)c * 4096 + 16 * lane;
+  const char* gt = reinterpret_cast<const char*>(grec) + ra_terms_off(K) + (size_t)c * 4096 + 16 * lane;
+  lds_u8* lx = lrec + (size_t)c * 4096;
+  lds_u8* lt = lrec + ra_terms_off(K) + (size_t)c * 4096;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    __builtin_amdgcn_global_load_lds((g_cu8*)(gx + 1024 * i), lx + 1024 * i, 16, 0, kDeviceScope);
+    __builtin_amdgcn_global_load_lds((g_cu8*)(gt + 1024 * i), lt + 1024 * i, 16, 0, kDeviceScope);
+  }
+  const uint32_t pw = __hip_atomic_load(reinterpret_cast<uint32_t*>(const_cast<uint8_t*>(grec + ra_p_off(K))) + c,
+                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (lane == 0) reinterpret_cast<__attribute__((address_space(3))) uint32_t*>(lrec + ra_p_off(K))[c] = pw;
 }
 
 // A operands and exponent of chunk c from an activation record in LDS.
@@ -382,8 +497,6 @@ __device__ __forceinline__ void gu_issue_weights(const gale_matrix* table, const
 // round robin from the last wavefront down, slot j / Wd.  Wavefront 0 combines.
 template <int NT, int NO>
 struct DownBuf {
-  uint32_t sw[NT][8];
-  uint32_t sc[NT][4];
   OutBuf o[NO];
 };
 
@@ -400,25 +513,27 @@ __device__ __forceinline__ void down_issue_rp(const gale_matrix* table, const in
   }
 }
 
-template <int NT, int NO>
-__device__ __forceinline__ void down_issue_weights(const gale_matrix* table, const int32_t* s_exp, int k, int C,
-                                                   int Wd, int wd, int tile, int lane, DownBuf<NT, NO>& b) {
-  const uint32_t sw_lane = 16u * (uint32_t)lane, sc_lane = 16u * (uint32_t)(lane & 15);
+// The sign words and block scales of this wavefront's first NT sign tasks of one tile,
+// straight from memory into its LDS slots (no registers): slot i holds the tile chunk's
+// 2 KB of sign words in the wave's load order (lane l's 16 bytes at 16 l and 1024 + 16 l)
+// and the 16 rows' scales at 2048 + 16 r.
+constexpr int kDownSlotBytes = 2048 + 256;
+
+template <int NT>
+__device__ __forceinline__ void down_prefetch_lds(const gale_matrix* table, const int32_t* s_exp, int k, int C,
+                                                  int Wd, int wd, int tile, int lane, lds_u8* slots) {
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
     const int s = sign_task(wd, i, Wd);
     if (s < k * C) {
       const int j = uni(s / C), c = uni(s - j * C);
       const auto* m = as_const(table) + uni(s_exp[j]) * 3 + 2;
-      const char* sg = reinterpret_cast<const char*>(m->signs);
-      const char* scl = reinterpret_cast<const char*>(m->block_scales);
-      const uint32_t o = ((uint32_t)tile * C + c) * 2048u + sw_lane;
-      const uint4 lo = ld16_stream(sg, o);
-      const uint4 hi = ld16_stream(sg, o + 1024u);
-      b.sw[i][0] = lo.x; b.sw[i][1] = lo.y; b.sw[i][2] = lo.z; b.sw[i][3] = lo.w;
-      b.sw[i][4] = hi.x; b.sw[i][5] = hi.y; b.sw[i][6] = hi.z; b.sw[i][7] = hi.w;
-      const uint4 sc = ld16_stream(scl, ((uint32_t)tile * C + c) * 256u + sc_lane);
-      b.sc[i][0] = sc.x; b.sc[i][1] = sc.y; b.sc[i][2] = sc.z; b.sc[i][3] = sc.w;
+      const char* sg = reinterpret_cast<const char*>(m->signs) + ((size_t)tile * C + c) * 2048;
+      const char* scl = reinterpret_cast<const char*>(m->block_scales) + ((size_t)tile * C + c) * 256;
+      lds_u8* dst = slots + i * kDownSlotBytes;
+      __builtin_amdgcn_global_load_lds((g_cu8*)(sg + 16 * lane), dst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((g_cu8*)(sg + 1024 + 16 * lane), dst + 1024, 16, 0, 0);
+      if (lane < 16) __builtin_amdgcn_global_load_lds((g_cu8*)(scl + 16 * lane), dst + 2048, 16, 0, 0);
     }
   }
 }
@@ -433,22 +548,80 @@ __device__ __forceinline__ void down_issue_chunks(const gale_matrix* table, cons
   }
 }
 
+// h of row rr of a gate/up unit from the split-K partials of its CH chunks (w1 then w3) and
+// the outlier sums: every partial is read before the first sum, at offsets fixed at compile
+// time (no registers of the scalar unit for them).
+template <int CH, int RR>
+__device__ __forceinline__ float combine_h(const lds_f32* red, const lds_f32* ored, int rr) {
+  float pa[CH], pg[CH];
+#pragma unroll
+  for (int q = 0; q < CH; ++q) {
+    pa[q] = red[q * RR + rr];
+    pg[q] = red[(CH + q) * RR + rr];
+  }
+  const float oa = ored[rr], og = ored[RR + rr];
+  float a = 0.f, g = 0.f;
+#pragma unroll
+  for (int q = 0; q < CH; ++q) a += pa[q];
+#pragma unroll
+  for (int q = 0; q < CH; ++q) g += pg[q];
+  a = a + oa;
+  g = g + og;
+  return silu_f(a) * g;
+}
+
+// y of the lane's row of a down tile: the sum over slots in order of w_j (the CI chunk
+// partials in order, plus the outlier sum).  Every partial is read before the first sum,
+// at offsets fixed at compile time; the reads for slots j >= k stay inside the LDS and are
+// not used.
+template <int CI>
+__device__ __forceinline__ float combine_y(const lds_f32* dpart, const lds_f32* dout, const float* s_w, int k,
+                                           int lane) {
+  float pv[GALE_MAX_TOPK][CI], po[GALE_MAX_TOPK], pw[GALE_MAX_TOPK];
+#pragma unroll
+  for (int j = 0; j < GALE_MAX_TOPK; ++j) {
+#pragma unroll
+    for (int c = 0; c < CI; ++c) pv[j][c] = dpart[(j * CI + c) * 16 + lane];
+    po[j] = dout[j * 16 + lane];
+    pw[j] = s_w[j];
+  }
+  float acc = 0.f;
+#pragma unroll
+  for (int j = 0; j < GALE_MAX_TOPK; ++j) {
+    if (j < k) {
+      float a = 0.f;
+#pragma unroll
+      for (int c = 0; c < CI; ++c) a += pv[j][c];
+      a = a + po[j];
+      acc = fmaf(pw[j], a, acc);
+    }
+  }
+  return acc;
+}
+
+// misc: selected experts (8 int32), their weights (8 fp32), header words (16 uint32), the
+// blocks this workgroup completed (kMaxBlocks int32) and their count
+constexpr int kMiscBytes = 128 + 4 * kMaxBlocks + 16;
+
 // LDS of the kernel.  The record region holds x's activation record during phases R and
 // G, then the h records of up to kp pairs during phase D.
 struct StackLds {
-  size_t rec, red, ored, dpart, dout, wout, misc, total;
+  uint32_t rec, red, ored, dpart, dout, wout, misc, dpre, total;
 };
-__host__ __device__ inline StackLds stack_lds(int H, int I, int k, int kp, int W, int R) {
+// nt_pre: sign-task slots per wavefront prefetched into LDS (0 when the tasks load as they run)
+__host__ __device__ inline StackLds stack_lds(int H, int I, int k, int kp, int W, int R, int nt_pre) {
   StackLds s;
-  const size_t rb = ra_bytes(H), rh = (size_t)kp * ra_bytes(I);
+  // (sizes of shapes far beyond the LDS are not meant: the caller checks total against it)
+  const uint32_t rb = (uint32_t)ra_bytes(H), rh = (uint32_t)(kp * ra_bytes(I));
   s.rec = 0;
   s.red = (rb > rh ? rb : rh);
-  s.ored = s.red + (size_t)2 * W * 16 * R * 4;          // two alternating sets
-  s.dpart = s.ored + (size_t)2 * 2 * 16 * R * 4;
-  s.dout = s.dpart + (size_t)2 * k * (I >> 10) * 16 * 4;
-  s.wout = s.dout + (size_t)2 * k * 16 * 4;
-  s.misc = s.wout + (size_t)W * kWaveOutBytes;
-  s.total = s.misc + 128;
+  s.ored = s.red + 2u * W * 16 * R * 4;          // two alternating sets
+  s.dpart = s.ored + 2u * 2 * 16 * R * 4;
+  s.dout = s.dpart + 2u * k * (I >> 10) * 16 * 4;
+  s.wout = s.dout + 2u * k * 16 * 4;
+  s.misc = s.wout + (uint32_t)W * kWaveOutBytes;
+  s.dpre = s.misc + kMiscBytes;
+  s.total = s.dpre + (uint32_t)(W - 1) * nt_pre * kDownSlotBytes;
   return s;
 }
 
@@ -470,10 +643,13 @@ __global__ void __launch_bounds__(512) decode_stack_kernel(const StackParams P) 
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
   const int W = (int)(blockDim.x >> 6), Wd = W - 1, wd = wave - 1;
-  const int C_H = P.H >> 10, C_I = P.I >> 10;
-  const int TI = P.I >> 4, T = P.k * TI;
+  const int C_H0 = P.H >> 10, C_I0 = P.I >> 10;
+  const int TI0 = P.I >> 4, T0 = P.k * TI0;
+  const int C_H = C_H0, C_I = C_I0;
   constexpr int RR = 16 * R;
-  const StackLds LL = stack_lds(P.H, P.I, P.k, P.kp, W, R);
+  constexpr bool kPrefetch = NT <= 2 && NO <= 1;   // the larger task sets load each task when it runs
+  const StackLds LL = stack_lds(P.H, P.I, P.k, P.kp, W, R, kPrefetch ? NT : 0);
+  lds_u8* dslots = (lds_u8*)(smem + LL.dpre) + (wave >= 1 ? wave - 1 : 0) * NT * kDownSlotBytes;
   uint8_t* rec = smem + LL.rec;
   lds_f32* red0 = (lds_f32*)(smem + LL.red);
   lds_f32* ored0 = (lds_f32*)(smem + LL.ored);
@@ -483,6 +659,8 @@ __global__ void __launch_bounds__(512) decode_stack_kernel(const StackParams P) 
   int32_t* s_exp = reinterpret_cast<int32_t*>(smem + LL.misc);
   float* s_w = reinterpret_cast<float*>(s_exp + 8);
   uint32_t* s_hdr = reinterpret_cast<uint32_t*>(s_exp + 16);
+  int32_t* s_last = s_exp + 32;
+  int32_t* s_nlast = s_last + kMaxBlocks;
 
   // the generation of this call, or nothing at all when the words are not valid
   if (wave == 0) {
@@ -505,17 +683,31 @@ __global__ void __launch_bounds__(512) decode_stack_kernel(const StackParams P) 
   if (s_hdr[2] == 0) return;
   const uint64_t gen = ((uint64_t)s_hdr[1] << 32) | s_hdr[0];
   const int set = (int)(gen & 1);
-  // zero the other set for the next call (the previous call, its last user, has ended)
-  if (wave == 1 && lane < kSubs)
-    __hip_atomic_store(P.sync + sub_word(set ^ 1, lane), (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-
   const int nb = (int)gridDim.x, b = (int)blockIdx.x;
-  const int gu0 = (int)((int64_t)P.gu_units * b / nb), gu1 = (int)((int64_t)P.gu_units * (b + 1) / nb);
-  const int dt0 = (int)((int64_t)P.down_tiles * b / nb), dt1 = (int)((int64_t)P.down_tiles * (b + 1) / nb);
-  const int half = uni(wave / C_H), cq = uni(wave - half * C_H);
-  int phase = 0;
+  // zero the other set for the next call (the previous call, its last user, has ended)
+  if (b == 0 && wave == 1) {
+    for (int i = lane; i < kSubs + 2 * kMaxBlocks; i += 64) {
+      const int w = i < kSubs ? sub_word(set ^ 1, i)
+                              : (i < kSubs + kMaxBlocks ? cnt_word(set ^ 1, i - kSubs)
+                                                        : flag_word(set ^ 1, i - kSubs - kMaxBlocks));
+      __hip_atomic_store(P.sync + w, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  // barrier 1: this workgroup has read the words (workgroup 0 rewrites them only after it)
+  int phase = 1;
+  if (wave == 0) arrive(P, set, lane);
+  const int gu00 = (int)((int64_t)P.gu_units * b / nb), gu10 = (int)((int64_t)P.gu_units * (b + 1) / nb);
+  const int dt00 = (int)((int64_t)P.down_tiles * b / nb), dt10 = (int)((int64_t)P.down_tiles * (b + 1) / nb);
+  const int half0 = uni(wave / C_H0), cq0 = uni(wave - half0 * C_H0);
 
   for (int l = 0; l < P.L; ++l) {
+    // The values the layer derives its addresses from, made opaque once per layer: the
+    // compiler then recomputes what it derives from them inside the layer instead of
+    // keeping it live across the layer loop (more than the scalar registers hold).
+    int Pk = P.k, PI = P.I, PH = P.H, Pkp = P.kp;
+    int C_H = C_H0, C_I = C_I0, TI = TI0, T = T0, gu0 = gu00, gu1 = gu10, dt0 = dt00, dt1 = dt10, half = half0, cq = cq0;
+    asm volatile("" : "+s"(Pk), "+s"(PI), "+s"(PH), "+s"(Pkp), "+s"(C_H), "+s"(C_I), "+s"(TI), "+s"(T));
+    asm volatile("" : "+s"(gu0), "+s"(gu1), "+s"(dt0), "+s"(dt1), "+s"(half), "+s"(cq));
     const gale_layer_io io = layer_io(P, l);
     const gale_matrix* table = reinterpret_cast<const gale_matrix*>(io.experts);
     if (l > 0) {
@@ -523,30 +715,30 @@ __global__ void __launch_bounds__(512) decode_stack_kernel(const StackParams P) 
       if (wave == 0) wait_barrier(P, set, phase, lane);
       __syncthreads();
     }
-    // ---- R: route (wave 0) while waves 1 .. C_H rotate x into the record
-    if (wave == 0) {
-      topk_wave(RouteIn{io.logits, io.select_bias, io.fixed_idx}, 0, P.E, P.k, lane, s_exp, s_w, s_exp);
-    } else if (wave <= C_H) {
-      prep_x_chunk(io.x, P.H, wave - 1, rec, lane);
-    } else if (wave == W - 1 && l == 0) {
-      warm_table(table, P.E, lane, s_hdr + 3);
+    // ---- R: waves 0 .. C_H-1 rotate x into the record, one chunk each, while wave C_H
+    //      routes the token
+    if (wave < C_H) {
+      prep_x_chunk(io.x, PH, wave, rec, lane);
+    } else if (wave == C_H) {
+      topk_wave(RouteIn{io.logits, io.select_bias, io.fixed_idx}, 0, P.E, Pk, lane, s_exp, s_w, s_exp);
     }
+    if (wave == W - 1 && l == 0) warm_table(table, P.E, lane, s_hdr + 3);
     __syncthreads();
-    if (b == 0 && tid < P.k) {
+    if (b == 0 && tid < Pk) {
       if (io.topk_idx) io.topk_idx[tid] = s_exp[tid];
       if (io.topk_w) io.topk_w[tid] = s_w[tid];
     }
 
-    // ---- G: gate/up units, then (waves 1 ..) the first down tile's loads.
-    // the down tasks' loads (prefetched during gate/up when a wave has at most two sign
-    // tasks and one outlier row; the larger task sets load each task when it runs)
-    constexpr bool kPrefetch = NT <= 2 && NO <= 1;
+    // ---- G: gate/up units.  With at most two sign tasks and one outlier row per wave
+    //      (waves 1 ..), the first down tile's sign words and scales go straight to LDS right
+    //      behind the first unit's loads, and its outlier entries into registers behind the
+    //      sign pass; the larger task sets load each task when it runs.
     GuBuf<R> gb;
     DownBuf<NT, NO> db;
     const bool down_tasks = kPrefetch && wave >= 1 && dt0 < dt1;
     if (gu0 < gu1) {
       Act act;
-      record_activation(rec, P.H, cq, lane, act);
+      record_activation(rec, PH, cq, lane, act);
       block_sums<1>(act);
       for (int u = gu0; u < gu1; ++u) {
         const int par = (u - gu0) & 1;
@@ -570,86 +762,122 @@ __global__ void __launch_bounds__(512) decode_stack_kernel(const StackParams P) 
           if ((lane & 3) == 0) ored[16 * wave + (lane >> 2)] = s;
         }
         __syncthreads();
-        // wave 0: split-K sums in a fixed order plus outliers, h = silu(a) g per row
-        if (wave == 0) {
+        // wave 0: split-K sums in a fixed order plus outliers, h = silu(a) g per row; the
+        // others meanwhile send the first down tile's sign words and scales to LDS and its
+        // outlier rows' CSR ranges to registers (after the gate/up loads, so that no gate/up
+        // wait includes them)
+        if (wave != 0) {
+          if (u == gu0 && down_tasks) {
+            down_prefetch_lds<NT>(table, s_exp, Pk, C_I, Wd, wd, dt0, lane, dslots);
+            down_issue_rp<NT, NO>(table, s_exp, Pk, Wd, wd, dt0, lane, db);
+          }
+        } else {
           for (int rr = lane; rr < RR; rr += 64) {
             const int t = u * R + (rr >> 4);
             if (t >= T) continue;
             const int pr = t / TI;
             const int n = (t - pr * TI) * 16 + (rr & 15);
-            float a = 0.f, g = 0.f;
-            for (int q = 0; q < C_H; ++q) a += red[q * RR + rr];
-            for (int q = 0; q < C_H; ++q) g += red[(C_H + q) * RR + rr];
-            a = a + ored[rr];
-            g = g + ored[RR + rr];
-            cst_f32(P.h + (size_t)pr * P.I + n, silu_f(a) * g);
+            float hv;
+            switch (C_H) {
+              case 1: hv = combine_h<1, RR>(red, ored, rr); break;
+              case 2: hv = combine_h<2, RR>(red, ored, rr); break;
+              case 3: hv = combine_h<3, RR>(red, ored, rr); break;
+              default: hv = combine_h<4, RR>(red, ored, rr); break;
+            }
+            cst_f32(P.h + (size_t)pr * PI + n, hv);
           }
         }
       }
+    } else if (down_tasks) {
+      down_prefetch_lds<NT>(table, s_exp, Pk, C_I, Wd, wd, dt0, lane, dslots);
+      down_issue_rp<NT, NO>(table, s_exp, Pk, Wd, wd, dt0, lane, db);
+      down_issue_chunks<NT, NO>(table, s_exp, Pk, Wd, wd, dt0, lane, db);
     }
-    // the first down tile's loads (waves 1 ..; wave 0 holds no loads at its arrival): they travel
-    // while the h stores complete and the barrier fills
-    if (down_tasks) {
-      down_issue_rp<NT, NO>(table, s_exp, P.k, Wd, wd, dt0, lane, db);
-      down_issue_weights<NT, NO>(table, s_exp, P.k, C_I, Wd, wd, dt0, lane, db);
-      down_issue_chunks<NT, NO>(table, s_exp, P.k, Wd, wd, dt0, lane, db);
+    // ---- hand-off of h: every (pair, 1024-block) of h is 64 tiles.  Wavefront 0 counts
+    //      this workgroup's stored tiles into the blocks they belong to; the workgroup whose
+    //      count completes a block rotates it into the shared record and raises its flag.
+    if (wave == 0) {
+      int mine = -1;
+      if (gu0 < gu1) {
+        stores_done();   // this workgroup's h rows are stored
+        const int t0 = gu0 * R, t1 = min(gu1 * R, T);
+        const int blk = (t0 >> 6) + lane;
+        if (blk <= ((t1 - 1) >> 6)) {
+          const int n = min(t1, 64 * blk + 64) - max(t0, 64 * blk);
+          const uint64_t old = __hip_atomic_fetch_add(P.sync + cnt_word(set, blk), (uint64_t)n, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT);
+          if (old + (uint64_t)n == 64ull * (uint64_t)(l + 1)) mine = blk;
+        }
+      }
+      const uint64_t m = __ballot(mine >= 0);
+      if (mine >= 0) s_last[__builtin_popcountll(m & ((1ull << lane) - 1ull))] = mine;
+      if (lane == 0) *s_nlast = __builtin_popcountll(m);
     }
-    ++phase;
-    if (wave == 0) arrive(P, set, lane);
+    __syncthreads();
+    for (int i = wave; i < *s_nlast; i += W) {
+      const int blk = s_last[i], j = blk / C_I, c = blk - j * C_I;
+      float f[16];
+      load_h_block(P.h + (size_t)j * PI, c, lane, f);
+      PrepLane o;
+      prep_lane(f, lane, true, o);
+      store_record_chunk_dev(o, P.rec + (size_t)j * ra_bytes(PI), PI, c, lane);
+      stores_done();   // the record chunk is stored before its flag
+      if (lane == 0)
+        __hip_atomic_store(P.sync + flag_word(set, blk), (uint64_t)(l + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     if (wave == W - 1 && W - 1 > 0 && l + 1 < P.L) {
-      // the next layer's descriptors into L2 while the barrier completes
+      // the next layer's descriptors into L2 ahead of its routing
       const gale_layer_io nio = layer_io(P, l + 1);
       warm_table(reinterpret_cast<const gale_matrix*>(nio.experts), P.E, lane, s_hdr + 3);
     }
-    if (wave == 0) wait_barrier(P, set, phase, lane);
-    __syncthreads();
+
+    // the first down tile's outlier entries (their CSR ranges have arrived meanwhile)
+    if (gu0 < gu1 && down_tasks) down_issue_chunks<NT, NO>(table, s_exp, Pk, Wd, wd, dt0, lane, db);
 
     // ---- D: this workgroup's down tiles, all k pairs each
-    const int npass = (P.k + P.kp - 1) / P.kp;
+    const int npass = (Pk + Pkp - 1) / Pkp;
     for (int tile = dt0; tile < dt1; ++tile) {
       const int par = (tile - dt0) & 1;
-      lds_f32* dpart = dpart0 + par * (P.k * C_I * 16);
-      lds_f32* dout = dout0 + par * (P.k * 16);
+      lds_f32* dpart = dpart0 + par * (Pk * C_I * 16);
+      lds_f32* dout = dout0 + par * (Pk * 16);
       if (kPrefetch && tile > dt0 && wave >= 1) {
-        down_issue_rp<NT, NO>(table, s_exp, P.k, Wd, wd, tile, lane, db);
-        down_issue_weights<NT, NO>(table, s_exp, P.k, C_I, Wd, wd, tile, lane, db);
-        down_issue_chunks<NT, NO>(table, s_exp, P.k, Wd, wd, tile, lane, db);
+        down_prefetch_lds<NT>(table, s_exp, Pk, C_I, Wd, wd, tile, lane, dslots);
+        down_issue_rp<NT, NO>(table, s_exp, Pk, Wd, wd, tile, lane, db);
+        down_issue_chunks<NT, NO>(table, s_exp, Pk, Wd, wd, tile, lane, db);
       }
       for (int ps = 0; ps < npass; ++ps) {
-        const int j0 = ps * P.kp, j1 = min(P.k, j0 + P.kp);
-        // rotate the pass's pairs once per layer when they all fit, else once per tile and pass
+        const int j0 = ps * Pkp, j1 = min(Pk, j0 + Pkp);
+        // stage the pass's records once per layer when they all fit, else once per tile and pass
         if (npass > 1 || tile == dt0) {
           if (npass > 1 && (tile > dt0 || ps > 0)) __syncthreads();   // the previous pass's reads are done
-          // blocks wave, wave + W, ...: two at a time, both blocks' loads in flight together
           const int nblk = (j1 - j0) * C_I;
-          for (int blk = wave; blk < nblk; blk += 2 * W) {
-            const int blk2 = blk + W;
+          for (int blk = wave; blk < nblk; blk += W) {
             const int jl = blk / C_I, c = blk - jl * C_I;
-            const int jl2 = blk2 / C_I, c2 = blk2 - jl2 * C_I;
-            float fa[16], fb[16];
-            load_h_block(P.h + (size_t)(j0 + jl) * P.I, c, lane, fa);
-            if (blk2 < nblk) load_h_block(P.h + (size_t)(j0 + jl2) * P.I, c2, lane, fb);
-            rotate_h_block(fa, P.I, c, rec + (size_t)jl * ra_bytes(P.I), lane);
-            __builtin_amdgcn_sched_barrier(0);   // one block's transform at a time (registers)
-            if (blk2 < nblk) rotate_h_block(fb, P.I, c2, rec + (size_t)jl2 * ra_bytes(P.I), lane);
+            wait_flag(P, set, (j0 + jl) * C_I + c, (uint64_t)(l + 1), lane);
+            stage_record_chunk(P.rec + (size_t)(j0 + jl) * ra_bytes(PI), (lds_u8*)(rec + (size_t)jl * ra_bytes(PI)),
+                               PI, c, lane);
           }
+          stores_done();   // this wave's global-to-LDS loads have landed
           __syncthreads();
         }
         if (wave >= 1) {
           // one task at a time (a rolled loop: the registers of one task's operands and
-          // products); the slot's weights are picked from the prefetched set
+          // products); the prefetched slots were written to LDS by this wave's own loads
+          if (kPrefetch) stores_done();
 #pragma unroll 1
           for (int i = 0; i < NT; ++i) {
             const int s = sign_task(wd, i, Wd);
             const int j = s / C_I;
-            if (s < P.k * C_I && j >= j0 && j < j1) {
+            if (s < Pk * C_I && j >= j0 && j < j1) {
               const int c = s - j * C_I;
               uint32_t w[8], sc[4];
               if constexpr (kPrefetch) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) w[e] = i == 0 ? db.sw[0][e] : db.sw[NT - 1][e];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) sc[e] = i == 0 ? db.sc[0][e] : db.sc[NT - 1][e];
+                const lds_u8* slot = dslots + i * kDownSlotBytes;
+                const u32x4 lo = *reinterpret_cast<const lds_v4*>(slot + 16 * lane);
+                const u32x4 hi = *reinterpret_cast<const lds_v4*>(slot + 1024 + 16 * lane);
+                const u32x4 sv = *reinterpret_cast<const lds_v4*>(slot + 2048 + 16 * (lane & 15));
+                w[0] = lo.x; w[1] = lo.y; w[2] = lo.z; w[3] = lo.w; w[4] = hi.x; w[5] = hi.y; w[6] = hi.z; w[7] = hi.w;
+                sc[0] = sv.x; sc[1] = sv.y; sc[2] = sv.z; sc[3] = sv.w;
               } else {
                 // the larger task sets load each task's weights when it runs
                 const int sj = s / C_I;
@@ -664,7 +892,7 @@ __global__ void __launch_bounds__(512) decode_stack_kernel(const StackParams P) 
                 sc[0] = sv.x; sc[1] = sv.y; sc[2] = sv.z; sc[3] = sv.w;
               }
               Act act;
-              record_activation(rec + (size_t)(j - j0) * ra_bytes(P.I), P.I, c, lane, act);
+              record_activation(rec + (size_t)(j - j0) * ra_bytes(PI), PI, c, lane, act);
               block_sums<1>(act);
               float acc[1];
               sign_tile<1>(act, w, sc, acc);
@@ -675,7 +903,7 @@ __global__ void __launch_bounds__(512) decode_stack_kernel(const StackParams P) 
 #pragma unroll 1
           for (int i = 0; i < NO; ++i) {
             const int j = out_task(wd, i, Wd);
-            if (j < P.k && j >= j0 && j < j1) {
+            if (j < Pk && j >= j0 && j < j1) {
               OutBuf o;
               if constexpr (kPrefetch) {
                 o = db.o[0];
@@ -684,7 +912,7 @@ __global__ void __launch_bounds__(512) decode_stack_kernel(const StackParams P) 
                 out_issue_rp(m2, tile * 16 + (lane >> 2), o);
                 out_issue_chunks(m2, tile * 16 + (lane >> 2), lane, o);
               }
-              const lds_f32* xt = (const lds_f32*)(rec + (size_t)(j - j0) * ra_bytes(P.I));
+              const lds_f32* xt = (const lds_f32*)(rec + (size_t)(j - j0) * ra_bytes(PI));
               const float s = outlier_row_sum(table + uni(s_exp[j]) * 3 + 2, o, true, xt, wout, lane);
               if ((lane & 3) == 0) dout[j * 16 + (lane >> 2)] = s;
             }
@@ -694,12 +922,12 @@ __global__ void __launch_bounds__(512) decode_stack_kernel(const StackParams P) 
       __syncthreads();
       // wave 0: y = sum over slots in order of w_j (sum over chunks in order + outliers)
       if (wave == 0 && lane < 16) {
-        float acc = 0.f;
-        for (int j = 0; j < P.k; ++j) {
-          float a = 0.f;
-          for (int c = 0; c < C_I; ++c) a += dpart[(j * C_I + c) * 16 + lane];
-          a = a + dout[j * 16 + lane];
-          acc = fmaf(s_w[j], a, acc);
+        float acc;
+        switch (C_I) {
+          case 1: acc = combine_y<1>(dpart, dout, s_w, Pk, lane); break;
+          case 2: acc = combine_y<2>(dpart, dout, s_w, Pk, lane); break;
+          case 3: acc = combine_y<3>(dpart, dout, s_w, Pk, lane); break;
+          default: acc = combine_y<4>(dpart, dout, s_w, Pk, lane); break;
         }
         const __half yh = __float2half_rn(acc);
         const uint32_t bits = (uint32_t)__half_as_ushort(yh);
@@ -713,11 +941,14 @@ __global__ void __launch_bounds__(512) decode_stack_kernel(const StackParams P) 
       if (wave == 0) arrive(P, set, lane);
     }
   }
-  // workgroup 0 (which passed the first barrier, so every workgroup has read the
-  // words) records this call's generation for the next call
-  if (b == 0 && tid == 0) {
-    __hip_atomic_store(P.sync + 1, sync_check(gen), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(P.sync + 0, gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // workgroup 0 records this call's generation for the next call, once every workgroup has
+  // read the words (barrier 1)
+  if (b == 0 && wave == 0) {
+    wait_barrier(P, set, 1, lane);
+    if (lane == 0) {
+      __hip_atomic_store(P.sync + 1, sync_check(gen), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(P.sync + 0, gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
@@ -734,25 +965,31 @@ static int down_slots(int hidden, int inter, int k, int* nt, int* no) {
 
 static int pairs_per_pass(int hidden, int inter, int k, int R) {
   const int W = 2 * (hidden >> 10);
+  int nt = 0, no = 0;
+  if (!down_slots(hidden, inter, k, &nt, &no)) return 0;
+  const int nt_pre = (nt <= 2 && no <= 1) ? nt : 0;
   for (int kp = k; kp >= 1; --kp)
-    if (stack_lds(hidden, inter, k, kp, W, R).total <= kGemvMaxLds) return kp;
+    if (stack_lds(hidden, inter, k, kp, W, R, nt_pre).total <= kGemvMaxLds) return kp;
   return 0;
 }
 
 bool decode_layer_supported(int hidden, int inter, int top_k) {
-  if (hidden % 1024 || inter % 1024 || hidden < 1024 || hidden > 4096 || inter < 1024) return false;
-  if (top_k < 1 || top_k > GALE_MAX_TOPK) return false;
+  if (hidden % 1024 || inter % 1024 || hidden < 1024 || hidden > 1024 * kMaxChunksH || inter < 1024 ||
+      inter > 1024 * kMaxChunksI)
+    return false;
+  if (top_k < 1 || top_k > GALE_MAX_TOPK || top_k * (inter >> 10) > kMaxBlocks) return false;
   int nt, no;
   if (!down_slots(hidden, inter, top_k, &nt, &no)) return false;
   return pairs_per_pass(hidden, inter, top_k, 1) >= 1;
 }
 
 size_t decode_stack_h_bytes(int inter, int top_k) { return (size_t)4 * inter * top_k; }
+size_t decode_stack_rec_bytes(int inter, int top_k) { return ra_bytes(inter) * (size_t)top_k; }
 
 template <int R, int NT, int NO>
 static hipError_t launch_stack_r(StackParams P, hipStream_t s) {
   const int W = 2 * (P.H >> 10);
-  const size_t smem = stack_lds(P.H, P.I, P.k, P.kp, W, R).total;
+  const size_t smem = stack_lds(P.H, P.I, P.k, P.kp, W, R, (NT <= 2 && NO <= 1) ? NT : 0).total;
   auto kern = &decode_stack_kernel<R, NT, NO>;
   if (smem > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -775,8 +1012,8 @@ static hipError_t launch_stack_t(StackParams P, int nt, int no, hipStream_t s) {
 }
 
 hipError_t launch_decode_stack(const gale_layer_io& io0, const gale_layer_io* layers_dev, int L, int E, int k,
-                               int hidden, int inter, float* h, uint64_t* sync, int tiles, int64_t wait_ticks,
-                               hipStream_t s) {
+                               int hidden, int inter, float* h, uint8_t* rec, uint64_t* sync, int tiles,
+                               int64_t wait_ticks, hipStream_t s) {
   StackParams P;
   P.io0 = io0;
   P.layers = layers_dev;
@@ -786,6 +1023,7 @@ hipError_t launch_decode_stack(const gale_layer_io& io0, const gale_layer_io* la
   P.H = hidden;
   P.I = inter;
   P.h = h;
+  P.rec = rec;
   P.sync = sync;
   P.wait_ticks = wait_ticks;
   const int C_H = hidden >> 10;

@@ -189,13 +189,15 @@ hipError_t launch_grouped_gemm(const gale_matrix* table, int gateup, int rows, i
 
 // one-launch decode of one token through one MoE layer or a stack of layers (route, gate/up +
 // SwiGLU, rotate h, down, combine per layer); sync: kDecodeSyncBytes of synchronisation words
-// (zero-filled before the first call), h: decode_stack_h_bytes(inter, top_k) of fp32 h
+// (zero-filled before the first call), h: decode_stack_h_bytes(inter, top_k) of fp32 h,
+// rec: decode_stack_rec_bytes(inter, top_k) for the activation records of the rotated h
 constexpr size_t kDecodeSyncBytes = GALE_SYNC_BYTES;
 bool decode_layer_supported(int hidden, int inter, int top_k);
 size_t decode_stack_h_bytes(int inter, int top_k);
+size_t decode_stack_rec_bytes(int inter, int top_k);
 hipError_t launch_decode_stack(const gale_layer_io& io0, const gale_layer_io* layers_dev, int L, int E, int k,
-                               int hidden, int inter, float* h, uint64_t* sync, int tiles, int64_t wait_ticks,
-                               hipStream_t s);
+                               int hidden, int inter, float* h, uint8_t* rec, uint64_t* sync, int tiles,
+                               int64_t wait_ticks, hipStream_t s);
 hipError_t launch_sync_init(void* sync, hipStream_t s);
 // 0: valid and no error; 1: the words were never zeroed; 2: a barrier wait gave up
 int sync_words_state(const uint64_t words[3]);

@@ -338,6 +338,14 @@ def test_route_exact_with_ties(q):
     roff2, rperm2 = O.group_by_expert(ridx2, 256)
     assert np.array_equal(idx2.cpu().numpy(), ridx2)
     assert np.array_equal(off2.cpu().numpy(), roff2) and np.array_equal(perm2.cpu().numpy(), rperm2)
+    # few experts, ties among them: with as many experts as slots every expert is taken,
+    # in (logit desc, index asc) order; a tie plus too few keys must not pass for no tie
+    for row in ([1.0, 1.0, 2.0, 3.0, 4.0, 5.0], [3.0] * 7, [1.0, 1.0, 2.0, 3.0, 4.0, 5.0, 1.0, 0.0]):
+        lg3 = torch.tensor([row, row[::-1]], dtype=torch.float32)
+        idx3, w3, _, _ = q.route_topk(lg3.to(DEV), 6, group=True)
+        ridx3, rw3 = O.route(lg3.numpy(), 6)
+        assert np.array_equal(idx3.cpu().numpy(), ridx3), row
+        assert np.abs(w3.cpu().numpy() - rw3).max() <= 1e-6
 
 
 @pytest.fixture(scope="module")

@@ -62,6 +62,6 @@ def test_static_entry_rejects_oversize():
     import quantized_expert_gemv_amd as qq
     lib = qq.lib()
     fake = 1 << 40                                      # never dereferenced: rejected on the host
-    # top-6 of an intermediate size of 3072 needs 4608 + 73,728 workspace bytes
+    # top-6 of an intermediate size of 3072 needs 40,960 + 73,728 + 148,992 workspace bytes
     assert lib.gale_moe_decode_stack_static(4096, 3072, 16, 6, 2, fake, 0, None) == -5
     assert b"static array" in lib.gale_last_error()
