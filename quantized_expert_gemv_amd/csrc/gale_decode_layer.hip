@@ -173,16 +173,17 @@ __device__ __forceinline__ void arrive(const StackParams& P, int set, int lane) 
 
 // Wavefront 0 waits until every workgroup has arrived at barrier `phase` (1, 2, ...)
 // of set `set`, or the time budget runs out (then E records it and the wait ends).
-// Polls keep four loads in flight, issued a short sleep apart (kPollSleep x 64 clocks), so
-// that a change is seen sooner after it lands than with one load at a time.
-constexpr int kPollSleep = 3;
+// A poll keeps two loads in flight, issued a short sleep apart (kPollSleep x 64 clocks):
+// a change is seen sooner after it lands than with one load at a time, while the few lines
+// that a whole grid polls see few requests at once.
+constexpr int kPollSleep = 2;
+
 __device__ __forceinline__ void gave_up(const StackParams& P, int lane) {
   if (lane == 0) (void)__hip_atomic_fetch_or(P.sync + 2, kErrWaitGaveUp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Poll the lane's word w until ok(value) holds (a wavefront-uniform test) or the time budget
-// runs out (then E records it).  Four loads stay in flight; every exit leaves the loop
-// directly, so each test waits only for its own load.
+// runs out (then E records it).
 template <typename Ok>
 __device__ __forceinline__ void poll_until(const StackParams& P, const uint64_t* w, Ok ok, int lane) {
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
@@ -190,22 +191,12 @@ __device__ __forceinline__ void poll_until(const StackParams& P, const uint64_t*
   __builtin_amdgcn_s_sleep(kPollSleep);
   uint64_t v1 = sync_load(w);
   __builtin_amdgcn_s_sleep(kPollSleep);
-  uint64_t v2 = sync_load(w);
-  __builtin_amdgcn_s_sleep(kPollSleep);
-  uint64_t v3 = sync_load(w);
-  __builtin_amdgcn_s_sleep(kPollSleep);
   for (;;) {
     if (ok(v0)) goto done;
     v0 = sync_load(w);
     __builtin_amdgcn_s_sleep(kPollSleep);
     if (ok(v1)) goto done;
     v1 = sync_load(w);
-    __builtin_amdgcn_s_sleep(kPollSleep);
-    if (ok(v2)) goto done;
-    v2 = sync_load(w);
-    __builtin_amdgcn_s_sleep(kPollSleep);
-    if (ok(v3)) goto done;
-    v3 = sync_load(w);
     __builtin_amdgcn_s_sleep(kPollSleep);
     if ((int64_t)(__builtin_amdgcn_s_memrealtime() - t0) >= P.wait_ticks) {
       gave_up(P, lane);
@@ -224,11 +215,12 @@ __device__ __forceinline__ void wait_barrier(const StackParams& P, int set, int 
   poll_until(P, w, [&](uint64_t v) { return __all(!watch || v >= target) != 0; }, lane);
 }
 
-// The wavefront waits until block flag `b` of set `set` reaches `target`, or the time
-// budget runs out (then E records it and the wait ends).
-__device__ __forceinline__ void wait_flag(const StackParams& P, int set, int b, uint64_t target, int lane) {
-  // one address for the whole wavefront: one request per poll
-  poll_until(P, P.sync + flag_word(set, b), [&](uint64_t v) { return __all(v >= target) != 0; }, lane);
+// The wavefront waits until the flags of blocks b0 .. b0 + n - 1 (n <= 64, one lane each) of
+// set `set` reach `target`, or the time budget runs out (then E records it and the wait ends).
+__device__ __forceinline__ void wait_flags(const StackParams& P, int set, int b0, int n, uint64_t target, int lane) {
+  const bool watch = lane < n;
+  poll_until(P, P.sync + flag_word(set, watch ? b0 + lane : b0),
+             [&](uint64_t v) { return __all(!watch || v >= target) != 0; }, lane);
 }
 
 // ---- activation records -------------------------------------------------------------
@@ -257,41 +249,23 @@ __device__ __forceinline__ void load_h_block(const float* hv, int c, int lane, f
   }
 }
 
-// The same record chunk as store_record_chunk makes for fp32 input, written with
-// device-scope stores into a record in global memory (read by workgroups on other XCDs).
-// Neighbouring lanes (2m, 2m + 1) swap halves so that every store is 16 bytes (x~) or 4
-// bytes (terms) per lane, with device-scope (sc1) buffer stores:
-//   x~, registers 2j, 2j+1 (elements 128 j + 2 l, + 1), for j = 0, 2, 4, 6: the even lane
-//       stores its own pair and its partner's for j (elements 128 j + 4 m .. + 3), the odd
-//       lane its partner's pair and its own for j + 1 (elements 128 (j + 1) + 4 m .. + 3);
-//   terms, word q of term t (low half: granule 2q, high half: granule 2q + 1): the even
-//       lane stores both lanes' low halves (uint16 128 q + 2 m, + 1), the odd lane both
-//       high halves (uint16 128 q + 64 + 2 m, + 1).
-__device__ __forceinline__ void store_record_chunk_dev(const PrepLane& o, uint8_t* rec, int K, int c, int lane) {
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(rec, 0, (int)ra_bytes(K), kBufferWord3);
-  const bool odd = (lane & 1) != 0;
-  const int m = lane >> 1;
-#pragma unroll
-  for (int j = 0; j < 8; j += 2) {
-    const float p0 = lane_xor<1>(o.x[2 * j]), p1 = lane_xor<1>(o.x[2 * j + 1]);
-    const float p2 = lane_xor<1>(o.x[2 * j + 2]), p3 = lane_xor<1>(o.x[2 * j + 3]);
-    const u32x4 v = odd ? u32x4{__float_as_uint(p2), __float_as_uint(p3), __float_as_uint(o.x[2 * j + 2]),
-                                __float_as_uint(o.x[2 * j + 3])}
-                        : u32x4{__float_as_uint(o.x[2 * j]), __float_as_uint(o.x[2 * j + 1]), __float_as_uint(p0),
-                                __float_as_uint(p1)};
-    const int elem = 128 * (odd ? j + 1 : j) + 4 * m;
-    __builtin_amdgcn_raw_buffer_store_b128(v, rs, c * 4096 + 4 * elem, 0, kDeviceScope);
-  }
-  const int toff = (int)ra_terms_off(K) + c * 4096;
-#pragma unroll
-  for (int t = 0; t < kTerms; ++t)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t w = o.t[t][q], pw = lane_xor_u32<1>(w);
-      const uint32_t v = odd ? ((pw >> 16) | (w & 0xFFFF0000u)) : ((w & 0xFFFFu) | (pw << 16));
-      __builtin_amdgcn_raw_buffer_store_b32(v, rs, toff + t * 1024 + 4 * (64 * q + (odd ? 32 : 0) + m), 0, kDeviceScope);
-    }
-  if (lane == 0) cst_u32(rec + ra_p_off(K) + 4 * (size_t)c, (uint32_t)o.p);
+// A compact chunk record in LDS (fp32 x~ at 0, the four terms at 4096, the exponent at
+// 8192: store_record_chunk's layout for K = 1024, c = 0), with room to keep the next one
+// 256-byte aligned.
+constexpr int kRotScratch = 8192 + 256;
+
+// Piece q (1 KB: x~ for q < 4, terms for q >= 4) of a compact chunk record in LDS into chunk
+// c of a record in global memory, 16 bytes per lane with a device-scope buffer store; piece
+// 0 also carries the exponent.
+__device__ __forceinline__ void copy_record_piece(const uint8_t* lrec, uint8_t* grec, int K, int c, int q,
+                                                  int lane) {
+  const u32x4 v = *reinterpret_cast<const lds_v4*>((const lds_u8*)lrec + q * 1024 + 16 * lane);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(grec, 0, (int)ra_bytes(K), kBufferWord3);
+  const int off = (q < 4 ? c * 4096 + q * 1024 : (int)ra_terms_off(K) + c * 4096 + (q - 4) * 1024) + 16 * lane;
+  __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, kDeviceScope);
+  if (q == 0 && lane == 0)
+    cst_u32(grec + ra_p_off(K) + 4 * (size_t)c, *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(
+                                                     (const lds_u8*)lrec + 8192));
 }
 
 // Chunk c of a record in global memory (written by another workgroup) into the same
@@ -764,8 +738,8 @@ __global__ void __launch_bounds__(512) decode_stack_kernel(const StackParams P) 
         __syncthreads();
         // wave 0: split-K sums in a fixed order plus outliers, h = silu(a) g per row; the
         // others meanwhile send the first down tile's sign words and scales to LDS and its
-        // outlier rows' CSR ranges to registers (after the gate/up loads, so that no gate/up
-        // wait includes them)
+        // outlier rows' CSR ranges to registers (after the gate/up loads: no gate/up wait
+        // includes them)
         if (wave != 0) {
           if (u == gu0 && down_tasks) {
             down_prefetch_lds<NT>(table, s_exp, Pk, C_I, Wd, wd, dt0, lane, dslots);
@@ -814,25 +788,43 @@ __global__ void __launch_bounds__(512) decode_stack_kernel(const StackParams P) 
       if (lane == 0) *s_nlast = __builtin_popcountll(m);
     }
     __syncthreads();
-    for (int i = wave; i < *s_nlast; i += W) {
-      const int blk = s_last[i], j = blk / C_I, c = blk - j * C_I;
-      float f[16];
-      load_h_block(P.h + (size_t)j * PI, c, lane, f);
-      PrepLane o;
-      prep_lane(f, lane, true, o);
-      store_record_chunk_dev(o, P.rec + (size_t)j * ra_bytes(PI), PI, c, lane);
-      stores_done();   // the record chunk is stored before its flag
-      if (lane == 0)
-        __hip_atomic_store(P.sync + flag_word(set, blk), (uint64_t)(l + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // The completed blocks, nrot at a time: one wavefront each rotates its block into a
+    // compact chunk record in LDS (the record region is free between gate/up and down), then
+    // all wavefronts copy them to the shared records in 1 KB pieces of 16-byte device-scope
+    // stores, and once every store is acknowledged the blocks' flags go up.
+    {
+      const int nlast = *s_nlast;
+      const int nrot_max = min(W, (int)(LL.red / kRotScratch));
+      for (int i0 = 0; i0 < nlast; i0 += nrot_max) {
+        const int nrot = min(nrot_max, nlast - i0);
+        if (wave < nrot) {
+          const int blk = s_last[i0 + wave], j = blk / C_I, c = blk - j * C_I;
+          float f[16];
+          load_h_block(P.h + (size_t)j * PI, c, lane, f);
+          PrepLane o;
+          prep_lane(f, lane, true, o);
+          store_record_chunk(o, GALE_F32, rec + wave * kRotScratch, 1024, 0, lane);
+        }
+        __syncthreads();
+        for (int piece = wave; piece < 8 * nrot; piece += W) {
+          const int r = piece >> 3, q = piece & 7;
+          const int blk = s_last[i0 + r], j = blk / C_I, c = blk - j * C_I;
+          copy_record_piece(rec + r * kRotScratch, P.rec + (size_t)j * ra_bytes(PI), PI, c, q, lane);
+        }
+        stores_done();   // this wavefront's pieces are stored
+        __syncthreads();
+        if (wave == 0 && lane < nrot)
+          __hip_atomic_store(P.sync + flag_word(set, s_last[i0 + lane]), (uint64_t)(l + 1), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
+    // the first down tile's outlier entries (their CSR ranges have arrived meanwhile)
+    if (gu0 < gu1 && down_tasks) down_issue_chunks<NT, NO>(table, s_exp, Pk, Wd, wd, dt0, lane, db);
     if (wave == W - 1 && W - 1 > 0 && l + 1 < P.L) {
       // the next layer's descriptors into L2 ahead of its routing
       const gale_layer_io nio = layer_io(P, l + 1);
       warm_table(reinterpret_cast<const gale_matrix*>(nio.experts), P.E, lane, s_hdr + 3);
     }
-
-    // the first down tile's outlier entries (their CSR ranges have arrived meanwhile)
-    if (gu0 < gu1 && down_tasks) down_issue_chunks<NT, NO>(table, s_exp, Pk, Wd, wd, dt0, lane, db);
 
     // ---- D: this workgroup's down tiles, all k pairs each
     const int npass = (Pk + Pkp - 1) / Pkp;
@@ -851,9 +843,11 @@ __global__ void __launch_bounds__(512) decode_stack_kernel(const StackParams P) 
         if (npass > 1 || tile == dt0) {
           if (npass > 1 && (tile > dt0 || ps > 0)) __syncthreads();   // the previous pass's reads are done
           const int nblk = (j1 - j0) * C_I;
+          // one wavefront watches the pass's block flags for the workgroup
+          if (wave == 0) wait_flags(P, set, j0 * C_I, nblk, (uint64_t)(l + 1), lane);
+          __syncthreads();
           for (int blk = wave; blk < nblk; blk += W) {
             const int jl = blk / C_I, c = blk - jl * C_I;
-            wait_flag(P, set, (j0 + jl) * C_I + c, (uint64_t)(l + 1), lane);
             stage_record_chunk(P.rec + (size_t)(j0 + jl) * ra_bytes(PI), (lds_u8*)(rec + (size_t)jl * ra_bytes(PI)),
                                PI, c, lane);
           }
