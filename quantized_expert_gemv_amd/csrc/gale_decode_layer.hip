@@ -466,9 +466,10 @@ __device__ __forceinline__ void gu_issue_weights(const gale_matrix* table, const
 }
 
 // ---- phase D: the down tasks of one workgroup ---------------------------------------
-// Wavefronts 1 .. W-1 (Wd of them) take the k C_I sign tasks (pair s / C_I, chunk
-// s % C_I) round robin, slot s / Wd; the k outlier rows (one 16-row group per pair) go
-// round robin from the last wavefront down, slot j / Wd.  Wavefront 0 combines.
+// All W wavefronts take the k C_I sign tasks (pair s / C_I, chunk s % C_I) round robin,
+// slot s / W (wavefronts w and w + 4 share a SIMD, so every SIMD gets the same share of the
+// matrix-core work); the k outlier rows (one 16-row group per pair) go round robin from the
+// last wavefront down, slot j / W.  Wavefront 0 then combines.
 template <int NT, int NO>
 struct DownBuf {
   OutBuf o[NO];
@@ -488,9 +489,9 @@ __device__ __forceinline__ void down_issue_rp(const gale_matrix* table, const in
 }
 
 // The sign words and block scales of this wavefront's first NT sign tasks of one tile,
-// straight from memory into its LDS slots (no registers): slot i holds the tile chunk's
-// 2 KB of sign words in the wave's load order (lane l's 16 bytes at 16 l and 1024 + 16 l)
-// and the 16 rows' scales at 2048 + 16 r.
+// straight from memory into LDS (no registers): task s has slot s, which holds the tile
+// chunk's 2 KB of sign words in the wave's load order (lane l's 16 bytes at 16 l and
+// 1024 + 16 l) and the 16 rows' scales at 2048 + 16 r.
 constexpr int kDownSlotBytes = 2048 + 256;
 
 template <int NT>
@@ -504,7 +505,7 @@ __device__ __forceinline__ void down_prefetch_lds(const gale_matrix* table, cons
       const auto* m = as_const(table) + uni(s_exp[j]) * 3 + 2;
       const char* sg = reinterpret_cast<const char*>(m->signs) + ((size_t)tile * C + c) * 2048;
       const char* scl = reinterpret_cast<const char*>(m->block_scales) + ((size_t)tile * C + c) * 256;
-      lds_u8* dst = slots + i * kDownSlotBytes;
+      lds_u8* dst = slots + s * kDownSlotBytes;
       __builtin_amdgcn_global_load_lds((g_cu8*)(sg + 16 * lane), dst, 16, 0, 0);
       __builtin_amdgcn_global_load_lds((g_cu8*)(sg + 1024 + 16 * lane), dst + 1024, 16, 0, 0);
       if (lane < 16) __builtin_amdgcn_global_load_lds((g_cu8*)(scl + 16 * lane), dst + 2048, 16, 0, 0);
@@ -582,8 +583,9 @@ constexpr int kMiscBytes = 128 + 4 * kMaxBlocks + 16;
 struct StackLds {
   uint32_t rec, red, ored, dpart, dout, wout, misc, dpre, total;
 };
-// nt_pre: sign-task slots per wavefront prefetched into LDS (0 when the tasks load as they run)
-__host__ __device__ inline StackLds stack_lds(int H, int I, int k, int kp, int W, int R, int nt_pre) {
+// pre: whether the sign tasks' weights are prefetched into LDS (one slot per task, k C_I of
+// them) or load as the tasks run
+__host__ __device__ inline StackLds stack_lds(int H, int I, int k, int kp, int W, int R, bool pre) {
   StackLds s;
   // (sizes of shapes far beyond the LDS are not meant: the caller checks total against it)
   const uint32_t rb = (uint32_t)ra_bytes(H), rh = (uint32_t)(kp * ra_bytes(I));
@@ -595,7 +597,7 @@ __host__ __device__ inline StackLds stack_lds(int H, int I, int k, int kp, int W
   s.wout = s.dout + 2u * k * 16 * 4;
   s.misc = s.wout + (uint32_t)W * kWaveOutBytes;
   s.dpre = s.misc + kMiscBytes;
-  s.total = s.dpre + (uint32_t)(W - 1) * nt_pre * kDownSlotBytes;
+  s.total = s.dpre + (pre ? (uint32_t)(k * (I >> 10)) * kDownSlotBytes : 0u);
   return s;
 }
 
@@ -616,14 +618,14 @@ template <int R, int NT, int NO>
 __global__ void __launch_bounds__(512) decode_stack_kernel(const StackParams P) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
-  const int W = (int)(blockDim.x >> 6), Wd = W - 1, wd = wave - 1;
+  const int W = (int)(blockDim.x >> 6), Wd = W, wd = wave;   // the down tasks' wavefronts
   const int C_H0 = P.H >> 10, C_I0 = P.I >> 10;
   const int TI0 = P.I >> 4, T0 = P.k * TI0;
   const int C_H = C_H0, C_I = C_I0;
   constexpr int RR = 16 * R;
   constexpr bool kPrefetch = NT <= 2 && NO <= 1;   // the larger task sets load each task when it runs
-  const StackLds LL = stack_lds(P.H, P.I, P.k, P.kp, W, R, kPrefetch ? NT : 0);
-  lds_u8* dslots = (lds_u8*)(smem + LL.dpre) + (wave >= 1 ? wave - 1 : 0) * NT * kDownSlotBytes;
+  const StackLds LL = stack_lds(P.H, P.I, P.k, P.kp, W, R, kPrefetch);
+  lds_u8* dslots = (lds_u8*)(smem + LL.dpre);   // one slot per sign task
   uint8_t* rec = smem + LL.rec;
   lds_f32* red0 = (lds_f32*)(smem + LL.red);
   lds_f32* ored0 = (lds_f32*)(smem + LL.ored);
@@ -709,7 +711,7 @@ __global__ void __launch_bounds__(512) decode_stack_kernel(const StackParams P) 
     //      sign pass; the larger task sets load each task when it runs.
     GuBuf<R> gb;
     DownBuf<NT, NO> db;
-    const bool down_tasks = kPrefetch && wave >= 1 && dt0 < dt1;
+    const bool down_tasks = kPrefetch && dt0 < dt1;
     if (gu0 < gu1) {
       Act act;
       record_activation(rec, PH, cq, lane, act);
@@ -818,8 +820,15 @@ __global__ void __launch_bounds__(512) decode_stack_kernel(const StackParams P) 
                              __HIP_MEMORY_SCOPE_AGENT);
       }
     }
-    // the first down tile's outlier entries (their CSR ranges have arrived meanwhile)
-    if (gu0 < gu1 && down_tasks) down_issue_chunks<NT, NO>(table, s_exp, Pk, Wd, wd, dt0, lane, db);
+    // the first down tile's outlier entries (their CSR ranges have arrived meanwhile); wave 0's
+    // sign tasks only now (its stores had to be acknowledged first, with no loads in flight)
+    if (gu0 < gu1 && down_tasks) {
+      if (wave == 0) {
+        down_prefetch_lds<NT>(table, s_exp, Pk, C_I, Wd, wd, dt0, lane, dslots);
+        down_issue_rp<NT, NO>(table, s_exp, Pk, Wd, wd, dt0, lane, db);
+      }
+      down_issue_chunks<NT, NO>(table, s_exp, Pk, Wd, wd, dt0, lane, db);
+    }
     if (wave == W - 1 && W - 1 > 0 && l + 1 < P.L) {
       // the next layer's descriptors into L2 ahead of its routing
       const gale_layer_io nio = layer_io(P, l + 1);
@@ -832,7 +841,7 @@ __global__ void __launch_bounds__(512) decode_stack_kernel(const StackParams P) 
       const int par = (tile - dt0) & 1;
       lds_f32* dpart = dpart0 + par * (Pk * C_I * 16);
       lds_f32* dout = dout0 + par * (Pk * 16);
-      if (kPrefetch && tile > dt0 && wave >= 1) {
+      if (kPrefetch && tile > dt0) {
         down_prefetch_lds<NT>(table, s_exp, Pk, C_I, Wd, wd, tile, lane, dslots);
         down_issue_rp<NT, NO>(table, s_exp, Pk, Wd, wd, tile, lane, db);
         down_issue_chunks<NT, NO>(table, s_exp, Pk, Wd, wd, tile, lane, db);
@@ -854,7 +863,7 @@ __global__ void __launch_bounds__(512) decode_stack_kernel(const StackParams P) 
           stores_done();   // this wave's global-to-LDS loads have landed
           __syncthreads();
         }
-        if (wave >= 1) {
+        {
           // one task at a time (a rolled loop: the registers of one task's operands and
           // products); the prefetched slots were written to LDS by this wave's own loads
           if (kPrefetch) stores_done();
@@ -866,7 +875,7 @@ __global__ void __launch_bounds__(512) decode_stack_kernel(const StackParams P) 
               const int c = s - j * C_I;
               uint32_t w[8], sc[4];
               if constexpr (kPrefetch) {
-                const lds_u8* slot = dslots + i * kDownSlotBytes;
+                const lds_u8* slot = dslots + s * kDownSlotBytes;
                 const u32x4 lo = *reinterpret_cast<const lds_v4*>(slot + 16 * lane);
                 const u32x4 hi = *reinterpret_cast<const lds_v4*>(slot + 1024 + 16 * lane);
                 const u32x4 sv = *reinterpret_cast<const lds_v4*>(slot + 2048 + 16 * (lane & 15));
@@ -949,8 +958,7 @@ __global__ void __launch_bounds__(512) decode_stack_kernel(const StackParams P) 
 // ---- host side ----------------------------------------------------------------------
 // Down tasks per wavefront of a shape, or 0 when they do not fit the built variants.
 static int down_slots(int hidden, int inter, int k, int* nt, int* no) {
-  const int W = 2 * (hidden >> 10), Wd = W - 1, C_I = inter >> 10;
-  if (Wd < 1) return 0;
+  const int W = 2 * (hidden >> 10), Wd = W, C_I = inter >> 10;
   const int need_t = (k * C_I + Wd - 1) / Wd, need_o = (k + Wd - 1) / Wd;
   if (need_t <= 2 && need_o <= 1) { *nt = 2; *no = 1; return 1; }   // prefetched during gate/up
   if (need_t <= 4 && need_o <= 2) { *nt = 4; *no = 2; return 1; }   // loaded task by task
@@ -961,9 +969,9 @@ static int pairs_per_pass(int hidden, int inter, int k, int R) {
   const int W = 2 * (hidden >> 10);
   int nt = 0, no = 0;
   if (!down_slots(hidden, inter, k, &nt, &no)) return 0;
-  const int nt_pre = (nt <= 2 && no <= 1) ? nt : 0;
+  const bool pre = nt <= 2 && no <= 1;
   for (int kp = k; kp >= 1; --kp)
-    if (stack_lds(hidden, inter, k, kp, W, R, nt_pre).total <= kGemvMaxLds) return kp;
+    if (stack_lds(hidden, inter, k, kp, W, R, pre).total <= kGemvMaxLds) return kp;
   return 0;
 }
 
@@ -983,7 +991,7 @@ size_t decode_stack_rec_bytes(int inter, int top_k) { return ra_bytes(inter) * (
 template <int R, int NT, int NO>
 static hipError_t launch_stack_r(StackParams P, hipStream_t s) {
   const int W = 2 * (P.H >> 10);
-  const size_t smem = stack_lds(P.H, P.I, P.k, P.kp, W, R, (NT <= 2 && NO <= 1) ? NT : 0).total;
+  const size_t smem = stack_lds(P.H, P.I, P.k, P.kp, W, R, NT <= 2 && NO <= 1).total;
   auto kern = &decode_stack_kernel<R, NT, NO>;
   if (smem > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
