@@ -696,7 +696,10 @@ __global__ void __launch_bounds__(512) decode_stack_kernel(const StackParams P) 
     if (wave < C_H) {
       prep_x_chunk(io.x, PH, wave, rec, lane);
     } else if (wave == C_H) {
+      // the routing is the longer of the two and shares its SIMD with wave 0: it issues first
+      __builtin_amdgcn_s_setprio(3);
       topk_wave(RouteIn{io.logits, io.select_bias, io.fixed_idx}, 0, P.E, Pk, lane, s_exp, s_w, s_exp);
+      __builtin_amdgcn_s_setprio(0);
     }
     if (wave == W - 1 && l == 0) warm_table(table, P.E, lane, s_hdr + 3);
     __syncthreads();
