@@ -176,7 +176,7 @@ __device__ __forceinline__ void arrive(const StackParams& P, int set, int lane) 
 // A poll keeps two loads in flight, issued a short sleep apart (kPollSleep x 64 clocks):
 // a change is seen sooner after it lands than with one load at a time, while the few lines
 // that a whole grid polls see few requests at once.
-constexpr int kPollSleep = 2;
+constexpr int kPollSleep = 1;
 
 __device__ __forceinline__ void gave_up(const StackParams& P, int lane) {
   if (lane == 0) (void)__hip_atomic_fetch_or(P.sync + 2, kErrWaitGaveUp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
