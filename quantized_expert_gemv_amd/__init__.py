@@ -14,3 +14,4 @@ from .binding import (  # noqa: F401
     GALE_SYNC_NO_WAIT, GALE_SYNC_BYTES, GALE_ERR_SYNC, moe_workspace, sync_init, sync_status,
     decode_stack_workspace_bytes, layer_table, moe_decode_stack,
 )
+from .pack_files import Pack, PackWriter, LoadedStack, load_stack, read_manifest  # noqa: F401,E402
