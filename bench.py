@@ -14,13 +14,14 @@ Reported:
                HIP graph) and one launch for the whole stack -- and the fastest is the value
                (all three give the same outputs bit for bit; checked here)
   tokens_per_s steps per second
-  roofline     the GEMV kernel at its sustained launch shape: one launch over 1024
-               distinct [2048, 4096] matrices of the resident stack (w1 and w3 of 512
-               experts), one token each, prepared activations, timed with HIP events on the
-               launch stream; algorithmic bytes 1,405,952 per matrix
-  gemv_single_matrix  the single-matrix workload as configured: FWHT-1024 of each matrix's
-               own x and the activation split, then the GEMV (two launches), over the same
-               1024 matrices; and one matrix per call (launch-latency bound)
+  roofline     the single-matrix workload as configured at its sustained launch shape: one
+               launch over 1024 distinct [2048, 4096] matrices of the resident stack (w1 and
+               w3 of 512 experts), each with its own fp16 x, which the GEMV kernel rotates
+               (FWHT-1024) and splits into fp8 terms itself before its products; timed with
+               HIP events on the launch stream; algorithmic bytes 1,405,952 per matrix
+  gemv_single_matrix  the same workload (sustained), the same kernel on activation records
+               prepared before the timed region, and one matrix per call (launch-latency
+               bound)
   ffn          one expert FFN, one token: one expert per call, and 256 distinct experts per
                launch (each its own x), GB/s of 4,196,352 algorithmic bytes per expert
   decode_batches, prefill  one MoE layer at 1/4/16/32 tokens; the 2048-token grouped prefill
@@ -385,36 +386,10 @@ def main() -> int:
     n = min(args.gemv_mats, len(w13_all) // 2)
     sets = [q.matrix_table(w13_all[i * n:(i + 1) * n]) for i in range(2)]     # two disjoint sets, alternated
     xg = torch.stack([gen_x(seed, (0x30000 + i,), 1, HIDDEN, device=dev) for i in range(n)])
-    rec = q.prepare_activations(xg)
     yg = torch.empty(n, 1, INTER, dtype=torch.float16, device=dev)
-    gemv_args = [(INTER, HIDDEN, t.ptr(), n, rec.data_ptr(), q.GALE_F16, 0, 1, yg.data_ptr(), q.GALE_F16, None, 0,
-                  q.GALE_X_PREPARED) for t in sets]
     flip = [0]
-
-    def gemv_call():
-        a = gemv_args[flip[0]]
-        flip[0] ^= 1
-        rc = lib.gale_expert_gemv(*a, torch.cuda.current_stream().cuda_stream)
-        if rc:
-            raise RuntimeError(lib.gale_last_error().decode())
-
-    # The device reaches its steady clocks only after some time under load: stream the
-    # sustained-GEMV pool for a while before any timed region.
-    t_w = time.time()
-    while time.time() - t_w < args.device_warm_s:
-        for _ in range(16):
-            gemv_call()
-        torch.cuda.synchronize()
-    for _ in range(GEMV_WARM_CALLS):
-        gemv_call()
-    torch.cuda.synchronize()
-    ms_gemv = time_events(gemv_call, args.gemv_reps)
-    gemv_gbps = n * GEMV_UNIT_BYTES / (ms_gemv * 1e-3) / 1e9
-    log(f"sustained GEMV: {n} matrices in {ms_gemv * 1e3:.1f} us -> {gemv_gbps:.0f} GB/s "
-        f"({100 * gemv_gbps / HBM_PEAK_GBPS:.1f}% of 8 TB/s)")
-
-    # ---- the single-matrix workload as configured: FWHT-1024 and the activation split of each
-    #      matrix's own fp16 x, then the GEMV (gale_expert_gemv on raw x: two launches)
+    # the single-matrix workload as configured: each matrix's own fp16 x, rotated and split
+    # inside the GEMV kernel (gale_expert_gemv on raw x, one token per matrix: one launch)
     wsg = torch.empty(max(q.gemv_workspace_bytes(INTER, HIDDEN, n, 1, 0), 256), dtype=torch.uint8, device=dev)
     e2e_args = [(INTER, HIDDEN, t.ptr(), n, xg.data_ptr(), q.GALE_F16, 0, 1, yg.data_ptr(), q.GALE_F16,
                  wsg.data_ptr(), wsg.numel(), 0) for t in sets]
@@ -426,13 +401,41 @@ def main() -> int:
         if rc:
             raise RuntimeError(lib.gale_last_error().decode())
 
+    # The device reaches its steady clocks only after some time under load: stream the
+    # sustained-GEMV pool for a while before any timed region.
+    t_w = time.time()
+    while time.time() - t_w < args.device_warm_s:
+        for _ in range(16):
+            gemv_e2e_call()
+        torch.cuda.synchronize()
     for _ in range(GEMV_WARM_CALLS):
         gemv_e2e_call()
     torch.cuda.synchronize()
-    ms_e2e = time_events(gemv_e2e_call, args.gemv_reps)
-    e2e_gbps = n * GEMV_UNIT_BYTES / (ms_e2e * 1e-3) / 1e9
-    log(f"single-matrix workload as configured (rotation + GEMV, {n} distinct matrices): {ms_e2e * 1e3:.1f} us "
-        f"-> {e2e_gbps:.0f} GB/s ({100 * e2e_gbps / HBM_PEAK_GBPS:.1f}% of 8 TB/s)")
+    ms_gemv = time_events(gemv_e2e_call, args.gemv_reps)
+    gemv_gbps = n * GEMV_UNIT_BYTES / (ms_gemv * 1e-3) / 1e9
+    log(f"single-matrix workload as configured (rotation + split + GEMV in one launch, {n} distinct matrices): "
+        f"{ms_gemv * 1e3:.1f} us -> {gemv_gbps:.0f} GB/s ({100 * gemv_gbps / HBM_PEAK_GBPS:.1f}% of 8 TB/s)")
+
+    # ---- the same GEMV on activation records prepared before the timed region
+    rec = q.prepare_activations(xg)
+    gemv_args = [(INTER, HIDDEN, t.ptr(), n, rec.data_ptr(), q.GALE_F16, 0, 1, yg.data_ptr(), q.GALE_F16, None, 0,
+                  q.GALE_X_PREPARED) for t in sets]
+
+    def gemv_call():
+        a = gemv_args[flip[0]]
+        flip[0] ^= 1
+        rc = lib.gale_expert_gemv(*a, torch.cuda.current_stream().cuda_stream)
+        if rc:
+            raise RuntimeError(lib.gale_last_error().decode())
+
+    for _ in range(GEMV_WARM_CALLS):
+        gemv_call()
+    torch.cuda.synchronize()
+    ms_rec = time_events(gemv_call, args.gemv_reps)
+    rec_gbps = n * GEMV_UNIT_BYTES / (ms_rec * 1e-3) / 1e9
+    log(f"the same GEMV on prepared records: {ms_rec * 1e3:.1f} us -> {rec_gbps:.0f} GB/s "
+        f"({100 * rec_gbps / HBM_PEAK_GBPS:.1f}% of 8 TB/s)")
+    del rec
     # one matrix per call (a different one each time), FWHT + GEMV: launch-latency bound
     one_tabs = [q.matrix_table([w13_all[i]]) for i in range(0, 2 * n, 2 * n // 64)]
     ws1 = torch.empty(max(q.gemv_workspace_bytes(INTER, HIDDEN, 1, 1, 0), 256), dtype=torch.uint8, device=dev)
@@ -451,7 +454,8 @@ def main() -> int:
         gemv_one_call()
     ms_one_iso = time_isolated(gemv_one_call, 64)
     ms_one_tp = time_events(gemv_one_call, 256)
-    log(f"one matrix per call: {ms_one_iso * 1e3:.2f} us isolated, {ms_one_tp * 1e3:.2f} us back to back")
+    log(f"one matrix per call (one launch): {ms_one_iso * 1e3:.2f} us isolated, "
+        f"{ms_one_tp * 1e3:.2f} us back to back")
     del one_tabs
 
     # ---- one expert FFN, one token: one expert per call, and 256 distinct experts per launch
@@ -669,20 +673,26 @@ def main() -> int:
         "bytes_per_token": bytes_per_token,
         "roofline": {"bound": "hbm", "achieved": round(gemv_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gemv_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "kernel": "gemv_kernel<1,4,false,512,2> (fp4 sign-plane MFMA GEMV)",
+                     "kernel": "gemv_kernel<1,4,false,512,2,true> (FWHT-1024 and fp8 split of x in LDS, "
+                               "then the fp4 sign-plane MFMA GEMV with outliers; one launch)",
                      "launch": f"{n} distinct [2048,4096] matrices (w1, w3 of {n // 2} experts) x 1 token, "
-                               f"prepared activations; two disjoint sets alternated",
+                               f"each with its own fp16 x; two disjoint sets alternated",
                      "bytes_per_launch": n * GEMV_UNIT_BYTES, "avg_launch_us": round(ms_gemv * 1e3, 2),
                      "source_sha256": gemv_source_hash()[:16]},
         "gemv_single_matrix": {
             "workload": "one [2048 out, 4096 in] matrix, 1 token: FWHT-1024 of x and the fp8 activation split, "
-                        "then the GEMV (two launches)",
-            "sustained": {"matrices_per_call": n, "avg_call_us": round(ms_e2e * 1e3, 2),
-                          "gbps": round(e2e_gbps, 1), "frac_of_peak": round(e2e_gbps / HBM_PEAK_GBPS, 4),
-                          "note": "each matrix with its own x; rotation + split + GEMV inside the timed call"},
+                        "then the GEMV (one launch)",
+            "sustained": {"matrices_per_call": n, "avg_call_us": round(ms_gemv * 1e3, 2),
+                          "gbps": round(gemv_gbps, 1), "frac_of_peak": round(gemv_gbps / HBM_PEAK_GBPS, 4),
+                          "note": "each matrix with its own x; rotation + split + GEMV inside the timed call "
+                                  "(the roofline launch)"},
+            "prepared_records": {"matrices_per_call": n, "avg_call_us": round(ms_rec * 1e3, 2),
+                                 "gbps": round(rec_gbps, 1), "frac_of_peak": round(rec_gbps / HBM_PEAK_GBPS, 4),
+                                 "note": "the same GEMV on activation records prepared before the timed region "
+                                         "(33 KB each instead of the 8 KB fp16 x)"},
             "one_matrix_per_call": {"isolated_us": round(ms_one_iso * 1e3, 2),
                                     "back_to_back_us": round(ms_one_tp * 1e3, 2),
-                                    "note": "launch-latency bound (two launches per call)"}},
+                                    "note": "launch-latency bound (one launch per call)"}},
         "ffn": {"workload": "one expert FFN (w1, w3 [2048,4096], w2 [4096,2048]), 1 token",
                 "sustained": {"experts_per_launch": EXPERTS, "avg_launch_us": round(ms_ffn_many * 1e3, 2),
                               "gbps": round(ffn_gbps, 1), "frac_of_peak": round(ffn_gbps / HBM_PEAK_GBPS, 4),

@@ -229,7 +229,10 @@ size_t gale_gemv_workspace_bytes(int32_t rows, int32_t cols, int32_t n_mat, int3
  *    dtype x_dtype (GALE_F16 / GALE_F32); flags GALE_X_ROTATED means x is already H.x.
  * y: [n_mat][n_tok][rows], dtype y_dtype.  ws: gale_gemv_workspace_bytes(...) bytes,
  * 256-byte aligned.  With GALE_X_PREPARED, x holds the prepared records (same indexing,
- * x_dtype ignored) and ws may be NULL.  fp32 accumulation. */
+ * x_dtype ignored) and ws may be NULL.  fp32 accumulation.
+ * With n_tok == 1 and cols <= 8192 the rotation, the activation split and the GEMV run in one
+ * kernel launch (ws is then left untouched, but its size is still checked); otherwise the
+ * records are prepared in ws first.  Both give the same bits. */
 int gale_expert_gemv(int32_t rows, int32_t cols, const gale_matrix* mats_dev, int32_t n_mat,
                      const void* x, int32_t x_dtype, int32_t x_shared, int32_t n_tok,
                      void* y, int32_t y_dtype, void* ws, size_t ws_bytes, uint32_t flags,

@@ -354,19 +354,28 @@ extern "C" int gale_expert_gemv(int32_t rows, int32_t cols, const gale_matrix* m
     return GALE_ERR_ALIGN;
   }
   const int64_t n_x = (int64_t)(x_shared ? 1 : n_mat) * n_tok;
-  const uint8_t* ra;
-  if (prepared) {
-    ra = reinterpret_cast<const uint8_t*>(x);
-  } else {
+  // one token per matrix, at most eight 1024-column chunks: the GEMV rotates and splits x
+  // itself (one launch, no record in memory)
+  const int slots = pick_slots(n_tok);
+  const int out_chunks = pick_out_chunks(flags, slots, cols, 0, cols);
+  const bool fused = !prepared && n_tok == 1 && cols <= 8192 &&
+                     gemv_smem_bytes(cols, 1, 4, 0, 1, out_chunks, 1) <= kGemvMaxLds;
+  const uint8_t* ra = nullptr;
+  if (!prepared) {
+    // the workspace contract does not depend on which path runs
     const GemvWs W = gemv_ws(cols, n_x);
     if (ws_bytes < W.total) { set_error("%s: workspace %zu < %zu bytes", fn, ws_bytes, W.total); return GALE_ERR_WORKSPACE; }
+  }
+  if (prepared) {
+    ra = reinterpret_cast<const uint8_t*>(x);
+  } else if (!fused) {
+    const GemvWs W = gemv_ws(cols, n_x);
     uint8_t* raw = reinterpret_cast<uint8_t*>(ws) + W.ra;
     st = hip_status(fn, launch_prep(x, x_dtype, cols, (int)n_x, cols, (flags & GALE_X_ROTATED) ? 1 : 0, raw,
                                     ra_bytes(cols), stream));
     if (st) return st;
     ra = raw;
   }
-  const int slots = pick_slots(n_tok);
   GemvParams P;
   memset(&P, 0, sizeof(P));
   P.table = mats_dev;
@@ -387,10 +396,16 @@ extern "C" int gale_expert_gemv(int32_t rows, int32_t cols, const gale_matrix* m
   P.y_stride = rows;
   P.gateup = 0;
   const int ntiles = rows / 16;
-  P.out_chunks = pick_out_chunks(flags, slots, cols, 0, cols);
+  P.out_chunks = out_chunks;
   const int R = pick_tiles(P.n_items, ntiles, cols, slots, P.out_chunks, flags);
   P.row_groups = (ntiles + R - 1) / R;
   P.stage_xt = stage_ok(cols, slots);
+  if (fused) {
+    P.x = x;
+    P.x_dtype = x_dtype;
+    P.x_rotated = (flags & GALE_X_ROTATED) ? 1 : 0;
+    P.x_stride = cols;
+  }
   return hip_status(fn, launch_gemv(P, slots, R, (int64_t)P.n_items * P.row_groups, stream));
 }
 

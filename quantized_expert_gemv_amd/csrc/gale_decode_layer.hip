@@ -286,24 +286,6 @@ __device__ __forceinline__ void stage_record_chunk(const uint8_t* grec, lds_u8* 
   if (lane == 0) reinterpret_cast<__attribute__((address_space(3))) uint32_t*>(lrec + ra_p_off(K))[c] = pw;
 }
 
-// A operands and exponent of chunk c from an activation record in LDS.
-__device__ __forceinline__ void record_activation(const uint8_t* rec, int K, int c, int lane, Act& a) {
-  const int nl = lane & 15, g = lane >> 4;
-  const int term = nl >> 2;
-  const uint8_t* tb = rec + ra_terms_off(K) + ((size_t)c * 4 + term) * 1024 + 32 * g;
-#pragma unroll
-  for (int d = 0; d < 8; ++d) a.A[d] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-  if ((nl & 3) == 0) {
-#pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      const uint4 a0 = *reinterpret_cast<const uint4*>(tb + 128 * d);
-      const uint4 a1 = *reinterpret_cast<const uint4*>(tb + 128 * d + 16);
-      a.A[d] = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-    }
-  }
-  a.pexp[0] = reinterpret_cast<const int32_t*>(rec + ra_p_off(K))[c];
-}
-
 // ---- outliers of one 16-row group (shared by both phases) ----------------------------
 // Loads of a group's CSR entries: the 16-byte chunks holding the uint16 columns and
 // packed int4 values of [e0, e1) (e0 from lane 0's rp0, e1 from lane 60's rp1), and

@@ -46,6 +46,7 @@
 #include "gale_internal.h"
 #include "gale_decode.h"
 #include "gale_gemv_core.h"
+#include "gale_rotate.h"
 
 namespace gale {
 
@@ -248,11 +249,39 @@ __device__ __forceinline__ void stage_activation(const GemvParams& P, const Geo&
   }
 }
 
-template <int NS, int R, bool GATEUP, int OC>
+// Raw activations (FX): wavefront c rotates and splits chunk c of an item's x into the
+// workgroup's LDS record with the same code and layout as a prepared record, so every
+// product equals the one from a record prepared by prep_kernel.  The first item's x comes
+// with plain loads; every later item's x is copied global-to-LDS one unit ahead, with the
+// loads of the unit that starts it, so it costs no registers while in flight.
+__device__ __forceinline__ const char* x_chunk(const GemvParams& P, const Geo& G, int v) {
+  const int64_t isz = P.x_dtype == GALE_F16 ? 2 : 4;
+  return reinterpret_cast<const char*>(P.x) + ((int64_t)v * P.x_stride + (int64_t)G.c * 1024) * isz;
+}
+
+__device__ __forceinline__ void issue_x_copy(const GemvParams& P, const Geo& G, int v, lds_u8* xstage) {
+  const int isz = P.x_dtype == GALE_F16 ? 2 : 4;
+  const char* src = x_chunk(P, G, v) + 16 * G.lane;
+  lds_u8* dst = xstage + G.c * 1024 * isz;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (j < isz) __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) uint8_t*)(src + 1024 * j),
+                                                  dst + 1024 * j, 16, 0, 0);
+}
+
+// Chunk c of the record of x (16 values of this lane, in the coalesced layout of x's dtype).
+__device__ __forceinline__ void prep_x_record(const GemvParams& P, const Geo& G, const float f[16], uint8_t* lrec) {
+  PrepLane o;
+  prep_lane(f, G.lane, !P.x_rotated, o);
+  store_record_chunk(o, P.x_dtype, lrec, G.K, G.c, G.lane);
+}
+
+template <int NS, int R, bool GATEUP, int OC, bool FX>
 __device__ __forceinline__ void process_unit(const GemvParams& P, const Geo& G, const Pos& cur_pos, Item& it,
                                              UnitBuf<R, OC>& cur, UnitBuf<R, OC>& nxt, const Pos& p1, const Desc& d1,
                                              const Pos& p2, const Desc& d2, int& act_item, Act& act,
-                                             lds_f32* red, lds_f32* ored, lds_f32* xt, lds_u8* wout) {
+                                             lds_f32* red, lds_f32* ored, lds_f32* xt, lds_u8* wout,
+                                             uint8_t* lrec, uint8_t* xstage) {
   constexpr int HALVES = GATEUP ? 2 : 1;
   constexpr int RR = R * 16;
   const int item = cur_pos.item;
@@ -262,9 +291,19 @@ __device__ __forceinline__ void process_unit(const GemvParams& P, const Geo& G, 
   //    next unit's loads so that waiting for it never waits for them
   if (item != act_item) {
     it = decode_item<NS>(P, item);
-    load_activation<NS>(P, G, it, act);
-    stage_activation<NS>(P, G, it, xt);
-    __syncthreads();
+    if constexpr (FX) {
+      // this wavefront's copy of the item's x chunk (issued a unit ago) has landed
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+      float f[16];
+      load_block_coalesced(xstage + G.c * 1024 * (P.x_dtype == GALE_F16 ? 2 : 4), P.x_dtype, G.lane, f);
+      prep_x_record(P, G, f, lrec);
+      __syncthreads();
+      record_activation(lrec, G.K, G.c, G.lane, act);
+    } else {
+      load_activation<NS>(P, G, it, act);
+      stage_activation<NS>(P, G, it, xt);
+      __syncthreads();
+    }
     block_sums<NS>(act);
     act_item = item;
   }
@@ -282,6 +321,10 @@ __device__ __forceinline__ void process_unit(const GemvParams& P, const Geo& G, 
   nxt.rp0 = cur.np0;
   nxt.rp1 = cur.np1;
   issue_unit<R, OC>(P, G, p1, d1, p2, d2, nxt);
+  if constexpr (FX) {
+    // the next unit starts another item (at the end of the range p1 is this unit): its x
+    if (p1.item != item) issue_x_copy(P, G, decode_item<NS>(P, p1.item).ra0, (lds_u8*)xstage);
+  }
 
   // 4. sign pass over the wave's R tiles
 #pragma unroll
@@ -431,8 +474,10 @@ __device__ __forceinline__ void process_unit(const GemvParams& P, const Geo& G, 
 // NS: activation vectors per item (1, 2 or 4); R: row tiles per unit (R <= chunks);
 // GATEUP: two matrices (w1, w3) and a SwiGLU epilogue.  blockDim.x = 64 * C * (GATEUP ? 2 : 1)
 // <= MAXT: 512 for up to eight wavefronts, 1024 (half the registers per lane) beyond.
-template <int NS, int R, bool GATEUP, int MAXT, int OC>
+// FX: raw activations (one vector per item, no gate/up pair): the record is built in LDS.
+template <int NS, int R, bool GATEUP, int MAXT, int OC, bool FX>
 __global__ void __launch_bounds__(MAXT) gemv_kernel(const GemvParams P) {
+  static_assert(!FX || (NS == 1 && !GATEUP), "raw activations: one vector per item, one matrix");
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int HALVES = GATEUP ? 2 : 1;
   constexpr int RR = R * 16;
@@ -469,6 +514,10 @@ __global__ void __launch_bounds__(MAXT) gemv_kernel(const GemvParams P) {
   lds_u8* wbase = reinterpret_cast<lds_u8*>(ored0 + 2 * ored_n);
   lds_u8* wout = wbase + G.wave * wave_out_bytes(OC);          // this wave's outlier staging slice
   lds_f32* xt = reinterpret_cast<lds_f32*>(wbase + (size_t)HALVES * G.C * wave_out_bytes(OC));   // [NS][K] when staged
+  // FX: the item's whole record from xt on (x~ is its first part), then the x copies
+  const size_t lrec_off = (size_t)4 * (red_n * 2 + ored_n * 2) + (size_t)HALVES * G.C * wave_out_bytes(OC);
+  uint8_t* lrec = smem + lrec_off;
+  uint8_t* xstage = smem + lrec_off + ra_bytes(G.K);
 
   const int n_items = P.implicit_items ? P.n_items : uni(*as_const(P.n_items_dev));
   const int total = n_items * G.RG;
@@ -490,7 +539,9 @@ __global__ void __launch_bounds__(MAXT) gemv_kernel(const GemvParams P) {
     pc.item = uni(u0 / G.RG);
     pc.rg = uni(u0 - pc.item * G.RG);
     it = decode_item<NS>(P, pc.item);
-    load_activation<NS>(P, G, it, act);
+    float xf[16];
+    if constexpr (FX) load_block_coalesced(x_chunk(P, G, it.ra0), P.x_dtype, G.lane, xf);
+    else load_activation<NS>(P, G, it, act);
     const Desc d0 = load_desc(P, G, uni(it.mat));
     p1 = pos_next(pc, u1, G.RG);
     d1 = p1.item == pc.item ? d0 : load_desc(P, G, item_mat(P, p1.item));
@@ -499,23 +550,30 @@ __global__ void __launch_bounds__(MAXT) gemv_kernel(const GemvParams P) {
     b0.rp0 = d0.rptr[n];
     b0.rp1 = d0.rptr[n + (n < P.rows ? 1 : 0)];
     issue_unit<R, OC>(P, G, pc, d0, p1, d1, b0);
-    stage_activation<NS>(P, G, it, xt);
-    __syncthreads();
+    if constexpr (FX) {
+      prep_x_record(P, G, xf, lrec);
+      __syncthreads();
+      record_activation(lrec, G.K, G.c, G.lane, act);
+    } else {
+      stage_activation<NS>(P, G, it, xt);
+      __syncthreads();
+    }
     block_sums<NS>(act);
     act_item = pc.item;
     p2 = pos_next(p1, u1, G.RG);
     d2 = p2.item == p1.item ? d1 : load_desc(P, G, item_mat(P, p2.item));
   }
   for (;;) {
-    process_unit<NS, R, GATEUP, OC>(P, G, pc, it, b0, b1, p1, d1, p2, d2, act_item, act, red0, ored0, xt, wout);
+    process_unit<NS, R, GATEUP, OC, FX>(P, G, pc, it, b0, b1, p1, d1, p2, d2, act_item, act, red0, ored0, xt, wout,
+                                        lrec, xstage);
     if (pc.u + 1 >= u1) break;
     pc = p1;
     p1 = p2;
     d1 = d2;
     p2 = pos_next(p2, u1, G.RG);
     d2 = p2.item == p1.item ? d1 : load_desc(P, G, item_mat(P, p2.item));
-    process_unit<NS, R, GATEUP, OC>(P, G, pc, it, b1, b0, p1, d1, p2, d2, act_item, act, red0 + red_n,
-                                ored0 + ored_n, xt, wout);
+    process_unit<NS, R, GATEUP, OC, FX>(P, G, pc, it, b1, b0, p1, d1, p2, d2, act_item, act, red0 + red_n,
+                                        ored0 + ored_n, xt, wout, lrec, xstage);
     if (pc.u + 1 >= u1) break;
     pc = p1;
     p1 = p2;
@@ -525,11 +583,12 @@ __global__ void __launch_bounds__(MAXT) gemv_kernel(const GemvParams P) {
   }
 }
 
-size_t gemv_smem_bytes(int cols, int slots, int tiles, int gateup, int stage_xt, int out_chunks) {
+size_t gemv_smem_bytes(int cols, int slots, int tiles, int gateup, int stage_xt, int out_chunks, int fused) {
   const int halves = gateup ? 2 : 1;
   const int C = cols >> 10;
   const size_t f = 2 * ((size_t)halves * C * tiles * 16 * slots + (size_t)halves * tiles * 16 * slots);
   size_t b = f * 4 + (size_t)halves * C * (size_t)(64 * 16 * (out_chunks + out_chunks / 4 + 1));
+  if (fused) return b + ra_bytes(cols) + (size_t)cols * 4;   // the record, then x copies of either dtype
   if (stage_xt) b += (size_t)slots * cols * 4;
   return b;
 }
@@ -546,25 +605,47 @@ int device_cu_count() {
   return cached[dev];
 }
 
-template <int NS, int R, bool G, int MAXT, int OC>
+template <int NS, int R, bool G, int MAXT, int OC, bool FX>
 static hipError_t launch_b(const GemvParams& p, int block, int64_t max_units, hipStream_t s) {
-  const size_t smem = gemv_smem_bytes(p.cols, NS, R, G, p.stage_xt, OC);
+  const size_t smem = gemv_smem_bytes(p.cols, NS, R, G, p.stage_xt, OC, FX ? 1 : 0);
   int occ = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemv_kernel<NS, R, G, MAXT, OC>, block, smem) != hipSuccess ||
-      occ < 1)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemv_kernel<NS, R, G, MAXT, OC, FX>, block, smem) !=
+          hipSuccess || occ < 1)
     occ = 1;
   const int64_t grid = std::min<int64_t>(max_units, (int64_t)device_cu_count() * occ);
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemv_kernel<NS, R, G, MAXT, OC>), dim3((unsigned)grid), dim3(block), smem, s, p);
+  hipLaunchKernelGGL((gemv_kernel<NS, R, G, MAXT, OC, FX>), dim3((unsigned)grid), dim3(block), smem, s, p);
   return hipGetLastError();
 }
 
-template <int NS, int R, bool G, int OC>
+template <int NS, int R, bool G, int OC, bool FX = false>
 static hipError_t launch_t(const GemvParams& p, int64_t max_units, hipStream_t s) {
   const int block = 64 * (p.cols >> 10) * (G ? 2 : 1);
   if (block > kGemvMaxThreads) return hipErrorInvalidConfiguration;   // the host checks first
-  if (block <= 512) return launch_b<NS, R, G, 512, OC>(p, block, max_units, s);
-  return launch_b<NS, R, G, 1024, OC>(p, block, max_units, s);
+  if constexpr (FX) {
+    if (block > 512) return hipErrorInvalidConfiguration;           // the host checks first
+    return launch_b<NS, R, G, 512, OC, true>(p, block, max_units, s);
+  } else {
+    if (block <= 512) return launch_b<NS, R, G, 512, OC, false>(p, block, max_units, s);
+    return launch_b<NS, R, G, 1024, OC, false>(p, block, max_units, s);
+  }
+}
+
+// Raw activations, one vector per item: the staging and tile counts the host picks for one
+// vector (two chunks: up to four tiles, four: up to three, eight: up to two).
+template <int OC>
+static hipError_t launch_fx(const GemvParams& p, int tiles, int64_t max_units, hipStream_t s) {
+  switch (tiles) {
+    case 1: return launch_t<1, 1, false, OC, true>(p, max_units, s);
+    case 2: return launch_t<1, 2, false, OC, true>(p, max_units, s);
+    case 3:
+      if constexpr (OC <= 4) return launch_t<1, 3, false, OC, true>(p, max_units, s);
+      else return hipErrorInvalidValue;
+    case 4:
+      if constexpr (OC <= 2) return launch_t<1, 4, false, OC, true>(p, max_units, s);
+      else return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
 }
 
 // Row tiles per unit by outlier staging.  One chunk (the down phase of a layer whose
@@ -616,6 +697,13 @@ static hipError_t launch_o(const GemvParams& p, int slots, int tiles, int64_t ma
 
 hipError_t launch_gemv(const GemvParams& p, int slots, int tiles_per_unit, int64_t max_units, hipStream_t s) {
   if (max_units <= 0) return hipSuccess;
+  if (p.x) {
+    if (slots != 1 || p.gateup) return hipErrorInvalidValue;   // the host checks first
+    if (p.out_chunks == 8) return launch_fx<8>(p, tiles_per_unit, max_units, s);
+    if (p.out_chunks == 4) return launch_fx<4>(p, tiles_per_unit, max_units, s);
+    if (p.out_chunks == 2) return launch_fx<2>(p, tiles_per_unit, max_units, s);
+    return hipErrorInvalidValue;
+  }
   if (p.gateup) return launch_o<true>(p, slots, tiles_per_unit, max_units, s);
   return launch_o<false>(p, slots, tiles_per_unit, max_units, s);
 }

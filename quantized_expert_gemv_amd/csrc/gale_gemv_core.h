@@ -100,6 +100,24 @@ struct Act {
   int pexp[4];
 };
 
+// A operands and exponent of chunk c from an activation record in LDS.
+__device__ __forceinline__ void record_activation(const uint8_t* rec, int K, int c, int lane, Act& a) {
+  const int nl = lane & 15, g = lane >> 4;
+  const int term = nl >> 2;
+  const uint8_t* tb = rec + ra_terms_off(K) + ((size_t)c * 4 + term) * 1024 + 32 * g;
+#pragma unroll
+  for (int d = 0; d < 8; ++d) a.A[d] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+  if ((nl & 3) == 0) {
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const uint4 a0 = *reinterpret_cast<const uint4*>(tb + 128 * d);
+      const uint4 a1 = *reinterpret_cast<const uint4*>(tb + 128 * d + 16);
+      a.A[d] = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+    }
+  }
+  a.pexp[0] = reinterpret_cast<const int32_t*>(rec + ra_p_off(K))[c];
+}
+
 // -S per 0/1 block and slot: the MFMA against an all -1.0 operand sums each term row.
 template <int NS>
 __device__ __forceinline__ void block_sums(Act& a) {

@@ -248,6 +248,41 @@ def test_gemv_many_matrices_sampled(q):
     assert torch.count_nonzero(z) == 0
 
 
+@pytest.mark.parametrize("rows,cols,n_mat,xdt,rotated,shared,flags", [
+    (2048, 4096, 40, torch.float16, False, False, 0),           # the single-matrix workload shape
+    (80, 2048, 200, torch.float32, False, False, "t1"),         # ragged, many items per workgroup
+    (80, 2048, 200, torch.float16, False, False, "t2"),
+    (80, 2048, 97, torch.float16, False, False, "t4"),
+    (64, 7168, 30, torch.float32, True, False, 0),              # 7 chunks, pre-rotated fp32 input
+    (2048, 4096, 12, torch.float16, False, True, 0),            # one x shared by every matrix
+    (2048, 4096, 24, torch.float16, False, False, "s1"),        # 2,048-entry outlier staging
+    (2048, 4096, 24, torch.float16, False, False, "s2"),        # 4,096-entry outlier staging
+])
+def test_gemv_one_launch_equals_prepared(q, rows, cols, n_mat, xdt, rotated, shared, flags):
+    """One token per matrix: the GEMV rotates and splits x itself, in one launch, with the same
+    record code as the preparation kernel, so its output equals prepare + GEMV bit for bit
+    (row tiles per unit, outlier stagings, dtypes, shared x, items crossing workgroups)."""
+    f = {0: 0, "t1": q.gale_tiles_flag(1), "t2": q.gale_tiles_flag(2), "t4": q.gale_tiles_flag(4),
+         "s1": q.gale_outlier_stage_flag(100), "s2": q.gale_outlier_stage_flag(200)}[flags]
+    if rotated:
+        f |= q.GALE_X_ROTATED
+    mats = gen_matrices(config_seed(21), [(rows, cols, i) for i in range(n_mat)], rows, cols, device=DEV)
+    tab = q.matrix_table([q.pack_matrix(m) for m in mats])
+    n_x = 1 if shared else n_mat
+    x = torch.stack([gen_x(config_seed(21), (rows, cols, 500 + i), 1, cols, device=DEV) for i in range(n_x)]).to(xdt)
+    xin = x[0] if shared else x
+    print(f"one-launch GEMV [{rows},{cols}] x{n_mat} {xdt} rotated={rotated} shared={shared} flags={flags}", flush=True)
+    y1 = q.expert_gemv(tab, rows, cols, xin, x_shared=shared, y_dtype=torch.float32, flags=f)
+    rec = q.prepare_activations(x.reshape(-1, cols), rotated=rotated)
+    y2 = q.expert_gemv(tab, rows, cols, rec, x_shared=shared, y_dtype=torch.float32,
+                       flags=(f & ~q.GALE_X_ROTATED) | q.GALE_X_PREPARED)
+    assert torch.equal(y1, y2)
+    i = n_mat - 1
+    xi = (x[0] if shared else x[i]).float().cpu().numpy()
+    ref = O.gemv(mats[i].numpy(), xi, pre_rotated=rotated)
+    assert O.rel_l2(np_of(y1[i]), ref).max() <= CLOSED_TOL
+
+
 # ----------------------------------------------------------------------------
 # FFN
 # ----------------------------------------------------------------------------
