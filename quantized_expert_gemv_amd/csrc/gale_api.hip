@@ -98,6 +98,17 @@ static int pick_tiles(int64_t items, int ntiles, int cols, int slots, int out_ch
 
 static int pick_slots(int n_tok) { return n_tok >= 4 ? 4 : (n_tok >= 2 ? 2 : 1); }
 
+// Whether a phase of one vector per item can take raw activations (the GEMV rotates and
+// splits x itself): at most eight chunks per matrix (sixteen wavefronts for a gate/up pair
+// do not fit), a staging the raw-activation builds cover, and the LDS of the larger layout.
+static bool raw_x_ok(int cols, int gateup, uint32_t flags, int ref_cols) {
+  const int C = cols >> 10;
+  if (C > (gateup ? 4 : 8)) return false;
+  const int oc = pick_out_chunks(flags, 1, cols, gateup, ref_cols);
+  if (gateup ? (oc != 2 && oc != 4) : (oc != 1 && oc != 2 && oc != 4 && oc != 8)) return false;
+  return gemv_smem_bytes(cols, 1, 4, gateup, 1, oc, 1) <= kGemvMaxLds;
+}
+
 // Activation vectors per GEMV work item of the MoE layer.  Decode batches spread their pairs
 // thinly (T k / E pairs per expert on average): items of one or two vectors then run the
 // wider row-tile units of the single-vector builds and waste no MFMA rows on empty slots
@@ -358,8 +369,7 @@ extern "C" int gale_expert_gemv(int32_t rows, int32_t cols, const gale_matrix* m
   // itself (one launch, no record in memory)
   const int slots = pick_slots(n_tok);
   const int out_chunks = pick_out_chunks(flags, slots, cols, 0, cols);
-  const bool fused = !prepared && n_tok == 1 && cols <= 8192 &&
-                     gemv_smem_bytes(cols, 1, 4, 0, 1, out_chunks, 1) <= kGemvMaxLds;
+  const bool fused = !prepared && n_tok == 1 && raw_x_ok(cols, 0, flags, cols);
   const uint8_t* ra = nullptr;
   if (!prepared) {
     // the workspace contract does not depend on which path runs
@@ -422,7 +432,7 @@ static int run_gemv_phase(const char* fn, const gale_matrix* table, int stride, 
                           int rows, int cols, const uint8_t* ra, int implicit, int n_tok, int x_shared,
                           int n_items, const WorkItem* items, const int32_t* n_items_dev, int ra_div,
                           int item_bound, void* y, int y_dtype, int gateup, int slots, uint32_t flags,
-                          hipStream_t s, int ref_cols) {
+                          hipStream_t s, int ref_cols, const void* raw_x = nullptr, int raw_dtype = 0) {
   GemvParams P;
   memset(&P, 0, sizeof(P));
   P.table = table;
@@ -451,8 +461,14 @@ static int run_gemv_phase(const char* fn, const gale_matrix* table, int stride, 
   const int R = pick_tiles(bound, ntiles, cols, slots, P.out_chunks, flags);
   P.row_groups = (ntiles + R - 1) / R;
   P.stage_xt = stage_ok(cols, slots);
+  if (raw_x) {
+    P.x = raw_x;
+    P.x_dtype = raw_dtype;
+    P.x_stride = cols;
+  }
   return hip_status(fn, launch_gemv(P, slots, R, bound * P.row_groups, s));
 }
+
 
 extern "C" int gale_expert_ffn(int32_t hidden, int32_t inter, const gale_expert* experts_dev, int32_t n_exp,
                                const void* x, int32_t x_shared, int32_t n_tok, void* y, void* ws,
@@ -479,16 +495,24 @@ extern "C" int gale_expert_ffn(int32_t hidden, int32_t inter, const gale_expert*
   uint8_t* ra_h = base + W.ra_h;
   const gale_matrix* table = reinterpret_cast<const gale_matrix*>(experts_dev);
   const int slots = pick_slots(n_tok);
-  st = hip_status(fn, launch_prep(x, GALE_F16, hidden, (int)n_x, hidden, 0, ra_x, ra_bytes(hidden), stream));
-  if (st) return st;
+  // one token per expert: each GEMV phase rotates and splits its input itself (same bits)
+  const bool raw_up = n_tok == 1 && raw_x_ok(hidden, 1, 0, hidden);
+  const bool raw_down = n_tok == 1 && raw_x_ok(inter, 0, 0, hidden);
+  if (!raw_up) {
+    st = hip_status(fn, launch_prep(x, GALE_F16, hidden, (int)n_x, hidden, 0, ra_x, ra_bytes(hidden), stream));
+    if (st) return st;
+  }
   const int n_groups = (n_tok + slots - 1) / slots;
   st = run_gemv_phase(fn, table, 3, 0, 1, inter, hidden, ra_x, 1, n_tok, x_shared ? 1 : 0, n_exp * n_groups,
-                      nullptr, nullptr, 1, 0, h, GALE_F32, 1, slots, 0, stream, hidden);
+                      nullptr, nullptr, 1, 0, h, GALE_F32, 1, slots, 0, stream, hidden, raw_up ? x : nullptr,
+                      GALE_F16);
   if (st) return st;
-  st = hip_status(fn, launch_prep(h, GALE_F32, inter, (int)n_p, inter, 0, ra_h, ra_bytes(inter), stream));
-  if (st) return st;
+  if (!raw_down) {
+    st = hip_status(fn, launch_prep(h, GALE_F32, inter, (int)n_p, inter, 0, ra_h, ra_bytes(inter), stream));
+    if (st) return st;
+  }
   return run_gemv_phase(fn, table, 3, 2, 2, hidden, inter, ra_h, 1, n_tok, 0, n_exp * n_groups, nullptr,
-                        nullptr, 1, 0, y, GALE_F16, 0, slots, 0, stream, hidden);
+                        nullptr, 1, 0, y, GALE_F16, 0, slots, 0, stream, hidden, raw_down ? h : nullptr, GALE_F32);
 }
 
 // ============================================================================

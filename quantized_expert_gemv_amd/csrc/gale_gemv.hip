@@ -292,11 +292,14 @@ __device__ __forceinline__ void process_unit(const GemvParams& P, const Geo& G, 
   if (item != act_item) {
     it = decode_item<NS>(P, item);
     if constexpr (FX) {
-      // this wavefront's copy of the item's x chunk (issued a unit ago) has landed
-      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-      float f[16];
-      load_block_coalesced(xstage + G.c * 1024 * (P.x_dtype == GALE_F16 ? 2 : 4), P.x_dtype, G.lane, f);
-      prep_x_record(P, G, f, lrec);
+      // the w1 (or only) wavefront of chunk c builds the chunk's record; its copy of the
+      // item's x chunk (issued a unit ago) has landed
+      if (G.half == 0) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+        float f[16];
+        load_block_coalesced(xstage + G.c * 1024 * (P.x_dtype == GALE_F16 ? 2 : 4), P.x_dtype, G.lane, f);
+        prep_x_record(P, G, f, lrec);
+      }
       __syncthreads();
       record_activation(lrec, G.K, G.c, G.lane, act);
     } else {
@@ -323,7 +326,7 @@ __device__ __forceinline__ void process_unit(const GemvParams& P, const Geo& G, 
   issue_unit<R, OC>(P, G, p1, d1, p2, d2, nxt);
   if constexpr (FX) {
     // the next unit starts another item (at the end of the range p1 is this unit): its x
-    if (p1.item != item) issue_x_copy(P, G, decode_item<NS>(P, p1.item).ra0, (lds_u8*)xstage);
+    if (p1.item != item && G.half == 0) issue_x_copy(P, G, decode_item<NS>(P, p1.item).ra0, (lds_u8*)xstage);
   }
 
   // 4. sign pass over the wave's R tiles
@@ -474,10 +477,11 @@ __device__ __forceinline__ void process_unit(const GemvParams& P, const Geo& G, 
 // NS: activation vectors per item (1, 2 or 4); R: row tiles per unit (R <= chunks);
 // GATEUP: two matrices (w1, w3) and a SwiGLU epilogue.  blockDim.x = 64 * C * (GATEUP ? 2 : 1)
 // <= MAXT: 512 for up to eight wavefronts, 1024 (half the registers per lane) beyond.
-// FX: raw activations (one vector per item, no gate/up pair): the record is built in LDS.
+// FX: raw activations (one vector per item): the record is built in LDS (by the w1 half's
+// wavefronts when the item is a gate/up pair; both halves read it).
 template <int NS, int R, bool GATEUP, int MAXT, int OC, bool FX>
 __global__ void __launch_bounds__(MAXT) gemv_kernel(const GemvParams P) {
-  static_assert(!FX || (NS == 1 && !GATEUP), "raw activations: one vector per item, one matrix");
+  static_assert(!FX || NS == 1, "raw activations: one vector per item");
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int HALVES = GATEUP ? 2 : 1;
   constexpr int RR = R * 16;
@@ -540,8 +544,11 @@ __global__ void __launch_bounds__(MAXT) gemv_kernel(const GemvParams P) {
     pc.rg = uni(u0 - pc.item * G.RG);
     it = decode_item<NS>(P, pc.item);
     float xf[16];
-    if constexpr (FX) load_block_coalesced(x_chunk(P, G, it.ra0), P.x_dtype, G.lane, xf);
-    else load_activation<NS>(P, G, it, act);
+    if constexpr (FX) {
+      if (G.half == 0) load_block_coalesced(x_chunk(P, G, it.ra0), P.x_dtype, G.lane, xf);
+    } else {
+      load_activation<NS>(P, G, it, act);
+    }
     const Desc d0 = load_desc(P, G, uni(it.mat));
     p1 = pos_next(pc, u1, G.RG);
     d1 = p1.item == pc.item ? d0 : load_desc(P, G, item_mat(P, p1.item));
@@ -551,7 +558,7 @@ __global__ void __launch_bounds__(MAXT) gemv_kernel(const GemvParams P) {
     b0.rp1 = d0.rptr[n + (n < P.rows ? 1 : 0)];
     issue_unit<R, OC>(P, G, pc, d0, p1, d1, b0);
     if constexpr (FX) {
-      prep_x_record(P, G, xf, lrec);
+      if (G.half == 0) prep_x_record(P, G, xf, lrec);
       __syncthreads();
       record_activation(lrec, G.K, G.c, G.lane, act);
     } else {
@@ -633,16 +640,16 @@ static hipError_t launch_t(const GemvParams& p, int64_t max_units, hipStream_t s
 
 // Raw activations, one vector per item: the staging and tile counts the host picks for one
 // vector (two chunks: up to four tiles, four: up to three, eight: up to two).
-template <int OC>
+template <bool G, int OC>
 static hipError_t launch_fx(const GemvParams& p, int tiles, int64_t max_units, hipStream_t s) {
   switch (tiles) {
-    case 1: return launch_t<1, 1, false, OC, true>(p, max_units, s);
-    case 2: return launch_t<1, 2, false, OC, true>(p, max_units, s);
+    case 1: return launch_t<1, 1, G, OC, true>(p, max_units, s);
+    case 2: return launch_t<1, 2, G, OC, true>(p, max_units, s);
     case 3:
-      if constexpr (OC <= 4) return launch_t<1, 3, false, OC, true>(p, max_units, s);
+      if constexpr (OC <= 4) return launch_t<1, 3, G, OC, true>(p, max_units, s);
       else return hipErrorInvalidValue;
     case 4:
-      if constexpr (OC <= 2) return launch_t<1, 4, false, OC, true>(p, max_units, s);
+      if constexpr (OC == 2) return launch_t<1, 4, G, OC, true>(p, max_units, s);
       else return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
@@ -698,10 +705,16 @@ static hipError_t launch_o(const GemvParams& p, int slots, int tiles, int64_t ma
 hipError_t launch_gemv(const GemvParams& p, int slots, int tiles_per_unit, int64_t max_units, hipStream_t s) {
   if (max_units <= 0) return hipSuccess;
   if (p.x) {
-    if (slots != 1 || p.gateup) return hipErrorInvalidValue;   // the host checks first
-    if (p.out_chunks == 8) return launch_fx<8>(p, tiles_per_unit, max_units, s);
-    if (p.out_chunks == 4) return launch_fx<4>(p, tiles_per_unit, max_units, s);
-    if (p.out_chunks == 2) return launch_fx<2>(p, tiles_per_unit, max_units, s);
+    if (slots != 1) return hipErrorInvalidValue;   // the host checks first
+    if (p.gateup) {
+      if (p.out_chunks == 4) return launch_fx<true, 4>(p, tiles_per_unit, max_units, s);
+      if (p.out_chunks == 2) return launch_fx<true, 2>(p, tiles_per_unit, max_units, s);
+      return hipErrorInvalidValue;
+    }
+    if (p.out_chunks == 8) return launch_fx<false, 8>(p, tiles_per_unit, max_units, s);
+    if (p.out_chunks == 4) return launch_fx<false, 4>(p, tiles_per_unit, max_units, s);
+    if (p.out_chunks == 2) return launch_fx<false, 2>(p, tiles_per_unit, max_units, s);
+    if (p.out_chunks == 1) return launch_fx<false, 1>(p, tiles_per_unit, max_units, s);
     return hipErrorInvalidValue;
   }
   if (p.gateup) return launch_o<true>(p, slots, tiles_per_unit, max_units, s);

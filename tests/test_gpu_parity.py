@@ -302,6 +302,32 @@ def test_ffn_one_expert_config(q):
     assert e <= REL_L2_BAR
 
 
+@pytest.mark.parametrize("shared", [False, True])
+def test_ffn_one_token_equals_batched_token(q, shared):
+    """One token per expert: both GEMV phases rotate and split their inputs themselves (one
+    launch each); the same token inside a two-token batch goes through prepared records.
+    Each token's products are independent of the other's, so the outputs agree bit for bit;
+    and the one-token outputs match the oracle."""
+    seed = config_seed(22)
+    E = 12
+    ex = [_expert(q, seed, e) for e in range(E)]
+    tab = q.expert_table([p for _, p in ex])
+    if shared:
+        x1 = gen_x(seed, (9,), 1, 4096, device=DEV)
+        x2 = torch.cat([x1, gen_x(seed, (10,), 1, 4096, device=DEV)])
+    else:
+        x1 = torch.stack([gen_x(seed, (100 + e,), 1, 4096, device=DEV) for e in range(E)])
+        x2 = torch.cat([x1, torch.stack([gen_x(seed, (200 + e,), 1, 4096, device=DEV) for e in range(E)])], dim=1)
+    y1 = q.expert_ffn(tab, 4096, 2048, x1, x_shared=shared)
+    y2 = q.expert_ffn(tab, 4096, 2048, x2, x_shared=shared)
+    assert torch.equal(y1[:, 0], y2[:, 0])
+    for e in (0, E - 1):
+        (w1, w3, w2), _ = ex[e]
+        xe = (x1 if shared else x1[e]).cpu().numpy()
+        ref = O.ffn(w1.numpy(), w3.numpy(), w2.numpy(), xe)
+        assert O.rel_l2(np_of(y1[e]), ref).max() <= REL_L2_BAR
+
+
 def test_ffn_tokens_and_experts(q):
     seed = config_seed(12)
     ex = [_expert(q, seed, e) for e in range(2)]
