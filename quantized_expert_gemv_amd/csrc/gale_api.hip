@@ -100,13 +100,21 @@ static int pick_slots(int n_tok) { return n_tok >= 4 ? 4 : (n_tok >= 2 ? 2 : 1);
 
 // Whether a phase of one vector per item can take raw activations (the GEMV rotates and
 // splits x itself): at most eight chunks per matrix (sixteen wavefronts for a gate/up pair
-// do not fit), a staging the raw-activation builds cover, and the LDS of the larger layout.
+// do not fit), a staging the raw-activation builds cover, and an LDS layout (record and x
+// copies on top of the staging) that keeps as many workgroups per CU as the prepared path:
+// the kernels hold two wavefronts per SIMD (more than 128 registers), eight per CU.
 static bool raw_x_ok(int cols, int gateup, uint32_t flags, int ref_cols) {
   const int C = cols >> 10;
   if (C > (gateup ? 4 : 8)) return false;
   const int oc = pick_out_chunks(flags, 1, cols, gateup, ref_cols);
   if (gateup ? (oc != 2 && oc != 4) : (oc != 1 && oc != 2 && oc != 4 && oc != 8)) return false;
-  return gemv_smem_bytes(cols, 1, 4, gateup, 1, oc, 1) <= kGemvMaxLds;
+  const size_t raw = gemv_smem_bytes(cols, 1, 4, gateup, 1, oc, 1);
+  const size_t prep = gemv_smem_bytes(cols, 1, 4, gateup, 1, oc, 0);
+  if (raw > kGemvMaxLds) return false;
+  const int by_regs = std::max(1, 8 / ((gateup ? 2 : 1) * C));
+  const int occ_raw = std::min(by_regs, (int)(kGemvMaxLds / raw));
+  const int occ_prep = std::min(by_regs, (int)(kGemvMaxLds / prep));
+  return occ_raw >= occ_prep;
 }
 
 // Activation vectors per GEMV work item of the MoE layer.  Decode batches spread their pairs
