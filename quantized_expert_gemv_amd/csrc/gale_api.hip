@@ -620,9 +620,12 @@ static int moe_layer(const char* fn, int32_t hidden, int32_t inter, const gale_e
                                               reinterpret_cast<uint64_t*>(base + W.sync), forced,
                                               decode_wait_ticks(flags), stream));
   }
+  // decode items of one vector: each GEMV phase rotates and splits its input itself (same bits)
+  const bool raw_up = path == kDecode && slots == 1 && raw_x_ok(hidden, 1, flags, hidden);
+  const bool raw_down = path == kDecode && slots == 1 && raw_x_ok(inter, 0, flags, hidden);
   if (path == kDecode) {
     st = hip_status(fn, launch_route_prep(rin, n_tok, n_experts, top_k, idx, wts, items, n_items, slots, x,
-                                          GALE_F16, hidden, ra_x, ra_bytes(hidden), stream));
+                                          GALE_F16, hidden, raw_up ? nullptr : ra_x, ra_bytes(hidden), stream));
     if (st) return st;
   } else {
     if (use_items) {
@@ -642,7 +645,7 @@ static int moe_layer(const char* fn, int32_t hidden, int32_t inter, const gale_e
   // gate/up + SwiGLU: h[pair]
   if (use_items) {
     st = run_gemv_phase(fn, table, 3, 0, 1, inter, hidden, ra_x, 0, 0, 0, 0, items, n_items, top_k, bound, h,
-                        GALE_F32, 1, slots, flags, stream, hidden);
+                        GALE_F32, 1, slots, flags, stream, hidden, raw_up ? x : nullptr, GALE_F16);
     if (st) return st;
   }
   if (use_gemm) {
@@ -652,10 +655,12 @@ static int moe_layer(const char* fn, int32_t hidden, int32_t inter, const gale_e
   }
   // rotate h; down: yp[pair]
   if (use_items) {
-    st = hip_status(fn, launch_prep(h, GALE_F32, inter, P, inter, 0, ra_h, ra_bytes(inter), stream, pair_items));
-    if (st) return st;
+    if (!raw_down) {
+      st = hip_status(fn, launch_prep(h, GALE_F32, inter, P, inter, 0, ra_h, ra_bytes(inter), stream, pair_items));
+      if (st) return st;
+    }
     st = run_gemv_phase(fn, table, 3, 2, 2, hidden, inter, ra_h, 0, 0, 0, 0, items, n_items, 1, bound, yp,
-                        GALE_F32, 0, slots, flags, stream, hidden);
+                        GALE_F32, 0, slots, flags, stream, hidden, raw_down ? h : nullptr, GALE_F32);
     if (st) return st;
   }
   if (use_gemm) {

@@ -157,7 +157,8 @@ __global__ void __launch_bounds__(512) route_prep_kernel(const RouteIn rin, int 
 hipError_t launch_route_prep(const RouteIn& rin, int n_tok, int n_exp, int k, int32_t* idx, float* w,
                              WorkItem* items, int32_t* n_items, int max_slots, const void* x, int x_dtype, int K,
                              uint8_t* ra, size_t ra_stride, hipStream_t s) {
-  const int64_t waves = (int64_t)n_tok * (K / 1024);
+  // ra == nullptr: routing only (the GEMV rotates and splits x itself)
+  const int64_t waves = ra ? (int64_t)n_tok * (K / 1024) : 0;
   const int64_t grid = 1 + (waves + 7) / 8;
   hipLaunchKernelGGL(route_prep_kernel, dim3((unsigned)grid), dim3(512), 0, s, rin, n_tok, n_exp, k, max_slots,
                      idx, w, items, n_items, x, x_dtype, K, ra, ra_stride);
