@@ -325,8 +325,10 @@ size_t gale_decode_stack_workspace_bytes(int32_t hidden, int32_t inter, int32_t 
  * (DeepSeek-V4-Flash GALE model card, "Measured performance": 43 layers x 6 routed experts
  * per token; the DeepSeek-V4-Pro GALE page's batch-1 notes put the floor in launches).
  * Layer l computes exactly gale_moe_layer_fwd of one token on layers_dev[l] (same results
- * bit for bit), and reads its logits and x only after every row of layer l-1's y has been
- * stored, as separate launches in stream order would: x of layer l may be y of layer l-1.
+ * bit for bit), and reads its x only after every row of layer l-1's y has been stored, as
+ * separate launches in stream order would: x of layer l may be y of layer l-1.  Logits,
+ * selection biases and fixed experts are inputs of the call: layer l's logits may be read
+ * while layer l-1 runs, so they must not alias any layer's y.
  * layers_dev: device array of n_layers gale_layer_io (read by the kernel); at most one of
  * select_bias / fixed_idx per layer.  hidden and inter as the one-launch layer takes them
  * (gale_moe_layer_fwd); n_experts <= GALE_MAX_EXPERTS, top_k <= GALE_MAX_TOPK.

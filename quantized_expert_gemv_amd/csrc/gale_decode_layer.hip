@@ -657,6 +657,7 @@ __global__ void __launch_bounds__(512) decode_stack_kernel(const StackParams P) 
   const int gu00 = (int)((int64_t)P.gu_units * b / nb), gu10 = (int)((int64_t)P.gu_units * (b + 1) / nb);
   const int dt00 = (int)((int64_t)P.down_tiles * b / nb), dt10 = (int)((int64_t)P.down_tiles * (b + 1) / nb);
   const int half0 = uni(wave / C_H0), cq0 = uni(wave - half0 * C_H0);
+  float lgv[4];   // the routing wave's logits of the next layer (plain routing), loaded a layer ahead
 
   for (int l = 0; l < P.L; ++l) {
     // The values the layer derives its addresses from, made opaque once per layer: the
@@ -680,7 +681,10 @@ __global__ void __launch_bounds__(512) decode_stack_kernel(const StackParams P) 
     } else if (wave == C_H) {
       // the routing is the longer of the two and shares its SIMD with wave 0: it issues first
       __builtin_amdgcn_s_setprio(3);
-      topk_wave(RouteIn{io.logits, io.select_bias, io.fixed_idx}, 0, P.E, Pk, lane, s_exp, s_w, s_exp);
+      if (l > 0 && io.select_bias == nullptr && io.fixed_idx == nullptr && P.E <= 256)
+        topk_wave_vals(lgv, P.E, Pk, lane, s_exp, s_w, s_exp);
+      else
+        topk_wave(RouteIn{io.logits, io.select_bias, io.fixed_idx}, 0, P.E, Pk, lane, s_exp, s_w, s_exp);
       __builtin_amdgcn_s_setprio(0);
     }
     if (wave == W - 1 && l == 0) warm_table(table, P.E, lane, s_hdr + 3);
@@ -927,6 +931,12 @@ __global__ void __launch_bounds__(512) decode_stack_kernel(const StackParams P) 
     if (l + 1 < P.L) {
       ++phase;
       if (wave == 0) arrive(P, set, lane);
+      if (wave == C_H) {
+        // the next layer's logits are inputs no layer of the call writes: load them now
+        const float* lg = layer_io(P, l + 1).logits;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) lgv[j] = lane + 64 * j < P.E ? lg[lane + 64 * j] : 0.f;
+      }
     }
   }
   // workgroup 0 records this call's generation for the next call, once every workgroup has

@@ -255,6 +255,19 @@ __device__ __forceinline__ void topk_wave(const RouteIn& in, int t, int E, int k
   topk_softmax_store(m, my_v, my_i, k, lane, out_idx, out_w, lds_idx);
 }
 
+// Plain top-k of one token from its logits already in registers (v[j]: expert lane + 64 j,
+// E <= 256): the same keys and selection as topk_wave.
+__device__ __forceinline__ void topk_wave_vals(const float v[4], int E, int k, int lane, int32_t* out_idx,
+                                               float* out_w, int32_t* lds_idx) {
+  uint32_t key[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) key[j] = lane + 64 * j < E ? logit_key(v[j]) : 0u;
+  int my_i = 0;
+  uint32_t my_key = 0, top = 0;
+  if (!select_topk_untied<4>(key, k, lane, my_i, my_key, top, lds_idx)) select_topk<4>(key, k, lane, my_i, my_key, top);
+  topk_softmax_store(key_to_logit(top), key_to_logit(my_key), my_i, k, lane, out_idx, out_w, lds_idx);
+}
+
 // Plain top-k of several tokens by one wavefront: each token's logits are loaded one token
 // ahead of its selection, so only the first load's latency is exposed (E <= 256).
 __device__ __forceinline__ void topk_tokens(const float* __restrict__ logits, int t0, int T, int step, int E,
