@@ -638,6 +638,38 @@ def test_moe_decode_stack_equals_layer_calls(q, layer):
     assert q.sync_status(ws)[0] == 0
 
 
+def test_moe_decode_stack_mixed_routing(q, layer):
+    """A stack whose layers route in turn by plain top-k, with a selection bias, plain again,
+    with fixed experts and plain again (a plain layer after another layer takes its logits
+    loaded while that layer ends; the variants load theirs in the layer): every layer equals
+    its own call (routing, weights, outputs bit for bit), and the routing matches the oracle."""
+    seed, canon, tab = layer
+    L = 5
+    rng = np.random.default_rng(55)
+    xs = [gen_x(seed, (4500 + l,), 1, 4096, device=DEV) for l in range(L)]
+    lgs = [gen_logits_normal(seed, (4500 + l,), 1, 256, device=DEV) for l in range(L)]
+    bias = torch.from_numpy((rng.standard_normal(256) * 0.5).astype(np.float32)).to(DEV)
+    fixed = torch.from_numpy(rng.permutation(256)[:6].astype(np.int32)[None]).to(DEV)
+    kws = [{}, {"select_bias": bias}, {}, {"fixed_idx": fixed}, {}]
+    ys = [torch.empty(1, 4096, dtype=torch.float16, device=DEV) for _ in range(L)]
+    idx = [torch.empty(1, 6, dtype=torch.int32, device=DEV) for _ in range(L)]
+    wts = [torch.empty(1, 6, dtype=torch.float32, device=DEV) for _ in range(L)]
+    lt = q.layer_table([dict(experts=tab, logits=lgs[l], x=xs[l], y=ys[l], topk_idx=idx[l], topk_w=wts[l], **kws[l])
+                        for l in range(L)])
+    ws = q.moe_workspace(q.decode_stack_workspace_bytes(4096, 2048, 6), DEV)
+    print("decode stack, mixed routing", flush=True)
+    q.moe_decode_stack(4096, 2048, 256, 6, lt, ws=ws)
+    for l in range(L):
+        yr, ir, wr = q.moe_layer_fwd(tab, 4096, 2048, lgs[l], xs[l], top_k=6, flags=q.GALE_DECODE_STAGED, **kws[l])
+        assert torch.equal(idx[l], ir) and torch.equal(wts[l], wr), l
+        assert torch.equal(ys[l], yr), l
+        okw = {k: v.cpu().numpy() for k, v in kws[l].items()}
+        ridx, rw = O.route(lgs[l].cpu().numpy(), 6, **okw)
+        assert np.array_equal(idx[l].cpu().numpy(), ridx), l
+        assert np.abs(wts[l].cpu().numpy() - rw).max() <= 1e-6
+    assert q.sync_status(ws)[0] == 0
+
+
 def test_moe_one_launch_top_k_and_outlier_edges(q):
     """One token through experts whose rows carry 0, 1, 300 (past the staged outlier
     chunks) or 41 / 20 outliers, with top_k 1, 8 and 3 in turn on one workspace (the
