@@ -257,6 +257,8 @@ def test_gemv_many_matrices_sampled(q):
     (2048, 4096, 12, torch.float16, False, True, 0),            # one x shared by every matrix
     (2048, 4096, 24, torch.float16, False, False, "s1"),        # 2,048-entry outlier staging
     (2048, 4096, 24, torch.float16, False, False, "s2"),        # 4,096-entry outlier staging
+    (48, 1024, 300, torch.float16, False, False, 0),            # one chunk: one wavefront per workgroup
+    (32, 8192, 40, torch.float16, False, False, 0),             # eight chunks: the widest one-launch workgroup
 ])
 def test_gemv_one_launch_equals_prepared(q, rows, cols, n_mat, xdt, rotated, shared, flags):
     """One token per matrix: the GEMV rotates and splits x itself, in one launch, with the same
