@@ -236,7 +236,8 @@ __device__ __forceinline__ void load_activation(const GemvParams& P, const Geo& 
   }
 }
 
-// fp32 x~ of the item's vectors into LDS for the outlier gather (when it fits)
+// fp32 x~ of the item's vectors into LDS for the outlier gather (when it fits); with several
+// vectors, interleaved by column (xt[NS col + i]) so one gather reads every vector's value
 template <int NS>
 __device__ __forceinline__ void stage_activation(const GemvParams& P, const Geo& G, const Item& it, lds_f32* xt) {
   if (!P.stage_xt) return;
@@ -244,8 +245,35 @@ __device__ __forceinline__ void stage_activation(const GemvParams& P, const Geo&
     if (i >= it.nslots) break;
     const int ra = sel4(i, it.ra0, it.ra1, it.ra2, it.ra3);
     const u32x4* src = reinterpret_cast<const u32x4*>(P.ra + (size_t)ra * P.ra_stride);
-    lds_v4* dst = reinterpret_cast<lds_v4*>(xt + i * G.K);
-    for (int q = G.tid; q < (G.K >> 2); q += (int)blockDim.x) dst[q] = src[q];
+    if constexpr (NS == 1) {
+      lds_v4* dst = reinterpret_cast<lds_v4*>(xt);
+      for (int q = G.tid; q < (G.K >> 2); q += (int)blockDim.x) dst[q] = src[q];
+    } else {
+      for (int q = G.tid; q < (G.K >> 2); q += (int)blockDim.x) {
+        const u32x4 v = src[q];
+        xt[NS * (4 * q + 0) + i] = __uint_as_float(v.x);
+        xt[NS * (4 * q + 1) + i] = __uint_as_float(v.y);
+        xt[NS * (4 * q + 2) + i] = __uint_as_float(v.z);
+        xt[NS * (4 * q + 3) + i] = __uint_as_float(v.w);
+      }
+    }
+  }
+}
+
+// Every vector's x~ at column col from the staged copy (one LDS read)
+template <int NS>
+__device__ __forceinline__ void xs_at(const lds_f32* xt, int col, float* x) {
+  if constexpr (NS == 1) {
+    x[0] = xt[col];
+  } else if constexpr (NS == 2) {
+    typedef float v2f_t __attribute__((ext_vector_type(2)));
+    typedef __attribute__((address_space(3))) const v2f_t lds_v2f;
+    const v2f_t v = *reinterpret_cast<lds_v2f*>(xt + 2 * col);
+    x[0] = v[0]; x[1] = v[1];
+  } else {
+    typedef __attribute__((address_space(3))) const v4f lds_v4f;
+    const v4f v = *reinterpret_cast<lds_v4f*>(xt + 4 * col);
+    x[0] = v[0]; x[1] = v[1]; x[2] = v[2]; x[3] = v[3];
   }
 }
 
@@ -362,44 +390,47 @@ __device__ __forceinline__ void process_unit(const GemvParams& P, const Geo& G, 
         int col[8], by[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) { col[j] = lc[p + 4 * j - cbase]; by[j] = lv[((p + 4 * j) >> 1) - vbase]; }
+        // every vector's values (slots past the item's vectors compute into sums never stored)
+        float x[8][NS];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xs_at<NS>(xt, col[j], x[j]);
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
-          if (i < it.nslots) {
-            float x[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) x[j] = xt[i * G.K + col[j]];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) o[i] = fmaf(nibble_value(by[j], p), x[j], o[i]);
-          }
+          for (int j = 0; j < 8; ++j) o[i] = fmaf(nibble_value(by[j], p), x[j][i], o[i]);
         }
       }
       for (; p + 12 < p_mid; p += 16) {
         const int col0 = lc[p - cbase], col1 = lc[p + 4 - cbase], col2 = lc[p + 8 - cbase], col3 = lc[p + 12 - cbase];
         const int by0 = lv[(p >> 1) - vbase], by1 = lv[((p + 4) >> 1) - vbase];
         const int by2 = lv[((p + 8) >> 1) - vbase], by3 = lv[((p + 12) >> 1) - vbase];
+        float x0[NS], x1[NS], x2[NS], x3[NS];
+        xs_at<NS>(xt, col0, x0);
+        xs_at<NS>(xt, col1, x1);
+        xs_at<NS>(xt, col2, x2);
+        xs_at<NS>(xt, col3, x3);
 #pragma unroll
-        for (int i = 0; i < NS; ++i) {
-          if (i < it.nslots) {
-            const float x0 = xt[i * G.K + col0], x1 = xt[i * G.K + col1], x2 = xt[i * G.K + col2], x3 = xt[i * G.K + col3];
-            o[i] = fmaf(nibble_value(by3, p), x3, fmaf(nibble_value(by2, p), x2,
-                   fmaf(nibble_value(by1, p), x1, fmaf(nibble_value(by0, p), x0, o[i]))));
-          }
-        }
+        for (int i = 0; i < NS; ++i)
+          o[i] = fmaf(nibble_value(by3, p), x3[i], fmaf(nibble_value(by2, p), x2[i],
+                 fmaf(nibble_value(by1, p), x1[i], fmaf(nibble_value(by0, p), x0[i], o[i]))));
       }
       for (; p + 4 < p_mid; p += 8) {
         const int col0 = lc[p - cbase], col1 = lc[p + 4 - cbase];
         const float q0 = nibble_value(lv[(p >> 1) - vbase], p);
         const float q1 = nibble_value(lv[((p + 4) >> 1) - vbase], p + 4);
+        float x0[NS], x1[NS];
+        xs_at<NS>(xt, col0, x0);
+        xs_at<NS>(xt, col1, x1);
 #pragma unroll
-        for (int i = 0; i < NS; ++i)
-          if (i < it.nslots) o[i] = fmaf(q1, xt[i * G.K + col1], fmaf(q0, xt[i * G.K + col0], o[i]));
+        for (int i = 0; i < NS; ++i) o[i] = fmaf(q1, x1[i], fmaf(q0, x0[i], o[i]));
       }
       for (; p < p_mid; p += 4) {
         const int col = lc[p - cbase];
         const float q = nibble_value(lv[(p >> 1) - vbase], p);
+        float x0[NS];
+        xs_at<NS>(xt, col, x0);
 #pragma unroll
-        for (int i = 0; i < NS; ++i)
-          if (i < it.nslots) o[i] = fmaf(q, xt[i * G.K + col], o[i]);
+        for (int i = 0; i < NS; ++i) o[i] = fmaf(q, x0[i], o[i]);
       }
     } else {
       for (; p < p_mid; p += 4) {
@@ -434,7 +465,7 @@ __device__ __forceinline__ void process_unit(const GemvParams& P, const Geo& G, 
             const int ra = sel4(i, it.ra0, it.ra1, it.ra2, it.ra3);
             const float* xg = reinterpret_cast<const float*>(P.ra + (size_t)ra * P.ra_stride);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) o[i] = fmaf(q[j], P.stage_xt ? xt[i * G.K + col[j]] : xg[col[j]], o[i]);
+            for (int j = 0; j < 8; ++j) o[i] = fmaf(q[j], P.stage_xt ? xt[NS * col[j] + i] : xg[col[j]], o[i]);
           }
         }
       }
