@@ -30,7 +30,12 @@ Reported:
                on bounded samples (scaled as stated); its outputs also check the GPU step
   stream_ceiling  a plain elementwise kernel (negate, fp32) over a 1 GiB buffer: the
                HBM rate a trivial streaming kernel reaches on this device; it is also the
-               known-size reference that scales the HBM byte counters behind "traffic"
+               known-size reference that scales the HBM byte counters behind "traffic";
+               beside it a read-only pass over the same 1 GiB (the library's plain streaming-read
+               diagnostic kernel)
+  step_spread, launch_spread  median, p10 and p90 of single calls (one HIP event between
+               back-to-back calls) for the value's step and the roofline launch; the value and
+               the roofline themselves are averages over their timed regions
 
 "traffic" is read from profiles/gemv_kernel_traffic.txt, written from two rocprofv3
 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this script; it is reported only while the
@@ -62,6 +67,7 @@ PREFILL_TOKENS = 2048
 PREFILL_FLOP = 2 * TOPK * PREFILL_TOKENS * 3 * INTER * HIDDEN      # dense-equivalent, 618.5 GFLOP
 MFMA_FP16_PEAK_TFLOPS = 2500.0
 CEIL_BYTES = 1 << 30            # one side of the streaming-ceiling kernel
+READ_GRID = 8192                # workgroups of the read-only streaming kernel (32 per CU)
 GEMV_SOURCES = ("gale_gemv.hip", "gale_gemv_core.h", "gale_decode.h", "gale_internal.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_kernel_traffic.txt")
 
@@ -137,6 +143,28 @@ def time_events(fn, reps: int):
     e.record()
     e.synchronize()
     return s.elapsed_time(e) / reps
+
+
+def time_spread(fn, reps: int):
+    """Per-call milliseconds of reps back-to-back calls of fn (one HIP event between calls on the
+    current stream): (median, p10, p90)."""
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for i in range(reps):
+        fn()
+        ev[i + 1].record()
+    ev[-1].synchronize()
+    d = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))
+    pick = lambda f: d[min(reps - 1, int(f * (reps - 1) + 0.5))]
+    return pick(0.5), pick(0.1), pick(0.9)
+
+
+def spread_dict(sp, scale: float = 1e3, unit: str = "us"):
+    med, p10, p90 = sp
+    nd = 4 if unit == "ms" else 2
+    return {f"median_{unit}": round(med * scale, nd), f"p10_{unit}": round(p10 * scale, nd),
+            f"p90_{unit}": round(p90 * scale, nd)}
 
 
 def time_isolated(fn, reps: int):
@@ -413,6 +441,7 @@ def main() -> int:
     torch.cuda.synchronize()
     ms_gemv = time_events(gemv_e2e_call, args.gemv_reps)
     gemv_gbps = n * GEMV_UNIT_BYTES / (ms_gemv * 1e-3) / 1e9
+    gemv_spread = time_spread(gemv_e2e_call, args.gemv_reps)
     log(f"single-matrix workload as configured (rotation + split + GEMV in one launch, {n} distinct matrices): "
         f"{ms_gemv * 1e3:.1f} us -> {gemv_gbps:.0f} GB/s ({100 * gemv_gbps / HBM_PEAK_GBPS:.1f}% of 8 TB/s)")
 
@@ -575,6 +604,9 @@ def main() -> int:
     modes = {"layer_calls_eager": ms_eager, "layer_calls_graph": ms_graph, "stack_launch": ms_stack}
     best_mode = min((m for m in modes if modes[m] is not None), key=lambda m: modes[m])
     ms_step = modes[best_mode]
+    step_fns = {"layer_calls_eager": step, "layer_calls_graph": (g.replay if ms_graph is not None else None),
+                "stack_launch": stack_step}
+    step_spread = time_spread(step_fns[best_mode], args.steps)
     bytes_per_token = 43 * TOPK * EXPERT_BYTES * L // 43
     gbps = bytes_per_token / (ms_step * 1e-3) / 1e9
 
@@ -632,6 +664,9 @@ def main() -> int:
         prefill()
     torch.cuda.synchronize()
     ms_prefill = time_events(prefill, args.prefill_reps)
+    loads = torch.bincount(torch.topk(lgp, TOPK, dim=1).indices.flatten(), minlength=EXPERTS).sort().values.cpu()
+    expert_loads = {"max": int(loads[-1]), "median": int(loads[EXPERTS // 2]), "min": int(loads[0]),
+                    "top32_share": round(float(loads[-32:].sum()) / float(loads.sum()), 4)}
     prefill_tflops = PREFILL_FLOP / (ms_prefill * 1e-3) / 1e12
     log(f"grouped prefill: {PREFILL_TOKENS} tokens in {ms_prefill:.3f} ms -> "
         f"{PREFILL_TOKENS / ms_prefill * 1e3:.0f} tokens/s, {prefill_tflops:.1f} dense-equivalent TFLOP/s")
@@ -645,8 +680,25 @@ def main() -> int:
     torch.cuda.synchronize()
     ms_ceil = time_events(lambda: torch.neg(src, out=dst), 10)
     ceil_gbps = 2 * CEIL_BYTES / (ms_ceil * 1e-3) / 1e9
-    del src, dst
-    log(f"streaming ceiling (elementwise negate, 2 x 1 GiB): {ceil_gbps:.0f} GB/s")
+    del dst
+    # a read-only pass over the same 1 GiB: the library's plain streaming-read kernel (16 bytes per
+    # lane per step, one word written per workgroup)
+    sink = torch.empty(READ_GRID, dtype=torch.int32, device=dev)
+
+    def read_pass():
+        rc = lib.gale_read_stream(src.data_ptr(), CEIL_BYTES, sink.data_ptr(), READ_GRID,
+                                  torch.cuda.current_stream().cuda_stream)
+        if rc:
+            raise RuntimeError(lib.gale_last_error().decode())
+
+    for _ in range(3):
+        read_pass()
+    torch.cuda.synchronize()
+    ms_read = time_events(read_pass, 10)
+    read_gbps = CEIL_BYTES / (ms_read * 1e-3) / 1e9
+    del src, sink
+    log(f"streaming ceiling (elementwise negate, 2 x 1 GiB): {ceil_gbps:.0f} GB/s; read-only (gale_read_stream, "
+        f"1 GiB): {read_gbps:.0f} GB/s")
     traffic = recorded_traffic(n)
 
     out = {
@@ -671,6 +723,7 @@ def main() -> int:
         "hbm_frac_step": round(gbps / HBM_PEAK_GBPS, 4),
         "step_mode": best_mode,
         "ms_per_step_modes": {m: (None if v is None else round(v, 5)) for m, v in modes.items()},
+        "step_spread": spread_dict(step_spread, 1.0, "ms"),
         "ms_per_step_eager": round(ms_eager, 5),
         "ms_per_step_graph": None if ms_graph is None else round(ms_graph, 5),
         "bytes_per_token": bytes_per_token,
@@ -681,6 +734,7 @@ def main() -> int:
                      "launch": f"{n} distinct [2048,4096] matrices (w1, w3 of {n // 2} experts) x 1 token, "
                                f"each with its own fp16 x; two disjoint sets alternated",
                      "bytes_per_launch": n * GEMV_UNIT_BYTES, "avg_launch_us": round(ms_gemv * 1e3, 2),
+                     "launch_spread": spread_dict(gemv_spread),
                      "source_sha256": gemv_source_hash()[:16]},
         "gemv_single_matrix": {
             "workload": "one [2048 out, 4096 in] matrix, 1 token: FWHT-1024 of x and the fp8 activation split, "
@@ -708,10 +762,13 @@ def main() -> int:
                                 f"Zipf(1.1) top-6 routing, grouped path",
                     "ms": round(ms_prefill, 4), "tokens_per_s": round(PREFILL_TOKENS / ms_prefill * 1e3, 1),
                     "dense_equiv_tflops": round(prefill_tflops, 2),
-                    "frac_of_fp16_mfma_peak": round(prefill_tflops / MFMA_FP16_PEAK_TFLOPS, 4)},
+                    "frac_of_fp16_mfma_peak": round(prefill_tflops / MFMA_FP16_PEAK_TFLOPS, 4),
+                    "pairs_per_expert": expert_loads},
         "gemv_sweep": sweep,
         "stream_ceiling": {"value": round(ceil_gbps, 1), "unit": "GB/s",
-                           "kernel": "torch.neg fp32, read 1 GiB + write 1 GiB"},
+                           "kernel": "torch.neg fp32, read 1 GiB + write 1 GiB",
+                           "read_only_gbps": round(read_gbps, 1),
+                           "read_only_kernel": "gale_read_stream: wave-contiguous 4 KB runs of 16-byte nontemporal loads over 1 GiB"},
     }
 
     if not args.no_cpu:
@@ -720,7 +777,7 @@ def main() -> int:
         per_cfg, cores, model, err, n_l = cpu_baselines(synth, O, seed, dev, xs, logits, ys, L)
         st = per_cfg["stack_token"]
         out["cpu_baseline"] = {"value": st["gbps_all_cores"], "unit": "GB/s", "cores": cores, "kind": "oracle",
-                               "cpu_model": model, "tokens_per_s": round(1.0 / st["s_per_token_all_cores"], 5),
+                               "cpu_model": model, "nproc": os.cpu_count(), "tokens_per_s": round(1.0 / st["s_per_token_all_cores"], 5),
                                "sample": st["sample"] + " (route + 6 fp64 dequantize/matvec FFNs per layer)",
                                "per_workload": per_cfg}
         out["parity_rel_l2_sampled_layers"] = err

@@ -384,6 +384,15 @@ int gale_route_topk(const float* logits, int32_t n_tok, int32_t n_experts, int32
                     int32_t* topk_idx, float* topk_w, int32_t* offsets, int32_t* perm,
                     void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Diagnostic, not a step of the method: reads `bytes` bytes at device pointer src (16-byte
+ * aligned, a positive multiple of 16) once with a plain streaming kernel, 16 bytes per lane per
+ * step, on `stream`, and writes one folded word per workgroup to the device array sink
+ * (4-byte aligned, sink_words >= 1 words; the grid is at most sink_words workgroups).  Timed
+ * by the caller, it gives the HBM read rate a trivial kernel reaches on this device, the
+ * practical ceiling next to the 8 TB/s peak.  Errors: GALE_ERR_NULL, GALE_ERR_SHAPE,
+ * GALE_ERR_ALIGN, GALE_ERR_HIP (a launch failure). */
+int gale_read_stream(const void* src, size_t bytes, uint32_t* sink, int32_t sink_words, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -122,6 +122,7 @@ _SIGS = {
     "gale_moe_decode_stack": (_I32, [_I32, _I32, _I32, _I32, _I32, _P, _P, _SZ, _U32, _P]),
     "gale_moe_decode_stack_static": (_I32, [_I32, _I32, _I32, _I32, _I32, _P, _U32, _P]),
     "gale_sync_init": (_I32, [_P, _P]),
+    "gale_read_stream": (_I32, [_P, ctypes.c_size_t, _P, ctypes.c_int32, _P]),
     "gale_sync_status": (_I32, [_P, ctypes.POINTER(ctypes.c_uint64)]),
 }
 

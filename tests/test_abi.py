@@ -183,3 +183,15 @@ def test_decode_stack_validation_before_gpu_work():
     assert L.gale_moe_decode_stack(4096, 2048, 256, 9, 2, fake, fake, 1 << 30, 0, None) == -2      # top_k
     assert L.gale_sync_init(None, None) == -1
     assert L.gale_sync_init(fake + 8, None) == -4
+
+
+def test_read_stream_validation_before_gpu_work():
+    """The streaming-read diagnostic refuses bad arguments on the host."""
+    L = q.lib()
+    fake = 1 << 40                      # never dereferenced: every call below fails validation
+    assert L.gale_read_stream(None, 1024, fake, 4, None) == -1
+    assert L.gale_read_stream(fake, 1024, None, 4, None) == -1
+    assert L.gale_read_stream(fake, 1000, fake, 4, None) == -2      # not a multiple of 16
+    assert L.gale_read_stream(fake, 0, fake, 4, None) == -2
+    assert L.gale_read_stream(fake, 1024, fake, 0, None) == -2
+    assert L.gale_read_stream(fake + 8, 1024, fake, 4, None) == -4  # alignment

@@ -882,3 +882,22 @@ def test_moe_closed_form(q):
     ref = np.zeros((3, 4096))
     ref[:, :2048] = coef[:, None] * xs * xs / (1 + np.exp(-xs))
     assert O.rel_l2(np_of(y), ref).max() <= 1e-3
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("n_bytes,sink_words", [(16, 1), (1 << 20, 64), ((1 << 20) + 48, 4096)])
+def test_read_stream_reads_every_word(q, n_bytes, sink_words):
+    """The streaming-read diagnostic reads every 16-byte granule once: the XOR of its per-workgroup
+    words equals the XOR of all 32-bit words of the buffer."""
+    g = torch.Generator().manual_seed(n_bytes)
+    host = torch.randint(-2 ** 31, 2 ** 31 - 1, (n_bytes // 4,), dtype=torch.int64, generator=g).to(torch.int32)
+    buf = host.to(DEV)
+    sink = torch.zeros(sink_words, dtype=torch.int32, device=DEV)
+    rc = q.lib().gale_read_stream(buf.data_ptr(), n_bytes, sink.data_ptr(), sink_words,
+                                  torch.cuda.current_stream().cuda_stream)
+    assert rc == 0
+    torch.cuda.synchronize()
+    grid = min((n_bytes // 16 + 255) // 256, sink_words)
+    want = int(np.bitwise_xor.reduce(host.numpy().view(np.uint32)))
+    got = int(np.bitwise_xor.reduce(sink[:grid].cpu().numpy().view(np.uint32)))
+    assert got == want
