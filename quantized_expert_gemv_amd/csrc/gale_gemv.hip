@@ -194,13 +194,13 @@ __device__ __forceinline__ void issue_unit(const GemvParams& P, const Geo& G, co
   for (int k = 0; k < OC; ++k) {
     int ch = cf + 64 * k + G.lane;
     ch = ch < cl ? ch : cl;
-    b.oc[k] = ld16(dv.ocols, (uint32_t)ch * 16u);
+    b.oc[k] = ld16_stream(dv.ocols, (uint32_t)ch * 16u);
   }
 #pragma unroll
   for (int k = 0; k < val_chunks(OC); ++k) {
     int ch = vf + 64 * k + G.lane;
     ch = ch < vl ? ch : vl;
-    b.ov[k] = ld16(dv.ovals, (uint32_t)ch * 16u);
+    b.ov[k] = ld16_stream(dv.ovals, (uint32_t)ch * 16u);
   }
   bool ok;
   const int n = outlier_row<R>(P, G, v.rg, &ok);

@@ -41,7 +41,7 @@ __device__ __forceinline__ uint4 ld16(const char* base, uint32_t off) {
   const u32x4 v = *reinterpret_cast<const u32x4*>(base + off);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
-// the same for data read exactly once (sign words, block scales)
+// the same for data read exactly once (sign words, block scales, outlier chunks)
 __device__ __forceinline__ uint4 ld16_stream(const char* base, uint32_t off) {
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + off));
   return make_uint4(v.x, v.y, v.z, v.w);
