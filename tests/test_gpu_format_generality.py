@@ -18,6 +18,8 @@ import torch
 import oracle as O
 from synth import config_seed, gen_logits_normal, gen_logits_zipf, gen_matrices, gen_matrix, gen_x
 
+from tests.test_gpu_parity import oracle_pool
+
 pytestmark = pytest.mark.gpu
 
 REL_L2_BAR = 2e-3
@@ -93,12 +95,12 @@ def test_moe_outlier_budgets_decode_and_grouped(q, frac):
     yd, idx, _ = q.moe_layer_fwd(tab, 4096, 2048, lg[:1], x[:1], top_k=6)
     yg, _, _ = q.moe_layer_fwd(tab, 4096, 2048, lg, x, top_k=6, flags=q.GALE_PATH_GROUPED | q.GALE_GROUPED_GEMM)
     yi, _, _ = q.moe_layer_fwd(tab, 4096, 2048, lg, x, top_k=6, flags=q.GALE_PATH_GROUPED | q.GALE_GROUPED_ITEMS)
-    sample = [0, T - 1]
-    yref, ridx, _ = O.moe(expert_of, lg.cpu().numpy()[sample], x.cpu().numpy()[sample], k=6)
+    with oracle_pool() as ex:
+        yref, ridx, _ = O.moe(expert_of, lg.cpu().numpy(), x.cpu().numpy(), k=6, map_fn=ex.map)
     assert np.array_equal(idx.cpu().numpy(), ridx[:1])
     e_dec = O.rel_l2(np_of(yd[0]), yref[0]).max()
-    e_gemm = O.rel_l2(np_of(yg[sample]), yref).max()
-    e_items = O.rel_l2(np_of(yi[sample]), yref).max()
+    e_gemm = O.rel_l2(np_of(yg), yref).max()             # every token
+    e_items = O.rel_l2(np_of(yi), yref).max()
     e_gi = O.rel_l2(np_of(yg), np_of(yi)).max()
     print(f"moe outliers {frac:.0%}: decode {e_dec:.3e}, GEMM {e_gemm:.3e}, items {e_items:.3e}, GEMM vs items {e_gi:.3e}")
     assert max(e_dec, e_gemm, e_items, e_gi) <= REL_L2_BAR
@@ -185,7 +187,7 @@ def test_pro_geometry_ffn(q):
 def test_pro_geometry_moe(q):
     # 384 routed experts whose descriptors cycle over 6 distinct weight sets; decode of one
     # and of four tokens, and the grouped path on a Zipf-skewed batch (hybrid, all-GEMM
-    # and all-items), against the oracle on sampled tokens
+    # and all-items), against the oracle on every token
     seed = config_seed(24)
     D = 6
     canon, packed = experts(q, seed, D, PRO_HIDDEN, PRO_INTER)
@@ -206,14 +208,14 @@ def test_pro_geometry_moe(q):
     assert np.array_equal(idx.cpu().numpy(), ridx)
     assert np.array_equal(idx1.cpu().numpy(), ridx[:1])
     counts = np.bincount(ridx.ravel(), minlength=PRO_EXPERTS)
-    sample = [0, int(np.nonzero((ridx == int(np.argmax(counts))).any(axis=1))[0][-1])]
-    yref, _, _ = O.moe(expert_of, lgn[sample], x.cpu().numpy()[sample], k=6)
+    with oracle_pool() as ex:
+        yref, _, _ = O.moe(expert_of, lgn, x.cpu().numpy(), k=6, map_fn=ex.map)
     errs = {
         "decode T=1": O.rel_l2(np_of(y1[0]), yref[0]).max(),
-        "decode T=4": O.rel_l2(np_of(y4[0]), yref[0]).max(),
-        "hybrid": O.rel_l2(np_of(yh[sample]), yref).max(),
-        "GEMM": O.rel_l2(np_of(yg[sample]), yref).max(),
-        "items": O.rel_l2(np_of(yi[sample]), yref).max(),
+        "decode T=4": O.rel_l2(np_of(y4), yref[:4]).max(),
+        "hybrid": O.rel_l2(np_of(yh), yref).max(),
+        "GEMM": O.rel_l2(np_of(yg), yref).max(),
+        "items": O.rel_l2(np_of(yi), yref).max(),
         "GEMM vs items": O.rel_l2(np_of(yg), np_of(yi)).max(),
         "hybrid vs items": O.rel_l2(np_of(yh), np_of(yi)).max(),
     }
