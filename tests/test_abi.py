@@ -195,3 +195,18 @@ def test_read_stream_validation_before_gpu_work():
     assert L.gale_read_stream(fake, 0, fake, 4, None) == -2
     assert L.gale_read_stream(fake, 1024, fake, 0, None) == -2
     assert L.gale_read_stream(fake + 8, 1024, fake, 4, None) == -4  # alignment
+
+
+def test_empty_inputs_refused_before_gpu_work():
+    """No tokens, matrices or experts: refused on the host with GALE_ERR_SHAPE."""
+    L = q.lib()
+    fake = 1 << 40                      # never dereferenced: every call below fails validation
+    # gale_expert_gemv(rows, cols, table, n_mat, x, x_dtype, x_shared, n_tok, y, y_dtype, ws, ws_bytes, flags, stream)
+    assert L.gale_expert_gemv(2048, 4096, fake, 0, fake, 0, 0, 1, fake, 0, fake, 1 << 30, 0, None) == -2
+    assert L.gale_expert_gemv(2048, 4096, fake, 1, fake, 0, 0, 0, fake, 0, fake, 1 << 30, 0, None) == -2
+    # gale_expert_ffn(hidden, inter, table, n_exp, x, x_shared, n_tok, y, ws, ws_bytes, stream)
+    assert L.gale_expert_ffn(4096, 2048, fake, 0, fake, 0, 1, fake, fake, 1 << 30, None) == -2
+    assert L.gale_expert_ffn(4096, 2048, fake, 1, fake, 0, 0, fake, fake, 1 << 30, None) == -2
+    # gale_moe_layer_fwd(hidden, inter, table, n_experts, logits, top_k, x, n_tok, y, idx, w, ws, ws_bytes, flags, stream)
+    assert L.gale_moe_layer_fwd(4096, 2048, fake, 256, fake, 6, fake, 0, fake, None, None, fake, 1 << 30, 0, None) == -2
+    assert L.gale_moe_layer_fwd(4096, 2048, fake, 0, fake, 6, fake, 1, fake, None, None, fake, 1 << 30, 0, None) == -2
